@@ -1,0 +1,338 @@
+"""PuzzleKV CPU oracle -- plain, slow, double-precision reference.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code
+with the HIP path (``long_context_decode_pkv_amd``) and neither imports the other.
+
+Source of every formula: the page "PuzzleKV: Page-Wise Low-Rank Decomposition for
+KV Cache Compression" (arXiv 2608.23843).  Section / equation numbers below refer
+to that page.
+
+What the oracle computes is the plain definition of the method's result:
+
+    o = softmax(q K^T / sqrt(d)) V                      (Sec. 3.2, Eq. 1)
+
+where K and V equal the dense cache except that every page classified as
+factorized is replaced by its rank-r truncated SVD U_r Sigma_r W_r^T (Sec. 3.2
+"Truncated SVD"; Sec. 3.3 Eq. 2).  It uses no Gram matrix, no online softmax and
+no split-K: those are the method's machinery, which the GPU path implements.
+The page-wise Eq. 4 / Eq. 5 states are provided separately
+(``page_state_factored``, ``page_state_dense``, ``merge_states``) so that a test
+can show they reproduce the plain definition.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+  * the sink is the first s/P pages, the window the w/P most recently completed
+    pages plus the page still being filled (Sec. 3.3 (1)-(3); Sec. 4.1
+    "Implementation");
+  * the factor placement is Lf = U_r Sigma_r (P x r), Rf = W_r^T (r x d); the
+    page's Eq. 2 puts Sigma on the right factor, the product is identical;
+  * the "stored" variant rounds Lf and Rf to the cache dtype, nearest-even;
+  * query head h reads KV head floor(h / G) (contiguous GQA groups);
+  * no causal mask: the single decode query sees every cached token.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpkv_oracle.so")
+_LIB = None
+
+# Page classes.  Their numeric values are the ones the C-ABI's page table
+# reports (an interface value both sides must agree on, not shared code).
+SINK, FACT, WIN, PART = 1, 2, 3, 4
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_LIB_PATH):
+            from oracle import build as _build  # noqa: WPS433 (build once, on demand)
+            _build.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.pkvo_svd.argtypes = [vp, ci, ci, vp, vp, vp]
+        lib.pkvo_svd.restype = ci
+        lib.pkvo_svd_batch.argtypes = [vp, i64, ci, ci, vp, vp, vp]
+        lib.pkvo_svd_batch.restype = ci
+        lib.pkvo_round_array.argtypes = [vp, i64, ci]
+        lib.pkvo_round_array.restype = None
+        lib.pkvo_bf16_encode.argtypes = [vp, vp, i64]
+        lib.pkvo_bf16_encode.restype = None
+        lib.pkvo_bf16_decode.argtypes = [vp, vp, i64]
+        lib.pkvo_bf16_decode.restype = None
+        lib.pkvo_num_threads.argtypes = []
+        lib.pkvo_num_threads.restype = ci
+        _LIB = lib
+    return _LIB
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    """OpenMP threads the C core uses (OMP_NUM_THREADS)."""
+    return int(_lib().pkvo_num_threads())
+
+
+# --------------------------------------------------------------------------
+# Storage dtypes
+# --------------------------------------------------------------------------
+
+def bf16_bits(x) -> np.ndarray:
+    """Nearest bfloat16 of each double, ties to even, as uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _lib().pkvo_bf16_encode(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def bf16_decode(bits) -> np.ndarray:
+    """bfloat16 bit patterns -> float64 (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float64)
+    _lib().pkvo_bf16_decode(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def round_to(x, dtype) -> np.ndarray:
+    """Round to the storage dtype ('bf16', 'f32') nearest-even, back to float64.
+    dtype None returns an unrounded float64 copy."""
+    y = np.array(x, dtype=np.float64, copy=True, order="C")
+    mode = {"bf16": 0, "f32": 1, None: 2}[dtype]
+    _lib().pkvo_round_array(_ptr(y), y.size, mode)
+    return y
+
+
+# --------------------------------------------------------------------------
+# Truncated SVD of a page (Sec. 3.2 "Truncated SVD"; Sec. 3.3 Eq. 2)
+# --------------------------------------------------------------------------
+
+def svd(X):
+    """X (n x m, n <= m) -> U (n x n), S (n,), Wt (n x m); X = U diag(S) Wt,
+    S descending.  One-sided Jacobi in double; raises if it does not converge."""
+    X = np.ascontiguousarray(X, dtype=np.float64)
+    n, m = X.shape
+    U = np.empty((n, n))
+    S = np.empty(n)
+    Wt = np.empty((n, m))
+    rc = _lib().pkvo_svd(_ptr(X), n, m, _ptr(U), _ptr(S), _ptr(Wt))
+    if rc < 0:
+        raise RuntimeError(f"oracle Jacobi SVD failed (status {rc})")
+    return U, S, Wt
+
+
+def svd_batch(X):
+    """Batched svd over the leading axes of X (..., n, m)."""
+    X = np.ascontiguousarray(X, dtype=np.float64)
+    lead = X.shape[:-2]
+    n, m = X.shape[-2:]
+    cnt = int(np.prod(lead)) if lead else 1
+    U = np.empty(lead + (n, n))
+    S = np.empty(lead + (n,))
+    Wt = np.empty(lead + (n, m))
+    if cnt:
+        rc = _lib().pkvo_svd_batch(_ptr(X), cnt, n, m, _ptr(U), _ptr(S), _ptr(Wt))
+        if rc < 0:
+            raise RuntimeError(f"oracle Jacobi SVD failed (status {rc})")
+    return U, S, Wt
+
+
+def truncate(U, S, Wt, r):
+    """Rank-r factors in the stored placement: Lf = U_r Sigma_r, Rf = W_r^T."""
+    Lf = U[..., :, :r] * S[..., None, :r]
+    Rf = Wt[..., :r, :].copy()
+    return Lf, Rf
+
+
+def factorize(X, r, store=None):
+    """Rank-r factors of each page of X (..., P, d), optionally rounded to the
+    storage dtype.  Returns (Lf, Rf, S) with S the page's full spectrum."""
+    U, S, Wt = svd_batch(X)
+    Lf, Rf = truncate(U, S, Wt, r)
+    if store is not None:
+        Lf = round_to(Lf, store)
+        Rf = round_to(Rf, store)
+    return Lf, Rf, S
+
+
+def optimal_error(S, r):
+    """Eckart-Young-Mirsky: the best rank-r Frobenius error from the spectrum."""
+    tail = np.asarray(S)[..., r:]
+    return np.sqrt(np.sum(tail * tail, axis=-1))
+
+
+# --------------------------------------------------------------------------
+# Page classification (Sec. 3.3 (1)-(3) and "Incremental Cache Update (5)")
+# --------------------------------------------------------------------------
+
+def classify(T, P, s, w, n_fact=None):
+    """Class and slot of each logical page of a T-token cache.
+
+    Sink: the first s/P pages.  Window: the w/P most recently completed pages
+    (and, while a promotion is pending, the page that has just left it).  The
+    page still being filled is PART.  Every other completed page is FACT.
+    n_fact=None is the steady state in which every eligible page has been
+    factorized; otherwise exactly the first n_fact eligible pages are FACT.
+
+    Slots: SINK -> p, FACT -> p - n_s (factor storage is filled in page
+    order), WIN/PART -> (p - n_s) mod (n_w + 1) (a ring of window buffers).
+    """
+    if P <= 0 or s % P or w % P or T < 0:
+        raise ValueError("s and w must be multiples of P")
+    n_s, n_w = s // P, w // P
+    n_pages = -(-T // P)
+    cls = np.zeros(n_pages, dtype=np.int32)
+    slot = np.zeros(n_pages, dtype=np.int32)
+    completed = [p for p in range(n_pages) if (p + 1) * P <= T]
+    non_sink_done = [p for p in completed if p >= n_s]
+    if n_fact is None:
+        n_elig = max(0, len(non_sink_done) - n_w)
+    else:
+        n_elig = n_fact
+    fact_set = set(non_sink_done[:n_elig])
+    for p in range(n_pages):
+        if p < n_s:
+            cls[p], slot[p] = SINK, p
+        elif p in fact_set:
+            cls[p], slot[p] = FACT, p - n_s
+        elif p in completed:
+            cls[p], slot[p] = WIN, (p - n_s) % (n_w + 1)
+        else:
+            cls[p], slot[p] = PART, (p - n_s) % (n_w + 1)
+    return cls, slot
+
+
+# --------------------------------------------------------------------------
+# Attention (Sec. 3.2 Eq. 1) and the page-wise states (Sec. 3.3 Eq. 4, Eq. 5)
+# --------------------------------------------------------------------------
+
+def attention(q, K, V):
+    """softmax(q K^T / sqrt(d)) V for q (G, d), K and V (T, d), in float64."""
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    d = q.shape[-1]
+    scores = (q @ K.T) / math.sqrt(d)
+    scores = scores - scores.max(axis=-1, keepdims=True)
+    wts = np.exp(scores)
+    wts = wts / wts.sum(axis=-1, keepdims=True)
+    return wts @ V
+
+
+def page_state_factored(q, LfK, RfK, LfV, RfV):
+    """Eq. 4: (m_p, l_p, o_p) of one factorized page, contracting q with the
+    small factors first: s = (q RfK^T) LfK^T / sqrt(d), o = (e^(s-m) LfV) RfV."""
+    q = np.asarray(q, dtype=np.float64)
+    d = q.shape[-1]
+    s = ((q @ RfK.T) @ LfK.T) / math.sqrt(d)
+    m = s.max(axis=-1)
+    e = np.exp(s - m[..., None])
+    return m, e.sum(axis=-1), (e @ LfV) @ RfV
+
+
+def page_state_dense(q, Kp, Vp):
+    """Eq. 4's state for a dense page (same triple, from stored K_p and V_p)."""
+    q = np.asarray(q, dtype=np.float64)
+    d = q.shape[-1]
+    s = (q @ np.asarray(Kp, dtype=np.float64).T) / math.sqrt(d)
+    m = s.max(axis=-1)
+    e = np.exp(s - m[..., None])
+    return m, e.sum(axis=-1), e @ np.asarray(Vp, dtype=np.float64)
+
+
+def merge_states(states):
+    """Eq. 5: m = max_p m_p;  o = sum e^(m_p-m) o_p / sum e^(m_p-m) l_p.
+    An empty state (l = 0, m = -inf) contributes nothing."""
+    ms = np.stack([st[0] for st in states])
+    m = ms.max(axis=0)
+    num = 0.0
+    den = 0.0
+    for mp, lp, op in states:
+        wgt = np.where(np.isneginf(mp), 0.0, np.exp(np.where(np.isneginf(mp), 0.0, mp - m)))
+        num = num + wgt[..., None] * op
+        den = den + wgt * lp
+    return num / den[..., None]
+
+
+# --------------------------------------------------------------------------
+# Whole-cache decode (the quantity the GPU path is checked against)
+# --------------------------------------------------------------------------
+
+def reconstruct_cache(X, T, P, s, w, r, store, n_fact=None, with_metrics=False):
+    """X: (T, d) dense pages of one (sequence, KV head, K or V).  Returns
+    (Xhat_stored, Xhat_exact, metrics) where FACT pages are replaced by their
+    rank-r truncated SVD (stored = factors rounded to `store`)."""
+    X = np.asarray(X, dtype=np.float64)[:T]
+    cls, _ = classify(T, P, s, w, n_fact)
+    fact = np.nonzero(cls == FACT)[0]
+    Xs = X.copy()
+    Xe = X.copy()
+    metrics = None
+    if len(fact):
+        pages = np.stack([X[p * P:(p + 1) * P] for p in fact])
+        U, S, Wt = svd_batch(pages)
+        Lf, Rf = truncate(U, S, Wt, r)
+        exact = Lf @ Rf
+        Lfs = round_to(Lf, store) if store else Lf
+        Rfs = round_to(Rf, store) if store else Rf
+        stored = Lfs @ Rfs
+        for k, p in enumerate(fact):
+            Xs[p * P:(p + 1) * P] = stored[k]
+            Xe[p * P:(p + 1) * P] = exact[k]
+        if with_metrics:
+            metrics = dict(
+                pages=fact,
+                S=S,
+                opt=optimal_error(S, r),
+                norm=np.sqrt((pages ** 2).sum(axis=(-2, -1))),
+                err_exact=np.sqrt(((pages - exact) ** 2).sum(axis=(-2, -1))),
+                err_stored=np.sqrt(((pages - stored) ** 2).sum(axis=(-2, -1))),
+            )
+    return Xs, Xe, metrics
+
+
+def decode(q, K, V, T, P, s, w, r_k, r_v, store, n_fact=None, kv_heads=None):
+    """Attention output of one decode step over a hybrid cache.
+
+    q: (B, H_q, d); K, V: (B, H_kv, >=T, d) holding the stored (already
+    dtype-rounded) values.  Returns dict(o_stored, o_exact) of shape
+    (B, H_q, d); query heads of KV heads not in `kv_heads` are left NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    o_s = np.full((B, Hq, d), np.nan)
+    o_e = np.full((B, Hq, d), np.nan)
+    heads = range(Hkv) if kv_heads is None else kv_heads
+    for b in range(B):
+        for h in heads:
+            Ks, Ke, _ = reconstruct_cache(K[b, h], T, P, s, w, r_k, store, n_fact)
+            Vs, Ve, _ = reconstruct_cache(V[b, h], T, P, s, w, r_v, store, n_fact)
+            qs = q[b, h * G:(h + 1) * G]
+            o_s[b, h * G:(h + 1) * G] = attention(qs, Ks, Vs)
+            o_e[b, h * G:(h + 1) * G] = attention(qs, Ke, Ve)
+    return dict(o_stored=o_s, o_exact=o_e)
+
+
+# --------------------------------------------------------------------------
+# Storage accounting (Sec. 1; Sec. 3.3 Eq. 3; App. D.1 Eq. 6)
+# --------------------------------------------------------------------------
+
+def storage_ratio(P, r_k, r_v, d):
+    """Eq. 3: elements of a factorized K/V page pair over its dense elements,
+    counted from the factor shapes: Lf is P x r, Rf is r x d."""
+    factor_elems = (P * r_k + r_k * d) + (P * r_v + r_v * d)
+    dense_elems = 2 * P * d
+    return factor_elems / dense_elems
+
+
+def kv_cache_elements(n_layers, n_kv_heads, T, d):
+    """Sec. 1: K and V of every layer and KV head, T tokens of d each."""
+    return 2 * n_layers * n_kv_heads * T * d
