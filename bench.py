@@ -1,0 +1,311 @@
+"""Benchmark of the PuzzleKV hot path on one MI355X.
+
+Default workload (qwen3-32b-layer-128k): one layer of a Qwen3-32B-shaped cache,
+B = 1, 64 query heads, 8 KV heads, d = 128, T = 131072 bf16 tokens, P = 64,
+r = 24, sink 64, window 128; 2045 factorized pages per KV head.  A step is one
+decode step of the hot path: append the new token's K/V row, promote the page
+leaving the window when one is due (page decomposition), and run mixed decode
+attention for every query head.  Inputs are seeded synthetic pages with the
+sigma_i = i^-1.2 spectrum (synth.py), resident in HBM before timing.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Prints one JSON line.  Other workloads: llama3.1-8b-layer (B = 8, T = 32768,
+r = 16) and compress (batched page decomposition, 524288 pages, r in {8,16,32}).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+CACHE_DIR = os.environ.get("PKV_BENCH_CACHE", "/tmp/pkv_bench_inputs")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cached_inputs(cfg_id, T, workers):
+    import synth
+    os.makedirs(CACHE_DIR, exist_ok=True)
+    path = os.path.join(CACHE_DIR, f"cfg{cfg_id}_T{T}.npz")
+    if os.path.exists(path):
+        z = np.load(path, allow_pickle=False)
+        return dict(K=z["K"], V=z["V"], q=z["q"])
+    t = time.time()
+    d = synth.decode_inputs(cfg_id, T=T, workers=workers)
+    log(f"generated workload {cfg_id} inputs T={T} in {time.time() - t:.1f}s")
+    np.savez(path, K=d["K"], V=d["V"], q=d["q"])
+    return dict(K=d["K"], V=d["V"], q=d["q"])
+
+
+def to_dev(a, dtype):
+    import torch
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a.astype(np.float32)).cuda()
+
+
+def decode_bytes(cfg, B, Hkv, Hq, T, n_fact):
+    """Algorithmic bytes one mixed-attention launch must move: factors of every
+    factorized page (r (P + d) elements per K and per V page), the valid rows
+    of every dense page (K and V), q in, o out (fp32)."""
+    esz = 2 if cfg["dtype"] == "bf16" else 4
+    P, d = cfg["P"], cfg["d"]
+    fact = n_fact * (cfg["r_k"] + cfg["r_v"]) * (P + d) * esz
+    dense = (T - n_fact * P) * d * 2 * esz
+    return B * Hkv * (fact + dense) + B * Hq * d * esz + B * Hq * d * 4
+
+
+def cpu_baseline_decode(cfg, K, V, q, T):
+    """The oracle on a bounded sample: KV head 0 of the same cache.  The
+    oracle reconstructs that head (Jacobi SVD of its factorized pages,
+    truncation, storage rounding; timed -> pages/s), then its naive float64
+    attention for the head's query heads is timed and scaled to the full step
+    (all (sequence, KV head) pairs) -> tokens/s."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    P, s, w = cfg["P"], cfg["s"], cfg["w"]
+    n_pairs = K.shape[0] * K.shape[1]
+    G = q.shape[1] // K.shape[1]
+    k64 = synth.storage_to_f64(K[0, 0, :T], cfg["dtype"])
+    v64 = synth.storage_to_f64(V[0, 0, :T], cfg["dtype"])
+    q64 = synth.storage_to_f64(q[0, :G], cfg["dtype"])
+    n_fact = int((oracle.classify(T, P, s, w)[0] == oracle.FACT).sum())
+    t = time.perf_counter()
+    Khat = oracle.reconstruct_cache(k64, T, P, s, w, cfg["r_k"], cfg["dtype"])[0]
+    Vhat = oracle.reconstruct_cache(v64, T, P, s, w, cfg["r_v"], cfg["dtype"])[0]
+    t_rec = time.perf_counter() - t
+    reps = 3
+    t = time.perf_counter()
+    for _ in range(reps):
+        oracle.attention(q64, Khat, Vhat)
+    t_att = (time.perf_counter() - t) / reps
+    step = t_att * n_pairs
+    return dict(value=K.shape[0] / step, unit="tokens/s", cores=int(max(blas, oracle.num_threads())),
+                kind="oracle",
+                sample=(f"KV head 0 of the same cache: naive float64 attention of its {G} query "
+                        f"heads over T={T} reconstructed tokens took {t_att * 1e3:.1f} ms, scaled "
+                        f"by {n_pairs} (sequence, KV head) pairs per step; the oracle's "
+                        f"reconstruction of that head ({2 * n_fact} Jacobi SVDs) ran at "
+                        f"{2 * n_fact / t_rec:.1f} pages/s"),
+                svd_pages_per_s=2 * n_fact / t_rec)
+
+
+def bench_decode(args, cfg_id, name):
+    import torch
+    import synth
+    import long_context_decode_pkv_amd as pkv
+
+    cfg = dict(synth.CONFIGS[cfg_id])
+    B, Hq, Hkv, T0 = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"]
+    total = T0 + args.warmup + args.steps
+    inp = cached_inputs(cfg_id, total, workers=args.workers)
+    dt = cfg["dtype"]
+    Kd, Vd = to_dev(inp["K"], dt), to_dev(inp["V"], dt)
+    cache = pkv.Cache(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, rank_k=cfg["r_k"], rank_v=cfg["r_v"],
+                      sink=cfg["s"], window=cfg["w"], max_tokens=total, dtype=dt)
+    K0 = Kd[:, :, :T0].contiguous()
+    V0 = Vd[:, :, :T0].contiguous()
+    rows_k = [Kd[:, :, t].contiguous() for t in range(T0, total)]
+    rows_v = [Vd[:, :, t].contiguous() for t in range(T0, total)]
+    qs = [to_dev(synth.step_queries(cfg_id, t, B, Hq, cfg["d"], dt), dt) for t in range(total - T0)]
+    out = torch.empty((B, Hq, cfg["d"]), dtype=torch.float32, device="cuda:0")
+    ws = cache.workspace(0)
+    torch.cuda.synchronize()
+
+    # prefill: dense pools + decomposition of every factorized page
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    cache.prefill(K0, V0)
+    e1.record()
+    torch.cuda.synchronize()
+    t_prefill = e0.elapsed_time(e1) * 1e-3
+    n_fact0 = cache.state()[1]
+    pages0 = B * Hkv * n_fact0 * 2
+    log(f"prefill T={T0}: {pages0} pages decomposed in {t_prefill * 1e3:.2f} ms")
+    del K0, V0
+
+    def step(i, events=None):
+        if cache.append(rows_k[i], rows_v[i]):
+            cache.promote()
+        T, nf, _ = cache.state()
+        if events is not None:
+            events[0].record()
+        cache.decode(qs[i], out=out, workspace=ws)
+        if events is not None:
+            events[1].record()
+        return T, nf
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    states = []
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for j in range(args.steps):
+        states.append(step(args.warmup + j, evs[j]))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t
+    durs = np.array([a.elapsed_time(b) * 1e-3 for a, b in evs])
+    nbytes = np.array([decode_bytes(cfg, B, Hkv, Hq, T, nf) for T, nf in states], dtype=np.float64)
+    achieved = nbytes.sum() / durs.sum() / 1e9
+    log(f"decode launch: mean {durs.mean() * 1e6:.2f} us, median {np.median(durs) * 1e6:.2f} us, "
+        f"{nbytes.mean() / 1e6:.1f} MB -> {achieved:.0f} GB/s")
+
+    # same launches with the 256 MB Infinity Cache flushed before each one
+    flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device="cuda:0")
+    fl = []
+    for j in range(min(args.steps, 16)):
+        flush.fill_(j & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        cache.decode(qs[args.warmup + j], out=out, workspace=ws)
+        b.record()
+        fl.append((a, b))
+    torch.cuda.synchronize()
+    dfl = np.array([a.elapsed_time(b) * 1e-3 for a, b in fl])
+    T_last, nf_last = cache.state()[:2]
+    b_last = decode_bytes(cfg, B, Hkv, Hq, T_last, nf_last)
+    log(f"decode launch after cache flush: mean {dfl.mean() * 1e6:.2f} us -> "
+        f"{b_last / dfl.mean() / 1e9:.0f} GB/s")
+
+    res = {
+        "metric": "decode-attn tokens/s (one layer, batch tokens per second of a full decode step)",
+        "value": B * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 storage, f32 math" if dt == "bf16" else "f32",
+        "data": "synthetic (seeded generator, workload recipe)",
+        "config": {"workload": name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": cfg["d"],
+                   "context_tokens": T0, "page_len": cfg["P"], "rank_k": cfg["r_k"],
+                   "rank_v": cfg["r_v"], "sink": cfg["s"], "window": cfg["w"],
+                   "step": "append + promote when due + mixed decode attention"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode_mfma_kernel (split + fused Eq. 5 merge)",
+                     "launch_us_mean": durs.mean() * 1e6,
+                     "bytes_per_launch": float(nbytes.mean()),
+                     "flushed_launch_us_mean": dfl.mean() * 1e6,
+                     "flushed_achieved": b_last / dfl.mean() / 1e9},
+        "decode_effective_GBps": achieved,
+        "pages_compressed_per_s": pages0 / t_prefill,
+        "prefill_ms": t_prefill * 1e3,
+    }
+    if args.cpu_baseline:
+        log("timing the oracle on a bounded sample (cpu_baseline)")
+        cb = cpu_baseline_decode(cfg, inp["K"], inp["V"], inp["q"], T0)
+        res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        res["cpu_baseline_svd_pages_per_s"] = cb["svd_pages_per_s"]
+    return res
+
+
+def bench_compress(args):
+    """Batched prefill compression (workload 5): 524288 pages per rank setting."""
+    import torch
+    import synth
+    import long_context_decode_pkv_amd as pkv
+
+    cfg = synth.CONFIGS[5]
+    n_total = cfg["layers"] * cfg["Hkv"] * 2 * cfg["pages_per_head"]
+    n_distinct = args.distinct_pages
+    path = os.path.join(CACHE_DIR, f"cfg5_pool{n_distinct}.npy")
+    os.makedirs(CACHE_DIR, exist_ok=True)
+    if os.path.exists(path):
+        pool = np.load(path, allow_pickle=False)
+    else:
+        t = time.time()
+        pool = synth.to_storage(synth.compression_pages(np.arange(n_distinct), n_total), "bf16")
+        np.save(path, pool)
+        log(f"generated {n_distinct} distinct pages in {time.time() - t:.1f}s")
+    Xp = to_dev(pool, "bf16")
+    X = Xp.repeat((n_total + n_distinct - 1) // n_distinct, 1, 1)[:n_total].contiguous()
+    del Xp
+    results = {}
+    for r in cfg["ranks"]:
+        Lf = torch.empty((n_total, 64, r), dtype=torch.bfloat16, device="cuda:0")
+        Rf = torch.empty((n_total, r, 128), dtype=torch.bfloat16, device="cuda:0")
+        for _ in range(args.warmup):
+            pkv.lib().pkv_compress_pages(X.data_ptr(), n_total // 64, 64, 128, r, 0, 0,
+                                         Lf.data_ptr(), Rf.data_ptr(), None,
+                                         torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            st = pkv.lib().pkv_compress_pages(X.data_ptr(), n_total, 64, 128, r, 0, 0, Lf.data_ptr(),
+                                              Rf.data_ptr(), None,
+                                              torch.cuda.current_stream().cuda_stream)
+            assert st == 0
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) * 1e-3 / args.steps
+        results[r] = n_total / t
+        log(f"compress r={r}: {t * 1e3:.1f} ms per {n_total} pages -> {n_total / t:.3e} pages/s")
+    r0 = cfg["ranks"][1]
+    return {
+        "metric": "pages compressed/s (batched page decomposition)",
+        "value": results[r0], "unit": "pages/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": n_total / results[r0] * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in/out, f32 eigen-solve",
+        "data": f"synthetic: {n_distinct} distinct seeded pages tiled to {n_total}",
+        "config": {"workload": "batched-prefill-compression", "pages": n_total, "rank": r0,
+                   "pages_per_s_by_rank": results},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="qwen3-32b-layer-128k",
+                    choices=["qwen3-32b-layer-128k", "llama3.1-8b-layer", "compress"])
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--workers", type=int, default=1)
+    ap.add_argument("--distinct-pages", type=int, default=8192)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    import long_context_decode_pkv_amd as pkv
+    if not os.path.exists(pkv.LIB_PATH):
+        from long_context_decode_pkv_amd import build
+        build.build()
+    pkv.lib()
+    if args.workload == "compress":
+        res = bench_compress(args)
+    elif args.workload == "llama3.1-8b-layer":
+        res = bench_decode(args, 2, args.workload)
+    else:
+        res = bench_decode(args, 3, args.workload)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,236 @@
+/*
+ * pkv.h -- C-ABI of the MI355X (gfx950) PuzzleKV hot path.
+ *
+ * Method: "PuzzleKV: Page-Wise Low-Rank Decomposition for KV Cache
+ * Compression" (arXiv 2608.23843).  Each completed P-token page of one layer's
+ * KV head is stored as rank-r factors (Sec. 3.3, Eq. 2) obtained from the
+ * page's P x P Gram matrix (Sec. 3.3, text after Eq. 3); a sink region and a
+ * recent window stay dense (Sec. 3.3, steps (1)-(3)); decode attention runs
+ * directly on dense and factorized pages with an online-softmax merge
+ * (Sec. 3.3 (4), Eq. 4 and Eq. 5); new pages are factorized once as they
+ * leave the window (Sec. 3.3 "Incremental Cache Update (5)").
+ *
+ * Conventions for every call
+ *  - Return value: a pkv_status (0 = PKV_OK).  No call throws; when a call
+ *    returns an error it has changed no state and enqueued no work.
+ *  - Pointers named "device" point to GPU memory the caller owns (for example
+ *    torch tensors).  The library never allocates or frees device memory and
+ *    never synchronizes a stream, except pkv_read_page_table, which must
+ *    return host data.  Host handles (pkv_cache) are allocated by
+ *    pkv_cache_create and freed by pkv_cache_destroy.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    device work of a call is enqueued on it in order.
+ *  - Calls on one cache must be serialized by the caller (they update the
+ *    cache's host-side state); distinct caches are independent.
+ *  - dtype: PKV_BF16 (bfloat16 storage, float32 arithmetic) or PKV_F32.
+ *    K, V, q and the stored factors share the cache's dtype; attention output
+ *    is float32.
+ *  - Fixed in this version: head_dim d = 128 and page length P = 64 (other
+ *    values return PKV_ERR_UNSUPPORTED); GQA group size G = H_q / H_kv <= 8.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,       /* bad size, null or misaligned pointer, bad combination */
+  PKV_ERR_UNSUPPORTED = 2,       /* valid for the method, not implemented (d != 128, P != 64, G > 8) */
+  PKV_ERR_CAPACITY = 3,          /* more tokens than max_tokens, workspace too small */
+  PKV_ERR_NOT_ELIGIBLE = 4,      /* promotion requested with no page waiting */
+  PKV_ERR_PROMOTION_PENDING = 5, /* append refused: a completed page must be promoted first */
+  PKV_ERR_DEVICE = 6             /* a HIP runtime call or kernel launch failed */
+} pkv_status;
+
+typedef enum pkv_dtype { PKV_BF16 = 0, PKV_F32 = 1 } pkv_dtype;
+
+/* Page classes reported by the page table (Sec. 3.3 (1)-(3), Sec. 4.1). */
+typedef enum pkv_page_class {
+  PKV_PAGE_UNUSED = 0, /* beyond the current length */
+  PKV_PAGE_SINK = 1,   /* one of the first s/P pages; dense */
+  PKV_PAGE_FACT = 2,   /* completed page stored as factors */
+  PKV_PAGE_WIN = 3,    /* completed page in the dense recent window */
+  PKV_PAGE_PART = 4    /* page still being filled; dense */
+} pkv_page_class;
+
+/* Factor part selector for pkv_pack_factors / pkv_unpack_factors. */
+typedef enum pkv_factor_kind { PKV_KEYS = 0, PKV_VALUES = 1 } pkv_factor_kind;
+
+/* Shape and parameters of one layer's hybrid cache (passed by pointer). */
+typedef struct pkv_shape {
+  int32_t batch;      /* B sequences; all have the same length T */
+  int32_t n_q_heads;  /* H_q */
+  int32_t n_kv_heads; /* H_kv, H_q % H_kv == 0; query head h reads KV head h / G */
+  int32_t head_dim;   /* d (must be 128) */
+  int32_t page_len;   /* P (must be 64) */
+  int32_t rank_k;     /* r_K, 1 <= r_K <= min(P, d) */
+  int32_t rank_v;     /* r_V, 1 <= r_V <= min(P, d) */
+  int32_t sink;       /* s: dense sink tokens, a multiple of P (may be 0) */
+  int32_t window;     /* w: dense window tokens (completed pages), a multiple of P */
+  int32_t max_tokens; /* capacity T_max >= 1 */
+  int32_t dtype;      /* pkv_dtype */
+} pkv_shape;
+
+/*
+ * Device-buffer layout of a cache (byte offsets from the caller's buffer,
+ * every region 256-byte aligned).  With n_s = s/P, n_w = w/P:
+ *   sink_k  [B][H_kv][n_s][P][d]        keys, row-major
+ *   sink_v  [B][H_kv][n_s][d][P]        values, transposed per page
+ *   win_k   [B][H_kv][n_w+1][P][d]      ring of window/partial key pages
+ *   win_v   [B][H_kv][n_w+1][d][P]      ring of value pages, transposed
+ *   factors [B][H_kv][F_max][factor_page_bytes]   K part, then V part
+ *   page_table [max_pages] int32: (class << 24) | slot
+ * The factor parts use a fixed interleaved order matched to the attention
+ * kernel's matrix-core register layout; pkv_pack_factors and
+ * pkv_unpack_factors convert between it and row-major Lf (P x r), Rf (r x d).
+ * Ranks are padded to a multiple of 8 inside a part (padding is zero).
+ */
+typedef struct pkv_layout {
+  uint64_t sink_k, sink_v, win_k, win_v, factors, page_table;
+  uint64_t total_bytes;
+  int64_t n_sink_slots;      /* n_s */
+  int64_t n_ring_slots;      /* n_w + 1 */
+  int64_t max_fact_pages;    /* F_max = max(0, floor(T_max/P) - n_s - n_w) */
+  int64_t max_pages;         /* ceil(T_max / P) */
+  int64_t elem_bytes;        /* 2 (bf16) or 4 (f32) */
+  int64_t dense_page_bytes;  /* P * d * elem_bytes */
+  int64_t factor_k_elems;    /* packed elements of a K part: r8_K (P + d) */
+  int64_t factor_v_elems;    /* r8_V (P + d) */
+  int64_t factor_page_bytes; /* (factor_k_elems + factor_v_elems) * elem_bytes */
+} pkv_layout;
+
+typedef struct pkv_cache pkv_cache; /* opaque host handle */
+
+/* Human-readable name of a status code (static string). */
+const char* pkv_status_string(int32_t status);
+const char* pkv_version(void);
+
+/* Eq. 3 (also App. D.1 Eq. 6): storage of a factorized K/V page pair over
+ * its dense storage, (r_K + r_V)(P + d) / (2 P d).  Host only. */
+double pkv_storage_ratio(int32_t P, int32_t r_k, int32_t r_v, int32_t d);
+
+/*
+ * Page classification of a T-token cache (Sec. 3.3 (1)-(3) and (5); Sec. 4.1
+ * default dense region).  Host only, no GPU needed.
+ *   n_fact < 0: steady state -- every completed non-sink page except the n_w
+ *               most recent is FACT;
+ *   n_fact >= 0: exactly the first n_fact such pages are FACT (the state
+ *               between a page-completing append and its promotion).
+ * Writes cls[p] (pkv_page_class) and slot[p] for p < n_pages; pages beyond
+ * ceil(T/P) get UNUSED / 0.  Slots: SINK p; FACT p - n_s; WIN and PART
+ * (p - n_s) mod (n_w + 1).  Errors: INVALID_ARG if s or w is not a multiple
+ * of P, T < 0, or a pointer is null.
+ */
+int32_t pkv_classify(int64_t T, int32_t P, int32_t s, int32_t w, int64_t n_fact, int32_t* cls,
+                     int32_t* slot, int64_t n_pages);
+
+/* Packed elements of one factor part for rank r (= r8 (P + d), r8 = r
+ * rounded up to a multiple of 8).  Host only. */
+int32_t pkv_factor_part_elems(int32_t P, int32_t d, int32_t r, int64_t* elems);
+
+/*
+ * Host-side conversion between row-major factors (float32 Lf [P][r] with
+ * Lf = U_r Sigma_r, Rf [r][d] with Rf = W_r^T; Sec. 3.2 "Truncated SVD",
+ * Sec. 3.3 Eq. 2) and one packed factor part.  `dtype` is the part's element
+ * type (PKV_BF16 rounds nearest-even).  `packed` is host memory of
+ * pkv_factor_part_elems elements.  Host only.
+ */
+int32_t pkv_pack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t dtype,
+                         const float* Lf, const float* Rf, void* packed);
+int32_t pkv_unpack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t dtype,
+                           const void* packed, float* Lf, float* Rf);
+
+/* Bytes and layout of the device buffer a cache of this shape needs. */
+int32_t pkv_cache_layout(const pkv_shape* shape, pkv_layout* out);
+
+/* Create a cache over a caller-owned device buffer of at least
+ * pkv_cache_layout().total_bytes bytes, 256-byte aligned.  The buffer's
+ * contents are set by pkv_prefill.  Host only (no GPU work). */
+int32_t pkv_cache_create(const pkv_shape* shape, void* device_buffer, uint64_t device_bytes,
+                         pkv_cache** out);
+void pkv_cache_destroy(pkv_cache* cache);
+
+/* Host-side state: current length T, FACT pages stored, and whether a
+ * completed page waits for pkv_promote_page. */
+int32_t pkv_cache_state(const pkv_cache* cache, int64_t* T, int64_t* n_fact, int32_t* pending);
+
+/*
+ * Batched page decomposition (Sec. 3.3, text after Eq. 3): for each of
+ * n_pages pages X (P x d, row-major, contiguous, `in_dtype`) form the Gram
+ * matrix G = X X^T in float32, take its top-r eigenvectors Q (float32 Jacobi
+ * eigen-solve, one page per wavefront), and write
+ *   Lf = Q diag(sigma)  (P x r),   Rf = diag(1/sigma) Q^T X  (r x d),
+ *   sigma_i = || (Q^T X)_i ||,
+ * so Lf Rf is the rank-r truncated SVD of X (Sec. 3.2; Eckart-Young-Mirsky).
+ * Outputs (device, row-major, `out_dtype`): Lf [n_pages][P][r],
+ * Rf [n_pages][r][d]; sigma [n_pages][r] float32 (may be NULL).  Rows with
+ * sigma = 0 are zero.  Errors: INVALID_ARG (null/misaligned pointers, bad r),
+ * UNSUPPORTED (P != 64 or d != 128), DEVICE (launch failure).
+ */
+int32_t pkv_compress_pages(const void* X, int64_t n_pages, int32_t P, int32_t d, int32_t r,
+                           int32_t in_dtype, int32_t out_dtype, void* Lf, void* Rf, float* sigma,
+                           void* stream);
+
+/*
+ * Prefill (Sec. 3.3 (1)-(3)): from dense K, V (device, [B][H_kv][T][d], cache
+ * dtype) build the hybrid cache: copy sink, window and partial pages into the
+ * dense pools, factorize every FACT page of every (sequence, KV head, K/V)
+ * with the kernel of pkv_compress_pages into the factor pool, and fill the
+ * page table.  Resets the cache to length T (1 <= T <= max_tokens).
+ */
+int32_t pkv_prefill(pkv_cache* cache, const void* K, const void* V, int64_t T, void* stream);
+
+/*
+ * Append one token (Sec. 3.3 "Incremental Cache Update (5)"): k_new, v_new
+ * (device, [B][H_kv][d], cache dtype) go to row T mod P of page T / P, which
+ * joins attention at once; T += 1.  If this append completes a page and the
+ * oldest window page must leave the window, *promotion_pending (may be NULL)
+ * is set to 1 and pkv_promote_page must run before the next append.
+ * Errors: CAPACITY (T == max_tokens), PROMOTION_PENDING.
+ */
+int32_t pkv_append(pkv_cache* cache, const void* k_new, const void* v_new,
+                   int32_t* promotion_pending, void* stream);
+
+/* Factorize the page that left the window (once; factors go to the next
+ * factor slot, its ring slot is released) and mark it FACT.  At most one page
+ * per call (Sec. 3.3 (5)).  Errors: NOT_ELIGIBLE when nothing is waiting. */
+int32_t pkv_promote_page(pkv_cache* cache, void* stream);
+
+/* Workspace bytes pkv_decode_attn needs for n_split splits per (sequence,
+ * KV head); n_split = 0 selects the library's choice. */
+int32_t pkv_decode_workspace_bytes(const pkv_cache* cache, int32_t n_split, uint64_t* bytes);
+
+/*
+ * Mixed decode attention (Sec. 3.3 (4), Eq. 4 and Eq. 5): for every query
+ * head, softmax(q K^T / sqrt(d)) V over all T cached tokens, where factorized
+ * pages are evaluated through their factors (scores (q Rf_K^T) Lf_K^T, output
+ * (e^(s-m) Lf_V) Rf_V) without reconstructing them, dense pages directly, and
+ * page-wise partial states are merged by online softmax within and across
+ * splits (the last workgroup of each (sequence, KV head) merges the splits).
+ * q: device [B][H_q][d] (cache dtype); out: device float32 [B][H_q][d];
+ * workspace: device, >= pkv_decode_workspace_bytes bytes, 256-byte aligned,
+ * zero-filled before its first use (it ends every call with its arrival
+ * counters back at zero, so it can be reused without clearing; calls that
+ * share one workspace must not overlap).
+ * Errors: INVALID_ARG (T == 0, null or misaligned pointers), CAPACITY
+ * (workspace too small).
+ */
+int32_t pkv_decode_attn(const pkv_cache* cache, const void* q, float* out, void* workspace,
+                        uint64_t workspace_bytes, int32_t n_split, void* stream);
+
+/* Copy the page table to host: cls[p], slot[p] for p < n (n <= max_pages).
+ * Synchronizes `stream`. */
+int32_t pkv_read_page_table(const pkv_cache* cache, int32_t* cls, int32_t* slot, int64_t n,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,304 @@
+"""PuzzleKV page-wise low-rank KV cache for MI355X (gfx950).
+
+Thin Python binding of ``libpkv.so`` (C-ABI in ``include/pkv.h``): argument
+marshalling only.  Every step of the hot path -- page decomposition, dense
+pool maintenance, append / promotion and mixed decode attention -- runs in the
+library's HIP kernels; torch provides device memory and streams.  There is no
+fallback: if the library is not built, every call raises.
+
+Method: "PuzzleKV: Page-Wise Low-Rank Decomposition for KV Cache Compression"
+(Sec. 3.3 steps (1)-(5), Eq. 2-5).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PKV_OK = 0
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "capacity exceeded",
+          4: "no page waiting for promotion", 5: "promotion pending", 6: "device error"}
+BF16, F32 = 0, 1
+KEYS, VALUES = 0, 1
+UNUSED, SINK, FACT, WIN, PART = 0, 1, 2, 3, 4
+PAGE_LEN, HEAD_DIM = 64, 128
+
+
+class PKVError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "n_q_heads", "n_kv_heads", "head_dim", "page_len", "rank_k", "rank_v", "sink",
+        "window", "max_tokens", "dtype")]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in (
+        "sink_k", "sink_v", "win_k", "win_v", "factors", "page_table", "total_bytes")] + \
+        [(n, ctypes.c_int64) for n in (
+            "n_sink_slots", "n_ring_slots", "max_fact_pages", "max_pages", "elem_bytes",
+            "dense_page_bytes", "factor_k_elems", "factor_v_elems", "factor_page_bytes")]
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded libpkv.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m long_context_decode_pkv_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+    P = ctypes.POINTER
+    sig = {
+        "pkv_status_string": ([i32], ctypes.c_char_p),
+        "pkv_version": ([], ctypes.c_char_p),
+        "pkv_storage_ratio": ([i32, i32, i32, i32], ctypes.c_double),
+        "pkv_classify": ([i64, i32, i32, i32, i64, vp, vp, i64], i32),
+        "pkv_factor_part_elems": ([i32, i32, i32, P(i64)], i32),
+        "pkv_pack_factors": ([i32, i32, i32, i32, i32, vp, vp, vp], i32),
+        "pkv_unpack_factors": ([i32, i32, i32, i32, i32, vp, vp, vp], i32),
+        "pkv_cache_layout": ([P(Shape), P(Layout)], i32),
+        "pkv_cache_create": ([P(Shape), vp, u64, P(vp)], i32),
+        "pkv_cache_destroy": ([vp], None),
+        "pkv_cache_state": ([vp, P(i64), P(i64), P(i32)], i32),
+        "pkv_compress_pages": ([vp, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp], i32),
+        "pkv_prefill": ([vp, vp, vp, i64, vp], i32),
+        "pkv_append": ([vp, vp, vp, P(i32), vp], i32),
+        "pkv_promote_page": ([vp, vp], i32),
+        "pkv_decode_workspace_bytes": ([vp, i32, P(u64)], i32),
+        "pkv_decode_attn": ([vp, vp, vp, vp, u64, i32, vp], i32),
+        "pkv_read_page_table": ([vp, vp, vp, i64, vp], i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _LIB = L
+    return L
+
+
+def _check(status: int, what: str):
+    if status != PKV_OK:
+        raise PKVError(status, what)
+
+
+def _np_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stream(device=None):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t == torch.bfloat16:
+        return BF16
+    if t == torch.float32:
+        return F32
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def _dev_ptr(t, dtype_code=None, what="tensor"):
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype_code is not None and _dtype_code(t.dtype) != dtype_code:
+        raise ValueError(f"{what} has dtype {t.dtype}, cache dtype differs")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ------------------------------------------------------------------ host-only
+
+def version() -> str:
+    return lib().pkv_version().decode()
+
+
+def storage_ratio(P: int, r_k: int, r_v: int, d: int) -> float:
+    """Eq. 3: (r_K + r_V)(P + d) / (2 P d)."""
+    return float(lib().pkv_storage_ratio(P, r_k, r_v, d))
+
+
+def classify(T: int, P: int, s: int, w: int, n_fact: int = -1, n_pages: int | None = None):
+    """(cls, slot) int32 arrays of the logical pages of a T-token cache."""
+    if n_pages is None:
+        n_pages = -(-T // P) if P > 0 else 0
+    cls = np.zeros(n_pages, dtype=np.int32)
+    slot = np.zeros(n_pages, dtype=np.int32)
+    _check(lib().pkv_classify(T, P, s, w, n_fact, _np_ptr(cls), _np_ptr(slot), n_pages),
+           "pkv_classify")
+    return cls, slot
+
+
+def factor_part_elems(r: int, P: int = PAGE_LEN, d: int = HEAD_DIM) -> int:
+    n = ctypes.c_int64()
+    _check(lib().pkv_factor_part_elems(P, d, r, ctypes.byref(n)), "pkv_factor_part_elems")
+    return n.value
+
+
+def pack_factors(kind: int, r: int, dtype: int, Lf, Rf) -> np.ndarray:
+    """Row-major float32 Lf (P x r), Rf (r x d) -> one packed factor part
+    (uint16 bf16 bits or float32)."""
+    Lf = np.ascontiguousarray(Lf, dtype=np.float32)
+    Rf = np.ascontiguousarray(Rf, dtype=np.float32)
+    n = factor_part_elems(r)
+    out = np.zeros(n, dtype=np.uint16 if dtype == BF16 else np.float32)
+    _check(lib().pkv_pack_factors(kind, PAGE_LEN, HEAD_DIM, r, dtype, _np_ptr(Lf), _np_ptr(Rf),
+                                  _np_ptr(out)), "pkv_pack_factors")
+    return out
+
+
+def unpack_factors(kind: int, r: int, dtype: int, packed):
+    """One packed factor part -> float32 Lf (P x r), Rf (r x d)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint16 if dtype == BF16 else np.float32)
+    Lf = np.zeros((PAGE_LEN, r), dtype=np.float32)
+    Rf = np.zeros((r, HEAD_DIM), dtype=np.float32)
+    _check(lib().pkv_unpack_factors(kind, PAGE_LEN, HEAD_DIM, r, dtype, _np_ptr(packed),
+                                    _np_ptr(Lf), _np_ptr(Rf)), "pkv_unpack_factors")
+    return Lf, Rf
+
+
+def make_shape(batch, n_q_heads, n_kv_heads, rank_k, rank_v, sink, window, max_tokens, dtype,
+               head_dim=HEAD_DIM, page_len=PAGE_LEN) -> Shape:
+    return Shape(batch, n_q_heads, n_kv_heads, head_dim, page_len, rank_k, rank_v, sink, window,
+                 max_tokens, dtype)
+
+
+def cache_layout(shape: Shape) -> dict:
+    lay = Layout()
+    _check(lib().pkv_cache_layout(ctypes.byref(shape), ctypes.byref(lay)), "pkv_cache_layout")
+    return {name: getattr(lay, name) for name, _ in Layout._fields_}
+
+
+# ------------------------------------------------------------------ device
+
+def compress_pages(X, r: int, out_dtype=None, with_sigma: bool = True):
+    """Batched page decomposition: X (n, 64, 128) bf16 / f32 device tensor ->
+    Lf (n, 64, r), Rf (n, r, 128) in out_dtype (default X's), sigma (n, r) f32."""
+    import torch
+    if X.dim() != 3 or X.shape[1:] != (PAGE_LEN, HEAD_DIM):
+        raise ValueError("X must be (n_pages, 64, 128)")
+    out_dtype = X.dtype if out_dtype is None else out_dtype
+    n = X.shape[0]
+    Lf = torch.empty((n, PAGE_LEN, r), dtype=out_dtype, device=X.device)
+    Rf = torch.empty((n, r, HEAD_DIM), dtype=out_dtype, device=X.device)
+    sg = torch.empty((n, r), dtype=torch.float32, device=X.device) if with_sigma else None
+    _check(lib().pkv_compress_pages(_dev_ptr(X, what="X"), n, PAGE_LEN, HEAD_DIM, r,
+                                    _dtype_code(X.dtype), _dtype_code(out_dtype),
+                                    ctypes.c_void_p(Lf.data_ptr()), ctypes.c_void_p(Rf.data_ptr()),
+                                    ctypes.c_void_p(sg.data_ptr()) if sg is not None else None,
+                                    _stream(X.device)), "pkv_compress_pages")
+    return Lf, Rf, sg
+
+
+class Cache:
+    """One layer's hybrid PuzzleKV cache over a torch-owned device buffer."""
+
+    def __init__(self, batch, n_q_heads, n_kv_heads, rank_k, rank_v, sink, window, max_tokens,
+                 dtype="bf16", device="cuda:0"):
+        import torch
+        self.device = torch.device(device)
+        self.dtype_code = BF16 if dtype in ("bf16", torch.bfloat16) else F32
+        self.torch_dtype = torch.bfloat16 if self.dtype_code == BF16 else torch.float32
+        self.shape = make_shape(batch, n_q_heads, n_kv_heads, rank_k, rank_v, sink, window,
+                                max_tokens, self.dtype_code)
+        self.layout = cache_layout(self.shape)
+        self.buffer = torch.empty(self.layout["total_bytes"], dtype=torch.uint8, device=self.device)
+        h = ctypes.c_void_p()
+        _check(lib().pkv_cache_create(ctypes.byref(self.shape), ctypes.c_void_p(self.buffer.data_ptr()),
+                                      self.layout["total_bytes"], ctypes.byref(h)), "pkv_cache_create")
+        self._h = h
+        self._ws = None
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _LIB is not None:
+            _LIB.pkv_cache_destroy(h)
+            self._h = None
+
+    # -- state
+    def state(self):
+        T, nf, pend = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+        _check(lib().pkv_cache_state(self._h, ctypes.byref(T), ctypes.byref(nf), ctypes.byref(pend)),
+               "pkv_cache_state")
+        return T.value, nf.value, bool(pend.value)
+
+    @property
+    def T(self):
+        return self.state()[0]
+
+    # -- hot path
+    def prefill(self, K, V):
+        T = K.shape[2]
+        _check(lib().pkv_prefill(self._h, _dev_ptr(K, self.dtype_code, "K"),
+                                 _dev_ptr(V, self.dtype_code, "V"), T, _stream(self.device)),
+               "pkv_prefill")
+
+    def append(self, k, v) -> bool:
+        pend = ctypes.c_int32()
+        _check(lib().pkv_append(self._h, _dev_ptr(k, self.dtype_code, "k"),
+                                _dev_ptr(v, self.dtype_code, "v"), ctypes.byref(pend),
+                                _stream(self.device)), "pkv_append")
+        return bool(pend.value)
+
+    def promote(self):
+        _check(lib().pkv_promote_page(self._h, _stream(self.device)), "pkv_promote_page")
+
+    def workspace_bytes(self, n_split: int = 0) -> int:
+        n = ctypes.c_uint64()
+        _check(lib().pkv_decode_workspace_bytes(self._h, n_split, ctypes.byref(n)),
+               "pkv_decode_workspace_bytes")
+        return n.value
+
+    def workspace(self, n_split: int = 0):
+        import torch
+        need = self.workspace_bytes(n_split)
+        if self._ws is None or self._ws.numel() < need:
+            # zero-filled once; the library leaves its counters at zero
+            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def decode(self, q, out=None, n_split: int = 0, workspace=None):
+        import torch
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+        ws = self.workspace(n_split) if workspace is None else workspace
+        _check(lib().pkv_decode_attn(self._h, _dev_ptr(q, self.dtype_code, "q"),
+                                     _dev_ptr(out, None, "out"), ctypes.c_void_p(ws.data_ptr()),
+                                     ws.numel(), n_split, _stream(self.device)), "pkv_decode_attn")
+        return out
+
+    # -- inspection
+    def page_table(self, n: int | None = None):
+        if n is None:
+            n = self.layout["max_pages"]
+        cls = np.zeros(n, dtype=np.int32)
+        slot = np.zeros(n, dtype=np.int32)
+        _check(lib().pkv_read_page_table(self._h, _np_ptr(cls), _np_ptr(slot), n,
+                                         _stream(self.device)), "pkv_read_page_table")
+        return cls, slot
+
+    def factor_part(self, b: int, h: int, slot: int, kind: int):
+        """Device view (uint8) of one packed factor part of the pool."""
+        L = self.layout
+        base = L["factors"] + ((b * self.shape.n_kv_heads + h) * L["max_fact_pages"] + slot) * \
+            L["factor_page_bytes"]
+        kbytes = L["factor_k_elems"] * L["elem_bytes"]
+        if kind == KEYS:
+            return self.buffer[base: base + kbytes]
+        return self.buffer[base + kbytes: base + L["factor_page_bytes"]]

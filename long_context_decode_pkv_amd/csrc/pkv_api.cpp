@@ -1,0 +1,463 @@
+// C-ABI entry points of libpkv (declared in include/pkv.h).
+//
+// Host side of the hybrid cache: argument validation, device-buffer layout,
+// the length / promotion state machine of PuzzleKV's incremental update
+// (Sec. 3.3 "Incremental Cache Update (5)"), and kernel dispatch.  No entry
+// point allocates device memory; none throws.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+using namespace pkv;
+
+struct pkv_cache {
+  pkv_shape shape;
+  pkv_layout lay;
+  uint8_t* base;
+  int64_t T;
+  int64_t n_fact;
+  int32_t pending;  // a completed page waits for promotion
+};
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int32_t check_shape(const pkv_shape* s) {
+  if (!s) return PKV_ERR_INVALID_ARG;
+  if (s->batch < 1 || s->n_kv_heads < 1 || s->n_q_heads < 1) return PKV_ERR_INVALID_ARG;
+  if (s->n_q_heads % s->n_kv_heads) return PKV_ERR_INVALID_ARG;
+  if (s->dtype != PKV_BF16 && s->dtype != PKV_F32) return PKV_ERR_INVALID_ARG;
+  if (s->page_len < 1 || s->head_dim < 1) return PKV_ERR_INVALID_ARG;
+  if (s->sink < 0 || s->window < 0 || s->sink % s->page_len || s->window % s->page_len)
+    return PKV_ERR_INVALID_ARG;
+  const int rmax = s->page_len < s->head_dim ? s->page_len : s->head_dim;
+  if (s->rank_k < 1 || s->rank_v < 1 || s->rank_k > rmax || s->rank_v > rmax)
+    return PKV_ERR_INVALID_ARG;
+  if (s->max_tokens < 1) return PKV_ERR_INVALID_ARG;
+  if (s->head_dim != kD || s->page_len != kP) return PKV_ERR_UNSUPPORTED;
+  if (s->n_q_heads / s->n_kv_heads > kMaxG) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+void make_layout(const pkv_shape* s, pkv_layout* L) {
+  std::memset(L, 0, sizeof(*L));
+  const int64_t P = s->page_len, d = s->head_dim, B = s->batch, H = s->n_kv_heads;
+  const int64_t n_s = s->sink / P, n_w = s->window / P;
+  L->elem_bytes = s->dtype == PKV_BF16 ? 2 : 4;
+  L->n_sink_slots = n_s;
+  L->n_ring_slots = n_w + 1;
+  L->max_pages = (s->max_tokens + P - 1) / P;
+  const int64_t fmax = s->max_tokens / P - n_s - n_w;
+  L->max_fact_pages = fmax > 0 ? fmax : 0;
+  L->dense_page_bytes = P * d * L->elem_bytes;
+  L->factor_k_elems = part_elems(s->rank_k);
+  L->factor_v_elems = part_elems(s->rank_v);
+  L->factor_page_bytes = (L->factor_k_elems + L->factor_v_elems) * L->elem_bytes;
+  uint64_t off = 0;
+  const uint64_t sink_bytes = (uint64_t)B * H * n_s * L->dense_page_bytes;
+  const uint64_t ring_bytes = (uint64_t)B * H * (n_w + 1) * L->dense_page_bytes;
+  L->sink_k = off;
+  off = align_up(off + sink_bytes);
+  L->sink_v = off;
+  off = align_up(off + sink_bytes);
+  L->win_k = off;
+  off = align_up(off + ring_bytes);
+  L->win_v = off;
+  off = align_up(off + ring_bytes);
+  L->factors = off;
+  off = align_up(off + (uint64_t)B * H * L->max_fact_pages * L->factor_page_bytes);
+  L->page_table = off;
+  off = align_up(off + (uint64_t)L->max_pages * 4);
+  L->total_bytes = off;
+}
+
+CacheGeom geom_of(const pkv_cache* c) {
+  CacheGeom g;
+  g.B = c->shape.batch;
+  g.Hkv = c->shape.n_kv_heads;
+  g.Hq = c->shape.n_q_heads;
+  g.G = g.Hq / g.Hkv;
+  g.n_s = c->shape.sink / c->shape.page_len;
+  g.n_w = c->shape.window / c->shape.page_len;
+  g.F_max = c->lay.max_fact_pages;
+  g.max_pages = c->lay.max_pages;
+  g.dtype = c->shape.dtype;
+  g.r_k = c->shape.rank_k;
+  g.r_v = c->shape.rank_v;
+  g.base = c->base;
+  g.lay = c->lay;
+  return g;
+}
+
+int32_t dev_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_DEVICE; }
+
+// Steady-state number of factorized pages at length T.
+int64_t steady_fact(int64_t T, int64_t P, int64_t n_s, int64_t n_w) {
+  const int64_t f = T / P - n_s - n_w;
+  return f > 0 ? f : 0;
+}
+
+float bf16_round_host(float x, uint16_t* bits) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  uint16_t b;
+  if ((u & 0x7fffffffu) > 0x7f800000u) {
+    b = (uint16_t)((u >> 16) | 0x40u);
+  } else {
+    u += 0x7fffu + ((u >> 16) & 1u);
+    b = (uint16_t)(u >> 16);
+  }
+  *bits = b;
+  uint32_t w = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &w, 4);
+  return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int32_t status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape";
+    case PKV_ERR_CAPACITY: return "capacity exceeded";
+    case PKV_ERR_NOT_ELIGIBLE: return "no page waiting for promotion";
+    case PKV_ERR_PROMOTION_PENDING: return "promotion pending";
+    case PKV_ERR_DEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
+
+double pkv_storage_ratio(int32_t P, int32_t r_k, int32_t r_v, int32_t d) {
+  if (P <= 0 || d <= 0) return NAN;
+  return (double)(r_k + r_v) * (double)(P + d) / (2.0 * P * d);
+}
+
+int32_t pkv_classify(int64_t T, int32_t P, int32_t s, int32_t w, int64_t n_fact, int32_t* cls,
+                     int32_t* slot, int64_t n_pages) {
+  if (P < 1 || s < 0 || w < 0 || s % P || w % P || T < 0 || n_pages < 0) return PKV_ERR_INVALID_ARG;
+  if (n_pages > 0 && (!cls || !slot)) return PKV_ERR_INVALID_ARG;
+  const int64_t n_s = s / P, n_w = w / P;
+  const int64_t n_full = T / P, used = (T + P - 1) / P;
+  const int64_t nf = n_fact < 0 ? steady_fact(T, P, n_s, n_w) : n_fact;
+  if (nf > (n_full - n_s > 0 ? n_full - n_s : 0)) return PKV_ERR_INVALID_ARG;
+  for (int64_t p = 0; p < n_pages; ++p) {
+    int32_t c, sl = 0;
+    if (p >= used) {
+      c = PKV_PAGE_UNUSED;
+    } else if (p < n_s) {
+      c = PKV_PAGE_SINK;
+      sl = (int32_t)p;
+    } else if (p < n_s + nf) {
+      c = PKV_PAGE_FACT;
+      sl = (int32_t)(p - n_s);
+    } else {
+      c = p < n_full ? PKV_PAGE_WIN : PKV_PAGE_PART;
+      sl = (int32_t)((p - n_s) % (n_w + 1));
+    }
+    cls[p] = c;
+    slot[p] = sl;
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_factor_part_elems(int32_t P, int32_t d, int32_t r, int64_t* elems) {
+  if (!elems) return PKV_ERR_INVALID_ARG;
+  if (P != kP || d != kD) return PKV_ERR_UNSUPPORTED;
+  if (r < 1 || r > kP) return PKV_ERR_INVALID_ARG;
+  *elems = part_elems(r);
+  return PKV_OK;
+}
+
+int32_t pkv_pack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t dtype,
+                         const float* Lf, const float* Rf, void* packed) {
+  int64_t n;
+  int32_t st = pkv_factor_part_elems(P, d, r, &n);
+  if (st != PKV_OK) return st;
+  if ((kind != PKV_KEYS && kind != PKV_VALUES) || (dtype != PKV_BF16 && dtype != PKV_F32) || !Lf ||
+      !Rf || !packed)
+    return PKV_ERR_INVALID_ARG;
+  const PackDims pd = pack_dims(r);
+  const int r8 = 8 * pd.n8;
+  auto put = [&](int64_t idx, float v) {
+    if (dtype == PKV_BF16) {
+      uint16_t b;
+      bf16_round_host(v, &b);
+      ((uint16_t*)packed)[idx] = b;
+    } else {
+      ((float*)packed)[idx] = v;
+    }
+  };
+  for (int i = 0; i < r8; ++i) {
+    for (int c = 0; c < kD; ++c) {
+      const float v = i < r ? Rf[(int64_t)i * kD + c] : 0.f;
+      put(kind == PKV_KEYS ? off_rf_k(pd, i, c) : off_rf_v(pd, i, c), v);
+    }
+    for (int j = 0; j < kP; ++j) {
+      const float v = i < r ? Lf[(int64_t)j * r + i] : 0.f;
+      put(kind == PKV_KEYS ? off_lf_k(pd, j, i) : off_lf_v(pd, j, i), v);
+    }
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_unpack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t dtype,
+                           const void* packed, float* Lf, float* Rf) {
+  int64_t n;
+  int32_t st = pkv_factor_part_elems(P, d, r, &n);
+  if (st != PKV_OK) return st;
+  if ((kind != PKV_KEYS && kind != PKV_VALUES) || (dtype != PKV_BF16 && dtype != PKV_F32) || !Lf ||
+      !Rf || !packed)
+    return PKV_ERR_INVALID_ARG;
+  const PackDims pd = pack_dims(r);
+  auto get = [&](int64_t idx) -> float {
+    if (dtype == PKV_BF16) {
+      uint32_t w = (uint32_t)((const uint16_t*)packed)[idx] << 16;
+      float f;
+      std::memcpy(&f, &w, 4);
+      return f;
+    }
+    return ((const float*)packed)[idx];
+  };
+  for (int i = 0; i < r; ++i) {
+    for (int c = 0; c < kD; ++c)
+      Rf[(int64_t)i * kD + c] = get(kind == PKV_KEYS ? off_rf_k(pd, i, c) : off_rf_v(pd, i, c));
+    for (int j = 0; j < kP; ++j)
+      Lf[(int64_t)j * r + i] = get(kind == PKV_KEYS ? off_lf_k(pd, j, i) : off_lf_v(pd, j, i));
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_cache_layout(const pkv_shape* shape, pkv_layout* out) {
+  int32_t st = check_shape(shape);
+  if (st != PKV_OK) return st;
+  if (!out) return PKV_ERR_INVALID_ARG;
+  make_layout(shape, out);
+  return PKV_OK;
+}
+
+int32_t pkv_cache_create(const pkv_shape* shape, void* device_buffer, uint64_t device_bytes,
+                         pkv_cache** out) {
+  int32_t st = check_shape(shape);
+  if (st != PKV_OK) return st;
+  if (!out || !device_buffer || !aligned(device_buffer, kAlign)) return PKV_ERR_INVALID_ARG;
+  pkv_layout lay;
+  make_layout(shape, &lay);
+  if (device_bytes < lay.total_bytes) return PKV_ERR_CAPACITY;
+  pkv_cache* c = new (std::nothrow) pkv_cache;
+  if (!c) return PKV_ERR_INVALID_ARG;
+  c->shape = *shape;
+  c->lay = lay;
+  c->base = (uint8_t*)device_buffer;
+  c->T = 0;
+  c->n_fact = 0;
+  c->pending = 0;
+  *out = c;
+  return PKV_OK;
+}
+
+void pkv_cache_destroy(pkv_cache* cache) { delete cache; }
+
+int32_t pkv_cache_state(const pkv_cache* c, int64_t* T, int64_t* n_fact, int32_t* pending) {
+  if (!c) return PKV_ERR_INVALID_ARG;
+  if (T) *T = c->T;
+  if (n_fact) *n_fact = c->n_fact;
+  if (pending) *pending = c->pending;
+  return PKV_OK;
+}
+
+int32_t pkv_compress_pages(const void* X, int64_t n_pages, int32_t P, int32_t d, int32_t r,
+                           int32_t in_dtype, int32_t out_dtype, void* Lf, void* Rf, float* sigma,
+                           void* stream) {
+  if (P != kP || d != kD) return PKV_ERR_UNSUPPORTED;
+  if (n_pages < 0 || r < 1 || r > kP) return PKV_ERR_INVALID_ARG;
+  if ((in_dtype != PKV_BF16 && in_dtype != PKV_F32) || (out_dtype != PKV_BF16 && out_dtype != PKV_F32))
+    return PKV_ERR_INVALID_ARG;
+  if (n_pages == 0) return PKV_OK;
+  if (!X || !Lf || !Rf || !aligned(X, 16) || !aligned(Lf, 4) || !aligned(Rf, 4) ||
+      (sigma && !aligned(sigma, 4)))
+    return PKV_ERR_INVALID_ARG;
+  CompressJob job;
+  std::memset(&job, 0, sizeof(job));
+  job.n_pages = n_pages;
+  job.n_kind = 1;
+  job.n_f = n_pages;
+  job.in_base[0] = job.in_base[1] = X;
+  job.in_trans[0] = job.in_trans[1] = 0;
+  job.in_bh_stride = 0;
+  job.in_f_stride = (int64_t)kP * kD;
+  job.in_dtype = in_dtype;
+  job.rank[0] = job.rank[1] = r;
+  job.out_dtype = out_dtype;
+  job.fac = nullptr;
+  job.lf = Lf;
+  job.rf = Rf;
+  job.sigma = sigma;
+  return dev_status(launch_compress(job, (hipStream_t)stream));
+}
+
+int32_t pkv_prefill(pkv_cache* c, const void* K, const void* V, int64_t T, void* stream) {
+  if (!c || !K || !V) return PKV_ERR_INVALID_ARG;
+  if (T < 1) return PKV_ERR_INVALID_ARG;
+  if (T > c->shape.max_tokens) return PKV_ERR_CAPACITY;
+  if (!aligned(K, 16) || !aligned(V, 16)) return PKV_ERR_INVALID_ARG;
+  const CacheGeom g = geom_of(c);
+  const int64_t n_fact = steady_fact(T, kP, g.n_s, g.n_w);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_prefill_dense(g, K, V, T, n_fact, s);
+  if (e == hipSuccess && n_fact > 0) {
+    CompressJob job;
+    std::memset(&job, 0, sizeof(job));
+    job.n_kind = 2;
+    job.n_f = n_fact;
+    job.n_pages = (int64_t)g.B * g.Hkv * n_fact * 2;
+    const int64_t esz = c->lay.elem_bytes;
+    job.in_base[0] = (const uint8_t*)K + (int64_t)g.n_s * kP * kD * esz;
+    job.in_base[1] = (const uint8_t*)V + (int64_t)g.n_s * kP * kD * esz;
+    job.in_trans[0] = job.in_trans[1] = 0;
+    job.in_bh_stride = T * kD;
+    job.in_f_stride = (int64_t)kP * kD;
+    job.in_dtype = g.dtype;
+    job.rank[0] = g.r_k;
+    job.rank[1] = g.r_v;
+    job.out_dtype = g.dtype;
+    job.fac = c->base + c->lay.factors;
+    job.fac_bh_pages = g.F_max;
+    job.f0 = 0;
+    job.page_bytes = c->lay.factor_page_bytes;
+    job.k_part_bytes = c->lay.factor_k_elems * esz;
+    e = launch_compress(job, s);
+  }
+  if (e == hipSuccess) e = launch_table_fill(g, T, n_fact, s);
+  if (e != hipSuccess) return PKV_ERR_DEVICE;
+  c->T = T;
+  c->n_fact = n_fact;
+  c->pending = 0;
+  return PKV_OK;
+}
+
+int32_t pkv_append(pkv_cache* c, const void* k_new, const void* v_new, int32_t* promotion_pending,
+                   void* stream) {
+  if (!c || !k_new || !v_new) return PKV_ERR_INVALID_ARG;
+  if (c->pending) return PKV_ERR_PROMOTION_PENDING;
+  if (c->T >= c->shape.max_tokens) return PKV_ERR_CAPACITY;
+  const CacheGeom g = geom_of(c);
+  hipError_t e = launch_append(g, k_new, v_new, c->T, (hipStream_t)stream);
+  if (e != hipSuccess) return PKV_ERR_DEVICE;
+  c->T += 1;
+  // a completed page enters the window; the oldest window page leaves it
+  const int64_t n_old_ok = steady_fact(c->T, kP, g.n_s, g.n_w);
+  c->pending = n_old_ok > c->n_fact ? 1 : 0;
+  if (promotion_pending) *promotion_pending = c->pending;
+  return PKV_OK;
+}
+
+int32_t pkv_promote_page(pkv_cache* c, void* stream) {
+  if (!c) return PKV_ERR_INVALID_ARG;
+  if (!c->pending) return PKV_ERR_NOT_ELIGIBLE;
+  const CacheGeom g = geom_of(c);
+  const int64_t f = c->n_fact;            // factor slot of the page
+  const int64_t p_old = g.n_s + f;        // logical page leaving the window
+  if (f >= g.F_max) return PKV_ERR_CAPACITY;
+  const int64_t ring = (p_old - g.n_s) % (g.n_w + 1);
+  const int64_t esz = c->lay.elem_bytes;
+  const int64_t ppg = (int64_t)kP * kD;
+  CompressJob job;
+  std::memset(&job, 0, sizeof(job));
+  job.n_kind = 2;
+  job.n_f = 1;
+  job.n_pages = (int64_t)g.B * g.Hkv * 2;
+  job.in_base[0] = c->base + c->lay.win_k + ring * ppg * esz;
+  job.in_base[1] = c->base + c->lay.win_v + ring * ppg * esz;
+  job.in_trans[0] = 0;
+  job.in_trans[1] = 1;  // value pages are stored transposed
+  job.in_bh_stride = (int64_t)(g.n_w + 1) * ppg;
+  job.in_f_stride = 0;
+  job.in_dtype = g.dtype;
+  job.rank[0] = g.r_k;
+  job.rank[1] = g.r_v;
+  job.out_dtype = g.dtype;
+  job.fac = c->base + c->lay.factors;
+  job.fac_bh_pages = g.F_max;
+  job.f0 = f;
+  job.page_bytes = c->lay.factor_page_bytes;
+  job.k_part_bytes = c->lay.factor_k_elems * esz;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_compress(job, s);
+  if (e == hipSuccess) e = launch_table_set(g, p_old, table_entry(PKV_PAGE_FACT, (int)f), s);
+  if (e != hipSuccess) return PKV_ERR_DEVICE;
+  c->n_fact += 1;
+  c->pending = 0;
+  return PKV_OK;
+}
+
+int32_t pkv_decode_workspace_bytes(const pkv_cache* c, int32_t n_split, uint64_t* bytes) {
+  if (!c || !bytes || n_split < 0) return PKV_ERR_INVALID_ARG;
+  const CacheGeom g = geom_of(c);
+  const int ns = n_split > 0 ? n_split : decode_default_splits(g, c->T, c->n_fact);
+  const uint64_t rows = (uint64_t)g.B * g.Hq * ns;
+  *bytes = align_up(rows * kD * 4) + align_up(rows * 2 * 4) + align_up((uint64_t)g.B * g.Hkv * 4);
+  return PKV_OK;
+}
+
+int32_t pkv_decode_attn(const pkv_cache* c, const void* q, float* out, void* workspace,
+                        uint64_t workspace_bytes, int32_t n_split, void* stream) {
+  if (!c || !q || !out || !workspace || n_split < 0) return PKV_ERR_INVALID_ARG;
+  if (c->T < 1) return PKV_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(out, 4) || !aligned(workspace, kAlign)) return PKV_ERR_INVALID_ARG;
+  const CacheGeom g = geom_of(c);
+  const int ns = n_split > 0 ? n_split : decode_default_splits(g, c->T, c->n_fact);
+  uint64_t need = 0;
+  pkv_decode_workspace_bytes(c, ns, &need);
+  if (workspace_bytes < need) return PKV_ERR_CAPACITY;
+  AttnJob job;
+  job.q = q;
+  job.out = out;
+  job.ws_o = (float*)workspace;
+  const uint64_t rows = (uint64_t)g.B * g.Hq * ns;
+  job.ws_ml = (float*)((uint8_t*)workspace + align_up(rows * kD * 4));
+  job.counters = (int32_t*)((uint8_t*)job.ws_ml + align_up(rows * 2 * 4));
+  job.n_split = ns;
+  job.T = c->T;
+  job.n_fact = c->n_fact;
+  return dev_status(launch_decode(g, job, (hipStream_t)stream));
+}
+
+int32_t pkv_read_page_table(const pkv_cache* c, int32_t* cls, int32_t* slot, int64_t n,
+                            void* stream) {
+  if (!c || n < 0 || n > c->lay.max_pages) return PKV_ERR_INVALID_ARG;
+  if (n == 0) return PKV_OK;
+  if (!cls || !slot) return PKV_ERR_INVALID_ARG;
+  int32_t* tmp = new (std::nothrow) int32_t[n];
+  if (!tmp) return PKV_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(tmp, c->base + c->lay.page_table, n * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    delete[] tmp;
+    return PKV_ERR_DEVICE;
+  }
+  for (int64_t p = 0; p < n; ++p) {
+    cls[p] = table_class(tmp[p]);
+    slot[p] = table_slot(tmp[p]);
+  }
+  delete[] tmp;
+  return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+// Dense pools, page table and token append of the hybrid cache.
+//
+// PuzzleKV Sec. 3.3 (1)-(3): after prefill the sink pages and the recent
+// window (completed window pages plus the page being filled) stay dense;
+// Sec. 3.3 "Incremental Cache Update (5)": each new key/value pair is written
+// into the most recent dense page and takes part in attention at once.
+//
+// Dense pages live in two pools per (sequence, KV head): n_s sink slots and a
+// ring of n_w + 1 window slots (n_w completed pages plus the partial page; the
+// slot of the page that leaves the window is the one the next page reuses).
+// Keys are stored row-major [P][d]; values transposed [d][P] so the attention
+// kernel's p V contraction reads contiguous page rows.
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+// Logical page held by a dense slot of a cache of length T with n_fact
+// factorized pages, or -1 when the slot is unused.
+__device__ inline int64_t slot_page(int slot_id, int n_s, int n_w, int64_t T, int64_t n_fact) {
+  const int64_t n_pages = (T + kP - 1) / kP;
+  if (slot_id < n_s) return slot_id < n_pages ? slot_id : -1;
+  const int k = slot_id - n_s;
+  const int64_t first = (int64_t)n_s + n_fact;  // first dense page after the factors
+  if (first >= n_pages) return -1;
+  const int64_t ring = n_w + 1;
+  const int64_t off = ((k - (first - n_s)) % ring + ring) % ring;
+  const int64_t p = first + off;
+  return p < n_pages ? p : -1;
+}
+
+template <typename Elem>
+__global__ __launch_bounds__(256) void prefill_dense_kernel(CacheGeom g, const Elem* K, const Elem* V,
+                                                            int64_t T, int64_t n_fact) {
+  __shared__ Elem tile[kP][kD + 2];
+  const int slot_id = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = (int64_t)b * g.Hkv + h;
+  const int64_t p = slot_page(slot_id, g.n_s, g.n_w, T, n_fact);
+  const int64_t nv = p < 0 ? 0 : ((T - p * kP) < kP ? (T - p * kP) : kP);
+  Elem *dk, *dv;
+  const int64_t ppg = (int64_t)kP * kD;
+  if (slot_id < g.n_s) {
+    dk = (Elem*)(g.base + g.lay.sink_k) + (bh * g.n_s + slot_id) * ppg;
+    dv = (Elem*)(g.base + g.lay.sink_v) + (bh * g.n_s + slot_id) * ppg;
+  } else {
+    const int k = slot_id - g.n_s;
+    dk = (Elem*)(g.base + g.lay.win_k) + (bh * (g.n_w + 1) + k) * ppg;
+    dv = (Elem*)(g.base + g.lay.win_v) + (bh * (g.n_w + 1) + k) * ppg;
+  }
+  const Elem* sk = K + (bh * T + (p < 0 ? 0 : p * kP)) * kD;
+  const Elem* sv = V + (bh * T + (p < 0 ? 0 : p * kP)) * kD;
+  for (int idx = threadIdx.x; idx < kP * kD; idx += 256) {
+    const int j = idx / kD, c = idx % kD;
+    dk[idx] = j < nv ? sk[idx] : Elem(0);
+    tile[j][c] = j < nv ? sv[idx] : Elem(0);
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kP * kD; idx += 256) {
+    const int c = idx / kP, j = idx % kP;
+    dv[idx] = tile[j][c];
+  }
+}
+
+__device__ inline int32_t classify_entry(int64_t p, int64_t T, int n_s, int n_w, int64_t n_fact) {
+  const int64_t n_full = T / kP, n_pages = (T + kP - 1) / kP;
+  if (p >= n_pages) return table_entry(PKV_PAGE_UNUSED, 0);
+  if (p < n_s) return table_entry(PKV_PAGE_SINK, (int)p);
+  if (p < n_s + n_fact) return table_entry(PKV_PAGE_FACT, (int)(p - n_s));
+  const int ring = (int)((p - n_s) % (n_w + 1));
+  return table_entry(p < n_full ? PKV_PAGE_WIN : PKV_PAGE_PART, ring);
+}
+
+__global__ void table_fill_kernel(int32_t* table, int64_t max_pages, int64_t T, int n_s, int n_w,
+                                  int64_t n_fact) {
+  const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p < max_pages) table[p] = classify_entry(p, T, n_s, n_w, n_fact);
+}
+
+__global__ void table_set_kernel(int32_t* table, int64_t page, int32_t entry) {
+  if (threadIdx.x == 0) table[page] = entry;
+}
+
+template <typename Elem>
+__global__ __launch_bounds__(128) void append_kernel(CacheGeom g, const Elem* k, const Elem* v,
+                                                     int64_t T) {
+  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const int64_t bh = (int64_t)b * g.Hkv + h;
+  const int64_t p = T / kP;
+  const int row = (int)(T % kP);
+  const int64_t ppg = (int64_t)kP * kD;
+  Elem *dk, *dv;
+  if (p < g.n_s) {
+    dk = (Elem*)(g.base + g.lay.sink_k) + (bh * g.n_s + p) * ppg;
+    dv = (Elem*)(g.base + g.lay.sink_v) + (bh * g.n_s + p) * ppg;
+  } else {
+    const int64_t slot = (p - g.n_s) % (g.n_w + 1);
+    dk = (Elem*)(g.base + g.lay.win_k) + (bh * (g.n_w + 1) + slot) * ppg;
+    dv = (Elem*)(g.base + g.lay.win_v) + (bh * (g.n_w + 1) + slot) * ppg;
+  }
+  dk[row * kD + c] = k[bh * kD + c];
+  dv[(int64_t)c * kP + row] = v[bh * kD + c];
+  if (b == 0 && h == 0 && c == 0) {
+    int32_t* table = (int32_t*)(g.base + g.lay.page_table);
+    int32_t e;
+    if (p < g.n_s) e = table_entry(PKV_PAGE_SINK, (int)p);
+    else e = table_entry(row == kP - 1 ? PKV_PAGE_WIN : PKV_PAGE_PART, (int)((p - g.n_s) % (g.n_w + 1)));
+    table[p] = e;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_dense(const CacheGeom& g, const void* K, const void* V, int64_t T,
+                                int64_t n_fact, hipStream_t stream) {
+  const dim3 grid(g.n_s + g.n_w + 1, g.Hkv, g.B);
+  if (g.dtype == PKV_BF16)
+    hipLaunchKernelGGL(prefill_dense_kernel<uint16_t>, grid, dim3(256), 0, stream, g,
+                       (const uint16_t*)K, (const uint16_t*)V, T, n_fact);
+  else
+    hipLaunchKernelGGL(prefill_dense_kernel<float>, grid, dim3(256), 0, stream, g, (const float*)K,
+                       (const float*)V, T, n_fact);
+  return hipGetLastError();
+}
+
+hipError_t launch_table_fill(const CacheGeom& g, int64_t T, int64_t n_fact, hipStream_t stream) {
+  const unsigned blocks = (unsigned)((g.max_pages + 255) / 256);
+  hipLaunchKernelGGL(table_fill_kernel, dim3(blocks), dim3(256), 0, stream,
+                     (int32_t*)(g.base + g.lay.page_table), g.max_pages, T, g.n_s, g.n_w, n_fact);
+  return hipGetLastError();
+}
+
+hipError_t launch_table_set(const CacheGeom& g, int64_t page, int32_t entry, hipStream_t stream) {
+  hipLaunchKernelGGL(table_set_kernel, dim3(1), dim3(64), 0, stream,
+                     (int32_t*)(g.base + g.lay.page_table), page, entry);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const CacheGeom& g, const void* k, const void* v, int64_t T,
+                         hipStream_t stream) {
+  const dim3 grid(g.Hkv, g.B);
+  if (g.dtype == PKV_BF16)
+    hipLaunchKernelGGL(append_kernel<uint16_t>, grid, dim3(kD), 0, stream, g, (const uint16_t*)k,
+                       (const uint16_t*)v, T);
+  else
+    hipLaunchKernelGGL(append_kernel<float>, grid, dim3(kD), 0, stream, g, (const float*)k,
+                       (const float*)v, T);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,759 @@
+// Mixed dense / factorized decode attention on gfx950.
+//
+// PuzzleKV Sec. 3.3 (4), Eq. 4 and Eq. 5: every page of the hybrid cache --
+// dense sink and window pages, and factorized history pages -- yields the
+// online-softmax state (m_p, l_p, o_p); factorized pages are evaluated through
+// their factors, contracting the query with the small factors first
+//     s = (q Rf_K^T) Lf_K^T / sqrt(d),   o = (e^(s - m) Lf_V) Rf_V,
+// so no page is ever reconstructed.  States are merged by the FlashAttention
+// reduction (Eq. 5): within a wavefront as pages stream by, across the
+// wavefronts of a workgroup in LDS, and across workgroups (splits) by the
+// last workgroup of each (sequence, KV head) to finish.
+//
+// bf16 path (decode_mfma_kernel): one wavefront owns a contiguous run of pages
+// of one (sequence, KV head) and all G <= 8 query heads of that KV head.  All
+// four contractions run on v_mfma_f32_16x16x32_bf16.  The 16 MFMA columns
+// hold the G query heads twice: columns 0..7 carry the bf16-rounded operand
+// (q, t, p or u) and columns 8..15 its bf16 remainder, so the fp32 operand
+// enters with ~16 significant bits while the stored bf16 factors are used
+// exactly; the two column halves are summed with one row rotation (DPP).
+// Scores are kept in log2 units (q is pre-scaled by log2(e)/sqrt(d)).
+//
+// fp32 path and shapes the matrix-core kernel does not cover
+// (decode_valu_kernel): plain fp32 VALU arithmetic, one workgroup per split.
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DecodeArgs {
+  const void* q;
+  const uint8_t* fac;
+  const void* sink_k;
+  const void* sink_v;
+  const void* win_k;
+  const void* win_v;
+  const int32_t* table;
+  float* ws_o;
+  float* ws_ml;
+  int32_t* counters;  // [B * H_kv], zero between calls
+  float* out;
+  int B, Hkv, G, n_split;
+  int n_s, n_w;
+  int r_k, r_v;
+  int64_t T, n_fact, F_max;
+  int64_t page_bytes, k_part_bytes;
+  int64_t cost_dense, cost_fact;
+  float qscale;
+};
+
+// Work list of one (sequence, KV head): D dense pages (sink pages first, then
+// the window / partial pages), then F factorized pages.  Unit e maps to the
+// logical page below; waves take contiguous cost-balanced ranges of units.
+struct WorkList {
+  int64_t n_sinkp, first_tail, D, F;
+};
+
+__device__ inline WorkList work_list(const DecodeArgs& a) {
+  WorkList w;
+  const int64_t n_pages = (a.T + kP - 1) / kP;
+  w.n_sinkp = n_pages < a.n_s ? n_pages : a.n_s;
+  w.first_tail = a.n_s + a.n_fact;
+  const int64_t tail = n_pages - w.first_tail;
+  w.D = w.n_sinkp + (tail > 0 ? tail : 0);
+  w.F = a.n_fact;
+  return w;
+}
+
+__device__ inline int64_t unit_bound(const WorkList& w, const DecodeArgs& a, int64_t wi,
+                                     int64_t W) {
+  const int64_t total = w.D * a.cost_dense + w.F * a.cost_fact;
+  const int64_t x = total * wi / W;
+  const int64_t dc = w.D * a.cost_dense;
+  if (x <= dc) return (x + a.cost_dense - 1) / a.cost_dense;
+  return w.D + (x - dc + a.cost_fact - 1) / a.cost_fact;
+}
+
+__device__ inline int64_t unit_page(const WorkList& w, const DecodeArgs& a, int64_t e) {
+  if (e < w.n_sinkp) return e;
+  if (e < w.D) return w.first_tail + (e - w.n_sinkp);
+  return a.n_s + (e - w.D);
+}
+
+__device__ inline float ror8(float x) {
+  // lane n of each 16-lane row receives lane (n + 8) mod 16
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, true));
+}
+
+// bf16 part of x on lanes whose column is < 8, bf16 remainder on the others.
+__device__ inline __bf16 split_bf16(float x, bool lo) {
+  const __bf16 hi = (__bf16)x;
+  const __bf16 rem = (__bf16)(x - (float)hi);
+  return lo ? rem : hi;
+}
+
+__device__ inline floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+struct __attribute__((aligned(4))) U32x3 {
+  uint32_t x, y, z;
+};
+
+__device__ inline bf16x8 ld16(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *(const uint4*)p);
+}
+
+
+// W (even, <= 8) consecutive bf16 kept at their exact width in registers.
+template <int W>
+struct RawW {
+  uint32_t d[W / 2];
+};
+
+template <int W>
+__device__ inline void ldraw(RawW<W>& r, const uint16_t* p) {
+  if constexpr (W == 8) {
+    const uint4 v = *(const uint4*)p;
+    r.d[0] = v.x;
+    r.d[1] = v.y;
+    r.d[2] = v.z;
+    r.d[3] = v.w;
+  } else if constexpr (W == 6) {
+    const U32x3 v = *(const U32x3*)p;
+    r.d[0] = v.x;
+    r.d[1] = v.y;
+    r.d[2] = v.z;
+  } else if constexpr (W == 4) {
+    const uint2 v = *(const uint2*)p;
+    r.d[0] = v.x;
+    r.d[1] = v.y;
+  } else {
+    r.d[0] = *(const uint32_t*)p;
+  }
+}
+
+// slots 0..W-1 from r, zeros above
+template <int W>
+__device__ inline bf16x8 operand(const RawW<W>& r) {
+  uint4 u = {0u, 0u, 0u, 0u};
+  u.x = r.d[0];
+  if constexpr (W >= 4) u.y = r.d[1];
+  if constexpr (W >= 6) u.z = r.d[2];
+  if constexpr (W >= 8) u.w = r.d[3];
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+template <int N8>
+struct FactDims {
+  static constexpr int A = 2 * N8;
+  static constexpr int RT = (A + 3) / 4;
+  static constexpr int KS2 = (A + 7) / 8;
+  static constexpr bool kPartialTile = (A % 4) != 0;
+  static constexpr int64_t K1 = 1024 * N8;
+  static constexpr int64_t V1 = 512 * N8;
+  static constexpr int width(int ks) { return (A - 8 * ks) < 8 ? (A - 8 * ks) : 8; }
+  static constexpr int W0 = width(0);
+  static constexpr int W1 = KS2 > 1 ? width(1) : 2;
+};
+
+// K part / V part of one factorized page in matrix-core operand order.
+template <int N8>
+struct KRegs {
+  using Dm = FactDims<N8>;
+  bf16x8 k1[Dm::RT][4];
+  RawW<Dm::W0> k2a[4];
+  RawW<Dm::W1> k2b[Dm::KS2 > 1 ? 4 : 1];
+  __device__ bf16x8 k2(int mt, int ks) const { return ks == 0 ? operand(k2a[mt]) : operand(k2b[mt]); }
+};
+
+template <int N8>
+struct VRegs {
+  using Dm = FactDims<N8>;
+  bf16x8 v1[Dm::RT][2];
+  RawW<Dm::W0> v2a[8];
+  RawW<Dm::W1> v2b[Dm::KS2 > 1 ? 8 : 1];
+  __device__ bf16x8 v2(int mt, int ks) const { return ks == 0 ? operand(v2a[mt]) : operand(v2b[mt]); }
+};
+
+// Rank tiles (K1, V1): the last tile of an odd N8 is stored compacted; lanes
+// whose row is not stored read a valid address and are zeroed.
+struct TileLane {
+  int lam;
+  bool ok;
+};
+
+__device__ inline TileLane tile_lane(int lane) {
+  const int rho = lane & 15, qk = lane >> 4;
+  TileLane t;
+  t.ok = (rho & 3) < 2;
+  t.lam = t.ok ? qk * 8 + (rho >> 2) * 2 + (rho & 3) : 0;
+  return t;
+}
+
+template <int N8>
+__device__ inline void load_keys(KRegs<N8>& R, const uint16_t* kp, int lane) {
+  using Dm = FactDims<N8>;
+  const TileLane tl = tile_lane(lane);
+#pragma unroll
+  for (int mt = 0; mt < Dm::RT; ++mt) {
+    const bool part = Dm::kPartialTile && (mt == Dm::RT - 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (!part) {
+        R.k1[mt][ks] = ld16(kp + mt * 2048 + ks * 512 + lane * 8);
+      } else {
+        const bf16x8 v = ld16(kp + mt * 2048 + ks * 256 + tl.lam * 8);
+        R.k1[mt][ks] = tl.ok ? v : bf16x8{};
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const uint16_t* base = kp + Dm::K1 + mt * 64 * Dm::A;
+    ldraw(R.k2a[mt], base + lane * Dm::W0);
+    if constexpr (Dm::KS2 > 1) ldraw(R.k2b[mt], base + 512 + lane * Dm::W1);
+  }
+}
+
+template <int N8>
+__device__ inline void load_values(VRegs<N8>& R, const uint16_t* vp, int lane) {
+  using Dm = FactDims<N8>;
+  const TileLane tl = tile_lane(lane);
+#pragma unroll
+  for (int mt = 0; mt < Dm::RT; ++mt) {
+    const bool part = Dm::kPartialTile && (mt == Dm::RT - 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (!part) {
+        R.v1[mt][ks] = ld16(vp + mt * 1024 + ks * 512 + lane * 8);
+      } else {
+        const bf16x8 v = ld16(vp + mt * 1024 + ks * 256 + tl.lam * 8);
+        R.v1[mt][ks] = tl.ok ? v : bf16x8{};
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const uint16_t* base = vp + Dm::V1 + mt * 64 * Dm::A;
+    ldraw(R.v2a[mt], base + lane * Dm::W0);
+    if constexpr (Dm::KS2 > 1) ldraw(R.v2b[mt], base + 512 + lane * Dm::W1);
+  }
+}
+
+struct SoftState {
+  float m, l;
+  floatx4 o[8];
+};
+
+// Fold one page's 64 raw scores (MFMA output, hi/lo column halves not yet
+// summed) into the running state; returns the probability operand pb[2].
+__device__ inline void softmax_page(SoftState& st, const floatx4 (&acc)[4], int nvalid, int q4,
+                                    bool lo, bf16x8 (&pb)[2]) {
+  float s[4][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float x = acc[mt][v] + ror8(acc[mt][v]);
+      const int j = 16 * q4 + 4 * mt + v;
+      x = j < nvalid ? x : -INFINITY;
+      s[mt][v] = x;
+      mx = fmaxf(mx, x);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st.m, mx);
+  const float alpha = exp2f(st.m - m_new);
+  float ps = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float p = exp2f(s[mt][v] - m_new);
+      s[mt][v] = p;
+      ps += p;
+    }
+  }
+  ps += __shfl_xor(ps, 16);
+  ps += __shfl_xor(ps, 32);
+  st.l = st.l * alpha + ps;
+  st.m = m_new;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) st.o[mt] *= alpha;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[ks][e] = split_bf16(s[2 * ks + e / 4][e % 4], lo);
+  }
+}
+
+// hi/lo-combined rank vector of rank tiles -> B operand slots.
+template <int N8>
+__device__ inline void rank_operand(const floatx4 (&acc)[FactDims<N8>::RT], bool lo,
+                                    bf16x8 (&out)[FactDims<N8>::KS2]) {
+  using Dm = FactDims<N8>;
+#pragma unroll
+  for (int ks = 0; ks < Dm::KS2; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int mt = 2 * ks + e / 4;
+      float x = 0.f;
+      if (mt < Dm::RT) x = acc[mt][e % 4] + ror8(acc[mt][e % 4]);
+      out[ks][e] = split_bf16(x, lo);
+    }
+  }
+}
+
+// Eq. 4, key half: t = Rf_K q, s = Lf_K t, online-softmax update; returns
+// the probability operand.
+template <int N8>
+__device__ inline void fact_keys(SoftState& st, const KRegs<N8>& R, const bf16x8 (&qb)[4], int q4,
+                                 bool lo, bf16x8 (&pb)[2]) {
+  using Dm = FactDims<N8>;
+  floatx4 at[Dm::RT];
+#pragma unroll
+  for (int mt = 0; mt < Dm::RT; ++mt) {
+    at[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) at[mt] = mfma(R.k1[mt][ks], qb[ks], at[mt]);
+  }
+  bf16x8 tb[Dm::KS2];
+  rank_operand<N8>(at, lo, tb);
+  floatx4 as_[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    as_[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < Dm::KS2; ++ks) as_[mt] = mfma(R.k2(mt, ks), tb[ks], as_[mt]);
+  }
+  softmax_page(st, as_, kP, q4, lo, pb);
+}
+
+// Eq. 4, value half: u = Lf_V^T p, o += Rf_V^T u.
+template <int N8>
+__device__ inline void fact_values(SoftState& st, const VRegs<N8>& R, const bf16x8 (&pb)[2],
+                                   bool lo) {
+  using Dm = FactDims<N8>;
+  floatx4 au[Dm::RT];
+#pragma unroll
+  for (int mt = 0; mt < Dm::RT; ++mt) {
+    au[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) au[mt] = mfma(R.v1[mt][ks], pb[ks], au[mt]);
+  }
+  bf16x8 ub[Dm::KS2];
+  rank_operand<N8>(au, lo, ub);
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+    for (int ks = 0; ks < Dm::KS2; ++ks) st.o[mt] = mfma(R.v2(mt, ks), ub[ks], st.o[mt]);
+  }
+}
+
+__device__ inline void dense_page(SoftState& st, const uint16_t* Kp, const uint16_t* Vt, int nvalid,
+                                  const bf16x8 (&qb)[4], int lane, bool lo) {
+  const int n = lane & 15, q4 = lane >> 4;
+  // score tile rows follow the page-row order of the factor path
+  floatx4 as_[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int j = 16 * (n >> 2) + 4 * mt + (n & 3);
+    as_[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      as_[mt] = mfma(ld16(Kp + j * kD + 32 * ks + 8 * q4), qb[ks], as_[mt]);
+  }
+  bf16x8 pb[2];
+  softmax_page(st, as_, nvalid, q4, lo, pb);
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      st.o[mt] = mfma(ld16(Vt + (16 * mt + n) * kP + 16 * q4 + 8 * ks), pb[ks], st.o[mt]);
+  }
+}
+
+// Eq. 5 across splits.  Every workgroup publishes its (m, l, o) for the G
+// query heads of its (sequence, KV head), then counts itself in; the last one
+// to arrive merges all splits and writes the normalized output, and resets the
+// counter for the next call.  The fences order the partial-state stores and
+// loads at device scope (the 8 XCDs have separate L2 caches).
+__device__ void finish_splits(const DecodeArgs& a, int b, int h) {
+  __shared__ int last;
+  const int Hq = a.Hkv * a.G;
+  __threadfence();
+  __syncthreads();
+  int32_t* ctr = a.counters + (int64_t)b * a.Hkv + h;
+  if (threadIdx.x == 0) last = (atomicAdd(ctr, 1) == a.n_split - 1) ? 1 : 0;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  for (int idx = threadIdx.x; idx < a.G * kD; idx += blockDim.x) {
+    const int gg = idx / kD, c = idx % kD;
+    const int64_t row = (int64_t)b * Hq + (int64_t)h * a.G + gg;
+    const float* ml = a.ws_ml + row * a.n_split * 2;
+    float M = -INFINITY;
+    for (int sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, __builtin_nontemporal_load(ml + 2 * sp));
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+      for (int sp = 0; sp < a.n_split; ++sp) {
+        const float wt = exp2f(__builtin_nontemporal_load(ml + 2 * sp) - M);
+        L += wt * __builtin_nontemporal_load(ml + 2 * sp + 1);
+        O += wt * __builtin_nontemporal_load(a.ws_o + (row * a.n_split + sp) * kD + c);
+      }
+    }
+    a.out[row * kD + c] = L > 0.f ? O / L : 0.f;
+  }
+  if (threadIdx.x == 0) atomicExch(ctr, 0);
+}
+
+constexpr int kWaves = 4;
+
+template <int N8>
+__global__ __launch_bounds__(256, (N8 <= 6 ? 2 : 1)) void decode_mfma_kernel(DecodeArgs a) {
+  __shared__ float sm_o[kWaves][kMaxG][kD];
+  __shared__ float sm_m[kWaves][kMaxG];
+  __shared__ float sm_l[kWaves][kMaxG];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, q4 = lane >> 4;
+  const bool lo = n >= 8;
+  const int g = n & 7;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int Hq = a.Hkv * a.G;
+  const int64_t bh = (int64_t)b * a.Hkv + h;
+
+  // query operand: q * log2(e)/sqrt(d), split into bf16 + remainder columns
+  bf16x8 qb[4];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)b * Hq + (int64_t)h * a.G + g) * kD;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 raw = g < a.G ? ld16(qp + 32 * ks + 8 * q4) : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb[ks][e] = split_bf16((float)raw[e] * a.qscale, lo);
+    }
+  }
+
+  SoftState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) st.o[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const WorkList wl = work_list(a);
+  const int64_t W = (int64_t)a.n_split * kWaves;
+  const int64_t wi = (int64_t)split * kWaves + wave;
+  const int64_t e0 = unit_bound(wl, a, wi, W), e1 = unit_bound(wl, a, wi + 1, W);
+
+  // dense pages of this range
+  const int64_t d_end = e1 < wl.D ? e1 : wl.D;
+  for (int64_t e = e0; e < d_end; ++e) {
+    const int64_t p = unit_page(wl, a, e);
+    const int32_t ent = a.table[p];
+    const int cls = table_class(ent), slot = table_slot(ent);
+    const int64_t ppg = (int64_t)kP * kD;
+    const uint16_t *Kp, *Vt;
+    if (cls == PKV_PAGE_SINK) {
+      Kp = (const uint16_t*)a.sink_k + (bh * a.n_s + slot) * ppg;
+      Vt = (const uint16_t*)a.sink_v + (bh * a.n_s + slot) * ppg;
+    } else {
+      Kp = (const uint16_t*)a.win_k + (bh * (a.n_w + 1) + slot) * ppg;
+      Vt = (const uint16_t*)a.win_v + (bh * (a.n_w + 1) + slot) * ppg;
+    }
+    const int64_t rem = a.T - p * kP;
+    dense_page(st, Kp, Vt, (int)(rem < kP ? rem : kP), qb, lane, lo);
+  }
+
+  // factorized pages: the next page's key part streams in while this page's
+  // value half runs, and its value part while its key half runs
+  int64_t e = e0 > wl.D ? e0 : wl.D;
+  if (e < e1) {
+    const uint8_t* fac_bh = a.fac + bh * a.F_max * a.page_bytes;
+    auto page_ptr = [&](int64_t ee) {
+      const int64_t p = unit_page(wl, a, ee);
+      return fac_bh + (int64_t)table_slot(a.table[p]) * a.page_bytes;
+    };
+    KRegs<N8> kr;
+    VRegs<N8> vr;
+    const uint8_t* pp = page_ptr(e);
+    load_keys<N8>(kr, (const uint16_t*)pp, lane);
+    load_values<N8>(vr, (const uint16_t*)(pp + a.k_part_bytes), lane);
+    for (; e < e1; ++e) {
+      bf16x8 pb[2];
+      fact_keys<N8>(st, kr, qb, q4, lo, pb);
+      const bool more = e + 1 < e1;
+      const uint8_t* pn = more ? page_ptr(e + 1) : pp;
+      if (more) load_keys<N8>(kr, (const uint16_t*)pn, lane);
+      fact_values<N8>(st, vr, pb, lo);
+      if (more) load_values<N8>(vr, (const uint16_t*)(pn + a.k_part_bytes), lane);
+      pp = pn;
+    }
+  }
+
+  // combine the hi/lo column halves of o, then merge the waves in LDS
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) st.o[mt][v] += ror8(st.o[mt][v]);
+  }
+  if (n < 8) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sm_o[wave][n][16 * mt + 4 * q4 + v] = st.o[mt][v];
+    }
+    if (q4 == 0) {
+      sm_m[wave][n] = st.m;
+      sm_l[wave][n] = st.l;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < a.G * kD; idx += blockDim.x) {
+    const int gg = idx / kD, c = idx % kD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][gg]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float wt = exp2f(sm_m[w][gg] - M);  // empty waves: exp2(-inf) = 0
+        L += wt * sm_l[w][gg];
+        O += wt * sm_o[w][gg][c];
+      }
+    }
+    const int64_t row = ((int64_t)b * Hq + (int64_t)h * a.G + gg) * a.n_split + split;
+    a.ws_o[row * kD + c] = O;
+    if (c == 0) {
+      a.ws_ml[row * 2 + 0] = M;
+      a.ws_ml[row * 2 + 1] = L;
+    }
+  }
+  finish_splits(a, b, h);
+}
+
+// ---------------------------------------------------------------------------
+// Generic VALU kernel (fp32 or bf16 storage, any rank <= 64, G <= 8)
+// ---------------------------------------------------------------------------
+
+template <typename Elem>
+__device__ inline float ld_elem(const void* base, int64_t idx) {
+  if constexpr (sizeof(Elem) == 2)
+    return __uint_as_float((uint32_t)((const uint16_t*)base)[idx] << 16);
+  else
+    return ((const float*)base)[idx];
+}
+
+template <typename Elem>
+__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+  __shared__ float qs[kMaxG][kD];
+  __shared__ float ts[kMaxG][kP];
+  __shared__ float ss[kMaxG][kP];
+  __shared__ float us[kMaxG][kP];
+  __shared__ float sh_alpha[kMaxG];
+  __shared__ float sh_m[kMaxG];
+  __shared__ float sh_l[kMaxG];
+
+  const int tid = threadIdx.x;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int G = a.G;
+  const int Hq = a.Hkv * G;
+  const int64_t bh = (int64_t)b * a.Hkv + h;
+  const PackDims pk = pack_dims(a.r_k), pv = pack_dims(a.r_v);
+  constexpr int kEsz = sizeof(Elem);
+
+  for (int idx = tid; idx < G * kD; idx += 256) {
+    const int g = idx / kD, c = idx % kD;
+    qs[g][c] = ld_elem<Elem>(a.q, ((int64_t)b * Hq + (int64_t)h * G + g) * kD + c) * a.qscale;
+  }
+  if (tid < kMaxG) {
+    sh_m[tid] = -INFINITY;
+    sh_l[tid] = 0.f;
+  }
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+
+  const WorkList wl = work_list(a);
+  const int64_t e0 = unit_bound(wl, a, split, a.n_split), e1 = unit_bound(wl, a, split + 1, a.n_split);
+  for (int64_t e = e0; e < e1; ++e) {
+    const int64_t p = unit_page(wl, a, e);
+    const int32_t ent = a.table[p];
+    const int cls = table_class(ent), slot = table_slot(ent);
+    const bool dense = e < wl.D;
+    const int64_t rem = a.T - p * kP;
+    const int nv = dense ? (int)(rem < kP ? rem : kP) : kP;
+    const void *Kp = nullptr, *Vt = nullptr, *kpart = nullptr, *vpart = nullptr;
+    if (dense) {
+      const int64_t ppg = (int64_t)kP * kD;
+      if (cls == PKV_PAGE_SINK) {
+        Kp = (const uint8_t*)a.sink_k + (bh * a.n_s + slot) * ppg * kEsz;
+        Vt = (const uint8_t*)a.sink_v + (bh * a.n_s + slot) * ppg * kEsz;
+      } else {
+        Kp = (const uint8_t*)a.win_k + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
+        Vt = (const uint8_t*)a.win_v + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
+      }
+      for (int idx = tid; idx < G * kP; idx += 256) {
+        const int g = idx / kP, j = idx % kP;
+        float acc = -INFINITY;
+        if (j < nv) {
+          acc = 0.f;
+          for (int c = 0; c < kD; ++c) acc += qs[g][c] * ld_elem<Elem>(Kp, (int64_t)j * kD + c);
+        }
+        ss[g][j] = acc;
+      }
+    } else {
+      kpart = a.fac + (bh * a.F_max + slot) * a.page_bytes;
+      vpart = (const uint8_t*)kpart + a.k_part_bytes;
+      for (int idx = tid; idx < G * a.r_k; idx += 256) {
+        const int g = idx / a.r_k, i = idx % a.r_k;
+        float acc = 0.f;
+        for (int c = 0; c < kD; ++c) acc += ld_elem<Elem>(kpart, off_rf_k(pk, i, c)) * qs[g][c];
+        ts[g][i] = acc;
+      }
+      __syncthreads();
+      for (int idx = tid; idx < G * kP; idx += 256) {
+        const int g = idx / kP, j = idx % kP;
+        float acc = 0.f;
+        for (int i = 0; i < a.r_k; ++i) acc += ld_elem<Elem>(kpart, off_lf_k(pk, j, i)) * ts[g][i];
+        ss[g][j] = acc;
+      }
+    }
+    __syncthreads();
+    if (tid < G) {
+      float mx = -INFINITY;
+      for (int j = 0; j < kP; ++j) mx = fmaxf(mx, ss[tid][j]);
+      const float m_new = fmaxf(sh_m[tid], mx);
+      const float alpha = exp2f(sh_m[tid] - m_new);
+      float sum = 0.f;
+      for (int j = 0; j < kP; ++j) {
+        const float pj = exp2f(ss[tid][j] - m_new);
+        ss[tid][j] = pj;
+        sum += pj;
+      }
+      sh_l[tid] = sh_l[tid] * alpha + sum;
+      sh_m[tid] = m_new;
+      sh_alpha[tid] = alpha;
+    }
+    __syncthreads();
+    if (dense) {
+      for (int k = 0; k < 4; ++k) {
+        const int idx = tid + 256 * k, g = idx / kD, c = idx % kD;
+        if (g >= G) break;
+        float acc = o[k] * sh_alpha[g];
+        for (int j = 0; j < nv; ++j) acc += ss[g][j] * ld_elem<Elem>(Vt, (int64_t)c * kP + j);
+        o[k] = acc;
+      }
+    } else {
+      for (int idx = tid; idx < G * a.r_v; idx += 256) {
+        const int g = idx / a.r_v, i = idx % a.r_v;
+        float acc = 0.f;
+        for (int j = 0; j < kP; ++j) acc += ld_elem<Elem>(vpart, off_lf_v(pv, j, i)) * ss[g][j];
+        us[g][i] = acc;
+      }
+      __syncthreads();
+      for (int k = 0; k < 4; ++k) {
+        const int idx = tid + 256 * k, g = idx / kD, c = idx % kD;
+        if (g >= G) break;
+        float acc = o[k] * sh_alpha[g];
+        for (int i = 0; i < a.r_v; ++i) acc += ld_elem<Elem>(vpart, off_rf_v(pv, i, c)) * us[g][i];
+        o[k] = acc;
+      }
+    }
+    __syncthreads();
+  }
+  for (int k = 0; k < 4; ++k) {
+    const int idx = tid + 256 * k, g = idx / kD, c = idx % kD;
+    if (g >= G) break;
+    const int64_t row = ((int64_t)b * Hq + (int64_t)h * G + g) * a.n_split + split;
+    a.ws_o[row * kD + c] = o[k];
+    if (c == 0) {
+      a.ws_ml[row * 2 + 0] = sh_m[g];
+      a.ws_ml[row * 2 + 1] = sh_l[g];
+    }
+  }
+  finish_splits(a, b, h);
+}
+
+}  // namespace
+
+int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact) {
+  (void)n_fact;
+  const int64_t pages = (T + kP - 1) / kP;
+  const int64_t bh = (int64_t)g.B * g.Hkv;
+  int64_t s = (512 + bh - 1) / bh;        // about two workgroups per CU on 256 CUs
+  const int64_t cap = (pages + 3) / 4;    // at least ~4 pages per workgroup
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  if (s > 1024) s = 1024;
+  return (int)s;
+}
+
+hipError_t launch_decode(const CacheGeom& g, const AttnJob& job, hipStream_t stream) {
+  DecodeArgs a;
+  a.q = job.q;
+  a.fac = g.base + g.lay.factors;
+  a.sink_k = g.base + g.lay.sink_k;
+  a.sink_v = g.base + g.lay.sink_v;
+  a.win_k = g.base + g.lay.win_k;
+  a.win_v = g.base + g.lay.win_v;
+  a.table = (const int32_t*)(g.base + g.lay.page_table);
+  a.ws_o = job.ws_o;
+  a.ws_ml = job.ws_ml;
+  a.counters = job.counters;
+  a.out = job.out;
+  a.B = g.B;
+  a.Hkv = g.Hkv;
+  a.G = g.G;
+  a.n_split = job.n_split;
+  a.n_s = g.n_s;
+  a.n_w = g.n_w;
+  a.r_k = g.r_k;
+  a.r_v = g.r_v;
+  a.T = job.T;
+  a.n_fact = job.n_fact;
+  a.F_max = g.F_max;
+  a.page_bytes = g.lay.factor_page_bytes;
+  a.k_part_bytes = g.lay.factor_k_elems * g.lay.elem_bytes;
+  // cost of a unit ~ bytes it streams (dense: K and V pages)
+  a.cost_dense = 2 * g.lay.dense_page_bytes / 64;
+  a.cost_fact = g.lay.factor_page_bytes / 64;
+  a.qscale = kLog2e / sqrtf((float)kD);
+
+  const dim3 grid(job.n_split, g.Hkv, g.B);
+  const int n8k = (g.r_k + 7) / 8, n8v = (g.r_v + 7) / 8;
+  if (g.dtype == PKV_BF16 && n8k == n8v) {
+    switch (n8k) {
+#define PKV_CASE(N)                                                                 \
+  case N:                                                                           \
+    hipLaunchKernelGGL(decode_mfma_kernel<N>, grid, dim3(256), 0, stream, a); \
+    break;
+      PKV_CASE(1)
+      PKV_CASE(2)
+      PKV_CASE(3)
+      PKV_CASE(4)
+      PKV_CASE(5)
+      PKV_CASE(6)
+      PKV_CASE(7)
+      PKV_CASE(8)
+#undef PKV_CASE
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else if (g.dtype == PKV_BF16) {
+    hipLaunchKernelGGL(decode_valu_kernel<uint16_t>, grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(decode_valu_kernel<float>, grid, dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

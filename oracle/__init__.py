@@ -336,3 +336,69 @@ def storage_ratio(P, r_k, r_v, d):
 def kv_cache_elements(n_layers, n_kv_heads, T, d):
     """Sec. 1: K and V of every layer and KV head, T tokens of d each."""
     return 2 * n_layers * n_kv_heads * T * d
+
+
+class IncrementalDecoder:
+    """Decode-step oracle for a growing cache (Sec. 3.3 (5)): a page is
+    factorized once, when it becomes FACT, and never revisited, so the result
+    at length T equals ``decode`` at length T; caching only saves time.
+
+    K, V: (B, H_kv, T_max, d) float64 stored values of every token that will
+    ever be appended.
+    """
+
+    def __init__(self, K, V, P, s, w, r_k, r_v, store, kv_heads=None):
+        self.K = np.asarray(K, dtype=np.float64)
+        self.V = np.asarray(V, dtype=np.float64)
+        self.P, self.s, self.w = P, s, w
+        self.r = (r_k, r_v)
+        self.store = store
+        B, Hkv = self.K.shape[:2]
+        self.heads = [(b, h) for b in range(B) for h in (range(Hkv) if kv_heads is None else kv_heads)]
+        self.done = {}  # (b, h, kind, p) -> (stored, exact) reconstructions
+
+    def _factorize_new(self, fact_pages):
+        todo = [(b, h, kind, p) for (b, h) in self.heads for kind in (0, 1) for p in fact_pages
+                if (b, h, kind, p) not in self.done]
+        if not todo:
+            return
+        P = self.P
+        for kind in (0, 1):
+            items = [t for t in todo if t[2] == kind]
+            if not items:
+                continue
+            src = self.K if kind == 0 else self.V
+            pages = np.stack([src[b, h, p * P:(p + 1) * P] for (b, h, _, p) in items])
+            U, S, Wt = svd_batch(pages)
+            Lf, Rf = truncate(U, S, Wt, self.r[kind])
+            exact = Lf @ Rf
+            if self.store:
+                stored = round_to(Lf, self.store) @ round_to(Rf, self.store)
+            else:
+                stored = exact
+            for k, key in enumerate(items):
+                self.done[key] = (stored[k], exact[k])
+
+    def step(self, q, T):
+        """Attention outputs (o_stored, o_exact), shape (B, H_q, d), at length T
+        (query heads of KV heads outside `kv_heads` are NaN)."""
+        q = np.asarray(q, dtype=np.float64)
+        B, Hq, d = q.shape
+        Hkv = self.K.shape[1]
+        G = Hq // Hkv
+        cls, _ = classify(T, self.P, self.s, self.w)
+        fact = [int(p) for p in np.nonzero(cls == FACT)[0]]
+        self._factorize_new(fact)
+        o_s = np.full((B, Hq, d), np.nan)
+        o_e = np.full((B, Hq, d), np.nan)
+        P = self.P
+        for (b, h) in self.heads:
+            Ks, Vs = self.K[b, h, :T].copy(), self.V[b, h, :T].copy()
+            Ke, Ve = Ks.copy(), Vs.copy()
+            for p in fact:
+                Ks[p * P:(p + 1) * P], Ke[p * P:(p + 1) * P] = self.done[(b, h, 0, p)]
+                Vs[p * P:(p + 1) * P], Ve[p * P:(p + 1) * P] = self.done[(b, h, 1, p)]
+            qs = q[b, h * G:(h + 1) * G]
+            o_s[b, h * G:(h + 1) * G] = attention(qs, Ks, Vs)
+            o_e[b, h * G:(h + 1) * G] = attention(qs, Ke, Ve)
+        return o_s, o_e

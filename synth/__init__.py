@@ -116,11 +116,14 @@ def haar_columns(Z: np.ndarray) -> np.ndarray:
 
 def spectrum_pages(g: np.random.Generator, n_pages: int, P: int, d: int,
                    decay: float = 1.2) -> np.ndarray:
+    import torch
+
     k = min(P, d)
     U = haar_columns(g.standard_normal((n_pages, P, P)))[..., :, :k]
     W = haar_columns(g.standard_normal((n_pages, d, k)))
     sig = np.arange(1, k + 1, dtype=np.float64) ** (-decay)
-    return (U * sig[None, None, :]) @ np.swapaxes(W, -1, -2)
+    Us = torch.from_numpy(np.ascontiguousarray(U * sig[None, None, :]))
+    return torch.matmul(Us, torch.from_numpy(W).transpose(-1, -2)).numpy()
 
 
 def kv_head(cfg: dict, b: int, h: int, T: int, layer: int = 0):
@@ -145,13 +148,21 @@ def kv_head(cfg: dict, b: int, h: int, T: int, layer: int = 0):
     return out[0], out[1]
 
 
+def _stored_head(args):
+    cfg, b, h, T = args
+    k, v = kv_head(cfg, b, h, T)
+    return to_storage(k, cfg["dtype"]), to_storage(v, cfg["dtype"])
+
+
 def decode_inputs(cfg_id: int, T: int | None = None, B: int | None = None,
-                  kv_heads: int | None = None, with_f64: bool = False):
+                  kv_heads: int | None = None, with_f64: bool = False, workers: int = 1):
     """Stored K, V (B, H_kv, T, d) and q (B, H_q, d) for workload cfg_id.
 
     T, B and kv_heads may shrink a workload for quick tests (the recipe and
     streams are unchanged, so a shrunk input is a prefix/subset of the full
-    one).  Stored arrays are uint16 (bf16 bits) or float32.
+    one).  Stored arrays are uint16 (bf16 bits) or float32.  workers > 1
+    generates (sequence, KV head) streams on that many threads; the
+    bytes do not depend on it.
     """
     cfg = dict(CONFIGS[cfg_id])
     if T is None:
@@ -164,11 +175,18 @@ def decode_inputs(cfg_id: int, T: int | None = None, B: int | None = None,
     sdt = np.uint16 if cfg["dtype"] == "bf16" else np.float32
     K = np.empty((B, Hkv, T, d), dtype=sdt)
     V = np.empty((B, Hkv, T, d), dtype=sdt)
-    for b in range(B):
-        for h in range(Hkv):
-            k, v = kv_head(cfg, b, h, T)
-            K[b, h] = to_storage(k, cfg["dtype"])
-            V[b, h] = to_storage(v, cfg["dtype"])
+    jobs = [(cfg, b, h, T) for b in range(B) for h in range(Hkv)]
+    if workers > 1 and len(jobs) > 1:
+        import concurrent.futures as cf
+
+        # bulk numpy draws and torch QR / matmul release the GIL
+        with cf.ThreadPoolExecutor(max_workers=min(workers, len(jobs))) as ex:
+            results = list(ex.map(_stored_head, jobs))
+    else:
+        results = [_stored_head(j) for j in jobs]
+    for (_, b, h, _), (ks, vs) in zip(jobs, results):
+        K[b, h] = ks
+        V[b, h] = vs
     q = np.empty((B, Hq, d), dtype=sdt)
     for b in range(B):
         q[b] = to_storage(rng(cfg["seed"], b, 0, 0, KIND_Q).standard_normal((Hq, d)),

@@ -1,0 +1,124 @@
+"""GPU parity of prefill + mixed decode attention against the oracle.
+
+Gate (whole output tensor): max |o_gpu - o_ref| <= 1e-2 max |o_ref| for bf16
+storage, <= 1e-4 max |o_ref| for fp32 storage, where o_ref is the oracle's
+attention over the cache whose factorized pages are the oracle's own rank-r
+SVD factors rounded to the storage dtype ("stored" reading).  The error
+against the unrounded oracle is printed beside it.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import long_context_decode_pkv_amd as pkv
+from gpu_common import TOL, make_cache, rel_err, require_gpu, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(cfg_id, T, B=None, kv_heads=None, r_k=None, r_v=None, s=None, w=None, n_splits=(0,),
+             label="", Hq_override=None):
+    import torch
+    require_gpu()
+    d = synth.decode_inputs(cfg_id, T=T, B=B, kv_heads=kv_heads, with_f64=True)
+    cfg = d["cfg"]
+    if Hq_override is not None:  # different GQA group: fresh queries of that many heads
+        d["Hq"] = Hq_override
+        d["G"] = Hq_override // d["Hkv"]
+        g = synth.rng(cfg["seed"], 99, 0, 0, synth.KIND_Q)
+        q = synth.to_storage(g.standard_normal((d["B"], Hq_override, 128)), cfg["dtype"])
+        d["q"], d["q64"] = q, synth.storage_to_f64(q, cfg["dtype"])
+    rk = cfg["r_k"] if r_k is None else r_k
+    rv = cfg["r_v"] if r_v is None else r_v
+    ss = cfg["s"] if s is None else s
+    ww = cfg["w"] if w is None else w
+    cache = make_cache(d, r_k=rk, r_v=rv, s=ss, w=ww)
+    cache.prefill(to_dev(d["K"], cfg["dtype"]), to_dev(d["V"], cfg["dtype"]))
+    q = to_dev(d["q"], cfg["dtype"])
+    ref = oracle.decode(d["q64"], d["K64"], d["V64"], d["T"], 64, ss, ww, rk, rv, cfg["dtype"])
+    outs = []
+    for ns in n_splits:
+        o = to_f64(cache.decode(q, n_split=ns))
+        torch.cuda.synchronize()
+        e_s, e_e = rel_err(o, ref["o_stored"]), rel_err(o, ref["o_exact"])
+        print(f"[decode {label} cfg{cfg_id} T={T} r=({rk},{rv}) split={ns}] "
+              f"err_vs_stored={e_s:.3e} err_vs_exact={e_e:.3e}")
+        assert e_s <= TOL[cfg["dtype"]], (label, ns, e_s)
+        outs.append(o)
+    # the page table is the oracle's classification
+    cls, slot = cache.page_table(-(-d["T"] // 64))
+    ocls, oslot = oracle.classify(d["T"], 64, ss, ww)
+    np.testing.assert_array_equal(cls, ocls)
+    np.testing.assert_array_equal(slot, oslot)
+    return outs, ref, cache, d
+
+
+def test_tiny_fp32_workload():
+    run_case(1, 1024, label="workload1")
+
+
+def test_tiny_fp32_full_rank_equals_dense():
+    outs, ref, _, d = run_case(1, 1024, r_k=64, r_v=64, label="full rank")
+    dense = oracle.attention(d["q64"][0], d["K64"][0, 0], d["V64"][0, 0])
+    assert rel_err(outs[0][0], dense) <= 1e-4
+
+
+def test_llama_shape_reduced_ragged():
+    run_case(2, 64 * 40 + 37, B=2, kv_heads=2, n_splits=(0, 1, 3, 64), label="llama-reduced")
+
+
+def test_qwen_shape_reduced_ragged():
+    run_case(3, 64 * 48 + 5, B=1, kv_heads=2, n_splits=(0, 2, 5), label="qwen-reduced")
+
+
+@pytest.mark.parametrize("r", [8, 32, 40, 64])
+def test_bf16_other_ranks(r):
+    run_case(2, 64 * 20 + 1, B=1, kv_heads=2, r_k=r, r_v=r, label=f"rank{r}")
+
+
+@pytest.mark.parametrize("rk,rv", [(16, 14), (24, 16)])
+def test_bf16_asymmetric_ranks(rk, rv):
+    run_case(2, 64 * 16 + 30, B=1, kv_heads=2, r_k=rk, r_v=rv, label="asym")
+
+
+@pytest.mark.parametrize("Hq", [2, 6, 16])
+def test_gqa_group_sizes(Hq):
+    run_case(2, 64 * 12 + 9, B=1, kv_heads=2, Hq_override=Hq, label=f"G={Hq // 2}")
+
+
+@pytest.mark.parametrize("T", [1, 40, 64, 65, 192, 64 + 128 + 40, 256])
+def test_short_and_dense_only_caches(T):
+    outs, ref, _, d = run_case(2, T, B=1, kv_heads=2, label="short")
+    cls, _ = oracle.classify(T, 64, 64, 128)
+    if not np.any(cls == oracle.FACT):  # dense only: plain attention on the raw cache
+        for h in range(d["Hkv"]):
+            G = d["G"]
+            dense = oracle.attention(d["q64"][0, h * G:(h + 1) * G], d["K64"][0, h], d["V64"][0, h])
+            assert rel_err(outs[0][0, h * G:(h + 1) * G], dense) <= TOL["bf16"]
+
+
+def test_no_sink_no_window():
+    run_case(2, 64 * 10 + 3, B=1, kv_heads=2, s=0, w=0, label="s=w=0")
+
+
+def test_more_splits_than_pages():
+    run_case(2, 64 * 6 + 2, B=1, kv_heads=1, n_splits=(1, 7, 300), label="empty splits")
+
+
+def test_decode_errors():
+    import torch
+    require_gpu()
+    d = synth.decode_inputs(2, T=300, B=1, kv_heads=1)
+    cache = make_cache(d, max_tokens=400)
+    q = to_dev(d["q"], "bf16")
+    with pytest.raises(pkv.PKVError) as ei:  # empty cache
+        cache.decode(q)
+    assert ei.value.status == 1
+    cache.prefill(to_dev(d["K"], "bf16"), to_dev(d["V"], "bf16"))
+    small = torch.empty(16, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(pkv.PKVError) as ei:
+        cache.decode(q, workspace=small)
+    assert ei.value.status == 3
+    with pytest.raises(ValueError):
+        cache.decode(q.float())

@@ -1,0 +1,184 @@
+"""CPU tests of the C-ABI library: it loads without a GPU, exports every
+symbol include/pkv.h declares, and its host-only logic (classification, slot
+policy, packed factor layout, storage accounting, argument validation) agrees
+with the oracle or with closed forms.  No device compute is called here."""
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import long_context_decode_pkv_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _built():
+    if not os.path.exists(pkv.LIB_PATH):
+        from long_context_decode_pkv_amd import build
+        build.build()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 15
+    L = ctypes.CDLL(pkv.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_classify_matches_oracle_exhaustive():
+    for P in (16, 32, 64):
+        for s, w in itertools.product((0, P, 2 * P), (0, P, 2 * P, 3 * P)):
+            for T in list(range(0, 12 * P + 3)) + [64 * P + 1, 100 * P]:
+                cls, slot = pkv.classify(T, P, s, w)
+                ocls, oslot = oracle.classify(T, P, s, w)
+                np.testing.assert_array_equal(cls, ocls, err_msg=f"{T} {P} {s} {w}")
+                np.testing.assert_array_equal(slot, oslot, err_msg=f"{T} {P} {s} {w}")
+
+
+def test_classify_pending_state_matches_oracle():
+    P, s, w = 64, 64, 128
+    for T in (8192 + 64 * k for k in range(1, 4)):
+        steady = (T // P) - 1 - 2
+        cls, slot = pkv.classify(T, P, s, w, n_fact=steady - 1)
+        ocls, oslot = oracle.classify(T, P, s, w, n_fact=steady - 1)
+        np.testing.assert_array_equal(cls, ocls)
+        np.testing.assert_array_equal(slot, oslot)
+
+
+def test_classify_rejects_bad_arguments():
+    with pytest.raises(pkv.PKVError):
+        pkv.classify(100, 64, 32, 128)
+    with pytest.raises(pkv.PKVError):
+        pkv.classify(100, 64, 64, 100)
+    with pytest.raises(pkv.PKVError):
+        pkv.classify(-1, 64, 64, 128, n_pages=1)
+
+
+def test_storage_ratio_is_eq3_and_agrees_with_oracle():
+    for P, rk, rv, d in ((32, 16, 14, 128), (64, 16, 16, 128), (64, 24, 24, 128), (16, 9, 9, 128)):
+        assert abs(pkv.storage_ratio(P, rk, rv, d) - oracle.storage_ratio(P, rk, rv, d)) < 1e-15
+
+
+@pytest.mark.parametrize("r", [1, 7, 8, 14, 16, 24, 32, 40, 48, 56, 64])
+def test_packed_layout_is_a_bijection(r):
+    """Every (operand, row, col) of the two factor parts maps to a distinct
+    slot and every slot of the part is used."""
+    n = pkv.factor_part_elems(r)
+    r8 = -(-r // 8) * 8
+    assert n == r8 * (64 + 128)
+    for kind in (pkv.KEYS, pkv.VALUES):
+        # encode each entry's identity in its value, pack, and check coverage
+        Lf = np.arange(64 * r8, dtype=np.float32).reshape(64, r8)[:, :r] + 1
+        Rf = np.arange(r8 * 128, dtype=np.float32).reshape(r8, 128)[:r] + 1 + 64 * r8
+        packed = pkv.pack_factors(kind, r, pkv.F32, Lf, Rf)
+        vals = packed[packed != 0]
+        assert len(np.unique(vals)) == len(vals) == 64 * r + r * 128
+        Lb, Rb = pkv.unpack_factors(kind, r, pkv.F32, packed)
+        np.testing.assert_array_equal(Lb, Lf)
+        np.testing.assert_array_equal(Rb, Rf)
+
+
+def test_pack_bf16_rounds_nearest_even():
+    g = np.random.default_rng(0)
+    r = 24
+    Lf = g.standard_normal((64, r)).astype(np.float32)
+    Rf = g.standard_normal((r, 128)).astype(np.float32)
+    packed = pkv.pack_factors(pkv.KEYS, r, pkv.BF16, Lf, Rf)
+    Lb, Rb = pkv.unpack_factors(pkv.KEYS, r, pkv.BF16, packed)
+    np.testing.assert_array_equal(Lb, oracle.round_to(Lf, "bf16").astype(np.float32))
+    np.testing.assert_array_equal(Rb, oracle.round_to(Rf, "bf16").astype(np.float32))
+
+
+def test_operand_order_of_packed_parts():
+    """Spot-check the documented lane order: K part starts with Rf_K tile 0,
+    reduction step 0, lane l -> row l % 16 (rank 2*n8*(l%16//4) + l%4),
+    channels 8*(l//16) .. +7."""
+    r = 24  # n8 = 3, six ranks per lane quad
+    Lf = np.zeros((64, r), np.float32)
+    Rf = np.arange(r * 128, dtype=np.float32).reshape(r, 128)
+    packed = pkv.pack_factors(pkv.KEYS, r, pkv.F32, Lf, Rf)
+    for lane in (0, 5, 17, 63):
+        rho, qk = lane % 16, lane // 16
+        rank = 6 * (rho // 4) + rho % 4
+        np.testing.assert_array_equal(packed[lane * 8: lane * 8 + 8], Rf[rank, 8 * qk: 8 * qk + 8])
+
+
+def _shape(**kw):
+    base = dict(batch=2, n_q_heads=8, n_kv_heads=2, rank_k=16, rank_v=16, sink=64, window=128,
+                max_tokens=4096, dtype=pkv.BF16)
+    base.update(kw)
+    return pkv.make_shape(**base)
+
+
+def test_layout_sizes():
+    lay = pkv.cache_layout(_shape())
+    assert lay["max_pages"] == 64
+    assert lay["max_fact_pages"] == 64 - 1 - 2
+    assert lay["factor_page_bytes"] == 2 * (16 * 192) * 2
+    assert lay["dense_page_bytes"] == 64 * 128 * 2
+    for k in ("sink_k", "sink_v", "win_k", "win_v", "factors", "page_table", "total_bytes"):
+        assert lay[k] % 256 == 0
+    assert lay["factors"] >= lay["win_v"] + 2 * 2 * 3 * lay["dense_page_bytes"]
+    assert lay["total_bytes"] >= lay["page_table"] + 4 * lay["max_pages"]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), 2), (dict(page_len=32), 2), (dict(n_q_heads=32, n_kv_heads=2), 2),
+    (dict(sink=32), 1), (dict(window=100), 1), (dict(rank_k=0), 1), (dict(rank_v=65), 1),
+    (dict(n_q_heads=7), 1), (dict(max_tokens=0), 1), (dict(dtype=5), 1),
+])
+def test_layout_validation(kw, status):
+    with pytest.raises(pkv.PKVError) as ei:
+        pkv.cache_layout(_shape(**kw))
+    assert ei.value.status == status
+
+
+def test_create_validation_without_gpu():
+    L = pkv.lib()
+    sh = _shape()
+    lay = pkv.cache_layout(sh)
+    h = ctypes.c_void_p()
+    # misaligned buffer pointer and a buffer that is too small
+    assert L.pkv_cache_create(ctypes.byref(sh), ctypes.c_void_p(256 * 1000 + 8), lay["total_bytes"],
+                              ctypes.byref(h)) == 1
+    assert L.pkv_cache_create(ctypes.byref(sh), ctypes.c_void_p(256 * 1000), lay["total_bytes"] - 1,
+                              ctypes.byref(h)) == 3
+    # a handle over a fake address: host-side state calls work, no GPU touched
+    assert L.pkv_cache_create(ctypes.byref(sh), ctypes.c_void_p(256 * 1000), lay["total_bytes"],
+                              ctypes.byref(h)) == 0
+    T, nf, pend = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    assert L.pkv_cache_state(h, ctypes.byref(T), ctypes.byref(nf), ctypes.byref(pend)) == 0
+    assert (T.value, nf.value, pend.value) == (0, 0, 0)
+    assert L.pkv_promote_page(h, None) == 4          # nothing waiting
+    assert L.pkv_prefill(h, None, None, 10, None) == 1
+    assert L.pkv_prefill(h, ctypes.c_void_p(4096), ctypes.c_void_p(4096), 5000, None) == 3
+    ws = ctypes.c_uint64()
+    assert L.pkv_decode_workspace_bytes(h, 4, ctypes.byref(ws)) == 0
+    assert ws.value >= 2 * 8 * 4 * 130 * 4
+    # empty cache: attention is refused before any launch
+    assert L.pkv_decode_attn(h, ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096),
+                             ws.value, 4, None) == 1
+    L.pkv_cache_destroy(h)
+
+
+def test_compress_validation_without_gpu():
+    L = pkv.lib()
+    p = ctypes.c_void_p(4096)
+    assert L.pkv_compress_pages(p, 4, 32, 128, 8, 0, 0, p, p, None, None) == 2
+    assert L.pkv_compress_pages(p, 4, 64, 128, 0, 0, 0, p, p, None, None) == 1
+    assert L.pkv_compress_pages(p, 4, 64, 128, 65, 0, 0, p, p, None, None) == 1
+    assert L.pkv_compress_pages(None, 4, 64, 128, 8, 0, 0, p, p, None, None) == 1
+    assert L.pkv_compress_pages(p, 0, 64, 128, 8, 0, 0, p, p, None, None) == 0
+    assert L.pkv_compress_pages(ctypes.c_void_p(4098), 4, 64, 128, 8, 0, 0, p, p, None, None) == 1
