@@ -2,11 +2,15 @@
 
 Default workload (qwen3-32b-layer-128k): one layer of a Qwen3-32B-shaped cache,
 B = 1, 64 query heads, 8 KV heads, d = 128, T = 131072 bf16 tokens, P = 64,
-r = 24, sink 64, window 128; 2045 factorized pages per KV head.  A step is one
-decode step of the hot path: append the new token's K/V row, promote the page
-leaving the window when one is due (page decomposition), and run mixed decode
-attention for every query head.  Inputs are seeded synthetic pages with the
-sigma_i = i^-1.2 spectrum (synth.py), resident in HBM before timing.
+r = 24, sink 64, window 128; 2045 factorized pages per KV head.  A layer step
+is one decode step of the hot path on one layer: append the new token's K/V
+row, promote the page leaving the window when one is due (page
+decomposition), and run mixed decode attention for every query head (the
+partial-state kernel, then the cross-split merge).  Four independent layer
+caches of this shape are stepped in rotation, as the layers of a model would
+be, so no cache's 302 MB is served from the 256 MB Infinity Cache on reuse.
+Inputs are seeded synthetic pages with the sigma_i = i^-1.2 spectrum
+(synth.py), resident in HBM before timing.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
@@ -106,93 +110,102 @@ def cpu_baseline_decode(cfg, K, V, q, T):
 
 
 def bench_decode(args, cfg_id, name):
+    """One decode step of the workload's layer, on NL independent layer caches
+    in rotation (a decode step of an NL-layer stack), so that no cache is
+    re-read from the 256 MB Infinity Cache between its uses."""
     import torch
     import synth
     import long_context_decode_pkv_amd as pkv
 
     cfg = dict(synth.CONFIGS[cfg_id])
     B, Hq, Hkv, T0 = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"]
+    NL = args.layers
     total = T0 + args.warmup + args.steps
     inp = cached_inputs(cfg_id, total, workers=args.workers)
     dt = cfg["dtype"]
     Kd, Vd = to_dev(inp["K"], dt), to_dev(inp["V"], dt)
-    cache = pkv.Cache(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, rank_k=cfg["r_k"], rank_v=cfg["r_v"],
-                      sink=cfg["s"], window=cfg["w"], max_tokens=total, dtype=dt)
+    caches = [pkv.Cache(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, rank_k=cfg["r_k"], rank_v=cfg["r_v"],
+                        sink=cfg["s"], window=cfg["w"], max_tokens=total, dtype=dt)
+              for _ in range(NL)]
     K0 = Kd[:, :, :T0].contiguous()
     V0 = Vd[:, :, :T0].contiguous()
     rows_k = [Kd[:, :, t].contiguous() for t in range(T0, total)]
     rows_v = [Vd[:, :, t].contiguous() for t in range(T0, total)]
     qs = [to_dev(synth.step_queries(cfg_id, t, B, Hq, cfg["d"], dt), dt) for t in range(total - T0)]
     out = torch.empty((B, Hq, cfg["d"]), dtype=torch.float32, device="cuda:0")
-    ws = cache.workspace(0)
+    del Kd, Vd
     torch.cuda.synchronize()
 
-    # prefill: dense pools + decomposition of every factorized page
+    # prefill (dense pools + decomposition of every factorized page), timed on layer 0
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    cache.prefill(K0, V0)
+    caches[0].prefill(K0, V0)
     e1.record()
+    for c in caches[1:]:
+        c.prefill(K0, V0)
     torch.cuda.synchronize()
     t_prefill = e0.elapsed_time(e1) * 1e-3
-    n_fact0 = cache.state()[1]
+    n_fact0 = caches[0].state()[1]
     pages0 = B * Hkv * n_fact0 * 2
-    log(f"prefill T={T0}: {pages0} pages decomposed in {t_prefill * 1e3:.2f} ms")
+    log(f"prefill T={T0}: {pages0} pages decomposed in {t_prefill * 1e3:.2f} ms; {NL} layer caches")
     del K0, V0
+    wss = [c.workspace(0) for c in caches]  # sized for the library's split count at this length
 
-    def step(i, events=None):
-        if cache.append(rows_k[i], rows_v[i]):
-            cache.promote()
-        T, nf, _ = cache.state()
-        if events is not None:
-            events[0].record()
-        cache.decode(qs[i], out=out, workspace=ws)
-        if events is not None:
-            events[1].record()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def layer_step(c, ws, i, rec=None):
+        if c.append(rows_k[i], rows_v[i]):
+            if rec is not None:
+                rec["promote"][0].record()
+                rec["promoted"] = True
+            c.promote()
+            if rec is not None:
+                rec["promote"][1].record()
+        T, nf, _ = c.state()
+        if rec is not None:
+            rec["partial"][0].record()
+        c.decode_partial(qs[i], workspace=ws)
+        if rec is not None:
+            rec["partial"][1].record()
+        c.decode_merge(out, workspace=ws)
+        if rec is not None:
+            rec["merge"][1].record()
         return T, nf
 
     for i in range(args.warmup):
-        step(i)
+        for c, ws in zip(caches, wss):
+            layer_step(c, ws, i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    recs = [[{"partial": (ev(), ev()), "merge": (None, ev()), "promote": (ev(), ev())}
+             for _ in range(NL)] for _ in range(args.steps)]
     states = []
     torch.cuda.synchronize()
     t = time.perf_counter()
     for j in range(args.steps):
-        states.append(step(args.warmup + j, evs[j]))
+        for li, (c, ws) in enumerate(zip(caches, wss)):
+            states.append(layer_step(c, ws, args.warmup + j, recs[j][li]))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t
-    durs = np.array([a.elapsed_time(b) * 1e-3 for a, b in evs])
+    flat = [r for step in recs for r in step]
+    durs = np.array([r["partial"][0].elapsed_time(r["partial"][1]) * 1e-3 for r in flat])
+    merges = np.array([r["partial"][1].elapsed_time(r["merge"][1]) * 1e-3 for r in flat])
+    promos = [r["promote"][0].elapsed_time(r["promote"][1]) * 1e-3 for r in flat if r.get("promoted")]
     nbytes = np.array([decode_bytes(cfg, B, Hkv, Hq, T, nf) for T, nf in states], dtype=np.float64)
     achieved = nbytes.sum() / durs.sum() / 1e9
-    log(f"decode launch: mean {durs.mean() * 1e6:.2f} us, median {np.median(durs) * 1e6:.2f} us, "
-        f"{nbytes.mean() / 1e6:.1f} MB -> {achieved:.0f} GB/s")
-
-    # same launches with the 256 MB Infinity Cache flushed before each one
-    flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device="cuda:0")
-    fl = []
-    for j in range(min(args.steps, 16)):
-        flush.fill_(j & 0xFF)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        cache.decode(qs[args.warmup + j], out=out, workspace=ws)
-        b.record()
-        fl.append((a, b))
-    torch.cuda.synchronize()
-    dfl = np.array([a.elapsed_time(b) * 1e-3 for a, b in fl])
-    T_last, nf_last = cache.state()[:2]
-    b_last = decode_bytes(cfg, B, Hkv, Hq, T_last, nf_last)
-    log(f"decode launch after cache flush: mean {dfl.mean() * 1e6:.2f} us -> "
-        f"{b_last / dfl.mean() / 1e9:.0f} GB/s")
+    layer_steps = args.steps * NL
+    log(f"partial kernel: mean {durs.mean() * 1e6:.2f} us (median {np.median(durs) * 1e6:.2f}), "
+        f"{nbytes.mean() / 1e6:.1f} MB -> {achieved:.0f} GB/s; merge {merges.mean() * 1e6:.2f} us; "
+        f"{len(promos)} promotions, mean {np.mean(promos) * 1e6 if promos else 0:.1f} us; "
+        f"layer step {elapsed / layer_steps * 1e6:.1f} us")
 
     res = {
-        "metric": "decode-attn tokens/s (one layer, batch tokens per second of a full decode step)",
-        "value": B * args.steps / elapsed,
+        "metric": "decode-attn tokens/s (one layer: batch tokens per second of a layer decode step)",
+        "value": B * layer_steps / elapsed,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": elapsed / args.steps * 1e3,
+        "ms_per_step": elapsed / layer_steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -201,14 +214,16 @@ def bench_decode(args, cfg_id, name):
         "config": {"workload": name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": cfg["d"],
                    "context_tokens": T0, "page_len": cfg["P"], "rank_k": cfg["r_k"],
                    "rank_v": cfg["r_v"], "sink": cfg["s"], "window": cfg["w"],
-                   "step": "append + promote when due + mixed decode attention"},
+                   "layer_caches_rotated": NL,
+                   "step": "append + promote when due + decode partial + merge, per layer"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode_mfma_kernel (split + fused Eq. 5 merge)",
+                     "kernel": "decode_mfma_kernel (pkv_decode_partial)",
                      "launch_us_mean": durs.mean() * 1e6,
-                     "bytes_per_launch": float(nbytes.mean()),
-                     "flushed_launch_us_mean": dfl.mean() * 1e6,
-                     "flushed_achieved": b_last / dfl.mean() / 1e9},
+                     "bytes_per_launch": float(nbytes.mean())},
+        "breakdown_us": {"decode_partial": durs.mean() * 1e6, "decode_merge_incl_gap": merges.mean() * 1e6,
+                         "promote_mean": float(np.mean(promos) * 1e6) if promos else None,
+                         "promotions": len(promos)},
         "decode_effective_GBps": achieved,
         "pages_compressed_per_s": pages0 / t_prefill,
         "prefill_ms": t_prefill * 1e3,
@@ -284,6 +299,8 @@ def main():
                     choices=["qwen3-32b-layer-128k", "llama3.1-8b-layer", "compress"])
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--workers", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=4,
+                    help="independent layer caches decoded in rotation (defeats cache reuse)")
     ap.add_argument("--distinct-pages", type=int, default=8192)
     args = ap.parse_args()
     if args.gpus != 1:

@@ -203,7 +203,7 @@ int32_t pkv_append(pkv_cache* cache, const void* k_new, const void* v_new,
 int32_t pkv_promote_page(pkv_cache* cache, void* stream);
 
 /* Workspace bytes pkv_decode_attn needs for n_split splits per (sequence,
- * KV head); n_split = 0 selects the library's choice. */
+ * KV head); n_split = 0 selects the library's choice; at most 512. */
 int32_t pkv_decode_workspace_bytes(const pkv_cache* cache, int32_t n_split, uint64_t* bytes);
 
 /*
@@ -211,18 +211,37 @@ int32_t pkv_decode_workspace_bytes(const pkv_cache* cache, int32_t n_split, uint
  * head, softmax(q K^T / sqrt(d)) V over all T cached tokens, where factorized
  * pages are evaluated through their factors (scores (q Rf_K^T) Lf_K^T, output
  * (e^(s-m) Lf_V) Rf_V) without reconstructing them, dense pages directly, and
- * page-wise partial states are merged by online softmax within and across
- * splits (the last workgroup of each (sequence, KV head) merges the splits).
- * q: device [B][H_q][d] (cache dtype); out: device float32 [B][H_q][d];
- * workspace: device, >= pkv_decode_workspace_bytes bytes, 256-byte aligned,
- * zero-filled before its first use (it ends every call with its arrival
- * counters back at zero, so it can be reused without clearing; calls that
- * share one workspace must not overlap).
- * Errors: INVALID_ARG (T == 0, null or misaligned pointers), CAPACITY
- * (workspace too small).
+ * page-wise partial states are merged by online softmax within each split
+ * and then across splits.  Equivalent to pkv_decode_partial followed by
+ * pkv_decode_merge on the same stream.
+ * q: device [B][H_q][d] (cache dtype), 16-byte aligned; out: device float32
+ * [B][H_q][d], 16-byte aligned; workspace: device, 256-byte aligned, at least
+ * pkv_decode_workspace_bytes(n_split) bytes (no initialization needed; calls
+ * that share one workspace must not overlap).
+ * Errors: INVALID_ARG (T == 0, null or misaligned pointers, n_split > 512),
+ * CAPACITY (workspace too small).
  */
 int32_t pkv_decode_attn(const pkv_cache* cache, const void* q, float* out, void* workspace,
                         uint64_t workspace_bytes, int32_t n_split, void* stream);
+
+/*
+ * First half of pkv_decode_attn: the page-wise states of Eq. 4, already
+ * merged within each of n_split page ranges per (sequence, KV head).  Writes
+ * to the workspace, per row = (b * H_q + h) * n_split + split:
+ *   float o[row][d]        at byte 0 (unnormalized sum of e^(s-m) v),
+ *   float (m, l)[row][2]   at byte align256(B * H_q * n_split * d * 4),
+ * with m in log2 units (scores are scaled by log2(e)/sqrt(d)) and an empty
+ * range reported as m = -inf, l = 0, o = 0.  These are the states a
+ * context-parallel shard would exchange before the Eq. 5 merge.
+ */
+int32_t pkv_decode_partial(const pkv_cache* cache, const void* q, void* workspace,
+                           uint64_t workspace_bytes, int32_t n_split, void* stream);
+
+/* Second half: the Eq. 5 merge of the n_split partial states of every
+ * (sequence, query head) in the workspace into the normalized float32
+ * output out [B][H_q][d] (16-byte aligned). */
+int32_t pkv_decode_merge(const pkv_cache* cache, const void* workspace, uint64_t workspace_bytes,
+                         int32_t n_split, float* out, void* stream);
 
 /* Copy the page table to host: cls[p], slot[p] for p < n (n <= max_pages).
  * Synchronizes `stream`. */

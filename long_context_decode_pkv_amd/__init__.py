@@ -80,6 +80,8 @@ def lib():
         "pkv_promote_page": ([vp, vp], i32),
         "pkv_decode_workspace_bytes": ([vp, i32, P(u64)], i32),
         "pkv_decode_attn": ([vp, vp, vp, vp, u64, i32, vp], i32),
+        "pkv_decode_partial": ([vp, vp, vp, u64, i32, vp], i32),
+        "pkv_decode_merge": ([vp, vp, u64, i32, vp, vp], i32),
         "pkv_read_page_table": ([vp, vp, vp, i64, vp], i32),
     }
     for name, (args, res) in sig.items():
@@ -269,8 +271,7 @@ class Cache:
         import torch
         need = self.workspace_bytes(n_split)
         if self._ws is None or self._ws.numel() < need:
-            # zero-filled once; the library leaves its counters at zero
-            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._ws
 
     def decode(self, q, out=None, n_split: int = 0, workspace=None):
@@ -281,6 +282,22 @@ class Cache:
         _check(lib().pkv_decode_attn(self._h, _dev_ptr(q, self.dtype_code, "q"),
                                      _dev_ptr(out, None, "out"), ctypes.c_void_p(ws.data_ptr()),
                                      ws.numel(), n_split, _stream(self.device)), "pkv_decode_attn")
+        return out
+
+    def decode_partial(self, q, n_split: int = 0, workspace=None):
+        """Eq. 4 states merged within each split, left in the workspace."""
+        ws = self.workspace(n_split) if workspace is None else workspace
+        _check(lib().pkv_decode_partial(self._h, _dev_ptr(q, self.dtype_code, "q"),
+                                        ctypes.c_void_p(ws.data_ptr()), ws.numel(), n_split,
+                                        _stream(self.device)), "pkv_decode_partial")
+        return ws
+
+    def decode_merge(self, out, n_split: int = 0, workspace=None):
+        """Eq. 5 merge of the workspace's partial states into out."""
+        ws = self.workspace(n_split) if workspace is None else workspace
+        _check(lib().pkv_decode_merge(self._h, ctypes.c_void_p(ws.data_ptr()), ws.numel(), n_split,
+                                      _dev_ptr(out, None, "out"), _stream(self.device)),
+               "pkv_decode_merge")
         return out
 
     # -- inspection

@@ -407,35 +407,70 @@ int32_t pkv_promote_page(pkv_cache* c, void* stream) {
 }
 
 int32_t pkv_decode_workspace_bytes(const pkv_cache* c, int32_t n_split, uint64_t* bytes) {
-  if (!c || !bytes || n_split < 0) return PKV_ERR_INVALID_ARG;
+  if (!c || !bytes || n_split < 0 || n_split > kMaxDecodeSplits) return PKV_ERR_INVALID_ARG;
   const CacheGeom g = geom_of(c);
   const int ns = n_split > 0 ? n_split : decode_default_splits(g, c->T, c->n_fact);
   const uint64_t rows = (uint64_t)g.B * g.Hq * ns;
-  *bytes = align_up(rows * kD * 4) + align_up(rows * 2 * 4) + align_up((uint64_t)g.B * g.Hkv * 4);
+  *bytes = align_up(rows * kD * 4) + align_up(rows * 2 * 4);
   return PKV_OK;
 }
 
-int32_t pkv_decode_attn(const pkv_cache* c, const void* q, float* out, void* workspace,
-                        uint64_t workspace_bytes, int32_t n_split, void* stream) {
-  if (!c || !q || !out || !workspace || n_split < 0) return PKV_ERR_INVALID_ARG;
+namespace {
+
+// Shared argument checks of the decode calls; fills job (without out).
+int32_t decode_job(const pkv_cache* c, const void* q, void* workspace, uint64_t workspace_bytes,
+                   int32_t n_split, AttnJob* job) {
+  if (!c || !workspace || n_split < 0 || n_split > kMaxDecodeSplits) return PKV_ERR_INVALID_ARG;
   if (c->T < 1) return PKV_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(out, 4) || !aligned(workspace, kAlign)) return PKV_ERR_INVALID_ARG;
+  if ((q && !aligned(q, 16)) || !aligned(workspace, kAlign)) return PKV_ERR_INVALID_ARG;
   const CacheGeom g = geom_of(c);
   const int ns = n_split > 0 ? n_split : decode_default_splits(g, c->T, c->n_fact);
   uint64_t need = 0;
   pkv_decode_workspace_bytes(c, ns, &need);
   if (workspace_bytes < need) return PKV_ERR_CAPACITY;
-  AttnJob job;
-  job.q = q;
-  job.out = out;
-  job.ws_o = (float*)workspace;
   const uint64_t rows = (uint64_t)g.B * g.Hq * ns;
-  job.ws_ml = (float*)((uint8_t*)workspace + align_up(rows * kD * 4));
-  job.counters = (int32_t*)((uint8_t*)job.ws_ml + align_up(rows * 2 * 4));
-  job.n_split = ns;
-  job.T = c->T;
-  job.n_fact = c->n_fact;
-  return dev_status(launch_decode(g, job, (hipStream_t)stream));
+  job->q = q;
+  job->out = nullptr;
+  job->ws_o = (float*)workspace;
+  job->ws_ml = (float*)((uint8_t*)workspace + align_up(rows * kD * 4));
+  job->n_split = ns;
+  job->T = c->T;
+  job->n_fact = c->n_fact;
+  return PKV_OK;
+}
+
+}  // namespace
+
+int32_t pkv_decode_partial(const pkv_cache* c, const void* q, void* workspace,
+                           uint64_t workspace_bytes, int32_t n_split, void* stream) {
+  if (!q) return PKV_ERR_INVALID_ARG;
+  AttnJob job;
+  int32_t st = decode_job(c, q, workspace, workspace_bytes, n_split, &job);
+  if (st != PKV_OK) return st;
+  return dev_status(launch_partial(geom_of(c), job, (hipStream_t)stream));
+}
+
+int32_t pkv_decode_merge(const pkv_cache* c, const void* workspace, uint64_t workspace_bytes,
+                         int32_t n_split, float* out, void* stream) {
+  if (!out || !aligned(out, 16)) return PKV_ERR_INVALID_ARG;
+  AttnJob job;
+  int32_t st = decode_job(c, nullptr, (void*)workspace, workspace_bytes, n_split, &job);
+  if (st != PKV_OK) return st;
+  job.out = out;
+  return dev_status(launch_merge(geom_of(c), job, (hipStream_t)stream));
+}
+
+int32_t pkv_decode_attn(const pkv_cache* c, const void* q, float* out, void* workspace,
+                        uint64_t workspace_bytes, int32_t n_split, void* stream) {
+  if (!q || !out || !aligned(out, 16)) return PKV_ERR_INVALID_ARG;
+  AttnJob job;
+  int32_t st = decode_job(c, q, workspace, workspace_bytes, n_split, &job);
+  if (st != PKV_OK) return st;
+  job.out = out;
+  const CacheGeom g = geom_of(c);
+  hipError_t e = launch_partial(g, job, (hipStream_t)stream);
+  if (e == hipSuccess) e = launch_merge(g, job, (hipStream_t)stream);
+  return dev_status(e);
 }
 
 int32_t pkv_read_page_table(const pkv_cache* c, int32_t* cls, int32_t* slot, int64_t n,

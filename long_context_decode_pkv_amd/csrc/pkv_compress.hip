@@ -71,55 +71,43 @@ __device__ inline void store_gram_tile(float* Gs, int ta, int tb, floatx4 acc, i
   }
 }
 
-template <typename Elem>
-__device__ void gram(const Elem* X, int trans, float* Gs, int lane) {
+// 8 consecutive channels c0.. of page row `row` as a bf16 MFMA operand.
+__device__ inline bf16x8 row8(const uint16_t* X, int trans, int row, int c0) {
+  if (!trans) return __builtin_bit_cast(bf16x8, *(const uint4*)(X + row * kD + c0));
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(__bf16, X[(c0 + e) * kP + row]);
+  return v;
+}
+
+// The 10 upper 16x16 tiles of G = X X^T, spread over the page's waves.
+template <typename Elem, int WPP>
+__device__ void gram(const Elem* X, int trans, float* Gs, int lane, int wv) {
   const int i = lane & 15, q = lane >> 4;
-  if constexpr (sizeof(Elem) == 2) {
-    for (int ta = 0; ta < 4; ++ta) {
-      bf16x8 a[4];
+  for (int tile = wv; tile < 10; tile += WPP) {
+    // tile -> (ta, tb), ta <= tb
+    int ta = 0, rem = tile;
+    while (rem >= 4 - ta) {
+      rem -= 4 - ta;
+      ++ta;
+    }
+    const int tb = ta + rem;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (sizeof(Elem) == 2) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int row = 16 * ta + i, c0 = 32 * ks + 8 * q;
-        if (!trans) {
-          uint4 raw = *(const uint4*)(X + row * kD + c0);
-          a[ks] = __builtin_bit_cast(bf16x8, raw);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) a[ks][e] = __builtin_bit_cast(__bf16, X[(c0 + e) * kP + row]);
-        }
+        const bf16x8 av = row8(X, trans, 16 * ta + i, 32 * ks + 8 * q);
+        const bf16x8 bv = row8(X, trans, 16 * tb + i, 32 * ks + 8 * q);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
       }
-      for (int tb = ta; tb < 4; ++tb) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          bf16x8 bop;
-          const int row = 16 * tb + i, c0 = 32 * ks + 8 * q;
-          if (tb == ta) {
-            bop = a[ks];
-          } else if (!trans) {
-            uint4 raw = *(const uint4*)(X + row * kD + c0);
-            bop = __builtin_bit_cast(bf16x8, raw);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bop[e] = __builtin_bit_cast(__bf16, X[(c0 + e) * kP + row]);
-          }
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bop, acc, 0, 0, 0);
-        }
-        store_gram_tile(Gs, ta, tb, acc, lane);
+    } else {
+      for (int kc = 0; kc < kD / 4; ++kc) {
+        const float av = page_elem(X, trans, 16 * ta + i, 4 * kc + q);
+        const float bv = page_elem(X, trans, 16 * tb + i, 4 * kc + q);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
       }
     }
-  } else {
-    for (int ta = 0; ta < 4; ++ta) {
-      for (int tb = ta; tb < 4; ++tb) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int kc = 0; kc < kD / 4; ++kc) {
-          const float av = page_elem(X, trans, 16 * ta + i, 4 * kc + q);
-          const float bv = page_elem(X, trans, 16 * tb + i, 4 * kc + q);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
-        }
-        store_gram_tile(Gs, ta, tb, acc, lane);
-      }
-    }
+    store_gram_tile(Gs, ta, tb, acc, lane);
   }
 }
 
@@ -134,75 +122,160 @@ __device__ inline void rr_pair(int t, int k, int& p, int& qq) {
   }
 }
 
-__device__ void jacobi(float* Gs, float* Vs, int lane) {
-  // trace -> absolute floor for off-diagonal entries
-  float tr = Gs[lane * kLd + lane];
+struct JacobiShared {
+  float c[32], s[32];
+  float trace;
+  int any[2];  // a rotation happened in the sweep of this parity
+};
+
+// Advance a circle-method index to the next round: every index below 63
+// moves to the next seat (mod 63), index 63 stays.
+__device__ inline int rr_next(int x) { return x == 63 ? 63 : (x == 62 ? 0 : x + 1); }
+
+// Cyclic Jacobi on G (in LDS), accumulating the rotations into V.  Each round
+// rotates the 32 disjoint pairs of the circle-method schedule.  G <- J^T G J
+// is applied block by block: the 2x2 block at (pair i, pair j) is read once,
+// rotated on both sides and written once; V <- V J in the same pass.  Each
+// thread gathers all operands of its blocks before rotating, so the LDS reads
+// pipeline.  A thread's blocks keep their pair numbers across rounds; their
+// row/column indices advance one seat per round.  Two barriers per round and
+// one sweep-level convergence test.
+template <int WPP>
+__device__ void jacobi(float* Gs, float* Vs, JacobiShared& sh, int lane, int wv) {
+  constexpr int NT = 64 * WPP;
+  constexpr int NB = 1024 / NT;  // G blocks per thread per round
+  constexpr int NV = 2048 / NT;  // V (row, pair) updates per thread per round
+  const int tid = wv * 64 + lane;
+  if (wv == 0) {
+    float tr = Gs[lane * kLd + lane];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) tr += __shfl_xor(tr, o);
-  const float tol_abs = tr * 0x1p-30f;
+    for (int o = 32; o >= 1; o >>= 1) tr += __shfl_xor(tr, o);
+    if (lane == 0) {
+      sh.trace = tr;
+      sh.any[0] = 0;
+      sh.any[1] = 0;
+    }
+  }
+  __syncthreads();
+  const float tol_abs = sh.trace * 0x1p-30f;
   const float tol_rel = 0x1p-23f;
 
   for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
-    int rotated_any = 0;
+    // indices at round 0 of the sweep
+    int pa = 0, qa = 0;  // phase-A pair (threads < 32)
+    if (tid < 32) rr_pair(0, tid, pa, qa);
+    int bpi[NB], bqi[NB], bpj[NB], bqj[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int blk = tid + NT * u;
+      rr_pair(0, blk >> 5, bpi[u], bqi[u]);
+      rr_pair(0, blk & 31, bpj[u], bqj[u]);
+    }
+    int vp_[NV], vq_[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) rr_pair(0, (tid + NT * u) >> 6, vp_[u], vq_[u]);
+
     for (int t = 0; t < 63; ++t) {
-      // phase A: lane k < 32 owns pair k
-      float c = 1.f, s = 0.f;
-      int p = 0, qq = 0;
-      bool rot = false;
-      if (lane < 32) {
-        rr_pair(t, lane, p, qq);
-        const float app = Gs[p * kLd + p], aqq = Gs[qq * kLd + qq], apq = Gs[p * kLd + qq];
+      // phase A: thread k < 32 owns pair k
+      if (tid < 32) {
+        const float app = Gs[pa * kLd + pa], aqq = Gs[qa * kLd + qa], apq = Gs[pa * kLd + qa];
         const float thr = fmaxf(tol_rel * sqrtf(fabsf(app * aqq)), tol_abs);
+        float c = 1.f, s = 0.f;
         if (fabsf(apq) > thr) {
           const float tau = (aqq - app) / (2.f * apq);
           const float tt = copysignf(1.f, tau) / (fabsf(tau) + sqrtf(1.f + tau * tau));
           c = 1.f / sqrtf(1.f + tt * tt);
           s = tt * c;
-          rot = true;
+          sh.any[sweep & 1] = 1;
+        }
+        sh.c[tid] = c;
+        sh.s[tid] = s;
+      }
+      __syncthreads();
+      // every thread has read the previous sweep's flag by now: reset the
+      // flag the next sweep will use
+      if (t == 0 && tid == 0) sh.any[(sweep + 1) & 1] = 0;
+      // G <- J^T G J over this thread's 2x2 blocks (pair i, pair j)
+      {
+        float g[NB][4];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          g[u][0] = Gs[bpi[u] * kLd + bpj[u]];
+          g[u][1] = Gs[bpi[u] * kLd + bqj[u]];
+          g[u][2] = Gs[bqi[u] * kLd + bpj[u]];
+          g[u][3] = Gs[bqi[u] * kLd + bqj[u]];
+        }
+        float vp[NV], vq[NV];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const int row = ((tid + NT * u) & 63) * kLd;
+          vp[u] = Vs[row + vp_[u]];
+          vq[u] = Vs[row + vq_[u]];
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const int blk = tid + NT * u;
+          const int i = blk >> 5, j = blk & 31;
+          const float c1 = sh.c[i], s1 = sh.s[i], c2 = sh.c[j], s2 = sh.s[j];
+          // rows (J^T .): [p; q] <- [c p - s q; s p + c q]
+          const float A = c1 * g[u][0] - s1 * g[u][2], Bv = c1 * g[u][1] - s1 * g[u][3];
+          const float C = s1 * g[u][0] + c1 * g[u][2], D = s1 * g[u][1] + c1 * g[u][3];
+          // columns (. J)
+          Gs[bpi[u] * kLd + bpj[u]] = c2 * A - s2 * Bv;
+          Gs[bpi[u] * kLd + bqj[u]] = s2 * A + c2 * Bv;
+          Gs[bqi[u] * kLd + bpj[u]] = c2 * C - s2 * D;
+          Gs[bqi[u] * kLd + bqj[u]] = s2 * C + c2 * D;
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const int idx = tid + NT * u;
+          const int row = (idx & 63) * kLd, j = idx >> 6;
+          const float c = sh.c[j], s = sh.s[j];
+          Vs[row + vp_[u]] = c * vp[u] - s * vq[u];
+          Vs[row + vq_[u]] = s * vp[u] + c * vq[u];
         }
       }
-      const unsigned long long mask = __ballot(rot);
-      if (mask == 0ull) continue;  // uniform: nothing to rotate this round
-      rotated_any = 1;
       __syncthreads();
-      // phase B: G <- G J and V <- V J (columns p, q); lane = row
-#pragma unroll 4
-      for (int k = 0; k < 32; ++k) {
-        const float ck = lane_value(c, k), sk = lane_value(s, k);
-        int pk, qk;
-        rr_pair(t, k, pk, qk);
-        const float gp = Gs[lane * kLd + pk], gq = Gs[lane * kLd + qk];
-        Gs[lane * kLd + pk] = ck * gp - sk * gq;
-        Gs[lane * kLd + qk] = sk * gp + ck * gq;
-        const float vp = Vs[lane * kLd + pk], vq = Vs[lane * kLd + qk];
-        Vs[lane * kLd + pk] = ck * vp - sk * vq;
-        Vs[lane * kLd + qk] = sk * vp + ck * vq;
+      // a rotation annihilates its pair's off-diagonal exactly; the next
+      // round's phase A reads other entries and its barrier orders these
+      if (tid < 32 && sh.s[tid] != 0.f) {
+        Gs[pa * kLd + qa] = 0.f;
+        Gs[qa * kLd + pa] = 0.f;
       }
-      __syncthreads();
-      // phase C: G <- J^T G (rows p, q); lane = column
-#pragma unroll 4
-      for (int k = 0; k < 32; ++k) {
-        const float ck = lane_value(c, k), sk = lane_value(s, k);
-        int pk, qk;
-        rr_pair(t, k, pk, qk);
-        const float gp = Gs[pk * kLd + lane], gq = Gs[qk * kLd + lane];
-        Gs[pk * kLd + lane] = ck * gp - sk * gq;
-        Gs[qk * kLd + lane] = sk * gp + ck * gq;
+      // next round's indices
+      pa = rr_next(pa);
+      qa = rr_next(qa);
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        bpi[u] = rr_next(bpi[u]);
+        bqi[u] = rr_next(bqi[u]);
+        bpj[u] = rr_next(bpj[u]);
+        bqj[u] = rr_next(bqj[u]);
       }
-      __syncthreads();
-      if (rot) {  // the rotation annihilates the pair's off-diagonal exactly
-        Gs[p * kLd + qq] = 0.f;
-        Gs[qq * kLd + p] = 0.f;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        vp_[u] = rr_next(vp_[u]);
+        vq_[u] = rr_next(vq_[u]);
       }
-      __syncthreads();
     }
-    if (!rotated_any) break;
+    __syncthreads();
+    if (!sh.any[sweep & 1]) break;
   }
 }
 
-template <typename Elem>
-__device__ void compress_one(const CompressJob& job, int64_t n, float* Gs, float* Vs, int* sel,
-                             float* sig, int lane) {
+struct CompressShared {
+  float G[kP * kLd];
+  float V[kP * kLd];
+  JacobiShared js;
+  int sel[kP];
+  float sig2[16][kP];
+  float sig[kP];
+};
+
+template <typename Elem, int WPP>
+__device__ void compress_one(const CompressJob& job, int64_t n, CompressShared& sh, int lane,
+                             int wv) {
+  const int tid = wv * 64 + lane;
   const int kind = (int)(n % job.n_kind);
   const int64_t f = (n / job.n_kind) % job.n_f;
   const int64_t bh = n / ((int64_t)job.n_kind * job.n_f);
@@ -211,70 +284,90 @@ __device__ void compress_one(const CompressJob& job, int64_t n, float* Gs, float
   const int r = job.rank[kind];
 
   // 1. Gram matrix, eigenvector accumulator = I
-  gram<Elem>(X, trans, Gs, lane);
-  for (int j = 0; j < kP; ++j) Vs[j * kLd + lane] = (j == lane) ? 1.f : 0.f;
+  gram<Elem, WPP>(X, trans, sh.G, lane, wv);
+  for (int idx = tid; idx < kP * kP; idx += 64 * WPP) {
+    const int j = idx / kP, c = idx % kP;
+    sh.V[j * kLd + c] = (j == c) ? 1.f : 0.f;
+  }
   __syncthreads();
 
   // 2. Jacobi eigen-solve
-  jacobi(Gs, Vs, lane);
-  __syncthreads();
+  jacobi<WPP>(sh.G, sh.V, sh.js, lane, wv);
 
-  // 3. top-r selection: rank of lane's eigenvalue (descending, ties by index)
-  {
-    const float lam = Gs[lane * kLd + lane];
+  // 3. top-r selection: rank of each eigenvalue (descending, ties by index)
+  if (wv == 0) {
+    const float lam = sh.G[lane * kLd + lane];
     int rank = 0;
     for (int y = 0; y < kP; ++y) {
-      const float ly = Gs[y * kLd + y];
+      const float ly = sh.G[y * kLd + y];
       rank += (ly > lam || (ly == lam && y < lane)) ? 1 : 0;
     }
-    sel[rank] = lane;
+    sh.sel[rank] = lane;
   }
   __syncthreads();
 
-  // R = Q_r^T X in fp32 on the matrix cores, 16 ranks x 16 channels per tile.
+  // R = Q_r^T X in fp32 on the matrix cores; each wave takes 8 / WPP of the
+  // 16-channel column tiles, all 16-rank row tiles
+  constexpr int MC = 8 / WPP;
   const int ci = lane & 15, q = lane >> 4;
   const int RT16 = (r + 15) / 16;
-  floatx4 R[4][8];
+  floatx4 R[4][MC];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
-    for (int mc = 0; mc < 8; ++mc) R[mi][mc] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < MC; ++m) R[mi][m] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
+  int colsel[4];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
-    if (mi >= RT16) break;
     const int irow = 16 * mi + ci;
-    const int col = irow < r ? sel[irow] : -1;
-    for (int kc = 0; kc < kP / 4; ++kc) {
-      const int j = 4 * kc + q;
-      const float av = col >= 0 ? Vs[j * kLd + col] : 0.f;
+    colsel[mi] = irow < r ? sh.sel[irow] : -1;
+  }
+  // X operands of a reduction step are loaded once and reused by every rank tile
+#pragma unroll 2
+  for (int kc = 0; kc < kP / 4; ++kc) {
+    const int j = 4 * kc + q;
+    float bv[MC];
 #pragma unroll
-      for (int mc = 0; mc < 8; ++mc) {
-        const float bv = page_elem(X, trans, j, 16 * mc + ci);
-        R[mi][mc] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, R[mi][mc], 0, 0, 0);
+    for (int m = 0; m < MC; ++m) bv[m] = page_elem(X, trans, j, 16 * (wv * MC + m) + ci);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      if (mi < RT16) {
+        const float av = colsel[mi] >= 0 ? sh.V[j * kLd + colsel[mi]] : 0.f;
+#pragma unroll
+        for (int m = 0; m < MC; ++m)
+          R[mi][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[m], R[mi][m], 0, 0, 0);
       }
     }
   }
-  // sigma_i = ||R_i||: lane (ci, q) holds rows 16 mi + 4 q + v, columns 16 mc + ci
+  // sigma_i^2 = sum over channels of R_i^2: lane (ci, q) holds rows
+  // 16 mi + 4 q + v of its wave's channel tiles
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
-    if (mi >= RT16) break;
+    if (mi < RT16) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float ss = 0.f;
+      for (int v = 0; v < 4; ++v) {
+        float ss = 0.f;
 #pragma unroll
-      for (int mc = 0; mc < 8; ++mc) ss += R[mi][mc][v] * R[mi][mc][v];
+        for (int m = 0; m < MC; ++m) ss += R[mi][m][v] * R[mi][m][v];
 #pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-      const int i = 16 * mi + 4 * q + v;
-      if (ci == 0 && i < kP) sig[i] = sqrtf(ss);
+        for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+        if (ci == 0) sh.sig2[wv][16 * mi + 4 * q + v] = ss;
+      }
     }
+  }
+  __syncthreads();
+  if (tid < kP) {
+    float ss = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPP; ++w) ss += sh.sig2[w][tid];
+    sh.sig[tid] = sqrtf(ss);
   }
   __syncthreads();
 
   // 4. store Rf = R / sigma and Lf = Q diag(sigma)
   const bool packed = job.fac != nullptr;
-  PackDims pd = pack_dims(r);
+  const PackDims pd = pack_dims(r);
   const int r_store = packed ? 8 * pd.n8 : r;
   uint8_t* part = nullptr;
   if (packed)
@@ -282,50 +375,57 @@ __device__ void compress_one(const CompressJob& job, int64_t n, float* Gs, float
            (int64_t)kind * job.k_part_bytes;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
-    if (16 * mi >= r_store) break;
+    if (16 * mi < r_store) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int i = 16 * mi + 4 * q + v;
-      if (i >= r_store) continue;
-      const float sg = i < r ? sig[i] : 0.f;
-      const float inv = sg > 0.f ? 1.f / sg : 0.f;
+      for (int v = 0; v < 4; ++v) {
+        const int i = 16 * mi + 4 * q + v;
+        if (i < r_store) {
+          const float sg = i < r ? sh.sig[i] : 0.f;
+          const float inv = sg > 0.f ? 1.f / sg : 0.f;
 #pragma unroll
-      for (int mc = 0; mc < 8; ++mc) {
-        const int c = 16 * mc + ci;
-        const float val = (i < r) ? R[mi][mc][v] * inv : 0.f;
-        int64_t idx;
-        if (!packed) idx = n * (int64_t)r * kD + (int64_t)i * kD + c;
-        else idx = (kind == 0) ? off_rf_k(pd, i, c) : off_rf_v(pd, i, c);
-        store_elem(packed ? (void*)part : job.rf, idx, job.out_dtype, val);
+          for (int m = 0; m < MC; ++m) {
+            const int c = 16 * (wv * MC + m) + ci;
+            const float val = (i < r) ? R[mi][m][v] * inv : 0.f;
+            int64_t idx;
+            if (!packed) idx = n * (int64_t)r * kD + (int64_t)i * kD + c;
+            else idx = (kind == 0) ? off_rf_k(pd, i, c) : off_rf_v(pd, i, c);
+            store_elem(packed ? (void*)part : job.rf, idx, job.out_dtype, val);
+          }
+        }
       }
     }
   }
-  for (int i = 0; i < r_store; ++i) {
+  for (int i = wv; i < r_store; i += WPP) {
     const int j = lane;  // page row
     float val = 0.f;
     if (i < r) {
-      const float sg = sig[i];
-      val = sg > 0.f ? Vs[j * kLd + sel[i]] * sg : 0.f;
+      const float sg = sh.sig[i];
+      val = sg > 0.f ? sh.V[j * kLd + sh.sel[i]] * sg : 0.f;
     }
     int64_t idx;
     if (!packed) idx = n * (int64_t)kP * r + (int64_t)j * r + i;
     else idx = (kind == 0) ? off_lf_k(pd, j, i) : off_lf_v(pd, j, i);
     store_elem(packed ? (void*)part : job.lf, idx, job.out_dtype, val);
   }
-  if (!packed && job.sigma != nullptr && lane < r) job.sigma[n * r + lane] = sig[lane];
+  if (!packed && job.sigma != nullptr && tid < r) job.sigma[n * r + tid] = sh.sig[tid];
   __syncthreads();
 }
 
-template <typename Elem>
-__global__ __launch_bounds__(64) void compress_kernel(CompressJob job) {
-  __shared__ float Gs[kP * kLd];
-  __shared__ float Vs[kP * kLd];
-  __shared__ int sel[kP];
-  __shared__ float sig[kP];
-  const int lane = threadIdx.x;
+// Throughput mode (4 waves per page) is held to 128 VGPRs so that four pages
+// share a CU, as the LDS allows (measured: 507K pages/s at four pages per CU,
+// 448K at three, 332K at two, 181K at one, despite the spills this costs);
+// latency mode keeps the full register budget.
+template <typename Elem, int WPP>
+__global__ __launch_bounds__(64 * WPP, (WPP == 4 ? 4 : 1)) void compress_kernel(CompressJob job) {
+  __shared__ CompressShared sh;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   for (int64_t n = blockIdx.x; n < job.n_pages; n += gridDim.x)
-    compress_one<Elem>(job, n, Gs, Vs, sel, sig, lane);
+    compress_one<Elem, WPP>(job, n, sh, lane, wv);
 }
+
+// Few pages (a promotion): eight waves per page to cut latency.  Many pages
+// (prefill, batched compression): four waves per page, four pages per CU.
+constexpr int64_t kLatencyModePages = 512;
 
 }  // namespace
 
@@ -333,10 +433,14 @@ hipError_t launch_compress(const CompressJob& job, hipStream_t stream) {
   if (job.n_pages <= 0) return hipSuccess;
   const int64_t cap = 1 << 30;
   const unsigned grid = (unsigned)(job.n_pages < cap ? job.n_pages : cap);
-  if (job.in_dtype == PKV_BF16)
-    hipLaunchKernelGGL(compress_kernel<uint16_t>, dim3(grid), dim3(64), 0, stream, job);
-  else
-    hipLaunchKernelGGL(compress_kernel<float>, dim3(grid), dim3(64), 0, stream, job);
+  const bool few = job.n_pages <= kLatencyModePages;
+  if (job.in_dtype == PKV_BF16) {
+    if (few) hipLaunchKernelGGL((compress_kernel<uint16_t, 8>), dim3(grid), dim3(512), 0, stream, job);
+    else hipLaunchKernelGGL((compress_kernel<uint16_t, 4>), dim3(grid), dim3(256), 0, stream, job);
+  } else {
+    if (few) hipLaunchKernelGGL((compress_kernel<float, 8>), dim3(grid), dim3(512), 0, stream, job);
+    else hipLaunchKernelGGL((compress_kernel<float, 4>), dim3(grid), dim3(256), 0, stream, job);
+  }
   return hipGetLastError();
 }
 

@@ -7,8 +7,10 @@
 //     s = (q Rf_K^T) Lf_K^T / sqrt(d),   o = (e^(s - m) Lf_V) Rf_V,
 // so no page is ever reconstructed.  States are merged by the FlashAttention
 // reduction (Eq. 5): within a wavefront as pages stream by, across the
-// wavefronts of a workgroup in LDS, and across workgroups (splits) by the
-// last workgroup of each (sequence, KV head) to finish.
+// wavefronts of a workgroup in LDS, and across workgroups (splits) in a small
+// second kernel (the kernel boundary orders the partial states across the
+// 8 XCDs, which an in-kernel device-scope fence per workgroup did at a far
+// higher cost).
 //
 // bf16 path (decode_mfma_kernel): one wavefront owns a contiguous run of pages
 // of one (sequence, KV head) and all G <= 8 query heads of that KV head.  All
@@ -41,8 +43,6 @@ struct DecodeArgs {
   const int32_t* table;
   float* ws_o;
   float* ws_ml;
-  int32_t* counters;  // [B * H_kv], zero between calls
-  float* out;
   int B, Hkv, G, n_split;
   int n_s, n_w;
   int r_k, r_v;
@@ -90,23 +90,31 @@ __device__ inline float ror8(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, true));
 }
 
-// bf16 part of x on lanes whose column is < 8, bf16 remainder on the others.
-__device__ inline __bf16 split_bf16(float x, bool lo) {
-  const __bf16 hi = (__bf16)x;
-  const __bf16 rem = (__bf16)(x - (float)hi);
-  return lo ? rem : hi;
+// bf16 part of x on lanes whose column is < 8, bf16 remainder on the others:
+// rem_lane is 0 or 1 per lane; x - bf16(x) is exact (Sterbenz), so one FMA
+// and one rounding give either part without computing both.
+__device__ inline __bf16 split_bf16(float x, float rem_lane) {
+  const float h = (float)(__bf16)x;
+  return (__bf16)__builtin_fmaf(-rem_lane, h, x);
 }
+
+// 2^x on the transcendental unit (v_exp_f32); results below 2^-126 flush to
+// zero, which is harmless for softmax weights.
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-struct __attribute__((aligned(4))) U32x3 {
-  uint32_t x, y, z;
-};
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x3 __attribute__((ext_vector_type(3), aligned(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2), aligned(4)));
 
+// Streaming loads: factor and dense pages are read once per decode step, so
+// they are fetched non-temporally (measured ~13% more read bandwidth on
+// gfx950 than cached loads for this access pattern).
 __device__ inline bf16x8 ld16(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *(const uint4*)p);
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)p));
 }
 
 
@@ -119,22 +127,22 @@ struct RawW {
 template <int W>
 __device__ inline void ldraw(RawW<W>& r, const uint16_t* p) {
   if constexpr (W == 8) {
-    const uint4 v = *(const uint4*)p;
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
     r.d[0] = v.x;
     r.d[1] = v.y;
     r.d[2] = v.z;
     r.d[3] = v.w;
   } else if constexpr (W == 6) {
-    const U32x3 v = *(const U32x3*)p;
+    const u32x3 v = __builtin_nontemporal_load((const u32x3*)p);
     r.d[0] = v.x;
     r.d[1] = v.y;
     r.d[2] = v.z;
   } else if constexpr (W == 4) {
-    const uint2 v = *(const uint2*)p;
+    const u32x2 v = __builtin_nontemporal_load((const u32x2*)p);
     r.d[0] = v.x;
     r.d[1] = v.y;
   } else {
-    r.d[0] = *(const uint32_t*)p;
+    r.d[0] = __builtin_nontemporal_load((const uint32_t*)p);
   }
 }
 
@@ -254,7 +262,7 @@ struct SoftState {
 // Fold one page's 64 raw scores (MFMA output, hi/lo column halves not yet
 // summed) into the running state; returns the probability operand pb[2].
 __device__ inline void softmax_page(SoftState& st, const floatx4 (&acc)[4], int nvalid, int q4,
-                                    bool lo, bf16x8 (&pb)[2]) {
+                                    float rem, bf16x8 (&pb)[2]) {
   float s[4][4];
   float mx = -INFINITY;
 #pragma unroll
@@ -271,13 +279,13 @@ __device__ inline void softmax_page(SoftState& st, const floatx4 (&acc)[4], int 
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float m_new = fmaxf(st.m, mx);
-  const float alpha = exp2f(st.m - m_new);
+  const float alpha = fast_exp2(st.m - m_new);
   float ps = 0.f;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float p = exp2f(s[mt][v] - m_new);
+      const float p = fast_exp2(s[mt][v] - m_new);
       s[mt][v] = p;
       ps += p;
     }
@@ -291,13 +299,13 @@ __device__ inline void softmax_page(SoftState& st, const floatx4 (&acc)[4], int 
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pb[ks][e] = split_bf16(s[2 * ks + e / 4][e % 4], lo);
+    for (int e = 0; e < 8; ++e) pb[ks][e] = split_bf16(s[2 * ks + e / 4][e % 4], rem);
   }
 }
 
 // hi/lo-combined rank vector of rank tiles -> B operand slots.
 template <int N8>
-__device__ inline void rank_operand(const floatx4 (&acc)[FactDims<N8>::RT], bool lo,
+__device__ inline void rank_operand(const floatx4 (&acc)[FactDims<N8>::RT], float rem,
                                     bf16x8 (&out)[FactDims<N8>::KS2]) {
   using Dm = FactDims<N8>;
 #pragma unroll
@@ -307,7 +315,7 @@ __device__ inline void rank_operand(const floatx4 (&acc)[FactDims<N8>::RT], bool
       const int mt = 2 * ks + e / 4;
       float x = 0.f;
       if (mt < Dm::RT) x = acc[mt][e % 4] + ror8(acc[mt][e % 4]);
-      out[ks][e] = split_bf16(x, lo);
+      out[ks][e] = split_bf16(x, rem);
     }
   }
 }
@@ -316,7 +324,7 @@ __device__ inline void rank_operand(const floatx4 (&acc)[FactDims<N8>::RT], bool
 // the probability operand.
 template <int N8>
 __device__ inline void fact_keys(SoftState& st, const KRegs<N8>& R, const bf16x8 (&qb)[4], int q4,
-                                 bool lo, bf16x8 (&pb)[2]) {
+                                 float rem, bf16x8 (&pb)[2]) {
   using Dm = FactDims<N8>;
   floatx4 at[Dm::RT];
 #pragma unroll
@@ -326,7 +334,7 @@ __device__ inline void fact_keys(SoftState& st, const KRegs<N8>& R, const bf16x8
     for (int ks = 0; ks < 4; ++ks) at[mt] = mfma(R.k1[mt][ks], qb[ks], at[mt]);
   }
   bf16x8 tb[Dm::KS2];
-  rank_operand<N8>(at, lo, tb);
+  rank_operand<N8>(at, rem, tb);
   floatx4 as_[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
@@ -334,13 +342,13 @@ __device__ inline void fact_keys(SoftState& st, const KRegs<N8>& R, const bf16x8
 #pragma unroll
     for (int ks = 0; ks < Dm::KS2; ++ks) as_[mt] = mfma(R.k2(mt, ks), tb[ks], as_[mt]);
   }
-  softmax_page(st, as_, kP, q4, lo, pb);
+  softmax_page(st, as_, kP, q4, rem, pb);
 }
 
 // Eq. 4, value half: u = Lf_V^T p, o += Rf_V^T u.
 template <int N8>
 __device__ inline void fact_values(SoftState& st, const VRegs<N8>& R, const bf16x8 (&pb)[2],
-                                   bool lo) {
+                                   float rem) {
   using Dm = FactDims<N8>;
   floatx4 au[Dm::RT];
 #pragma unroll
@@ -350,7 +358,7 @@ __device__ inline void fact_values(SoftState& st, const VRegs<N8>& R, const bf16
     for (int ks = 0; ks < 2; ++ks) au[mt] = mfma(R.v1[mt][ks], pb[ks], au[mt]);
   }
   bf16x8 ub[Dm::KS2];
-  rank_operand<N8>(au, lo, ub);
+  rank_operand<N8>(au, rem, ub);
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
@@ -359,7 +367,7 @@ __device__ inline void fact_values(SoftState& st, const VRegs<N8>& R, const bf16
 }
 
 __device__ inline void dense_page(SoftState& st, const uint16_t* Kp, const uint16_t* Vt, int nvalid,
-                                  const bf16x8 (&qb)[4], int lane, bool lo) {
+                                  const bf16x8 (&qb)[4], int lane, float rem) {
   const int n = lane & 15, q4 = lane >> 4;
   // score tile rows follow the page-row order of the factor path
   floatx4 as_[4];
@@ -372,7 +380,7 @@ __device__ inline void dense_page(SoftState& st, const uint16_t* Kp, const uint1
       as_[mt] = mfma(ld16(Kp + j * kD + 32 * ks + 8 * q4), qb[ks], as_[mt]);
   }
   bf16x8 pb[2];
-  softmax_page(st, as_, nvalid, q4, lo, pb);
+  softmax_page(st, as_, nvalid, q4, rem, pb);
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
@@ -381,51 +389,23 @@ __device__ inline void dense_page(SoftState& st, const uint16_t* Kp, const uint1
   }
 }
 
-// Eq. 5 across splits.  Every workgroup publishes its (m, l, o) for the G
-// query heads of its (sequence, KV head), then counts itself in; the last one
-// to arrive merges all splits and writes the normalized output, and resets the
-// counter for the next call.  The fences order the partial-state stores and
-// loads at device scope (the 8 XCDs have separate L2 caches).
-__device__ void finish_splits(const DecodeArgs& a, int b, int h) {
-  __shared__ int last;
-  const int Hq = a.Hkv * a.G;
-  __threadfence();
-  __syncthreads();
-  int32_t* ctr = a.counters + (int64_t)b * a.Hkv + h;
-  if (threadIdx.x == 0) last = (atomicAdd(ctr, 1) == a.n_split - 1) ? 1 : 0;
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  for (int idx = threadIdx.x; idx < a.G * kD; idx += blockDim.x) {
-    const int gg = idx / kD, c = idx % kD;
-    const int64_t row = (int64_t)b * Hq + (int64_t)h * a.G + gg;
-    const float* ml = a.ws_ml + row * a.n_split * 2;
-    float M = -INFINITY;
-    for (int sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, __builtin_nontemporal_load(ml + 2 * sp));
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-      for (int sp = 0; sp < a.n_split; ++sp) {
-        const float wt = exp2f(__builtin_nontemporal_load(ml + 2 * sp) - M);
-        L += wt * __builtin_nontemporal_load(ml + 2 * sp + 1);
-        O += wt * __builtin_nontemporal_load(a.ws_o + (row * a.n_split + sp) * kD + c);
-      }
-    }
-    a.out[row * kD + c] = L > 0.f ? O / L : 0.f;
-  }
-  if (threadIdx.x == 0) atomicExch(ctr, 0);
-}
+constexpr int kMaxSplits = kMaxDecodeSplits;
 
 constexpr int kWaves = 4;
 
+// Waves per SIMD the matrix-core kernel is compiled for (register budget):
+// small ranks fit 3 (<= 168 VGPRs), the common ranks 2, the largest 1.
+constexpr int mfma_waves_per_simd(int n8) { return n8 <= 2 ? 3 : (n8 <= 6 ? 2 : 1); }
+
 template <int N8>
-__global__ __launch_bounds__(256, (N8 <= 6 ? 2 : 1)) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, mfma_waves_per_simd(N8)) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ float sm_o[kWaves][kMaxG][kD];
   __shared__ float sm_m[kWaves][kMaxG];
   __shared__ float sm_l[kWaves][kMaxG];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, q4 = lane >> 4;
-  const bool lo = n >= 8;
+  const float rem = n >= 8 ? 1.f : 0.f;  // remainder column
   const int g = n & 7;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int Hq = a.Hkv * a.G;
@@ -437,9 +417,10 @@ __global__ __launch_bounds__(256, (N8 <= 6 ? 2 : 1)) void decode_mfma_kernel(Dec
     const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)b * Hq + (int64_t)h * a.G + g) * kD;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 raw = g < a.G ? ld16(qp + 32 * ks + 8 * q4) : bf16x8{};
+      bf16x8 raw = g < a.G ? __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 32 * ks + 8 * q4))
+                           : bf16x8{};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qb[ks][e] = split_bf16((float)raw[e] * a.qscale, lo);
+      for (int e = 0; e < 8; ++e) qb[ks][e] = split_bf16((float)raw[e] * a.qscale, rem);
     }
   }
 
@@ -469,8 +450,8 @@ __global__ __launch_bounds__(256, (N8 <= 6 ? 2 : 1)) void decode_mfma_kernel(Dec
       Kp = (const uint16_t*)a.win_k + (bh * (a.n_w + 1) + slot) * ppg;
       Vt = (const uint16_t*)a.win_v + (bh * (a.n_w + 1) + slot) * ppg;
     }
-    const int64_t rem = a.T - p * kP;
-    dense_page(st, Kp, Vt, (int)(rem < kP ? rem : kP), qb, lane, lo);
+    const int64_t left = a.T - p * kP;
+    dense_page(st, Kp, Vt, (int)(left < kP ? left : kP), qb, lane, rem);
   }
 
   // factorized pages: the next page's key part streams in while this page's
@@ -489,11 +470,11 @@ __global__ __launch_bounds__(256, (N8 <= 6 ? 2 : 1)) void decode_mfma_kernel(Dec
     load_values<N8>(vr, (const uint16_t*)(pp + a.k_part_bytes), lane);
     for (; e < e1; ++e) {
       bf16x8 pb[2];
-      fact_keys<N8>(st, kr, qb, q4, lo, pb);
+      fact_keys<N8>(st, kr, qb, q4, rem, pb);
       const bool more = e + 1 < e1;
       const uint8_t* pn = more ? page_ptr(e + 1) : pp;
       if (more) load_keys<N8>(kr, (const uint16_t*)pn, lane);
-      fact_values<N8>(st, vr, pb, lo);
+      fact_values<N8>(st, vr, pb, rem);
       if (more) load_values<N8>(vr, (const uint16_t*)(pn + a.k_part_bytes), lane);
       pp = pn;
     }
@@ -538,7 +519,6 @@ __global__ __launch_bounds__(256, (N8 <= 6 ? 2 : 1)) void decode_mfma_kernel(Dec
       a.ws_ml[row * 2 + 1] = L;
     }
   }
-  finish_splits(a, b, h);
 }
 
 // ---------------------------------------------------------------------------
@@ -680,7 +660,47 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
       a.ws_ml[row * 2 + 1] = sh_l[g];
     }
   }
-  finish_splits(a, b, h);
+}
+
+// Eq. 5 across splits: one 64-lane workgroup per (sequence, query head).
+// The lanes read the split maxima and form the split weights e^(m_s - M) in
+// LDS, then lanes 0..31 accumulate 4 consecutive channels each over all
+// splits with 16-byte loads, several splits in flight at a time.
+__global__ __launch_bounds__(64) void merge_kernel(const float* ws_o, const float* ws_ml,
+                                                   float* out, int n_split) {
+  __shared__ float sh_w[kMaxSplits];
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float2* ml = (const float2*)(ws_ml + row * n_split * 2);
+  float M = -INFINITY;
+  for (int sp = lane; sp < n_split; sp += 64) M = fmaxf(M, ml[sp].x);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float L = 0.f;
+  for (int sp = lane; sp < n_split; sp += 64) {
+    const float2 v = ml[sp];
+    const float wt = M == -INFINITY ? 0.f : exp2f(v.x - M);  // empty split: weight 0
+    sh_w[sp] = wt;
+    L += wt * v.y;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  __syncthreads();
+  if (lane < kD / 4) {
+    const float4* op = (const float4*)(ws_o + row * n_split * kD) + lane;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int sp = 0; sp < n_split; ++sp) {
+      const float4 v = op[(int64_t)sp * (kD / 4)];
+      const float wt = sh_w[sp];
+      acc.x += wt * v.x;
+      acc.y += wt * v.y;
+      acc.z += wt * v.z;
+      acc.w += wt * v.w;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    ((float4*)(out + row * kD))[lane] = float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+  }
 }
 
 }  // namespace
@@ -689,7 +709,11 @@ int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact) {
   (void)n_fact;
   const int64_t pages = (T + kP - 1) / kP;
   const int64_t bh = (int64_t)g.B * g.Hkv;
-  int64_t s = (512 + bh - 1) / bh;        // about two workgroups per CU on 256 CUs
+  // one resident round: 256 CUs x (waves per SIMD) four-wave workgroups
+  const int n8 = (g.r_k > g.r_v ? g.r_k + 7 : g.r_v + 7) / 8;
+  const int64_t target = 256LL * (g.dtype == PKV_BF16 ? mfma_waves_per_simd(n8) : 2);
+  int64_t s = (target + bh - 1) / bh;
+  if (s > kMaxSplits) s = kMaxSplits;
   const int64_t cap = (pages + 3) / 4;    // at least ~4 pages per workgroup
   if (s > cap) s = cap;
   if (s < 1) s = 1;
@@ -697,7 +721,13 @@ int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact) {
   return (int)s;
 }
 
-hipError_t launch_decode(const CacheGeom& g, const AttnJob& job, hipStream_t stream) {
+hipError_t launch_merge(const CacheGeom& g, const AttnJob& job, hipStream_t stream) {
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((int64_t)g.B * g.Hq)), dim3(64), 0, stream,
+                     job.ws_o, job.ws_ml, job.out, job.n_split);
+  return hipGetLastError();
+}
+
+hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t stream) {
   DecodeArgs a;
   a.q = job.q;
   a.fac = g.base + g.lay.factors;
@@ -708,8 +738,6 @@ hipError_t launch_decode(const CacheGeom& g, const AttnJob& job, hipStream_t str
   a.table = (const int32_t*)(g.base + g.lay.page_table);
   a.ws_o = job.ws_o;
   a.ws_ml = job.ws_ml;
-  a.counters = job.counters;
-  a.out = job.out;
   a.B = g.B;
   a.Hkv = g.Hkv;
   a.G = g.G;

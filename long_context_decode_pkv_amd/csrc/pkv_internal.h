@@ -12,6 +12,7 @@ namespace pkv {
 constexpr int kP = 64;    // page length supported by the kernels
 constexpr int kD = 128;   // head dim supported by the kernels
 constexpr int kMaxG = 8;  // query heads per KV head handled by one wave
+constexpr int kMaxDecodeSplits = 512;  // workgroups per (sequence, KV head) in one decode
 
 // --------------------------------------------------------------------------
 // Packed factor part layout (P = 64, d = 128).
@@ -176,12 +177,12 @@ struct AttnJob {
   float* out;
   float* ws_o;   // [B*Hq][n_split][d]
   float* ws_ml;  // [B*Hq][n_split][2]
-  int32_t* counters;  // [B*Hkv], zero between calls
   int n_split;
   int64_t T, n_fact;
 };
 
-hipError_t launch_decode(const CacheGeom& g, const AttnJob& job, hipStream_t stream);
+hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t stream);
+hipError_t launch_merge(const CacheGeom& g, const AttnJob& job, hipStream_t stream);
 int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact);
 
 }  // namespace pkv

@@ -122,3 +122,39 @@ def test_decode_errors():
     assert ei.value.status == 3
     with pytest.raises(ValueError):
         cache.decode(q.float())
+
+
+def test_partial_states_and_merge():
+    """pkv_decode_partial leaves Eq. 4 states merged within each split: with
+    one split, o / l is the attention output and m the largest score in log2
+    units; partial + merge on several splits equals pkv_decode_attn."""
+    import math
+    import torch
+    require_gpu()
+    d = synth.decode_inputs(2, T=64 * 9 + 11, B=2, kv_heads=2, with_f64=True)
+    cache = make_cache(d)
+    cache.prefill(to_dev(d["K"], "bf16"), to_dev(d["V"], "bf16"))
+    q = to_dev(d["q"], "bf16")
+    B, Hq, G = d["B"], d["Hq"], d["G"]
+    ws = cache.decode_partial(q, n_split=1)
+    torch.cuda.synchronize()
+    rows = B * Hq
+    o = ws[: rows * 128 * 4].view(torch.float32).view(rows, 128).cpu().numpy().astype(np.float64)
+    off = -(-rows * 128 * 4 // 256) * 256
+    ml = ws[off: off + rows * 8].view(torch.float32).view(rows, 2).cpu().numpy().astype(np.float64)
+    ref = oracle.decode(d["q64"], d["K64"], d["V64"], d["T"], 64, 64, 128, 16, 16, "bf16")
+    np.testing.assert_allclose((o / ml[:, 1:2]).reshape(B, Hq, 128), ref["o_stored"],
+                               atol=1e-2 * np.abs(ref["o_stored"]).max())
+    # m: the largest score q.k/sqrt(d) over the cache, in log2 units
+    for b in range(B):
+        for hq in range(Hq):
+            h = hq // G
+            Ks, _, _ = oracle.reconstruct_cache(d["K64"][b, h], d["T"], 64, 64, 128, 16, "bf16")
+            smax = (Ks @ d["q64"][b, hq]).max() / math.sqrt(128) * math.log2(math.e)
+            assert abs(ml[b * Hq + hq, 0] - smax) <= 1e-2 * max(1.0, abs(smax))
+    full = to_f64(cache.decode(q, n_split=5))
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda:0")
+    ws = cache.decode_partial(q, n_split=5)
+    cache.decode_merge(out, n_split=5, workspace=ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_f64(out), full)
