@@ -32,6 +32,36 @@ HBM_PEAK_GBS = 8000.0
 CACHE_DIR = os.environ.get("PKV_BENCH_CACHE", "/tmp/pkv_bench_inputs")
 
 
+# HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc runs of
+# this script (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled
+# by what the same counter reads for the 1 GiB device copy of `--workload copy`
+# (FETCH_SIZE reads 524303.5 KiB for 2^30 bytes read -> x1.99994; WRITE_SIZE
+# reads 1048576 KiB for 2^30 bytes written -> x1.0).  A figure holds only for
+# the kernel sources whose hash it carries; any change to them makes it null.
+PMC_TRAFFIC = {
+    "qwen3-32b-layer-128k": {"sha256": "22ab3166c5553dbb3770a155eb9cb74cfb349d29f2333cc8676aed4b4157fefe",
+                             "fetch": 302998605, "write": 2228224},
+}
+TRAFFIC_SOURCES = ("long_context_decode_pkv_amd/csrc/pkv_decode.hip",
+                   "long_context_decode_pkv_amd/csrc/pkv_internal.h")
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def pmc_traffic(workload):
+    t = PMC_TRAFFIC.get(workload)
+    if not t or t["sha256"] is None or t["sha256"] != kernel_sources_sha256():
+        return None
+    return t
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -155,18 +185,14 @@ def bench_decode(args, cfg_id, name):
 
     def layer_step(c, ws, i, rec=None):
         if c.append(rows_k[i], rows_v[i]):
-            if rec is not None:
-                rec["promote"][0].record()
+            if rec is not None:  # the decomposition kernel's own duration
+                pkv.time_next_kernel(*rec["promote"])
                 rec["promoted"] = True
             c.promote()
-            if rec is not None:
-                rec["promote"][1].record()
         T, nf, _ = c.state()
-        if rec is not None:
-            rec["partial"][0].record()
+        if rec is not None:  # the partial kernel's own duration
+            pkv.time_next_kernel(*rec["partial"])
         c.decode_partial(qs[i], workspace=ws)
-        if rec is not None:
-            rec["partial"][1].record()
         c.decode_merge(out, workspace=ws)
         if rec is not None:
             rec["merge"][1].record()
@@ -178,6 +204,8 @@ def bench_decode(args, cfg_id, name):
     torch.cuda.synchronize()
     recs = [[{"partial": (ev(), ev()), "merge": (None, ev()), "promote": (ev(), ev())}
              for _ in range(NL)] for _ in range(args.steps)]
+    for e in (e for step in recs for r in step for pair in r.values() for e in pair if e is not None):
+        e.record()  # creates the event before the timed region
     states = []
     torch.cuda.synchronize()
     t = time.perf_counter()
@@ -193,8 +221,10 @@ def bench_decode(args, cfg_id, name):
     nbytes = np.array([decode_bytes(cfg, B, Hkv, Hq, T, nf) for T, nf in states], dtype=np.float64)
     achieved = nbytes.sum() / durs.sum() / 1e9
     layer_steps = args.steps * NL
+    traffic = pmc_traffic(name)
     log(f"partial kernel: mean {durs.mean() * 1e6:.2f} us (median {np.median(durs) * 1e6:.2f}), "
-        f"{nbytes.mean() / 1e6:.1f} MB -> {achieved:.0f} GB/s; merge {merges.mean() * 1e6:.2f} us; "
+        f"{nbytes.mean() / 1e6:.1f} MB -> {achieved:.0f} GB/s; partial end to merge end "
+        f"{merges.mean() * 1e6:.2f} us; "
         f"{len(promos)} promotions, mean {np.mean(promos) * 1e6 if promos else 0:.1f} us; "
         f"layer step {elapsed / layer_steps * 1e6:.1f} us")
 
@@ -217,11 +247,15 @@ def bench_decode(args, cfg_id, name):
                    "layer_caches_rotated": NL,
                    "step": "append + promote when due + decode partial + merge, per layer"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None if traffic is None else traffic["fetch"] + traffic["write"],
                      "kernel": "decode_mfma_kernel (pkv_decode_partial)",
                      "launch_us_mean": durs.mean() * 1e6,
-                     "bytes_per_launch": float(nbytes.mean())},
-        "breakdown_us": {"decode_partial": durs.mean() * 1e6, "decode_merge_incl_gap": merges.mean() * 1e6,
+                     "bytes_per_launch": float(nbytes.mean()),
+                     "traffic_read_write": None if traffic is None else [traffic["fetch"],
+                                                                         traffic["write"]]},
+        "breakdown_us": {"decode_partial": durs.mean() * 1e6,
+                         "partial_end_to_merge_end": merges.mean() * 1e6,
                          "promote_mean": float(np.mean(promos) * 1e6) if promos else None,
                          "promotions": len(promos)},
         "decode_effective_GBps": achieved,
@@ -258,6 +292,7 @@ def bench_compress(args):
     X = Xp.repeat((n_total + n_distinct - 1) // n_distinct, 1, 1)[:n_total].contiguous()
     del Xp
     results = {}
+    steps = max(1, min(args.steps, 4))  # one launch is about a second
     for r in cfg["ranks"]:
         Lf = torch.empty((n_total, 64, r), dtype=torch.bfloat16, device="cuda:0")
         Rf = torch.empty((n_total, r, 128), dtype=torch.bfloat16, device="cuda:0")
@@ -266,22 +301,26 @@ def bench_compress(args):
                                          Lf.data_ptr(), Rf.data_ptr(), None,
                                          torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(args.steps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        for a, b in evs:
+            pkv.time_next_kernel(a, b)  # the kernel's own duration
             st = pkv.lib().pkv_compress_pages(X.data_ptr(), n_total, 64, 128, r, 0, 0, Lf.data_ptr(),
                                               Rf.data_ptr(), None,
                                               torch.cuda.current_stream().cuda_stream)
             assert st == 0
-        b.record()
         torch.cuda.synchronize()
-        t = a.elapsed_time(b) * 1e-3 / args.steps
+        t = sum(a.elapsed_time(b) for a, b in evs) * 1e-3 / steps
         results[r] = n_total / t
         log(f"compress r={r}: {t * 1e3:.1f} ms per {n_total} pages -> {n_total / t:.3e} pages/s")
     r0 = cfg["ranks"][1]
     return {
         "metric": "pages compressed/s (batched page decomposition)",
-        "value": results[r0], "unit": "pages/s", "n_gpus": 1, "steps": args.steps,
+        "value": results[r0], "unit": "pages/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": n_total / results[r0] * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in/out, f32 eigen-solve",
         "data": f"synthetic: {n_distinct} distinct seeded pages tiled to {n_total}",
@@ -290,13 +329,35 @@ def bench_compress(args):
     }
 
 
+def bench_copy(args):
+    """Plain device-to-device copy of a known size: the reference that scales
+    the HBM traffic counters (FETCH_SIZE, WRITE_SIZE) read under rocprofv3."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) * 1e-3 / args.steps
+    return {"metric": "device copy bandwidth (counter calibration)", "value": 2 * n / t / 1e9,
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": 0, "ms_per_step": t * 1e3,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+            "data": "synthetic", "config": {"workload": "copy", "bytes_read_per_copy": n,
+                                            "bytes_written_per_copy": n}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="qwen3-32b-layer-128k",
-                    choices=["qwen3-32b-layer-128k", "llama3.1-8b-layer", "compress"])
+                    choices=["qwen3-32b-layer-128k", "llama3.1-8b-layer", "compress", "copy"])
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--workers", type=int, default=1)
     ap.add_argument("--layers", type=int, default=4,
@@ -317,6 +378,8 @@ def main():
     pkv.lib()
     if args.workload == "compress":
         res = bench_compress(args)
+    elif args.workload == "copy":
+        res = bench_copy(args)
     elif args.workload == "llama3.1-8b-layer":
         res = bench_decode(args, 2, args.workload)
     else:

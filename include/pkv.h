@@ -248,6 +248,20 @@ int32_t pkv_decode_merge(const pkv_cache* cache, const void* workspace, uint64_t
 int32_t pkv_read_page_table(const pkv_cache* cache, int32_t* cls, int32_t* slot, int64_t n,
                             void* stream);
 
+/* Kernel timing (measurement only; no passage of the method).
+ *
+ * start_event, stop_event: hipEvent_t handles (as void*) that the caller
+ * created with timing enabled and owns.  The next launch, on this host thread,
+ * of a decode-partial kernel (pkv_decode_partial, pkv_decode_attn) or of a
+ * page-decomposition kernel (pkv_compress_pages, pkv_prefill,
+ * pkv_promote_page) records start_event when that kernel begins executing
+ * and stop_event when it ends, so hipEventElapsedTime gives the kernel's own
+ * duration without the launch gaps around it.  The request is then cleared;
+ * a call that launches no such kernel leaves it pending.  Both NULL clears a
+ * pending request.  Not for use under stream capture.
+ * Errors: PKV_ERR_INVALID_ARG if exactly one handle is NULL (nothing set). */
+int32_t pkv_time_next_kernel(void* start_event, void* stop_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -83,6 +83,7 @@ def lib():
         "pkv_decode_partial": ([vp, vp, vp, u64, i32, vp], i32),
         "pkv_decode_merge": ([vp, vp, u64, i32, vp, vp], i32),
         "pkv_read_page_table": ([vp, vp, vp, i64, vp], i32),
+        "pkv_time_next_kernel": ([vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -123,6 +124,21 @@ def _dev_ptr(t, dtype_code=None, what="tensor"):
     if dtype_code is not None and _dtype_code(t.dtype) != dtype_code:
         raise ValueError(f"{what} has dtype {t.dtype}, cache dtype differs")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def time_next_kernel(start=None, stop=None):
+    """Bracket the next decode-partial or page-decomposition kernel that this
+    thread launches with two timing events (torch.cuda.Event with
+    enable_timing=True): afterwards start.elapsed_time(stop) is that kernel's
+    own execution time.  No arguments clears a pending request."""
+    if start is None and stop is None:
+        _check(lib().pkv_time_next_kernel(None, None), "pkv_time_next_kernel")
+        return
+    for e in (start, stop):
+        if not e.cuda_event:  # torch creates the event at its first record
+            e.record()
+    _check(lib().pkv_time_next_kernel(ctypes.c_void_p(start.cuda_event),
+                                      ctypes.c_void_p(stop.cuda_event)), "pkv_time_next_kernel")
 
 
 # ------------------------------------------------------------------ host-only

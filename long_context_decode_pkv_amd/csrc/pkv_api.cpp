@@ -26,6 +26,8 @@ struct pkv_cache {
 
 namespace {
 
+thread_local KernelEvents t_kernel_events;
+
 constexpr uint64_t kAlign = 256;
 
 uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -125,6 +127,14 @@ float bf16_round_host(float x, uint16_t* bits) {
 }
 
 }  // namespace
+
+namespace pkv {
+KernelEvents take_kernel_events() {
+  const KernelEvents e = t_kernel_events;
+  t_kernel_events = KernelEvents{};
+  return e;
+}
+}  // namespace pkv
 
 extern "C" {
 
@@ -492,6 +502,13 @@ int32_t pkv_read_page_table(const pkv_cache* c, int32_t* cls, int32_t* slot, int
     slot[p] = table_slot(tmp[p]);
   }
   delete[] tmp;
+  return PKV_OK;
+}
+
+int32_t pkv_time_next_kernel(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return PKV_ERR_INVALID_ARG;
+  t_kernel_events.start = (hipEvent_t)start_event;
+  t_kernel_events.stop = (hipEvent_t)stop_event;
   return PKV_OK;
 }
 

@@ -434,12 +434,21 @@ hipError_t launch_compress(const CompressJob& job, hipStream_t stream) {
   const int64_t cap = 1 << 30;
   const unsigned grid = (unsigned)(job.n_pages < cap ? job.n_pages : cap);
   const bool few = job.n_pages <= kLatencyModePages;
+  const KernelEvents ev = take_kernel_events();
   if (job.in_dtype == PKV_BF16) {
-    if (few) hipLaunchKernelGGL((compress_kernel<uint16_t, 8>), dim3(grid), dim3(512), 0, stream, job);
-    else hipLaunchKernelGGL((compress_kernel<uint16_t, 4>), dim3(grid), dim3(256), 0, stream, job);
+    if (few)
+      hipExtLaunchKernelGGL((compress_kernel<uint16_t, 8>), dim3(grid), dim3(512), 0, stream, ev.start,
+                            ev.stop, 0, job);
+    else
+      hipExtLaunchKernelGGL((compress_kernel<uint16_t, 4>), dim3(grid), dim3(256), 0, stream, ev.start,
+                            ev.stop, 0, job);
   } else {
-    if (few) hipLaunchKernelGGL((compress_kernel<float, 8>), dim3(grid), dim3(512), 0, stream, job);
-    else hipLaunchKernelGGL((compress_kernel<float, 4>), dim3(grid), dim3(256), 0, stream, job);
+    if (few)
+      hipExtLaunchKernelGGL((compress_kernel<float, 8>), dim3(grid), dim3(512), 0, stream, ev.start,
+                            ev.stop, 0, job);
+    else
+      hipExtLaunchKernelGGL((compress_kernel<float, 4>), dim3(grid), dim3(256), 0, stream, ev.start,
+                            ev.stop, 0, job);
   }
   return hipGetLastError();
 }

@@ -757,12 +757,13 @@ hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t st
   a.qscale = kLog2e / sqrtf((float)kD);
 
   const dim3 grid(job.n_split, g.Hkv, g.B);
+  const KernelEvents ev = take_kernel_events();
   const int n8k = (g.r_k + 7) / 8, n8v = (g.r_v + 7) / 8;
   if (g.dtype == PKV_BF16 && n8k == n8v) {
     switch (n8k) {
 #define PKV_CASE(N)                                                                 \
   case N:                                                                           \
-    hipLaunchKernelGGL(decode_mfma_kernel<N>, grid, dim3(256), 0, stream, a); \
+    hipExtLaunchKernelGGL(decode_mfma_kernel<N>, grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a); \
     break;
       PKV_CASE(1)
       PKV_CASE(2)
@@ -777,9 +778,9 @@ hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t st
         return hipErrorInvalidValue;
     }
   } else if (g.dtype == PKV_BF16) {
-    hipLaunchKernelGGL(decode_valu_kernel<uint16_t>, grid, dim3(256), 0, stream, a);
+    hipExtLaunchKernelGGL(decode_valu_kernel<uint16_t>, grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a);
   } else {
-    hipLaunchKernelGGL(decode_valu_kernel<float>, grid, dim3(256), 0, stream, a);
+    hipExtLaunchKernelGGL(decode_valu_kernel<float>, grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a);
   }
   return hipGetLastError();
 }

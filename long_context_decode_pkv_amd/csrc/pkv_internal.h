@@ -2,6 +2,7 @@
 // C-ABI).  Host and device code both include this header.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -152,6 +153,14 @@ struct CompressJob {
   void* rf;
   float* sigma;
 };
+
+// Events the caller asked to bracket the next decode-partial or page
+// decomposition kernel with (pkv_time_next_kernel).  Taking them clears the
+// request; both are null when none is pending.
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+KernelEvents take_kernel_events();
 
 hipError_t launch_compress(const CompressJob& job, hipStream_t stream);
 

@@ -182,3 +182,15 @@ def test_compress_validation_without_gpu():
     assert L.pkv_compress_pages(None, 4, 64, 128, 8, 0, 0, p, p, None, None) == 1
     assert L.pkv_compress_pages(p, 0, 64, 128, 8, 0, 0, p, p, None, None) == 0
     assert L.pkv_compress_pages(ctypes.c_void_p(4098), 4, 64, 128, 8, 0, 0, p, p, None, None) == 1
+
+
+def test_time_next_kernel_validation_without_gpu():
+    """Both handles or neither; a call that launches nothing leaves the
+    request pending, and (NULL, NULL) clears it."""
+    L = pkv.lib()
+    p = ctypes.c_void_p(4096)
+    assert L.pkv_time_next_kernel(p, None) == 1
+    assert L.pkv_time_next_kernel(None, p) == 1
+    assert L.pkv_time_next_kernel(p, p) == 0
+    assert L.pkv_compress_pages(p, 0, 64, 128, 8, 0, 0, p, p, None, None) == 0  # no launch
+    assert L.pkv_time_next_kernel(None, None) == 0
