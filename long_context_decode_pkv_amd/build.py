@@ -18,7 +18,7 @@ OUT = os.path.join(PKG, "libpkv.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["pkv_api.cpp", "pkv_compress.hip", "pkv_decode.hip", "pkv_cache.hip"]
+SOURCES = ["pkv_api.cpp", "pkv_compress.hip", "pkv_compress_tri.hip", "pkv_decode.hip", "pkv_cache.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -1,4 +1,5 @@
-// Batched page decomposition on gfx950.
+// Batched page decomposition on gfx950, Jacobi route (any rank; launch_compress
+// sends ranks up to 32 to the tridiagonal route in pkv_compress_tri.hip).
 //
 // PuzzleKV (Sec. 3.3, text after Eq. 3) obtains each page's factors from the
 // page's P x P Gram matrix G = X X^T: its top-r eigenvectors Q are the leading
@@ -23,42 +24,14 @@
 //   4. Lf = Q_r diag(sigma), Rf = diag(1/sigma) R (zero when sigma = 0),
 //      rounded nearest-even to the output dtype, stored row-major or into a
 //      cache's packed factor part.
-#include "pkv_internal.h"
+#include "pkv_compress_common.h"
 
 namespace pkv {
 namespace {
 
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+using namespace cmp;
 
-constexpr int kLd = 65;  // LDS row stride in floats: row/column walks hit distinct banks
 constexpr int kMaxSweeps = 24;
-
-__device__ inline float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-__device__ inline uint16_t f32_to_bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// Element (j, c) of a page, j < P (token), c < d (channel).
-template <typename Elem>
-__device__ inline float page_elem(const Elem* X, int trans, int j, int c) {
-  Elem v = trans ? X[c * kP + j] : X[j * kD + c];
-  if constexpr (sizeof(Elem) == 2) return bf16_bits_to_f32(v);
-  else return v;
-}
-
-__device__ inline float lane_value(float x, int k) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k));
-}
-
-__device__ inline void store_elem(void* base, int64_t idx, int dtype, float v) {
-  if (dtype == PKV_BF16) ((uint16_t*)base)[idx] = f32_to_bf16_bits(v);
-  else ((float*)base)[idx] = v;
-}
 
 // G tile (16ta.., 16tb..) into LDS (and its mirror).
 __device__ inline void store_gram_tile(float* Gs, int ta, int tb, floatx4 acc, int lane) {
@@ -71,19 +44,9 @@ __device__ inline void store_gram_tile(float* Gs, int ta, int tb, floatx4 acc, i
   }
 }
 
-// 8 consecutive channels c0.. of page row `row` as a bf16 MFMA operand.
-__device__ inline bf16x8 row8(const uint16_t* X, int trans, int row, int c0) {
-  if (!trans) return __builtin_bit_cast(bf16x8, *(const uint4*)(X + row * kD + c0));
-  bf16x8 v;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(__bf16, X[(c0 + e) * kP + row]);
-  return v;
-}
-
 // The 10 upper 16x16 tiles of G = X X^T, spread over the page's waves.
 template <typename Elem, int WPP>
 __device__ void gram(const Elem* X, int trans, float* Gs, int lane, int wv) {
-  const int i = lane & 15, q = lane >> 4;
   for (int tile = wv; tile < 10; tile += WPP) {
     // tile -> (ta, tb), ta <= tb
     int ta = 0, rem = tile;
@@ -92,21 +55,7 @@ __device__ void gram(const Elem* X, int trans, float* Gs, int lane, int wv) {
       ++ta;
     }
     const int tb = ta + rem;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (sizeof(Elem) == 2) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 av = row8(X, trans, 16 * ta + i, 32 * ks + 8 * q);
-        const bf16x8 bv = row8(X, trans, 16 * tb + i, 32 * ks + 8 * q);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
-      }
-    } else {
-      for (int kc = 0; kc < kD / 4; ++kc) {
-        const float av = page_elem(X, trans, 16 * ta + i, 4 * kc + q);
-        const float bv = page_elem(X, trans, 16 * tb + i, 4 * kc + q);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
-      }
-    }
+    const floatx4 acc = gram_tile(X, trans, ta, tb, lane);
     store_gram_tile(Gs, ta, tb, acc, lane);
   }
 }
@@ -431,10 +380,12 @@ constexpr int64_t kLatencyModePages = 512;
 
 hipError_t launch_compress(const CompressJob& job, hipStream_t stream) {
   if (job.n_pages <= 0) return hipSuccess;
+  const KernelEvents ev = take_kernel_events();
+  const int r_max = job.n_kind == 2 && job.rank[1] > job.rank[0] ? job.rank[1] : job.rank[0];
+  if (r_max <= kTriMaxRank) return launch_compress_tri(job, stream, ev.start, ev.stop);
   const int64_t cap = 1 << 30;
   const unsigned grid = (unsigned)(job.n_pages < cap ? job.n_pages : cap);
   const bool few = job.n_pages <= kLatencyModePages;
-  const KernelEvents ev = take_kernel_events();
   if (job.in_dtype == PKV_BF16) {
     if (few)
       hipExtLaunchKernelGGL((compress_kernel<uint16_t, 8>), dim3(grid), dim3(512), 0, stream, ev.start,

@@ -1,0 +1,127 @@
+// Device helpers shared by the two page-decomposition kernels
+// (pkv_compress.hip: Jacobi, any rank; pkv_compress_tri.hip: tridiagonal
+// route, ranks up to 32).
+#pragma once
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace cmp {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kLd = 65;  // LDS row stride in floats: row/column walks hit distinct banks
+
+__device__ inline float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ inline uint16_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Element (j, c) of a page, j < P (token), c < d (channel).
+template <typename Elem>
+__device__ inline float page_elem(const Elem* X, int trans, int j, int c) {
+  Elem v = trans ? X[c * kP + j] : X[j * kD + c];
+  if constexpr (sizeof(Elem) == 2) return bf16_bits_to_f32(v);
+  else return v;
+}
+
+__device__ inline void store_elem(void* base, int64_t idx, int dtype, float v) {
+  if (dtype == PKV_BF16) ((uint16_t*)base)[idx] = f32_to_bf16_bits(v);
+  else ((float*)base)[idx] = v;
+}
+
+// 8 consecutive channels c0.. of page row `row` as a bf16 MFMA operand.
+__device__ inline bf16x8 row8(const uint16_t* X, int trans, int row, int c0) {
+  if (!trans) return __builtin_bit_cast(bf16x8, *(const uint4*)(X + row * kD + c0));
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(__bf16, X[(c0 + e) * kP + row]);
+  return v;
+}
+
+// One 16x16 tile (rows 16 ta.., columns 16 tb..) of G = X X^T on the matrix
+// cores: lane l holds G[16 ta + 4 (l / 16) + v][16 tb + l % 16], v < 4.
+template <typename Elem>
+__device__ inline floatx4 gram_tile(const Elem* X, int trans, int ta, int tb, int lane) {
+  const int i = lane & 15, q = lane >> 4;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (sizeof(Elem) == 2) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 av = row8(X, trans, 16 * ta + i, 32 * ks + 8 * q);
+      const bf16x8 bv = row8(X, trans, 16 * tb + i, 32 * ks + 8 * q);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+    }
+  } else {
+#pragma unroll 4
+    for (int kc = 0; kc < kD / 4; ++kc) {
+      if ((kc & 3) == 0) __builtin_amdgcn_sched_barrier(0);
+      const float av = page_elem(X, trans, 16 * ta + i, 4 * kc + q);
+      const float bv = page_elem(X, trans, 16 * tb + i, 4 * kc + q);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
+// Where page n of a job comes from and goes to.
+struct PageRef {
+  int kind;
+  int64_t f, bh;
+  int trans, r;
+  const void* X;
+};
+
+__device__ inline PageRef page_ref(const CompressJob& job, int64_t n, int elem_bytes) {
+  PageRef p;
+  p.kind = (int)(n % job.n_kind);
+  p.f = (n / job.n_kind) % job.n_f;
+  p.bh = n / ((int64_t)job.n_kind * job.n_f);
+  p.trans = job.in_trans[p.kind];
+  p.r = job.rank[p.kind];
+  p.X = (const uint8_t*)job.in_base[p.kind] +
+        (p.bh * job.in_bh_stride + p.f * job.in_f_stride) * elem_bytes;
+  return p;
+}
+
+// Destination of factor element Rf[i][c] (i < r_store) and Lf[j][i].
+struct FactorDst {
+  bool packed;
+  PackDims pd;
+  int r, r_store, kind;
+  int64_t n;
+  void* rf;
+  void* lf;
+  __device__ FactorDst(const CompressJob& job, const PageRef& p, int64_t n_) {
+    packed = job.fac != nullptr;
+    pd = pack_dims(p.r);
+    r = p.r;
+    r_store = packed ? 8 * pd.n8 : p.r;
+    kind = p.kind;
+    n = n_;
+    if (packed) {
+      uint8_t* part = job.fac + ((p.bh * job.fac_bh_pages) + job.f0 + p.f) * job.page_bytes +
+                      (int64_t)p.kind * job.k_part_bytes;
+      rf = lf = part;
+    } else {
+      rf = job.rf;
+      lf = job.lf;
+    }
+  }
+  __device__ int64_t rf_idx(int i, int c) const {
+    if (!packed) return n * (int64_t)r * kD + (int64_t)i * kD + c;
+    return kind == 0 ? off_rf_k(pd, i, c) : off_rf_v(pd, i, c);
+  }
+  __device__ int64_t lf_idx(int j, int i) const {
+    if (!packed) return n * (int64_t)kP * r + (int64_t)j * r + i;
+    return kind == 0 ? off_lf_k(pd, j, i) : off_lf_v(pd, j, i);
+  }
+};
+
+}  // namespace cmp
+}  // namespace pkv

@@ -1,0 +1,460 @@
+// Batched page decomposition on gfx950, tridiagonal route (ranks r <= 32).
+//
+// PuzzleKV (Sec. 3.3, text after Eq. 3) takes each page's factors from the
+// page's P x P Gram matrix G = X X^T: its top-r eigenvectors Q are the leading
+// left singular vectors, and R = Q^T X.  The page leaves the eigen-method
+// open.  This kernel uses the classical symmetric route: Householder
+// reduction to tridiagonal form, bisection on Sturm sequence counts for the
+// r largest eigenvalues, one eigenvector per eigenvalue from a twisted
+// factorization, back-transformation.  That is ~0.5 MFLOP of eigen-work per
+// page against ~20 MFLOP for Jacobi sweeps, and it has no data-dependent
+// iteration count.
+//
+// One 64-lane wavefront (one workgroup) per page.  Lane i owns row i of G and
+// row i of the accumulated Householder product Q_H in registers.
+//
+//   1. G = X X^T on the matrix cores (bf16 inputs: v_mfma_f32_16x16x32_bf16,
+//      exact products, fp32 accumulation; fp32 inputs: v_mfma_f32_16x16x4_f32),
+//      staged through LDS one 16-row band at a time into the row registers.
+//   2. 62 Householder steps G <- H G H (H = I - tau v v^T, the LAPACK slarfg
+//      convention: v_{k+1} = 1, beta = -sign(alpha) ||x||), each a matrix-vector
+//      product and a rank-2 update on the lane's row; Q_H <- Q_H H on the
+//      lane's row of Q_H.  The reflector and the update vector are broadcast
+//      through LDS.  Result: T = diag(a) + offdiag(b), G = Q_H T Q_H^T.
+//   3. The r largest eigenvalues of T by multisection: 64 / r' lanes per
+//      eigenvalue (r' = r rounded up to a power of two) each count the
+//      eigenvalues below their own point (Sturm count = number of negative
+//      pivots of the LDL^T factorization of T - x I), a fixed number of rounds
+//      to 2^-25 of the Gershgorin span.
+//   4. For each eigenvalue lambda the eigenvector of T from the twisted
+//      factorization of T - lambda I: forward pivots d+_i, backward pivots
+//      d-_i, twist index k = argmin |d+_k + d-_k - (a_k - lambda)|, z_k = 1 and
+//      the two one-sided recurrences outward from k.
+//   5. Q_r = Q_H Z, R = Q_r^T X on the matrix cores in fp32, sigma_i = ||R_i||,
+//      Lf = Q_r diag(sigma), Rf = diag(1/sigma) R (zero where sigma = 0), rounded
+//      nearest-even to the output dtype.
+#include "pkv_compress_common.h"
+
+namespace pkv {
+namespace {
+
+using namespace cmp;
+
+constexpr int kZs = 36;  // LDS row stride of Z and Q_r (floats; 16-byte aligned rows)
+
+struct TriShared {
+  union {
+    float band[16 * kLd];  // one 16-row band of G on its way into the row registers
+    float Z[kP * kZs];     // eigenvectors of T as columns, then Q_r
+  } u;
+  float xrow[kP];  // row k of the current G
+  float v[kP];     // Householder vector
+  float w[kP];     // rank-2 update vector
+  float a[kP];     // diagonal of T
+  float b[kP];     // b[i] = T[i][i+1], b[63] = 0
+  float b2s[kP];   // b2s[i] = b[i-1]^2, b2s[0] = 0
+  float sig[kTriMaxRank];
+};
+
+template <int Op>
+__device__ __forceinline__ float combine(float p, float q) {
+  if constexpr (Op == 0) return p + q;
+  else if constexpr (Op == 1) return fmaxf(p, q);
+  else return fminf(p, q);
+}
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp_mov(float y) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), Ctrl, 0xf, 0xf, false));
+}
+
+// Sum (Op 0) / max (1) / min (2) over the 16 lanes of each DPP row, in every
+// lane of the row.
+template <int Op>
+__device__ __forceinline__ float row16_reduce(float x) {
+  x = combine<Op>(x, dpp_mov<0xb1>(x));   // quad_perm [1,0,3,2]
+  x = combine<Op>(x, dpp_mov<0x4e>(x));   // quad_perm [2,3,0,1]
+  x = combine<Op>(x, dpp_mov<0x141>(x));  // row_half_mirror
+  x = combine<Op>(x, dpp_mov<0x140>(x));  // row_mirror
+  return x;
+}
+
+template <int Op>
+__device__ __forceinline__ float wave_reduce(float x) {
+  const float s = row16_reduce<Op>(x);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 48));
+  if constexpr (Op == 0) return (r0 + r1) + (r2 + r3);
+  else if constexpr (Op == 1) return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+  else return fminf(fminf(r0, r1), fminf(r2, r3));
+}
+
+// 1. G into the row registers: lane i gets G[i][0..63].
+template <typename Elem>
+__device__ __forceinline__ void gram_rows(const Elem* X, int trans, TriShared& sh, float (&g)[kP], int lane) {
+  const int c = lane & 15, q = lane >> 4;
+  for (int ta = 0; ta < 4; ++ta) {
+    for (int tb = 0; tb < 4; ++tb) {
+      __builtin_amdgcn_sched_barrier(0);
+      const floatx4 acc = gram_tile(X, trans, ta, tb, lane);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sh.u.band[(4 * q + v) * kLd + 16 * tb + c] = acc[v];
+    }
+    __syncthreads();
+    if (q == ta) {
+#pragma unroll
+      for (int j = 0; j < kP; ++j) g[j] = sh.u.band[c * kLd + j];
+    }
+    __syncthreads();
+  }
+}
+
+// 2. Householder tridiagonalization.  On return lane i holds a_i (my_a), b_i
+// (my_b) and row i of Q_H.
+__device__ __forceinline__ void tridiagonalize(TriShared& sh, float (&g)[kP], float (&qh)[kP], int lane,
+                                      float& my_a, float& my_b) {
+#pragma unroll
+  for (int j = 0; j < kP; ++j) qh[j] = (j == lane) ? 1.f : 0.f;
+  my_a = 0.f;
+  my_b = 0.f;
+  for (int k = 0; k < kP - 1; ++k) {
+    if (lane == k) {
+#pragma unroll
+      for (int jc = 0; jc < kP / 4; ++jc)
+        *(float4*)&sh.xrow[4 * jc] = float4{g[4 * jc], g[4 * jc + 1], g[4 * jc + 2], g[4 * jc + 3]};
+    }
+    __syncthreads();
+    const float x = sh.xrow[lane];  // G[k][lane] = G[lane][k]
+    if (lane == k) my_a = x;
+    const float alpha = sh.xrow[k + 1];
+    const float tail = wave_reduce<0>(lane >= k + 2 ? x * x : 0.f);
+    // H_k = I - tau v v^T; tail == 0 means no reflection (tau = 0, v = e_{k+1})
+    const bool refl = tail > 0.f;
+    const float xn = sqrtf(fmaf(alpha, alpha, tail));
+    const float beta = refl ? (alpha >= 0.f ? -xn : xn) : alpha;
+    const float tau = refl ? (beta - alpha) / beta : 0.f;
+    const float scal = refl ? 1.f / (alpha - beta) : 0.f;
+    const float vi = lane == k + 1 ? 1.f : (lane >= k + 2 ? x * scal : 0.f);
+    sh.v[lane] = vi;
+    __syncthreads();
+    // p = tau G v (rows > k), t = Q_H v
+    float pacc = 0.f, tacc = 0.f;
+#pragma unroll
+    for (int jc = 0; jc < kP / 4; ++jc) {
+      __builtin_amdgcn_sched_barrier(0);
+      const float4 vv = *(const float4*)&sh.v[4 * jc];
+      pacc = fmaf(g[4 * jc], vv.x, pacc);
+      pacc = fmaf(g[4 * jc + 1], vv.y, pacc);
+      pacc = fmaf(g[4 * jc + 2], vv.z, pacc);
+      pacc = fmaf(g[4 * jc + 3], vv.w, pacc);
+      tacc = fmaf(qh[4 * jc], vv.x, tacc);
+      tacc = fmaf(qh[4 * jc + 1], vv.y, tacc);
+      tacc = fmaf(qh[4 * jc + 2], vv.z, tacc);
+      tacc = fmaf(qh[4 * jc + 3], vv.w, tacc);
+    }
+    const float pi = lane > k ? tau * pacc : 0.f;
+    const float K = 0.5f * tau * wave_reduce<0>(pi * vi);
+    const float wi = fmaf(-K, vi, pi);
+    sh.w[lane] = wi;
+    __syncthreads();
+    // G <- G - v w^T - w v^T ; Q_H <- Q_H - tau (Q_H v) v^T
+    const float tq = tau * tacc;
+#pragma unroll
+    for (int jc = 0; jc < kP / 4; ++jc) {
+      __builtin_amdgcn_sched_barrier(0);
+      const float4 vv = *(const float4*)&sh.v[4 * jc];
+      const float4 ww = *(const float4*)&sh.w[4 * jc];
+      g[4 * jc] = fmaf(-vi, ww.x, fmaf(-wi, vv.x, g[4 * jc]));
+      g[4 * jc + 1] = fmaf(-vi, ww.y, fmaf(-wi, vv.y, g[4 * jc + 1]));
+      g[4 * jc + 2] = fmaf(-vi, ww.z, fmaf(-wi, vv.z, g[4 * jc + 2]));
+      g[4 * jc + 3] = fmaf(-vi, ww.w, fmaf(-wi, vv.w, g[4 * jc + 3]));
+      qh[4 * jc] = fmaf(-tq, vv.x, qh[4 * jc]);
+      qh[4 * jc + 1] = fmaf(-tq, vv.y, qh[4 * jc + 1]);
+      qh[4 * jc + 2] = fmaf(-tq, vv.z, qh[4 * jc + 2]);
+      qh[4 * jc + 3] = fmaf(-tq, vv.w, qh[4 * jc + 3]);
+    }
+    if (lane == k) my_b = beta;
+    __syncthreads();
+  }
+  // the last diagonal entry is already in place: no reflection touches it
+  if (lane == kP - 1) my_a = g[kP - 1];
+}
+
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Number of eigenvalues of T below x: negative pivots of T - x I = L D L^T.
+__device__ __forceinline__ int sturm_count(const TriShared& sh, float x, float pivmin) {
+  int cnt = 0;
+  float d = 1.f;
+#pragma unroll 4
+  for (int ic = 0; ic < kP / 4; ++ic) {
+    const float4 a4 = *(const float4*)&sh.a[4 * ic];
+    const float4 b4 = *(const float4*)&sh.b2s[4 * ic];
+    const float av[4] = {a4.x, a4.y, a4.z, a4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      d = fmaf(-bv[e], rcp(d), av[e] - x);
+      d = fabsf(d) < pivmin ? -pivmin : d;
+      cnt += d < 0.f ? 1 : 0;
+    }
+  }
+  return cnt;
+}
+
+// Fixed multisection rounds for L points per eigenvalue: (L+1)^n >= 2^25.
+__device__ __forceinline__ int multisection_rounds(int L) {
+  switch (L) {
+    case 2: return 16;
+    case 4: return 11;
+    case 8: return 8;
+    case 16: return 7;
+    default: return 5;  // 32, 64
+  }
+}
+
+// 4. Eigenvector of T for eigenvalue lam by the twisted factorization, into
+// column `col` of Z (LDS, stride kZs), normalized; all zeros if it could not be
+// formed.  The column doubles as the scratch for the pivots, so a lane holds
+// no per-row state in registers.  Lanes sharing a column compute identical
+// values; only `writer` lanes store.
+__device__ __forceinline__ void twisted_vector(TriShared& sh, float lam, float pivmin, int col,
+                                               bool writer) {
+  auto guard = [pivmin](float d) { return fabsf(d) < pivmin ? -pivmin : d; };
+  float* Zc = sh.u.Z + col;
+  // forward pivots d+_i -> Z[i]
+  float d = 1.f;
+  for (int i = 0; i < kP; ++i) {
+    d = guard(fmaf(-sh.b2s[i], rcp(d), sh.a[i] - lam));
+    if (writer) Zc[i * kZs] = d;
+  }
+  __syncthreads();
+  // backward pivots d-_i (b2s[i + 1] = b_i^2) and the twist index
+  float dm = 1.f, best = __builtin_inff();
+  int kk = kP - 1;
+  for (int i = kP - 1; i >= 0; --i) {
+    const float ai = sh.a[i] - lam;
+    dm = guard(fmaf(-(i < kP - 1 ? sh.b2s[i + 1] : 0.f), rcp(dm), ai));
+    const float gam = fabsf(Zc[i * kZs] + dm - ai);
+    if (gam < best) {
+      best = gam;
+      kk = i;
+    }
+  }
+  // z_kk = 1; above kk: z_i = -b_{i-1} z_{i-1} / d-_i, so the d-_i are formed
+  // again top-down and kept where i > kk
+  dm = 1.f;
+  for (int i = kP - 1; i > kk; --i) {
+    dm = guard(fmaf(-(i < kP - 1 ? sh.b2s[i + 1] : 0.f), rcp(dm), sh.a[i] - lam));
+    if (writer) Zc[i * kZs] = dm;
+  }
+  __syncthreads();
+  float ss = 1.f, zz = 1.f;
+  for (int i = kk + 1; i < kP; ++i) {
+    zz = -sh.b[i - 1] * zz * rcp(Zc[i * kZs]);
+    ss = fmaf(zz, zz, ss);
+    if (writer) Zc[i * kZs] = zz;
+  }
+  // below kk: z_i = -b_i z_{i+1} / d+_i
+  zz = 1.f;
+  for (int i = kk - 1; i >= 0; --i) {
+    zz = -sh.b[i] * zz * rcp(Zc[i * kZs]);
+    ss = fmaf(zz, zz, ss);
+    if (writer) Zc[i * kZs] = zz;
+  }
+  if (writer) Zc[kk * kZs] = 1.f;
+  __syncthreads();
+  const bool ok = ss > 0.f && ss < __builtin_inff();
+  const float inv = ok ? rsqrtf(ss) : 0.f;
+  for (int i = 0; i < kP; ++i) {
+    const float zi = Zc[i * kZs];
+    if (writer) Zc[i * kZs] = ok ? zi * inv : 0.f;
+  }
+}
+
+template <typename Elem>
+__device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t n, TriShared& sh, int lane) {
+  const PageRef pr = page_ref(job, n, (int)sizeof(Elem));
+  const Elem* X = (const Elem*)pr.X;
+  const int r = pr.r;
+
+  float qh[kP];
+  float my_a, my_b;
+  {
+    float g[kP];
+    gram_rows<Elem>(X, pr.trans, sh, g, lane);
+    tridiagonalize(sh, g, qh, lane, my_a, my_b);
+  }
+
+  // T to LDS, Gershgorin interval, pivot floor
+  sh.a[lane] = my_a;
+  sh.b[lane] = lane < kP - 1 ? my_b : 0.f;
+  __syncthreads();
+  const float bl = lane > 0 ? sh.b[lane - 1] : 0.f, br = sh.b[lane];
+  sh.b2s[lane] = bl * bl;
+  const float glo = wave_reduce<2>(my_a - fabsf(bl) - fabsf(br));
+  const float ghi = wave_reduce<1>(my_a + fabsf(bl) + fabsf(br));
+  const float pivmin = 0x1p-126f * fmaxf(1.f, wave_reduce<1>(br * br));
+  __syncthreads();
+
+  // 3. the r largest eigenvalues: L lanes per eigenvalue
+  int rp = 1;
+  while (rp < r) rp <<= 1;
+  const int L = kP / rp;
+  const int t = lane & (L - 1);
+  const int jl = lane / L;
+  const int j = jl < r ? jl : r - 1;  // descending index
+  const int m = kP - 1 - j;           // ascending index
+  float lo = glo, hi = ghi;
+  const int rounds = multisection_rounds(L);
+  const float frac = (float)(t + 1) / (float)(L + 1);
+  for (int it = 0; it < rounds; ++it) {
+    const float x = fmaf(hi - lo, frac, lo);
+    const int cnt = sturm_count(sh, x, pivmin);
+    float nlo = cnt <= m ? x : lo, nhi = cnt <= m ? hi : x;
+    for (int o = 1; o < L; o <<= 1) {
+      nlo = fmaxf(nlo, __shfl_xor(nlo, o));
+      nhi = fminf(nhi, __shfl_xor(nhi, o));
+    }
+    lo = nlo;
+    hi = nhi;
+  }
+  const float lam = 0.5f * (lo + hi);
+
+  // 4. eigenvectors of T -> Z[:, j]
+  twisted_vector(sh, lam, pivmin, j, t == 0 && jl < r);
+  __syncthreads();
+
+  // 5a. Q_r = Q_H Z: lane i forms row i
+  float qr[kTriMaxRank];
+#pragma unroll
+  for (int jc = 0; jc < kTriMaxRank / 4; ++jc) {
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (4 * jc < r) {
+#pragma unroll
+      for (int mm = 0; mm < kP; ++mm) {
+        if ((mm & 3) == 0) __builtin_amdgcn_sched_barrier(0);
+        const float4 z4 = *(const float4*)&sh.u.Z[mm * kZs + 4 * jc];
+        acc.x = fmaf(qh[mm], z4.x, acc.x);
+        acc.y = fmaf(qh[mm], z4.y, acc.y);
+        acc.z = fmaf(qh[mm], z4.z, acc.z);
+        acc.w = fmaf(qh[mm], z4.w, acc.w);
+      }
+    }
+    qr[4 * jc] = acc.x;
+    qr[4 * jc + 1] = acc.y;
+    qr[4 * jc + 2] = acc.z;
+    qr[4 * jc + 3] = acc.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int jc = 0; jc < kTriMaxRank / 4; ++jc) {
+    if (4 * jc < r)
+      *(float4*)&sh.u.Z[lane * kZs + 4 * jc] = float4{qr[4 * jc], qr[4 * jc + 1], qr[4 * jc + 2], qr[4 * jc + 3]};
+  }
+  __syncthreads();
+
+  // 5b. R = Q_r^T X in fp32 on the matrix cores: lane (ci, q) holds
+  // R[16 mi + 4 q + v][16 mc + ci]
+  const int ci = lane & 15, q = lane >> 4;
+  const int RT16 = (r + 15) / 16;
+  floatx4 R[2][8];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+    for (int mc = 0; mc < 8; ++mc) R[mi][mc] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll 2
+  for (int kc = 0; kc < kP / 4; ++kc) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int jr = 4 * kc + q;
+    float bv[8];
+#pragma unroll
+    for (int mc = 0; mc < 8; ++mc) bv[mc] = page_elem(X, pr.trans, jr, 16 * mc + ci);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      if (mi < RT16) {
+        const int col = 16 * mi + ci;
+        const float av = col < r ? sh.u.Z[jr * kZs + col] : 0.f;
+#pragma unroll
+        for (int mc = 0; mc < 8; ++mc)
+          R[mi][mc] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[mc], R[mi][mc], 0, 0, 0);
+      }
+    }
+  }
+  // sigma_i = ||R_i||
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    if (mi < RT16) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float ss = 0.f;
+#pragma unroll
+        for (int mc = 0; mc < 8; ++mc) ss = fmaf(R[mi][mc][v], R[mi][mc][v], ss);
+        ss = row16_reduce<0>(ss);
+        const int i = 16 * mi + 4 * q + v;
+        if (ci == 0 && i < r) sh.sig[i] = sqrtf(ss);
+      }
+    }
+  }
+  __syncthreads();
+
+  // 6. Rf = R / sigma, Lf = Q_r diag(sigma)
+  const FactorDst dst(job, pr, n);
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    if (16 * mi < dst.r_store) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = 16 * mi + 4 * q + v;
+        if (i < dst.r_store) {
+          const float sg = i < r ? sh.sig[i] : 0.f;
+          const float inv = sg > 0.f ? 1.f / sg : 0.f;
+#pragma unroll
+          for (int mc = 0; mc < 8; ++mc) {
+            const float val = i < r ? R[mi][mc][v] * inv : 0.f;
+            store_elem(dst.rf, dst.rf_idx(i, 16 * mc + ci), job.out_dtype, val);
+          }
+        }
+      }
+    }
+  }
+  for (int i = 0; i < dst.r_store; ++i) {
+    float val = 0.f;
+    if (i < r) {
+      const float sg = sh.sig[i];
+      val = sg > 0.f ? sh.u.Z[lane * kZs + i] * sg : 0.f;
+    }
+    store_elem(dst.lf, dst.lf_idx(lane, i), job.out_dtype, val);
+  }
+  if (!dst.packed && job.sigma != nullptr && lane < r) job.sigma[n * r + lane] = sh.sig[lane];
+  __syncthreads();
+}
+
+// One page per workgroup (no page loop: a loop around the page body costs the
+// register allocator ~70 extra VGPRs).  Page n = blockIdx.y * gridDim.x + blockIdx.x.
+template <typename Elem>
+__global__ __launch_bounds__(64, 3) void compress_tri_kernel(CompressJob job) {
+  __shared__ TriShared sh;
+  const int64_t n = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  if (n < job.n_pages) compress_tri_one<Elem>(job, n, sh, threadIdx.x);
+}
+
+}  // namespace
+
+hipError_t launch_compress_tri(const CompressJob& job, hipStream_t stream, hipEvent_t start,
+                               hipEvent_t stop) {
+  constexpr int64_t kGx = 65536;
+  const int64_t gx = job.n_pages < kGx ? job.n_pages : kGx;
+  const int64_t gy = (job.n_pages + gx - 1) / gx;
+  if (gy > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)gx, (unsigned)gy);
+  if (job.in_dtype == PKV_BF16)
+    hipExtLaunchKernelGGL(compress_tri_kernel<uint16_t>, grid, dim3(64), 0, stream, start, stop, 0, job);
+  else
+    hipExtLaunchKernelGGL(compress_tri_kernel<float>, grid, dim3(64), 0, stream, start, stop, 0, job);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -163,6 +163,11 @@ struct KernelEvents {
 KernelEvents take_kernel_events();
 
 hipError_t launch_compress(const CompressJob& job, hipStream_t stream);
+// Tridiagonal-route decomposition for ranks up to kTriMaxRank (launch_compress
+// dispatches to it).
+constexpr int kTriMaxRank = 32;
+hipError_t launch_compress_tri(const CompressJob& job, hipStream_t stream, hipEvent_t start,
+                               hipEvent_t stop);
 
 struct CacheGeom {
   int B, Hkv, Hq, G;
