@@ -139,11 +139,13 @@ __device__ __forceinline__ void tridiagonalize(TriShared& sh, float (&g)[kP], fl
     const float vi = lane == k + 1 ? 1.f : (lane >= k + 2 ? x * scal : 0.f);
     sh.v[lane] = vi;
     __syncthreads();
-    // p = tau G v (rows > k), t = Q_H v
+    // p = tau G v (rows > k), t = Q_H v; v_j = 0 for j <= k, so 4-column
+    // chunks left of k + 1 are skipped (uniform branch)
     float pacc = 0.f, tacc = 0.f;
 #pragma unroll
     for (int jc = 0; jc < kP / 4; ++jc) {
       __builtin_amdgcn_sched_barrier(0);
+      if (4 * jc + 3 <= k) continue;
       const float4 vv = *(const float4*)&sh.v[4 * jc];
       pacc = fmaf(g[4 * jc], vv.x, pacc);
       pacc = fmaf(g[4 * jc + 1], vv.y, pacc);
@@ -164,6 +166,7 @@ __device__ __forceinline__ void tridiagonalize(TriShared& sh, float (&g)[kP], fl
 #pragma unroll
     for (int jc = 0; jc < kP / 4; ++jc) {
       __builtin_amdgcn_sched_barrier(0);
+      if (4 * jc + 3 <= k) continue;
       const float4 vv = *(const float4*)&sh.v[4 * jc];
       const float4 ww = *(const float4*)&sh.w[4 * jc];
       g[4 * jc] = fmaf(-vi, ww.x, fmaf(-wi, vv.x, g[4 * jc]));
