@@ -150,7 +150,7 @@ def bench_decode(args, cfg_id, name):
     cfg = dict(synth.CONFIGS[cfg_id])
     B, Hq, Hkv, T0 = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"]
     NL = args.layers
-    total = T0 + args.warmup + args.steps
+    total = T0 + args.warmup + 2 * args.steps  # timed pass, then an instrumented pass
     inp = cached_inputs(cfg_id, total, workers=args.workers)
     dt = cfg["dtype"]
     Kd, Vd = to_dev(inp["K"], dt), to_dev(inp["V"], dt)
@@ -179,45 +179,61 @@ def bench_decode(args, cfg_id, name):
     pages0 = B * Hkv * n_fact0 * 2
     log(f"prefill T={T0}: {pages0} pages decomposed in {t_prefill * 1e3:.2f} ms; {NL} layer caches")
     del K0, V0
-    wss = [c.workspace(0) for c in caches]  # sized for the library's split count at this length
+    wss = [c.workspace(512) for c in caches]  # fits every split count
+    P, n_s, n_w = cfg["P"], cfg["s"] // cfg["P"], cfg["w"] // cfg["P"]
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     def layer_step(c, ws, i, rec=None):
-        if c.append(rows_k[i], rows_v[i]):
-            if rec is not None:  # the decomposition kernel's own duration
-                pkv.time_next_kernel(*rec["promote"])
-                rec["promoted"] = True
-            c.promote()
+        """pkv_decode_step: promotion when a page leaves the window, attention
+        over the cached tokens, then the merge, which adds the new token's
+        state and writes the token into the cache (no append launch)."""
+        if rec is None:
+            c.step(rows_k[i], rows_v[i], qs[i], out=out, workspace=ws)
+            return None
         T, nf, _ = c.state()
-        if rec is not None:  # the partial kernel's own duration
-            pkv.time_next_kernel(*rec["partial"])
-        c.decode_partial(qs[i], workspace=ws)
-        c.decode_merge(out, workspace=ws)
-        if rec is not None:
-            rec["merge"][1].record()
-        return T, nf
+        due = (T + 1) // P - n_s - n_w > nf
+        # the partial kernel's own duration, or the promotion's
+        pkv.time_next_kernel(*(rec["promote"] if due else rec["partial"]))
+        rec["promoted"] = due
+        c.step(rows_k[i], rows_v[i], qs[i], out=out, workspace=ws)
+        rec["merge"][1].record()
+        return T + 1, nf + (1 if due else 0)
 
     for i in range(args.warmup):
         for c, ws in zip(caches, wss):
             layer_step(c, ws, i)
     torch.cuda.synchronize()
+    # timed pass: exactly `steps` layer steps per layer cache, nothing but the
+    # library calls inside the timed region
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for j in range(args.steps):
+        for c, ws in zip(caches, wss):
+            layer_step(c, ws, args.warmup + j)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t
+
+    # instrumented pass (not part of `value`): the same steps on the next
+    # tokens, each attention launch bracketed by its kernel's own events
     recs = [[{"partial": (ev(), ev()), "merge": (None, ev()), "promote": (ev(), ev())}
              for _ in range(NL)] for _ in range(args.steps)]
     for e in (e for step in recs for r in step for pair in r.values() for e in pair if e is not None):
-        e.record()  # creates the event before the timed region
+        e.record()  # creates the event before the pass
     states = []
     torch.cuda.synchronize()
     t = time.perf_counter()
     for j in range(args.steps):
         for li, (c, ws) in enumerate(zip(caches, wss)):
-            states.append(layer_step(c, ws, args.warmup + j, recs[j][li]))
+            states.append(layer_step(c, ws, args.warmup + args.steps + j, recs[j][li]))
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t
+    elapsed_instr = time.perf_counter() - t
     flat = [r for step in recs for r in step]
-    durs = np.array([r["partial"][0].elapsed_time(r["partial"][1]) * 1e-3 for r in flat])
-    merges = np.array([r["partial"][1].elapsed_time(r["merge"][1]) * 1e-3 for r in flat])
-    promos = [r["promote"][0].elapsed_time(r["promote"][1]) * 1e-3 for r in flat if r.get("promoted")]
+    keep = [k for k, r in enumerate(flat) if not r["promoted"]]
+    durs = np.array([flat[k]["partial"][0].elapsed_time(flat[k]["partial"][1]) * 1e-3 for k in keep])
+    merges = np.array([flat[k]["partial"][1].elapsed_time(flat[k]["merge"][1]) * 1e-3 for k in keep])
+    promos = [r["promote"][0].elapsed_time(r["promote"][1]) * 1e-3 for r in flat if r["promoted"]]
+    states = [states[k] for k in keep]
     nbytes = np.array([decode_bytes(cfg, B, Hkv, Hq, T, nf) for T, nf in states], dtype=np.float64)
     achieved = nbytes.sum() / durs.sum() / 1e9
     layer_steps = args.steps * NL
@@ -226,7 +242,8 @@ def bench_decode(args, cfg_id, name):
         f"{nbytes.mean() / 1e6:.1f} MB -> {achieved:.0f} GB/s; partial end to merge end "
         f"{merges.mean() * 1e6:.2f} us; "
         f"{len(promos)} promotions, mean {np.mean(promos) * 1e6 if promos else 0:.1f} us; "
-        f"layer step {elapsed / layer_steps * 1e6:.1f} us")
+        f"layer step {elapsed / layer_steps * 1e6:.1f} us "
+        f"({elapsed_instr / layer_steps * 1e6:.1f} us with per-launch events)")
 
     res = {
         "metric": "decode-attn tokens/s (one layer: batch tokens per second of a layer decode step)",
@@ -245,7 +262,8 @@ def bench_decode(args, cfg_id, name):
                    "context_tokens": T0, "page_len": cfg["P"], "rank_k": cfg["r_k"],
                    "rank_v": cfg["r_v"], "sink": cfg["s"], "window": cfg["w"],
                    "layer_caches_rotated": NL,
-                   "step": "append + promote when due + decode partial + merge, per layer"},
+                   "step": "pkv_decode_step per layer: promotion when a page leaves the window, "
+                           "decode partial, merge with the appended token folded in"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None if traffic is None else traffic["fetch"] + traffic["write"],
@@ -257,6 +275,7 @@ def bench_decode(args, cfg_id, name):
         "breakdown_us": {"decode_partial": durs.mean() * 1e6,
                          "partial_end_to_merge_end": merges.mean() * 1e6,
                          "promote_mean": float(np.mean(promos) * 1e6) if promos else None,
+                         "layer_step_with_events": elapsed_instr / layer_steps * 1e6,
                          "promotions": len(promos)},
         "decode_effective_GBps": achieved,
         "pages_compressed_per_s": pages0 / t_prefill,

@@ -151,7 +151,8 @@ int32_t pkv_cache_layout(const pkv_shape* shape, pkv_layout* out);
 
 /* Create a cache over a caller-owned device buffer of at least
  * pkv_cache_layout().total_bytes bytes, 256-byte aligned.  The buffer's
- * contents are set by pkv_prefill.  Host only (no GPU work). */
+ * contents are set by pkv_prefill (call it, possibly with T = 0, before
+ * pkv_append or pkv_decode_step).  Host only (no GPU work). */
 int32_t pkv_cache_create(const pkv_shape* shape, void* device_buffer, uint64_t device_bytes,
                          pkv_cache** out);
 void pkv_cache_destroy(pkv_cache* cache);
@@ -182,7 +183,9 @@ int32_t pkv_compress_pages(const void* X, int64_t n_pages, int32_t P, int32_t d,
  * dtype) build the hybrid cache: copy sink, window and partial pages into the
  * dense pools, factorize every FACT page of every (sequence, KV head, K/V)
  * with the kernel of pkv_compress_pages into the factor pool, and fill the
- * page table.  Resets the cache to length T (1 <= T <= max_tokens).
+ * page table.  Resets the cache to length T (0 <= T <= max_tokens); T = 0
+ * zero-fills the dense pools and empties the table (K, V may then be NULL).
+ * A cache is first used after a prefill.
  */
 int32_t pkv_prefill(pkv_cache* cache, const void* K, const void* V, int64_t T, void* stream);
 
@@ -247,6 +250,31 @@ int32_t pkv_decode_merge(const pkv_cache* cache, const void* workspace, uint64_t
  * Synchronizes `stream`. */
 int32_t pkv_read_page_table(const pkv_cache* cache, int32_t* cls, int32_t* slot, int64_t n,
                             void* stream);
+
+/*
+ * One decode step of a layer: PuzzleKV Sec. 3.3 (5) then (4) -- append the
+ * new token's key and value (k_new, v_new: [B][H_kv][d] in the cache dtype,
+ * 16-byte aligned), factorize the page that leaves the recent window when this
+ * token completes a page (as pkv_promote_page), then the mixed attention of q
+ * over all T + 1 tokens into out [B][H_q][d] float32, as pkv_decode_attn.
+ * The cache afterwards is byte-identical to that of pkv_append +
+ * pkv_promote_page (when due) + pkv_decode_attn; the output agrees with theirs
+ * to float32 rounding.  The append costs no launch of its own: attention runs
+ * over the T cached tokens, and the cross-split merge adds the new token's
+ * state (score q.k_new / sqrt(d), weight 1, value v_new) beside the split
+ * states (Eq. 5) and writes the token into its dense page.  With w = 0 the
+ * completed page is factorized in the same step, so there the token is
+ * appended by a launch of its own first.
+ * workspace: at least pkv_decode_workspace_bytes for the length after the
+ * append (any length up to max_tokens when sized for n_split = 512).  T
+ * advances by one on success.
+ * Errors: INVALID_ARG (null or misaligned pointers), CAPACITY (T ==
+ * max_tokens, no free factor slot, workspace too small), PROMOTION_PENDING
+ * (a promotion from pkv_append is still waiting); nothing is changed then.
+ */
+int32_t pkv_decode_step(pkv_cache* cache, const void* k_new, const void* v_new, const void* q,
+                        float* out, void* workspace, uint64_t workspace_bytes, int32_t n_split,
+                        void* stream);
 
 /* Kernel timing (measurement only; no passage of the method).
  *

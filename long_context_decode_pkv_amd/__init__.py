@@ -84,6 +84,7 @@ def lib():
         "pkv_decode_merge": ([vp, vp, u64, i32, vp, vp], i32),
         "pkv_read_page_table": ([vp, vp, vp, i64, vp], i32),
         "pkv_time_next_kernel": ([vp, vp], i32),
+        "pkv_decode_step": ([vp, vp, vp, vp, vp, vp, u64, i32, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -262,10 +263,11 @@ class Cache:
 
     # -- hot path
     def prefill(self, K, V):
+        """Build the cache from dense K, V [B][H_kv][T][d] (T may be 0)."""
         T = K.shape[2]
-        _check(lib().pkv_prefill(self._h, _dev_ptr(K, self.dtype_code, "K"),
-                                 _dev_ptr(V, self.dtype_code, "V"), T, _stream(self.device)),
-               "pkv_prefill")
+        kp = _dev_ptr(K, self.dtype_code, "K") if T else None
+        vp = _dev_ptr(V, self.dtype_code, "V") if T else None
+        _check(lib().pkv_prefill(self._h, kp, vp, T, _stream(self.device)), "pkv_prefill")
 
     def append(self, k, v) -> bool:
         pend = ctypes.c_int32()
@@ -314,6 +316,21 @@ class Cache:
         _check(lib().pkv_decode_merge(self._h, ctypes.c_void_p(ws.data_ptr()), ws.numel(), n_split,
                                       _dev_ptr(out, None, "out"), _stream(self.device)),
                "pkv_decode_merge")
+        return out
+
+    def step(self, k, v, q, out=None, n_split: int = 0, workspace=None):
+        """One decode step (pkv_decode_step): append (k, v), promote the page
+        leaving the window when due, attend q over all tokens -> out."""
+        import torch
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+        # auto split counts never exceed 512: that workspace fits any length
+        ws = self.workspace(n_split or 512) if workspace is None else workspace
+        _check(lib().pkv_decode_step(self._h, _dev_ptr(k, self.dtype_code, "k"),
+                                     _dev_ptr(v, self.dtype_code, "v"),
+                                     _dev_ptr(q, self.dtype_code, "q"), _dev_ptr(out, None, "out"),
+                                     ctypes.c_void_p(ws.data_ptr()), ws.numel(), n_split,
+                                     _stream(self.device)), "pkv_decode_step")
         return out
 
     # -- inspection

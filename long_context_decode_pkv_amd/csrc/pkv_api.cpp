@@ -126,6 +126,46 @@ float bf16_round_host(float x, uint16_t* bits) {
   return f;
 }
 
+// Factorize the page that leaves the recent window (logical page n_s + n_fact,
+// in ring slot (p - n_s) mod (n_w + 1)) into factor slot n_fact, flip its
+// table entry to FACT and count it (Sec. 3.3 (5)).
+int32_t promote_now(pkv_cache* c, void* stream) {
+  const CacheGeom g = geom_of(c);
+  const int64_t f = c->n_fact;            // factor slot of the page
+  const int64_t p_old = g.n_s + f;        // logical page leaving the window
+  if (f >= g.F_max) return PKV_ERR_CAPACITY;
+  const int64_t ring = (p_old - g.n_s) % (g.n_w + 1);
+  const int64_t esz = c->lay.elem_bytes;
+  const int64_t ppg = (int64_t)kP * kD;
+  CompressJob job;
+  std::memset(&job, 0, sizeof(job));
+  job.n_kind = 2;
+  job.n_f = 1;
+  job.n_pages = (int64_t)g.B * g.Hkv * 2;
+  job.in_base[0] = c->base + c->lay.win_k + ring * ppg * esz;
+  job.in_base[1] = c->base + c->lay.win_v + ring * ppg * esz;
+  job.in_trans[0] = 0;
+  job.in_trans[1] = 1;  // value pages are stored transposed
+  job.in_bh_stride = (int64_t)(g.n_w + 1) * ppg;
+  job.in_f_stride = 0;
+  job.in_dtype = g.dtype;
+  job.rank[0] = g.r_k;
+  job.rank[1] = g.r_v;
+  job.out_dtype = g.dtype;
+  job.fac = c->base + c->lay.factors;
+  job.fac_bh_pages = g.F_max;
+  job.f0 = f;
+  job.page_bytes = c->lay.factor_page_bytes;
+  job.k_part_bytes = c->lay.factor_k_elems * esz;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_compress(job, s);
+  if (e == hipSuccess) e = launch_table_set(g, p_old, table_entry(PKV_PAGE_FACT, (int)f), s);
+  if (e != hipSuccess) return PKV_ERR_DEVICE;
+  c->n_fact += 1;
+  return PKV_OK;
+}
+
+
 }  // namespace
 
 namespace pkv {
@@ -322,10 +362,9 @@ int32_t pkv_compress_pages(const void* X, int64_t n_pages, int32_t P, int32_t d,
 }
 
 int32_t pkv_prefill(pkv_cache* c, const void* K, const void* V, int64_t T, void* stream) {
-  if (!c || !K || !V) return PKV_ERR_INVALID_ARG;
-  if (T < 1) return PKV_ERR_INVALID_ARG;
+  if (!c || T < 0) return PKV_ERR_INVALID_ARG;
+  if (T > 0 && (!K || !V || !aligned(K, 16) || !aligned(V, 16))) return PKV_ERR_INVALID_ARG;
   if (T > c->shape.max_tokens) return PKV_ERR_CAPACITY;
-  if (!aligned(K, 16) || !aligned(V, 16)) return PKV_ERR_INVALID_ARG;
   const CacheGeom g = geom_of(c);
   const int64_t n_fact = steady_fact(T, kP, g.n_s, g.n_w);
   hipStream_t s = (hipStream_t)stream;
@@ -380,40 +419,9 @@ int32_t pkv_append(pkv_cache* c, const void* k_new, const void* v_new, int32_t* 
 int32_t pkv_promote_page(pkv_cache* c, void* stream) {
   if (!c) return PKV_ERR_INVALID_ARG;
   if (!c->pending) return PKV_ERR_NOT_ELIGIBLE;
-  const CacheGeom g = geom_of(c);
-  const int64_t f = c->n_fact;            // factor slot of the page
-  const int64_t p_old = g.n_s + f;        // logical page leaving the window
-  if (f >= g.F_max) return PKV_ERR_CAPACITY;
-  const int64_t ring = (p_old - g.n_s) % (g.n_w + 1);
-  const int64_t esz = c->lay.elem_bytes;
-  const int64_t ppg = (int64_t)kP * kD;
-  CompressJob job;
-  std::memset(&job, 0, sizeof(job));
-  job.n_kind = 2;
-  job.n_f = 1;
-  job.n_pages = (int64_t)g.B * g.Hkv * 2;
-  job.in_base[0] = c->base + c->lay.win_k + ring * ppg * esz;
-  job.in_base[1] = c->base + c->lay.win_v + ring * ppg * esz;
-  job.in_trans[0] = 0;
-  job.in_trans[1] = 1;  // value pages are stored transposed
-  job.in_bh_stride = (int64_t)(g.n_w + 1) * ppg;
-  job.in_f_stride = 0;
-  job.in_dtype = g.dtype;
-  job.rank[0] = g.r_k;
-  job.rank[1] = g.r_v;
-  job.out_dtype = g.dtype;
-  job.fac = c->base + c->lay.factors;
-  job.fac_bh_pages = g.F_max;
-  job.f0 = f;
-  job.page_bytes = c->lay.factor_page_bytes;
-  job.k_part_bytes = c->lay.factor_k_elems * esz;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_compress(job, s);
-  if (e == hipSuccess) e = launch_table_set(g, p_old, table_entry(PKV_PAGE_FACT, (int)f), s);
-  if (e != hipSuccess) return PKV_ERR_DEVICE;
-  c->n_fact += 1;
-  c->pending = 0;
-  return PKV_OK;
+  const int32_t st = promote_now(c, stream);
+  if (st == PKV_OK) c->pending = 0;
+  return st;
 }
 
 int32_t pkv_decode_workspace_bytes(const pkv_cache* c, int32_t n_split, uint64_t* bytes) {
@@ -427,26 +435,32 @@ int32_t pkv_decode_workspace_bytes(const pkv_cache* c, int32_t n_split, uint64_t
 
 namespace {
 
-// Shared argument checks of the decode calls; fills job (without out).
-int32_t decode_job(const pkv_cache* c, const void* q, void* workspace, uint64_t workspace_bytes,
-                   int32_t n_split, AttnJob* job) {
+// Shared argument checks of the decode calls for a cache of length T with
+// n_fact factorized pages; fills job (without out).
+int32_t decode_job_at(const pkv_cache* c, int64_t T, int64_t n_fact, const void* q, void* workspace,
+                      uint64_t workspace_bytes, int32_t n_split, AttnJob* job, bool allow_empty = false) {
   if (!c || !workspace || n_split < 0 || n_split > kMaxDecodeSplits) return PKV_ERR_INVALID_ARG;
-  if (c->T < 1) return PKV_ERR_INVALID_ARG;
+  if (T < (allow_empty ? 0 : 1)) return PKV_ERR_INVALID_ARG;
   if ((q && !aligned(q, 16)) || !aligned(workspace, kAlign)) return PKV_ERR_INVALID_ARG;
   const CacheGeom g = geom_of(c);
-  const int ns = n_split > 0 ? n_split : decode_default_splits(g, c->T, c->n_fact);
-  uint64_t need = 0;
-  pkv_decode_workspace_bytes(c, ns, &need);
-  if (workspace_bytes < need) return PKV_ERR_CAPACITY;
+  const int ns = n_split > 0 ? n_split : decode_default_splits(g, T, n_fact);
   const uint64_t rows = (uint64_t)g.B * g.Hq * ns;
+  const uint64_t need = align_up(rows * kD * 4) + align_up(rows * 2 * 4);
+  if (workspace_bytes < need) return PKV_ERR_CAPACITY;
   job->q = q;
   job->out = nullptr;
   job->ws_o = (float*)workspace;
   job->ws_ml = (float*)((uint8_t*)workspace + align_up(rows * kD * 4));
   job->n_split = ns;
-  job->T = c->T;
-  job->n_fact = c->n_fact;
+  job->T = T;
+  job->n_fact = n_fact;
   return PKV_OK;
+}
+
+int32_t decode_job(const pkv_cache* c, const void* q, void* workspace, uint64_t workspace_bytes,
+                   int32_t n_split, AttnJob* job) {
+  if (!c) return PKV_ERR_INVALID_ARG;
+  return decode_job_at(c, c->T, c->n_fact, q, workspace, workspace_bytes, n_split, job);
 }
 
 }  // namespace
@@ -481,6 +495,63 @@ int32_t pkv_decode_attn(const pkv_cache* c, const void* q, float* out, void* wor
   hipError_t e = launch_partial(g, job, (hipStream_t)stream);
   if (e == hipSuccess) e = launch_merge(g, job, (hipStream_t)stream);
   return dev_status(e);
+}
+
+int32_t pkv_decode_step(pkv_cache* c, const void* k_new, const void* v_new, const void* q,
+                        float* out, void* workspace, uint64_t workspace_bytes, int32_t n_split,
+                        void* stream) {
+  if (!c || !k_new || !v_new || !q || !out) return PKV_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16)) return PKV_ERR_INVALID_ARG;
+  if (c->pending) return PKV_ERR_PROMOTION_PENDING;
+  if (c->T >= c->shape.max_tokens) return PKV_ERR_CAPACITY;
+  const CacheGeom g = geom_of(c);
+  const int64_t T0 = c->T, T1 = T0 + 1;
+  const int64_t p = T0 / kP;                // page of the new token
+  const int row = (int)(T0 % kP);
+  const bool promote = steady_fact(T1, kP, g.n_s, g.n_w) > c->n_fact;
+  const int64_t p_old = g.n_s + c->n_fact;  // page leaving the window when promote
+  if (promote && c->n_fact >= g.F_max) return PKV_ERR_CAPACITY;
+  hipStream_t s = (hipStream_t)stream;
+  if (promote && p_old == p) {
+    // no window (w = 0): the page the token completes is factorized at once,
+    // so the token must be in place first; separate launches
+    AttnJob job;
+    int32_t st = decode_job_at(c, T1, c->n_fact + 1, q, workspace, workspace_bytes, n_split, &job);
+    if (st != PKV_OK) return st;
+    job.out = out;
+    st = pkv_append(c, k_new, v_new, nullptr, stream);
+    if (st == PKV_OK) st = pkv_promote_page(c, stream);
+    if (st != PKV_OK) return st;
+    hipError_t e = launch_partial(g, job, s);
+    if (e == hipSuccess) e = launch_merge(g, job, s);
+    return dev_status(e);
+  }
+  // Attend over the T0 cached tokens (after the promotion, which does not
+  // touch the page of the new token); the merge adds the new token's state
+  // and writes the token into its page.
+  AttnJob job;
+  int32_t st = decode_job_at(c, T0, c->n_fact + (promote ? 1 : 0), q, workspace, workspace_bytes,
+                             n_split, &job, true);
+  if (st != PKV_OK) return st;
+  job.out = out;
+  if (promote) {
+    st = promote_now(c, stream);
+    if (st != PKV_OK) return st;
+  }
+  job.k_new = k_new;
+  job.v_new = v_new;
+  job.app_page = p;
+  job.app_row = row;
+  job.app_entry = p < g.n_s ? table_entry(PKV_PAGE_SINK, (int)p)
+                            : table_entry(row == kP - 1 ? PKV_PAGE_WIN : PKV_PAGE_PART,
+                                          (int)((p - g.n_s) % (g.n_w + 1)));
+  hipError_t e = hipSuccess;
+  if (T0 > 0) e = launch_partial(g, job, s);
+  if (T0 == 0) job.n_split = 0;  // nothing cached yet: the new token alone
+  if (e == hipSuccess) e = launch_merge(g, job, s);
+  if (e != hipSuccess) return PKV_ERR_DEVICE;
+  c->T = T1;
+  return PKV_OK;
 }
 
 int32_t pkv_read_page_table(const pkv_cache* c, int32_t* cls, int32_t* slot, int64_t n,

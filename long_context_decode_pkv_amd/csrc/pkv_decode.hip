@@ -662,44 +662,161 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   }
 }
 
-// Eq. 5 across splits: one 64-lane workgroup per (sequence, query head).
-// The lanes read the split maxima and form the split weights e^(m_s - M) in
-// LDS, then lanes 0..31 accumulate 4 consecutive channels each over all
-// splits with 16-byte loads, several splits in flight at a time.
-__global__ __launch_bounds__(64) void merge_kernel(const float* ws_o, const float* ws_ml,
-                                                   float* out, int n_split) {
-  __shared__ float sh_w[kMaxSplits];
+// Arguments of the cross-split merge.  With k_new set, the merge also takes
+// the token appended in this decode step: its state (score q.k_new in log2
+// units, l = 1, o = v_new) joins the n_split partial states, and the token is
+// stored in row app_row of its dense page for later steps.
+struct MergeArgs {
+  const float* ws_o;
+  const float* ws_ml;
+  float* out;
+  int n_split;
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  int dtype;
+  float qscale;
+  int G, Hkv;
+  uint8_t* k_dst;   // page of (b, h) = (0, 0) receiving the token's key row
+  uint8_t* v_dst;   // its transposed value page
+  int64_t dst_bh_stride;  // bytes between the pages of consecutive (b, h)
+  int app_row;
+  int32_t* table_w;
+  int64_t app_page;
+  int32_t app_entry;
+};
+
+__device__ inline float load_elem(const void* p, int64_t i, int dtype) {
+  if (dtype == PKV_BF16) return __uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
+  return ((const float*)p)[i];
+}
+
+// Eq. 5 across splits: one 256-thread workgroup per (sequence, query head),
+// arranged as 8 groups of 32 lanes; lane c4 of group grp owns channels
+// 4 c4 .. 4 c4 + 3 of the splits grp, grp + 8, ...  Every load of the merge
+// (the split maxima, the group's own split states and partial outputs, q and
+// the new key) is issued up front, so the kernel waits on memory about once:
+// one barrier publishes the global maximum (and the new token's score), each
+// group then weights its own splits, and a second barrier sums the 8 groups.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeGroups = kMergeThreads / (kD / 4);
+constexpr int kMergePrefetch = 8;  // splits per group held in registers (n_split <= 64)
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
+  __shared__ float sh_m[kMergeThreads / 64], sh_dot[kMergeThreads / 64];
+  __shared__ float4 sh_acc[kMergeGroups][kD / 4];
+  __shared__ float sh_l[kMergeGroups];
   const int64_t row = blockIdx.x;
-  const int lane = threadIdx.x;
-  const float2* ml = (const float2*)(ws_ml + row * n_split * 2);
-  float M = -INFINITY;
-  for (int sp = lane; sp < n_split; sp += 64) M = fmaxf(M, ml[sp].x);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float L = 0.f;
-  for (int sp = lane; sp < n_split; sp += 64) {
-    const float2 v = ml[sp];
-    const float wt = M == -INFINITY ? 0.f : exp2f(v.x - M);  // empty split: weight 0
-    sh_w[sp] = wt;
-    L += wt * v.y;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int grp = tid / (kD / 4), c4 = tid % (kD / 4);
+  const int n_split = m.n_split;
+  const float2* ml = (const float2*)(m.ws_ml + row * n_split * 2);
+  const float4* op = (const float4*)(m.ws_o + row * n_split * kD) + c4;
+
+  // loads
+  float qk = 0.f;
+  int64_t bh = 0;
+  if (m.k_new) {
+    const int Hq = m.G * m.Hkv;
+    const int hq = (int)(row % Hq);
+    bh = (row / Hq) * m.Hkv + hq / m.G;
+    if (tid < kD) qk = load_elem(m.q, row * kD + tid, m.dtype) * load_elem(m.k_new, bh * kD + tid, m.dtype);
   }
+  float4 vnew = {0.f, 0.f, 0.f, 0.f};
+  if (m.k_new && tid < kD / 4) {
+    const int64_t vb = bh * kD + 4 * tid;
+    vnew = float4{load_elem(m.v_new, vb, m.dtype), load_elem(m.v_new, vb + 1, m.dtype),
+                  load_elem(m.v_new, vb + 2, m.dtype), load_elem(m.v_new, vb + 3, m.dtype)};
+  }
+  float mx = -INFINITY;
+  for (int sp = tid; sp < n_split; sp += kMergeThreads) mx = fmaxf(mx, ml[sp].x);
+  float2 own[kMergePrefetch];
+  float4 ov[kMergePrefetch];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  for (int i = 0; i < kMergePrefetch; ++i) {
+    const int sp = grp + kMergeGroups * i;
+    if (sp < n_split) {
+      own[i] = ml[sp];
+      ov[i] = op[(int64_t)sp * (kD / 4)];
+    }
+  }
+  // the new token goes into its dense page (one workgroup per (sequence, KV
+  // head)) and its table entry is set (one workgroup)
+  if (m.k_new) {
+    const int hq = (int)(row % (m.G * m.Hkv));
+    if (hq % m.G == 0 && tid < kD) {
+      const int esz = m.dtype == PKV_BF16 ? 2 : 4;
+      uint8_t* kd = m.k_dst + bh * m.dst_bh_stride + ((int64_t)m.app_row * kD + tid) * esz;
+      uint8_t* vd = m.v_dst + bh * m.dst_bh_stride + ((int64_t)tid * kP + m.app_row) * esz;
+      if (esz == 2) {
+        *(uint16_t*)kd = ((const uint16_t*)m.k_new)[bh * kD + tid];
+        *(uint16_t*)vd = ((const uint16_t*)m.v_new)[bh * kD + tid];
+      } else {
+        *(float*)kd = ((const float*)m.k_new)[bh * kD + tid];
+        *(float*)vd = ((const float*)m.v_new)[bh * kD + tid];
+      }
+    }
+    if (row == 0 && tid == 0) m.table_w[m.app_page] = m.app_entry;
+  }
+
+  // global maximum and the new token's score (log2 units)
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+    qk += __shfl_xor(qk, o);
+  }
+  if (lane == 0) {
+    sh_m[wv] = mx;
+    sh_dot[wv] = qk;
+  }
   __syncthreads();
-  if (lane < kD / 4) {
-    const float4* op = (const float4*)(ws_o + row * n_split * kD) + lane;
-    float4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int sp = 0; sp < n_split; ++sp) {
-      const float4 v = op[(int64_t)sp * (kD / 4)];
-      const float wt = sh_w[sp];
-      acc.x += wt * v.x;
-      acc.y += wt * v.y;
-      acc.z += wt * v.z;
-      acc.w += wt * v.w;
+  float M = -INFINITY, s_new = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kMergeThreads / 64; ++w) M = fmaxf(M, sh_m[w]);
+  if (m.k_new) s_new = (sh_dot[0] + sh_dot[1]) * m.qscale;
+  M = fmaxf(M, s_new);
+
+  // this group's splits, weighted e^(m_s - M) (empty split: weight 0)
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.f;
+  auto add = [&](float2 st, float4 v) {
+    const float wt = M == -INFINITY ? 0.f : exp2f(st.x - M);
+    acc.x += wt * v.x;
+    acc.y += wt * v.y;
+    acc.z += wt * v.z;
+    acc.w += wt * v.w;
+    lsum += wt * st.y;
+  };
+#pragma unroll
+  for (int i = 0; i < kMergePrefetch; ++i)
+    if (grp + kMergeGroups * i < n_split) add(own[i], ov[i]);
+  for (int sp = grp + kMergeGroups * kMergePrefetch; sp < n_split; sp += kMergeGroups)
+    add(ml[sp], op[(int64_t)sp * (kD / 4)]);
+  sh_acc[grp][c4] = acc;
+  if (c4 == 0) sh_l[grp] = lsum;
+  __syncthreads();
+  if (tid < kD / 4) {
+    float4 t = sh_acc[0][tid];
+    float L = sh_l[0];
+#pragma unroll
+    for (int gi = 1; gi < kMergeGroups; ++gi) {
+      const float4 u = sh_acc[gi][tid];
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
+      L += sh_l[gi];
+    }
+    if (m.k_new) {
+      const float w_new = exp2f(s_new - M);
+      t.x += w_new * vnew.x;
+      t.y += w_new * vnew.y;
+      t.z += w_new * vnew.z;
+      t.w += w_new * vnew.w;
+      L += w_new;
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    ((float4*)(out + row * kD))[lane] = float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    ((float4*)(m.out + row * kD))[tid] = float4{t.x * inv, t.y * inv, t.z * inv, t.w * inv};
   }
 }
 
@@ -722,8 +839,40 @@ int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact) {
 }
 
 hipError_t launch_merge(const CacheGeom& g, const AttnJob& job, hipStream_t stream) {
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((int64_t)g.B * g.Hq)), dim3(64), 0, stream,
-                     job.ws_o, job.ws_ml, job.out, job.n_split);
+  MergeArgs m;
+  m.ws_o = job.ws_o;
+  m.ws_ml = job.ws_ml;
+  m.out = job.out;
+  m.n_split = job.n_split;
+  m.q = job.q;
+  m.k_new = job.k_new;
+  m.v_new = job.v_new;
+  m.dtype = g.dtype;
+  m.qscale = kLog2e / sqrtf((float)kD);
+  m.G = g.G;
+  m.Hkv = g.Hkv;
+  m.k_dst = m.v_dst = nullptr;
+  m.dst_bh_stride = 0;
+  m.app_row = job.app_row;
+  m.table_w = (int32_t*)(g.base + g.lay.page_table);
+  m.app_page = job.app_page;
+  m.app_entry = job.app_entry;
+  if (job.k_new) {
+    const int64_t ppg_bytes = (int64_t)kP * kD * g.lay.elem_bytes;
+    const int64_t p = job.app_page;
+    if (p < g.n_s) {
+      m.k_dst = g.base + g.lay.sink_k + p * ppg_bytes;
+      m.v_dst = g.base + g.lay.sink_v + p * ppg_bytes;
+      m.dst_bh_stride = g.n_s * ppg_bytes;
+    } else {
+      const int64_t slot = (p - g.n_s) % (g.n_w + 1);
+      m.k_dst = g.base + g.lay.win_k + slot * ppg_bytes;
+      m.v_dst = g.base + g.lay.win_v + slot * ppg_bytes;
+      m.dst_bh_stride = (int64_t)(g.n_w + 1) * ppg_bytes;
+    }
+  }
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((int64_t)g.B * g.Hq)), dim3(kMergeThreads), 0, stream,
+                     m);
   return hipGetLastError();
 }
 

@@ -193,6 +193,16 @@ struct AttnJob {
   float* ws_ml;  // [B*Hq][n_split][2]
   int n_split;
   int64_t T, n_fact;
+  // Optional append folded into the merge (launch_merge): the new token
+  // (k_new / v_new [B][H_kv][d]) joins the Eq. 5 merge as one more state
+  // beside the splits (which cover tokens 0 .. T - 1), and is written to
+  // row app_row of page app_page (table entry app_entry after the append).
+  // k_new == nullptr: no append.
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  int64_t app_page = -1;
+  int app_row = -1;
+  int32_t app_entry = 0;
 };
 
 hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t stream);
