@@ -1,0 +1,170 @@
+"""GPU parity at the workloads' full sizes, in the launch configurations that
+bench.py times (default split counts, one launch over the whole batch).
+
+Sampling, so that the oracle finishes in seconds:
+- Workloads 2 and 3 (one decode step) and 4 (512 incremental steps): every
+  (sequence, KV head) holds the recipe's pages of (sequence 0, KV head 0),
+  so one oracle reconstruction serves all heads.  The queries are the
+  recipe's own, distinct per query head, and every query head's output is
+  checked (tolerance of the storage dtype).  Workload 4 checks its page table
+  at all 512 steps and the outputs at the steps around each promotion and at
+  every 32nd step.
+- Workload 5 (524288 pages): the bench's pool of 8192 distinct recipe pages
+  tiled to 524288.  All noise pages of the pool and 512 sampled pool pages are
+  checked against the oracle's SVD, each at one of its tiled copies, by the
+  reconstruction bound for bf16 factors; other copies of a page must hold
+  bit-identical factors.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import long_context_decode_pkv_amd as pkv
+from gpu_common import TOL, rel_err, require_gpu, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def replicated_kv(cfg_id, T):
+    """Stored K, V (B, H_kv, T, d) whose every head is the recipe's head
+    (0, 0), and that head's float64 values."""
+    cfg = synth.CONFIGS[cfg_id]
+    k, v = synth.kv_head(cfg, 0, 0, T)
+    ks, vs = synth.to_storage(k, cfg["dtype"]), synth.to_storage(v, cfg["dtype"])
+    shape = (cfg["B"], cfg["Hkv"]) + ks.shape
+    K = np.ascontiguousarray(np.broadcast_to(ks, shape))
+    V = np.ascontiguousarray(np.broadcast_to(vs, shape))
+    return K, V, synth.storage_to_f64(ks, cfg["dtype"]), synth.storage_to_f64(vs, cfg["dtype"])
+
+
+def recipe_queries(cfg_id):
+    cfg = synth.CONFIGS[cfg_id]
+    d = synth.decode_inputs(cfg_id, T=1)  # q does not depend on T
+    return d["q"], synth.storage_to_f64(d["q"], cfg["dtype"])
+
+
+def make_full_cache(cfg, max_tokens):
+    return pkv.Cache(batch=cfg["B"], n_q_heads=cfg["Hq"], n_kv_heads=cfg["Hkv"], rank_k=cfg["r_k"],
+                     rank_v=cfg["r_v"], sink=cfg["s"], window=cfg["w"], max_tokens=max_tokens,
+                     dtype=cfg["dtype"])
+
+
+def oracle_outputs(q64, Khat, Vhat):
+    """Naive attention of every query head (B, H_q, d) over one reconstructed head."""
+    B, Hq, d = q64.shape
+    return oracle.attention(q64.reshape(B * Hq, d), Khat, Vhat).reshape(B, Hq, d)
+
+
+def decode_full(cfg_id):
+    import torch
+    require_gpu()
+    cfg = synth.CONFIGS[cfg_id]
+    T, P, dt = cfg["T"], cfg["P"], cfg["dtype"]
+    K, V, k64, v64 = replicated_kv(cfg_id, T + 1)
+    q, q64 = recipe_queries(cfg_id)
+    cache = make_full_cache(cfg, T + 1)
+    Kd, Vd = to_dev(K, dt), to_dev(V, dt)
+    cache.prefill(Kd[:, :, :T].contiguous(), Vd[:, :, :T].contiguous())
+    qd = to_dev(q, dt)
+    o1 = to_f64(cache.decode(qd))  # pkv_decode_attn, default split count
+    # the bench's path: one pkv_decode_step appending token T
+    o2 = to_f64(cache.step(Kd[:, :, T].contiguous(), Vd[:, :, T].contiguous(), qd))
+    torch.cuda.synchronize()
+    for TT, o in ((T, o1), (T + 1, o2)):
+        Ks = oracle.reconstruct_cache(k64[:TT], TT, P, cfg["s"], cfg["w"], cfg["r_k"], dt)[0]
+        Vs = oracle.reconstruct_cache(v64[:TT], TT, P, cfg["s"], cfg["w"], cfg["r_v"], dt)[0]
+        ref = oracle_outputs(q64, Ks, Vs)
+        err = rel_err(o, ref)
+        print(f"[full size workload {cfg_id}] T={TT}: max err / max|o_ref| = {err:.3e} "
+              f"over {o.shape[0] * o.shape[1]} query heads")
+        assert err <= TOL[dt], (cfg_id, TT, err)
+    cls, slot = cache.page_table(-(-(T + 1) // P))
+    ocls, oslot = oracle.classify(T + 1, P, cfg["s"], cfg["w"])
+    np.testing.assert_array_equal(cls, ocls)
+    np.testing.assert_array_equal(slot, oslot)
+
+
+def test_qwen3_32b_layer_128k_full():
+    decode_full(3)
+
+
+def test_llama31_8b_layer_32k_full():
+    decode_full(2)
+
+
+def test_incremental_512_steps_full():
+    import torch
+    require_gpu()
+    cfg_id = 4
+    cfg = synth.CONFIGS[cfg_id]
+    T0, steps, P, dt = cfg["T"], cfg["steps"], cfg["P"], cfg["dtype"]
+    K, V, k64, v64 = replicated_kv(cfg_id, T0 + steps)
+    B, Hq = cfg["B"], cfg["Hq"]
+    cache = make_full_cache(cfg, T0 + steps)
+    Kd, Vd = to_dev(K, dt), to_dev(V, dt)
+    cache.prefill(Kd[:, :, :T0].contiguous(), Vd[:, :, :T0].contiguous())
+    ws = cache.workspace(512)
+    # one oracle head serves every (sequence, KV head): all B * H_q query heads on it
+    inc = oracle.IncrementalDecoder(k64[None, None], v64[None, None], P, cfg["s"], cfg["w"],
+                                    cfg["r_k"], cfg["r_v"], dt)
+    checked, promos, worst = 0, [], 0.0
+    for t in range(steps):
+        T = T0 + t
+        nf_before = cache.state()[1]
+        qs = synth.step_queries(cfg_id, t, B, Hq, 128, dt)
+        o = cache.step(Kd[:, :, T].contiguous(), Vd[:, :, T].contiguous(), to_dev(qs, dt),
+                       workspace=ws)
+        if cache.state()[1] > nf_before:
+            promos.append(t + 1)
+        cls, slot = cache.page_table(-(-(T + 1) // P))
+        ocls, oslot = oracle.classify(T + 1, P, cfg["s"], cfg["w"])
+        np.testing.assert_array_equal(cls, ocls, err_msg=f"step {t}")
+        np.testing.assert_array_equal(slot, oslot, err_msg=f"step {t}")
+        if (T + 1) % P in (0, 1) or t % 32 == 0 or t == steps - 1:
+            torch.cuda.synchronize()
+            q64 = synth.storage_to_f64(qs, dt).reshape(1, B * Hq, 128)
+            ref = inc.step(q64, T + 1)[0].reshape(B, Hq, 128)
+            err = rel_err(to_f64(o), ref)
+            worst = max(worst, err)
+            checked += 1
+            assert err <= TOL[dt], (t, err)
+    print(f"[full size workload 4] {steps} steps from T={T0}: promotions at {promos}; "
+          f"outputs checked at {checked} steps, worst err {worst:.3e}; page table at every step")
+    assert promos == [64 * k for k in range(1, steps // 64 + 1)]
+
+
+def test_batched_compression_full():
+    import torch
+    require_gpu()
+    cfg = synth.CONFIGS[5]
+    n_total = cfg["layers"] * cfg["Hkv"] * 2 * cfg["pages_per_head"]
+    n_pool = 8192
+    pool = synth.to_storage(synth.compression_pages(np.arange(n_pool), n_total), "bf16")
+    Xp = to_dev(pool, "bf16")
+    X = Xp.repeat(n_total // n_pool, 1, 1).contiguous()
+    assert X.shape[0] == n_total
+    g = np.random.default_rng(5)
+    noise = synth.noise_page_ids(5, n_total, 0.02)
+    noise = noise[noise < n_pool]
+    ids = np.unique(np.concatenate([noise, g.choice(n_pool, 512, replace=False)]))
+    copies = g.integers(0, n_total // n_pool, ids.size)
+    X64 = synth.storage_to_f64(pool[ids], "bf16")
+    U, S, Wt = oracle.svd_batch(X64)
+    nrm = np.sqrt((X64 ** 2).sum(axis=(1, 2)))
+    for r in cfg["ranks"]:
+        Lf, Rf, _ = pkv.compress_pages(X, r, out_dtype=torch.bfloat16, with_sigma=False)
+        torch.cuda.synchronize()
+        at = torch.from_numpy(ids + n_pool * copies).to("cuda:0")
+        L64, R64 = to_f64(Lf[at]), to_f64(Rf[at])
+        err = np.sqrt(((X64 - L64 @ R64) ** 2).sum(axis=(1, 2)))
+        opt = oracle.optimal_error(S, r)
+        bound = np.sqrt((1.001 * opt + 1e-5 * nrm) ** 2 + (2.0 ** -8 * nrm) ** 2)
+        worst = float(np.max(err / bound))
+        print(f"[full size workload 5] r={r}: {n_total} pages in one launch; {ids.size} pool "
+              f"pages checked ({noise.size} noise pages), worst err/bound {worst:.4f}")
+        assert np.all(err <= bound), (r, worst)
+        # other copies of the same pages: bit-identical factors
+        alt = torch.from_numpy(ids + n_pool * ((copies + 1) % (n_total // n_pool))).to("cuda:0")
+        assert torch.equal(Lf[at], Lf[alt]) and torch.equal(Rf[at], Rf[alt])
+        del Lf, Rf
