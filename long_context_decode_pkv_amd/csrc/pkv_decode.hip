@@ -394,8 +394,16 @@ constexpr int kMaxSplits = kMaxDecodeSplits;
 constexpr int kWaves = 4;
 
 // Waves per SIMD the matrix-core kernel is compiled for (register budget):
-// small ranks fit 3 (<= 168 VGPRs), the common ranks 2, the largest 1.
-constexpr int mfma_waves_per_simd(int n8) { return n8 <= 2 ? 3 : (n8 <= 6 ? 2 : 1); }
+// 2 up to r = 48, 1 above.  Three waves of the small ranks without key double
+// buffering streamed less (Llama-shaped layer, r = 16: 4.7 TB/s at 3 waves,
+// 6.45 TB/s at 2 waves with double-buffered keys).
+constexpr int mfma_waves_per_simd(int n8) { return n8 <= 6 ? 2 : 1; }
+
+// Key parts double-buffered where the extra page half fits the budget above
+// without spilling (all but r/8 = 5, 6).  Qwen3-32B-shaped layer (r = 24):
+// 51.8 -> 50.7 us.
+template <int N8>
+constexpr bool kKeyDoubleBuffer = N8 <= 4 || N8 >= 7;
 
 template <int N8>
 __global__ __launch_bounds__(256, mfma_waves_per_simd(N8)) void decode_mfma_kernel(DecodeArgs a) {
@@ -455,28 +463,48 @@ __global__ __launch_bounds__(256, mfma_waves_per_simd(N8)) void decode_mfma_kern
   }
 
   // factorized pages: the next page's key part streams in while this page's
-  // value half runs, and its value part while its key half runs
+  // value half runs, and its value part while its key half runs; where the
+  // register budget allows (kKeyDoubleBuffer), key parts are double-buffered
+  // so that K(e + 2) streams in from the end of page e's key half
   int64_t e = e0 > wl.D ? e0 : wl.D;
   if (e < e1) {
+    // the factor slot of logical page n_s + f is f (pages are factorized in
+    // order and never revisited), so unit e lives in slot e - D
     const uint8_t* fac_bh = a.fac + bh * a.F_max * a.page_bytes;
-    auto page_ptr = [&](int64_t ee) {
-      const int64_t p = unit_page(wl, a, ee);
-      return fac_bh + (int64_t)table_slot(a.table[p]) * a.page_bytes;
-    };
-    KRegs<N8> kr;
+    const int64_t kpb = a.k_part_bytes;
+    auto kptr = [&](int64_t ee) { return (const uint16_t*)(fac_bh + (ee - wl.D) * a.page_bytes); };
+    auto vptr = [&](int64_t ee) { return (const uint16_t*)(fac_bh + (ee - wl.D) * a.page_bytes + kpb); };
     VRegs<N8> vr;
-    const uint8_t* pp = page_ptr(e);
-    load_keys<N8>(kr, (const uint16_t*)pp, lane);
-    load_values<N8>(vr, (const uint16_t*)(pp + a.k_part_bytes), lane);
-    for (; e < e1; ++e) {
-      bf16x8 pb[2];
-      fact_keys<N8>(st, kr, qb, q4, rem, pb);
-      const bool more = e + 1 < e1;
-      const uint8_t* pn = more ? page_ptr(e + 1) : pp;
-      if (more) load_keys<N8>(kr, (const uint16_t*)pn, lane);
-      fact_values<N8>(st, vr, pb, rem);
-      if (more) load_values<N8>(vr, (const uint16_t*)(pn + a.k_part_bytes), lane);
-      pp = pn;
+    if constexpr (kKeyDoubleBuffer<N8>) {
+      KRegs<N8> ka, kb;
+      load_keys<N8>(ka, kptr(e), lane);
+      load_values<N8>(vr, vptr(e), lane);
+      if (e + 1 < e1) load_keys<N8>(kb, kptr(e + 1), lane);
+      auto step = [&](KRegs<N8>& kc) {
+        bf16x8 pb[2];
+        fact_keys<N8>(st, kc, qb, q4, rem, pb);
+        if (e + 2 < e1) load_keys<N8>(kc, kptr(e + 2), lane);
+        fact_values<N8>(st, vr, pb, rem);
+        if (e + 1 < e1) load_values<N8>(vr, vptr(e + 1), lane);
+      };
+      while (true) {
+        step(ka);
+        if (++e >= e1) break;
+        step(kb);
+        if (++e >= e1) break;
+      }
+    } else {
+      KRegs<N8> kr;
+      load_keys<N8>(kr, kptr(e), lane);
+      load_values<N8>(vr, vptr(e), lane);
+      for (; e < e1; ++e) {
+        bf16x8 pb[2];
+        fact_keys<N8>(st, kr, qb, q4, rem, pb);
+        const bool more = e + 1 < e1;
+        if (more) load_keys<N8>(kr, kptr(e + 1), lane);
+        fact_values<N8>(st, vr, pb, rem);
+        if (more) load_values<N8>(vr, vptr(e + 1), lane);
+      }
     }
   }
 
@@ -826,15 +854,17 @@ int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact) {
   (void)n_fact;
   const int64_t pages = (T + kP - 1) / kP;
   const int64_t bh = (int64_t)g.B * g.Hkv;
-  // one resident round: 256 CUs x (waves per SIMD) four-wave workgroups
-  const int n8 = (g.r_k > g.r_v ? g.r_k + 7 : g.r_v + 7) / 8;
-  const int64_t target = 256LL * (g.dtype == PKV_BF16 ? mfma_waves_per_simd(n8) : 2);
-  int64_t s = (target + bh - 1) / bh;
-  if (s > kMaxSplits) s = kMaxSplits;
-  const int64_t cap = (pages + 3) / 4;    // at least ~4 pages per workgroup
+  // Two four-wave workgroups per CU fill the chip at 2 waves per SIMD; halve
+  // the split count while a wave would get fewer than 16 pages and a CU would
+  // still get a workgroup.  Long runs per wave stream better than more waves
+  // (Qwen3-32B-shaped 128K layer: 32 splits 48.0 us, 64 splits 49.5 us).
+  const int wps = g.dtype == PKV_BF16 ? mfma_waves_per_simd((g.r_k > g.r_v ? g.r_k + 7 : g.r_v + 7) / 8) : 2;
+  int64_t s = (256LL * wps + bh - 1) / bh;
+  while (s > 1 && pages < 16 * 4 * s && (s / 2) * bh >= 256) s /= 2;
+  const int64_t cap = (pages + 3) / 4;  // at least ~4 pages per workgroup
   if (s > cap) s = cap;
+  if (s > kMaxSplits) s = kMaxSplits;
   if (s < 1) s = 1;
-  if (s > 1024) s = 1024;
   return (int)s;
 }
 
