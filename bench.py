@@ -181,6 +181,10 @@ def bench_decode(args, cfg_id, name):
     del K0, V0
     wss = [c.workspace(512) for c in caches]  # fits every split count
     P, n_s, n_w = cfg["P"], cfg["s"] // cfg["P"], cfg["w"] // cfg["P"]
+    aux = torch.cuda.Stream() if args.aux else None  # default priority
+    if aux is not None:
+        for c in caches:  # completed window pages are factorized early, on aux
+            c.set_aux_stream(aux)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
@@ -193,9 +197,11 @@ def bench_decode(args, cfg_id, name):
             return None
         T, nf, _ = c.state()
         due = (T + 1) // P - n_s - n_w > nf
-        # the partial kernel's own duration, or the promotion's
-        pkv.time_next_kernel(*(rec["promote"] if due else rec["partial"]))
-        rec["promoted"] = due
+        # the partial kernel's own duration, or (synchronous promotions) the
+        # decomposition's, which is then the first kernel of the step
+        timed_promo = due and aux is None
+        pkv.time_next_kernel(*(rec["promote"] if timed_promo else rec["partial"]))
+        rec["promoted"] = timed_promo
         c.step(rows_k[i], rows_v[i], qs[i], out=out, workspace=ws)
         rec["merge"][1].record()
         return T + 1, nf + (1 if due else 0)
@@ -233,6 +239,20 @@ def bench_decode(args, cfg_id, name):
     durs = np.array([flat[k]["partial"][0].elapsed_time(flat[k]["partial"][1]) * 1e-3 for k in keep])
     merges = np.array([flat[k]["partial"][1].elapsed_time(flat[k]["merge"][1]) * 1e-3 for k in keep])
     promos = [r["promote"][0].elapsed_time(r["promote"][1]) * 1e-3 for r in flat if r["promoted"]]
+    if aux is not None:
+        # early factorizations overlap later steps; time the same launch
+        # (one page of every (sequence, KV head, K/V)) on its own
+        pages = np.ascontiguousarray(inp["K"][:, :, :2 * P].reshape(-1, P, cfg["d"])[:2 * B * Hkv])
+        Xp = to_dev(pages, dt)
+        for _ in range(6):
+            a, b = ev(), ev()
+            a.record()
+            b.record()
+            pkv.time_next_kernel(a, b)
+            pkv.compress_pages(Xp, cfg["r_k"], with_sigma=False)
+            torch.cuda.synchronize()
+            promos.append(a.elapsed_time(b) * 1e-3)
+        promos = promos[1:]
     states = [states[k] for k in keep]
     nbytes = np.array([decode_bytes(cfg, B, Hkv, Hq, T, nf) for T, nf in states], dtype=np.float64)
     achieved = nbytes.sum() / durs.sum() / 1e9
@@ -263,7 +283,8 @@ def bench_decode(args, cfg_id, name):
                    "rank_v": cfg["r_v"], "sink": cfg["s"], "window": cfg["w"],
                    "layer_caches_rotated": NL,
                    "step": "pkv_decode_step per layer: promotion when a page leaves the window, "
-                           "decode partial, merge with the appended token folded in"},
+                           "decode partial, merge with the appended token folded in",
+                   "early_factorization": bool(args.aux)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None if traffic is None else traffic["fetch"] + traffic["write"],
@@ -454,6 +475,9 @@ def main():
     ap.add_argument("--layers", type=int, default=4,
                     help="independent layer caches decoded in rotation (defeats cache reuse)")
     ap.add_argument("--distinct-pages", type=int, default=8192)
+    ap.add_argument("--aux", action="store_true",
+                    help="decode workloads: factorize completed window pages early on a second "
+                         "stream (pkv_cache_set_aux_stream); measured slower on the 128K layer")
     ap.add_argument("--no-compress", dest="with_compress", action="store_false",
                     help="decode workloads: skip the batched-compression figure")
     args = ap.parse_args()

@@ -276,6 +276,25 @@ int32_t pkv_decode_step(pkv_cache* cache, const void* k_new, const void* v_new, 
                         float* out, void* workspace, uint64_t workspace_bytes, int32_t n_split,
                         void* stream);
 
+/*
+ * Early page factorization for pkv_decode_step (Sec. 3.3 (5): a page is
+ * factorized once, when it leaves the recent window; its factors depend only
+ * on the page's own tokens, which are final once the page is complete).
+ * aux_stream: a second hipStream_t (as void*) of the caller, at default
+ * priority, that outlives the cache's use of it.  When set, the step whose
+ * token completes a window page enqueues that page's factorization on
+ * aux_stream, ordered after the step's own work on its stream; the step at
+ * which the page leaves the window (w / P pages later) makes its stream wait
+ * for that factorization and flips the table entry.  The factorization thus
+ * overlaps later decode steps instead of lengthening one.  Outputs and cache
+ * contents are identical to those without it.  NULL (the default) turns it
+ * off.  Creates and owns a few hipEvents (no device memory).
+ * Errors: UNSUPPORTED (more than 64 window ring slots), PROMOTION_PENDING
+ * (changing or clearing the stream while early factorizations are
+ * outstanding), DEVICE.
+ */
+int32_t pkv_cache_set_aux_stream(pkv_cache* cache, void* aux_stream);
+
 /* Kernel timing (measurement only; no passage of the method).
  *
  * start_event, stop_event: hipEvent_t handles (as void*) that the caller

@@ -85,6 +85,7 @@ def lib():
         "pkv_read_page_table": ([vp, vp, vp, i64, vp], i32),
         "pkv_time_next_kernel": ([vp, vp], i32),
         "pkv_decode_step": ([vp, vp, vp, vp, vp, vp, u64, i32, vp], i32),
+        "pkv_cache_set_aux_stream": ([vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -317,6 +318,14 @@ class Cache:
                                       _dev_ptr(out, None, "out"), _stream(self.device)),
                "pkv_decode_merge")
         return out
+
+    def set_aux_stream(self, stream=None):
+        """Factorize completed window pages early on `stream` (a
+        torch.cuda.Stream at default priority), overlapping later steps;
+        None turns it off (pkv_cache_set_aux_stream)."""
+        ptr = ctypes.c_void_p(stream.cuda_stream) if stream is not None else None
+        _check(lib().pkv_cache_set_aux_stream(self._h, ptr), "pkv_cache_set_aux_stream")
+        self._aux = stream  # keep the stream alive while the cache uses it
 
     def step(self, k, v, q, out=None, n_split: int = 0, workspace=None):
         """One decode step (pkv_decode_step): append (k, v), promote the page

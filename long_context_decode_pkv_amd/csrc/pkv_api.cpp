@@ -15,6 +15,13 @@
 
 using namespace pkv;
 
+// Early factorization (pkv_cache_set_aux_stream): a window page is factorized
+// on the caller's auxiliary stream as soon as its last token is written; the
+// step at which it leaves the window then waits for that work and flips its
+// table entry.  Pages [early_lo, early_hi) are factorized or in flight;
+// ready[ring slot] marks the completion of each.
+constexpr int kMaxRing = 64;
+
 struct pkv_cache {
   pkv_shape shape;
   pkv_layout lay;
@@ -22,6 +29,11 @@ struct pkv_cache {
   int64_t T;
   int64_t n_fact;
   int32_t pending;  // a completed page waits for promotion
+  hipStream_t aux = nullptr;
+  hipEvent_t written = nullptr;
+  hipEvent_t ready[kMaxRing] = {};
+  int n_ready = 0;
+  int64_t early_lo = 0, early_hi = 0;
 };
 
 namespace {
@@ -129,12 +141,12 @@ float bf16_round_host(float x, uint16_t* bits) {
 // Factorize the page that leaves the recent window (logical page n_s + n_fact,
 // in ring slot (p - n_s) mod (n_w + 1)) into factor slot n_fact, flip its
 // table entry to FACT and count it (Sec. 3.3 (5)).
-int32_t promote_now(pkv_cache* c, void* stream) {
+// Factorize window page p (in ring slot (p - n_s) mod (n_w + 1)) into factor
+// slot p - n_s, on `stream`.
+hipError_t factorize_page(pkv_cache* c, int64_t p, hipStream_t s) {
   const CacheGeom g = geom_of(c);
-  const int64_t f = c->n_fact;            // factor slot of the page
-  const int64_t p_old = g.n_s + f;        // logical page leaving the window
-  if (f >= g.F_max) return PKV_ERR_CAPACITY;
-  const int64_t ring = (p_old - g.n_s) % (g.n_w + 1);
+  const int64_t f = p - g.n_s;
+  const int64_t ring = f % (g.n_w + 1);
   const int64_t esz = c->lay.elem_bytes;
   const int64_t ppg = (int64_t)kP * kD;
   CompressJob job;
@@ -157,12 +169,52 @@ int32_t promote_now(pkv_cache* c, void* stream) {
   job.f0 = f;
   job.page_bytes = c->lay.factor_page_bytes;
   job.k_part_bytes = c->lay.factor_k_elems * esz;
+  return launch_compress(job, s);
+}
+
+// The page leaving the window (n_s + n_fact) becomes FACT: factorized now, or
+// (early factorization) waited for on `stream`; then its table entry flips.
+int32_t promote_now(pkv_cache* c, void* stream) {
+  const CacheGeom g = geom_of(c);
+  const int64_t f = c->n_fact;            // factor slot of the page
+  const int64_t p_old = g.n_s + f;        // logical page leaving the window
+  if (f >= g.F_max) return PKV_ERR_CAPACITY;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_compress(job, s);
+  hipError_t e = hipSuccess;
+  if (c->early_lo <= p_old && p_old < c->early_hi) {
+    e = hipStreamWaitEvent(s, c->ready[f % (g.n_w + 1)], 0);
+    c->early_lo = p_old + 1;
+  } else {
+    e = factorize_page(c, p_old, s);
+  }
   if (e == hipSuccess) e = launch_table_set(g, p_old, table_entry(PKV_PAGE_FACT, (int)f), s);
   if (e != hipSuccess) return PKV_ERR_DEVICE;
   c->n_fact += 1;
   return PKV_OK;
+}
+
+// After the launch that wrote the last token of window page p: factorize it
+// on the auxiliary stream, ordered after that launch.
+int32_t factorize_early(pkv_cache* c, int64_t p, hipStream_t main) {
+  const CacheGeom g = geom_of(c);
+  if (p - g.n_s >= g.F_max) return PKV_OK;  // never leaves the window within capacity
+  hipError_t e = hipEventRecord(c->written, main);
+  if (e == hipSuccess) e = hipStreamWaitEvent(c->aux, c->written, 0);
+  if (e == hipSuccess) e = factorize_page(c, p, c->aux);
+  if (e == hipSuccess) e = hipEventRecord(c->ready[(p - g.n_s) % (g.n_w + 1)], c->aux);
+  if (e != hipSuccess) return PKV_ERR_DEVICE;
+  if (c->early_lo == c->early_hi) c->early_lo = p;
+  c->early_hi = p + 1;
+  return PKV_OK;
+}
+
+void release_aux(pkv_cache* c) {
+  if (c->written) (void)hipEventDestroy(c->written);
+  for (int i = 0; i < c->n_ready; ++i) (void)hipEventDestroy(c->ready[i]);
+  c->written = nullptr;
+  c->n_ready = 0;
+  c->aux = nullptr;
+  c->early_lo = c->early_hi = 0;
 }
 
 
@@ -321,7 +373,34 @@ int32_t pkv_cache_create(const pkv_shape* shape, void* device_buffer, uint64_t d
   return PKV_OK;
 }
 
-void pkv_cache_destroy(pkv_cache* cache) { delete cache; }
+void pkv_cache_destroy(pkv_cache* cache) {
+  if (!cache) return;
+  release_aux(cache);
+  delete cache;
+}
+
+int32_t pkv_cache_set_aux_stream(pkv_cache* c, void* aux_stream) {
+  if (!c) return PKV_ERR_INVALID_ARG;
+  if (c->aux) {
+    // work already queued there must finish before its events go away
+    if (c->early_lo < c->early_hi) return PKV_ERR_PROMOTION_PENDING;
+    release_aux(c);
+  }
+  if (!aux_stream) return PKV_OK;
+  const int ring = c->lay.n_ring_slots;
+  if (ring > kMaxRing) return PKV_ERR_UNSUPPORTED;
+  if (hipEventCreateWithFlags(&c->written, hipEventDisableTiming) != hipSuccess) return PKV_ERR_DEVICE;
+  for (int i = 0; i < ring; ++i) {
+    if (hipEventCreateWithFlags(&c->ready[i], hipEventDisableTiming) != hipSuccess) {
+      release_aux(c);
+      return PKV_ERR_DEVICE;
+    }
+    c->n_ready = i + 1;
+  }
+  c->aux = (hipStream_t)aux_stream;
+  c->early_lo = c->early_hi = 0;
+  return PKV_OK;
+}
 
 int32_t pkv_cache_state(const pkv_cache* c, int64_t* T, int64_t* n_fact, int32_t* pending) {
   if (!c) return PKV_ERR_INVALID_ARG;
@@ -368,6 +447,12 @@ int32_t pkv_prefill(pkv_cache* c, const void* K, const void* V, int64_t T, void*
   const CacheGeom g = geom_of(c);
   const int64_t n_fact = steady_fact(T, kP, g.n_s, g.n_w);
   hipStream_t s = (hipStream_t)stream;
+  if (c->aux && c->early_lo < c->early_hi) {
+    // early factorizations still in flight read the ring slots and write the
+    // factor slots this prefill overwrites
+    for (int i = 0; i < c->n_ready; ++i)
+      if (hipStreamWaitEvent(s, c->ready[i], 0) != hipSuccess) return PKV_ERR_DEVICE;
+  }
   hipError_t e = launch_prefill_dense(g, K, V, T, n_fact, s);
   if (e == hipSuccess && n_fact > 0) {
     CompressJob job;
@@ -397,6 +482,7 @@ int32_t pkv_prefill(pkv_cache* c, const void* K, const void* V, int64_t T, void*
   c->T = T;
   c->n_fact = n_fact;
   c->pending = 0;
+  c->early_lo = c->early_hi = 0;
   return PKV_OK;
 }
 
@@ -551,6 +637,9 @@ int32_t pkv_decode_step(pkv_cache* c, const void* k_new, const void* v_new, cons
   if (e == hipSuccess) e = launch_merge(g, job, s);
   if (e != hipSuccess) return PKV_ERR_DEVICE;
   c->T = T1;
+  // the token completed window page p: factorize it ahead of the step at
+  // which it leaves the window
+  if (c->aux && row == kP - 1 && p >= g.n_s && g.n_w > 0) return factorize_early(c, p, s);
   return PKV_OK;
 }
 

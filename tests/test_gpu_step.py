@@ -144,3 +144,56 @@ def test_step_errors():
     with pytest.raises(pkv.PKVError) as ei:  # full
         cache.step(k, v, q)
     assert ei.value.status == 3
+
+
+def test_step_with_early_factorization():
+    """Pages factorized early on an auxiliary stream: outputs and caches
+    bit-identical to the synchronous step, across several promotions."""
+    import torch
+    require_gpu()
+    cfg_id, T0, steps = 2, 64 * 12 + 40, 300
+    d = synth.decode_inputs(cfg_id, T=T0 + steps, B=2, kv_heads=2)
+    dt = d["cfg"]["dtype"]
+    a, b, Kd, Vd = _twin_caches(d, T0, steps)
+    aux = torch.cuda.Stream()
+    a.set_aux_stream(aux)
+    ws_a, ws_b = a.workspace(512), b.workspace(512)
+    promos = 0
+    for t in range(steps):
+        T = T0 + t
+        k = Kd[:, :, T].contiguous()
+        v = Vd[:, :, T].contiguous()
+        q = to_dev(synth.step_queries(cfg_id, t, d["B"], d["Hq"], 128, dt), dt)
+        nf = b.state()[1]
+        oa = a.step(k, v, q, workspace=ws_a)
+        ob = b.step(k, v, q, workspace=ws_b)
+        promos += b.state()[1] > nf
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), (t, (oa - ob).abs().max().item())
+        assert a.state() == b.state()
+    aux.synchronize()
+    assert torch.equal(a.buffer, b.buffer)
+    print(f"[early factorization] {steps} steps, {promos} promotions: bit-identical")
+    assert promos >= 4
+
+
+def test_aux_stream_switching():
+    import torch
+    require_gpu()
+    d = synth.decode_inputs(2, T=64 * 8, B=1, kv_heads=1)
+    cache = make_cache(d, max_tokens=64 * 8)
+    Kd, Vd = to_dev(d["K"], "bf16"), to_dev(d["V"], "bf16")
+    cache.prefill(Kd[:, :, :64 * 4 + 62].contiguous(), Vd[:, :, :64 * 4 + 62].contiguous())
+    aux = torch.cuda.Stream()
+    cache.set_aux_stream(aux)
+    q = to_dev(d["q"], "bf16")
+    for T in (64 * 4 + 62, 64 * 4 + 63):  # the second step completes a window page
+        cache.step(Kd[:, :, T].contiguous(), Vd[:, :, T].contiguous(), q)
+    with pytest.raises(pkv.PKVError) as ei:  # its factorization is outstanding
+        cache.set_aux_stream(None)
+    assert ei.value.status == 5
+    torch.cuda.synchronize()
+    # a prefill resets the cache (and orders itself after the early work)
+    cache.prefill(Kd[:, :, :100].contiguous(), Vd[:, :, :100].contiguous())
+    cache.set_aux_stream(None)
+    cache.set_aux_stream(aux)

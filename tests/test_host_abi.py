@@ -170,6 +170,8 @@ def test_create_validation_without_gpu():
     # empty cache: attention is refused before any launch
     assert L.pkv_decode_attn(h, ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096),
                              ws.value, 4, None) == 1
+    assert L.pkv_cache_set_aux_stream(h, None) == 0  # off by default; clearing is a no-op
+    assert L.pkv_cache_set_aux_stream(None, None) == 1
     L.pkv_cache_destroy(h)
 
 
