@@ -79,16 +79,23 @@ __device__ __forceinline__ float row16_reduce(float x) {
   return x;
 }
 
+template <int Op, int Ctrl, int RowMask>
+__device__ __forceinline__ float dpp_rows(float y) {
+  // lanes outside RowMask keep the identity of Op
+  constexpr float id = Op == 0 ? 0.f : (Op == 1 ? -__builtin_inff() : __builtin_inff());
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(id), __float_as_int(y), Ctrl, RowMask, 0xf, false));
+}
+
+// Sum / max / min over the whole wave: row reductions, then row 0 into row 1
+// and row 2 into row 3 (row_bcast:15), then rows 0-1 into rows 2-3
+// (row_bcast:31); lane 63 holds the result.
 template <int Op>
 __device__ __forceinline__ float wave_reduce(float x) {
-  const float s = row16_reduce<Op>(x);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 48));
-  if constexpr (Op == 0) return (r0 + r1) + (r2 + r3);
-  else if constexpr (Op == 1) return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-  else return fminf(fminf(r0, r1), fminf(r2, r3));
+  float s = row16_reduce<Op>(x);
+  s = combine<Op>(s, dpp_rows<Op, 0x142, 0xa>(s));
+  s = combine<Op>(s, dpp_rows<Op, 0x143, 0xc>(s));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 63));
 }
 
 // 1. G into the row registers: lane i gets G[i][0..63].
@@ -132,10 +139,11 @@ __device__ __forceinline__ void tridiagonalize(TriShared& sh, float (&g)[kP], fl
     const float tail = wave_reduce<0>(lane >= k + 2 ? x * x : 0.f);
     // H_k = I - tau v v^T; tail == 0 means no reflection (tau = 0, v = e_{k+1})
     const bool refl = tail > 0.f;
-    const float xn = sqrtf(fmaf(alpha, alpha, tail));
+    // v_sqrt_f32 / v_rcp_f32 (1 ulp): the reflector's own rounding is of that order
+    const float xn = __builtin_amdgcn_sqrtf(fmaf(alpha, alpha, tail));
     const float beta = refl ? (alpha >= 0.f ? -xn : xn) : alpha;
-    const float tau = refl ? (beta - alpha) / beta : 0.f;
-    const float scal = refl ? 1.f / (alpha - beta) : 0.f;
+    const float tau = refl ? (beta - alpha) * __builtin_amdgcn_rcpf(beta) : 0.f;
+    const float scal = refl ? __builtin_amdgcn_rcpf(alpha - beta) : 0.f;
     const float vi = lane == k + 1 ? 1.f : (lane >= k + 2 ? x * scal : 0.f);
     sh.v[lane] = vi;
     __syncthreads();
@@ -187,8 +195,10 @@ __device__ __forceinline__ void tridiagonalize(TriShared& sh, float (&g)[kP], fl
 
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// Number of eigenvalues of T below x: negative pivots of T - x I = L D L^T.
-__device__ __forceinline__ int sturm_count(const TriShared& sh, float x, float pivmin) {
+// Number of eigenvalues of T below x: non-positive pivots of T - x I = L D L^T.
+// The couplings b2s are floored at a tiny positive value (setup), so a zero
+// pivot gives rcp = inf and the next pivot -inf, never 0 * inf.
+__device__ __forceinline__ int sturm_count(const TriShared& sh, float x) {
   int cnt = 0;
   float d = 1.f;
 #pragma unroll 4
@@ -199,21 +209,21 @@ __device__ __forceinline__ int sturm_count(const TriShared& sh, float x, float p
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       d = fmaf(-bv[e], rcp(d), av[e] - x);
-      d = fabsf(d) < pivmin ? -pivmin : d;
-      cnt += d < 0.f ? 1 : 0;
+      cnt += d <= 0.f ? 1 : 0;
     }
   }
   return cnt;
 }
 
-// Fixed multisection rounds for L points per eigenvalue: (L+1)^n >= 2^25.
+// Rounds of L-point multisection after the 65-point first round:
+// 65 (L + 1)^n >= 2^25.
 __device__ __forceinline__ int multisection_rounds(int L) {
   switch (L) {
-    case 2: return 16;
-    case 4: return 11;
-    case 8: return 8;
-    case 16: return 7;
-    default: return 5;  // 32, 64
+    case 2: return 12;
+    case 4: return 9;
+    case 8: return 6;
+    case 16: return 5;
+    default: return 4;  // 32, 64
   }
 }
 
@@ -295,13 +305,16 @@ __device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t
   sh.b[lane] = lane < kP - 1 ? my_b : 0.f;
   __syncthreads();
   const float bl = lane > 0 ? sh.b[lane - 1] : 0.f, br = sh.b[lane];
-  sh.b2s[lane] = bl * bl;
   const float glo = wave_reduce<2>(my_a - fabsf(bl) - fabsf(br));
   const float ghi = wave_reduce<1>(my_a + fabsf(bl) + fabsf(br));
   const float pivmin = 0x1p-126f * fmaxf(1.f, wave_reduce<1>(br * br));
+  sh.b2s[lane] = fmaxf(bl * bl, 0x1p-126f);
   __syncthreads();
 
-  // 3. the r largest eigenvalues: L lanes per eigenvalue
+  // 3. the r largest eigenvalues.  First round: the 64 lanes count at 64
+  // points spread over the Gershgorin interval, which brackets every
+  // eigenvalue to 1/65 of it; then L lanes per eigenvalue refine their
+  // bracket by L-point multisection.
   int rp = 1;
   while (rp < r) rp <<= 1;
   const int L = kP / rp;
@@ -310,11 +323,24 @@ __device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t
   const int j = jl < r ? jl : r - 1;  // descending index
   const int m = kP - 1 - j;           // ascending index
   float lo = glo, hi = ghi;
+  {
+    const float x0 = fmaf(ghi - glo, (float)(lane + 1) / (float)(kP + 1), glo);
+    sh.xrow[lane] = x0;
+    sh.w[lane] = __int_as_float(sturm_count(sh, x0));
+    __syncthreads();
+#pragma unroll 8
+    for (int l = 0; l < kP; ++l) {
+      const float xl = sh.xrow[l];
+      const int cl = __float_as_int(sh.w[l]);
+      if (cl <= m) lo = fmaxf(lo, xl);
+      else hi = fminf(hi, xl);
+    }
+  }
   const int rounds = multisection_rounds(L);
   const float frac = (float)(t + 1) / (float)(L + 1);
   for (int it = 0; it < rounds; ++it) {
     const float x = fmaf(hi - lo, frac, lo);
-    const int cnt = sturm_count(sh, x, pivmin);
+    const int cnt = sturm_count(sh, x);
     float nlo = cnt <= m ? x : lo, nhi = cnt <= m ? hi : x;
     for (int o = 1; o < L; o <<= 1) {
       nlo = fmaxf(nlo, __shfl_xor(nlo, o));
