@@ -161,6 +161,70 @@ def factorize(X, r, store=None):
     return Lf, Rf, S
 
 
+# --------------------------------------------------------------------------
+# INT4 factors (Sec. 4.3 "Quantization Compatibility")
+# --------------------------------------------------------------------------
+
+INT4_MAX = 7  # symmetric INT4: codes -7 .. 7
+
+
+def quantize_int4(x, axis):
+    """Symmetric INT4 quantization of x with one scale per group, a group
+    being all entries along `axis` (Sec. 4.3).  Per group: s = max|x| / 7,
+    rounded nearest-even to bfloat16 (the scale is stored at 16 bits);
+    q = x / s rounded half to even, clamped to [-7, 7]; q = 0 where s = 0.
+    Returns (q as int8, s as float64 with `axis` kept, length 1)."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.max(np.abs(x), axis=axis, keepdims=True)
+    s = round_to(amax / INT4_MAX, "bf16")
+    safe = np.where(s > 0, s, 1.0)
+    q = np.clip(np.rint(x / safe), -INT4_MAX, INT4_MAX)
+    q = np.where(s > 0, q, 0.0)
+    return q.astype(np.int8), s
+
+
+def dequantize_int4(q, s):
+    return q.astype(np.float64) * s
+
+
+def int4_factors(U, S, Wt, r, kind):
+    """Sec. 4.3: the singular values are split between the two factors,
+    Lt = U_r Sigma_r^(1/2) (P x r) and Rt = Sigma_r^(1/2) W_r^T (r x d), and
+    each factor is INT4-quantized: Lt column-wise for keys and row-wise for
+    values, Rt column-wise for both.  Returns the dequantized (Lt, Rt)."""
+    h = np.sqrt(S[..., :r])
+    Lt = U[..., :, :r] * h[..., None, :]
+    Rt = Wt[..., :r, :] * h[..., :, None]
+    lq, ls = quantize_int4(Lt, axis=-2 if kind == "K" else -1)
+    rq, rs = quantize_int4(Rt, axis=-2)
+    return dequantize_int4(lq, ls), dequantize_int4(rq, rs)
+
+
+def stored_factors(U, S, Wt, r, store, kind):
+    """The rank-r factors a cache stores: bf16 / f32 / exact (store None)
+    placements of Eq. 2 (Lf = U_r Sigma_r, Rf = W_r^T, rounded), or the INT4
+    factors of Sec. 4.3 (store 'int4'), as float64."""
+    if store == "int4":
+        return int4_factors(U, S, Wt, r, kind)
+    Lf, Rf = truncate(U, S, Wt, r)
+    if store:
+        Lf, Rf = round_to(Lf, store), round_to(Rf, store)
+    return Lf, Rf
+
+
+def int4_storage_ratio(T, P, d, r_k, r_v, n_dense_pages):
+    """Whole-cache storage of a T-token cache (T a multiple of P) with INT4
+    factors and 16-bit scales, over its dense bf16 storage (Sec. 4.3): a
+    factorized K/V page pair holds (r_K + r_V)(P + d) four-bit codes and the
+    scales of its four factors (r_K per column of Lt_K, d per column of Rt_K,
+    P per row of Lt_V, d per column of Rt_V); dense pages keep 2 P d bf16."""
+    n_pages = T // P
+    n_fact = n_pages - n_dense_pages
+    fact_bytes = (r_k + r_v) * (P + d) / 2 + 2 * (r_k + d + P + d)
+    dense_bytes = 2 * P * d * 2
+    return (n_fact * fact_bytes + n_dense_pages * dense_bytes) / (n_pages * dense_bytes)
+
+
 def optimal_error(S, r):
     """Eckart-Young-Mirsky: the best rank-r Frobenius error from the spectrum."""
     tail = np.asarray(S)[..., r:]
@@ -264,10 +328,11 @@ def merge_states(states):
 # Whole-cache decode (the quantity the GPU path is checked against)
 # --------------------------------------------------------------------------
 
-def reconstruct_cache(X, T, P, s, w, r, store, n_fact=None, with_metrics=False):
-    """X: (T, d) dense pages of one (sequence, KV head, K or V).  Returns
-    (Xhat_stored, Xhat_exact, metrics) where FACT pages are replaced by their
-    rank-r truncated SVD (stored = factors rounded to `store`)."""
+def reconstruct_cache(X, T, P, s, w, r, store, n_fact=None, with_metrics=False, kind="K"):
+    """X: (T, d) dense pages of one (sequence, KV head, K or V: `kind`).
+    Returns (Xhat_stored, Xhat_exact, metrics) where FACT pages are replaced
+    by their rank-r truncated SVD (stored = the factors the cache keeps, see
+    stored_factors)."""
     X = np.asarray(X, dtype=np.float64)[:T]
     cls, _ = classify(T, P, s, w, n_fact)
     fact = np.nonzero(cls == FACT)[0]
@@ -279,8 +344,7 @@ def reconstruct_cache(X, T, P, s, w, r, store, n_fact=None, with_metrics=False):
         U, S, Wt = svd_batch(pages)
         Lf, Rf = truncate(U, S, Wt, r)
         exact = Lf @ Rf
-        Lfs = round_to(Lf, store) if store else Lf
-        Rfs = round_to(Rf, store) if store else Rf
+        Lfs, Rfs = stored_factors(U, S, Wt, r, store, kind)
         stored = Lfs @ Rfs
         for k, p in enumerate(fact):
             Xs[p * P:(p + 1) * P] = stored[k]
@@ -313,8 +377,8 @@ def decode(q, K, V, T, P, s, w, r_k, r_v, store, n_fact=None, kv_heads=None):
     heads = range(Hkv) if kv_heads is None else kv_heads
     for b in range(B):
         for h in heads:
-            Ks, Ke, _ = reconstruct_cache(K[b, h], T, P, s, w, r_k, store, n_fact)
-            Vs, Ve, _ = reconstruct_cache(V[b, h], T, P, s, w, r_v, store, n_fact)
+            Ks, Ke, _ = reconstruct_cache(K[b, h], T, P, s, w, r_k, store, n_fact, kind="K")
+            Vs, Ve, _ = reconstruct_cache(V[b, h], T, P, s, w, r_v, store, n_fact, kind="V")
             qs = q[b, h * G:(h + 1) * G]
             o_s[b, h * G:(h + 1) * G] = attention(qs, Ks, Vs)
             o_e[b, h * G:(h + 1) * G] = attention(qs, Ke, Ve)
@@ -372,10 +436,8 @@ class IncrementalDecoder:
             U, S, Wt = svd_batch(pages)
             Lf, Rf = truncate(U, S, Wt, self.r[kind])
             exact = Lf @ Rf
-            if self.store:
-                stored = round_to(Lf, self.store) @ round_to(Rf, self.store)
-            else:
-                stored = exact
+            Ls, Rs = stored_factors(U, S, Wt, self.r[kind], self.store, "K" if kind == 0 else "V")
+            stored = Ls @ Rs
             for k, key in enumerate(items):
                 self.done[key] = (stored[k], exact[k])
 
