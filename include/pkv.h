@@ -22,9 +22,11 @@
  *    device work of a call is enqueued on it in order.
  *  - Calls on one cache must be serialized by the caller (they update the
  *    cache's host-side state); distinct caches are independent.
- *  - dtype: PKV_BF16 (bfloat16 storage, float32 arithmetic) or PKV_F32.
- *    K, V, q and the stored factors share the cache's dtype; attention output
- *    is float32.
+ *  - dtype: PKV_BF16 (bfloat16 storage, float32 arithmetic), PKV_F32, or
+ *    PKV_BF16_INT4 (bfloat16 K, V, q and dense pages; factor pages held as
+ *    the INT4 factors of Sec. 4.3).  K, V, q and the dense pages have the
+ *    cache's element type (bf16 for PKV_BF16_INT4); attention output is
+ *    float32.
  *  - Fixed in this version: head_dim d = 128 and page length P = 64 (other
  *    values return PKV_ERR_UNSUPPORTED); GQA group size G = H_q / H_kv <= 8.
  */
@@ -48,7 +50,16 @@ typedef enum pkv_status {
   PKV_ERR_DEVICE = 6             /* a HIP runtime call or kernel launch failed */
 } pkv_status;
 
-typedef enum pkv_dtype { PKV_BF16 = 0, PKV_F32 = 1 } pkv_dtype;
+/*
+ * Storage formats.  PKV_BF16_INT4 (Sec. 4.3 "Quantization Compatibility"):
+ * the singular values are split between the factors, Lt = U_r Sigma_r^(1/2)
+ * (P x r) and Rt = Sigma_r^(1/2) W_r^T (r x d), and each factor is stored as
+ * symmetric 4-bit codes c in -7..7 with one bfloat16 scale s per group:
+ * per column of Lt_K, Rt_K and Rt_V, per row of Lt_V;
+ * s = bf16_rne(max |x| / 7), c = clamp(rint(x / s), -7, 7) (c = 0 where
+ * s = 0), x ~ c s.  Ranks up to 32; dense pages are bfloat16.
+ */
+typedef enum pkv_dtype { PKV_BF16 = 0, PKV_F32 = 1, PKV_BF16_INT4 = 2 } pkv_dtype;
 
 /* Page classes reported by the page table (Sec. 3.3 (1)-(3), Sec. 4.1). */
 typedef enum pkv_page_class {
@@ -90,6 +101,8 @@ typedef struct pkv_shape {
  * kernel's matrix-core register layout; pkv_pack_factors and
  * pkv_unpack_factors convert between it and row-major Lf (P x r), Rf (r x d).
  * Ranks are padded to a multiple of 8 inside a part (padding is zero).
+ * PKV_BF16_INT4 parts hold codes and scales in their own interleaved order;
+ * pkv_pack_factors_int4 and pkv_unpack_factors_int4 convert it.
  */
 typedef struct pkv_layout {
   uint64_t sink_k, sink_v, win_k, win_v, factors, page_table;
@@ -98,11 +111,13 @@ typedef struct pkv_layout {
   int64_t n_ring_slots;      /* n_w + 1 */
   int64_t max_fact_pages;    /* F_max = max(0, floor(T_max/P) - n_s - n_w) */
   int64_t max_pages;         /* ceil(T_max / P) */
-  int64_t elem_bytes;        /* 2 (bf16) or 4 (f32) */
+  int64_t elem_bytes;        /* bytes of a dense element: 2 (bf16, bf16+int4) or 4 (f32) */
   int64_t dense_page_bytes;  /* P * d * elem_bytes */
-  int64_t factor_k_elems;    /* packed elements of a K part: r8_K (P + d) */
+  int64_t factor_k_elems;    /* packed elements (INT4: codes) of a K part: r8_K (P + d) */
   int64_t factor_v_elems;    /* r8_V (P + d) */
-  int64_t factor_page_bytes; /* (factor_k_elems + factor_v_elems) * elem_bytes */
+  int64_t factor_page_bytes; /* factor_k_bytes + factor_v_bytes */
+  int64_t factor_k_bytes;    /* bytes of a K part (its offset in the page is 0) */
+  int64_t factor_v_bytes;    /* bytes of a V part (offset factor_k_bytes) */
 } pkv_layout;
 
 typedef struct pkv_cache pkv_cache; /* opaque host handle */
@@ -145,6 +160,28 @@ int32_t pkv_pack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t 
                          const float* Lf, const float* Rf, void* packed);
 int32_t pkv_unpack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t dtype,
                            const void* packed, float* Lf, float* Rf);
+
+/* Bytes of one factor part (kind: PKV_KEYS / PKV_VALUES) of rank r in
+ * storage format `dtype` (for PKV_BF16_INT4 the INT4 part of Sec. 4.3; its
+ * K and V parts differ in size).  Host only. */
+int32_t pkv_factor_part_bytes(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t dtype,
+                              int64_t* bytes);
+
+/*
+ * Host-side conversion between one PKV_BF16_INT4 factor part (host memory of
+ * pkv_factor_part_bytes bytes) and its codes and scales (Sec. 4.3):
+ *   Lq [P][r] int8 codes of Lt, Rq [r][d] int8 codes of Rt, values -7..7;
+ *   Ls scales of Lt: [r] (keys, per column) or [P] (values, per row);
+ *   Rs [d] scales of Rt (per column).
+ * Scales are float32 here and bfloat16 in the part (packing rounds
+ * nearest-even).  Packing sets padding ranks to code 0, scale 0.
+ * Errors: INVALID_ARG (null pointer, bad kind, r < 1, r > min(P, d), a code
+ * outside -7..7), UNSUPPORTED (P != 64, d != 128, r > 32).  Host only.
+ */
+int32_t pkv_pack_factors_int4(int32_t kind, int32_t P, int32_t d, int32_t r, const int8_t* Lq,
+                              const float* Ls, const int8_t* Rq, const float* Rs, void* packed);
+int32_t pkv_unpack_factors_int4(int32_t kind, int32_t P, int32_t d, int32_t r, const void* packed,
+                                int8_t* Lq, float* Ls, int8_t* Rq, float* Rs);
 
 /* Bytes and layout of the device buffer a cache of this shape needs. */
 int32_t pkv_cache_layout(const pkv_shape* shape, pkv_layout* out);

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 PKV_OK = 0
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "capacity exceeded",
           4: "no page waiting for promotion", 5: "promotion pending", 6: "device error"}
-BF16, F32 = 0, 1
+BF16, F32, BF16_INT4 = 0, 1, 2
 KEYS, VALUES = 0, 1
 UNUSED, SINK, FACT, WIN, PART = 0, 1, 2, 3, 4
 PAGE_LEN, HEAD_DIM = 64, 128
@@ -45,7 +45,8 @@ class Layout(ctypes.Structure):
         "sink_k", "sink_v", "win_k", "win_v", "factors", "page_table", "total_bytes")] + \
         [(n, ctypes.c_int64) for n in (
             "n_sink_slots", "n_ring_slots", "max_fact_pages", "max_pages", "elem_bytes",
-            "dense_page_bytes", "factor_k_elems", "factor_v_elems", "factor_page_bytes")]
+            "dense_page_bytes", "factor_k_elems", "factor_v_elems", "factor_page_bytes",
+            "factor_k_bytes", "factor_v_bytes")]
 
 
 _LIB = None
@@ -70,6 +71,9 @@ def lib():
         "pkv_factor_part_elems": ([i32, i32, i32, P(i64)], i32),
         "pkv_pack_factors": ([i32, i32, i32, i32, i32, vp, vp, vp], i32),
         "pkv_unpack_factors": ([i32, i32, i32, i32, i32, vp, vp, vp], i32),
+        "pkv_factor_part_bytes": ([i32, i32, i32, i32, i32, P(i64)], i32),
+        "pkv_pack_factors_int4": ([i32, i32, i32, i32, vp, vp, vp, vp, vp], i32),
+        "pkv_unpack_factors_int4": ([i32, i32, i32, i32, vp, vp, vp, vp, vp], i32),
         "pkv_cache_layout": ([P(Shape), P(Layout)], i32),
         "pkv_cache_create": ([P(Shape), vp, u64, P(vp)], i32),
         "pkv_cache_destroy": ([vp], None),
@@ -193,6 +197,45 @@ def unpack_factors(kind: int, r: int, dtype: int, packed):
     return Lf, Rf
 
 
+def factor_part_bytes(kind: int, r: int, dtype: int, P: int = PAGE_LEN, d: int = HEAD_DIM) -> int:
+    n = ctypes.c_int64()
+    _check(lib().pkv_factor_part_bytes(kind, P, d, r, dtype, ctypes.byref(n)), "pkv_factor_part_bytes")
+    return n.value
+
+
+def pack_factors_int4(kind: int, r: int, Lq, Ls, Rq, Rs) -> np.ndarray:
+    """Host packing of INT4 codes (Lq (64, r), Rq (r, 128), values -7..7) and
+    scales (Ls (r,) for keys / (64,) for values, Rs (128,)) into one part
+    (uint8)."""
+    Lq = np.ascontiguousarray(Lq, dtype=np.int8)
+    Rq = np.ascontiguousarray(Rq, dtype=np.int8)
+    Ls = np.ascontiguousarray(Ls, dtype=np.float32)
+    Rs = np.ascontiguousarray(Rs, dtype=np.float32)
+    if Lq.shape != (PAGE_LEN, r) or Rq.shape != (r, HEAD_DIM) or Rs.shape != (HEAD_DIM,) or \
+            Ls.shape != ((r,) if kind == KEYS else (PAGE_LEN,)):
+        raise ValueError("code / scale shapes do not match the part")
+    out = np.zeros(factor_part_bytes(kind, r, BF16_INT4), dtype=np.uint8)
+    _check(lib().pkv_pack_factors_int4(kind, PAGE_LEN, HEAD_DIM, r, _np_ptr(Lq), _np_ptr(Ls),
+                                       _np_ptr(Rq), _np_ptr(Rs), _np_ptr(out)),
+           "pkv_pack_factors_int4")
+    return out
+
+
+def unpack_factors_int4(kind: int, r: int, packed):
+    """Inverse of pack_factors_int4: (Lq, Ls, Rq, Rs)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    if packed.size < factor_part_bytes(kind, r, BF16_INT4):
+        raise ValueError("packed part too small")
+    Lq = np.zeros((PAGE_LEN, r), dtype=np.int8)
+    Rq = np.zeros((r, HEAD_DIM), dtype=np.int8)
+    Ls = np.zeros(r if kind == KEYS else PAGE_LEN, dtype=np.float32)
+    Rs = np.zeros(HEAD_DIM, dtype=np.float32)
+    _check(lib().pkv_unpack_factors_int4(kind, PAGE_LEN, HEAD_DIM, r, _np_ptr(packed), _np_ptr(Lq),
+                                         _np_ptr(Ls), _np_ptr(Rq), _np_ptr(Rs)),
+           "pkv_unpack_factors_int4")
+    return Lq, Ls, Rq, Rs
+
+
 def make_shape(batch, n_q_heads, n_kv_heads, rank_k, rank_v, sink, window, max_tokens, dtype,
                head_dim=HEAD_DIM, page_len=PAGE_LEN) -> Shape:
     return Shape(batch, n_q_heads, n_kv_heads, head_dim, page_len, rank_k, rank_v, sink, window,
@@ -233,8 +276,17 @@ class Cache:
                  dtype="bf16", device="cuda:0"):
         import torch
         self.device = torch.device(device)
-        self.dtype_code = BF16 if dtype in ("bf16", torch.bfloat16) else F32
-        self.torch_dtype = torch.bfloat16 if self.dtype_code == BF16 else torch.float32
+        if dtype in ("bf16", torch.bfloat16):
+            self.dtype_code = BF16
+        elif dtype in ("f32", torch.float32):
+            self.dtype_code = F32
+        elif dtype == "int4":  # bf16 dense pages, INT4 factor pages (Sec. 4.3)
+            self.dtype_code = BF16_INT4
+        else:
+            raise ValueError(f"unsupported cache dtype {dtype}")
+        # element type of K, V, q and the dense pages
+        self.elem_code = F32 if self.dtype_code == F32 else BF16
+        self.torch_dtype = torch.float32 if self.dtype_code == F32 else torch.bfloat16
         self.shape = make_shape(batch, n_q_heads, n_kv_heads, rank_k, rank_v, sink, window,
                                 max_tokens, self.dtype_code)
         self.layout = cache_layout(self.shape)
@@ -266,14 +318,14 @@ class Cache:
     def prefill(self, K, V):
         """Build the cache from dense K, V [B][H_kv][T][d] (T may be 0)."""
         T = K.shape[2]
-        kp = _dev_ptr(K, self.dtype_code, "K") if T else None
-        vp = _dev_ptr(V, self.dtype_code, "V") if T else None
+        kp = _dev_ptr(K, self.elem_code, "K") if T else None
+        vp = _dev_ptr(V, self.elem_code, "V") if T else None
         _check(lib().pkv_prefill(self._h, kp, vp, T, _stream(self.device)), "pkv_prefill")
 
     def append(self, k, v) -> bool:
         pend = ctypes.c_int32()
-        _check(lib().pkv_append(self._h, _dev_ptr(k, self.dtype_code, "k"),
-                                _dev_ptr(v, self.dtype_code, "v"), ctypes.byref(pend),
+        _check(lib().pkv_append(self._h, _dev_ptr(k, self.elem_code, "k"),
+                                _dev_ptr(v, self.elem_code, "v"), ctypes.byref(pend),
                                 _stream(self.device)), "pkv_append")
         return bool(pend.value)
 
@@ -298,7 +350,7 @@ class Cache:
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
         ws = self.workspace(n_split) if workspace is None else workspace
-        _check(lib().pkv_decode_attn(self._h, _dev_ptr(q, self.dtype_code, "q"),
+        _check(lib().pkv_decode_attn(self._h, _dev_ptr(q, self.elem_code, "q"),
                                      _dev_ptr(out, None, "out"), ctypes.c_void_p(ws.data_ptr()),
                                      ws.numel(), n_split, _stream(self.device)), "pkv_decode_attn")
         return out
@@ -306,7 +358,7 @@ class Cache:
     def decode_partial(self, q, n_split: int = 0, workspace=None):
         """Eq. 4 states merged within each split, left in the workspace."""
         ws = self.workspace(n_split) if workspace is None else workspace
-        _check(lib().pkv_decode_partial(self._h, _dev_ptr(q, self.dtype_code, "q"),
+        _check(lib().pkv_decode_partial(self._h, _dev_ptr(q, self.elem_code, "q"),
                                         ctypes.c_void_p(ws.data_ptr()), ws.numel(), n_split,
                                         _stream(self.device)), "pkv_decode_partial")
         return ws
@@ -335,9 +387,9 @@ class Cache:
             out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
         # auto split counts never exceed 512: that workspace fits any length
         ws = self.workspace(n_split or 512) if workspace is None else workspace
-        _check(lib().pkv_decode_step(self._h, _dev_ptr(k, self.dtype_code, "k"),
-                                     _dev_ptr(v, self.dtype_code, "v"),
-                                     _dev_ptr(q, self.dtype_code, "q"), _dev_ptr(out, None, "out"),
+        _check(lib().pkv_decode_step(self._h, _dev_ptr(k, self.elem_code, "k"),
+                                     _dev_ptr(v, self.elem_code, "v"),
+                                     _dev_ptr(q, self.elem_code, "q"), _dev_ptr(out, None, "out"),
                                      ctypes.c_void_p(ws.data_ptr()), ws.numel(), n_split,
                                      _stream(self.device)), "pkv_decode_step")
         return out
@@ -357,7 +409,7 @@ class Cache:
         L = self.layout
         base = L["factors"] + ((b * self.shape.n_kv_heads + h) * L["max_fact_pages"] + slot) * \
             L["factor_page_bytes"]
-        kbytes = L["factor_k_elems"] * L["elem_bytes"]
+        kbytes = L["factor_k_bytes"]
         if kind == KEYS:
             return self.buffer[base: base + kbytes]
         return self.buffer[base + kbytes: base + L["factor_page_bytes"]]

@@ -50,7 +50,8 @@ int32_t check_shape(const pkv_shape* s) {
   if (!s) return PKV_ERR_INVALID_ARG;
   if (s->batch < 1 || s->n_kv_heads < 1 || s->n_q_heads < 1) return PKV_ERR_INVALID_ARG;
   if (s->n_q_heads % s->n_kv_heads) return PKV_ERR_INVALID_ARG;
-  if (s->dtype != PKV_BF16 && s->dtype != PKV_F32) return PKV_ERR_INVALID_ARG;
+  if (s->dtype != PKV_BF16 && s->dtype != PKV_F32 && s->dtype != PKV_BF16_INT4)
+    return PKV_ERR_INVALID_ARG;
   if (s->page_len < 1 || s->head_dim < 1) return PKV_ERR_INVALID_ARG;
   if (s->sink < 0 || s->window < 0 || s->sink % s->page_len || s->window % s->page_len)
     return PKV_ERR_INVALID_ARG;
@@ -60,6 +61,8 @@ int32_t check_shape(const pkv_shape* s) {
   if (s->max_tokens < 1) return PKV_ERR_INVALID_ARG;
   if (s->head_dim != kD || s->page_len != kP) return PKV_ERR_UNSUPPORTED;
   if (s->n_q_heads / s->n_kv_heads > kMaxG) return PKV_ERR_UNSUPPORTED;
+  if (s->dtype == PKV_BF16_INT4 && (s->rank_k > kQ4MaxRank || s->rank_v > kQ4MaxRank))
+    return PKV_ERR_UNSUPPORTED;
   return PKV_OK;
 }
 
@@ -67,7 +70,7 @@ void make_layout(const pkv_shape* s, pkv_layout* L) {
   std::memset(L, 0, sizeof(*L));
   const int64_t P = s->page_len, d = s->head_dim, B = s->batch, H = s->n_kv_heads;
   const int64_t n_s = s->sink / P, n_w = s->window / P;
-  L->elem_bytes = s->dtype == PKV_BF16 ? 2 : 4;
+  L->elem_bytes = s->dtype == PKV_F32 ? 4 : 2;
   L->n_sink_slots = n_s;
   L->n_ring_slots = n_w + 1;
   L->max_pages = (s->max_tokens + P - 1) / P;
@@ -76,7 +79,14 @@ void make_layout(const pkv_shape* s, pkv_layout* L) {
   L->dense_page_bytes = P * d * L->elem_bytes;
   L->factor_k_elems = part_elems(s->rank_k);
   L->factor_v_elems = part_elems(s->rank_v);
-  L->factor_page_bytes = (L->factor_k_elems + L->factor_v_elems) * L->elem_bytes;
+  if (s->dtype == PKV_BF16_INT4) {
+    L->factor_k_bytes = q4_dims(s->rank_k).k_bytes;
+    L->factor_v_bytes = q4_dims(s->rank_v).v_bytes;
+  } else {
+    L->factor_k_bytes = L->factor_k_elems * L->elem_bytes;
+    L->factor_v_bytes = L->factor_v_elems * L->elem_bytes;
+  }
+  L->factor_page_bytes = L->factor_k_bytes + L->factor_v_bytes;
   uint64_t off = 0;
   const uint64_t sink_bytes = (uint64_t)B * H * n_s * L->dense_page_bytes;
   const uint64_t ring_bytes = (uint64_t)B * H * (n_w + 1) * L->dense_page_bytes;
@@ -160,7 +170,7 @@ hipError_t factorize_page(pkv_cache* c, int64_t p, hipStream_t s) {
   job.in_trans[1] = 1;  // value pages are stored transposed
   job.in_bh_stride = (int64_t)(g.n_w + 1) * ppg;
   job.in_f_stride = 0;
-  job.in_dtype = g.dtype;
+  job.in_dtype = dense_dtype(g.dtype);
   job.rank[0] = g.r_k;
   job.rank[1] = g.r_v;
   job.out_dtype = g.dtype;
@@ -168,7 +178,7 @@ hipError_t factorize_page(pkv_cache* c, int64_t p, hipStream_t s) {
   job.fac_bh_pages = g.F_max;
   job.f0 = f;
   job.page_bytes = c->lay.factor_page_bytes;
-  job.k_part_bytes = c->lay.factor_k_elems * esz;
+  job.k_part_bytes = c->lay.factor_k_bytes;
   return launch_compress(job, s);
 }
 
@@ -345,6 +355,117 @@ int32_t pkv_unpack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_
   return PKV_OK;
 }
 
+int32_t pkv_factor_part_bytes(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t dtype,
+                              int64_t* bytes) {
+  if (!bytes || (kind != PKV_KEYS && kind != PKV_VALUES)) return PKV_ERR_INVALID_ARG;
+  if (P != kP || d != kD) return PKV_ERR_UNSUPPORTED;
+  if (r < 1 || r > kP) return PKV_ERR_INVALID_ARG;
+  if (dtype == PKV_BF16 || dtype == PKV_F32) {
+    *bytes = part_elems(r) * (dtype == PKV_BF16 ? 2 : 4);
+    return PKV_OK;
+  }
+  if (dtype != PKV_BF16_INT4) return PKV_ERR_INVALID_ARG;
+  if (r > kQ4MaxRank) return PKV_ERR_UNSUPPORTED;
+  const Q4Dims q = q4_dims(r);
+  *bytes = kind == PKV_KEYS ? q.k_bytes : q.v_bytes;
+  return PKV_OK;
+}
+
+namespace {
+
+int32_t check_q4_part(int32_t kind, int32_t P, int32_t d, int32_t r) {
+  if (P != kP || d != kD) return PKV_ERR_UNSUPPORTED;
+  if (kind != PKV_KEYS && kind != PKV_VALUES) return PKV_ERR_INVALID_ARG;
+  if (r < 1 || r > kP) return PKV_ERR_INVALID_ARG;
+  if (r > kQ4MaxRank) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+void put_nibble(uint8_t* part, const Q4Slot& s, int code) {
+  const int byte = s.bit / 8, sh = s.bit % 8;
+  uint8_t& b = part[s.byte + byte];
+  b = (uint8_t)((b & ~(0xF << sh)) | ((code + 8) << sh));
+}
+
+int get_nibble(const uint8_t* part, const Q4Slot& s) {
+  return ((part[s.byte + s.bit / 8] >> (s.bit % 8)) & 0xF) - 8;
+}
+
+void put_scale(uint8_t* part, int64_t byte, float v) {
+  uint16_t b;
+  bf16_round_host(v, &b);
+  std::memcpy(part + byte, &b, 2);
+}
+
+float get_scale(const uint8_t* part, int64_t byte) {
+  uint16_t b;
+  std::memcpy(&b, part + byte, 2);
+  const uint32_t w = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &w, 4);
+  return f;
+}
+
+}  // namespace
+
+int32_t pkv_pack_factors_int4(int32_t kind, int32_t P, int32_t d, int32_t r, const int8_t* Lq,
+                              const float* Ls, const int8_t* Rq, const float* Rs, void* packed) {
+  const int32_t st = check_q4_part(kind, P, d, r);
+  if (st != PKV_OK) return st;
+  if (!Lq || !Ls || !Rq || !Rs || !packed) return PKV_ERR_INVALID_ARG;
+  for (int64_t n = 0; n < (int64_t)kP * r; ++n)
+    if (Lq[n] < -7 || Lq[n] > 7) return PKV_ERR_INVALID_ARG;
+  for (int64_t n = 0; n < (int64_t)r * kD; ++n)
+    if (Rq[n] < -7 || Rq[n] > 7) return PKV_ERR_INVALID_ARG;
+  const Q4Dims q = q4_dims(r);
+  const bool keys = kind == PKV_KEYS;
+  uint8_t* part = (uint8_t*)packed;
+  // every nibble starts as code 0 and every byte not holding a code or a
+  // scale as 0x88
+  std::memset(part, 0x88, (size_t)(keys ? q.k_bytes : q.v_bytes));
+  const int r8 = 8 * q.pd.n8;
+  for (int i = 0; i < r8; ++i) {
+    for (int c = 0; c < kD; ++c) {
+      const int code = i < r ? Rq[(int64_t)i * kD + c] : 0;
+      put_nibble(part, keys ? q4_rt_k(q, i, c) : q4_rt_v(q, i, c), code);
+    }
+    for (int j = 0; j < kP; ++j) {
+      const int code = i < r ? Lq[(int64_t)j * r + i] : 0;
+      put_nibble(part, keys ? q4_lt_k(q, j, i) : q4_lt_v(q, j, i), code);
+    }
+  }
+  for (int c = 0; c < kD; ++c) put_scale(part, keys ? q4_sr_k(q, c) : q4_sr_v(q, c), Rs[c]);
+  if (keys) {
+    for (int i = 0; i < r8; ++i) put_scale(part, q4_sl_k(q, i), i < r ? Ls[i] : 0.f);
+  } else {
+    for (int j = 0; j < kP; ++j) put_scale(part, q4_sl_v(q, j), Ls[j]);
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_unpack_factors_int4(int32_t kind, int32_t P, int32_t d, int32_t r, const void* packed,
+                                int8_t* Lq, float* Ls, int8_t* Rq, float* Rs) {
+  const int32_t st = check_q4_part(kind, P, d, r);
+  if (st != PKV_OK) return st;
+  if (!Lq || !Ls || !Rq || !Rs || !packed) return PKV_ERR_INVALID_ARG;
+  const Q4Dims q = q4_dims(r);
+  const bool keys = kind == PKV_KEYS;
+  const uint8_t* part = (const uint8_t*)packed;
+  for (int i = 0; i < r; ++i) {
+    for (int c = 0; c < kD; ++c)
+      Rq[(int64_t)i * kD + c] = (int8_t)get_nibble(part, keys ? q4_rt_k(q, i, c) : q4_rt_v(q, i, c));
+    for (int j = 0; j < kP; ++j)
+      Lq[(int64_t)j * r + i] = (int8_t)get_nibble(part, keys ? q4_lt_k(q, j, i) : q4_lt_v(q, j, i));
+  }
+  for (int c = 0; c < kD; ++c) Rs[c] = get_scale(part, keys ? q4_sr_k(q, c) : q4_sr_v(q, c));
+  if (keys) {
+    for (int i = 0; i < r; ++i) Ls[i] = get_scale(part, q4_sl_k(q, i));
+  } else {
+    for (int j = 0; j < kP; ++j) Ls[j] = get_scale(part, q4_sl_v(q, j));
+  }
+  return PKV_OK;
+}
+
 int32_t pkv_cache_layout(const pkv_shape* shape, pkv_layout* out) {
   int32_t st = check_shape(shape);
   if (st != PKV_OK) return st;
@@ -466,7 +587,7 @@ int32_t pkv_prefill(pkv_cache* c, const void* K, const void* V, int64_t T, void*
     job.in_trans[0] = job.in_trans[1] = 0;
     job.in_bh_stride = T * kD;
     job.in_f_stride = (int64_t)kP * kD;
-    job.in_dtype = g.dtype;
+    job.in_dtype = dense_dtype(g.dtype);
     job.rank[0] = g.r_k;
     job.rank[1] = g.r_v;
     job.out_dtype = g.dtype;
@@ -474,7 +595,7 @@ int32_t pkv_prefill(pkv_cache* c, const void* K, const void* V, int64_t T, void*
     job.fac_bh_pages = g.F_max;
     job.f0 = 0;
     job.page_bytes = c->lay.factor_page_bytes;
-    job.k_part_bytes = c->lay.factor_k_elems * esz;
+    job.k_part_bytes = c->lay.factor_k_bytes;
     e = launch_compress(job, s);
   }
   if (e == hipSuccess) e = launch_table_fill(g, T, n_fact, s);

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(128) void append_kernel(CacheGeom g, const Elem* k,
 hipError_t launch_prefill_dense(const CacheGeom& g, const void* K, const void* V, int64_t T,
                                 int64_t n_fact, hipStream_t stream) {
   const dim3 grid(g.n_s + g.n_w + 1, g.Hkv, g.B);
-  if (g.dtype == PKV_BF16)
+  if (dense_dtype(g.dtype) == PKV_BF16)
     hipLaunchKernelGGL(prefill_dense_kernel<uint16_t>, grid, dim3(256), 0, stream, g,
                        (const uint16_t*)K, (const uint16_t*)V, T, n_fact);
   else
@@ -138,7 +138,7 @@ hipError_t launch_table_set(const CacheGeom& g, int64_t page, int32_t entry, hip
 hipError_t launch_append(const CacheGeom& g, const void* k, const void* v, int64_t T,
                          hipStream_t stream) {
   const dim3 grid(g.Hkv, g.B);
-  if (g.dtype == PKV_BF16)
+  if (dense_dtype(g.dtype) == PKV_BF16)
     hipLaunchKernelGGL(append_kernel<uint16_t>, grid, dim3(kD), 0, stream, g, (const uint16_t*)k,
                        (const uint16_t*)v, T);
   else

@@ -32,7 +32,9 @@
 //      the two one-sided recurrences outward from k.
 //   5. Q_r = Q_H Z, R = Q_r^T X on the matrix cores in fp32, sigma_i = ||R_i||,
 //      Lf = Q_r diag(sigma), Rf = diag(1/sigma) R (zero where sigma = 0), rounded
-//      nearest-even to the output dtype.
+//      nearest-even to the output dtype.  INT4 caches (Sec. 4.3) instead
+//      store Lt = Q_r diag(sigma^(1/2)) and Rt = diag(sigma^(-1/2)) R as
+//      symmetric 4-bit codes with bf16 group scales (store_q4).
 #include "pkv_compress_common.h"
 
 namespace pkv {
@@ -286,7 +288,185 @@ __device__ __forceinline__ void twisted_vector(TriShared& sh, float lam, float p
   }
 }
 
-template <typename Elem>
+// 6'. INT4 factors of one page (Sec. 4.3), written into its packed part.
+// Groups: columns of Lt_K, rows of Lt_V, columns of Rt_K and Rt_V; per group
+// the scale is max |x| / 7 rounded nearest-even to bf16, and a code is
+// rint(x / scale) clamped to -7..7 (0 where the scale is 0).  The codes go to
+// LDS as nibble bytes (c + 8), then each lane assembles whole units of the
+// packed layout from them.
+__device__ __forceinline__ float q4_scale(float amax) { return bf16_bits_to_f32(f32_to_bf16_bits(amax / 7.f)); }
+
+__device__ __forceinline__ float q4_inv(float s) { return s > 0.f ? 1.f / s : 0.f; }
+
+__device__ __forceinline__ uint32_t q4_nibble(float x, float inv) {
+  return (uint32_t)((int)fminf(fmaxf(rintf(x * inv), -7.f), 7.f) + 8);
+}
+
+// W nibble bytes (stride `stride`) -> one unit of the packed layout
+__device__ __forceinline__ uint32_t q4_pack(const uint8_t* src, int stride, int n, int W) {
+  uint32_t u = 0;
+  for (int e = 0; e < W; ++e) u |= (e < n ? (uint32_t)src[e * stride] : 8u) << q4_nibble_bit(W, e);
+  return u;
+}
+
+__device__ __forceinline__ void q4_store_unit(uint8_t* p, uint32_t u, int ub) {
+  if (ub == 4) *(uint32_t*)p = u;
+  else if (ub == 2) *(uint16_t*)p = (uint16_t)u;
+  else *p = (uint8_t)u;
+}
+
+__device__ __forceinline__ void q4_store_scale(uint8_t* p, float s) { *(uint16_t*)p = f32_to_bf16_bits(s); }
+
+__device__ __forceinline__ void store_q4(const CompressJob& job, const PageRef& pr, TriShared& sh,
+                                         const floatx4 (&R)[2][8], int lane) {
+  const int r = pr.r;
+  const Q4Dims qd = q4_dims(r);
+  const int A = qd.pd.A, r8 = 8 * qd.pd.n8, ub = qd.ub;
+  const bool keys = pr.kind == 0;
+  uint8_t* part = job.fac + (pr.bh * job.fac_bh_pages + job.f0 + pr.f) * job.page_bytes +
+                  (int64_t)pr.kind * job.k_part_bytes;
+  float* hs = sh.w;      // sigma_i^(1/2)
+  float* ihs = sh.xrow;  // sigma_i^(-1/2), 0 where sigma_i = 0
+  float* lsc = sh.v;     // scales of the columns of Lt_K
+  float* linv = sh.b;    // their reciprocals
+  if (lane < kTriMaxRank) {
+    const float h = lane < r ? sqrtf(sh.sig[lane]) : 0.f;
+    hs[lane] = h;
+    ihs[lane] = q4_inv(h);
+  }
+  __syncthreads();
+
+  // Lt row j = lane
+  float lt[kTriMaxRank];
+  float lmax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kTriMaxRank; ++i) {
+    lt[i] = i < r ? sh.u.Z[lane * kZs + i] * hs[i] : 0.f;
+    lmax = fmaxf(lmax, fabsf(lt[i]));
+  }
+  if (keys) {
+    // column maxima of Lt_K: lanes i and i + 32 scan half of column i each
+    // (scaling by sigma_i^(1/2) > 0 commutes with the maximum)
+    const int i = lane & 31, j0 = (lane >> 5) * 32;
+    float m = 0.f;
+    if (i < r) {
+      for (int j = j0; j < j0 + 32; ++j) m = fmaxf(m, fabsf(sh.u.Z[j * kZs + i]));
+    }
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if (lane < kTriMaxRank) {
+      const float sc = i < r ? q4_scale(m * hs[i]) : 0.f;
+      lsc[lane] = sc;
+      linv[lane] = q4_inv(sc);
+    }
+  }
+  __syncthreads();  // Z is read for the last time above; the codes reuse it
+
+  uint8_t* Lc = (uint8_t*)sh.u.Z;              // [kP][32]  nibble bytes of Lt
+  uint8_t* Rc = Lc + kP * kTriMaxRank;          // [32][kD]  nibble bytes of Rt
+  const float lsv = keys ? 0.f : q4_scale(lmax);  // row scale of Lt_V
+  {
+    const float rinv = q4_inv(lsv);
+#pragma unroll
+    for (int i4 = 0; i4 < kTriMaxRank / 4; ++i4) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * i4 + e;
+        const uint32_t nb = i < r ? q4_nibble(lt[i], keys ? linv[i] : rinv) : 8u;
+        w |= nb << (8 * e);
+      }
+      if (4 * i4 < r8) *(uint32_t*)&Lc[lane * kTriMaxRank + 4 * i4] = w;
+    }
+  }
+  // Rt = diag(sigma^(-1/2)) R: lane (ci, q) holds rows 16 mi + 4 q + v of
+  // channel 16 mc + ci; a channel's maximum spans the four lanes ci + 16 q
+  {
+    const int ci = lane & 15, q = lane >> 4;
+    float ri[2][4];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) ri[mi][v] = ihs[16 * mi + 4 * q + v];
+    }
+#pragma unroll
+    for (int mc = 0; mc < 8; ++mc) {
+      float rt[2][4];
+      float m = 0.f;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          rt[mi][v] = R[mi][mc][v] * ri[mi][v];
+          m = fmaxf(m, fabsf(rt[mi][v]));
+        }
+      }
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      const float sc = q4_scale(m), inv = q4_inv(sc);
+      const int c = 16 * mc + ci;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int i = 16 * mi + 4 * q + v;
+          if (i < r8) Rc[i * kD + c] = (uint8_t)(i < r ? q4_nibble(rt[mi][v], inv) : 8u);
+        }
+      }
+      if (q == 0) q4_store_scale(part + (keys ? q4_sr_k(qd, c) : q4_sr_v(qd, c)), sc);
+    }
+  }
+  __syncthreads();
+
+  // assemble and store the units
+  const int full = A / 4, partial = A % 4 ? 1 : 0;
+  if (keys) {
+    // K1: Rt_K rank tiles, dwords of 8 channels
+    for (int u = lane; u < full * 256 + partial * 128; u += kP) {
+      int mt, row, ks, qk, b, v;
+      if (u < full * 256) {
+        mt = u / 256, row = (u % 256) / 4, ks = u % 4;
+        qk = row / 16, b = (row % 16) / 4, v = row % 4;
+      } else {
+        const int w = u - full * 256;
+        mt = full, row = w / 4, ks = w % 4;
+        qk = row / 8, b = (row % 8) / 2, v = row % 2;
+      }
+      const int i = A * b + 4 * mt + v;
+      *(uint32_t*)(part + mt * 1024 + (row * 4 + ks) * 4) = q4_pack(&Rc[i * kD + 32 * ks + 8 * qk], 1, 8, 8);
+    }
+    // K2: Lt_K page-row tiles, units of the lane quad's A ranks
+    for (int u = lane; u < 256; u += kP) {
+      const int ln = u / 4, mt = u % 4, qk = ln / 16, rho = ln % 16;
+      const int j = 16 * (rho / 4) + 4 * mt + rho % 4;
+      q4_store_unit(part + qd.k2 + (int64_t)u * ub, q4_pack(&Lc[j * kTriMaxRank + A * qk], 1, A, 2 * ub), ub);
+    }
+    if (lane < r8) q4_store_scale(part + q4_sl_k(qd, lane), lsc[lane]);
+  } else {
+    // V1: Lt_V^T rank tiles, dwords of 8 tokens
+    for (int u = lane; u < full * 128 + partial * 64; u += kP) {
+      int mt, row, ks, qk, b, v;
+      if (u < full * 128) {
+        mt = u / 128, row = (u % 128) / 2, ks = u % 2;
+        qk = row / 16, b = (row % 16) / 4, v = row % 4;
+      } else {
+        const int w = u - full * 128;
+        mt = full, row = w / 2, ks = w % 2;
+        qk = row / 8, b = (row % 8) / 2, v = row % 2;
+      }
+      const int i = A * b + 4 * mt + v;
+      *(uint32_t*)(part + mt * 512 + (row * 2 + ks) * 4) =
+          q4_pack(&Lc[(16 * qk + 8 * ks) * kTriMaxRank + i], kTriMaxRank, 8, 8);
+    }
+    // V2: Rt_V^T channel tiles, units of the lane quad's A ranks
+    for (int u = lane; u < 512; u += kP) {
+      const int ln = u / 8, mt = u % 8, qk = ln / 16, c = 16 * mt + ln % 16;
+      q4_store_unit(part + qd.v2 + (int64_t)u * ub, q4_pack(&Rc[A * qk * kD + c], kD, A, 2 * ub), ub);
+    }
+    q4_store_scale(part + q4_sl_v(qd, lane), lsv);
+  }
+}
+
+template <typename Elem, bool kQ4>
 __device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t n, TriShared& sh, int lane) {
   const PageRef pr = page_ref(job, n, (int)sizeof(Elem));
   const Elem* X = (const Elem*)pr.X;
@@ -429,6 +609,12 @@ __device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t
   }
   __syncthreads();
 
+  if constexpr (kQ4) {
+    store_q4(job, pr, sh, R, lane);
+    __syncthreads();
+    return;
+  }
+
   // 6. Rf = R / sigma, Lf = Q_r diag(sigma)
   const FactorDst dst(job, pr, n);
 #pragma unroll
@@ -463,11 +649,11 @@ __device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t
 
 // One page per workgroup (no page loop: a loop around the page body costs the
 // register allocator ~70 extra VGPRs).  Page n = blockIdx.y * gridDim.x + blockIdx.x.
-template <typename Elem>
+template <typename Elem, bool kQ4>
 __global__ __launch_bounds__(64, 3) void compress_tri_kernel(CompressJob job) {
   __shared__ TriShared sh;
   const int64_t n = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-  if (n < job.n_pages) compress_tri_one<Elem>(job, n, sh, threadIdx.x);
+  if (n < job.n_pages) compress_tri_one<Elem, kQ4>(job, n, sh, threadIdx.x);
 }
 
 }  // namespace
@@ -479,10 +665,14 @@ hipError_t launch_compress_tri(const CompressJob& job, hipStream_t stream, hipEv
   const int64_t gy = (job.n_pages + gx - 1) / gx;
   if (gy > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)gx, (unsigned)gy);
-  if (job.in_dtype == PKV_BF16)
-    hipExtLaunchKernelGGL(compress_tri_kernel<uint16_t>, grid, dim3(64), 0, stream, start, stop, 0, job);
+  const bool q4 = job.out_dtype == PKV_BF16_INT4;
+  if (q4 && (job.fac == nullptr || job.in_dtype != PKV_BF16)) return hipErrorInvalidValue;
+  if (q4)
+    hipExtLaunchKernelGGL((compress_tri_kernel<uint16_t, true>), grid, dim3(64), 0, stream, start, stop, 0, job);
+  else if (job.in_dtype == PKV_BF16)
+    hipExtLaunchKernelGGL((compress_tri_kernel<uint16_t, false>), grid, dim3(64), 0, stream, start, stop, 0, job);
   else
-    hipExtLaunchKernelGGL(compress_tri_kernel<float>, grid, dim3(64), 0, stream, start, stop, 0, job);
+    hipExtLaunchKernelGGL((compress_tri_kernel<float, false>), grid, dim3(64), 0, stream, start, stop, 0, job);
   return hipGetLastError();
 }
 

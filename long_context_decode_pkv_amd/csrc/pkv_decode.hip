@@ -260,10 +260,10 @@ struct SoftState {
 };
 
 // Fold one page's 64 raw scores (MFMA output, hi/lo column halves not yet
-// summed) into the running state; returns the probability operand pb[2].
-__device__ inline void softmax_page(SoftState& st, const floatx4 (&acc)[4], int nvalid, int q4,
-                                    float rem, bf16x8 (&pb)[2]) {
-  float s[4][4];
+// summed) into the running state; s receives the page's probabilities
+// e^(score - m) (slot [ks][e] of the value contraction in s[2 ks + e / 4][e % 4]).
+__device__ inline void softmax_probs(SoftState& st, const floatx4 (&acc)[4], int nvalid, int q4,
+                                     float (&s)[4][4]) {
   float mx = -INFINITY;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
@@ -296,6 +296,13 @@ __device__ inline void softmax_page(SoftState& st, const floatx4 (&acc)[4], int 
   st.m = m_new;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) st.o[mt] *= alpha;
+}
+
+// ... and the probability operand pb[2] of the value contraction.
+__device__ inline void softmax_page(SoftState& st, const floatx4 (&acc)[4], int nvalid, int q4,
+                                    float rem, bf16x8 (&pb)[2]) {
+  float s[4][4];
+  softmax_probs(st, acc, nvalid, q4, s);
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -389,9 +396,7 @@ __device__ inline void dense_page(SoftState& st, const uint16_t* Kp, const uint1
   }
 }
 
-constexpr int kMaxSplits = kMaxDecodeSplits;
-
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;  // waves per workgroup of the matrix-core kernel
 
 // Waves per SIMD the matrix-core kernel is compiled for (register budget):
 // 2 up to r = 48, 1 above.  Three waves of the small ranks without key double
@@ -399,17 +404,364 @@ constexpr int kWaves = 4;
 // 6.45 TB/s at 2 waves with double-buffered keys).
 constexpr int mfma_waves_per_simd(int n8) { return n8 <= 6 ? 2 : 1; }
 
-// Key parts double-buffered where the extra page half fits the budget above
-// without spilling (all but r/8 = 5, 6).  Qwen3-32B-shaped layer (r = 24):
-// 51.8 -> 50.7 us.
-template <int N8>
-constexpr bool kKeyDoubleBuffer = N8 <= 4 || N8 >= 7;
+// Factor formats of the matrix-core kernel.  A format supplies the register
+// image of a page's K part and V part (KRegs, VRegs) and their loads, the
+// per-wave query operand (Query, built from the fp32 query q log2(e)/sqrt(d)
+// of the lane's 32 channels or its bf16 hi/lo operand), and the two halves of Eq. 4 on a page:
+// keys() leaves the page's probabilities in Probs, values() accumulates the
+// page's output.
 
+// bf16 factors Lf = U Sigma, Rf = W^T (Sec. 3.3, Eq. 2), rank 8 N8.
 template <int N8>
-__global__ __launch_bounds__(256, mfma_waves_per_simd(N8)) void decode_mfma_kernel(DecodeArgs a) {
-  __shared__ float sm_o[kWaves][kMaxG][kD];
-  __shared__ float sm_m[kWaves][kMaxG];
-  __shared__ float sm_l[kWaves][kMaxG];
+struct Bf16Factors {
+  static constexpr int kWavesPerSimd = mfma_waves_per_simd(N8);
+  // Key parts double-buffered where the extra page half fits the budget
+  // without spilling (all but r/8 = 5, 6).  Qwen3-32B-shaped layer (r = 24):
+  // 51.8 -> 50.7 us.
+  static constexpr bool kKeyDoubleBuffer = N8 <= 4 || N8 >= 7;
+  static constexpr bool kLdsRing = false;
+  static constexpr int kLdsBytes = 0;
+  using K = KRegs<N8>;
+  using V = VRegs<N8>;
+  struct Query {
+    bf16x8 qb[4];
+  };
+  using Probs = bf16x8[2];
+  __device__ static void query(Query& Q, const float (&)[4][8], const bf16x8 (&qb)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) Q.qb[ks] = qb[ks];
+  }
+  __device__ static void load_keys(K& R, const uint8_t* kp, int lane) {
+    pkv::load_keys<N8>(R, (const uint16_t*)kp, lane);
+  }
+  __device__ static void load_values(V& R, const uint8_t* vp, int lane) {
+    pkv::load_values<N8>(R, (const uint16_t*)vp, lane);
+  }
+  __device__ static void keys(SoftState& st, const K& R, const Query& Q, int q4, float rem, Probs& pb) {
+    fact_keys<N8>(st, R, Q.qb, q4, rem, pb);
+  }
+  __device__ static void values(SoftState& st, const V& R, const Probs& pb, int q4, float rem) {
+    fact_values<N8>(st, R, pb, rem);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// INT4 factors (Sec. 4.3): Lt = U Sigma^(1/2), Rt = Sigma^(1/2) W^T as 4-bit
+// codes c with bf16 group scales (layout: pkv_internal.h).  A code nibble
+// n = c + 8 enters the matrix cores as the exact bf16 value 1 + n/16 =
+// 1.5 + c/16 (n in mantissa bits 3..6 of 1.0, two codes per and-or).  One
+// extra MFMA per contraction with the constant operand -1.5 removes the
+// offset (it starts the accumulator), leaving (1/16) sum c b.  The scales
+// fold into the fp32 vector operands:
+//   t / 16  = (1/16) Rq_K (sR_K o q)            B operand sR_K o q
+//   s       = (1/16) Lq_K (256 sL_K o (t / 16))  B operand 256 sL_K o t/16
+//   u / 16  = (1/16) Lq_V^T (sL_V o p)           B operand sL_V o p
+//   o      += 256 sR_V o (1/16) Rq_V^T (u / 16)  B operand u / 16
+// each B operand again as bf16 hi/lo columns.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// element e of a bf16 array held as dwords
+template <int E>
+__device__ __forceinline__ float bf16_at(const uint32_t* d) {
+  return E % 2 ? bf16_hi(d[E / 2]) : bf16_lo(d[E / 2]);
+}
+
+// codes 2k, 2k + 1 of a unit (bits 4k.. of each 16-bit half) -> bf16 pair
+template <int K>
+__device__ __forceinline__ uint32_t q4_pair(uint32_t u) {
+  const uint32_t sh = K == 0 ? (u << 3) : (u >> (4 * K - 3));
+  return (sh & 0x00780078u) | 0x3f803f80u;
+}
+
+// unit of W nibbles in the low 4 W bits of x -> operand slots 0 .. 2 NP - 1
+// (slots above are 0)
+template <int W, int NP>
+__device__ __forceinline__ bf16x8 q4_operand(uint32_t x) {
+  uint32_t u = x;
+  if constexpr (W == 4) u = x | (x << 8);
+  else if constexpr (W == 2) u = x | (x << 12);
+  uint4 w = {q4_pair<0>(u), 0u, 0u, 0u};
+  if constexpr (NP > 1) w.y = q4_pair<1>(u);
+  if constexpr (NP > 2) w.z = q4_pair<2>(u);
+  if constexpr (NP > 3) w.w = q4_pair<3>(u);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// unit m of UB bytes from consecutive dwords
+template <int UB>
+__device__ __forceinline__ uint32_t q4_unit(const uint32_t* d, int m) {
+  if constexpr (UB == 4) return d[m];
+  else if constexpr (UB == 2) return __builtin_amdgcn_ubfe(d[m / 2], 16 * (m % 2), 16);
+  else return __builtin_amdgcn_ubfe(d[m / 4], 8 * (m % 4), 8);
+}
+
+__device__ __forceinline__ bf16x8 q4_offset_operand() {
+  const uint4 w = {0xbfc0bfc0u, 0xbfc0bfc0u, 0xbfc0bfc0u, 0xbfc0bfc0u};  // -1.5
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Direct global -> LDS load of 16 bytes per lane (gfx950
+// global_load_lds_dwordx4, non-temporal as the streamed register loads):
+// lane l's bytes land at LDS address lds_base + 16 l.  Issued as inline
+// assembly, so the compiler neither tracks nor waits for it: the caller
+// waits with vm_wait before reading the LDS it fills.  lds_base must be
+// wave-uniform.  The load takes its LDS base from M0, which the compiler
+// reserves: M0 is saved and restored around it, with one wait state after
+// each M0 write (the SALU-write-M0 -> LDS-DMA hazard).
+__device__ __forceinline__ void lds_load16(const uint8_t* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off nt\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt unconstrained), then a compiler
+// barrier so that no LDS access moves above it.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// N consecutive dwords, streamed
+template <int N>
+__device__ __forceinline__ void ldw(uint32_t* d, const uint8_t* p) {
+  if constexpr (N == 4) {
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+    d[0] = v.x, d[1] = v.y, d[2] = v.z, d[3] = v.w;
+  } else if constexpr (N == 3) {
+    const u32x3 v = __builtin_nontemporal_load((const u32x3*)p);
+    d[0] = v.x, d[1] = v.y, d[2] = v.z;
+  } else if constexpr (N == 2) {
+    const u32x2 v = __builtin_nontemporal_load((const u32x2*)p);
+    d[0] = v.x, d[1] = v.y;
+  } else {
+    d[0] = __builtin_nontemporal_load((const uint32_t*)p);
+  }
+}
+
+// LDS budget of a four-wave workgroup at two workgroups per CU (160 KB).
+constexpr int kWgLdsBytes = 80 * 1024;
+
+template <int N8K, int N8V>
+struct Int4Factors {
+  static constexpr int AK = 2 * N8K, AV = 2 * N8V;  // ranks per lane quad
+  static constexpr int RTK = (AK + 3) / 4, RTV = (AV + 3) / 4;
+  static constexpr bool kPartK = AK % 4 != 0, kPartV = AV % 4 != 0;
+  static constexpr Q4Dims kQK = q4_dims(8 * N8K), kQV = q4_dims(8 * N8V);
+  static constexpr int UK = kQK.ub, UV = kQV.ub;  // K2 / V2 unit bytes
+  // byte offsets within the parts
+  static constexpr int kK2 = kQK.k2, kSRK = kQK.sr_k, kSLK = kQK.sl_k;
+  static constexpr int kV2 = kQV.v2, kSLV = kQV.sl_v, kSRV = kQV.sr_v;
+  static constexpr int kKBytes = kQK.k_bytes, kPageBytes = kQK.k_bytes + kQV.v_bytes;
+  static constexpr int kWavesPerSimd = 2;
+  static constexpr bool kKeyDoubleBuffer = false;
+  // Factor pages stream through a per-wave ring of kRingSlots page slots in
+  // LDS, filled by direct global -> LDS loads kRingSlots - 1 pages ahead of
+  // the page being computed (registers cannot hold that much prefetch).
+  static constexpr bool kLdsRing = true;
+  static constexpr int kRingSlots = (kWgLdsBytes / kWaves) / kPageBytes < 4
+                                        ? (kWgLdsBytes / kWaves) / kPageBytes : 4;
+  static constexpr int kStageLoads = (kPageBytes + 1023) / 1024;  // 1 KB per wave load
+  static constexpr int kLdsBytes = kWaves * kRingSlots * kPageBytes;
+  static_assert(kRingSlots >= 2, "an INT4 page pair must fit twice per wave");
+
+  struct K {
+    uint32_t k1[RTK][4];  // Rq_K rank tiles, one dword per reduction step
+    uint32_t k2[UK];      // Lq_K units of the 4 page-row tiles
+    uint32_t sr[16];      // sR_K of channels 32 ks + 8 q4 + e: [ks][e] as bf16 pairs
+    uint32_t sl[N8K];     // sL_K of the lane quad's ranks
+  };
+  struct V {
+    uint32_t v1[RTV][2];  // Lq_V^T rank tiles
+    uint32_t v2[2 * UV];  // Rq_V^T units of the 8 channel tiles
+    uint32_t sl[8];       // sL_V of tokens 16 q4 .. 16 q4 + 15
+    uint32_t sr[16];      // sR_V of channels 16 mt + 4 q4 + v: [mt][v]
+  };
+  struct Query {
+    float qf[4][8];
+  };
+  using Probs = float[4][4];
+
+  __device__ static void query(Query& Q, const float (&qs)[4][8], const bf16x8 (&)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Q.qf[ks][e] = qs[ks][e];
+    }
+  }
+
+  // Direct global -> LDS copy of one page pair (K part, then V part): load i
+  // moves bytes 1024 i + 16 lane .. + 15 of the page to the same offset of
+  // the slot.
+  __device__ static void stage(uint8_t* slot, const uint8_t* page, int lane) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(slot));  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < kStageLoads; ++i) {
+      const int off = 1024 * i + 16 * lane;
+      if (off < kPageBytes) lds_load16(page + off, base + 1024 * i);
+    }
+  }
+
+  // Wait until at most `pending` pages of staging loads are in flight.
+  __device__ static void wait_staged(int pending) {
+    static_assert(kStageLoads * (kRingSlots - 1) < 64, "vmcnt range");
+    switch (pending) {
+      case 0: vm_wait<0>(); break;
+      case 1: vm_wait<kStageLoads>(); break;
+      case 2: vm_wait<2 * kStageLoads>(); break;
+      default: vm_wait<3 * kStageLoads>(); break;
+    }
+  }
+
+  __device__ static void load_keys(K& R, const uint8_t* kp, int lane) {
+    const TileLane tl = tile_lane(lane);
+    const int q4 = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < RTK; ++mt) {
+      const bool part = kPartK && mt == RTK - 1;
+      ldw<4>(R.k1[mt], kp + mt * 1024 + (part ? tl.lam : lane) * 16);
+    }
+    ldw<UK>(R.k2, kp + kK2 + lane * 4 * UK);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) ldw<4>(&R.sr[4 * ks], kp + kSRK + 2 * (32 * ks + 8 * q4));
+    ldw<N8K>(R.sl, kp + kSLK + 2 * AK * q4);
+  }
+
+  __device__ static void load_values(V& R, const uint8_t* vp, int lane) {
+    const TileLane tl = tile_lane(lane);
+    const int q4 = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < RTV; ++mt) {
+      const bool part = kPartV && mt == RTV - 1;
+      ldw<2>(R.v1[mt], vp + mt * 512 + (part ? tl.lam : lane) * 8);
+    }
+    if constexpr (UV == 4) {
+      ldw<4>(R.v2, vp + kV2 + lane * 32);
+      ldw<4>(R.v2 + 4, vp + kV2 + lane * 32 + 16);
+    } else {
+      ldw<2 * UV>(R.v2, vp + kV2 + lane * 8 * UV);
+    }
+    ldw<4>(R.sl, vp + kSLV + 32 * q4);
+    ldw<4>(R.sl + 4, vp + kSLV + 32 * q4 + 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ldw<4>(&R.sr[4 * k], vp + kSRV + 64 * q4 + 16 * k);
+  }
+
+  // Eq. 4, key half on the codes: t = Rt_K q, s = Lt_K t, online softmax.
+  // Rank slots e >= A of the second contraction are zero: they belong to no
+  // rank (rows of the compacted tile that lanes only read as filler).
+  __device__ static void keys(SoftState& st, const K& R, const Query& Q, int q4, float rem, Probs& p) {
+    const bf16x8 off = q4_offset_operand();
+    bf16x8 qb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t d = R.sr[4 * ks + e / 2];
+        qb[ks][e] = split_bf16(Q.qf[ks][e] * (e % 2 ? bf16_hi(d) : bf16_lo(d)), rem);
+      }
+    }
+    floatx4 base = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) base = mfma(off, qb[ks], base);
+    floatx4 at[RTK];
+#pragma unroll
+    for (int mt = 0; mt < RTK; ++mt) {
+      at[mt] = base;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) at[mt] = mfma(q4_operand<8, 4>(R.k1[mt][ks]), qb[ks], at[mt]);
+    }
+    bf16x8 tb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = 0.f;
+      if (e < AK) {
+        const uint32_t d = R.sl[e / 2];
+        x = (at[e / 4][e % 4] + ror8(at[e / 4][e % 4])) * (256.f * (e % 2 ? bf16_hi(d) : bf16_lo(d)));
+      }
+      tb[e] = split_bf16(x, rem);
+    }
+    const floatx4 base2 = mfma(off, tb, floatx4{0.f, 0.f, 0.f, 0.f});
+    floatx4 as_[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) as_[mt] = mfma(q4_operand<2 * UK, N8K>(q4_unit<UK>(R.k2, mt)), tb, base2);
+    softmax_probs(st, as_, kP, q4, p);
+  }
+
+  // Eq. 4, value half on the codes: u = Lt_V^T p, o += Rt_V^T u.
+  __device__ static void values(SoftState& st, const V& R, const Probs& p, int q4, float rem) {
+    const bf16x8 off = q4_offset_operand();
+    bf16x8 pb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t d = R.sl[(8 * ks + e) / 2];
+        pb[ks][e] = split_bf16(p[2 * ks + e / 4][e % 4] * (e % 2 ? bf16_hi(d) : bf16_lo(d)), rem);
+      }
+    }
+    floatx4 base = mfma(off, pb[0], floatx4{0.f, 0.f, 0.f, 0.f});
+    base = mfma(off, pb[1], base);
+    floatx4 au[RTV];
+#pragma unroll
+    for (int mt = 0; mt < RTV; ++mt) {
+      au[mt] = base;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) au[mt] = mfma(q4_operand<8, 4>(R.v1[mt][ks]), pb[ks], au[mt]);
+    }
+    bf16x8 ub;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = e < AV ? au[e / 4][e % 4] + ror8(au[e / 4][e % 4]) : 0.f;
+      ub[e] = split_bf16(x, rem);
+    }
+    const floatx4 base2 = mfma(off, ub, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const floatx4 acc = mfma(q4_operand<2 * UV, N8V>(q4_unit<UV>(R.v2, mt)), ub, base2);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t d = R.sr[(4 * mt + v) / 2];
+        st.o[mt][v] = __builtin_fmaf(256.f * (v % 2 ? bf16_hi(d) : bf16_lo(d)), acc[v], st.o[mt][v]);
+      }
+    }
+  }
+};
+
+constexpr int kMaxSplits = kMaxDecodeSplits;
+
+// LDS of the cross-wave merge; a format's page ring shares the space (the
+// ring is drained before the merge writes it).
+struct WaveMergeLds {
+  float o[kWaves][kMaxG][kD];
+  float m[kWaves][kMaxG];
+  float l[kWaves][kMaxG];
+};
+
+template <class F>
+__global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int kLds = F::kLdsBytes > (int)sizeof(WaveMergeLds) ? F::kLdsBytes : (int)sizeof(WaveMergeLds);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  WaveMergeLds& mg = *reinterpret_cast<WaveMergeLds*>(lds);
+  auto& sm_o = mg.o;
+  auto& sm_m = mg.m;
+  auto& sm_l = mg.l;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, q4 = lane >> 4;
@@ -419,7 +771,9 @@ __global__ __launch_bounds__(256, mfma_waves_per_simd(N8)) void decode_mfma_kern
   const int Hq = a.Hkv * a.G;
   const int64_t bh = (int64_t)b * a.Hkv + h;
 
-  // query operand: q * log2(e)/sqrt(d), split into bf16 + remainder columns
+  // query q * log2(e)/sqrt(d) of the lane's channels 32 ks + 8 q4 + e; as
+  // an operand split into bf16 + remainder columns
+  float qs[4][8];
   bf16x8 qb[4];
   {
     const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)b * Hq + (int64_t)h * a.G + g) * kD;
@@ -428,7 +782,10 @@ __global__ __launch_bounds__(256, mfma_waves_per_simd(N8)) void decode_mfma_kern
       bf16x8 raw = g < a.G ? __builtin_bit_cast(bf16x8, *(const uint4*)(qp + 32 * ks + 8 * q4))
                            : bf16x8{};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qb[ks][e] = split_bf16((float)raw[e] * a.qscale, rem);
+      for (int e = 0; e < 8; ++e) {
+        qs[ks][e] = (float)raw[e] * a.qscale;
+        qb[ks][e] = split_bf16(qs[ks][e], rem);
+      }
     }
   }
 
@@ -468,24 +825,54 @@ __global__ __launch_bounds__(256, mfma_waves_per_simd(N8)) void decode_mfma_kern
   // so that K(e + 2) streams in from the end of page e's key half
   int64_t e = e0 > wl.D ? e0 : wl.D;
   if (e < e1) {
+    typename F::Query fq;
+    F::query(fq, qs, qb);
     // the factor slot of logical page n_s + f is f (pages are factorized in
     // order and never revisited), so unit e lives in slot e - D
     const uint8_t* fac_bh = a.fac + bh * a.F_max * a.page_bytes;
     const int64_t kpb = a.k_part_bytes;
-    auto kptr = [&](int64_t ee) { return (const uint16_t*)(fac_bh + (ee - wl.D) * a.page_bytes); };
-    auto vptr = [&](int64_t ee) { return (const uint16_t*)(fac_bh + (ee - wl.D) * a.page_bytes + kpb); };
-    VRegs<N8> vr;
-    if constexpr (kKeyDoubleBuffer<N8>) {
-      KRegs<N8> ka, kb;
-      load_keys<N8>(ka, kptr(e), lane);
-      load_values<N8>(vr, vptr(e), lane);
-      if (e + 1 < e1) load_keys<N8>(kb, kptr(e + 1), lane);
-      auto step = [&](KRegs<N8>& kc) {
-        bf16x8 pb[2];
-        fact_keys<N8>(st, kc, qb, q4, rem, pb);
-        if (e + 2 < e1) load_keys<N8>(kc, kptr(e + 2), lane);
-        fact_values<N8>(st, vr, pb, rem);
-        if (e + 1 < e1) load_values<N8>(vr, vptr(e + 1), lane);
+    auto kptr = [&](int64_t ee) { return fac_bh + (ee - wl.D) * a.page_bytes; };
+    auto vptr = [&](int64_t ee) { return fac_bh + (ee - wl.D) * a.page_bytes + kpb; };
+    if constexpr (F::kLdsRing) {
+      // ring slot s holds pages e with e = s (mod kRingSlots); pages up to
+      // e + kRingSlots - 1 are staged while page e is computed
+      constexpr int NS = F::kRingSlots;
+      uint8_t* ring = lds + wave * NS * F::kPageBytes;
+      int64_t next = e;  // next page to stage
+      int s_next = 0, s_cur = 0;
+      for (; next < e1 && next < e + NS - 1; ++next) {
+        F::stage(ring + s_next * F::kPageBytes, kptr(next), lane);
+        s_next = s_next + 1 == NS ? 0 : s_next + 1;
+      }
+      for (; e < e1; ++e) {
+        if (next < e1) {  // into the slot of page e - 1, read in full last iteration
+          F::stage(ring + s_next * F::kPageBytes, kptr(next), lane);
+          s_next = s_next + 1 == NS ? 0 : s_next + 1;
+          ++next;
+        }
+        F::wait_staged((int)(next - 1 - e));
+        const uint8_t* slot = ring + s_cur * F::kPageBytes;
+        s_cur = s_cur + 1 == NS ? 0 : s_cur + 1;
+        typename F::K kr;
+        F::load_keys(kr, slot, lane);
+        typename F::Probs pb;
+        F::keys(st, kr, fq, q4, rem, pb);
+        typename F::V vr;
+        F::load_values(vr, slot + F::kKBytes, lane);
+        F::values(st, vr, pb, q4, rem);
+      }
+    } else if constexpr (F::kKeyDoubleBuffer) {
+      typename F::V vr;
+      typename F::K ka, kb;
+      F::load_keys(ka, kptr(e), lane);
+      F::load_values(vr, vptr(e), lane);
+      if (e + 1 < e1) F::load_keys(kb, kptr(e + 1), lane);
+      auto step = [&](typename F::K& kc) {
+        typename F::Probs pb;
+        F::keys(st, kc, fq, q4, rem, pb);
+        if (e + 2 < e1) F::load_keys(kc, kptr(e + 2), lane);
+        F::values(st, vr, pb, q4, rem);
+        if (e + 1 < e1) F::load_values(vr, vptr(e + 1), lane);
       };
       while (true) {
         step(ka);
@@ -494,16 +881,17 @@ __global__ __launch_bounds__(256, mfma_waves_per_simd(N8)) void decode_mfma_kern
         if (++e >= e1) break;
       }
     } else {
-      KRegs<N8> kr;
-      load_keys<N8>(kr, kptr(e), lane);
-      load_values<N8>(vr, vptr(e), lane);
+      typename F::V vr;
+      typename F::K kr;
+      F::load_keys(kr, kptr(e), lane);
+      F::load_values(vr, vptr(e), lane);
       for (; e < e1; ++e) {
-        bf16x8 pb[2];
-        fact_keys<N8>(st, kr, qb, q4, rem, pb);
+        typename F::Probs pb;
+        F::keys(st, kr, fq, q4, rem, pb);
         const bool more = e + 1 < e1;
-        if (more) load_keys<N8>(kr, kptr(e + 1), lane);
-        fact_values<N8>(st, vr, pb, rem);
-        if (more) load_values<N8>(vr, vptr(e + 1), lane);
+        if (more) F::load_keys(kr, kptr(e + 1), lane);
+        F::values(st, vr, pb, q4, rem);
+        if (more) F::load_values(vr, vptr(e + 1), lane);
       }
     }
   }
@@ -514,6 +902,7 @@ __global__ __launch_bounds__(256, mfma_waves_per_simd(N8)) void decode_mfma_kern
 #pragma unroll
     for (int v = 0; v < 4; ++v) st.o[mt][v] += ror8(st.o[mt][v]);
   }
+  if constexpr (F::kLdsRing) __syncthreads();  // every wave is done with its ring
   if (n < 8) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
@@ -858,7 +1247,7 @@ int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact) {
   // the split count while a wave would get fewer than 16 pages and a CU would
   // still get a workgroup.  Long runs per wave stream better than more waves
   // (Qwen3-32B-shaped 128K layer: 32 splits 48.0 us, 64 splits 49.5 us).
-  const int wps = g.dtype == PKV_BF16 ? mfma_waves_per_simd((g.r_k > g.r_v ? g.r_k + 7 : g.r_v + 7) / 8) : 2;
+  const int wps = g.dtype == PKV_BF16 ? mfma_waves_per_simd((g.r_k > g.r_v ? g.r_k + 7 : g.r_v + 7) / 8) : 2;  // INT4 and fp32: 2
   int64_t s = (256LL * wps + bh - 1) / bh;
   while (s > 1 && pages < 16 * 4 * s && (s / 2) * bh >= 256) s /= 2;
   const int64_t cap = (pages + 3) / 4;  // at least ~4 pages per workgroup
@@ -877,7 +1266,7 @@ hipError_t launch_merge(const CacheGeom& g, const AttnJob& job, hipStream_t stre
   m.q = job.q;
   m.k_new = job.k_new;
   m.v_new = job.v_new;
-  m.dtype = g.dtype;
+  m.dtype = dense_dtype(g.dtype);
   m.qscale = kLog2e / sqrtf((float)kD);
   m.G = g.G;
   m.Hkv = g.Hkv;
@@ -929,7 +1318,7 @@ hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t st
   a.n_fact = job.n_fact;
   a.F_max = g.F_max;
   a.page_bytes = g.lay.factor_page_bytes;
-  a.k_part_bytes = g.lay.factor_k_elems * g.lay.elem_bytes;
+  a.k_part_bytes = g.lay.factor_k_bytes;
   // cost of a unit ~ bytes it streams (dense: K and V pages)
   a.cost_dense = 2 * g.lay.dense_page_bytes / 64;
   a.cost_fact = g.lay.factor_page_bytes / 64;
@@ -938,11 +1327,29 @@ hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t st
   const dim3 grid(job.n_split, g.Hkv, g.B);
   const KernelEvents ev = take_kernel_events();
   const int n8k = (g.r_k + 7) / 8, n8v = (g.r_v + 7) / 8;
-  if (g.dtype == PKV_BF16 && n8k == n8v) {
+  if (g.dtype == PKV_BF16_INT4) {
+    switch (n8k * 8 + n8v) {
+#define PKV_Q4(NK, NV)                                                                              \
+  case NK * 8 + NV:                                                                                 \
+    hipExtLaunchKernelGGL((decode_mfma_kernel<Int4Factors<NK, NV>>), grid, dim3(256), 0, stream,   \
+                          ev.start, ev.stop, 0, a);                                                 \
+    break;
+#define PKV_Q4_ROW(NK) PKV_Q4(NK, 1) PKV_Q4(NK, 2) PKV_Q4(NK, 3) PKV_Q4(NK, 4)
+      PKV_Q4_ROW(1)
+      PKV_Q4_ROW(2)
+      PKV_Q4_ROW(3)
+      PKV_Q4_ROW(4)
+#undef PKV_Q4_ROW
+#undef PKV_Q4
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else if (g.dtype == PKV_BF16 && n8k == n8v) {
     switch (n8k) {
-#define PKV_CASE(N)                                                                 \
-  case N:                                                                           \
-    hipExtLaunchKernelGGL(decode_mfma_kernel<N>, grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a); \
+#define PKV_CASE(N)                                                                                     \
+  case N:                                                                                               \
+    hipExtLaunchKernelGGL(decode_mfma_kernel<Bf16Factors<N>>, grid, dim3(256), 0, stream, ev.start, ev.stop, \
+                          0, a);                                                                        \
     break;
       PKV_CASE(1)
       PKV_CASE(2)

@@ -46,8 +46,8 @@ struct PackDims {
   int64_t k1, k2, v1, v2;  // element counts of the four operands
 };
 
-__host__ __device__ inline PackDims pack_dims(int r) {
-  PackDims p;
+__host__ __device__ constexpr PackDims pack_dims(int r) {
+  PackDims p{};
   p.n8 = (r + 7) / 8;
   p.A = 2 * p.n8;
   p.RT = (p.A + 3) / 4;
@@ -119,6 +119,114 @@ __host__ __device__ inline int64_t off_rf_v(const PackDims& p, int i, int c) {
   int lane = 16 * qk + rho;
   return p.v1 + (int64_t)mt * 64 * p.A + 512 * ks + lane * w + e;
 }
+
+// --------------------------------------------------------------------------
+// INT4 factor part layout (PuzzleKV Sec. 4.3): Lt = U_r Sigma_r^(1/2) and
+// Rt = Sigma_r^(1/2) W_r^T, each held as symmetric 4-bit codes c in -7..7
+// with one bf16 scale per group -- per column of Lt_K (rank), Rt_K and Rt_V
+// (channel), per row of Lt_V (token).  Ranks up to 32 (one 32-wide
+// reduction step over the rank, KS2 = 1).
+//
+// A code is stored as the nibble c + 8.  The operands keep the matrix-core
+// roles and lane order of the bf16 layout above; a lane's 8 reduction slots
+// of one MFMA step form one unit.  K1 / V1 units (8 channels / tokens) are
+// dwords; K2 / V2 units hold the lane quad's A ranks in UB bytes
+// (A = 2 -> 1 byte, 4 -> 2, 6 or 8 -> 4; padding nibbles hold 8, i.e. c = 0).
+// Within a unit of W = 2 UB nibbles, element e sits at bit
+// 4 ((e % 2) W / 2 + e / 2): for a dword, ((u >> 4k) & 0x000F000F) are the
+// nibbles of elements 2k and 2k + 1 in the two 16-bit halves.
+//
+// K part (byte offsets):  K1 codes  [tile][lane][ks 0..3] dwords; 1024 per
+//                                   full tile, 512 for a compacted last tile
+//                         K2 codes  [lane][mt 0..3] units
+//                         sR_K      [c] bf16, c < d
+//                         sL_K      [i] bf16, i < r8 (0 for padding ranks)
+// V part:                 V1 codes  [tile][lane][ks 0..1] dwords; 512 / 256
+//                         V2 codes  [lane][mt 0..7] units
+//                         sL_V      [j] bf16, j < P
+//                         sR_V      [q4][mt][v] bf16: channel 16 mt + 4 q4 + v
+// Each part is padded to a multiple of 64 bytes.
+// --------------------------------------------------------------------------
+
+constexpr int kQ4MaxRank = 32;
+
+__host__ __device__ constexpr int q4_unit_bytes(int A) { return A <= 2 ? 1 : (A <= 4 ? 2 : 4); }
+
+struct Q4Dims {
+  PackDims pd;
+  int ub;                     // bytes of a K2 / V2 unit
+  int64_t k2, sr_k, sl_k, k_bytes;
+  int64_t v2, sl_v, sr_v, v_bytes;
+};
+
+__host__ __device__ constexpr Q4Dims q4_dims(int r) {
+  Q4Dims q{};
+  q.pd = pack_dims(r);
+  const int A = q.pd.A, full = A / 4, part = (A % 4) ? 1 : 0;
+  q.ub = q4_unit_bytes(A);
+  q.k2 = (int64_t)full * 1024 + part * 512;
+  q.sr_k = q.k2 + 256LL * q.ub;
+  q.sl_k = q.sr_k + 2LL * kD;
+  q.k_bytes = (q.sl_k + 2LL * 4 * A + 63) / 64 * 64;
+  q.v2 = (int64_t)full * 512 + part * 256;
+  q.sl_v = q.v2 + 512LL * q.ub;
+  q.sr_v = q.sl_v + 2LL * kP;
+  q.v_bytes = (q.sr_v + 2LL * kD + 63) / 64 * 64;
+  return q;
+}
+
+__host__ __device__ inline int q4_nibble_bit(int W, int e) { return 4 * ((e % 2) * (W / 2) + e / 2); }
+
+// Location of one code: the unit's byte offset in the part, its width in
+// nibbles and the code's bit position in it.
+struct Q4Slot {
+  int64_t byte;
+  int W;
+  int bit;
+};
+
+// Row of rank i in its rank tile (full tile: lane 16 qk + rho; compacted
+// tile: qk * 8 + b * 2 + v).
+__host__ __device__ inline int q4_tile_row(const RankSlot& s, int qk) {
+  return s.partial ? qk * 8 + s.b * 2 + s.v : 16 * qk + s.rho;
+}
+
+// K1: Rt_K[i][c]
+__host__ __device__ inline Q4Slot q4_rt_k(const Q4Dims& q, int i, int c) {
+  const RankSlot s = rank_slot(q.pd, i);
+  const int ks = c / 32, qk = (c % 32) / 8, e = c % 8;
+  return Q4Slot{(int64_t)s.mt * 1024 + (q4_tile_row(s, qk) * 4 + ks) * 4, 8, q4_nibble_bit(8, e)};
+}
+
+// K2: Lt_K[j][i]
+__host__ __device__ inline Q4Slot q4_lt_k(const Q4Dims& q, int j, int i) {
+  const int mt = (j % 16) / 4, lane = 16 * (i / q.pd.A) + 4 * (j / 16) + j % 4;
+  return Q4Slot{q.k2 + ((int64_t)lane * 4 + mt) * q.ub, 2 * q.ub, q4_nibble_bit(2 * q.ub, i % q.pd.A)};
+}
+
+// V1: Lt_V[j][i] (as Lt_V^T)
+__host__ __device__ inline Q4Slot q4_lt_v(const Q4Dims& q, int j, int i) {
+  const RankSlot s = rank_slot(q.pd, i);
+  const int qk = j / 16, ks = (j % 16) / 8, e = j % 8;
+  return Q4Slot{(int64_t)s.mt * 512 + (q4_tile_row(s, qk) * 2 + ks) * 4, 8, q4_nibble_bit(8, e)};
+}
+
+// V2: Rt_V[i][c] (as Rt_V^T)
+__host__ __device__ inline Q4Slot q4_rt_v(const Q4Dims& q, int i, int c) {
+  const int mt = c / 16, lane = 16 * (i / q.pd.A) + c % 16;
+  return Q4Slot{q.v2 + ((int64_t)lane * 8 + mt) * q.ub, 2 * q.ub, q4_nibble_bit(2 * q.ub, i % q.pd.A)};
+}
+
+// Byte offsets of the scales.
+__host__ __device__ inline int64_t q4_sr_k(const Q4Dims& q, int c) { return q.sr_k + 2LL * c; }
+__host__ __device__ inline int64_t q4_sl_k(const Q4Dims& q, int i) { return q.sl_k + 2LL * i; }
+__host__ __device__ inline int64_t q4_sl_v(const Q4Dims& q, int j) { return q.sl_v + 2LL * j; }
+__host__ __device__ inline int64_t q4_sr_v(const Q4Dims& q, int c) {
+  return q.sr_v + 2LL * (((c % 16) / 4) * 32 + (c / 16) * 4 + c % 4);
+}
+
+// Dense pages of an INT4-factor cache are bf16.
+__host__ __device__ inline int dense_dtype(int dtype) { return dtype == PKV_F32 ? PKV_F32 : PKV_BF16; }
 
 // Page-table entry encoding.
 __host__ __device__ inline int32_t table_entry(int cls, int slot) { return (cls << 24) | slot; }

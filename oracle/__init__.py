@@ -187,16 +187,23 @@ def dequantize_int4(q, s):
     return q.astype(np.float64) * s
 
 
-def int4_factors(U, S, Wt, r, kind):
+def int4_codes(U, S, Wt, r, kind):
     """Sec. 4.3: the singular values are split between the two factors,
     Lt = U_r Sigma_r^(1/2) (P x r) and Rt = Sigma_r^(1/2) W_r^T (r x d), and
     each factor is INT4-quantized: Lt column-wise for keys and row-wise for
-    values, Rt column-wise for both.  Returns the dequantized (Lt, Rt)."""
+    values, Rt column-wise for both.  Returns (Lt, Rt) unquantized and the
+    codes and scales (lq, ls, rq, rs) of quantize_int4."""
     h = np.sqrt(S[..., :r])
     Lt = U[..., :, :r] * h[..., None, :]
     Rt = Wt[..., :r, :] * h[..., :, None]
     lq, ls = quantize_int4(Lt, axis=-2 if kind == "K" else -1)
     rq, rs = quantize_int4(Rt, axis=-2)
+    return Lt, Rt, lq, ls, rq, rs
+
+
+def int4_factors(U, S, Wt, r, kind):
+    """The dequantized INT4 factors (Lt, Rt) of int4_codes."""
+    _, _, lq, ls, rq, rs = int4_codes(U, S, Wt, r, kind)
     return dequantize_int4(lq, ls), dequantize_int4(rq, rs)
 
 
