@@ -15,7 +15,9 @@ Inputs are seeded synthetic pages with the sigma_i = i^-1.2 spectrum
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 Prints one JSON line.  Other workloads: llama3.1-8b-layer (B = 8, T = 32768,
-r = 16) and compress (batched page decomposition, 524288 pages, r in {8,16,32}).
+r = 16), qwen3-32b-layer-128k-int4 and llama3.1-8b-layer-int4 (the same
+layers with INT4 factor pages, PuzzleKV Sec. 4.3), and compress (batched page
+decomposition, 524288 pages, r in {8,16,32}).
 """
 import argparse
 import json
@@ -88,18 +90,23 @@ def to_dev(a, dtype):
     return torch.from_numpy(a.astype(np.float32)).cuda()
 
 
-def decode_bytes(cfg, B, Hkv, Hq, T, n_fact):
+def decode_bytes(cfg, B, Hkv, Hq, T, n_fact, store=None):
     """Algorithmic bytes one mixed-attention launch must move: factors of every
-    factorized page (r (P + d) elements per K and per V page), the valid rows
-    of every dense page (K and V), q in, o out (fp32)."""
+    factorized page (r (P + d) elements per K and per V page; INT4 pages:
+    (r_K + r_V)(P + d) / 2 code bytes and the 16-bit scales of their four
+    factors, 2 (r_K + d + P + d)), the valid rows of every dense page (K and
+    V), q in, o out (fp32)."""
     esz = 2 if cfg["dtype"] == "bf16" else 4
     P, d = cfg["P"], cfg["d"]
-    fact = n_fact * (cfg["r_k"] + cfg["r_v"]) * (P + d) * esz
+    if store == "int4":
+        fact = n_fact * ((cfg["r_k"] + cfg["r_v"]) * (P + d) // 2 + 2 * (cfg["r_k"] + d + P + d))
+    else:
+        fact = n_fact * (cfg["r_k"] + cfg["r_v"]) * (P + d) * esz
     dense = (T - n_fact * P) * d * 2 * esz
     return B * Hkv * (fact + dense) + B * Hq * d * esz + B * Hq * d * 4
 
 
-def cpu_baseline_decode(cfg, K, V, q, T):
+def cpu_baseline_decode(cfg, K, V, q, T, store=None):
     """The oracle on a bounded sample: KV head 0 of the same cache.  The
     oracle reconstructs that head (Jacobi SVD of its factorized pages,
     truncation, storage rounding; timed -> pages/s), then its naive float64
@@ -120,8 +127,9 @@ def cpu_baseline_decode(cfg, K, V, q, T):
     q64 = synth.storage_to_f64(q[0, :G], cfg["dtype"])
     n_fact = int((oracle.classify(T, P, s, w)[0] == oracle.FACT).sum())
     t = time.perf_counter()
-    Khat = oracle.reconstruct_cache(k64, T, P, s, w, cfg["r_k"], cfg["dtype"])[0]
-    Vhat = oracle.reconstruct_cache(v64, T, P, s, w, cfg["r_v"], cfg["dtype"])[0]
+    st = store or cfg["dtype"]
+    Khat = oracle.reconstruct_cache(k64, T, P, s, w, cfg["r_k"], st, kind="K")[0]
+    Vhat = oracle.reconstruct_cache(v64, T, P, s, w, cfg["r_v"], st, kind="V")[0]
     t_rec = time.perf_counter() - t
     reps = 3
     t = time.perf_counter()
@@ -139,7 +147,7 @@ def cpu_baseline_decode(cfg, K, V, q, T):
                 svd_pages_per_s=2 * n_fact / t_rec)
 
 
-def bench_decode(args, cfg_id, name):
+def bench_decode(args, cfg_id, name, store=None):
     """One decode step of the workload's layer, on NL independent layer caches
     in rotation (a decode step of an NL-layer stack), so that no cache is
     re-read from the 256 MB Infinity Cache between its uses."""
@@ -155,7 +163,7 @@ def bench_decode(args, cfg_id, name):
     dt = cfg["dtype"]
     Kd, Vd = to_dev(inp["K"], dt), to_dev(inp["V"], dt)
     caches = [pkv.Cache(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, rank_k=cfg["r_k"], rank_v=cfg["r_v"],
-                        sink=cfg["s"], window=cfg["w"], max_tokens=total, dtype=dt)
+                        sink=cfg["s"], window=cfg["w"], max_tokens=total, dtype=store or dt)
               for _ in range(NL)]
     K0 = Kd[:, :, :T0].contiguous()
     V0 = Vd[:, :, :T0].contiguous()
@@ -254,7 +262,7 @@ def bench_decode(args, cfg_id, name):
             promos.append(a.elapsed_time(b) * 1e-3)
         promos = promos[1:]
     states = [states[k] for k in keep]
-    nbytes = np.array([decode_bytes(cfg, B, Hkv, Hq, T, nf) for T, nf in states], dtype=np.float64)
+    nbytes = np.array([decode_bytes(cfg, B, Hkv, Hq, T, nf, store) for T, nf in states], dtype=np.float64)
     achieved = nbytes.sum() / durs.sum() / 1e9
     layer_steps = args.steps * NL
     traffic = pmc_traffic(name)
@@ -276,12 +284,13 @@ def bench_decode(args, cfg_id, name):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 storage, f32 math" if dt == "bf16" else "f32",
+        "dtype": ("bf16 dense pages + int4 factor pages (bf16 scales), f32 math" if store == "int4"
+                  else "bf16 storage, f32 math" if dt == "bf16" else "f32"),
         "data": "synthetic (seeded generator, workload recipe)",
         "config": {"workload": name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": cfg["d"],
                    "context_tokens": T0, "page_len": cfg["P"], "rank_k": cfg["r_k"],
                    "rank_v": cfg["r_v"], "sink": cfg["s"], "window": cfg["w"],
-                   "layer_caches_rotated": NL,
+                   "layer_caches_rotated": NL, "factor_store": store or dt,
                    "step": "pkv_decode_step per layer: promotion when a page leaves the window, "
                            "decode partial, merge with the appended token folded in",
                    "early_factorization": bool(args.aux)},
@@ -320,7 +329,7 @@ def bench_decode(args, cfg_id, name):
                            "roofline": compress_summary(cres, c5["ranks"][1])}
     if args.cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")
-        cb = cpu_baseline_decode(cfg, inp["K"], inp["V"], inp["q"], T0)
+        cb = cpu_baseline_decode(cfg, inp["K"], inp["V"], inp["q"], T0, store)
         res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
         res["cpu_baseline_svd_pages_per_s"] = cb["svd_pages_per_s"]
     return res
@@ -469,7 +478,8 @@ def main():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="qwen3-32b-layer-128k",
-                    choices=["qwen3-32b-layer-128k", "llama3.1-8b-layer", "compress", "copy"])
+                    choices=["qwen3-32b-layer-128k", "llama3.1-8b-layer", "qwen3-32b-layer-128k-int4",
+                             "llama3.1-8b-layer-int4", "compress", "copy"])
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--workers", type=int, default=1)
     ap.add_argument("--layers", type=int, default=4,
@@ -497,10 +507,10 @@ def main():
         res = bench_compress(args)
     elif args.workload == "copy":
         res = bench_copy(args)
-    elif args.workload == "llama3.1-8b-layer":
-        res = bench_decode(args, 2, args.workload)
+    elif args.workload.startswith("llama3.1-8b-layer"):
+        res = bench_decode(args, 2, args.workload, "int4" if args.workload.endswith("-int4") else None)
     else:
-        res = bench_decode(args, 3, args.workload)
+        res = bench_decode(args, 3, args.workload, "int4" if args.workload.endswith("-int4") else None)
     print(json.dumps(res), flush=True)
 
 

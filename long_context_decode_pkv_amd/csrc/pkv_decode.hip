@@ -310,6 +310,68 @@ __device__ inline void softmax_page(SoftState& st, const floatx4 (&acc)[4], int 
   }
 }
 
+// Online softmax of one full page with a lazily raised reference maximum:
+// st.m moves only when a score exceeds it by more than 2^kSlack (in log2
+// units), so the running output is rescaled only then (the result is the
+// same; weights up to 2^kSlack are exact in fp32).  Leaves 256 e^(s - m) in
+// p (the factor folds a power of two of the value contraction) and adds
+// sum e^(s - m) to st.l.
+constexpr float kSlack = 8.f;
+
+// x combined with lane l ^ 16 / l ^ 32 of each lane l: gfx950
+// v_permlane16_swap / v_permlane32_swap with both operands x return the pair
+// {x[l], x[l ^ 16]} (resp. l ^ 32) in every lane -- a VALU exchange instead
+// of an LDS round trip.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline void softmax_probs_lazy(SoftState& st, const floatx4 (&acc)[4], int q4, float (&p)[4][4]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      p[mt][v] = acc[mt][v] + ror8(acc[mt][v]);
+      mx = fmaxf(mx, p[mt][v]);
+    }
+  }
+  mx = max_xor32(max_xor16(mx));
+  if (__any(mx > st.m + kSlack)) {
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = fast_exp2(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) st.o[mt] *= alpha;
+    st.m = m_new;
+  }
+  const float mref = st.m - 8.f;  // 256 e^(s - m) = 2^(s - (m - 8))
+  float ps = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      p[mt][v] = fast_exp2(p[mt][v] - mref);
+      ps += p[mt][v];
+    }
+  }
+  ps = sum_xor32(sum_xor16(ps));
+  st.l = __builtin_fmaf(ps, 1.f / 256.f, st.l);
+}
+
 // hi/lo-combined rank vector of rank tiles -> B operand slots.
 template <int N8>
 __device__ inline void rank_operand(const floatx4 (&acc)[FactDims<N8>::RT], float rem,
@@ -450,14 +512,15 @@ struct Bf16Factors {
 // codes c with bf16 group scales (layout: pkv_internal.h).  A code nibble
 // n = c + 8 enters the matrix cores as the exact bf16 value 1 + n/16 =
 // 1.5 + c/16 (n in mantissa bits 3..6 of 1.0, two codes per and-or).  One
-// extra MFMA per contraction with the constant operand -1.5 removes the
-// offset (it starts the accumulator), leaving (1/16) sum c b.  The scales
-// fold into the fp32 vector operands:
-//   t / 16  = (1/16) Rq_K (sR_K o q)            B operand sR_K o q
-//   s       = (1/16) Lq_K (256 sL_K o (t / 16))  B operand 256 sL_K o t/16
-//   u / 16  = (1/16) Lq_V^T (sL_V o p)           B operand sL_V o p
-//   o      += 256 sR_V o (1/16) Rq_V^T (u / 16)  B operand u / 16
-// each B operand again as bf16 hi/lo columns.
+// extra MFMA per contraction with the constant operand -1.5 starts the
+// accumulator and removes the offset, leaving (1/16) sum c b.  The scales
+// fold into the fp32 vector operands, and the powers of two into the query
+// (x 256) and the softmax exponent (p x 256):
+//   16 t = (1/16) Rq_K (sR_K o 256 q)            B operand sR_K o 256 q
+//   s    = (1/16) Lq_K (sL_K o 16 t)             B operand sL_K o 16 t
+//   16 u = (1/16) Lq_V^T (sL_V o 256 p)          B operand sL_V o 256 p
+//   o   += sR_V o (1/16) Rq_V^T (16 u)           B operand 16 u
+// each B operand as bf16 hi/lo columns (hi = the truncated top 16 bits).
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
@@ -469,11 +532,30 @@ __device__ __forceinline__ float bf16_at(const uint32_t* d) {
   return E % 2 ? bf16_hi(d[E / 2]) : bf16_lo(d[E / 2]);
 }
 
+// A 32-bit constant materialized in a VGPR: VOP3 forms such as v_and_or_b32
+// take no literal operand on gfx950, and an SGPR operand is limited to one.
+// (The asm is side-effect free, so the compiler hoists it out of loops.)
+template <uint32_t C>
+__device__ __forceinline__ uint32_t vgpr_const() {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(C));
+  return r;
+}
+
 // codes 2k, 2k + 1 of a unit (bits 4k.. of each 16-bit half) -> bf16 pair
 template <int K>
 __device__ __forceinline__ uint32_t q4_pair(uint32_t u) {
   const uint32_t sh = K == 0 ? (u << 3) : (u >> (4 * K - 3));
-  return (sh & 0x00780078u) | 0x3f803f80u;
+  return (sh & vgpr_const<0x00780078u>()) | vgpr_const<0x3f803f80u>();
+}
+
+// Operand pair (x0, x1) as bf16 hi/lo columns: on hi lanes (rem 0) the top
+// 16 bits of x, on lo lanes (rem 1) the top 16 bits of x minus its top 16
+// bits (an exact fp32 difference); x0 in the low half.
+__device__ __forceinline__ uint32_t split2(float x0, float x1, float rem) {
+  const float y0 = __builtin_fmaf(-rem, __uint_as_float(__float_as_uint(x0) & 0xffff0000u), x0);
+  const float y1 = __builtin_fmaf(-rem, __uint_as_float(__float_as_uint(x1) & 0xffff0000u), x1);
+  return __builtin_amdgcn_perm(__float_as_uint(y1), __float_as_uint(y0), 0x07060302u);
 }
 
 // unit of W nibbles in the low 4 W bits of x -> operand slots 0 .. 2 NP - 1
@@ -602,7 +684,7 @@ struct Int4Factors {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Q.qf[ks][e] = qs[ks][e];
+      for (int e = 0; e < 8; ++e) Q.qf[ks][e] = 256.f * qs[ks][e];
     }
   }
 
@@ -666,16 +748,19 @@ struct Int4Factors {
   // Eq. 4, key half on the codes: t = Rt_K q, s = Lt_K t, online softmax.
   // Rank slots e >= A of the second contraction are zero: they belong to no
   // rank (rows of the compacted tile that lanes only read as filler).
+  // Leaves 256 p in p (see softmax_probs_lazy).
   __device__ static void keys(SoftState& st, const K& R, const Query& Q, int q4, float rem, Probs& p) {
     const bf16x8 off = q4_offset_operand();
     bf16x8 qb[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      uint4 w;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t d = R.sr[4 * ks + e / 2];
-        qb[ks][e] = split_bf16(Q.qf[ks][e] * (e % 2 ? bf16_hi(d) : bf16_lo(d)), rem);
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t d = R.sr[4 * ks + k];
+        (&w.x)[k] = split2(Q.qf[ks][2 * k] * bf16_lo(d), Q.qf[ks][2 * k + 1] * bf16_hi(d), rem);
       }
+      qb[ks] = __builtin_bit_cast(bf16x8, w);
     }
     floatx4 base = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -687,21 +772,20 @@ struct Int4Factors {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) at[mt] = mfma(q4_operand<8, 4>(R.k1[mt][ks]), qb[ks], at[mt]);
     }
-    bf16x8 tb;
+    uint4 w = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = 0.f;
-      if (e < AK) {
-        const uint32_t d = R.sl[e / 2];
-        x = (at[e / 4][e % 4] + ror8(at[e / 4][e % 4])) * (256.f * (e % 2 ? bf16_hi(d) : bf16_lo(d)));
-      }
-      tb[e] = split_bf16(x, rem);
+    for (int k = 0; k < N8K; ++k) {  // slots 2k, 2k + 1 < AK
+      const uint32_t d = R.sl[k];
+      const float t0 = at[k / 2][2 * (k % 2)] + ror8(at[k / 2][2 * (k % 2)]);
+      const float t1 = at[k / 2][2 * (k % 2) + 1] + ror8(at[k / 2][2 * (k % 2) + 1]);
+      (&w.x)[k] = split2(t0 * bf16_lo(d), t1 * bf16_hi(d), rem);
     }
+    const bf16x8 tb = __builtin_bit_cast(bf16x8, w);
     const floatx4 base2 = mfma(off, tb, floatx4{0.f, 0.f, 0.f, 0.f});
     floatx4 as_[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) as_[mt] = mfma(q4_operand<2 * UK, N8K>(q4_unit<UK>(R.k2, mt)), tb, base2);
-    softmax_probs(st, as_, kP, q4, p);
+    softmax_probs_lazy(st, as_, q4, p);
   }
 
   // Eq. 4, value half on the codes: u = Lt_V^T p, o += Rt_V^T u.
@@ -710,11 +794,14 @@ struct Int4Factors {
     bf16x8 pb[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      uint4 w;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t d = R.sl[(8 * ks + e) / 2];
-        pb[ks][e] = split_bf16(p[2 * ks + e / 4][e % 4] * (e % 2 ? bf16_hi(d) : bf16_lo(d)), rem);
+      for (int k = 0; k < 4; ++k) {  // tokens 16 q4 + 8 ks + 2k, + 1
+        const uint32_t d = R.sl[4 * ks + k];
+        const int mt = 2 * ks + k / 2, v = 2 * (k % 2);
+        (&w.x)[k] = split2(p[mt][v] * bf16_lo(d), p[mt][v + 1] * bf16_hi(d), rem);
       }
+      pb[ks] = __builtin_bit_cast(bf16x8, w);
     }
     floatx4 base = mfma(off, pb[0], floatx4{0.f, 0.f, 0.f, 0.f});
     base = mfma(off, pb[1], base);
@@ -725,12 +812,14 @@ struct Int4Factors {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) au[mt] = mfma(q4_operand<8, 4>(R.v1[mt][ks]), pb[ks], au[mt]);
     }
-    bf16x8 ub;
+    uint4 w = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = e < AV ? au[e / 4][e % 4] + ror8(au[e / 4][e % 4]) : 0.f;
-      ub[e] = split_bf16(x, rem);
+    for (int k = 0; k < N8V; ++k) {
+      const float u0 = au[k / 2][2 * (k % 2)] + ror8(au[k / 2][2 * (k % 2)]);
+      const float u1 = au[k / 2][2 * (k % 2) + 1] + ror8(au[k / 2][2 * (k % 2) + 1]);
+      (&w.x)[k] = split2(u0, u1, rem);
     }
+    const bf16x8 ub = __builtin_bit_cast(bf16x8, w);
     const floatx4 base2 = mfma(off, ub, floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
@@ -738,7 +827,7 @@ struct Int4Factors {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const uint32_t d = R.sr[(4 * mt + v) / 2];
-        st.o[mt][v] = __builtin_fmaf(256.f * (v % 2 ? bf16_hi(d) : bf16_lo(d)), acc[v], st.o[mt][v]);
+        st.o[mt][v] = __builtin_fmaf(v % 2 ? bf16_hi(d) : bf16_lo(d), acc[v], st.o[mt][v]);
       }
     }
   }
@@ -835,7 +924,9 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
     auto vptr = [&](int64_t ee) { return fac_bh + (ee - wl.D) * a.page_bytes + kpb; };
     if constexpr (F::kLdsRing) {
       // ring slot s holds pages e with e = s (mod kRingSlots); pages up to
-      // e + kRingSlots - 1 are staged while page e is computed
+      // e + kRingSlots - 1 are staged while page e is computed.  Register
+      // images are read from the ring half a page ahead of use: page e's V
+      // part before its key half, page e + 1's K part before e's value half.
       constexpr int NS = F::kRingSlots;
       uint8_t* ring = lds + wave * NS * F::kPageBytes;
       int64_t next = e;  // next page to stage
@@ -844,21 +935,25 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
         F::stage(ring + s_next * F::kPageBytes, kptr(next), lane);
         s_next = s_next + 1 == NS ? 0 : s_next + 1;
       }
+      typename F::K kr;
+      F::wait_staged((int)(next - 1 - e));
+      F::load_keys(kr, ring, lane);
       for (; e < e1; ++e) {
         if (next < e1) {  // into the slot of page e - 1, read in full last iteration
           F::stage(ring + s_next * F::kPageBytes, kptr(next), lane);
           s_next = s_next + 1 == NS ? 0 : s_next + 1;
           ++next;
         }
-        F::wait_staged((int)(next - 1 - e));
         const uint8_t* slot = ring + s_cur * F::kPageBytes;
         s_cur = s_cur + 1 == NS ? 0 : s_cur + 1;
-        typename F::K kr;
-        F::load_keys(kr, slot, lane);
-        typename F::Probs pb;
-        F::keys(st, kr, fq, q4, rem, pb);
         typename F::V vr;
         F::load_values(vr, slot + F::kKBytes, lane);
+        typename F::Probs pb;
+        F::keys(st, kr, fq, q4, rem, pb);
+        if (e + 1 < e1) {
+          F::wait_staged((int)(next - 2 - e));
+          F::load_keys(kr, ring + s_cur * F::kPageBytes, lane);
+        }
         F::values(st, vr, pb, q4, rem);
       }
     } else if constexpr (F::kKeyDoubleBuffer) {
@@ -1244,12 +1339,16 @@ int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact) {
   const int64_t pages = (T + kP - 1) / kP;
   const int64_t bh = (int64_t)g.B * g.Hkv;
   // Two four-wave workgroups per CU fill the chip at 2 waves per SIMD; halve
-  // the split count while a wave would get fewer than 16 pages and a CU would
-  // still get a workgroup.  Long runs per wave stream better than more waves
-  // (Qwen3-32B-shaped 128K layer: 32 splits 48.0 us, 64 splits 49.5 us).
+  // the split count while a wave would get fewer than min_run pages and a CU
+  // would still get a workgroup.  bf16 pages: long runs per wave stream
+  // better than more waves (Qwen3-32B-shaped 128K layer: 32 splits 48.0 us,
+  // 64 splits 49.5 us); INT4 pages are a third of the bytes and compute-bound
+  // per wave, so both workgroups per CU pay off (same layer: 32 splits
+  // 37.1 us, 64 splits 35.0 us).
   const int wps = g.dtype == PKV_BF16 ? mfma_waves_per_simd((g.r_k > g.r_v ? g.r_k + 7 : g.r_v + 7) / 8) : 2;  // INT4 and fp32: 2
+  const int64_t min_run = g.dtype == PKV_BF16_INT4 ? 8 : 16;
   int64_t s = (256LL * wps + bh - 1) / bh;
-  while (s > 1 && pages < 16 * 4 * s && (s / 2) * bh >= 256) s /= 2;
+  while (s > 1 && pages < min_run * 4 * s && (s / 2) * bh >= 256) s /= 2;
   const int64_t cap = (pages + 3) / 4;  // at least ~4 pages per workgroup
   if (s > cap) s = cap;
   if (s > kMaxSplits) s = kMaxSplits;

@@ -2,7 +2,8 @@
 bench.py times (default split counts, one launch over the whole batch).
 
 Sampling, so that the oracle finishes in seconds:
-- Workloads 2 and 3 (one decode step) and 4 (512 incremental steps): every
+- Workloads 2 and 3 (one decode step; workload 3 also with INT4 factor
+  pages) and 4 (512 incremental steps): every
   (sequence, KV head) holds the recipe's pages of (sequence 0, KV head 0),
   so one oracle reconstruction serves all heads.  The queries are the
   recipe's own, distinct per query head, and every query head's output is
@@ -44,10 +45,10 @@ def recipe_queries(cfg_id):
     return d["q"], synth.storage_to_f64(d["q"], cfg["dtype"])
 
 
-def make_full_cache(cfg, max_tokens):
+def make_full_cache(cfg, max_tokens, store=None):
     return pkv.Cache(batch=cfg["B"], n_q_heads=cfg["Hq"], n_kv_heads=cfg["Hkv"], rank_k=cfg["r_k"],
                      rank_v=cfg["r_v"], sink=cfg["s"], window=cfg["w"], max_tokens=max_tokens,
-                     dtype=cfg["dtype"])
+                     dtype=store or cfg["dtype"])
 
 
 def oracle_outputs(q64, Khat, Vhat):
@@ -56,14 +57,15 @@ def oracle_outputs(q64, Khat, Vhat):
     return oracle.attention(q64.reshape(B * Hq, d), Khat, Vhat).reshape(B, Hq, d)
 
 
-def decode_full(cfg_id):
+def decode_full(cfg_id, store=None):
     import torch
     require_gpu()
     cfg = synth.CONFIGS[cfg_id]
     T, P, dt = cfg["T"], cfg["P"], cfg["dtype"]
+    st = store or dt
     K, V, k64, v64 = replicated_kv(cfg_id, T + 1)
     q, q64 = recipe_queries(cfg_id)
-    cache = make_full_cache(cfg, T + 1)
+    cache = make_full_cache(cfg, T + 1, store)
     Kd, Vd = to_dev(K, dt), to_dev(V, dt)
     cache.prefill(Kd[:, :, :T].contiguous(), Vd[:, :, :T].contiguous())
     qd = to_dev(q, dt)
@@ -72,13 +74,13 @@ def decode_full(cfg_id):
     o2 = to_f64(cache.step(Kd[:, :, T].contiguous(), Vd[:, :, T].contiguous(), qd))
     torch.cuda.synchronize()
     for TT, o in ((T, o1), (T + 1, o2)):
-        Ks = oracle.reconstruct_cache(k64[:TT], TT, P, cfg["s"], cfg["w"], cfg["r_k"], dt)[0]
-        Vs = oracle.reconstruct_cache(v64[:TT], TT, P, cfg["s"], cfg["w"], cfg["r_v"], dt)[0]
+        Ks = oracle.reconstruct_cache(k64[:TT], TT, P, cfg["s"], cfg["w"], cfg["r_k"], st, kind="K")[0]
+        Vs = oracle.reconstruct_cache(v64[:TT], TT, P, cfg["s"], cfg["w"], cfg["r_v"], st, kind="V")[0]
         ref = oracle_outputs(q64, Ks, Vs)
         err = rel_err(o, ref)
-        print(f"[full size workload {cfg_id}] T={TT}: max err / max|o_ref| = {err:.3e} "
+        print(f"[full size workload {cfg_id} {st}] T={TT}: max err / max|o_ref| = {err:.3e} "
               f"over {o.shape[0] * o.shape[1]} query heads")
-        assert err <= TOL[dt], (cfg_id, TT, err)
+        assert err <= TOL[st], (cfg_id, TT, err)
     cls, slot = cache.page_table(-(-(T + 1) // P))
     ocls, oslot = oracle.classify(T + 1, P, cfg["s"], cfg["w"])
     np.testing.assert_array_equal(cls, ocls)
@@ -91,6 +93,11 @@ def test_qwen3_32b_layer_128k_full():
 
 def test_llama31_8b_layer_32k_full():
     decode_full(2)
+
+
+def test_qwen3_32b_layer_128k_int4_full():
+    # INT4 factor pages (Sec. 4.3), the bench's qwen3-32b-layer-128k-int4
+    decode_full(3, store="int4")
 
 
 def test_incremental_512_steps_full():
