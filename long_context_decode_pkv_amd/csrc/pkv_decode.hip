@@ -860,6 +860,29 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
   const int Hq = a.Hkv * a.G;
   const int64_t bh = (int64_t)b * a.Hkv + h;
 
+  const WorkList wl = work_list(a);
+  const int64_t W = (int64_t)a.n_split * kWaves;
+  const int64_t wi = (int64_t)split * kWaves + wave;
+  const int64_t e0 = unit_bound(wl, a, wi, W), e1 = unit_bound(wl, a, wi + 1, W);
+  // the factor slot of logical page n_s + f is f (pages are factorized in
+  // order and never revisited), so unit e >= D lives in slot e - D
+  const uint8_t* fac_bh = a.fac + bh * a.F_max * a.page_bytes;
+  auto kptr = [&](int64_t ee) { return fac_bh + (ee - wl.D) * a.page_bytes; };
+  auto vptr = [&](int64_t ee) { return fac_bh + (ee - wl.D) * a.page_bytes + a.k_part_bytes; };
+  const int64_t f0 = e0 > wl.D ? e0 : wl.D;  // first factorized unit of this wave
+
+  // ring formats: the first pages start streaming into LDS before the query
+  // is read, so the two memory latencies overlap
+  int64_t next = f0;  // next page to stage
+  int s_next = 0;
+  if constexpr (F::kLdsRing) {
+    uint8_t* ring = lds + wave * F::kRingSlots * F::kPageBytes;
+    for (; next < e1 && next < f0 + F::kRingSlots - 1; ++next) {
+      F::stage(ring + s_next * F::kPageBytes, kptr(next), lane);
+      s_next = s_next + 1 == F::kRingSlots ? 0 : s_next + 1;
+    }
+  }
+
   // query q * log2(e)/sqrt(d) of the lane's channels 32 ks + 8 q4 + e; as
   // an operand split into bf16 + remainder columns
   float qs[4][8];
@@ -884,11 +907,6 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) st.o[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const WorkList wl = work_list(a);
-  const int64_t W = (int64_t)a.n_split * kWaves;
-  const int64_t wi = (int64_t)split * kWaves + wave;
-  const int64_t e0 = unit_bound(wl, a, wi, W), e1 = unit_bound(wl, a, wi + 1, W);
-
   // dense pages of this range
   const int64_t d_end = e1 < wl.D ? e1 : wl.D;
   for (int64_t e = e0; e < d_end; ++e) {
@@ -912,16 +930,10 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
   // value half runs, and its value part while its key half runs; where the
   // register budget allows (kKeyDoubleBuffer), key parts are double-buffered
   // so that K(e + 2) streams in from the end of page e's key half
-  int64_t e = e0 > wl.D ? e0 : wl.D;
+  int64_t e = f0;
   if (e < e1) {
     typename F::Query fq;
     F::query(fq, qs, qb);
-    // the factor slot of logical page n_s + f is f (pages are factorized in
-    // order and never revisited), so unit e lives in slot e - D
-    const uint8_t* fac_bh = a.fac + bh * a.F_max * a.page_bytes;
-    const int64_t kpb = a.k_part_bytes;
-    auto kptr = [&](int64_t ee) { return fac_bh + (ee - wl.D) * a.page_bytes; };
-    auto vptr = [&](int64_t ee) { return fac_bh + (ee - wl.D) * a.page_bytes + kpb; };
     if constexpr (F::kLdsRing) {
       // ring slot s holds pages e with e = s (mod kRingSlots); pages up to
       // e + kRingSlots - 1 are staged while page e is computed.  Register
@@ -929,12 +941,7 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
       // part before its key half, page e + 1's K part before e's value half.
       constexpr int NS = F::kRingSlots;
       uint8_t* ring = lds + wave * NS * F::kPageBytes;
-      int64_t next = e;  // next page to stage
-      int s_next = 0, s_cur = 0;
-      for (; next < e1 && next < e + NS - 1; ++next) {
-        F::stage(ring + s_next * F::kPageBytes, kptr(next), lane);
-        s_next = s_next + 1 == NS ? 0 : s_next + 1;
-      }
+      int s_cur = 0;
       typename F::K kr;
       F::wait_staged((int)(next - 1 - e));
       F::load_keys(kr, ring, lane);
