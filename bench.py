@@ -41,8 +41,10 @@ CACHE_DIR = os.environ.get("PKV_BENCH_CACHE", "/tmp/pkv_bench_inputs")
 # reads 1048576 KiB for 2^30 bytes written -> x1.0).  A figure holds only for
 # the kernel sources whose hash it carries; any change to them makes it null.
 PMC_TRAFFIC = {
-    "qwen3-32b-layer-128k": {"sha256": "2e4df481febc0fb02cbc4ce9e455f7b24cce0fbd56943a01d305b0e71009f469",
-                             "fetch": 302990399, "write": 2228226},
+    "qwen3-32b-layer-128k": {"sha256": "a55478be83ea3beff15838ec8cfd0dc1c967bbc71892cf828dfc6f1795c7d948",
+                             "fetch": 302979740, "write": 1114112},
+    "qwen3-32b-layer-128k-int4": {"sha256": "a55478be83ea3beff15838ec8cfd0dc1c967bbc71892cf828dfc6f1795c7d948",
+                                  "fetch": 101460245, "write": 2228224},
 }
 TRAFFIC_SOURCES = ("long_context_decode_pkv_amd/csrc/pkv_decode.hip",
                    "long_context_decode_pkv_amd/csrc/pkv_internal.h")
