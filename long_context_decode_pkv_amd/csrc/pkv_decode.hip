@@ -493,6 +493,11 @@ struct Bf16Factors {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) Q.qb[ks] = qb[ks];
   }
+  // the dense pages' query operand
+  __device__ static void dense_query(bf16x8 (&qd)[4], const Query& Q, float) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qd[ks] = Q.qb[ks];
+  }
   __device__ static void load_keys(K& R, const uint8_t* kp, int lane) {
     pkv::load_keys<N8>(R, (const uint16_t*)kp, lane);
   }
@@ -687,6 +692,14 @@ struct Int4Factors {
       for (int e = 0; e < 8; ++e) Q.qf[ks][e] = 256.f * qs[ks][e];
     }
   }
+  // the dense pages' query operand (q log2(e)/sqrt(d) as bf16 + remainder)
+  __device__ static void dense_query(bf16x8 (&qd)[4], const Query& Q, float rem) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qd[ks][e] = split_bf16(Q.qf[ks][e] * (1.f / 256.f), rem);
+    }
+  }
 
   // Direct global -> LDS copy of one page pair (K part, then V part): load i
   // moves bytes 1024 i + 16 lane .. + 15 of the page to the same offset of
@@ -871,15 +884,26 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
   auto vptr = [&](int64_t ee) { return fac_bh + (ee - wl.D) * a.page_bytes + a.k_part_bytes; };
   const int64_t f0 = e0 > wl.D ? e0 : wl.D;  // first factorized unit of this wave
 
-  // ring formats: the first pages start streaming into LDS before the query
-  // is read, so the two memory latencies overlap
+  // the first factorized pages are requested before the query is read, so
+  // the two memory latencies overlap: staged into the LDS ring (ring
+  // formats) or loaded into the register images
   int64_t next = f0;  // next page to stage
   int s_next = 0;
+  typename F::K ka, kb;
+  typename F::V vr;
   if constexpr (F::kLdsRing) {
     uint8_t* ring = lds + wave * F::kRingSlots * F::kPageBytes;
     for (; next < e1 && next < f0 + F::kRingSlots - 1; ++next) {
       F::stage(ring + s_next * F::kPageBytes, kptr(next), lane);
       s_next = s_next + 1 == F::kRingSlots ? 0 : s_next + 1;
+    }
+  } else if constexpr (F::kKeyDoubleBuffer) {
+    // (single-buffered formats are the register-tight ranks: their first
+    // loads wait for the factorized section, which keeps them spill-free)
+    if (f0 < e1) {
+      F::load_keys(ka, kptr(f0), lane);
+      F::load_values(vr, vptr(f0), lane);
+      if (f0 + 1 < e1) F::load_keys(kb, kptr(f0 + 1), lane);
     }
   }
 
@@ -907,7 +931,75 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) st.o[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // dense pages of this range
+  // factorized pages: the next page's key part streams in while this page's
+  // value half runs, and its value part while its key half runs; where the
+  // register budget allows (kKeyDoubleBuffer), key parts are double-buffered
+  // so that K(e + 2) streams in from the end of page e's key half
+  int64_t e = f0;
+  typename F::Query fq;
+  F::query(fq, qs, qb);
+  if (e < e1) {
+    if constexpr (F::kLdsRing) {
+      // ring slot s holds pages e with e = s (mod kRingSlots); pages up to
+      // e + kRingSlots - 1 are staged while page e is computed.  Register
+      // images are read from the ring half a page ahead of use: page e's V
+      // part before its key half, page e + 1's K part before e's value half.
+      constexpr int NS = F::kRingSlots;
+      uint8_t* ring = lds + wave * NS * F::kPageBytes;
+      int s_cur = 0;
+      typename F::K& kr = ka;
+      F::wait_staged((int)(next - 1 - e));
+      F::load_keys(kr, ring, lane);
+      for (; e < e1; ++e) {
+        if (next < e1) {  // into the slot of page e - 1, read in full last iteration
+          F::stage(ring + s_next * F::kPageBytes, kptr(next), lane);
+          s_next = s_next + 1 == NS ? 0 : s_next + 1;
+          ++next;
+        }
+        const uint8_t* slot = ring + s_cur * F::kPageBytes;
+        s_cur = s_cur + 1 == NS ? 0 : s_cur + 1;
+        F::load_values(vr, slot + F::kKBytes, lane);
+        typename F::Probs pb;
+        F::keys(st, kr, fq, q4, rem, pb);
+        if (e + 1 < e1) {
+          F::wait_staged((int)(next - 2 - e));
+          F::load_keys(kr, ring + s_cur * F::kPageBytes, lane);
+        }
+        F::values(st, vr, pb, q4, rem);
+      }
+    } else if constexpr (F::kKeyDoubleBuffer) {
+      auto step = [&](typename F::K& kc) {
+        typename F::Probs pb;
+        F::keys(st, kc, fq, q4, rem, pb);
+        if (e + 2 < e1) F::load_keys(kc, kptr(e + 2), lane);
+        F::values(st, vr, pb, q4, rem);
+        if (e + 1 < e1) F::load_values(vr, vptr(e + 1), lane);
+      };
+      while (true) {
+        step(ka);
+        if (++e >= e1) break;
+        step(kb);
+        if (++e >= e1) break;
+      }
+    } else {
+      typename F::K& kr = ka;
+      F::load_keys(kr, kptr(e), lane);
+      F::load_values(vr, vptr(e), lane);
+      for (; e < e1; ++e) {
+        typename F::Probs pb;
+        F::keys(st, kr, fq, q4, rem, pb);
+        const bool more = e + 1 < e1;
+        if (more) F::load_keys(kr, kptr(e + 1), lane);
+        F::values(st, vr, pb, q4, rem);
+        if (more) F::load_values(vr, vptr(e + 1), lane);
+      }
+    }
+  }
+
+  // dense pages of this range (after the factorized ones: the query operand
+  // of the dense contraction is rebuilt here rather than kept live)
+  bf16x8 qd[4];
+  F::dense_query(qd, fq, rem);
   const int64_t d_end = e1 < wl.D ? e1 : wl.D;
   for (int64_t e = e0; e < d_end; ++e) {
     const int64_t p = unit_page(wl, a, e);
@@ -923,80 +1015,9 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
       Vt = (const uint16_t*)a.win_v + (bh * (a.n_w + 1) + slot) * ppg;
     }
     const int64_t left = a.T - p * kP;
-    dense_page(st, Kp, Vt, (int)(left < kP ? left : kP), qb, lane, rem);
+    dense_page(st, Kp, Vt, (int)(left < kP ? left : kP), qd, lane, rem);
   }
 
-  // factorized pages: the next page's key part streams in while this page's
-  // value half runs, and its value part while its key half runs; where the
-  // register budget allows (kKeyDoubleBuffer), key parts are double-buffered
-  // so that K(e + 2) streams in from the end of page e's key half
-  int64_t e = f0;
-  if (e < e1) {
-    typename F::Query fq;
-    F::query(fq, qs, qb);
-    if constexpr (F::kLdsRing) {
-      // ring slot s holds pages e with e = s (mod kRingSlots); pages up to
-      // e + kRingSlots - 1 are staged while page e is computed.  Register
-      // images are read from the ring half a page ahead of use: page e's V
-      // part before its key half, page e + 1's K part before e's value half.
-      constexpr int NS = F::kRingSlots;
-      uint8_t* ring = lds + wave * NS * F::kPageBytes;
-      int s_cur = 0;
-      typename F::K kr;
-      F::wait_staged((int)(next - 1 - e));
-      F::load_keys(kr, ring, lane);
-      for (; e < e1; ++e) {
-        if (next < e1) {  // into the slot of page e - 1, read in full last iteration
-          F::stage(ring + s_next * F::kPageBytes, kptr(next), lane);
-          s_next = s_next + 1 == NS ? 0 : s_next + 1;
-          ++next;
-        }
-        const uint8_t* slot = ring + s_cur * F::kPageBytes;
-        s_cur = s_cur + 1 == NS ? 0 : s_cur + 1;
-        typename F::V vr;
-        F::load_values(vr, slot + F::kKBytes, lane);
-        typename F::Probs pb;
-        F::keys(st, kr, fq, q4, rem, pb);
-        if (e + 1 < e1) {
-          F::wait_staged((int)(next - 2 - e));
-          F::load_keys(kr, ring + s_cur * F::kPageBytes, lane);
-        }
-        F::values(st, vr, pb, q4, rem);
-      }
-    } else if constexpr (F::kKeyDoubleBuffer) {
-      typename F::V vr;
-      typename F::K ka, kb;
-      F::load_keys(ka, kptr(e), lane);
-      F::load_values(vr, vptr(e), lane);
-      if (e + 1 < e1) F::load_keys(kb, kptr(e + 1), lane);
-      auto step = [&](typename F::K& kc) {
-        typename F::Probs pb;
-        F::keys(st, kc, fq, q4, rem, pb);
-        if (e + 2 < e1) F::load_keys(kc, kptr(e + 2), lane);
-        F::values(st, vr, pb, q4, rem);
-        if (e + 1 < e1) F::load_values(vr, vptr(e + 1), lane);
-      };
-      while (true) {
-        step(ka);
-        if (++e >= e1) break;
-        step(kb);
-        if (++e >= e1) break;
-      }
-    } else {
-      typename F::V vr;
-      typename F::K kr;
-      F::load_keys(kr, kptr(e), lane);
-      F::load_values(vr, vptr(e), lane);
-      for (; e < e1; ++e) {
-        typename F::Probs pb;
-        F::keys(st, kr, fq, q4, rem, pb);
-        const bool more = e + 1 < e1;
-        if (more) F::load_keys(kr, kptr(e + 1), lane);
-        F::values(st, vr, pb, q4, rem);
-        if (more) F::load_values(vr, vptr(e + 1), lane);
-      }
-    }
-  }
 
   // combine the hi/lo column halves of o, then merge the waves in LDS
 #pragma unroll
