@@ -227,6 +227,32 @@ int32_t pkv_compress_pages(const void* X, int64_t n_pages, int32_t P, int32_t d,
 int32_t pkv_prefill(pkv_cache* cache, const void* K, const void* V, int64_t T, void* stream);
 
 /*
+ * Chunked prefill (Sec. 3.3 (1)-(3) and (5) applied to C tokens at once):
+ * K, V (device, [B][H_kv][C][d], cache element type) are the next C tokens
+ * of every sequence.  The cache grows from T to T + C and ends in the steady
+ * state: every page that leaves the recent window within the chunk is
+ * factorized (from its ring slot, or straight from the chunk for pages that
+ * never enter the window), the remaining rows go to the dense pools, and the
+ * page table is refilled.  The factor pool, the page table and every valid
+ * dense row end as after C calls of pkv_append and pkv_promote_page (rows of
+ * a dense slot beyond its page's valid length are unspecified).  C = 0 does
+ * nothing.  All pages the call factorizes on a stream go to one launch.
+ * With an auxiliary stream set (pkv_cache_set_aux_stream), one launch there,
+ * ordered after the work already on `stream`, decomposes the pages
+ * factorized straight from the chunk and also the window's complete pages
+ * (early factorization, as pkv_append does for one page): the call returns
+ * with that work overlapping whatever the caller queues next.  The next
+ * attention call (pkv_decode_attn, pkv_decode_partial, pkv_decode_step) or
+ * pkv_prefill on a stream orders itself after the chunk's pages; a
+ * promotion or a later chunk waits for the early pages it needs.  K and V must stay unchanged until the
+ * auxiliary stream has passed the call's work.
+ * Errors: INVALID_ARG (C < 0, null or misaligned K / V), CAPACITY
+ * (T + C > max_tokens), PROMOTION_PENDING (a completed page waits for
+ * pkv_promote_page).
+ */
+int32_t pkv_prefill_chunk(pkv_cache* cache, const void* K, const void* V, int64_t C, void* stream);
+
+/*
  * Append one token (Sec. 3.3 "Incremental Cache Update (5)"): k_new, v_new
  * (device, [B][H_kv][d], cache dtype) go to row T mod P of page T / P, which
  * joins attention at once; T += 1.  If this append completes a page and the

@@ -80,6 +80,7 @@ def lib():
         "pkv_cache_state": ([vp, P(i64), P(i64), P(i32)], i32),
         "pkv_compress_pages": ([vp, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp], i32),
         "pkv_prefill": ([vp, vp, vp, i64, vp], i32),
+        "pkv_prefill_chunk": ([vp, vp, vp, i64, vp], i32),
         "pkv_append": ([vp, vp, vp, P(i32), vp], i32),
         "pkv_promote_page": ([vp, vp], i32),
         "pkv_decode_workspace_bytes": ([vp, i32, P(u64)], i32),
@@ -296,6 +297,7 @@ class Cache:
                                       self.layout["total_bytes"], ctypes.byref(h)), "pkv_cache_create")
         self._h = h
         self._ws = None
+        self._aux = None
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -321,6 +323,18 @@ class Cache:
         kp = _dev_ptr(K, self.elem_code, "K") if T else None
         vp = _dev_ptr(V, self.elem_code, "V") if T else None
         _check(lib().pkv_prefill(self._h, kp, vp, T, _stream(self.device)), "pkv_prefill")
+
+    def prefill_chunk(self, K, V):
+        """Extend the cache by the chunk K, V [B][H_kv][C][d] (chunked prefill)."""
+        if tuple(K.shape) != tuple(V.shape) or tuple(K.shape[:2]) != (self.shape.batch, self.shape.n_kv_heads):
+            raise ValueError("K, V must both be [B][H_kv][C][d]")
+        _check(lib().pkv_prefill_chunk(self._h, _dev_ptr(K, self.elem_code, "K"), _dev_ptr(V, self.elem_code, "V"),
+                                       K.shape[2], _stream(self.device)), "pkv_prefill_chunk")
+        if self._aux is not None and K.shape[2] > 0:
+            # the aux stream may still read the chunk: torch's allocator must
+            # not hand its memory out again before that work has passed
+            K.record_stream(self._aux)
+            V.record_stream(self._aux)
 
     def append(self, k, v) -> bool:
         pend = ctypes.c_int32()

@@ -6,6 +6,7 @@
 // point allocates device memory; none throws.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -34,6 +35,10 @@ struct pkv_cache {
   hipEvent_t ready[kMaxRing] = {};
   int n_ready = 0;
   int64_t early_lo = 0, early_hi = 0;
+  // pkv_prefill_chunk with an aux stream: the chunk's page decompositions run
+  // there; the next call that reads the factor pool waits for chunk_ready
+  hipEvent_t chunk_ready = nullptr;
+  mutable bool chunk_pending = false;
 };
 
 namespace {
@@ -148,38 +153,70 @@ float bf16_round_host(float x, uint16_t* bits) {
   return f;
 }
 
-// Factorize the page that leaves the recent window (logical page n_s + n_fact,
-// in ring slot (p - n_s) mod (n_w + 1)) into factor slot n_fact, flip its
-// table entry to FACT and count it (Sec. 3.3 (5)).
-// Factorize window page p (in ring slot (p - n_s) mod (n_w + 1)) into factor
-// slot p - n_s, on `stream`.
-hipError_t factorize_page(pkv_cache* c, int64_t p, hipStream_t s) {
+// Pages [p_lo, ...) of the recent-window ring (page p in ring slot
+// (p - n_s) mod (n_w + 1), value pages stored transposed), factorized into
+// factor slots p - n_s.
+CompressSrc ring_src(const pkv_cache* c, int64_t p_lo) {
   const CacheGeom g = geom_of(c);
-  const int64_t f = p - g.n_s;
-  const int64_t ring = f % (g.n_w + 1);
-  const int64_t esz = c->lay.elem_bytes;
   const int64_t ppg = (int64_t)kP * kD;
+  CompressSrc src;
+  std::memset(&src, 0, sizeof(src));
+  src.base[0] = c->base + c->lay.win_k;
+  src.base[1] = c->base + c->lay.win_v;
+  src.trans[0] = 0;
+  src.trans[1] = 1;
+  src.bh_stride = (int64_t)(g.n_w + 1) * ppg;
+  src.f_stride = ppg;
+  src.in_f0 = p_lo - g.n_s;
+  src.f_mod = g.n_w + 1;
+  src.out_f0 = p_lo - g.n_s;
+  return src;
+}
+
+// Whole pages of caller-owned K, V [B][H_kv][T][d] from row `row0` on, the
+// k-th factorized into factor slot out_f0 + k.
+CompressSrc dense_src(const pkv_cache* c, const void* K, const void* V, int64_t T, int64_t row0,
+                      int64_t out_f0) {
+  const int64_t esz = c->lay.elem_bytes;
+  CompressSrc src;
+  std::memset(&src, 0, sizeof(src));
+  src.base[0] = (const uint8_t*)K + row0 * kD * esz;
+  src.base[1] = (const uint8_t*)V + row0 * kD * esz;
+  src.bh_stride = T * kD;
+  src.f_stride = (int64_t)kP * kD;
+  src.out_f0 = out_f0;
+  return src;
+}
+
+// Decomposition of n0 pages of `a` then n1 pages of `b` into the factor pool,
+// one launch on `s` (nothing when n0 + n1 == 0).
+hipError_t factorize(const pkv_cache* c, const CompressSrc& a, int64_t n0, const CompressSrc& b,
+                     int64_t n1, hipStream_t s) {
+  if (n0 < 0 || n1 < 0) return hipErrorInvalidValue;
+  if (n0 + n1 == 0) return hipSuccess;
+  const CacheGeom g = geom_of(c);
   CompressJob job;
   std::memset(&job, 0, sizeof(job));
   job.n_kind = 2;
-  job.n_f = 1;
-  job.n_pages = (int64_t)g.B * g.Hkv * 2;
-  job.in_base[0] = c->base + c->lay.win_k + ring * ppg * esz;
-  job.in_base[1] = c->base + c->lay.win_v + ring * ppg * esz;
-  job.in_trans[0] = 0;
-  job.in_trans[1] = 1;  // value pages are stored transposed
-  job.in_bh_stride = (int64_t)(g.n_w + 1) * ppg;
-  job.in_f_stride = 0;
+  job.n_f = n0 + n1;
+  job.n_f_src0 = n0;
+  job.n_pages = (int64_t)g.B * g.Hkv * job.n_f * 2;
+  job.src[0] = a;
+  job.src[1] = b;
   job.in_dtype = dense_dtype(g.dtype);
   job.rank[0] = g.r_k;
   job.rank[1] = g.r_v;
   job.out_dtype = g.dtype;
   job.fac = c->base + c->lay.factors;
   job.fac_bh_pages = g.F_max;
-  job.f0 = f;
   job.page_bytes = c->lay.factor_page_bytes;
   job.k_part_bytes = c->lay.factor_k_bytes;
   return launch_compress(job, s);
+}
+
+// Factorize window pages [p_lo, p_hi) from their ring slots on `s`.
+hipError_t factorize_ring(const pkv_cache* c, int64_t p_lo, int64_t p_hi, hipStream_t s) {
+  return factorize(c, ring_src(c, p_lo), p_hi - p_lo, ring_src(c, p_lo), 0, s);
 }
 
 // The page leaving the window (n_s + n_fact) becomes FACT: factorized now, or
@@ -195,7 +232,7 @@ int32_t promote_now(pkv_cache* c, void* stream) {
     e = hipStreamWaitEvent(s, c->ready[f % (g.n_w + 1)], 0);
     c->early_lo = p_old + 1;
   } else {
-    e = factorize_page(c, p_old, s);
+    e = factorize_ring(c, p_old, p_old + 1, s);
   }
   if (e == hipSuccess) e = launch_table_set(g, p_old, table_entry(PKV_PAGE_FACT, (int)f), s);
   if (e != hipSuccess) return PKV_ERR_DEVICE;
@@ -210,7 +247,7 @@ int32_t factorize_early(pkv_cache* c, int64_t p, hipStream_t main) {
   if (p - g.n_s >= g.F_max) return PKV_OK;  // never leaves the window within capacity
   hipError_t e = hipEventRecord(c->written, main);
   if (e == hipSuccess) e = hipStreamWaitEvent(c->aux, c->written, 0);
-  if (e == hipSuccess) e = factorize_page(c, p, c->aux);
+  if (e == hipSuccess) e = factorize_ring(c, p, p + 1, c->aux);
   if (e == hipSuccess) e = hipEventRecord(c->ready[(p - g.n_s) % (g.n_w + 1)], c->aux);
   if (e != hipSuccess) return PKV_ERR_DEVICE;
   if (c->early_lo == c->early_hi) c->early_lo = p;
@@ -220,11 +257,34 @@ int32_t factorize_early(pkv_cache* c, int64_t p, hipStream_t main) {
 
 void release_aux(pkv_cache* c) {
   if (c->written) (void)hipEventDestroy(c->written);
+  if (c->chunk_ready) (void)hipEventDestroy(c->chunk_ready);
   for (int i = 0; i < c->n_ready; ++i) (void)hipEventDestroy(c->ready[i]);
   c->written = nullptr;
+  c->chunk_ready = nullptr;
+  c->chunk_pending = false;
   c->n_ready = 0;
   c->aux = nullptr;
   c->early_lo = c->early_hi = 0;
+}
+
+// Order `s` after the chunk decompositions still running on the aux stream
+// (the factor slots they write are read by the caller's next work).
+hipError_t wait_chunk(const pkv_cache* c, hipStream_t s) {
+  if (!c->chunk_pending) return hipSuccess;
+  const hipError_t e = hipStreamWaitEvent(s, c->chunk_ready, 0);
+  if (e == hipSuccess) c->chunk_pending = false;
+  return e;
+}
+
+// Order `s` after every early factorization still in flight (they read ring
+// slots and write factor slots that a prefill or chunk overwrites).
+hipError_t wait_early(const pkv_cache* c, hipStream_t s) {
+  if (!c->aux || c->early_lo >= c->early_hi) return hipSuccess;
+  for (int i = 0; i < c->n_ready; ++i) {
+    const hipError_t e = hipStreamWaitEvent(s, c->ready[i], 0);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 
@@ -504,13 +564,17 @@ int32_t pkv_cache_set_aux_stream(pkv_cache* c, void* aux_stream) {
   if (!c) return PKV_ERR_INVALID_ARG;
   if (c->aux) {
     // work already queued there must finish before its events go away
-    if (c->early_lo < c->early_hi) return PKV_ERR_PROMOTION_PENDING;
+    if (c->early_lo < c->early_hi || c->chunk_pending) return PKV_ERR_PROMOTION_PENDING;
     release_aux(c);
   }
   if (!aux_stream) return PKV_OK;
   const int ring = c->lay.n_ring_slots;
   if (ring > kMaxRing) return PKV_ERR_UNSUPPORTED;
   if (hipEventCreateWithFlags(&c->written, hipEventDisableTiming) != hipSuccess) return PKV_ERR_DEVICE;
+  if (hipEventCreateWithFlags(&c->chunk_ready, hipEventDisableTiming) != hipSuccess) {
+    release_aux(c);
+    return PKV_ERR_DEVICE;
+  }
   for (int i = 0; i < ring; ++i) {
     if (hipEventCreateWithFlags(&c->ready[i], hipEventDisableTiming) != hipSuccess) {
       release_aux(c);
@@ -547,10 +611,9 @@ int32_t pkv_compress_pages(const void* X, int64_t n_pages, int32_t P, int32_t d,
   job.n_pages = n_pages;
   job.n_kind = 1;
   job.n_f = n_pages;
-  job.in_base[0] = job.in_base[1] = X;
-  job.in_trans[0] = job.in_trans[1] = 0;
-  job.in_bh_stride = 0;
-  job.in_f_stride = (int64_t)kP * kD;
+  job.n_f_src0 = n_pages;
+  job.src[0].base[0] = job.src[0].base[1] = X;
+  job.src[0].f_stride = (int64_t)kP * kD;
   job.in_dtype = in_dtype;
   job.rank[0] = job.rank[1] = r;
   job.out_dtype = out_dtype;
@@ -568,35 +631,13 @@ int32_t pkv_prefill(pkv_cache* c, const void* K, const void* V, int64_t T, void*
   const CacheGeom g = geom_of(c);
   const int64_t n_fact = steady_fact(T, kP, g.n_s, g.n_w);
   hipStream_t s = (hipStream_t)stream;
-  if (c->aux && c->early_lo < c->early_hi) {
-    // early factorizations still in flight read the ring slots and write the
-    // factor slots this prefill overwrites
-    for (int i = 0; i < c->n_ready; ++i)
-      if (hipStreamWaitEvent(s, c->ready[i], 0) != hipSuccess) return PKV_ERR_DEVICE;
-  }
+  // early factorizations and chunk decompositions still in flight read the
+  // ring slots and write the factor slots this prefill overwrites
+  if (wait_early(c, s) != hipSuccess || wait_chunk(c, s) != hipSuccess) return PKV_ERR_DEVICE;
   hipError_t e = launch_prefill_dense(g, K, V, T, n_fact, s);
-  if (e == hipSuccess && n_fact > 0) {
-    CompressJob job;
-    std::memset(&job, 0, sizeof(job));
-    job.n_kind = 2;
-    job.n_f = n_fact;
-    job.n_pages = (int64_t)g.B * g.Hkv * n_fact * 2;
-    const int64_t esz = c->lay.elem_bytes;
-    job.in_base[0] = (const uint8_t*)K + (int64_t)g.n_s * kP * kD * esz;
-    job.in_base[1] = (const uint8_t*)V + (int64_t)g.n_s * kP * kD * esz;
-    job.in_trans[0] = job.in_trans[1] = 0;
-    job.in_bh_stride = T * kD;
-    job.in_f_stride = (int64_t)kP * kD;
-    job.in_dtype = dense_dtype(g.dtype);
-    job.rank[0] = g.r_k;
-    job.rank[1] = g.r_v;
-    job.out_dtype = g.dtype;
-    job.fac = c->base + c->lay.factors;
-    job.fac_bh_pages = g.F_max;
-    job.f0 = 0;
-    job.page_bytes = c->lay.factor_page_bytes;
-    job.k_part_bytes = c->lay.factor_k_bytes;
-    e = launch_compress(job, s);
+  if (e == hipSuccess) {
+    const CompressSrc src = dense_src(c, K, V, T, (int64_t)g.n_s * kP, 0);
+    e = factorize(c, src, n_fact, src, 0, s);
   }
   if (e == hipSuccess) e = launch_table_fill(g, T, n_fact, s);
   if (e != hipSuccess) return PKV_ERR_DEVICE;
@@ -604,6 +645,84 @@ int32_t pkv_prefill(pkv_cache* c, const void* K, const void* V, int64_t T, void*
   c->n_fact = n_fact;
   c->pending = 0;
   c->early_lo = c->early_hi = 0;
+  return PKV_OK;
+}
+
+int32_t pkv_prefill_chunk(pkv_cache* c, const void* K, const void* V, int64_t C, void* stream) {
+  if (!c || C < 0) return PKV_ERR_INVALID_ARG;
+  if (C == 0) return PKV_OK;
+  if (!K || !V || !aligned(K, 16) || !aligned(V, 16)) return PKV_ERR_INVALID_ARG;
+  if (c->pending) return PKV_ERR_PROMOTION_PENDING;
+  const int64_t T0 = c->T, T1 = T0 + C;
+  if (T1 > c->shape.max_tokens) return PKV_ERR_CAPACITY;
+  const CacheGeom g = geom_of(c);
+  const int64_t nf0 = c->n_fact, nf1 = steady_fact(T1, kP, g.n_s, g.n_w);
+  if (nf1 > g.F_max) return PKV_ERR_CAPACITY;
+  hipStream_t s = (hipStream_t)stream;
+  // early factorizations read ring slots that this chunk may overwrite
+  hipError_t e = wait_early(c, s);
+  const int64_t p0 = T0 / kP;              // page of token T0
+  const int64_t pc = (T0 + kP - 1) / kP;   // first page that starts inside the chunk
+  const int64_t np1 = (T1 + kP - 1) / kP;  // pages at T1
+  const int64_t leave_lo = g.n_s + nf0, fact_hi = g.n_s + nf1;  // pages that leave the window
+  // ... of them, those in the ring at T0 (none when T0 is inside the sink)
+  const int64_t ring_hi = std::max(leave_lo, std::min(fact_hi, pc));
+  const int64_t chunk_lo = std::max(leave_lo, pc);               // ... and those never in it
+  const int64_t n_chunk = fact_hi > chunk_lo ? fact_hi - chunk_lo : 0;
+  const CompressSrc chunk = dense_src(c, K, V, C, chunk_lo * kP - T0, chunk_lo - g.n_s);
+  // ring pages already factorized on the aux stream (their factor slots are
+  // written; the wait above ordered this stream after that work)
+  auto clamp = [](int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); };
+  const bool early = c->early_lo < c->early_hi;
+  const int64_t a_hi = early ? clamp(c->early_lo, leave_lo, ring_hi) : ring_hi;
+  const int64_t b_lo = early ? clamp(c->early_hi, leave_lo, ring_hi) : ring_hi;
+  // 1. the page filling at T0, when it leaves the window in this chunk: its
+  //    rows from the chunk first, in its ring slot
+  if (e == hipSuccess && T0 % kP != 0 && p0 >= g.n_s && p0 < fact_hi)
+    e = launch_chunk_dense(g, K, V, T0, T1, p0, p0 + 1, s);
+  // 2. decomposition of the pages leaving the window, as one launch: ring
+  //    pages [leave_lo, a_hi) and [b_lo, ring_hi), and -- without an aux
+  //    stream -- the chunk's own pages [chunk_lo, fact_hi)
+  if (e == hipSuccess) {
+    if (c->aux)
+      e = factorize(c, ring_src(c, leave_lo), a_hi - leave_lo, ring_src(c, b_lo), ring_hi - b_lo, s);
+    else
+      e = factorize(c, ring_src(c, leave_lo), a_hi - leave_lo, chunk, n_chunk, s);
+  }
+  // 3. rows of the pages that stay dense: sink pages, then the window and
+  //    the partial page (after step 2, which read the ring slots they reuse)
+  if (e == hipSuccess) e = launch_chunk_dense(g, K, V, T0, T1, p0, np1 < g.n_s ? np1 : g.n_s, s);
+  if (e == hipSuccess) e = launch_chunk_dense(g, K, V, T0, T1, p0 > fact_hi ? p0 : fact_hi, np1, s);
+  if (e == hipSuccess) e = launch_table_fill(g, T1, nf1, s);
+  // 4. with an aux stream, one launch there after the copies: the chunk's own
+  //    pages, and the window's complete pages not yet factorized (early
+  //    factorization: they leave the window later, and only wait for it)
+  int64_t x_lo = fact_hi, x_hi = fact_hi;
+  if (e == hipSuccess && c->aux) {
+    x_lo = early && c->early_hi > fact_hi ? c->early_hi : fact_hi;
+    x_hi = T1 / kP < g.n_s + g.F_max ? T1 / kP : g.n_s + g.F_max;
+    if (g.n_w == 0 || x_hi < x_lo) x_hi = x_lo;
+    if (x_hi > x_lo || n_chunk > 0) {
+      e = hipEventRecord(c->written, s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(c->aux, c->written, 0);
+      if (e == hipSuccess) e = factorize(c, ring_src(c, x_lo), x_hi - x_lo, chunk, n_chunk, c->aux);
+      for (int64_t p = x_lo; e == hipSuccess && p < x_hi; ++p)
+        e = hipEventRecord(c->ready[(p - g.n_s) % (g.n_w + 1)], c->aux);
+      if (e == hipSuccess && n_chunk > 0) {
+        e = hipEventRecord(c->chunk_ready, c->aux);
+        if (e == hipSuccess) c->chunk_pending = true;
+      }
+    }
+  }
+  if (e != hipSuccess) return PKV_ERR_DEVICE;
+  // early pages still in the window: the older ones that stay, then the new
+  const int64_t keep_lo = early && c->early_hi > fact_hi ? (c->early_lo > fact_hi ? c->early_lo : fact_hi)
+                                                        : x_lo;
+  c->early_lo = keep_lo;
+  c->early_hi = x_hi > keep_lo ? x_hi : keep_lo;
+  if (c->early_lo >= c->early_hi) c->early_lo = c->early_hi = 0;
+  c->T = T1;
+  c->n_fact = nf1;
   return PKV_OK;
 }
 
@@ -678,6 +797,7 @@ int32_t pkv_decode_partial(const pkv_cache* c, const void* q, void* workspace,
   AttnJob job;
   int32_t st = decode_job(c, q, workspace, workspace_bytes, n_split, &job);
   if (st != PKV_OK) return st;
+  if (wait_chunk(c, (hipStream_t)stream) != hipSuccess) return PKV_ERR_DEVICE;
   return dev_status(launch_partial(geom_of(c), job, (hipStream_t)stream));
 }
 
@@ -699,7 +819,8 @@ int32_t pkv_decode_attn(const pkv_cache* c, const void* q, float* out, void* wor
   if (st != PKV_OK) return st;
   job.out = out;
   const CacheGeom g = geom_of(c);
-  hipError_t e = launch_partial(g, job, (hipStream_t)stream);
+  hipError_t e = wait_chunk(c, (hipStream_t)stream);
+  if (e == hipSuccess) e = launch_partial(g, job, (hipStream_t)stream);
   if (e == hipSuccess) e = launch_merge(g, job, (hipStream_t)stream);
   return dev_status(e);
 }
@@ -719,6 +840,7 @@ int32_t pkv_decode_step(pkv_cache* c, const void* k_new, const void* v_new, cons
   const int64_t p_old = g.n_s + c->n_fact;  // page leaving the window when promote
   if (promote && c->n_fact >= g.F_max) return PKV_ERR_CAPACITY;
   hipStream_t s = (hipStream_t)stream;
+  if (wait_chunk(c, s) != hipSuccess) return PKV_ERR_DEVICE;
   if (promote && p_old == p) {
     // no window (w = 0): the page the token completes is factorized at once,
     // so the token must be in place first; separate launches

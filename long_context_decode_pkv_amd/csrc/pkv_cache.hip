@@ -61,6 +61,47 @@ __global__ __launch_bounds__(256) void prefill_dense_kernel(CacheGeom g, const E
   }
 }
 
+// Chunked prefill: rows of pages [p_lo, p_hi) that fall in the chunk's token
+// range [T0, T1) are copied from the chunk (K, V [B][H_kv][C][d], C = T1 - T0)
+// into the pages' dense slots (sink slot p, or ring slot (p - n_s) mod
+// (n_w + 1)); other rows of the slots are left as they are.  One workgroup per
+// (page, KV head, sequence).
+template <typename Elem>
+__global__ __launch_bounds__(256) void chunk_dense_kernel(CacheGeom g, const Elem* K, const Elem* V,
+                                                          int64_t T0, int64_t T1, int64_t p_lo) {
+  __shared__ Elem tile[kP][kD + 2];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t p = p_lo + blockIdx.x;
+  const int64_t bh = (int64_t)b * g.Hkv + h;
+  const int64_t C = T1 - T0;
+  const int64_t t0 = p * kP > T0 ? p * kP : T0;
+  const int64_t t1 = p * kP + kP < T1 ? p * kP + kP : T1;
+  if (t1 <= t0) return;
+  const int r0 = (int)(t0 - p * kP), nr = (int)(t1 - t0);
+  const int64_t ppg = (int64_t)kP * kD;
+  Elem *dk, *dv;
+  if (p < g.n_s) {
+    dk = (Elem*)(g.base + g.lay.sink_k) + (bh * g.n_s + p) * ppg;
+    dv = (Elem*)(g.base + g.lay.sink_v) + (bh * g.n_s + p) * ppg;
+  } else {
+    const int64_t slot = (p - g.n_s) % (g.n_w + 1);
+    dk = (Elem*)(g.base + g.lay.win_k) + (bh * (g.n_w + 1) + slot) * ppg;
+    dv = (Elem*)(g.base + g.lay.win_v) + (bh * (g.n_w + 1) + slot) * ppg;
+  }
+  const Elem* sk = K + (bh * C + (t0 - T0)) * kD;
+  const Elem* sv = V + (bh * C + (t0 - T0)) * kD;
+  for (int idx = threadIdx.x; idx < nr * kD; idx += 256) {
+    const int j = idx / kD, c = idx % kD;
+    dk[(r0 + j) * kD + c] = sk[idx];
+    tile[j][c] = sv[idx];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nr * kD; idx += 256) {
+    const int c = idx / nr, j = idx % nr;
+    dv[c * kP + r0 + j] = tile[j][c];
+  }
+}
+
 __device__ inline int32_t classify_entry(int64_t p, int64_t T, int n_s, int n_w, int64_t n_fact) {
   const int64_t n_full = T / kP, n_pages = (T + kP - 1) / kP;
   if (p >= n_pages) return table_entry(PKV_PAGE_UNUSED, 0);
@@ -119,6 +160,19 @@ hipError_t launch_prefill_dense(const CacheGeom& g, const void* K, const void* V
   else
     hipLaunchKernelGGL(prefill_dense_kernel<float>, grid, dim3(256), 0, stream, g, (const float*)K,
                        (const float*)V, T, n_fact);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_dense(const CacheGeom& g, const void* K, const void* V, int64_t T0, int64_t T1,
+                              int64_t p_lo, int64_t p_hi, hipStream_t stream) {
+  if (p_hi <= p_lo) return hipSuccess;
+  const dim3 grid((unsigned)(p_hi - p_lo), g.Hkv, g.B);
+  if (dense_dtype(g.dtype) == PKV_BF16)
+    hipLaunchKernelGGL(chunk_dense_kernel<uint16_t>, grid, dim3(256), 0, stream, g, (const uint16_t*)K,
+                       (const uint16_t*)V, T0, T1, p_lo);
+  else
+    hipLaunchKernelGGL(chunk_dense_kernel<float>, grid, dim3(256), 0, stream, g, (const float*)K,
+                       (const float*)V, T0, T1, p_lo);
   return hipGetLastError();
 }
 

@@ -225,12 +225,11 @@ template <typename Elem, int WPP>
 __device__ void compress_one(const CompressJob& job, int64_t n, CompressShared& sh, int lane,
                              int wv) {
   const int tid = wv * 64 + lane;
-  const int kind = (int)(n % job.n_kind);
-  const int64_t f = (n / job.n_kind) % job.n_f;
-  const int64_t bh = n / ((int64_t)job.n_kind * job.n_f);
-  const Elem* X = (const Elem*)job.in_base[kind] + bh * job.in_bh_stride + f * job.in_f_stride;
-  const int trans = job.in_trans[kind];
-  const int r = job.rank[kind];
+  const PageRef pr = page_ref(job, n, (int)sizeof(Elem));
+  const int kind = pr.kind;
+  const Elem* X = (const Elem*)pr.X;
+  const int trans = pr.trans;
+  const int r = pr.r;
 
   // 1. Gram matrix, eigenvector accumulator = I
   gram<Elem, WPP>(X, trans, sh.G, lane, wv);
@@ -319,9 +318,7 @@ __device__ void compress_one(const CompressJob& job, int64_t n, CompressShared& 
   const PackDims pd = pack_dims(r);
   const int r_store = packed ? 8 * pd.n8 : r;
   uint8_t* part = nullptr;
-  if (packed)
-    part = job.fac + ((bh * job.fac_bh_pages) + job.f0 + f) * job.page_bytes +
-           (int64_t)kind * job.k_part_bytes;
+  if (packed) part = factor_part(job, pr);
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     if (16 * mi < r_store) {

@@ -72,7 +72,8 @@ __device__ inline floatx4 gram_tile(const Elem* X, int trans, int ta, int tb, in
 // Where page n of a job comes from and goes to.
 struct PageRef {
   int kind;
-  int64_t f, bh;
+  int64_t bh;
+  int64_t slot;  // factor slot (cache jobs)
   int trans, r;
   const void* X;
 };
@@ -80,13 +81,23 @@ struct PageRef {
 __device__ inline PageRef page_ref(const CompressJob& job, int64_t n, int elem_bytes) {
   PageRef p;
   p.kind = (int)(n % job.n_kind);
-  p.f = (n / job.n_kind) % job.n_f;
+  const int64_t fj = (n / job.n_kind) % job.n_f;
   p.bh = n / ((int64_t)job.n_kind * job.n_f);
-  p.trans = job.in_trans[p.kind];
+  const bool second = fj >= job.n_f_src0;
+  const CompressSrc& src = second ? job.src[1] : job.src[0];
+  const int64_t f = second ? fj - job.n_f_src0 : fj;
+  int64_t in = src.in_f0 + f;
+  if (src.f_mod > 0) in %= src.f_mod;
+  p.slot = src.out_f0 + f;
+  p.trans = src.trans[p.kind];
   p.r = job.rank[p.kind];
-  p.X = (const uint8_t*)job.in_base[p.kind] +
-        (p.bh * job.in_bh_stride + p.f * job.in_f_stride) * elem_bytes;
+  p.X = (const uint8_t*)src.base[p.kind] + (p.bh * src.bh_stride + in * src.f_stride) * elem_bytes;
   return p;
+}
+
+// Packed factor part of a cache job's page.
+__device__ inline uint8_t* factor_part(const CompressJob& job, const PageRef& p) {
+  return job.fac + (p.bh * job.fac_bh_pages + p.slot) * job.page_bytes + (int64_t)p.kind * job.k_part_bytes;
 }
 
 // Destination of factor element Rf[i][c] (i < r_store) and Lf[j][i].
@@ -105,9 +116,7 @@ struct FactorDst {
     kind = p.kind;
     n = n_;
     if (packed) {
-      uint8_t* part = job.fac + ((p.bh * job.fac_bh_pages) + job.f0 + p.f) * job.page_bytes +
-                      (int64_t)p.kind * job.k_part_bytes;
-      rf = lf = part;
+      rf = lf = factor_part(job, p);
     } else {
       rf = job.rf;
       lf = job.lf;

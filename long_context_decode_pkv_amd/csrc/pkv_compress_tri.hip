@@ -323,8 +323,7 @@ __device__ __forceinline__ void store_q4(const CompressJob& job, const PageRef& 
   const Q4Dims qd = q4_dims(r);
   const int A = qd.pd.A, r8 = 8 * qd.pd.n8, ub = qd.ub;
   const bool keys = pr.kind == 0;
-  uint8_t* part = job.fac + (pr.bh * job.fac_bh_pages + job.f0 + pr.f) * job.page_bytes +
-                  (int64_t)pr.kind * job.k_part_bytes;
+  uint8_t* part = factor_part(job, pr);
   float* hs = sh.w;      // sigma_i^(1/2)
   float* ihs = sh.xrow;  // sigma_i^(-1/2), 0 where sigma_i = 0
   float* lsc = sh.v;     // scales of the columns of Lt_K
@@ -441,6 +440,9 @@ __device__ __forceinline__ void store_q4(const CompressJob& job, const PageRef& 
       q4_store_unit(part + qd.k2 + (int64_t)u * ub, q4_pack(&Lc[j * kTriMaxRank + A * qk], 1, A, 2 * ub), ub);
     }
     if (lane < r8) q4_store_scale(part + q4_sl_k(qd, lane), lsc[lane]);
+    // the part's tail up to its 64-byte boundary: the host packer's filler,
+    // so that a part's bytes depend on the page alone
+    for (int64_t b = qd.sl_k + 2 * r8 + lane; b < qd.k_bytes; b += kP) part[b] = 0x88;
   } else {
     // V1: Lt_V^T rank tiles, dwords of 8 tokens
     for (int u = lane; u < full * 128 + partial * 64; u += kP) {
@@ -463,6 +465,7 @@ __device__ __forceinline__ void store_q4(const CompressJob& job, const PageRef& 
       q4_store_unit(part + qd.v2 + (int64_t)u * ub, q4_pack(&Rc[A * qk * kD + c], kD, A, 2 * ub), ub);
     }
     q4_store_scale(part + q4_sl_v(qd, lane), lsv);
+    for (int64_t b = qd.sr_v + 2 * kD + lane; b < qd.v_bytes; b += kP) part[b] = 0x88;
   }
 }
 

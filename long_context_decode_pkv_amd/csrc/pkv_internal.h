@@ -238,22 +238,32 @@ __host__ __device__ inline int table_slot(int32_t e) { return e & 0xffffff; }
 // --------------------------------------------------------------------------
 
 // Where the pages to decompose come from and where their factors go.
+// One source of a job's pages.  Its page f (0 <= f < its count) is read
+// from input slot in_f0 + f -- taken modulo f_mod when f_mod > 0, for the
+// recent-window ring -- at base[kind] + bh * bh_stride + slot * f_stride
+// elements, and (cache jobs) its factors go to factor slot out_f0 + f.
+struct CompressSrc {
+  const void* base[2];          // per kind
+  int trans[2];                 // 0: page is [P][d]; 1: page stored as [d][P]
+  int64_t bh_stride;            // elements
+  int64_t f_stride;             // elements
+  int64_t in_f0, f_mod, out_f0;
+};
+
 struct CompressJob {
-  // page n -> kind = n % n_kind, f = (n / n_kind) % n_f, bh = n / (n_kind * n_f)
+  // page n -> kind = n % n_kind, f = (n / n_kind) % n_f, bh = n / (n_kind * n_f);
+  // f < n_f_src0 is page f of src[0], the others page f - n_f_src0 of src[1]
   int64_t n_pages;
   int n_kind;                   // 1 (standalone) or 2 (K and V of a cache)
   int64_t n_f;
-  const void* in_base[2];       // per kind
-  int in_trans[2];              // 0: page is [P][d]; 1: page stored as [d][P]
-  int64_t in_bh_stride;         // elements
-  int64_t in_f_stride;          // elements
+  int64_t n_f_src0;
+  CompressSrc src[2];
   int in_dtype;                 // pkv_dtype
   int rank[2];                  // per kind
   int out_dtype;
-  // packed output (cache): fac + ((bh * fac_bh_pages) + f0 + f) * page_bytes + kind * k_part_bytes
+  // packed output (cache): fac + (bh * fac_bh_pages + slot) * page_bytes + kind * k_part_bytes
   uint8_t* fac;
   int64_t fac_bh_pages;
-  int64_t f0;
   int64_t page_bytes;
   int64_t k_part_bytes;
   // row-major output (standalone) when fac == nullptr
@@ -289,6 +299,8 @@ struct CacheGeom {
 
 hipError_t launch_prefill_dense(const CacheGeom& g, const void* K, const void* V, int64_t T,
                                 int64_t n_fact, hipStream_t stream);
+hipError_t launch_chunk_dense(const CacheGeom& g, const void* K, const void* V, int64_t T0, int64_t T1,
+                              int64_t p_lo, int64_t p_hi, hipStream_t stream);
 hipError_t launch_table_fill(const CacheGeom& g, int64_t T, int64_t n_fact, hipStream_t stream);
 hipError_t launch_table_set(const CacheGeom& g, int64_t page, int32_t entry, hipStream_t stream);
 hipError_t launch_append(const CacheGeom& g, const void* k, const void* v, int64_t T,

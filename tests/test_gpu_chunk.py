@@ -1,0 +1,215 @@
+"""GPU tests of pkv_prefill_chunk (chunked prefill, PuzzleKV Sec. 3.3 (1)-(3)
+and (5) applied to many tokens at once).
+
+The reference is the token-by-token path on a twin cache (pkv_append, and
+pkv_promote_page whenever a page leaves the window): after every chunk the
+two caches must agree exactly -- host state, page table, every factorized
+page's packed factors (bit-identical: the same decomposition kernel on the
+same page bytes) and every valid dense row -- and so must their attention
+outputs (bit-identical).  The oracle checks the attention after chunks.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import long_context_decode_pkv_amd as pkv
+from gpu_common import TOL, make_cache, rel_err, require_gpu, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _valid_dense_rows(cache, T):
+    """{(b, h, page): (K rows, V columns)} of every dense page's valid rows."""
+    import torch
+    L, sh = cache.layout, cache.shape
+    B, H, P, d = sh.batch, sh.n_kv_heads, 64, 128
+    esz = L["elem_bytes"]
+    n_s, ring = L["n_sink_slots"], L["n_ring_slots"]
+    cls, slot = cache.page_table(-(-T // P))
+    buf = cache.buffer
+    out = {}
+    for p in range(len(cls)):
+        if cls[p] == pkv.FACT:
+            continue
+        nv = min(P, T - p * P)
+        for b in range(B):
+            for h in range(H):
+                if cls[p] == pkv.SINK:
+                    base_k = L["sink_k"] + ((b * H + h) * n_s + slot[p]) * P * d * esz
+                    base_v = L["sink_v"] + ((b * H + h) * n_s + slot[p]) * P * d * esz
+                else:
+                    base_k = L["win_k"] + ((b * H + h) * ring + slot[p]) * P * d * esz
+                    base_v = L["win_v"] + ((b * H + h) * ring + slot[p]) * P * d * esz
+                k = buf[base_k: base_k + P * d * esz].view(P, d * esz)[:nv].clone()
+                v = buf[base_v: base_v + P * d * esz].view(d, P * esz)[:, :nv * esz].clone()
+                out[(b, h, p)] = (k, v)
+    torch.cuda.synchronize()
+    return out
+
+
+def _assert_same_cache(a, b, label):
+    import torch
+    assert a.state() == b.state(), (label, a.state(), b.state())
+    T, nf, _ = a.state()
+    n = -(-T // 64)
+    for x, y in zip(a.page_table(n), b.page_table(n)):
+        np.testing.assert_array_equal(x, y, err_msg=label)
+    L, sh = a.layout, a.shape
+    for bb in range(sh.batch):
+        for h in range(sh.n_kv_heads):
+            for f in range(nf):
+                for kind in (pkv.KEYS, pkv.VALUES):
+                    assert torch.equal(a.factor_part(bb, h, f, kind), b.factor_part(bb, h, f, kind)), \
+                        (label, bb, h, f, kind)
+    da, db = _valid_dense_rows(a, T), _valid_dense_rows(b, T)
+    assert da.keys() == db.keys()
+    for key in da:
+        assert torch.equal(da[key][0], db[key][0]) and torch.equal(da[key][1], db[key][1]), (label, key)
+
+
+def _chunk_vs_tokens(cfg_id, T0, chunks, B=1, kv_heads=2, store=None, aux=False, **kw):
+    import torch
+    require_gpu()
+    total = T0 + sum(c[1] if isinstance(c, tuple) else c for c in chunks)
+    d = synth.decode_inputs(cfg_id, T=total, B=B, kv_heads=kv_heads)
+    dt = d["cfg"]["dtype"]
+    a = make_cache(d, max_tokens=total, store=store, **kw)
+    b = make_cache(d, max_tokens=total, store=store, **kw)
+    Kd, Vd = to_dev(d["K"], dt), to_dev(d["V"], dt)
+    for c in (a, b):
+        c.prefill(Kd[:, :, :T0].contiguous(), Vd[:, :, :T0].contiguous())
+    if aux:
+        stream = torch.cuda.Stream()
+        a.set_aux_stream(stream)
+    q = to_dev(d["q"], dt)
+    T = T0
+    for i, C in enumerate(chunks):
+        if isinstance(C, tuple):  # ("tok" | "step", n): n single tokens on both caches
+            kind, C = C
+            for t in range(T, T + C):
+                if kind == "step":  # append, promotion and attention in one call
+                    a.step(Kd[:, :, t].contiguous(), Vd[:, :, t].contiguous(), q)
+                elif a.append(Kd[:, :, t].contiguous(), Vd[:, :, t].contiguous()):
+                    a.promote()
+        else:
+            a.prefill_chunk(Kd[:, :, T:T + C].contiguous(), Vd[:, :, T:T + C].contiguous())
+        for t in range(T, T + C):
+            if b.append(Kd[:, :, t].contiguous(), Vd[:, :, t].contiguous()):
+                b.promote()
+        T += C
+        oa = a.decode(q)  # orders itself after an overlapped chunk decomposition
+        ob = b.decode(q)
+        torch.cuda.synchronize()
+        label = f"cfg{cfg_id} T0={T0} chunk {i} (C={C}, T={T})"
+        _assert_same_cache(a, b, label)
+        assert torch.equal(oa, ob), label
+    return a, d
+
+
+def test_chunks_match_token_by_token():
+    # ragged start, chunks that complete the partial page, span several
+    # window turnovers, and single tokens
+    _chunk_vs_tokens(2, 64 * 5 + 17, [40, 7, 64, 300, 1, 513, 64])
+
+
+def test_chunks_f32_pages():
+    _chunk_vs_tokens(1, 64 * 3 + 9, [100, 55, 600], kv_heads=1)
+
+
+def test_chunks_from_empty_cache_through_the_sink():
+    _chunk_vs_tokens(2, 0, [30, 20, 100, 1000])
+    # a first chunk that starts in the sink and leaves factorized pages
+    _chunk_vs_tokens(2, 0, [1000, 64])
+    _chunk_vs_tokens(2, 10, [700], aux=True)
+
+
+def test_chunks_without_window_or_sink():
+    _chunk_vs_tokens(2, 64 * 3 + 5, [59, 64, 200], w=0)
+    _chunk_vs_tokens(2, 64 * 2 + 1, [63, 130], s=0)
+
+
+def test_chunks_int4_pages():
+    _chunk_vs_tokens(3, 64 * 4 + 33, [31, 200, 700], store="int4")
+
+
+def test_chunks_on_aux_stream():
+    # the chunk-only pages decompose on the aux stream; every decode and the
+    # cache contents must be the same as on the token path
+    _chunk_vs_tokens(2, 64 * 5 + 17, [40, 600, 1, 900], B=2, aux=True)
+
+
+def test_chunks_between_appends():
+    # chunks after single appends and before them: appends leave pages for
+    # promotion, a chunk moves them on
+    _chunk_vs_tokens(2, 64 * 5 + 17, [("tok", 70), 300, ("tok", 47), 64, ("tok", 1), 1000, ("tok", 130), 5])
+
+
+def test_chunks_between_appends_on_aux_stream():
+    # early factorizations from appends and from chunks, consumed by later
+    # promotions and chunks, page-aligned chunks included
+    _chunk_vs_tokens(2, 64 * 5 + 17, [("tok", 70), 300, ("tok", 47), 64, ("tok", 1), 1000,
+                                      ("tok", 130), 5, 59, 256, ("tok", 200)], B=2, aux=True)
+    _chunk_vs_tokens(3, 64 * 6, [512, 512, ("tok", 64), 128, 2048], store="int4", aux=True)
+    _chunk_vs_tokens(2, 64 * 4 + 3, [("step", 130), 700, ("step", 200), 64, ("step", 3)], aux=True)
+
+
+def test_chunked_prefill_against_oracle():
+    import torch
+    require_gpu()
+    cfg_id, chunks = 3, [1000, 2048, 77, 1]
+    total = sum(chunks)
+    d = synth.decode_inputs(cfg_id, T=total, B=1, kv_heads=2, with_f64=True)
+    cfg = d["cfg"]
+    cache = make_cache(d, max_tokens=total)
+    Kd, Vd = to_dev(d["K"], "bf16"), to_dev(d["V"], "bf16")
+    cache.prefill(Kd[:, :, :0].contiguous(), Vd[:, :, :0].contiguous())
+    T = 0
+    for C in chunks:
+        cache.prefill_chunk(Kd[:, :, T:T + C].contiguous(), Vd[:, :, T:T + C].contiguous())
+        T += C
+    o = to_f64(cache.decode(to_dev(d["q"], "bf16")))
+    torch.cuda.synchronize()
+    ref = oracle.decode(d["q64"], d["K64"], d["V64"], T, 64, cfg["s"], cfg["w"], cfg["r_k"], cfg["r_v"],
+                        "bf16")
+    err = rel_err(o, ref["o_stored"])
+    print(f"[chunked prefill vs oracle] T={T}: err {err:.3e}")
+    assert err <= TOL["bf16"]
+    # and the same cache as a one-shot prefill
+    one = make_cache(d, max_tokens=total)
+    one.prefill(Kd.contiguous(), Vd.contiguous())
+    torch.cuda.synchronize()
+    assert one.state() == cache.state()
+    for f in range(cache.state()[1]):
+        for kind in (pkv.KEYS, pkv.VALUES):
+            assert torch.equal(one.factor_part(0, 1, f, kind), cache.factor_part(0, 1, f, kind))
+
+
+def test_chunk_errors():
+    import torch
+    require_gpu()
+    d = synth.decode_inputs(2, T=300, B=1, kv_heads=1)
+    Kd, Vd = to_dev(d["K"], "bf16"), to_dev(d["V"], "bf16")
+    cache = make_cache(d, max_tokens=200)
+    cache.prefill(Kd[:, :, :190].contiguous(), Vd[:, :, :190].contiguous())
+    with pytest.raises(pkv.PKVError) as ei:  # beyond capacity
+        cache.prefill_chunk(Kd[:, :, 190:210].contiguous(), Vd[:, :, 190:210].contiguous())
+    assert ei.value.status == 3
+    assert cache.state()[0] == 190
+    cache.prefill_chunk(Kd[:, :, :0].contiguous(), Vd[:, :, :0].contiguous())  # C = 0: nothing
+    assert cache.state()[0] == 190
+    # a completed page waiting for promotion refuses a chunk: with s = 64 and
+    # w = 128 the page completed by token 255 must leave the window
+    c2 = make_cache(d, max_tokens=300)
+    c2.prefill(Kd[:, :, :250].contiguous(), Vd[:, :, :250].contiguous())
+    pending = False
+    for t in range(250, 256):
+        pending = c2.append(Kd[:, :, t].contiguous(), Vd[:, :, t].contiguous())
+    assert pending
+    with pytest.raises(pkv.PKVError) as ei:
+        c2.prefill_chunk(Kd[:, :, 256:261].contiguous(), Vd[:, :, 256:261].contiguous())
+    assert ei.value.status == 5
+    c2.promote()
+    c2.prefill_chunk(Kd[:, :, 256:261].contiguous(), Vd[:, :, 256:261].contiguous())
+    assert c2.state()[:2] == (261, 1)
+    torch.cuda.synchronize()

@@ -96,6 +96,21 @@ def test_int4_decomposition_codes_match_oracle(cfg_id, r):
     assert equal >= 0.99 * total
 
 
+@pytest.mark.parametrize("r", [24, 8, 20, 32])
+def test_int4_parts_are_canonical(r):
+    """Every byte of a GPU-written part, padding included, is what the host
+    packer writes for the part's own codes and scales: pack(unpack(part))
+    reproduces it exactly, so a part depends on the page alone."""
+    require_gpu()
+    d, cache = _prefilled(3, 64 * 8, B=1, kv_heads=2, r_k=r, r_v=r)
+    for h in range(2):
+        for f in range(cache.state()[1]):
+            for kind in (pkv.KEYS, pkv.VALUES):
+                part = cache.factor_part(0, h, f, kind).cpu().numpy()
+                again = pkv.pack_factors_int4(kind, r, *pkv.unpack_factors_int4(kind, r, part))
+                np.testing.assert_array_equal(part, again, err_msg=f"h{h} page {f} kind {kind}")
+
+
 def _oracle_parts(d, cache, r_k, r_v):
     """Write the oracle's INT4 codes of every FACT page into the pool."""
     import torch

@@ -196,3 +196,26 @@ def test_time_next_kernel_validation_without_gpu():
     assert L.pkv_time_next_kernel(p, p) == 0
     assert L.pkv_compress_pages(p, 0, 64, 128, 8, 0, 0, p, p, None, None) == 0  # no launch
     assert L.pkv_time_next_kernel(None, None) == 0
+
+
+def test_prefill_chunk_validation_without_gpu():
+    """Argument and state checks of pkv_prefill_chunk fire before any launch."""
+    L = pkv.lib()
+    sh = _shape(max_tokens=256)
+    lay = pkv.cache_layout(sh)
+    h = ctypes.c_void_p()
+    assert L.pkv_cache_create(ctypes.byref(sh), ctypes.c_void_p(256 * 1000), lay["total_bytes"],
+                              ctypes.byref(h)) == 0
+    fake = ctypes.c_void_p(256 * 5000)
+    try:
+        assert L.pkv_prefill_chunk(None, fake, fake, 1, None) == 1
+        assert L.pkv_prefill_chunk(h, fake, fake, -1, None) == 1
+        assert L.pkv_prefill_chunk(h, fake, fake, 0, None) == 0           # nothing to do
+        assert L.pkv_prefill_chunk(h, None, fake, 4, None) == 1
+        assert L.pkv_prefill_chunk(h, ctypes.c_void_p(256 * 5000 + 2), fake, 4, None) == 1
+        assert L.pkv_prefill_chunk(h, fake, fake, 257, None) == 3         # beyond max_tokens
+        T, nf, pend = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+        assert L.pkv_cache_state(h, ctypes.byref(T), ctypes.byref(nf), ctypes.byref(pend)) == 0
+        assert (T.value, nf.value, pend.value) == (0, 0, 0)
+    finally:
+        L.pkv_cache_destroy(h)
