@@ -28,7 +28,11 @@ Readings taken where the pages are silent (each is listed in the design doc):
     page's Eq. 2 puts Sigma on the right factor, the product is identical;
   * the "stored" variant rounds Lf and Rf to the cache dtype, nearest-even;
   * query head h reads KV head floor(h / G) (contiguous GQA groups);
-  * no causal mask: the single decode query sees every cached token.
+  * no causal mask: the single decode query sees every cached token;
+  * pre-RoPE keys (App. D.3 compares them with post-RoPE keys and gives no
+    procedure): the cache stores and factorizes keys before rotation, and the
+    attention rotates every key at its token index with the half-split channel
+    pairing; the query arrives rotated.
 """
 from __future__ import annotations
 
@@ -332,6 +336,25 @@ def merge_states(states):
 
 
 # --------------------------------------------------------------------------
+# Pre-RoPE keys (App. D.3 "RoPE Key Analysis"; rotary embedding of RoFormer,
+# the page's ref. [15])
+# --------------------------------------------------------------------------
+
+def rope_rotate(X, positions, inv_freq):
+    """Rotary position embedding of the rows of X (n, d): row t turns each
+    channel pair (m, m + d/2) by the angle a = positions[t] * inv_freq[m]
+    (the pairing of the Llama / Qwen checkpoints):
+        x_m <- x_m cos a - x_{m+d/2} sin a,   x_{m+d/2} <- x_{m+d/2} cos a + x_m sin a.
+    Angles and rotation in float64; inv_freq holds d/2 frequencies."""
+    X = np.asarray(X, dtype=np.float64)
+    h = X.shape[-1] // 2
+    a = np.asarray(positions, dtype=np.float64)[:, None] * np.asarray(inv_freq, dtype=np.float64)[None, :]
+    c, sn = np.cos(a), np.sin(a)
+    x1, x2 = X[..., :h], X[..., h:]
+    return np.concatenate([x1 * c - x2 * sn, x2 * c + x1 * sn], axis=-1)
+
+
+# --------------------------------------------------------------------------
 # Whole-cache decode (the quantity the GPU path is checked against)
 # --------------------------------------------------------------------------
 
@@ -368,12 +391,17 @@ def reconstruct_cache(X, T, P, s, w, r, store, n_fact=None, with_metrics=False, 
     return Xs, Xe, metrics
 
 
-def decode(q, K, V, T, P, s, w, r_k, r_v, store, n_fact=None, kv_heads=None):
+def decode(q, K, V, T, P, s, w, r_k, r_v, store, n_fact=None, kv_heads=None, key_rope=None):
     """Attention output of one decode step over a hybrid cache.
 
     q: (B, H_q, d); K, V: (B, H_kv, >=T, d) holding the stored (already
     dtype-rounded) values.  Returns dict(o_stored, o_exact) of shape
     (B, H_q, d); query heads of KV heads not in `kv_heads` are left NaN.
+
+    key_rope (d/2 frequencies, or None): the cache holds pre-RoPE keys (App.
+    D.3) -- pages are factorized as stored, and every key, dense or
+    reconstructed, is rotated at its own position t (its token index) before
+    the scores; q is taken as already rotated.
     """
     q = np.asarray(q, dtype=np.float64)
     B, Hq, d = q.shape
@@ -386,6 +414,9 @@ def decode(q, K, V, T, P, s, w, r_k, r_v, store, n_fact=None, kv_heads=None):
         for h in heads:
             Ks, Ke, _ = reconstruct_cache(K[b, h], T, P, s, w, r_k, store, n_fact, kind="K")
             Vs, Ve, _ = reconstruct_cache(V[b, h], T, P, s, w, r_v, store, n_fact, kind="V")
+            if key_rope is not None:
+                Ks = rope_rotate(Ks, np.arange(T), key_rope)
+                Ke = rope_rotate(Ke, np.arange(T), key_rope)
             qs = q[b, h * G:(h + 1) * G]
             o_s[b, h * G:(h + 1) * G] = attention(qs, Ks, Vs)
             o_e[b, h * G:(h + 1) * G] = attention(qs, Ke, Ve)
@@ -418,9 +449,10 @@ class IncrementalDecoder:
     ever be appended.
     """
 
-    def __init__(self, K, V, P, s, w, r_k, r_v, store, kv_heads=None):
+    def __init__(self, K, V, P, s, w, r_k, r_v, store, kv_heads=None, key_rope=None):
         self.K = np.asarray(K, dtype=np.float64)
         self.V = np.asarray(V, dtype=np.float64)
+        self.key_rope = key_rope  # pre-RoPE keys, rotated at attention (see decode)
         self.P, self.s, self.w = P, s, w
         self.r = (r_k, r_v)
         self.store = store
@@ -467,6 +499,9 @@ class IncrementalDecoder:
             for p in fact:
                 Ks[p * P:(p + 1) * P], Ke[p * P:(p + 1) * P] = self.done[(b, h, 0, p)]
                 Vs[p * P:(p + 1) * P], Ve[p * P:(p + 1) * P] = self.done[(b, h, 1, p)]
+            if self.key_rope is not None:
+                Ks = rope_rotate(Ks, np.arange(T), self.key_rope)
+                Ke = rope_rotate(Ke, np.arange(T), self.key_rope)
             qs = q[b, h * G:(h + 1) * G]
             o_s[b, h * G:(h + 1) * G] = attention(qs, Ks, Vs)
             o_e[b, h * G:(h + 1) * G] = attention(qs, Ke, Ve)

@@ -198,6 +198,13 @@ def decode_inputs(cfg_id: int, T: int | None = None, B: int | None = None,
     return res
 
 
+def rope_inv_freq(base: float, d: int = 128) -> np.ndarray:
+    """Rotary frequencies base^(-2m/d), m < d/2, as float32 (the values both
+    sides receive; Qwen3 checkpoints use base 1e6, Llama 3.1 5e5 before its
+    frequency scaling)."""
+    return (float(base) ** (-np.arange(0, d, 2, dtype=np.float64) / d)).astype(np.float32)
+
+
 def step_queries(cfg_id: int, step: int, B: int, Hq: int, d: int, dtype: str):
     """Query of decode step `step` (workload 4)."""
     g = rng(CONFIGS[cfg_id]["seed"], 1000 + step, 0, 0, KIND_Q)
