@@ -108,7 +108,7 @@ def decode_bytes(cfg, B, Hkv, Hq, T, n_fact, store=None):
     return B * Hkv * (fact + dense) + B * Hq * d * esz + B * Hq * d * 4
 
 
-def cpu_baseline_decode(cfg, K, V, q, T, store=None):
+def cpu_baseline_decode(cfg, K, V, q, T, store=None, key_rope=None):
     """The oracle on a bounded sample: KV head 0 of the same cache.  The
     oracle reconstructs that head (Jacobi SVD of its factorized pages,
     truncation, storage rounding; timed -> pages/s), then its naive float64
@@ -136,7 +136,8 @@ def cpu_baseline_decode(cfg, K, V, q, T, store=None):
     reps = 3
     t = time.perf_counter()
     for _ in range(reps):
-        oracle.attention(q64, Khat, Vhat)
+        Ka = Khat if key_rope is None else oracle.rope_rotate(Khat, np.arange(T), key_rope)
+        oracle.attention(q64, Ka, Vhat)
     t_att = (time.perf_counter() - t) / reps
     step = t_att * n_pairs
     return dict(value=K.shape[0] / step, unit="tokens/s", cores=int(max(blas, oracle.num_threads())),
@@ -149,7 +150,10 @@ def cpu_baseline_decode(cfg, K, V, q, T, store=None):
                 svd_pages_per_s=2 * n_fact / t_rec)
 
 
-def bench_decode(args, cfg_id, name, store=None):
+ROPE_BASE = {2: 5e5, 3: 1e6}  # rotary bases of the Llama 3.1 and Qwen3 checkpoints
+
+
+def bench_decode(args, cfg_id, name, store=None, rope=False):
     """One decode step of the workload's layer, on NL independent layer caches
     in rotation (a decode step of an NL-layer stack), so that no cache is
     re-read from the 256 MB Infinity Cache between its uses."""
@@ -167,6 +171,10 @@ def bench_decode(args, cfg_id, name, store=None):
     caches = [pkv.Cache(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, rank_k=cfg["r_k"], rank_v=cfg["r_v"],
                         sink=cfg["s"], window=cfg["w"], max_tokens=total, dtype=store or dt)
               for _ in range(NL)]
+    freqs = synth.rope_inv_freq(ROPE_BASE[cfg_id]) if rope else None
+    if rope:  # pre-RoPE keys, rotated at attention (App. D.3)
+        for c in caches:
+            c.set_key_rope(freqs)
     K0 = Kd[:, :, :T0].contiguous()
     V0 = Vd[:, :, :T0].contiguous()
     rows_k = [Kd[:, :, t].contiguous() for t in range(T0, total)]
@@ -293,6 +301,8 @@ def bench_decode(args, cfg_id, name, store=None):
                    "context_tokens": T0, "page_len": cfg["P"], "rank_k": cfg["r_k"],
                    "rank_v": cfg["r_v"], "sink": cfg["s"], "window": cfg["w"],
                    "layer_caches_rotated": NL, "factor_store": store or dt,
+                   "keys": (f"pre-RoPE, rotated at attention (base {ROPE_BASE[cfg_id]:g})" if rope
+                            else "as given"),
                    "step": "pkv_decode_step per layer: promotion when a page leaves the window, "
                            "decode partial, merge with the appended token folded in",
                    "early_factorization": bool(args.aux)},
@@ -331,7 +341,7 @@ def bench_decode(args, cfg_id, name, store=None):
                            "roofline": compress_summary(cres, c5["ranks"][1])}
     if args.cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")
-        cb = cpu_baseline_decode(cfg, inp["K"], inp["V"], inp["q"], T0, store)
+        cb = cpu_baseline_decode(cfg, inp["K"], inp["V"], inp["q"], T0, store, freqs)
         res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
         res["cpu_baseline_svd_pages_per_s"] = cb["svd_pages_per_s"]
     return res
@@ -481,7 +491,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="qwen3-32b-layer-128k",
                     choices=["qwen3-32b-layer-128k", "llama3.1-8b-layer", "qwen3-32b-layer-128k-int4",
-                             "llama3.1-8b-layer-int4", "compress", "copy"])
+                             "llama3.1-8b-layer-int4", "qwen3-32b-layer-128k-prerope",
+                             "llama3.1-8b-layer-prerope", "compress", "copy"])
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--workers", type=int, default=1)
     ap.add_argument("--layers", type=int, default=4,
@@ -509,10 +520,10 @@ def main():
         res = bench_compress(args)
     elif args.workload == "copy":
         res = bench_copy(args)
-    elif args.workload.startswith("llama3.1-8b-layer"):
-        res = bench_decode(args, 2, args.workload, "int4" if args.workload.endswith("-int4") else None)
     else:
-        res = bench_decode(args, 3, args.workload, "int4" if args.workload.endswith("-int4") else None)
+        cfg_id = 2 if args.workload.startswith("llama3.1-8b-layer") else 3
+        res = bench_decode(args, cfg_id, args.workload, "int4" if args.workload.endswith("-int4") else None,
+                           rope=args.workload.endswith("-prerope"))
     print(json.dumps(res), flush=True)
 
 

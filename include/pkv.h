@@ -70,8 +70,11 @@ typedef enum pkv_page_class {
   PKV_PAGE_PART = 4    /* page still being filled; dense */
 } pkv_page_class;
 
-/* Factor part selector for pkv_pack_factors / pkv_unpack_factors. */
-typedef enum pkv_factor_kind { PKV_KEYS = 0, PKV_VALUES = 1 } pkv_factor_kind;
+/* Factor part selector for pkv_pack_factors / pkv_unpack_factors.
+ * PKV_KEYS_PRE_ROPE is the key part of a cache holding pre-RoPE keys
+ * (pkv_cache_set_key_rope): the same elements as PKV_KEYS, with Rf_K stored
+ * channel-major (in the order of the value part's Rf_V). */
+typedef enum pkv_factor_kind { PKV_KEYS = 0, PKV_VALUES = 1, PKV_KEYS_PRE_ROPE = 2 } pkv_factor_kind;
 
 /* Shape and parameters of one layer's hybrid cache (passed by pointer). */
 typedef struct pkv_shape {
@@ -161,7 +164,7 @@ int32_t pkv_pack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t 
 int32_t pkv_unpack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t dtype,
                            const void* packed, float* Lf, float* Rf);
 
-/* Bytes of one factor part (kind: PKV_KEYS / PKV_VALUES) of rank r in
+/* Bytes of one factor part (kind: any pkv_factor_kind) of rank r in
  * storage format `dtype` (for PKV_BF16_INT4 the INT4 part of Sec. 4.3; its
  * K and V parts differ in size).  Host only. */
 int32_t pkv_factor_part_bytes(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t dtype,
@@ -357,6 +360,26 @@ int32_t pkv_decode_step(pkv_cache* cache, const void* k_new, const void* v_new, 
  * outstanding), DEVICE.
  */
 int32_t pkv_cache_set_aux_stream(pkv_cache* cache, void* aux_stream);
+
+/*
+ * Pre-RoPE keys (App. D.3 "RoPE Key Analysis" compares factorizing keys
+ * before and after the rotary position embedding): from this call on, the
+ * keys given to pkv_prefill, pkv_prefill_chunk, pkv_append and
+ * pkv_decode_step are taken as pre-RoPE.  They are stored and factorized as
+ * given, and the attention calls rotate every key, dense or reconstructed
+ * from its factors, at its position t (its token index in the cache) before
+ * the scores.  Channel pair (m, m + d/2) turns by the angle t * inv_freq[m]
+ * (the pairing of the Llama and Qwen checkpoints); the angle is reduced in
+ * double precision, so positions up to max_tokens keep full accuracy.  The
+ * query is taken as already rotated at its own position.  Key parts then
+ * use the PKV_KEYS_PRE_ROPE layout.
+ * inv_freq: host, n_freq = d/2 finite float32 frequencies, copied; NULL
+ * turns pre-RoPE keys off.  Only on an empty cache (length 0: after
+ * pkv_cache_create or a pkv_prefill with T = 0).
+ * Errors: INVALID_ARG (null cache, n_freq != d/2, a non-finite frequency, a
+ * non-empty cache), UNSUPPORTED (PKV_BF16_INT4 caches).
+ */
+int32_t pkv_cache_set_key_rope(pkv_cache* cache, const float* inv_freq, int32_t n_freq);
 
 /* Kernel timing (measurement only; no passage of the method).
  *

@@ -23,7 +23,7 @@ PKV_OK = 0
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "capacity exceeded",
           4: "no page waiting for promotion", 5: "promotion pending", 6: "device error"}
 BF16, F32, BF16_INT4 = 0, 1, 2
-KEYS, VALUES = 0, 1
+KEYS, VALUES, KEYS_PRE_ROPE = 0, 1, 2
 UNUSED, SINK, FACT, WIN, PART = 0, 1, 2, 3, 4
 PAGE_LEN, HEAD_DIM = 64, 128
 
@@ -91,6 +91,7 @@ def lib():
         "pkv_time_next_kernel": ([vp, vp], i32),
         "pkv_decode_step": ([vp, vp, vp, vp, vp, vp, u64, i32, vp], i32),
         "pkv_cache_set_aux_stream": ([vp, vp], i32),
+        "pkv_cache_set_key_rope": ([vp, vp, i32], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -392,6 +393,17 @@ class Cache:
         ptr = ctypes.c_void_p(stream.cuda_stream) if stream is not None else None
         _check(lib().pkv_cache_set_aux_stream(self._h, ptr), "pkv_cache_set_aux_stream")
         self._aux = stream  # keep the stream alive while the cache uses it
+
+    def set_key_rope(self, inv_freq=None):
+        """Keys given from now on are pre-RoPE (App. D.3): they are stored and
+        factorized unrotated, and attention rotates each key at its token
+        index with these d/2 frequencies (None: off).  Only on an empty
+        cache (pkv_cache_set_key_rope)."""
+        if inv_freq is None:
+            _check(lib().pkv_cache_set_key_rope(self._h, None, 0), "pkv_cache_set_key_rope")
+            return
+        f = np.ascontiguousarray(inv_freq, dtype=np.float32)
+        _check(lib().pkv_cache_set_key_rope(self._h, _np_ptr(f), f.size), "pkv_cache_set_key_rope")
 
     def step(self, k, v, q, out=None, n_split: int = 0, workspace=None):
         """One decode step (pkv_decode_step): append (k, v), promote the page

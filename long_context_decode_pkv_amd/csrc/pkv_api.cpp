@@ -39,6 +39,9 @@ struct pkv_cache {
   // there; the next call that reads the factor pool waits for chunk_ready
   hipEvent_t chunk_ready = nullptr;
   mutable bool chunk_pending = false;
+  // pre-RoPE keys (pkv_cache_set_key_rope): rotary frequencies of pair (m, m + d/2)
+  int rope = 0;
+  float rope_freq[kD / 2] = {};
 };
 
 namespace {
@@ -125,6 +128,8 @@ CacheGeom geom_of(const pkv_cache* c) {
   g.r_v = c->shape.rank_v;
   g.base = c->base;
   g.lay = c->lay;
+  g.rope = c->rope;
+  std::memcpy(g.rope_freq, c->rope_freq, sizeof(g.rope_freq));
   return g;
 }
 
@@ -207,6 +212,7 @@ hipError_t factorize(const pkv_cache* c, const CompressSrc& a, int64_t n0, const
   job.rank[0] = g.r_k;
   job.rank[1] = g.r_v;
   job.out_dtype = g.dtype;
+  job.key_part_kind = c->rope ? PKV_KEYS_PRE_ROPE : PKV_KEYS;
   job.fac = c->base + c->lay.factors;
   job.fac_bh_pages = g.F_max;
   job.page_bytes = c->lay.factor_page_bytes;
@@ -361,8 +367,8 @@ int32_t pkv_pack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t 
   int64_t n;
   int32_t st = pkv_factor_part_elems(P, d, r, &n);
   if (st != PKV_OK) return st;
-  if ((kind != PKV_KEYS && kind != PKV_VALUES) || (dtype != PKV_BF16 && dtype != PKV_F32) || !Lf ||
-      !Rf || !packed)
+  if ((kind != PKV_KEYS && kind != PKV_VALUES && kind != PKV_KEYS_PRE_ROPE) ||
+      (dtype != PKV_BF16 && dtype != PKV_F32) || !Lf || !Rf || !packed)
     return PKV_ERR_INVALID_ARG;
   const PackDims pd = pack_dims(r);
   const int r8 = 8 * pd.n8;
@@ -378,11 +384,11 @@ int32_t pkv_pack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t 
   for (int i = 0; i < r8; ++i) {
     for (int c = 0; c < kD; ++c) {
       const float v = i < r ? Rf[(int64_t)i * kD + c] : 0.f;
-      put(kind == PKV_KEYS ? off_rf_k(pd, i, c) : off_rf_v(pd, i, c), v);
+      put(off_rf(kind, pd, i, c), v);
     }
     for (int j = 0; j < kP; ++j) {
       const float v = i < r ? Lf[(int64_t)j * r + i] : 0.f;
-      put(kind == PKV_KEYS ? off_lf_k(pd, j, i) : off_lf_v(pd, j, i), v);
+      put(off_lf(kind, pd, j, i), v);
     }
   }
   return PKV_OK;
@@ -393,8 +399,8 @@ int32_t pkv_unpack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_
   int64_t n;
   int32_t st = pkv_factor_part_elems(P, d, r, &n);
   if (st != PKV_OK) return st;
-  if ((kind != PKV_KEYS && kind != PKV_VALUES) || (dtype != PKV_BF16 && dtype != PKV_F32) || !Lf ||
-      !Rf || !packed)
+  if ((kind != PKV_KEYS && kind != PKV_VALUES && kind != PKV_KEYS_PRE_ROPE) ||
+      (dtype != PKV_BF16 && dtype != PKV_F32) || !Lf || !Rf || !packed)
     return PKV_ERR_INVALID_ARG;
   const PackDims pd = pack_dims(r);
   auto get = [&](int64_t idx) -> float {
@@ -408,16 +414,17 @@ int32_t pkv_unpack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_
   };
   for (int i = 0; i < r; ++i) {
     for (int c = 0; c < kD; ++c)
-      Rf[(int64_t)i * kD + c] = get(kind == PKV_KEYS ? off_rf_k(pd, i, c) : off_rf_v(pd, i, c));
+      Rf[(int64_t)i * kD + c] = get(off_rf(kind, pd, i, c));
     for (int j = 0; j < kP; ++j)
-      Lf[(int64_t)j * r + i] = get(kind == PKV_KEYS ? off_lf_k(pd, j, i) : off_lf_v(pd, j, i));
+      Lf[(int64_t)j * r + i] = get(off_lf(kind, pd, j, i));
   }
   return PKV_OK;
 }
 
 int32_t pkv_factor_part_bytes(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t dtype,
                               int64_t* bytes) {
-  if (!bytes || (kind != PKV_KEYS && kind != PKV_VALUES)) return PKV_ERR_INVALID_ARG;
+  if (!bytes || (kind != PKV_KEYS && kind != PKV_VALUES && kind != PKV_KEYS_PRE_ROPE))
+    return PKV_ERR_INVALID_ARG;
   if (P != kP || d != kD) return PKV_ERR_UNSUPPORTED;
   if (r < 1 || r > kP) return PKV_ERR_INVALID_ARG;
   if (dtype == PKV_BF16 || dtype == PKV_F32) {
@@ -425,7 +432,7 @@ int32_t pkv_factor_part_bytes(int32_t kind, int32_t P, int32_t d, int32_t r, int
     return PKV_OK;
   }
   if (dtype != PKV_BF16_INT4) return PKV_ERR_INVALID_ARG;
-  if (r > kQ4MaxRank) return PKV_ERR_UNSUPPORTED;
+  if (r > kQ4MaxRank || kind == PKV_KEYS_PRE_ROPE) return PKV_ERR_UNSUPPORTED;
   const Q4Dims q = q4_dims(r);
   *bytes = kind == PKV_KEYS ? q.k_bytes : q.v_bytes;
   return PKV_OK;
@@ -584,6 +591,22 @@ int32_t pkv_cache_set_aux_stream(pkv_cache* c, void* aux_stream) {
   }
   c->aux = (hipStream_t)aux_stream;
   c->early_lo = c->early_hi = 0;
+  return PKV_OK;
+}
+
+int32_t pkv_cache_set_key_rope(pkv_cache* c, const float* inv_freq, int32_t n_freq) {
+  if (!c) return PKV_ERR_INVALID_ARG;
+  if (c->shape.dtype == PKV_BF16_INT4) return PKV_ERR_UNSUPPORTED;
+  if (c->T != 0) return PKV_ERR_INVALID_ARG;
+  if (!inv_freq) {
+    c->rope = 0;
+    return PKV_OK;
+  }
+  if (n_freq != kD / 2) return PKV_ERR_INVALID_ARG;
+  for (int m = 0; m < kD / 2; ++m)
+    if (!std::isfinite(inv_freq[m])) return PKV_ERR_INVALID_ARG;
+  std::memcpy(c->rope_freq, inv_freq, sizeof(c->rope_freq));
+  c->rope = 1;
   return PKV_OK;
 }
 

@@ -334,7 +334,7 @@ __device__ void compress_one(const CompressJob& job, int64_t n, CompressShared& 
             const float val = (i < r) ? R[mi][m][v] * inv : 0.f;
             int64_t idx;
             if (!packed) idx = n * (int64_t)r * kD + (int64_t)i * kD + c;
-            else idx = (kind == 0) ? off_rf_k(pd, i, c) : off_rf_v(pd, i, c);
+            else idx = off_rf(kind == 0 ? job.key_part_kind : PKV_VALUES, pd, i, c);
             store_elem(packed ? (void*)part : job.rf, idx, job.out_dtype, val);
           }
         }

@@ -113,7 +113,7 @@ struct FactorDst {
     pd = pack_dims(p.r);
     r = p.r;
     r_store = packed ? 8 * pd.n8 : p.r;
-    kind = p.kind;
+    kind = p.kind == 0 ? job.key_part_kind : PKV_VALUES;  // part layout
     n = n_;
     if (packed) {
       rf = lf = factor_part(job, p);
@@ -124,11 +124,11 @@ struct FactorDst {
   }
   __device__ int64_t rf_idx(int i, int c) const {
     if (!packed) return n * (int64_t)r * kD + (int64_t)i * kD + c;
-    return kind == 0 ? off_rf_k(pd, i, c) : off_rf_v(pd, i, c);
+    return off_rf(kind, pd, i, c);
   }
   __device__ int64_t lf_idx(int j, int i) const {
     if (!packed) return n * (int64_t)kP * r + (int64_t)j * r + i;
-    return kind == 0 ? off_lf_k(pd, j, i) : off_lf_v(pd, j, i);
+    return off_lf(kind, pd, j, i);
   }
 };
 

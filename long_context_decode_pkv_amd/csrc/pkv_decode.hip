@@ -23,6 +23,9 @@
 //
 // fp32 path and shapes the matrix-core kernel does not cover
 // (decode_valu_kernel): plain fp32 VALU arithmetic, one workgroup per split.
+#include <cmath>
+#include <cstring>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -50,6 +53,8 @@ struct DecodeArgs {
   int64_t page_bytes, k_part_bytes;
   int64_t cost_dense, cost_fact;
   float qscale;
+  int rope;                     // pre-RoPE keys: rotate each key at its position
+  float rope_freq[kD / 2];
 };
 
 // Work list of one (sequence, KV head): D dense pages (sink pages first, then
@@ -482,6 +487,7 @@ struct Bf16Factors {
   // 51.8 -> 50.7 us.
   static constexpr bool kKeyDoubleBuffer = N8 <= 4 || N8 >= 7;
   static constexpr bool kLdsRing = false;
+  static constexpr bool kRope = false;
   static constexpr int kLdsBytes = 0;
   using K = KRegs<N8>;
   using V = VRegs<N8>;
@@ -508,6 +514,248 @@ struct Bf16Factors {
     fact_keys<N8>(st, R, Q.qb, q4, rem, pb);
   }
   __device__ static void values(SoftState& st, const V& R, const Probs& pb, int q4, float rem) {
+    fact_values<N8>(st, R, pb, rem);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Pre-RoPE keys (App. D.3): the key of token t enters its score rotated by the
+// rotary embedding at position t, channel pair (m, m + 64) turning by the
+// angle t theta_m.  A page starting at position p0 is scored as
+//   s_j = (R(p0)^T q) . (R(j) k_j),
+// so the query turns back by the page start once per page, and each key by
+// its offset j < 64 in the page, whose cos / sin the workgroup tabulates in
+// LDS at start.  Keys of factorized pages are reconstructed on the matrix
+// cores 16 tokens at a time (K_p^T = Rf_K^T Lf_K^T, with Rf_K stored
+// channel-major for it), rotated in fp32 and scored on the fp16 matrix cores
+// against the hi/lo query operand; dense pages take the same route from their
+// stored rows.  The rotated keys are rounded to fp16 (11-bit significand;
+// bf16's 8 bits cost up to ~9e-3 of the output on keys with outlier
+// channels) after a 2^-8 scaling folded into the cos / sin table, which keeps
+// keys up to ~1.6e7 in range; the query carries the 2^8.
+//
+// Channel order: a lane (column n = lane & 15, quad q4 = lane >> 4) holds
+// channels 16 ct + 4 q4 + v (ct < 8, v < 4) of one token -- the rows of the
+// reconstruction's output tiles -- so that the pair partners (ct, ct + 4)
+// share a lane; k-step ks of the score contraction takes tiles 2 ks and
+// 2 ks + 1 (element 4 (ct & 1) + v), and the query operand follows suit.
+
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+
+constexpr float kRopeKeyScale = 1.f / 256.f;  // folded into the offset table
+constexpr float kRopeQueryScale = 256.f;      // and undone on the query
+
+__device__ inline floatx4 mfma_f16(halfx8 a, halfx8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// fp16 part of x on lanes whose column is < 8, fp16 remainder on the others
+__device__ inline _Float16 split_f16(float x, float rem_lane) {
+  const float h = (float)(_Float16)x;
+  return (_Float16)__builtin_fmaf(-rem_lane, h, x);
+}
+
+// cos / sin of pos * theta: the angle is formed and reduced modulo 2 pi in
+// double precision (two-part 2 pi), the functions evaluated in float.
+__device__ inline void rope_sincos(int64_t pos, float theta, float& c, float& s) {
+  const double a = (double)pos * (double)theta;
+  const double k = rint(a * 0.15915494309189535);
+  double red = fma(-k, 6.283185307179586, a);
+  red = fma(-k, 2.4492935982947064e-16, red);
+  sincosf((float)red, &s, &c);
+}
+
+// cos / sin (j theta_m) for every in-page offset j and frequency m: row j
+// holds groups [ct][q4] of {cos v0..3, sin v0..3}, padded by 16 bytes so that
+// the 16 rows a lane quad reads fall in different banks; and, per wave,
+// cos / sin (p0 theta_m) of its current page.
+constexpr int kRopeRow = 8 * kD / 2 / 4 + 4;  // floats per table row
+struct RopeLds {
+  float table[kP][kRopeRow];
+  float base[kWaves][2][kD / 2];
+};
+
+__device__ inline void rope_table_fill(RopeLds& L, const float* freq) {
+  for (int idx = threadIdx.x; idx < kP * (kD / 2); idx += blockDim.x) {
+    const int j = idx / (kD / 2), m = idx % (kD / 2);
+    float c, s;
+    rope_sincos(j, freq[m], c, s);
+    float* grp = &L.table[j][((m >> 4) * 4 + ((m >> 2) & 3)) * 8];
+    grp[m & 3] = c * kRopeKeyScale;
+    grp[4 + (m & 3)] = s * kRopeKeyScale;
+  }
+}
+
+// The rotated query R(p0)^T q of a page starting at p0, as the hi/lo operand
+// (qs: the lane's channels in the order above, unrotated).  Lane m computes
+// cos / sin (p0 theta_m) into the wave's LDS slot; LDS operations of one wave
+// complete in order, so the reads below see it.
+__device__ inline void rope_page_query(halfx8 (&qb)[4], const float (&qs)[4][8], int64_t p0,
+                                       const float* freq, float (&base)[2][kD / 2], int lane, float rem) {
+  const int q4 = lane >> 4;
+  float c, s;
+  rope_sincos(p0, freq[lane], c, s);
+  base[0][lane] = c;
+  base[1][lane] = s;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int m0 = 16 * (2 * ks + half) + 4 * q4;
+      const float4 cb = *(const float4*)&base[0][m0];
+      const float4 sb = *(const float4*)&base[1][m0];
+      const float cv[4] = {cb.x, cb.y, cb.z, cb.w}, sv[4] = {sb.x, sb.y, sb.z, sb.w};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int e = 4 * half + v;
+        const float x = qs[ks][e], y = qs[ks + 2][e];
+        qb[ks][e] = split_f16(__builtin_fmaf(y, sv[v], x * cv[v]), rem);
+        qb[ks + 2][e] = split_f16(__builtin_fmaf(-x, sv[v], y * cv[v]), rem);
+      }
+    }
+  }
+}
+
+// lo[v], hi[v]: fp32 key channels 16 ct + 4 q4 + v and 64 more (ct < 4) of
+// the lane's token, at offset j in its page (row: table row j) -> rotated by
+// R(j), scaled by 2^-8, into their fp16 slots of the score contraction's A
+// operand (channel tile ct' -> step ct' / 2, elements 4 (ct' & 1) + v).
+__device__ inline void rope_key_pair(const floatx4& lo, const floatx4& hi, const float* row, int ct, int q4,
+                                     halfx8 (&ka)[4]) {
+  const float4 co = *(const float4*)(row + (ct * 4 + q4) * 8);
+  const float4 si = *(const float4*)(row + (ct * 4 + q4) * 8 + 4);
+  const float cv[4] = {co.x, co.y, co.z, co.w}, sv[4] = {si.x, si.y, si.z, si.w};
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float x = lo[v], y = hi[v];
+    ka[ct >> 1][4 * (ct & 1) + v] = (_Float16)__builtin_fmaf(-y, sv[v], x * cv[v]);
+    ka[(ct >> 1) + 2][4 * (ct & 1) + v] = (_Float16)__builtin_fmaf(x, sv[v], y * cv[v]);
+  }
+}
+
+// Score tile of a page from the rotated key operand and the hi/lo query.
+__device__ inline floatx4 rope_scores(const halfx8 (&ka)[4], const halfx8 (&qb)[4]) {
+  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) acc = mfma_f16(ka[ks], qb[ks], acc);
+  return acc;
+}
+
+// A dense page of pre-RoPE keys: rows loaded in the rotation's channel
+// order, rotated by their offsets; values as in dense_page.
+__device__ inline void dense_page_rope(SoftState& st, const uint16_t* Kp, const uint16_t* Vt, int nvalid,
+                                       const halfx8 (&qb)[4], const RopeLds& L, int lane, float rem) {
+  const int n = lane & 15, q4 = lane >> 4;
+  floatx4 as_[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int j = 16 * (n >> 2) + 4 * mt + (n & 3);
+    auto ld4 = [&](int ct) {
+      const u32x2 w = __builtin_nontemporal_load((const u32x2*)(Kp + j * kD + 16 * ct + 4 * q4));
+      return floatx4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+    };
+    halfx8 ka[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) rope_key_pair(ld4(ct), ld4(ct + 4), &L.table[j][0], ct, q4, ka);
+    as_[mt] = rope_scores(ka, qb);
+  }
+  bf16x8 pb[2];
+  softmax_page(st, as_, nvalid, q4, rem, pb);
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      st.o[mt] = mfma(ld16(Vt + (16 * mt + n) * kP + 16 * q4 + 8 * ks), pb[ks], st.o[mt]);
+  }
+}
+
+// Ranks of the matrix-core pre-RoPE path (r <= 32); larger ranks of
+// pre-RoPE caches take the VALU kernel.
+constexpr int kRopeMfmaMaxN8 = 4;
+
+// bf16 factors of pre-RoPE keys: the key part holds Rf_K channel-major (the
+// V part's Rf layout) and Lf_K as in Bf16Factors; the V part as there.
+template <int N8>
+struct RopeFactors {
+  using Dm = FactDims<N8>;
+  static constexpr int kWavesPerSimd = mfma_waves_per_simd(N8);
+  static constexpr bool kKeyDoubleBuffer = false;
+  static constexpr bool kLdsRing = false;
+  static constexpr bool kRope = true;
+  static constexpr int kLdsBytes = 0;
+  struct K {
+    RawW<Dm::W0> rfa[8];
+    RawW<Dm::W1> rfb[Dm::KS2 > 1 ? 8 : 1];
+    RawW<Dm::W0> k2a[4];
+    RawW<Dm::W1> k2b[Dm::KS2 > 1 ? 4 : 1];
+    __device__ bf16x8 rf(int ct, int ks) const { return ks == 0 ? operand(rfa[ct]) : operand(rfb[ct]); }
+    __device__ bf16x8 k2(int mt, int ks) const { return ks == 0 ? operand(k2a[mt]) : operand(k2b[mt]); }
+  };
+  using V = VRegs<N8>;
+  struct Query {
+    float qs[4][8];  // 2^8 q log2(e)/sqrt(d) in the rotation's channel order
+    halfx8 qb[4];    // R(p0)^T q of the current page, fp16 hi/lo columns
+  };
+  using Probs = bf16x8[2];
+  // element e of step ks <- channel 16 (2 ks + e / 4) + 4 q4 + e % 4
+  __device__ static void query(Query& Q, const uint16_t* qp, float qscale_, bool valid, int q4) {
+    const float qscale = qscale_ * kRopeQueryScale;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x2 w = u32x2{0u, 0u};
+        if (valid) w = *(const u32x2*)(qp + 16 * (2 * ks + half) + 4 * q4);
+        Q.qs[ks][4 * half + 0] = __uint_as_float(w.x << 16) * qscale;
+        Q.qs[ks][4 * half + 1] = __uint_as_float(w.x & 0xffff0000u) * qscale;
+        Q.qs[ks][4 * half + 2] = __uint_as_float(w.y << 16) * qscale;
+        Q.qs[ks][4 * half + 3] = __uint_as_float(w.y & 0xffff0000u) * qscale;
+      }
+    }
+  }
+  __device__ static void load_keys(K& R, const uint8_t* kp, int lane) {
+    const uint16_t* p = (const uint16_t*)kp;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const uint16_t* base = p + ct * 64 * Dm::A;
+      ldraw(R.rfa[ct], base + lane * Dm::W0);
+      if constexpr (Dm::KS2 > 1) ldraw(R.rfb[ct], base + 512 + lane * Dm::W1);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const uint16_t* base = p + Dm::K1 + mt * 64 * Dm::A;
+      ldraw(R.k2a[mt], base + lane * Dm::W0);
+      if constexpr (Dm::KS2 > 1) ldraw(R.k2b[mt], base + 512 + lane * Dm::W1);
+    }
+  }
+  __device__ static void load_values(V& R, const uint8_t* vp, int lane) {
+    pkv::load_values<N8>(R, (const uint16_t*)vp, lane);
+  }
+  // token tile mt: K_p^T columns = its 16 tokens, 8 channel tiles of rows
+  __device__ static void keys(SoftState& st, const K& R, const Query& Q, const RopeLds& L, int lane,
+                              float rem, Probs& pb) {
+    const int n = lane & 15, q4 = lane >> 4;
+    floatx4 as_[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const float* row = &L.table[16 * (n >> 2) + 4 * mt + (n & 3)][0];
+      halfx8 ka[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        floatx4 lo = floatx4{0.f, 0.f, 0.f, 0.f}, hi = lo;
+#pragma unroll
+        for (int ks = 0; ks < Dm::KS2; ++ks) {
+          lo = mfma(R.rf(ct, ks), R.k2(mt, ks), lo);
+          hi = mfma(R.rf(ct + 4, ks), R.k2(mt, ks), hi);
+        }
+        rope_key_pair(lo, hi, row, ct, q4, ka);
+      }
+      as_[mt] = rope_scores(ka, Q.qb);
+    }
+    softmax_page(st, as_, kP, q4, rem, pb);
+  }
+  __device__ static void values(SoftState& st, const V& R, const Probs& pb, int, float rem) {
     fact_values<N8>(st, R, pb, rem);
   }
 };
@@ -658,6 +906,7 @@ struct Int4Factors {
   static constexpr int kKBytes = kQK.k_bytes, kPageBytes = kQK.k_bytes + kQV.v_bytes;
   static constexpr int kWavesPerSimd = 2;
   static constexpr bool kKeyDoubleBuffer = false;
+  static constexpr bool kRope = false;
   // Factor pages stream through a per-wave ring of kRingSlots page slots in
   // LDS, filled by direct global -> LDS loads kRingSlots - 1 pages ahead of
   // the page being computed (registers cannot hold that much prefetch).
@@ -858,9 +1107,12 @@ struct WaveMergeLds {
 
 template <class F>
 __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int kLds = F::kLdsBytes > (int)sizeof(WaveMergeLds) ? F::kLdsBytes : (int)sizeof(WaveMergeLds);
+  constexpr int kLdsMain = F::kLdsBytes > (int)sizeof(WaveMergeLds) ? F::kLdsBytes : (int)sizeof(WaveMergeLds);
+  constexpr int kLdsMainAligned = (kLdsMain + 15) / 16 * 16;
+  constexpr int kLds = kLdsMainAligned + (F::kRope ? (int)sizeof(RopeLds) : 0);
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   WaveMergeLds& mg = *reinterpret_cast<WaveMergeLds*>(lds);
+  RopeLds& rl = *reinterpret_cast<RopeLds*>(lds + kLdsMainAligned);  // pre-RoPE formats only
   auto& sm_o = mg.o;
   auto& sm_m = mg.m;
   auto& sm_l = mg.l;
@@ -905,6 +1157,16 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
       F::load_values(vr, vptr(f0), lane);
       if (f0 + 1 < e1) F::load_keys(kb, kptr(f0 + 1), lane);
     }
+  } else if constexpr (F::kRope) {
+    // the first page's loads overlap the rotation table's construction
+    if (f0 < e1) {
+      F::load_keys(ka, kptr(f0), lane);
+      F::load_values(vr, vptr(f0), lane);
+    }
+  }
+  if constexpr (F::kRope) {
+    rope_table_fill(rl, a.rope_freq);
+    __syncthreads();
   }
 
   // query q * log2(e)/sqrt(d) of the lane's channels 32 ks + 8 q4 + e; as
@@ -937,7 +1199,10 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
   // so that K(e + 2) streams in from the end of page e's key half
   int64_t e = f0;
   typename F::Query fq;
-  F::query(fq, qs, qb);
+  if constexpr (F::kRope)
+    F::query(fq, (const uint16_t*)a.q + ((int64_t)b * Hq + (int64_t)h * a.G + g) * kD, a.qscale, g < a.G, q4);
+  else
+    F::query(fq, qs, qb);
   if (e < e1) {
     if constexpr (F::kLdsRing) {
       // ring slot s holds pages e with e = s (mod kRingSlots); pages up to
@@ -983,11 +1248,18 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
       }
     } else {
       typename F::K& kr = ka;
-      F::load_keys(kr, kptr(e), lane);
-      F::load_values(vr, vptr(e), lane);
+      if constexpr (!F::kRope) {  // (pre-RoPE formats loaded the first page above)
+        F::load_keys(kr, kptr(e), lane);
+        F::load_values(vr, vptr(e), lane);
+      }
       for (; e < e1; ++e) {
         typename F::Probs pb;
-        F::keys(st, kr, fq, q4, rem, pb);
+        if constexpr (F::kRope) {
+          rope_page_query(fq.qb, fq.qs, unit_page(wl, a, e) * kP, a.rope_freq, rl.base[wave], lane, rem);
+          F::keys(st, kr, fq, rl, lane, rem, pb);
+        } else {
+          F::keys(st, kr, fq, q4, rem, pb);
+        }
         const bool more = e + 1 < e1;
         if (more) F::load_keys(kr, kptr(e + 1), lane);
         F::values(st, vr, pb, q4, rem);
@@ -999,7 +1271,7 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
   // dense pages of this range (after the factorized ones: the query operand
   // of the dense contraction is rebuilt here rather than kept live)
   bf16x8 qd[4];
-  F::dense_query(qd, fq, rem);
+  if constexpr (!F::kRope) F::dense_query(qd, fq, rem);
   const int64_t d_end = e1 < wl.D ? e1 : wl.D;
   for (int64_t e = e0; e < d_end; ++e) {
     const int64_t p = unit_page(wl, a, e);
@@ -1015,7 +1287,12 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
       Vt = (const uint16_t*)a.win_v + (bh * (a.n_w + 1) + slot) * ppg;
     }
     const int64_t left = a.T - p * kP;
-    dense_page(st, Kp, Vt, (int)(left < kP ? left : kP), qd, lane, rem);
+    if constexpr (F::kRope) {
+      rope_page_query(fq.qb, fq.qs, p * kP, a.rope_freq, rl.base[wave], lane, rem);
+      dense_page_rope(st, Kp, Vt, (int)(left < kP ? left : kP), fq.qb, rl, lane, rem);
+    } else {
+      dense_page(st, Kp, Vt, (int)(left < kP ? left : kP), qd, lane, rem);
+    }
   }
 
 
@@ -1073,8 +1350,10 @@ __device__ inline float ld_elem(const void* base, int64_t idx) {
     return ((const float*)base)[idx];
 }
 
-template <typename Elem>
+template <typename Elem, bool kRope>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+  // pre-RoPE keys: the page's keys, stored or reconstructed, then rotated
+  __shared__ float kr[kRope ? kP : 1][kRope ? kD + 1 : 1];
   __shared__ float qs[kMaxG][kD];
   __shared__ float ts[kMaxG][kP];
   __shared__ float ss[kMaxG][kP];
@@ -1112,7 +1391,49 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     const int64_t rem = a.T - p * kP;
     const int nv = dense ? (int)(rem < kP ? rem : kP) : kP;
     const void *Kp = nullptr, *Vt = nullptr, *kpart = nullptr, *vpart = nullptr;
-    if (dense) {
+    if (kRope) {
+      const int64_t ppg = (int64_t)kP * kD;
+      if (!dense) {
+        kpart = a.fac + (bh * a.F_max + slot) * a.page_bytes;
+        vpart = (const uint8_t*)kpart + a.k_part_bytes;
+      } else if (cls == PKV_PAGE_SINK) {
+        Kp = (const uint8_t*)a.sink_k + (bh * a.n_s + slot) * ppg * kEsz;
+        Vt = (const uint8_t*)a.sink_v + (bh * a.n_s + slot) * ppg * kEsz;
+      } else {
+        Kp = (const uint8_t*)a.win_k + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
+        Vt = (const uint8_t*)a.win_v + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
+      }
+      for (int idx = tid; idx < kP * kD; idx += 256) {
+        const int j = idx / kD, c = idx % kD;
+        float x = 0.f;
+        if (dense) {
+          if (j < nv) x = ld_elem<Elem>(Kp, (int64_t)j * kD + c);
+        } else {
+          for (int i = 0; i < a.r_k; ++i)
+            x += ld_elem<Elem>(kpart, off_lf_k(pk, j, i)) * ld_elem<Elem>(kpart, off_rf_k_cm(pk, i, c));
+        }
+        kr[j][c] = x;
+      }
+      __syncthreads();
+      for (int idx = tid; idx < kP * (kD / 2); idx += 256) {
+        const int j = idx / (kD / 2), m = idx % (kD / 2);
+        float cs, sn;
+        rope_sincos(p * kP + j, a.rope_freq[m], cs, sn);
+        const float x = kr[j][m], y = kr[j][m + kD / 2];
+        kr[j][m] = x * cs - y * sn;
+        kr[j][m + kD / 2] = y * cs + x * sn;
+      }
+      __syncthreads();
+      for (int idx = tid; idx < G * kP; idx += 256) {
+        const int g = idx / kP, j = idx % kP;
+        float acc = -INFINITY;
+        if (j < nv) {
+          acc = 0.f;
+          for (int c = 0; c < kD; ++c) acc += qs[g][c] * kr[j][c];
+        }
+        ss[g][j] = acc;
+      }
+    } else if (dense) {
       const int64_t ppg = (int64_t)kP * kD;
       if (cls == PKV_PAGE_SINK) {
         Kp = (const uint8_t*)a.sink_k + (bh * a.n_s + slot) * ppg * kEsz;
@@ -1224,6 +1545,8 @@ struct MergeArgs {
   int32_t* table_w;
   int64_t app_page;
   int32_t app_entry;
+  int rope;                       // pre-RoPE keys: k_new turns by its position's angles
+  float rope_c[kD / 2], rope_s[kD / 2];
 };
 
 __device__ inline float load_elem(const void* p, int64_t i, int dtype) {
@@ -1260,7 +1583,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
     const int Hq = m.G * m.Hkv;
     const int hq = (int)(row % Hq);
     bh = (row / Hq) * m.Hkv + hq / m.G;
-    if (tid < kD) qk = load_elem(m.q, row * kD + tid, m.dtype) * load_elem(m.k_new, bh * kD + tid, m.dtype);
+    if (tid < kD) {
+      float kk = load_elem(m.k_new, bh * kD + tid, m.dtype);
+      if (m.rope) {  // pair (c, c + d/2) of the new key, rotated at its position
+        const int mm = tid & (kD / 2 - 1);
+        const float other = load_elem(m.k_new, bh * kD + (tid ^ (kD / 2)), m.dtype);
+        kk = tid < kD / 2 ? __builtin_fmaf(-other, m.rope_s[mm], kk * m.rope_c[mm])
+                          : __builtin_fmaf(other, m.rope_s[mm], kk * m.rope_c[mm]);
+      }
+      qk = load_elem(m.q, row * kD + tid, m.dtype) * kk;
+    }
   }
   float4 vnew = {0.f, 0.f, 0.f, 0.f};
   if (m.k_new && tid < kD / 4) {
@@ -1372,9 +1704,10 @@ int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact) {
   // better than more waves (Qwen3-32B-shaped 128K layer: 32 splits 48.0 us,
   // 64 splits 49.5 us); INT4 pages are a third of the bytes and compute-bound
   // per wave, so both workgroups per CU pay off (same layer: 32 splits
-  // 37.1 us, 64 splits 35.0 us).
+  // 37.1 us, 64 splits 35.0 us), and so do pre-RoPE keys, whose rotation is
+  // vector-ALU work (same layer: 32 splits 72.6 us, 64 splits 64.4 us).
   const int wps = g.dtype == PKV_BF16 ? mfma_waves_per_simd((g.r_k > g.r_v ? g.r_k + 7 : g.r_v + 7) / 8) : 2;  // INT4 and fp32: 2
-  const int64_t min_run = g.dtype == PKV_BF16_INT4 ? 8 : 16;
+  const int64_t min_run = (g.dtype == PKV_BF16_INT4 || g.rope) ? 8 : 16;
   int64_t s = (256LL * wps + bh - 1) / bh;
   while (s > 1 && pages < min_run * 4 * s && (s / 2) * bh >= 256) s /= 2;
   const int64_t cap = (pages + 3) / 4;  // at least ~4 pages per workgroup
@@ -1403,6 +1736,15 @@ hipError_t launch_merge(const CacheGeom& g, const AttnJob& job, hipStream_t stre
   m.table_w = (int32_t*)(g.base + g.lay.page_table);
   m.app_page = job.app_page;
   m.app_entry = job.app_entry;
+  m.rope = g.rope && job.k_new;
+  if (m.rope) {
+    const double pos = (double)(job.app_page * kP + job.app_row);
+    for (int mm = 0; mm < kD / 2; ++mm) {
+      const double ang = pos * (double)g.rope_freq[mm];
+      m.rope_c[mm] = (float)std::cos(ang);
+      m.rope_s[mm] = (float)std::sin(ang);
+    }
+  }
   if (job.k_new) {
     const int64_t ppg_bytes = (int64_t)kP * kD * g.lay.elem_bytes;
     const int64_t p = job.app_page;
@@ -1450,6 +1792,8 @@ hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t st
   a.cost_dense = 2 * g.lay.dense_page_bytes / 64;
   a.cost_fact = g.lay.factor_page_bytes / 64;
   a.qscale = kLog2e / sqrtf((float)kD);
+  a.rope = g.rope;
+  std::memcpy(a.rope_freq, g.rope_freq, sizeof(a.rope_freq));
 
   const dim3 grid(job.n_split, g.Hkv, g.B);
   const KernelEvents ev = take_kernel_events();
@@ -1471,11 +1815,16 @@ hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t st
       default:
         return hipErrorInvalidValue;
     }
-  } else if (g.dtype == PKV_BF16 && n8k == n8v) {
-    switch (n8k) {
+  } else if (g.dtype == PKV_BF16 && n8k == n8v && (!g.rope || n8k <= kRopeMfmaMaxN8)) {
+    switch (n8k * 2 + (g.rope ? 1 : 0)) {
 #define PKV_CASE(N)                                                                                     \
-  case N:                                                                                               \
+  case 2 * N:                                                                                           \
     hipExtLaunchKernelGGL(decode_mfma_kernel<Bf16Factors<N>>, grid, dim3(256), 0, stream, ev.start, ev.stop, \
+                          0, a);                                                                        \
+    break;
+#define PKV_ROPE(N)                                                                                     \
+  case 2 * N + 1:                                                                                       \
+    hipExtLaunchKernelGGL(decode_mfma_kernel<RopeFactors<N>>, grid, dim3(256), 0, stream, ev.start, ev.stop, \
                           0, a);                                                                        \
     break;
       PKV_CASE(1)
@@ -1486,14 +1835,25 @@ hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t st
       PKV_CASE(6)
       PKV_CASE(7)
       PKV_CASE(8)
+      PKV_ROPE(1)
+      PKV_ROPE(2)
+      PKV_ROPE(3)
+      PKV_ROPE(4)
+#undef PKV_ROPE
 #undef PKV_CASE
       default:
         return hipErrorInvalidValue;
     }
   } else if (g.dtype == PKV_BF16) {
-    hipExtLaunchKernelGGL(decode_valu_kernel<uint16_t>, grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a);
+    if (g.rope)
+      hipExtLaunchKernelGGL((decode_valu_kernel<uint16_t, true>), grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a);
+    else
+      hipExtLaunchKernelGGL((decode_valu_kernel<uint16_t, false>), grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a);
   } else {
-    hipExtLaunchKernelGGL(decode_valu_kernel<float>, grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a);
+    if (g.rope)
+      hipExtLaunchKernelGGL((decode_valu_kernel<float, true>), grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a);
+    else
+      hipExtLaunchKernelGGL((decode_valu_kernel<float, false>), grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a);
   }
   return hipGetLastError();
 }

@@ -120,6 +120,20 @@ __host__ __device__ inline int64_t off_rf_v(const PackDims& p, int i, int c) {
   return p.v1 + (int64_t)mt * 64 * p.A + 512 * ks + lane * w + e;
 }
 
+// Rf_K of a pre-RoPE cache's key part (PKV_KEYS_PRE_ROPE): channel-major,
+// in V2's order, at the start of the part (Lf_K follows at K2's offset).
+__host__ __device__ inline int64_t off_rf_k_cm(const PackDims& p, int i, int c) {
+  return off_rf_v(p, i, c) - p.v1;
+}
+
+// The offsets of a part of kind PKV_KEYS / PKV_VALUES / PKV_KEYS_PRE_ROPE.
+__host__ __device__ inline int64_t off_rf(int kind, const PackDims& p, int i, int c) {
+  return kind == PKV_KEYS ? off_rf_k(p, i, c) : (kind == PKV_VALUES ? off_rf_v(p, i, c) : off_rf_k_cm(p, i, c));
+}
+__host__ __device__ inline int64_t off_lf(int kind, const PackDims& p, int j, int i) {
+  return kind == PKV_VALUES ? off_lf_v(p, j, i) : off_lf_k(p, j, i);
+}
+
 // --------------------------------------------------------------------------
 // INT4 factor part layout (PuzzleKV Sec. 4.3): Lt = U_r Sigma_r^(1/2) and
 // Rt = Sigma_r^(1/2) W_r^T, each held as symmetric 4-bit codes c in -7..7
@@ -261,6 +275,7 @@ struct CompressJob {
   int in_dtype;                 // pkv_dtype
   int rank[2];                  // per kind
   int out_dtype;
+  int key_part_kind;            // layout of kind-0 parts: PKV_KEYS or PKV_KEYS_PRE_ROPE
   // packed output (cache): fac + (bh * fac_bh_pages + slot) * page_bytes + kind * k_part_bytes
   uint8_t* fac;
   int64_t fac_bh_pages;
@@ -295,6 +310,8 @@ struct CacheGeom {
   int r_k, r_v;
   uint8_t* base;
   pkv_layout lay;
+  int rope;                     // keys are pre-RoPE (pkv_cache_set_key_rope)
+  float rope_freq[kD / 2];
 };
 
 hipError_t launch_prefill_dense(const CacheGeom& g, const void* K, const void* V, int64_t T,

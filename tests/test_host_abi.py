@@ -78,7 +78,7 @@ def test_packed_layout_is_a_bijection(r):
     n = pkv.factor_part_elems(r)
     r8 = -(-r // 8) * 8
     assert n == r8 * (64 + 128)
-    for kind in (pkv.KEYS, pkv.VALUES):
+    for kind in (pkv.KEYS, pkv.VALUES, pkv.KEYS_PRE_ROPE):
         # encode each entry's identity in its value, pack, and check coverage
         Lf = np.arange(64 * r8, dtype=np.float32).reshape(64, r8)[:, :r] + 1
         Rf = np.arange(r8 * 128, dtype=np.float32).reshape(r8, 128)[:r] + 1 + 64 * r8
@@ -219,3 +219,44 @@ def test_prefill_chunk_validation_without_gpu():
         assert (T.value, nf.value, pend.value) == (0, 0, 0)
     finally:
         L.pkv_cache_destroy(h)
+
+
+@pytest.mark.parametrize("r", [8, 16, 24, 40])
+def test_pre_rope_key_part_is_channel_major(r):
+    """A pre-RoPE key part holds Rf_K in the value part's Rf order at its
+    start, and Lf_K where a key part holds it."""
+    g = np.random.default_rng(r)
+    Lf = g.standard_normal((64, r)).astype(np.float32)
+    Rf = g.standard_normal((r, 128)).astype(np.float32)
+    n8 = -(-r // 8)
+    k1 = 8 * n8 * 128  # Rf elements of a part
+    pre = pkv.pack_factors(pkv.KEYS_PRE_ROPE, r, pkv.F32, Lf, Rf)
+    val = pkv.pack_factors(pkv.VALUES, r, pkv.F32, np.zeros_like(Lf), Rf)
+    key = pkv.pack_factors(pkv.KEYS, r, pkv.F32, Lf, np.zeros_like(Rf))
+    v1 = 8 * n8 * 64
+    np.testing.assert_array_equal(pre[:k1], val[v1:])
+    np.testing.assert_array_equal(pre[k1:], key[k1:])
+    assert pkv.factor_part_bytes(pkv.KEYS_PRE_ROPE, r, pkv.BF16) == pkv.factor_part_bytes(pkv.KEYS, r, pkv.BF16)
+
+
+def test_set_key_rope_validation_without_gpu():
+    L = pkv.lib()
+    f = np.full(64, 0.5, np.float32)
+    fp = f.ctypes.data_as(ctypes.c_void_p)
+    assert L.pkv_cache_set_key_rope(None, fp, 64) == 1
+    for dtype, ok in ((pkv.BF16, 0), (pkv.F32, 0), (pkv.BF16_INT4, 2)):
+        sh = _shape(dtype=dtype)
+        lay = pkv.cache_layout(sh)
+        h = ctypes.c_void_p()
+        assert L.pkv_cache_create(ctypes.byref(sh), ctypes.c_void_p(256 * 1000), lay["total_bytes"],
+                                  ctypes.byref(h)) == 0
+        try:
+            assert L.pkv_cache_set_key_rope(h, fp, 64) == ok
+            if ok == 0:
+                assert L.pkv_cache_set_key_rope(h, fp, 63) == 1
+                bad = f.copy()
+                bad[7] = np.nan
+                assert L.pkv_cache_set_key_rope(h, bad.ctypes.data_as(ctypes.c_void_p), 64) == 1
+                assert L.pkv_cache_set_key_rope(h, None, 0) == 0
+        finally:
+            L.pkv_cache_destroy(h)
