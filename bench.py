@@ -462,6 +462,94 @@ def bench_compress(args):
     return out
 
 
+RAGGED_LENGTHS = [32768, 28672, 24576, 20480, 16384, 12288, 8192, 4096]
+
+
+def bench_ragged_batch(args):
+    """Serving batch: 8 sequences of different lengths (32K down to 4K) of the
+    Llama-3.1-8B-shaped layer, one cache each, attended in one
+    pkv_decode_attn_batch call per layer step (attention only: the appends
+    and promotions of a step are per-cache calls, timed by the decode
+    workloads).  Compared with one pkv_decode_attn per cache."""
+    import torch
+    import synth
+    import long_context_decode_pkv_amd as pkv
+
+    cfg = dict(synth.CONFIGS[2])
+    Hq, Hkv, d = cfg["Hq"], cfg["Hkv"], cfg["d"]
+    NL = args.layers
+    Tm = max(RAGGED_LENGTHS)
+    inp = cached_inputs(2, Tm, workers=args.workers)  # sequence i: batch row i, first T_i tokens
+    dt = cfg["dtype"]
+    layers = []
+    for _ in range(NL):
+        cs = []
+        for i, T in enumerate(RAGGED_LENGTHS):
+            c = pkv.Cache(batch=1, n_q_heads=Hq, n_kv_heads=Hkv, rank_k=cfg["r_k"], rank_v=cfg["r_v"],
+                          sink=cfg["s"], window=cfg["w"], max_tokens=T, dtype=dt)
+            c.prefill(to_dev(np.ascontiguousarray(inp["K"][i:i + 1, :, :T]), dt),
+                      to_dev(np.ascontiguousarray(inp["V"][i:i + 1, :, :T]), dt))
+            cs.append(c)
+        layers.append(cs)
+    n = len(RAGGED_LENGTHS)
+    q = to_dev(synth.step_queries(2, 0, n, Hq, d, dt), dt)
+    out = torch.empty((n, Hq, d), dtype=torch.float32, device="cuda:0")
+    nb = max(c.workspace_bytes(0) for cs in layers for c in cs) * n
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+    torch.cuda.synchronize()
+
+    def batched(cs):
+        pkv.decode_batch(cs, q, out=out, workspace=ws)
+
+    def separate(cs):
+        for i, c in enumerate(cs):
+            c.decode(q[i:i + 1], out=out[i:i + 1], workspace=ws)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            for cs in layers:
+                fn(cs)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(args.steps):
+            for cs in layers:
+                fn(cs)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / (args.steps * NL)
+
+    t_batch = timed(batched)
+    t_sep = timed(separate)
+    # the batched partial kernel's own duration
+    durs = []
+    for _ in range(args.steps):
+        for cs in layers:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            pkv.time_next_kernel(a, b)
+            batched(cs)
+            durs.append((a, b))
+    torch.cuda.synchronize()
+    dur = float(np.mean([a.elapsed_time(b) * 1e-3 for a, b in durs]))
+    nbytes = sum(decode_bytes(cfg, 1, Hkv, Hq, c.state()[0], c.state()[1]) for c in layers[0])
+    achieved = nbytes / dur / 1e9
+    log(f"ragged batch of {n}: batched {t_batch * 1e6:.1f} us, separate {t_sep * 1e6:.1f} us per layer; "
+        f"partial kernel {dur * 1e6:.1f} us, {nbytes / 1e6:.1f} MB -> {achieved:.0f} GB/s")
+    return {
+        "metric": "decode-attn tokens/s (one layer: attention for a batch of sequences of different lengths)",
+        "value": n / t_batch, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": t_batch * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 storage, f32 math", "data": "synthetic (seeded generator, workload-2 recipe)",
+        "config": {"workload": "llama3.1-8b-ragged-batch", "sequences": n, "lengths": RAGGED_LENGTHS,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "page_len": cfg["P"], "rank_k": cfg["r_k"],
+                   "rank_v": cfg["r_v"], "sink": cfg["s"], "window": cfg["w"], "layer_caches_rotated": NL,
+                   "step": "pkv_decode_attn_batch over one cache per sequence (attention only)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode_mfma_kernel (batched launch)", "launch_us_mean": dur * 1e6,
+                     "bytes_per_launch": nbytes},
+        "separate_calls_us_per_layer": t_sep * 1e6,
+    }
+
+
 def bench_copy(args):
     """Plain device-to-device copy of a known size: the reference that scales
     the HBM traffic counters (FETCH_SIZE, WRITE_SIZE) read under rocprofv3."""
@@ -492,7 +580,7 @@ def main():
     ap.add_argument("--workload", default="qwen3-32b-layer-128k",
                     choices=["qwen3-32b-layer-128k", "llama3.1-8b-layer", "qwen3-32b-layer-128k-int4",
                              "llama3.1-8b-layer-int4", "qwen3-32b-layer-128k-prerope",
-                             "llama3.1-8b-layer-prerope", "compress", "copy"])
+                             "llama3.1-8b-layer-prerope", "llama3.1-8b-ragged-batch", "compress", "copy"])
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--workers", type=int, default=1)
     ap.add_argument("--layers", type=int, default=4,
@@ -520,6 +608,8 @@ def main():
         res = bench_compress(args)
     elif args.workload == "copy":
         res = bench_copy(args)
+    elif args.workload == "llama3.1-8b-ragged-batch":
+        res = bench_ragged_batch(args)
     else:
         cfg_id = 2 if args.workload.startswith("llama3.1-8b-layer") else 3
         res = bench_decode(args, cfg_id, args.workload, "int4" if args.workload.endswith("-int4") else None,

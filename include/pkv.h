@@ -271,6 +271,30 @@ int32_t pkv_append(pkv_cache* cache, const void* k_new, const void* v_new,
  * per call (Sec. 3.3 (5)).  Errors: NOT_ELIGIBLE when nothing is waiting. */
 int32_t pkv_promote_page(pkv_cache* cache, void* stream);
 
+/*
+ * Attention for a batch of sequences of different lengths (serving batches),
+ * one cache per sequence -- each with its own pools and page table, so each
+ * has its own length T_i and its own page classes; the method of Sec. 3.3 (4)
+ * on every cache.  caches: host array of n handles (1 <= n <= 32) of batch 1
+ * whose shapes agree except max_tokens (heads, d, P, ranks, sink, window,
+ * dtype, pre-RoPE setting and frequencies); each holds T_i >= 1 tokens.
+ * q: device [n][H_q][d] (cache dtype), 16-byte aligned; out: device float32
+ * [n][H_q][d]; query row i attends over cache i.  One partial-attention
+ * launch covers every (cache, KV head, split) for the matrix-core formats
+ * whose K and V ranks pad to the same multiple of 8; other formats launch
+ * once per cache.  Then one merge launch.  workspace: 256-byte aligned
+ * device memory of pkv_decode_batch_workspace_bytes(caches, n, n_split)
+ * bytes.  Every cache's range is cut into n_split parts (0: the library's
+ * count for the batch's longest cache), and row i equals pkv_decode_attn on
+ * cache i with the same n_split bit for bit.
+ * Errors: INVALID_ARG (null or misaligned pointers, n out of range, shapes
+ * that differ, an empty cache), CAPACITY (workspace too small).
+ */
+int32_t pkv_decode_attn_batch(const pkv_cache* const* caches, int32_t n, const void* q, float* out,
+                              void* workspace, uint64_t workspace_bytes, int32_t n_split, void* stream);
+int32_t pkv_decode_batch_workspace_bytes(const pkv_cache* const* caches, int32_t n, int32_t n_split,
+                                         uint64_t* bytes);
+
 /* Workspace bytes pkv_decode_attn needs for n_split splits per (sequence,
  * KV head); n_split = 0 selects the library's choice; at most 512. */
 int32_t pkv_decode_workspace_bytes(const pkv_cache* cache, int32_t n_split, uint64_t* bytes);

@@ -92,6 +92,8 @@ def lib():
         "pkv_decode_step": ([vp, vp, vp, vp, vp, vp, u64, i32, vp], i32),
         "pkv_cache_set_aux_stream": ([vp, vp], i32),
         "pkv_cache_set_key_rope": ([vp, vp, i32], i32),
+        "pkv_decode_attn_batch": ([vp, i32, vp, vp, vp, u64, i32, vp], i32),
+        "pkv_decode_batch_workspace_bytes": ([vp, i32, i32, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -439,3 +441,24 @@ class Cache:
         if kind == KEYS:
             return self.buffer[base: base + kbytes]
         return self.buffer[base + kbytes: base + L["factor_page_bytes"]]
+
+
+def decode_batch(caches, q, out=None, n_split: int = 0, workspace=None):
+    """Attention for a batch of sequences of different lengths, one Cache of
+    batch 1 each (pkv_decode_attn_batch): q [n][H_q][d] -> out [n][H_q][d]
+    float32, row i over caches[i]."""
+    import torch
+    n = len(caches)
+    handles = (ctypes.c_void_p * n)(*[c._h for c in caches])
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=caches[0].device)
+    if workspace is None:
+        nb = ctypes.c_uint64()
+        _check(lib().pkv_decode_batch_workspace_bytes(handles, n, n_split, ctypes.byref(nb)),
+               "pkv_decode_batch_workspace_bytes")
+        workspace = torch.empty(max(int(nb.value), 1), dtype=torch.uint8, device=caches[0].device)
+    _check(lib().pkv_decode_attn_batch(handles, n, _dev_ptr(q, caches[0].elem_code, "q"),
+                                       _dev_ptr(out, None, "out"), ctypes.c_void_p(workspace.data_ptr()),
+                                       workspace.numel(), n_split, _stream(caches[0].device)),
+           "pkv_decode_attn_batch")
+    return out

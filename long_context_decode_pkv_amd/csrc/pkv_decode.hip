@@ -25,6 +25,7 @@
 // (decode_valu_kernel): plain fp32 VALU arithmetic, one workgroup per split.
 #include <cmath>
 #include <cstring>
+#include <type_traits>
 
 #include "pkv_internal.h"
 
@@ -64,15 +65,58 @@ struct WorkList {
   int64_t n_sinkp, first_tail, D, F;
 };
 
-__device__ inline WorkList work_list(const DecodeArgs& a) {
+__device__ inline WorkList work_list(int64_t T, int64_t n_fact, int n_s) {
   WorkList w;
-  const int64_t n_pages = (a.T + kP - 1) / kP;
-  w.n_sinkp = n_pages < a.n_s ? n_pages : a.n_s;
-  w.first_tail = a.n_s + a.n_fact;
+  const int64_t n_pages = (T + kP - 1) / kP;
+  w.n_sinkp = n_pages < n_s ? n_pages : n_s;
+  w.first_tail = n_s + n_fact;
   const int64_t tail = n_pages - w.first_tail;
   w.D = w.n_sinkp + (tail > 0 ? tail : 0);
-  w.F = a.n_fact;
+  w.F = n_fact;
   return w;
+}
+
+// One cache of a batched launch (pkv_decode_attn_batch): its pools, table,
+// length and factor count; its pools hold one sequence.
+struct BatchSeq {
+  const uint8_t* fac;
+  const void* sink_k;
+  const void* sink_v;
+  const void* win_k;
+  const void* win_v;
+  const int32_t* table;
+  int64_t T, n_fact, F_max;
+  int n_split;  // splits of this cache's range (<= the grid's); the others stay empty
+};
+
+struct DecodeBatchArgs {
+  DecodeArgs a;  // what the caches share (their per-cache fields unused)
+  BatchSeq seq[kMaxBatchCaches];
+};
+
+// What a workgroup attends over: sequence b of a cache's pools, or (batched
+// launch) cache b of the batch, whose pools hold sequence 0.
+struct SeqView {
+  const uint8_t* fac;
+  const void* sink_k;
+  const void* sink_v;
+  const void* win_k;
+  const void* win_v;
+  const int32_t* table;
+  int64_t T, n_fact, F_max;
+  int b_pool;
+  int n_split;  // workgroups x < n_split share the range; the others leave empty states
+};
+
+__device__ inline const DecodeArgs& common_args(const DecodeArgs& a) { return a; }
+__device__ inline const DecodeArgs& common_args(const DecodeBatchArgs& x) { return x.a; }
+
+__device__ inline SeqView seq_view(const DecodeArgs& a, int b) {
+  return SeqView{a.fac, a.sink_k, a.sink_v, a.win_k, a.win_v, a.table, a.T, a.n_fact, a.F_max, b, a.n_split};
+}
+__device__ inline SeqView seq_view(const DecodeBatchArgs& x, int b) {
+  const BatchSeq& s = x.seq[b];
+  return SeqView{s.fac, s.sink_k, s.sink_v, s.win_k, s.win_v, s.table, s.T, s.n_fact, s.F_max, 0, s.n_split};
 }
 
 __device__ inline int64_t unit_bound(const WorkList& w, const DecodeArgs& a, int64_t wi,
@@ -573,6 +617,7 @@ constexpr int kRopeRow = 8 * kD / 2 / 4 + 4;  // floats per table row
 struct RopeLds {
   float table[kP][kRopeRow];
   float base[kWaves][2][kD / 2];
+  uint4 q[kWaves][4][64];  // per wave: each lane's unrotated query (bf16 pairs), uint4 w of lane l at [w][l]
 };
 
 __device__ inline void rope_table_fill(RopeLds& L, const float* freq) {
@@ -587,16 +632,32 @@ __device__ inline void rope_table_fill(RopeLds& L, const float* freq) {
 }
 
 // The rotated query R(p0)^T q of a page starting at p0, as the hi/lo operand
-// (qs: the lane's channels in the order above, unrotated).  Lane m computes
-// cos / sin (p0 theta_m) into the wave's LDS slot; LDS operations of one wave
-// complete in order, so the reads below see it.
-__device__ inline void rope_page_query(halfx8 (&qb)[4], const float (&qs)[4][8], int64_t p0,
-                                       const float* freq, float (&base)[2][kD / 2], int lane, float rem) {
+// (qlds: the lane's channels in the order above, unrotated, as bf16 pairs;
+// element e of step ks is half e & 1 of word e / 2 of uint4 ks).  Lane m
+// computes cos / sin (p0 theta_m), times the query's scale, into the wave's
+// LDS slot; LDS operations of one wave complete in order, so the reads below
+// see it.
+__device__ inline void rope_page_query(halfx8 (&qb)[4], const uint4 (&qlds)[4][64], int64_t p0,
+                                       const float* freq, float qscale, float (&base)[2][kD / 2], int lane,
+                                       float rem) {
   const int q4 = lane >> 4;
   float c, s;
   rope_sincos(p0, freq[lane], c, s);
-  base[0][lane] = c;
-  base[1][lane] = s;
+  base[0][lane] = c * qscale;
+  base[1][lane] = s * qscale;
+  uint32_t qw[4][4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint4 w = qlds[ks][lane];
+    qw[ks][0] = w.x;
+    qw[ks][1] = w.y;
+    qw[ks][2] = w.z;
+    qw[ks][3] = w.w;
+  }
+  auto elem = [&](int ks, int e) {
+    const uint32_t w = qw[ks][e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  };
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -608,7 +669,7 @@ __device__ inline void rope_page_query(halfx8 (&qb)[4], const float (&qs)[4][8],
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int e = 4 * half + v;
-        const float x = qs[ks][e], y = qs[ks + 2][e];
+        const float x = elem(ks, e), y = elem(ks + 2, e);
         qb[ks][e] = split_f16(__builtin_fmaf(y, sv[v], x * cv[v]), rem);
         qb[ks + 2][e] = split_f16(__builtin_fmaf(-x, sv[v], y * cv[v]), rem);
       }
@@ -694,24 +755,25 @@ struct RopeFactors {
   };
   using V = VRegs<N8>;
   struct Query {
-    float qs[4][8];  // 2^8 q log2(e)/sqrt(d) in the rotation's channel order
-    halfx8 qb[4];    // R(p0)^T q of the current page, fp16 hi/lo columns
+    float qscale;  // 2^8 log2(e)/sqrt(d), applied with the page's rotation
+    halfx8 qb[4];  // R(p0)^T q of the current page, scaled, fp16 hi/lo columns
   };
   using Probs = bf16x8[2];
   // element e of step ks <- channel 16 (2 ks + e / 4) + 4 q4 + e % 4
-  __device__ static void query(Query& Q, const uint16_t* qp, float qscale_, bool valid, int q4) {
-    const float qscale = qscale_ * kRopeQueryScale;
+  // the lane's query (element e of step ks <- channel 16 (2 ks + e / 4) +
+  // 4 q4 + e % 4) into its LDS slot, read back once per page
+  __device__ static void query(Query& Q, RopeLds& L, int wave, const uint16_t* qp, float qscale, bool valid,
+                               int lane) {
+    const int q4 = lane >> 4;
+    Q.qscale = qscale * kRopeQueryScale;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x2 w = u32x2{0u, 0u};
-        if (valid) w = *(const u32x2*)(qp + 16 * (2 * ks + half) + 4 * q4);
-        Q.qs[ks][4 * half + 0] = __uint_as_float(w.x << 16) * qscale;
-        Q.qs[ks][4 * half + 1] = __uint_as_float(w.x & 0xffff0000u) * qscale;
-        Q.qs[ks][4 * half + 2] = __uint_as_float(w.y << 16) * qscale;
-        Q.qs[ks][4 * half + 3] = __uint_as_float(w.y & 0xffff0000u) * qscale;
+      u32x2 w0 = u32x2{0u, 0u}, w1 = w0;
+      if (valid) {
+        w0 = *(const u32x2*)(qp + 16 * (2 * ks) + 4 * q4);
+        w1 = *(const u32x2*)(qp + 16 * (2 * ks + 1) + 4 * q4);
       }
+      L.q[wave][ks][lane] = uint4{w0.x, w0.y, w1.x, w1.y};
     }
   }
   __device__ static void load_keys(K& R, const uint8_t* kp, int lane) {
@@ -1105,8 +1167,10 @@ struct WaveMergeLds {
   float l[kWaves][kMaxG];
 };
 
-template <class F>
-__global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(DecodeArgs a) {
+template <class F, class KA>
+__global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(KA kargs) {
+  const DecodeArgs& a = common_args(kargs);
+  const SeqView sv = seq_view(kargs, blockIdx.z);
   constexpr int kLdsMain = F::kLdsBytes > (int)sizeof(WaveMergeLds) ? F::kLdsBytes : (int)sizeof(WaveMergeLds);
   constexpr int kLdsMainAligned = (kLdsMain + 15) / 16 * 16;
   constexpr int kLds = kLdsMainAligned + (F::kRope ? (int)sizeof(RopeLds) : 0);
@@ -1123,15 +1187,17 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
   const int g = n & 7;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int Hq = a.Hkv * a.G;
-  const int64_t bh = (int64_t)b * a.Hkv + h;
+  const int64_t bh = (int64_t)sv.b_pool * a.Hkv + h;  // (sequence, KV head) in the pools
 
-  const WorkList wl = work_list(a);
-  const int64_t W = (int64_t)a.n_split * kWaves;
+  const WorkList wl = work_list(sv.T, sv.n_fact, a.n_s);
+  const int64_t W = (int64_t)sv.n_split * kWaves;
   const int64_t wi = (int64_t)split * kWaves + wave;
-  const int64_t e0 = unit_bound(wl, a, wi, W), e1 = unit_bound(wl, a, wi + 1, W);
+  const bool idle = split >= sv.n_split;  // beyond this cache's splits: an empty state
+  const int64_t e0 = idle ? wl.D + wl.F : unit_bound(wl, a, wi, W);
+  const int64_t e1 = idle ? wl.D + wl.F : unit_bound(wl, a, wi + 1, W);
   // the factor slot of logical page n_s + f is f (pages are factorized in
   // order and never revisited), so unit e >= D lives in slot e - D
-  const uint8_t* fac_bh = a.fac + bh * a.F_max * a.page_bytes;
+  const uint8_t* fac_bh = sv.fac + bh * sv.F_max * a.page_bytes;
   auto kptr = [&](int64_t ee) { return fac_bh + (ee - wl.D) * a.page_bytes; };
   auto vptr = [&](int64_t ee) { return fac_bh + (ee - wl.D) * a.page_bytes + a.k_part_bytes; };
   const int64_t f0 = e0 > wl.D ? e0 : wl.D;  // first factorized unit of this wave
@@ -1200,7 +1266,8 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
   int64_t e = f0;
   typename F::Query fq;
   if constexpr (F::kRope)
-    F::query(fq, (const uint16_t*)a.q + ((int64_t)b * Hq + (int64_t)h * a.G + g) * kD, a.qscale, g < a.G, q4);
+    F::query(fq, rl, wave, (const uint16_t*)a.q + ((int64_t)b * Hq + (int64_t)h * a.G + g) * kD, a.qscale,
+             g < a.G, lane);
   else
     F::query(fq, qs, qb);
   if (e < e1) {
@@ -1255,7 +1322,8 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
       for (; e < e1; ++e) {
         typename F::Probs pb;
         if constexpr (F::kRope) {
-          rope_page_query(fq.qb, fq.qs, unit_page(wl, a, e) * kP, a.rope_freq, rl.base[wave], lane, rem);
+          rope_page_query(fq.qb, rl.q[wave], unit_page(wl, a, e) * kP, a.rope_freq, fq.qscale, rl.base[wave],
+                          lane, rem);
           F::keys(st, kr, fq, rl, lane, rem, pb);
         } else {
           F::keys(st, kr, fq, q4, rem, pb);
@@ -1275,20 +1343,20 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(Deco
   const int64_t d_end = e1 < wl.D ? e1 : wl.D;
   for (int64_t e = e0; e < d_end; ++e) {
     const int64_t p = unit_page(wl, a, e);
-    const int32_t ent = a.table[p];
+    const int32_t ent = sv.table[p];
     const int cls = table_class(ent), slot = table_slot(ent);
     const int64_t ppg = (int64_t)kP * kD;
     const uint16_t *Kp, *Vt;
     if (cls == PKV_PAGE_SINK) {
-      Kp = (const uint16_t*)a.sink_k + (bh * a.n_s + slot) * ppg;
-      Vt = (const uint16_t*)a.sink_v + (bh * a.n_s + slot) * ppg;
+      Kp = (const uint16_t*)sv.sink_k + (bh * a.n_s + slot) * ppg;
+      Vt = (const uint16_t*)sv.sink_v + (bh * a.n_s + slot) * ppg;
     } else {
-      Kp = (const uint16_t*)a.win_k + (bh * (a.n_w + 1) + slot) * ppg;
-      Vt = (const uint16_t*)a.win_v + (bh * (a.n_w + 1) + slot) * ppg;
+      Kp = (const uint16_t*)sv.win_k + (bh * (a.n_w + 1) + slot) * ppg;
+      Vt = (const uint16_t*)sv.win_v + (bh * (a.n_w + 1) + slot) * ppg;
     }
-    const int64_t left = a.T - p * kP;
+    const int64_t left = sv.T - p * kP;
     if constexpr (F::kRope) {
-      rope_page_query(fq.qb, fq.qs, p * kP, a.rope_freq, rl.base[wave], lane, rem);
+      rope_page_query(fq.qb, rl.q[wave], p * kP, a.rope_freq, fq.qscale, rl.base[wave], lane, rem);
       dense_page_rope(st, Kp, Vt, (int)(left < kP ? left : kP), fq.qb, rl, lane, rem);
     } else {
       dense_page(st, Kp, Vt, (int)(left < kP ? left : kP), qd, lane, rem);
@@ -1350,8 +1418,10 @@ __device__ inline float ld_elem(const void* base, int64_t idx) {
     return ((const float*)base)[idx];
 }
 
-template <typename Elem, bool kRope>
-__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+template <typename Elem, bool kRope, class KA>
+__global__ __launch_bounds__(256) void decode_valu_kernel(KA kargs) {
+  const DecodeArgs& a = common_args(kargs);
+  const SeqView sv = seq_view(kargs, blockIdx.z);
   // pre-RoPE keys: the page's keys, stored or reconstructed, then rotated
   __shared__ float kr[kRope ? kP : 1][kRope ? kD + 1 : 1];
   __shared__ float qs[kMaxG][kD];
@@ -1366,7 +1436,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int G = a.G;
   const int Hq = a.Hkv * G;
-  const int64_t bh = (int64_t)b * a.Hkv + h;
+  const int64_t bh = (int64_t)sv.b_pool * a.Hkv + h;  // (sequence, KV head) in the pools
   const PackDims pk = pack_dims(a.r_k), pv = pack_dims(a.r_v);
   constexpr int kEsz = sizeof(Elem);
 
@@ -1381,27 +1451,29 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   float o[4] = {0.f, 0.f, 0.f, 0.f};
   __syncthreads();
 
-  const WorkList wl = work_list(a);
-  const int64_t e0 = unit_bound(wl, a, split, a.n_split), e1 = unit_bound(wl, a, split + 1, a.n_split);
+  const WorkList wl = work_list(sv.T, sv.n_fact, a.n_s);
+  const bool idle = split >= sv.n_split;  // beyond this cache's splits: an empty state
+  const int64_t e0 = idle ? wl.D + wl.F : unit_bound(wl, a, split, sv.n_split);
+  const int64_t e1 = idle ? wl.D + wl.F : unit_bound(wl, a, split + 1, sv.n_split);
   for (int64_t e = e0; e < e1; ++e) {
     const int64_t p = unit_page(wl, a, e);
-    const int32_t ent = a.table[p];
+    const int32_t ent = sv.table[p];
     const int cls = table_class(ent), slot = table_slot(ent);
     const bool dense = e < wl.D;
-    const int64_t rem = a.T - p * kP;
+    const int64_t rem = sv.T - p * kP;
     const int nv = dense ? (int)(rem < kP ? rem : kP) : kP;
     const void *Kp = nullptr, *Vt = nullptr, *kpart = nullptr, *vpart = nullptr;
     if (kRope) {
       const int64_t ppg = (int64_t)kP * kD;
       if (!dense) {
-        kpart = a.fac + (bh * a.F_max + slot) * a.page_bytes;
+        kpart = sv.fac + (bh * sv.F_max + slot) * a.page_bytes;
         vpart = (const uint8_t*)kpart + a.k_part_bytes;
       } else if (cls == PKV_PAGE_SINK) {
-        Kp = (const uint8_t*)a.sink_k + (bh * a.n_s + slot) * ppg * kEsz;
-        Vt = (const uint8_t*)a.sink_v + (bh * a.n_s + slot) * ppg * kEsz;
+        Kp = (const uint8_t*)sv.sink_k + (bh * a.n_s + slot) * ppg * kEsz;
+        Vt = (const uint8_t*)sv.sink_v + (bh * a.n_s + slot) * ppg * kEsz;
       } else {
-        Kp = (const uint8_t*)a.win_k + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
-        Vt = (const uint8_t*)a.win_v + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
+        Kp = (const uint8_t*)sv.win_k + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
+        Vt = (const uint8_t*)sv.win_v + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
       }
       for (int idx = tid; idx < kP * kD; idx += 256) {
         const int j = idx / kD, c = idx % kD;
@@ -1436,11 +1508,11 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     } else if (dense) {
       const int64_t ppg = (int64_t)kP * kD;
       if (cls == PKV_PAGE_SINK) {
-        Kp = (const uint8_t*)a.sink_k + (bh * a.n_s + slot) * ppg * kEsz;
-        Vt = (const uint8_t*)a.sink_v + (bh * a.n_s + slot) * ppg * kEsz;
+        Kp = (const uint8_t*)sv.sink_k + (bh * a.n_s + slot) * ppg * kEsz;
+        Vt = (const uint8_t*)sv.sink_v + (bh * a.n_s + slot) * ppg * kEsz;
       } else {
-        Kp = (const uint8_t*)a.win_k + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
-        Vt = (const uint8_t*)a.win_v + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
+        Kp = (const uint8_t*)sv.win_k + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
+        Vt = (const uint8_t*)sv.win_v + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
       }
       for (int idx = tid; idx < G * kP; idx += 256) {
         const int g = idx / kP, j = idx % kP;
@@ -1452,7 +1524,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
         ss[g][j] = acc;
       }
     } else {
-      kpart = a.fac + (bh * a.F_max + slot) * a.page_bytes;
+      kpart = sv.fac + (bh * sv.F_max + slot) * a.page_bytes;
       vpart = (const uint8_t*)kpart + a.k_part_bytes;
       for (int idx = tid; idx < G * a.r_k; idx += 256) {
         const int g = idx / a.r_k, i = idx % a.r_k;
@@ -1764,7 +1836,9 @@ hipError_t launch_merge(const CacheGeom& g, const AttnJob& job, hipStream_t stre
   return hipGetLastError();
 }
 
-hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t stream) {
+namespace {
+
+DecodeArgs make_args(const CacheGeom& g, const AttnJob& job) {
   DecodeArgs a;
   a.q = job.q;
   a.fac = g.base + g.lay.factors;
@@ -1794,16 +1868,25 @@ hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t st
   a.qscale = kLog2e / sqrtf((float)kD);
   a.rope = g.rope;
   std::memcpy(a.rope_freq, g.rope_freq, sizeof(a.rope_freq));
+  return a;
+}
 
-  const dim3 grid(job.n_split, g.Hkv, g.B);
+// The partial kernel of the cache format, with kernel arguments ka (one
+// cache, or a batch of caches: DecodeBatchArgs).  A batch covers the formats
+// with equal K and V ranks per 8; hipErrorNotSupported otherwise.
+template <class KA>
+hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStream_t stream) {
+  constexpr bool kBatch = std::is_same<KA, DecodeBatchArgs>::value;
   const KernelEvents ev = take_kernel_events();
   const int n8k = (g.r_k + 7) / 8, n8v = (g.r_v + 7) / 8;
   if (g.dtype == PKV_BF16_INT4) {
+    if (kBatch && n8k != n8v) return hipErrorNotSupported;
     switch (n8k * 8 + n8v) {
 #define PKV_Q4(NK, NV)                                                                              \
   case NK * 8 + NV:                                                                                 \
-    hipExtLaunchKernelGGL((decode_mfma_kernel<Int4Factors<NK, NV>>), grid, dim3(256), 0, stream,   \
-                          ev.start, ev.stop, 0, a);                                                 \
+    if constexpr (!kBatch || NK == NV)                                                              \
+      hipExtLaunchKernelGGL((decode_mfma_kernel<Int4Factors<NK, NV>, KA>), grid, dim3(256), 0, stream, \
+                            ev.start, ev.stop, 0, ka);                                              \
     break;
 #define PKV_Q4_ROW(NK) PKV_Q4(NK, 1) PKV_Q4(NK, 2) PKV_Q4(NK, 3) PKV_Q4(NK, 4)
       PKV_Q4_ROW(1)
@@ -1817,15 +1900,15 @@ hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t st
     }
   } else if (g.dtype == PKV_BF16 && n8k == n8v && (!g.rope || n8k <= kRopeMfmaMaxN8)) {
     switch (n8k * 2 + (g.rope ? 1 : 0)) {
-#define PKV_CASE(N)                                                                                     \
-  case 2 * N:                                                                                           \
-    hipExtLaunchKernelGGL(decode_mfma_kernel<Bf16Factors<N>>, grid, dim3(256), 0, stream, ev.start, ev.stop, \
-                          0, a);                                                                        \
+#define PKV_CASE(N)                                                                                       \
+  case 2 * N:                                                                                             \
+    hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Factors<N>, KA>), grid, dim3(256), 0, stream, ev.start, \
+                          ev.stop, 0, ka);                                                                \
     break;
-#define PKV_ROPE(N)                                                                                     \
-  case 2 * N + 1:                                                                                       \
-    hipExtLaunchKernelGGL(decode_mfma_kernel<RopeFactors<N>>, grid, dim3(256), 0, stream, ev.start, ev.stop, \
-                          0, a);                                                                        \
+#define PKV_ROPE(N)                                                                                       \
+  case 2 * N + 1:                                                                                         \
+    hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<N>, KA>), grid, dim3(256), 0, stream, ev.start, \
+                          ev.stop, 0, ka);                                                                \
     break;
       PKV_CASE(1)
       PKV_CASE(2)
@@ -1844,18 +1927,44 @@ hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t st
       default:
         return hipErrorInvalidValue;
     }
+  } else if (kBatch) {
+    return hipErrorNotSupported;
   } else if (g.dtype == PKV_BF16) {
     if (g.rope)
-      hipExtLaunchKernelGGL((decode_valu_kernel<uint16_t, true>), grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a);
+      hipExtLaunchKernelGGL((decode_valu_kernel<uint16_t, true, KA>), grid, dim3(256), 0, stream, ev.start,
+                            ev.stop, 0, ka);
     else
-      hipExtLaunchKernelGGL((decode_valu_kernel<uint16_t, false>), grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a);
+      hipExtLaunchKernelGGL((decode_valu_kernel<uint16_t, false, KA>), grid, dim3(256), 0, stream, ev.start,
+                            ev.stop, 0, ka);
   } else {
     if (g.rope)
-      hipExtLaunchKernelGGL((decode_valu_kernel<float, true>), grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a);
+      hipExtLaunchKernelGGL((decode_valu_kernel<float, true, KA>), grid, dim3(256), 0, stream, ev.start,
+                            ev.stop, 0, ka);
     else
-      hipExtLaunchKernelGGL((decode_valu_kernel<float, false>), grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a);
+      hipExtLaunchKernelGGL((decode_valu_kernel<float, false, KA>), grid, dim3(256), 0, stream, ev.start,
+                            ev.stop, 0, ka);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t stream) {
+  return dispatch_partial(g, make_args(g, job), dim3(job.n_split, g.Hkv, g.B), stream);
+}
+
+hipError_t launch_partial_batch(const CacheGeom* gs, const int64_t* T, const int64_t* n_fact, const int* ns,
+                                int n, const AttnJob& job, hipStream_t stream) {
+  if (n < 1 || n > kMaxBatchCaches) return hipErrorInvalidValue;
+  DecodeBatchArgs x;
+  x.a = make_args(gs[0], job);
+  for (int i = 0; i < n; ++i) {
+    const CacheGeom& g = gs[i];
+    x.seq[i] = BatchSeq{g.base + g.lay.factors, g.base + g.lay.sink_k, g.base + g.lay.sink_v,
+                        g.base + g.lay.win_k, g.base + g.lay.win_v,
+                        (const int32_t*)(g.base + g.lay.page_table), T[i], n_fact[i], g.F_max, ns[i]};
+  }
+  return dispatch_partial(gs[0], x, dim3(job.n_split, gs[0].Hkv, n), stream);
 }
 
 }  // namespace pkv

@@ -13,6 +13,7 @@ namespace pkv {
 constexpr int kP = 64;    // page length supported by the kernels
 constexpr int kD = 128;   // head dim supported by the kernels
 constexpr int kMaxG = 8;  // query heads per KV head handled by one wave
+constexpr int kMaxBatchCaches = 32;    // caches of one batched attention launch
 constexpr int kMaxDecodeSplits = 512;  // workgroups per (sequence, KV head) in one decode
 
 // --------------------------------------------------------------------------
@@ -343,6 +344,13 @@ struct AttnJob {
 };
 
 hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t stream);
+// One launch over n <= kMaxBatchCaches caches of batch 1 and equal shape
+// (gs[i], lengths T[i], factor counts n_fact[i]); workgroup z takes cache z,
+// whose range is shared by the first ns[i] <= job.n_split splits.
+// hipErrorNotSupported for formats without a batched kernel.
+hipError_t launch_partial_batch(const CacheGeom* gs, const int64_t* T, const int64_t* n_fact, const int* ns,
+                                int n, const AttnJob& job, hipStream_t stream);
+
 hipError_t launch_merge(const CacheGeom& g, const AttnJob& job, hipStream_t stream);
 int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact);
 

@@ -1,0 +1,151 @@
+"""GPU tests of pkv_decode_attn_batch: attention for a batch of sequences of
+different lengths, one cache (own pools, own page table) per sequence.
+
+Row i of the batched result must equal pkv_decode_attn on cache i with the
+same split count bit for bit (the same kernel code runs on the same pages),
+whatever the format: the batched matrix-core kernels and the per-cache
+fallback (fp32, unequal padded ranks, INT4 with unequal ranks).  Against the
+oracle each row meets the cache dtype's gate.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import long_context_decode_pkv_amd as pkv
+from gpu_common import TOL, make_cache, rel_err, require_gpu, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+# ragged lengths: sink only, all dense, page-aligned, long, one token past a page
+LENGTHS = [64 * 20 + 5, 40, 64 * 3 + 1, 64 * 50, 130, 64 * 7 + 63]
+
+
+def _batch(cfg_id, lengths, store=None, r_k=None, r_v=None, rope=None, kv_heads=2, with_f64=False):
+    """One cache per length (sequence i: decode_inputs with seed offset i)."""
+    caches, data = [], []
+    for i, T in enumerate(lengths):
+        d = synth.decode_inputs(cfg_id, T=T, B=1, kv_heads=kv_heads, with_f64=with_f64)
+        if i:  # distinct sequences: shift the keys and values of sequence i
+            d = synth.decode_inputs(cfg_id, T=T + 64 * i, B=1, kv_heads=kv_heads, with_f64=with_f64)
+            for k in ("K", "V") + (("K64", "V64") if with_f64 else ()):
+                d[k] = np.ascontiguousarray(d[k][:, :, 64 * i:64 * i + T])
+            d["T"] = T
+        dt = d["cfg"]["dtype"]
+        c = make_cache(d, r_k=r_k, r_v=r_v, max_tokens=T + 64, store=store)
+        if rope is not None:
+            c.set_key_rope(rope)
+        c.prefill(to_dev(d["K"], dt), to_dev(d["V"], dt))
+        caches.append(c)
+        data.append(d)
+    return caches, data
+
+
+def _queries(cfg_id, n, Hq, dtype):
+    g = synth.rng(synth.CONFIGS[cfg_id]["seed"], 77, 0, 0, synth.KIND_Q)
+    q = synth.to_storage(g.standard_normal((n, Hq, 128)), dtype)
+    return q
+
+
+def _check_equal_to_single(caches, q, n_split):
+    import torch
+    out = pkv.decode_batch(caches, q, n_split=n_split)
+    torch.cuda.synchronize()
+    for i, c in enumerate(caches):
+        o = c.decode(q[i:i + 1].contiguous(), n_split=n_split)
+        torch.cuda.synchronize()
+        assert torch.equal(out[i:i + 1], o), (i, n_split)
+    return out
+
+
+@pytest.mark.parametrize("store,r", [(None, 16), ("int4", 16), (None, 24)])
+def test_batch_equals_single_caches(store, r):
+    require_gpu()
+    caches, data = _batch(2, LENGTHS, store=store, r_k=r, r_v=r)
+    dt = "bf16"
+    q = to_dev(_queries(2, len(caches), data[0]["Hq"], dt), dt)
+    for ns in (1, 4, 16):
+        _check_equal_to_single(caches, q, ns)
+    # the library's split count for the batch (that of its longest cache):
+    # the per-cache results to fp32 rounding
+    import torch
+    out = to_f64(pkv.decode_batch(caches, q))
+    for i, c in enumerate(caches):
+        o = to_f64(c.decode(q[i:i + 1].contiguous()))
+        torch.cuda.synchronize()
+        assert rel_err(out[i:i + 1], o) <= 1e-5, i
+
+
+def test_batch_pre_rope_keys():
+    require_gpu()
+    f = synth.rope_inv_freq(5e5)
+    caches, data = _batch(2, LENGTHS, rope=f)
+    q = to_dev(_queries(2, len(caches), data[0]["Hq"], "bf16"), "bf16")
+    _check_equal_to_single(caches, q, 4)
+
+
+@pytest.mark.parametrize("cfg_id,store,rk,rv", [
+    (1, None, 16, 16),     # fp32: VALU kernel, one launch per cache
+    (2, None, 24, 16),     # unequal padded ranks
+    (2, "int4", 24, 16),   # INT4 with unequal padded ranks
+])
+def test_batch_per_cache_fallback(cfg_id, store, rk, rv):
+    require_gpu()
+    caches, data = _batch(cfg_id, [64 * 9 + 3, 70, 64 * 12], store=store, r_k=rk, r_v=rv, kv_heads=1)
+    dt = data[0]["cfg"]["dtype"]
+    q = to_dev(_queries(cfg_id, len(caches), data[0]["Hq"], dt), dt)
+    _check_equal_to_single(caches, q, 3)
+
+
+def test_batch_against_oracle():
+    import torch
+    require_gpu()
+    caches, data = _batch(3, [64 * 30 + 7, 64 * 4, 100], with_f64=True)
+    dt = "bf16"
+    qn = _queries(3, len(caches), data[0]["Hq"], dt)
+    out = to_f64(pkv.decode_batch(caches, to_dev(qn, dt)))
+    torch.cuda.synchronize()
+    q64 = synth.storage_to_f64(qn, dt)
+    for i, d in enumerate(data):
+        cfg = d["cfg"]
+        ref = oracle.decode(q64[i:i + 1], d["K64"], d["V64"], d["T"], 64, cfg["s"], cfg["w"], cfg["r_k"],
+                            cfg["r_v"], dt)
+        err = rel_err(out[i:i + 1], ref["o_stored"])
+        print(f"[batch vs oracle] cache {i} T={d['T']}: err {err:.3e}")
+        assert err <= TOL[dt]
+
+
+def test_batch_of_32_caches():
+    require_gpu()
+    lengths = [65 + 97 * i for i in range(32)]
+    caches, data = _batch(2, lengths, kv_heads=1)
+    q = to_dev(_queries(2, 32, data[0]["Hq"], "bf16"), "bf16")
+    _check_equal_to_single(caches, q, 2)
+
+
+def test_batch_errors():
+    import ctypes
+    import torch
+    require_gpu()
+    caches, data = _batch(2, [300, 200], kv_heads=1)
+    q = to_dev(_queries(2, 2, data[0]["Hq"], "bf16"), "bf16")
+    L = pkv.lib()
+    nb = ctypes.c_uint64()
+    for n in (0, 33):
+        hs = (ctypes.c_void_p * max(n, 1))(*([caches[0]._h] * max(n, 1)))
+        assert L.pkv_decode_batch_workspace_bytes(hs, n, 0, ctypes.byref(nb)) == 1
+    other = make_cache(data[0], r_k=8, r_v=8, max_tokens=400)
+    other.prefill(to_dev(data[0]["K"], "bf16"), to_dev(data[0]["V"], "bf16"))
+    with pytest.raises(pkv.PKVError) as ei:  # shapes differ
+        pkv.decode_batch([caches[0], other], q)
+    assert ei.value.status == 1
+    empty = make_cache(data[0], max_tokens=400)
+    empty.prefill(to_dev(data[0]["K"], "bf16")[:, :, :0].contiguous(),
+                  to_dev(data[0]["V"], "bf16")[:, :, :0].contiguous())
+    with pytest.raises(pkv.PKVError) as ei:  # an empty cache
+        pkv.decode_batch([caches[0], empty], q)
+    assert ei.value.status == 1
+    small = torch.empty(64, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(pkv.PKVError) as ei:
+        pkv.decode_batch(caches, q, workspace=small)
+    assert ei.value.status == 3

@@ -260,3 +260,26 @@ def test_set_key_rope_validation_without_gpu():
                 assert L.pkv_cache_set_key_rope(h, None, 0) == 0
         finally:
             L.pkv_cache_destroy(h)
+
+
+def test_batch_validation_without_gpu():
+    """pkv_decode_batch_workspace_bytes / pkv_decode_attn_batch reject bad
+    batches before any launch: null or out-of-range arguments, empty caches."""
+    L = pkv.lib()
+    nb = ctypes.c_uint64()
+    sh = _shape(batch=1, max_tokens=256)
+    lay = pkv.cache_layout(sh)
+    h = ctypes.c_void_p()
+    assert L.pkv_cache_create(ctypes.byref(sh), ctypes.c_void_p(256 * 1000), lay["total_bytes"],
+                              ctypes.byref(h)) == 0
+    try:
+        hs = (ctypes.c_void_p * 2)(h, h)
+        assert L.pkv_decode_batch_workspace_bytes(None, 1, 0, ctypes.byref(nb)) == 1
+        assert L.pkv_decode_batch_workspace_bytes(hs, 0, 0, ctypes.byref(nb)) == 1
+        assert L.pkv_decode_batch_workspace_bytes(hs, 33, 0, ctypes.byref(nb)) == 1
+        assert L.pkv_decode_batch_workspace_bytes(hs, 2, 0, None) == 1
+        assert L.pkv_decode_batch_workspace_bytes(hs, 2, 0, ctypes.byref(nb)) == 1  # empty caches
+        fake = ctypes.c_void_p(256 * 5000)
+        assert L.pkv_decode_attn_batch(hs, 2, fake, fake, fake, 1 << 20, 0, None) == 1
+    finally:
+        L.pkv_cache_destroy(h)
