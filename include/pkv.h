@@ -284,7 +284,7 @@ int32_t pkv_promote_page(pkv_cache* cache, void* stream);
  * whose K and V ranks pad to the same multiple of 8; other formats launch
  * once per cache.  Then one merge launch.  workspace: 256-byte aligned
  * device memory of pkv_decode_batch_workspace_bytes(caches, n, n_split)
- * bytes.  Every cache's range is cut into n_split parts (0: the library's
+ * bytes (which also takes empty caches).  Every cache's range is cut into n_split parts (0: the library's
  * count for the batch's longest cache), and row i equals pkv_decode_attn on
  * cache i with the same n_split bit for bit.
  * Errors: INVALID_ARG (null or misaligned pointers, n out of range, shapes
@@ -294,6 +294,28 @@ int32_t pkv_decode_attn_batch(const pkv_cache* const* caches, int32_t n, const v
                               void* workspace, uint64_t workspace_bytes, int32_t n_split, void* stream);
 int32_t pkv_decode_batch_workspace_bytes(const pkv_cache* const* caches, int32_t n, int32_t n_split,
                                          uint64_t* bytes);
+
+/*
+ * One decode step for a batch of sequences of different lengths, one cache of
+ * batch 1 per sequence (Sec. 3.3 (5) then (4) on every cache): for cache i,
+ * append (k_new[i], v_new[i]), promote the page leaving its window when due,
+ * and attend q[i] over its tokens including the new one -- what
+ * pkv_decode_step does on each cache, with one partial-attention launch and
+ * one merge (which writes every new token) for the whole batch; a promotion
+ * adds one decomposition launch for its cache.
+ * caches: n (1..32) handles as for pkv_decode_attn_batch; lengths may be 0.
+ * k_new, v_new: device [n][H_kv][d]; q: device [n][H_q][d] (cache dtype);
+ * out: device float32 [n][H_q][d]; all 16-byte aligned.  workspace: as for
+ * pkv_decode_attn_batch (pkv_decode_batch_workspace_bytes before the step).
+ * Every cache ends as after pkv_decode_step, and with the same n_split the
+ * outputs are bit-identical to it.  Caches without a recent window step one
+ * by one (their promoted page is the new token's).
+ * Errors: as pkv_decode_attn_batch, PROMOTION_PENDING, CAPACITY (a cache at
+ * max_tokens or without a free factor slot); nothing changes then.
+ */
+int32_t pkv_decode_step_batch(pkv_cache* const* caches, int32_t n, const void* k_new, const void* v_new,
+                              const void* q, float* out, void* workspace, uint64_t workspace_bytes,
+                              int32_t n_split, void* stream);
 
 /* Workspace bytes pkv_decode_attn needs for n_split splits per (sequence,
  * KV head); n_split = 0 selects the library's choice; at most 512. */

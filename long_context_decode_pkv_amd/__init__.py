@@ -94,6 +94,7 @@ def lib():
         "pkv_cache_set_key_rope": ([vp, vp, i32], i32),
         "pkv_decode_attn_batch": ([vp, i32, vp, vp, vp, u64, i32, vp], i32),
         "pkv_decode_batch_workspace_bytes": ([vp, i32, i32, vp], i32),
+        "pkv_decode_step_batch": ([vp, i32, vp, vp, vp, vp, vp, u64, i32, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -441,6 +442,36 @@ class Cache:
         if kind == KEYS:
             return self.buffer[base: base + kbytes]
         return self.buffer[base + kbytes: base + L["factor_page_bytes"]]
+
+
+def batch_workspace(caches, n_split: int = 0):
+    """Device workspace for decode_batch / step_batch on these caches."""
+    import torch
+    n = len(caches)
+    handles = (ctypes.c_void_p * n)(*[c._h for c in caches])
+    nb = ctypes.c_uint64()
+    _check(lib().pkv_decode_batch_workspace_bytes(handles, n, n_split, ctypes.byref(nb)),
+           "pkv_decode_batch_workspace_bytes")
+    return torch.empty(max(int(nb.value), 1), dtype=torch.uint8, device=caches[0].device)
+
+
+def step_batch(caches, k, v, q, out=None, n_split: int = 0, workspace=None):
+    """One decode step for a batch of sequences of different lengths, one
+    Cache of batch 1 each (pkv_decode_step_batch): k, v [n][H_kv][d], q
+    [n][H_q][d] -> out [n][H_q][d] float32."""
+    import torch
+    n = len(caches)
+    handles = (ctypes.c_void_p * n)(*[c._h for c in caches])
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=caches[0].device)
+    if workspace is None:
+        workspace = batch_workspace(caches, n_split)
+    ec = caches[0].elem_code
+    _check(lib().pkv_decode_step_batch(handles, n, _dev_ptr(k, ec, "k"), _dev_ptr(v, ec, "v"), _dev_ptr(q, ec, "q"),
+                                       _dev_ptr(out, None, "out"), ctypes.c_void_p(workspace.data_ptr()),
+                                       workspace.numel(), n_split, _stream(caches[0].device)),
+           "pkv_decode_step_batch")
+    return out
 
 
 def decode_batch(caches, q, out=None, n_split: int = 0, workspace=None):

@@ -829,12 +829,13 @@ bool batchable(const pkv_cache* a, const pkv_cache* b) {
 // Validates a batch; split counts (the grid's in *ns, each cache's in
 // ns_seq) and the workspace its attention needs.
 int32_t batch_plan(const pkv_cache* const* caches, int32_t n, int32_t n_split, int* ns, int* ns_seq,
-                   uint64_t* need) {
+                   uint64_t* need, bool allow_empty) {
   if (!caches || n < 1 || n > kMaxBatchCaches || n_split < 0 || n_split > kMaxDecodeSplits)
     return PKV_ERR_INVALID_ARG;
   int64_t T_max = 0, nf_max = 0;
   for (int i = 0; i < n; ++i) {
-    if (!caches[i] || !batchable(caches[0], caches[i]) || caches[i]->T < 1) return PKV_ERR_INVALID_ARG;
+    if (!caches[i] || !batchable(caches[0], caches[i]) || caches[i]->T < (allow_empty ? 0 : 1))
+      return PKV_ERR_INVALID_ARG;
     if (caches[i]->T > T_max) {
       T_max = caches[i]->T;
       nf_max = caches[i]->n_fact;
@@ -859,14 +860,14 @@ int32_t pkv_decode_batch_workspace_bytes(const pkv_cache* const* caches, int32_t
                                          uint64_t* bytes) {
   if (!bytes) return PKV_ERR_INVALID_ARG;
   int ns, ns_seq[kMaxBatchCaches];
-  return batch_plan(caches, n, n_split, &ns, ns_seq, bytes);
+  return batch_plan(caches, n, n_split, &ns, ns_seq, bytes, true);
 }
 
 int32_t pkv_decode_attn_batch(const pkv_cache* const* caches, int32_t n, const void* q, float* out,
                               void* workspace, uint64_t workspace_bytes, int32_t n_split, void* stream) {
   int ns, ns_seq[kMaxBatchCaches];
   uint64_t need;
-  const int32_t st = batch_plan(caches, n, n_split, &ns, ns_seq, &need);
+  const int32_t st = batch_plan(caches, n, n_split, &ns, ns_seq, &need, false);
   if (st != PKV_OK) return st;
   if (!q || !out || !workspace || !aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, kAlign))
     return PKV_ERR_INVALID_ARG;
@@ -1007,6 +1008,112 @@ int32_t pkv_decode_step(pkv_cache* c, const void* k_new, const void* v_new, cons
   // the token completed window page p: factorize it ahead of the step at
   // which it leaves the window
   if (c->aux && row == kP - 1 && p >= g.n_s && g.n_w > 0) return factorize_early(c, p, s);
+  return PKV_OK;
+}
+
+int32_t pkv_decode_step_batch(pkv_cache* const* caches, int32_t n, const void* k_new, const void* v_new,
+                              const void* q, float* out, void* workspace, uint64_t workspace_bytes,
+                              int32_t n_split, void* stream) {
+  int ns, ns_seq[kMaxBatchCaches];
+  uint64_t need;
+  int32_t st = batch_plan(caches, n, n_split, &ns, ns_seq, &need, true);
+  if (st != PKV_OK) return st;
+  if (!k_new || !v_new || !q || !out || !workspace || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+      !aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, kAlign))
+    return PKV_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return PKV_ERR_CAPACITY;
+  // every check before anything changes
+  bool one_by_one = false;
+  for (int i = 0; i < n; ++i) {
+    const pkv_cache* c = caches[i];
+    if (c->pending) return PKV_ERR_PROMOTION_PENDING;
+    if (c->T >= c->shape.max_tokens) return PKV_ERR_CAPACITY;
+    const CacheGeom g = geom_of(c);
+    const bool promote = steady_fact(c->T + 1, kP, g.n_s, g.n_w) > c->n_fact;
+    if (promote && c->n_fact >= g.F_max) return PKV_ERR_CAPACITY;
+    // no window: the page a token completes is factorized at once, after the
+    // token is in place (pkv_decode_step's separate launches)
+    if (promote && g.n_s + c->n_fact == c->T / kP) one_by_one = true;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const CacheGeom g0 = geom_of(caches[0]);
+  const int64_t esz = caches[0]->lay.elem_bytes;
+  if (one_by_one) {  // the caches step in turn, reusing the workspace (one stream)
+    for (int i = 0; i < n; ++i) {
+      st = pkv_decode_step(caches[i], (const uint8_t*)k_new + (int64_t)i * g0.Hkv * kD * esz,
+                           (const uint8_t*)v_new + (int64_t)i * g0.Hkv * kD * esz,
+                           (const uint8_t*)q + (int64_t)i * g0.Hq * kD * esz, out + (int64_t)i * g0.Hq * kD,
+                           workspace, workspace_bytes, ns, stream);
+      if (st != PKV_OK) return st;
+    }
+    return PKV_OK;
+  }
+  for (int i = 0; i < n; ++i)
+    if (wait_chunk(caches[i], s) != hipSuccess) return PKV_ERR_DEVICE;
+  // promotions of the pages leaving the windows (at most one per cache)
+  for (int i = 0; i < n; ++i) {
+    pkv_cache* c = caches[i];
+    const CacheGeom g = geom_of(c);
+    if (steady_fact(c->T + 1, kP, g.n_s, g.n_w) > c->n_fact) {
+      st = promote_now(c, stream);
+      if (st != PKV_OK) return st;
+    }
+  }
+  // attention over each cache's T_i tokens, then the merge with the new tokens
+  CacheGeom gs[kMaxBatchCaches];
+  int64_t T[kMaxBatchCaches], nf[kMaxBatchCaches];
+  AttnJob apps[kMaxBatchCaches];
+  for (int i = 0; i < n; ++i) {
+    const pkv_cache* c = caches[i];
+    gs[i] = geom_of(c);
+    T[i] = c->T;
+    nf[i] = c->n_fact;
+    const int64_t p = c->T / kP;
+    const int row = (int)(c->T % kP);
+    apps[i].app_page = p;
+    apps[i].app_row = row;
+    apps[i].app_entry = p < gs[i].n_s ? table_entry(PKV_PAGE_SINK, (int)p)
+                                      : table_entry(row == kP - 1 ? PKV_PAGE_WIN : PKV_PAGE_PART,
+                                                    (int)((p - gs[i].n_s) % (gs[i].n_w + 1)));
+  }
+  const uint64_t rows = (uint64_t)n * g0.Hq * ns;
+  AttnJob job;
+  job.q = q;
+  job.out = out;
+  job.ws_o = (float*)workspace;
+  job.ws_ml = (float*)((uint8_t*)workspace + align_up(rows * kD * 4));
+  job.n_split = ns;
+  job.T = T[0];
+  job.n_fact = nf[0];
+  hipError_t e = launch_partial_batch(gs, T, nf, ns_seq, n, job, s);
+  if (e == hipErrorNotSupported) {  // no batched kernel for this format: one launch per cache
+    (void)hipGetLastError();
+    e = hipSuccess;
+    for (int i = 0; i < n && e == hipSuccess; ++i) {
+      AttnJob ji = job;
+      ji.q = (const uint8_t*)q + (int64_t)i * g0.Hq * kD * esz;
+      ji.ws_o = job.ws_o + (int64_t)i * g0.Hq * ns * kD;
+      ji.ws_ml = job.ws_ml + (int64_t)i * g0.Hq * ns * 2;
+      ji.T = T[i];
+      ji.n_fact = nf[i];
+      e = launch_partial(gs[i], ji, s);
+    }
+  }
+  job.k_new = k_new;
+  job.v_new = v_new;
+  if (e == hipSuccess) e = launch_merge_batch(gs, n, job, apps, s);
+  if (e != hipSuccess) return PKV_ERR_DEVICE;
+  for (int i = 0; i < n; ++i) {
+    pkv_cache* c = caches[i];
+    const int64_t p = c->T / kP;
+    const int row = (int)(c->T % kP);
+    c->T += 1;
+    // a token that completed a window page: factorize it early (aux stream)
+    if (c->aux && row == kP - 1 && p >= gs[i].n_s && gs[i].n_w > 0) {
+      st = factorize_early(c, p, s);
+      if (st != PKV_OK) return st;
+    }
+  }
   return PKV_OK;
 }
 

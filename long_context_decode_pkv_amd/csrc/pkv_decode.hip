@@ -1599,6 +1599,20 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(KA kargs) {
 // the token appended in this decode step: its state (score q.k_new in log2
 // units, l = 1, o = v_new) joins the n_split partial states, and the token is
 // stored in row app_row of its dense page for later steps.
+// Where one sequence's appended token goes: its key row and value column
+// in page app_page of its (sequence, KV head) pages -- the pages of
+// (b, h) = (0, 0) at k_dst / v_dst, those of consecutive (b, h)
+// dst_bh_stride bytes apart -- and its page's table entry.
+struct AppendDst {
+  uint8_t* k_dst;
+  uint8_t* v_dst;
+  int64_t dst_bh_stride;
+  int32_t* table_w;
+  int64_t app_page;
+  int app_row;
+  int32_t app_entry;
+};
+
 struct MergeArgs {
   const float* ws_o;
   const float* ws_ml;
@@ -1610,16 +1624,29 @@ struct MergeArgs {
   int dtype;
   float qscale;
   int G, Hkv;
-  uint8_t* k_dst;   // page of (b, h) = (0, 0) receiving the token's key row
-  uint8_t* v_dst;   // its transposed value page
-  int64_t dst_bh_stride;  // bytes between the pages of consecutive (b, h)
-  int app_row;
-  int32_t* table_w;
-  int64_t app_page;
-  int32_t app_entry;
+  AppendDst app;                  // one cache: sequence b's pages are the (b, h) above
   int rope;                       // pre-RoPE keys: k_new turns by its position's angles
-  float rope_c[kD / 2], rope_s[kD / 2];
+  float rope_freq[kD / 2];
 };
+
+// The merge of a batch of caches of batch 1 (pkv_decode_step_batch): rows of
+// cache i follow those of cache i - 1; cache i's token goes to app[i].
+struct MergeBatchArgs {
+  MergeArgs m;
+  AppendDst app[kMaxBatchCaches];
+};
+
+__device__ inline const MergeArgs& merge_common(const MergeArgs& m) { return m; }
+__device__ inline const MergeArgs& merge_common(const MergeBatchArgs& x) { return x.m; }
+// the append destination of sequence seq, and the sequence's index in those pages
+__device__ inline const AppendDst& append_dst(const MergeArgs& m, int64_t) { return m.app; }
+__device__ inline const AppendDst& append_dst(const MergeBatchArgs& x, int64_t seq) { return x.app[seq]; }
+__device__ inline int64_t append_pool_seq(const MergeArgs&, int64_t seq) { return seq; }
+__device__ inline int64_t append_pool_seq(const MergeBatchArgs&, int64_t) { return 0; }
+// whether sequence seq's first workgroup writes the table entry (one table
+// per cache: once per launch, or once per cache of a batch)
+__device__ inline bool writes_table(const MergeArgs&, int64_t seq) { return seq == 0; }
+__device__ inline bool writes_table(const MergeBatchArgs&, int64_t) { return true; }
 
 __device__ inline float load_elem(const void* p, int64_t i, int dtype) {
   if (dtype == PKV_BF16) return __uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
@@ -1637,7 +1664,9 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeGroups = kMergeThreads / (kD / 4);
 constexpr int kMergePrefetch = 8;  // splits per group held in registers (n_split <= 64)
 
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
+template <class MA>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MA margs) {
+  const MergeArgs& m = merge_common(margs);
   __shared__ float sh_m[kMergeThreads / 64], sh_dot[kMergeThreads / 64];
   __shared__ float4 sh_acc[kMergeGroups][kD / 4];
   __shared__ float sh_l[kMergeGroups];
@@ -1650,21 +1679,21 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
 
   // loads
   float qk = 0.f;
-  int64_t bh = 0;
-  if (m.k_new) {
-    const int Hq = m.G * m.Hkv;
-    const int hq = (int)(row % Hq);
-    bh = (row / Hq) * m.Hkv + hq / m.G;
-    if (tid < kD) {
-      float kk = load_elem(m.k_new, bh * kD + tid, m.dtype);
-      if (m.rope) {  // pair (c, c + d/2) of the new key, rotated at its position
-        const int mm = tid & (kD / 2 - 1);
-        const float other = load_elem(m.k_new, bh * kD + (tid ^ (kD / 2)), m.dtype);
-        kk = tid < kD / 2 ? __builtin_fmaf(-other, m.rope_s[mm], kk * m.rope_c[mm])
-                          : __builtin_fmaf(other, m.rope_s[mm], kk * m.rope_c[mm]);
-      }
-      qk = load_elem(m.q, row * kD + tid, m.dtype) * kk;
+  const int Hq = m.G * m.Hkv;
+  const int hq = (int)(row % Hq);
+  const int64_t seq = row / Hq;
+  const int64_t bh = seq * m.Hkv + hq / m.G;  // (sequence, KV head) of k_new / v_new
+  const AppendDst& ad = append_dst(margs, seq);
+  if (m.k_new && tid < kD) {
+    float kk = load_elem(m.k_new, bh * kD + tid, m.dtype);
+    if (m.rope) {  // pair (c, c + d/2) of the new key, rotated at its position
+      const int mm = tid & (kD / 2 - 1);
+      const float other = load_elem(m.k_new, bh * kD + (tid ^ (kD / 2)), m.dtype);
+      float cs, sn;
+      rope_sincos(ad.app_page * kP + ad.app_row, m.rope_freq[mm], cs, sn);
+      kk = tid < kD / 2 ? __builtin_fmaf(-other, sn, kk * cs) : __builtin_fmaf(other, sn, kk * cs);
     }
+    qk = load_elem(m.q, row * kD + tid, m.dtype) * kk;
   }
   float4 vnew = {0.f, 0.f, 0.f, 0.f};
   if (m.k_new && tid < kD / 4) {
@@ -1687,11 +1716,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
   // the new token goes into its dense page (one workgroup per (sequence, KV
   // head)) and its table entry is set (one workgroup)
   if (m.k_new) {
-    const int hq = (int)(row % (m.G * m.Hkv));
     if (hq % m.G == 0 && tid < kD) {
       const int esz = m.dtype == PKV_BF16 ? 2 : 4;
-      uint8_t* kd = m.k_dst + bh * m.dst_bh_stride + ((int64_t)m.app_row * kD + tid) * esz;
-      uint8_t* vd = m.v_dst + bh * m.dst_bh_stride + ((int64_t)tid * kP + m.app_row) * esz;
+      const int64_t bhp = append_pool_seq(margs, seq) * m.Hkv + hq / m.G;  // its pages
+      uint8_t* kd = ad.k_dst + bhp * ad.dst_bh_stride + ((int64_t)ad.app_row * kD + tid) * esz;
+      uint8_t* vd = ad.v_dst + bhp * ad.dst_bh_stride + ((int64_t)tid * kP + ad.app_row) * esz;
       if (esz == 2) {
         *(uint16_t*)kd = ((const uint16_t*)m.k_new)[bh * kD + tid];
         *(uint16_t*)vd = ((const uint16_t*)m.v_new)[bh * kD + tid];
@@ -1700,7 +1729,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
         *(float*)vd = ((const float*)m.v_new)[bh * kD + tid];
       }
     }
-    if (row == 0 && tid == 0) m.table_w[m.app_page] = m.app_entry;
+    if (hq == 0 && tid == 0 && writes_table(margs, seq)) ad.table_w[ad.app_page] = ad.app_entry;
   }
 
   // global maximum and the new token's score (log2 units)
@@ -1789,7 +1818,9 @@ int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact) {
   return (int)s;
 }
 
-hipError_t launch_merge(const CacheGeom& g, const AttnJob& job, hipStream_t stream) {
+namespace {
+
+MergeArgs merge_args(const CacheGeom& g, const AttnJob& job) {
   MergeArgs m;
   m.ws_o = job.ws_o;
   m.ws_ml = job.ws_ml;
@@ -1802,37 +1833,51 @@ hipError_t launch_merge(const CacheGeom& g, const AttnJob& job, hipStream_t stre
   m.qscale = kLog2e / sqrtf((float)kD);
   m.G = g.G;
   m.Hkv = g.Hkv;
-  m.k_dst = m.v_dst = nullptr;
-  m.dst_bh_stride = 0;
-  m.app_row = job.app_row;
-  m.table_w = (int32_t*)(g.base + g.lay.page_table);
-  m.app_page = job.app_page;
-  m.app_entry = job.app_entry;
+  m.app = AppendDst{nullptr, nullptr, 0, nullptr, -1, -1, 0};
   m.rope = g.rope && job.k_new;
-  if (m.rope) {
-    const double pos = (double)(job.app_page * kP + job.app_row);
-    for (int mm = 0; mm < kD / 2; ++mm) {
-      const double ang = pos * (double)g.rope_freq[mm];
-      m.rope_c[mm] = (float)std::cos(ang);
-      m.rope_s[mm] = (float)std::sin(ang);
-    }
+  std::memcpy(m.rope_freq, g.rope_freq, sizeof(m.rope_freq));
+  return m;
+}
+
+// The append destination of job's token in cache g (page app_page: a sink
+// page or a ring slot).
+AppendDst append_dst_of(const CacheGeom& g, const AttnJob& job) {
+  AppendDst d{nullptr, nullptr, 0, (int32_t*)(g.base + g.lay.page_table), job.app_page, job.app_row,
+              job.app_entry};
+  const int64_t ppg_bytes = (int64_t)kP * kD * g.lay.elem_bytes;
+  const int64_t p = job.app_page;
+  if (p < g.n_s) {
+    d.k_dst = g.base + g.lay.sink_k + p * ppg_bytes;
+    d.v_dst = g.base + g.lay.sink_v + p * ppg_bytes;
+    d.dst_bh_stride = g.n_s * ppg_bytes;
+  } else {
+    const int64_t slot = (p - g.n_s) % (g.n_w + 1);
+    d.k_dst = g.base + g.lay.win_k + slot * ppg_bytes;
+    d.v_dst = g.base + g.lay.win_v + slot * ppg_bytes;
+    d.dst_bh_stride = (int64_t)(g.n_w + 1) * ppg_bytes;
   }
-  if (job.k_new) {
-    const int64_t ppg_bytes = (int64_t)kP * kD * g.lay.elem_bytes;
-    const int64_t p = job.app_page;
-    if (p < g.n_s) {
-      m.k_dst = g.base + g.lay.sink_k + p * ppg_bytes;
-      m.v_dst = g.base + g.lay.sink_v + p * ppg_bytes;
-      m.dst_bh_stride = g.n_s * ppg_bytes;
-    } else {
-      const int64_t slot = (p - g.n_s) % (g.n_w + 1);
-      m.k_dst = g.base + g.lay.win_k + slot * ppg_bytes;
-      m.v_dst = g.base + g.lay.win_v + slot * ppg_bytes;
-      m.dst_bh_stride = (int64_t)(g.n_w + 1) * ppg_bytes;
-    }
-  }
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((int64_t)g.B * g.Hq)), dim3(kMergeThreads), 0, stream,
-                     m);
+  return d;
+}
+
+}  // namespace
+
+hipError_t launch_merge(const CacheGeom& g, const AttnJob& job, hipStream_t stream) {
+  MergeArgs m = merge_args(g, job);
+  if (job.k_new) m.app = append_dst_of(g, job);
+  hipLaunchKernelGGL(merge_kernel<MergeArgs>, dim3((unsigned)((int64_t)g.B * g.Hq)), dim3(kMergeThreads), 0,
+                     stream, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_batch(const CacheGeom* gs, int n, const AttnJob& job, const AttnJob* apps,
+                              hipStream_t stream) {
+  if (n < 1 || n > kMaxBatchCaches) return hipErrorInvalidValue;
+  MergeBatchArgs x;
+  x.m = merge_args(gs[0], job);
+  for (int i = 0; i < n; ++i)
+    x.app[i] = job.k_new ? append_dst_of(gs[i], apps[i]) : AppendDst{nullptr, nullptr, 0, nullptr, -1, -1, 0};
+  hipLaunchKernelGGL(merge_kernel<MergeBatchArgs>, dim3((unsigned)((int64_t)n * gs[0].Hq)),
+                     dim3(kMergeThreads), 0, stream, x);
   return hipGetLastError();
 }
 

@@ -352,6 +352,11 @@ hipError_t launch_partial_batch(const CacheGeom* gs, const int64_t* T, const int
                                 int n, const AttnJob& job, hipStream_t stream);
 
 hipError_t launch_merge(const CacheGeom& g, const AttnJob& job, hipStream_t stream);
+// The merge of a batch of n caches of batch 1 (rows of cache i after those of
+// cache i - 1); with job.k_new set ([n][H_kv][d]), cache i's token goes to
+// the page, row and entry of apps[i] in cache gs[i].
+hipError_t launch_merge_batch(const CacheGeom* gs, int n, const AttnJob& job, const AttnJob* apps,
+                              hipStream_t stream);
 int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact);
 
 }  // namespace pkv

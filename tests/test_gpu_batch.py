@@ -149,3 +149,107 @@ def test_batch_errors():
     with pytest.raises(pkv.PKVError) as ei:
         pkv.decode_batch(caches, q, workspace=small)
     assert ei.value.status == 3
+
+
+def _step_twins(cfg_id, lengths, steps, kv_heads=2, store=None, rope=None, aux=False, w=None):
+    """Two identical sets of caches (one per length) with `steps` further
+    tokens per sequence: set a steps through pkv_decode_step_batch, set b
+    through pkv_decode_step per cache."""
+    import torch
+    seqs, A, Bs = [], [], []
+    for i, T in enumerate(lengths):
+        d = synth.decode_inputs(cfg_id, T=T + steps + 64 * i, B=1, kv_heads=kv_heads)
+        dt = d["cfg"]["dtype"]
+        Kd = to_dev(np.ascontiguousarray(d["K"][:, :, 64 * i:]), dt)
+        Vd = to_dev(np.ascontiguousarray(d["V"][:, :, 64 * i:]), dt)
+        for group in (A, Bs):
+            c = make_cache(d, max_tokens=T + steps, store=store, w=w)
+            if rope is not None:
+                c.set_key_rope(rope)
+            c.prefill(Kd[:, :, :T].contiguous(), Vd[:, :, :T].contiguous())
+            group.append(c)
+        seqs.append((Kd, Vd, T))
+    if aux:
+        st_a, st_b = torch.cuda.Stream(), torch.cuda.Stream()
+        for c in A:
+            c.set_aux_stream(st_a)
+        for c in Bs:
+            c.set_aux_stream(st_b)
+    return seqs, A, Bs, d
+
+
+def _run_step_twins(cfg_id, lengths, steps, n_split=4, **kw):
+    import torch
+    require_gpu()
+    seqs, A, Bs, d = _step_twins(cfg_id, lengths, steps, **kw)
+    dt = d["cfg"]["dtype"]
+    n, Hq = len(lengths), d["Hq"]
+    ws = pkv.batch_workspace(A, n_split)
+    for t in range(steps):
+        k = torch.stack([Kd[0, :, T + t] for Kd, _, T in seqs]).contiguous()
+        v = torch.stack([Vd[0, :, T + t] for _, Vd, T in seqs]).contiguous()
+        q = to_dev(synth.step_queries(cfg_id, t, n, Hq, 128, dt), dt)
+        oa = pkv.step_batch(A, k, v, q, n_split=n_split, workspace=ws)
+        for i, c in enumerate(Bs):
+            ob = c.step(k[i:i + 1].contiguous(), v[i:i + 1].contiguous(), q[i:i + 1].contiguous(), n_split=n_split)
+            torch.cuda.synchronize()
+            assert torch.equal(oa[i:i + 1], ob), (t, i)
+    torch.cuda.synchronize()
+    for a, b in zip(A, Bs):
+        assert a.state() == b.state()
+        T, nf, _ = a.state()
+        for x, y in zip(a.page_table(-(-T // 64)), b.page_table(-(-T // 64))):
+            np.testing.assert_array_equal(x, y)
+        for h in range(a.shape.n_kv_heads):
+            for f in range(nf):
+                for kind in (pkv.KEYS, pkv.VALUES):
+                    assert torch.equal(a.factor_part(0, h, f, kind), b.factor_part(0, h, f, kind))
+    return A
+
+
+@pytest.mark.parametrize("label,cfg_id,kw", [
+    ("bf16", 2, {}),
+    ("int4", 2, dict(store="int4")),
+    ("pre-RoPE", 2, dict(rope=synth.rope_inv_freq(5e5))),
+    ("aux stream", 2, dict(aux=True)),
+    ("fp32", 1, dict(kv_heads=1)),
+])
+def test_step_batch_equals_per_cache_steps(label, cfg_id, kw):
+    # an empty cache, one in the sink, and caches whose pages complete and
+    # leave the window at different steps
+    _run_step_twins(cfg_id, [0, 5, 64 * 3 + 60, 64 * 10 + 63, 64 * 20 + 1], 70, **kw)
+
+
+def test_step_batch_without_window():
+    # w = 0: a completed page is promoted by the step that completes it (the
+    # caches step one by one)
+    _run_step_twins(2, [64 * 2 + 62, 64 * 5 + 10], 70, w=0)
+
+
+def test_step_batch_against_oracle():
+    import torch
+    require_gpu()
+    cfg_id, steps = 4, 80
+    lengths = [64 * 6 + 3, 64 * 2 + 50, 17]
+    seqs, A, _, d = _step_twins(cfg_id, lengths, steps, kv_heads=1)
+    cfg = d["cfg"]
+    dt = cfg["dtype"]
+    incs = []
+    for Kd, Vd, T in seqs:
+        K64 = synth.storage_to_f64(Kd.view(torch.int16).cpu().numpy().view(np.uint16), dt)
+        V64 = synth.storage_to_f64(Vd.view(torch.int16).cpu().numpy().view(np.uint16), dt)
+        incs.append(oracle.IncrementalDecoder(K64, V64, 64, cfg["s"], cfg["w"], cfg["r_k"], cfg["r_v"], dt))
+    worst = 0.0
+    for t in range(steps):
+        k = torch.stack([Kd[0, :, T + t] for Kd, _, T in seqs]).contiguous()
+        v = torch.stack([Vd[0, :, T + t] for _, Vd, T in seqs]).contiguous()
+        qn = synth.step_queries(cfg_id, t, len(seqs), d["Hq"], 128, dt)
+        o = to_f64(pkv.step_batch(A, k, v, to_dev(qn, dt)))
+        torch.cuda.synchronize()
+        q64 = synth.storage_to_f64(qn, dt)
+        for i, (inc, (_, _, T)) in enumerate(zip(incs, seqs)):
+            ref, _ = inc.step(q64[i:i + 1], T + t + 1)
+            err = rel_err(o[i:i + 1], ref)
+            worst = max(worst, err)
+            assert err <= TOL[dt], (t, i, err)
+    print(f"[step batch vs oracle] {steps} steps x {len(seqs)} caches, worst err {worst:.3e}")

@@ -278,8 +278,11 @@ def test_batch_validation_without_gpu():
         assert L.pkv_decode_batch_workspace_bytes(hs, 0, 0, ctypes.byref(nb)) == 1
         assert L.pkv_decode_batch_workspace_bytes(hs, 33, 0, ctypes.byref(nb)) == 1
         assert L.pkv_decode_batch_workspace_bytes(hs, 2, 0, None) == 1
-        assert L.pkv_decode_batch_workspace_bytes(hs, 2, 0, ctypes.byref(nb)) == 1  # empty caches
+        assert L.pkv_decode_batch_workspace_bytes(hs, 2, 0, ctypes.byref(nb)) == 0  # empty caches: sized
+        assert nb.value > 0
         fake = ctypes.c_void_p(256 * 5000)
-        assert L.pkv_decode_attn_batch(hs, 2, fake, fake, fake, 1 << 20, 0, None) == 1
+        assert L.pkv_decode_attn_batch(hs, 2, fake, fake, fake, 1 << 20, 0, None) == 1  # nothing to attend
+        assert L.pkv_decode_step_batch(hs, 2, None, fake, fake, fake, fake, 1 << 20, 0, None) == 1
+        assert L.pkv_decode_step_batch(hs, 2, fake, fake, fake, fake, fake, 16, 0, None) == 3
     finally:
         L.pkv_cache_destroy(h)
