@@ -37,14 +37,14 @@ CACHE_DIR = os.environ.get("PKV_BENCH_CACHE", "/tmp/pkv_bench_inputs")
 # HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc runs of
 # this script (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled
 # by what the same counter reads for the 1 GiB device copy of `--workload copy`
-# (FETCH_SIZE reads 524301.7 KiB for 2^30 bytes read -> x1.99995; WRITE_SIZE
+# (FETCH_SIZE reads 524301.6 KiB for 2^30 bytes read -> x1.99995; WRITE_SIZE
 # reads 1048576 KiB for 2^30 bytes written -> x1.0).  A figure holds only for
 # the kernel sources whose hash it carries; any change to them makes it null.
 PMC_TRAFFIC = {
-    "qwen3-32b-layer-128k": {"sha256": "33ede824f159193bf0b276ed8ac1755e9e7f20901dc11a19e7bea59c47b03de4",
-                             "fetch": 303096080, "write": 1114112},
-    "qwen3-32b-layer-128k-int4": {"sha256": "33ede824f159193bf0b276ed8ac1755e9e7f20901dc11a19e7bea59c47b03de4",
-                                  "fetch": 101430898, "write": 2228224},
+    "qwen3-32b-layer-128k": {"sha256": "a540fc63791a8541acc2b6b82e06734dd0e96657af8c2ad87bb9f32f5021c975",
+                             "fetch": 303083054, "write": 1114112},
+    "qwen3-32b-layer-128k-int4": {"sha256": "a540fc63791a8541acc2b6b82e06734dd0e96657af8c2ad87bb9f32f5021c975",
+                                  "fetch": 101421083, "write": 2228307},
 }
 TRAFFIC_SOURCES = ("long_context_decode_pkv_amd/csrc/pkv_decode.hip",
                    "long_context_decode_pkv_amd/csrc/pkv_internal.h")
