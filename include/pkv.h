@@ -284,9 +284,12 @@ int32_t pkv_promote_page(pkv_cache* cache, void* stream);
  * whose K and V ranks pad to the same multiple of 8; other formats launch
  * once per cache.  Then one merge launch.  workspace: 256-byte aligned
  * device memory of pkv_decode_batch_workspace_bytes(caches, n, n_split)
- * bytes (which also takes empty caches).  Every cache's range is cut into n_split parts (0: the library's
- * count for the batch's longest cache), and row i equals pkv_decode_attn on
- * cache i with the same n_split bit for bit.
+ * bytes (which also takes empty caches).  n_split > 0: every cache's range
+ * is cut into n_split parts, and row i equals pkv_decode_attn on cache i
+ * with that n_split bit for bit.  n_split = 0: the library gives each cache
+ * splits in proportion to its pages (the workgroups of one round of the GPU
+ * shared out; formats without a batched kernel use one count), and rows
+ * agree with per-cache calls to fp32 rounding.
  * Errors: INVALID_ARG (null or misaligned pointers, n out of range, shapes
  * that differ, an empty cache), CAPACITY (workspace too small).
  */

@@ -843,12 +843,17 @@ int32_t batch_plan(const pkv_cache* const* caches, int32_t n, int32_t n_split, i
   }
   CacheGeom g = geom_of(caches[0]);
   g.B = n;  // the batch's (sequence, KV head) pairs
-  // Every cache's range takes all the splits.  (Shares in proportion to the
-  // lengths left idle workgroups in the grid that pushed active ones into a
-  // second round: 8 caches of 32K..4K tokens, 42.3 us uniform, 51.7 us
-  // proportional.)
-  *ns = n_split > 0 ? n_split : decode_default_splits(g, T_max, nf_max);
-  for (int i = 0; i < n; ++i) ns_seq[i] = *ns;
+  if (n_split == 0 && batched_kernel(g)) {
+    // the library's count: splits in proportion to each cache's pages
+    int64_t T[kMaxBatchCaches];
+    for (int i = 0; i < n; ++i) T[i] = caches[i]->T;
+    *ns = decode_batch_splits(g, T, n, ns_seq);
+  } else {
+    // every cache's range in n_split parts (the per-cache launches of formats
+    // without a batched kernel share one split count too)
+    *ns = n_split > 0 ? n_split : decode_default_splits(g, T_max, nf_max);
+    for (int i = 0; i < n; ++i) ns_seq[i] = *ns;
+  }
   const uint64_t rows = (uint64_t)n * g.Hq * *ns;
   *need = align_up(rows * kD * 4) + align_up(rows * 2 * 4);
   return PKV_OK;
@@ -908,11 +913,7 @@ int32_t pkv_decode_attn_batch(const pkv_cache* const* caches, int32_t n, const v
       e = launch_partial(gs[i], ji, s);
     }
   }
-  if (e == hipSuccess) {
-    CacheGeom gm = gs[0];
-    gm.B = n;
-    e = launch_merge(gm, job, s);
-  }
+  if (e == hipSuccess) e = launch_merge_batch(gs, n, job, nullptr, ns_seq, s);
   return dev_status(e);
 }
 
@@ -1101,7 +1102,7 @@ int32_t pkv_decode_step_batch(pkv_cache* const* caches, int32_t n, const void* k
   }
   job.k_new = k_new;
   job.v_new = v_new;
-  if (e == hipSuccess) e = launch_merge_batch(gs, n, job, apps, s);
+  if (e == hipSuccess) e = launch_merge_batch(gs, n, job, apps, ns_seq, s);
   if (e != hipSuccess) return PKV_ERR_DEVICE;
   for (int i = 0; i < n; ++i) {
     pkv_cache* c = caches[i];

@@ -23,6 +23,7 @@
 //
 // fp32 path and shapes the matrix-core kernel does not cover
 // (decode_valu_kernel): plain fp32 VALU arithmetic, one workgroup per split.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <type_traits>
@@ -86,11 +87,15 @@ struct BatchSeq {
   const void* win_v;
   const int32_t* table;
   int64_t T, n_fact, F_max;
-  int n_split;  // splits of this cache's range (<= the grid's); the others stay empty
+  int split_base;  // first grid column of this cache's splits
+  int n_split;     // its splits (the workspace rows keep the batch's stride)
 };
 
+// A batched launch's grid is compact: column x belongs to the cache whose
+// splits [split_base, split_base + n_split) contain it.
 struct DecodeBatchArgs {
   DecodeArgs a;  // what the caches share (their per-cache fields unused)
+  int n_seq;
   BatchSeq seq[kMaxBatchCaches];
 };
 
@@ -105,18 +110,26 @@ struct SeqView {
   const int32_t* table;
   int64_t T, n_fact, F_max;
   int b_pool;
-  int n_split;  // workgroups x < n_split share the range; the others leave empty states
+  int n_split;  // splits sharing this range
+  int b;        // sequence row of q, the workspace and out
+  int split;    // this workgroup's split
 };
 
 __device__ inline const DecodeArgs& common_args(const DecodeArgs& a) { return a; }
 __device__ inline const DecodeArgs& common_args(const DecodeBatchArgs& x) { return x.a; }
 
-__device__ inline SeqView seq_view(const DecodeArgs& a, int b) {
-  return SeqView{a.fac, a.sink_k, a.sink_v, a.win_k, a.win_v, a.table, a.T, a.n_fact, a.F_max, b, a.n_split};
+__device__ inline SeqView seq_view(const DecodeArgs& a) {
+  const int b = blockIdx.z;
+  return SeqView{a.fac, a.sink_k, a.sink_v, a.win_k, a.win_v, a.table, a.T, a.n_fact, a.F_max,
+                 b, a.n_split, b, (int)blockIdx.x};
 }
-__device__ inline SeqView seq_view(const DecodeBatchArgs& x, int b) {
-  const BatchSeq& s = x.seq[b];
-  return SeqView{s.fac, s.sink_k, s.sink_v, s.win_k, s.win_v, s.table, s.T, s.n_fact, s.F_max, 0, s.n_split};
+__device__ inline SeqView seq_view(const DecodeBatchArgs& x) {
+  const int col = blockIdx.x;
+  int i = 0;
+  while (i + 1 < x.n_seq && col >= x.seq[i + 1].split_base) ++i;  // uniform, <= 32 steps
+  const BatchSeq& s = x.seq[i];
+  return SeqView{s.fac, s.sink_k, s.sink_v, s.win_k, s.win_v, s.table, s.T, s.n_fact, s.F_max,
+                 0, s.n_split, i, col - s.split_base};
 }
 
 __device__ inline int64_t unit_bound(const WorkList& w, const DecodeArgs& a, int64_t wi,
@@ -1170,7 +1183,7 @@ struct WaveMergeLds {
 template <class F, class KA>
 __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(KA kargs) {
   const DecodeArgs& a = common_args(kargs);
-  const SeqView sv = seq_view(kargs, blockIdx.z);
+  const SeqView sv = seq_view(kargs);
   constexpr int kLdsMain = F::kLdsBytes > (int)sizeof(WaveMergeLds) ? F::kLdsBytes : (int)sizeof(WaveMergeLds);
   constexpr int kLdsMainAligned = (kLdsMain + 15) / 16 * 16;
   constexpr int kLds = kLdsMainAligned + (F::kRope ? (int)sizeof(RopeLds) : 0);
@@ -1185,16 +1198,14 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(KA k
   const int n = lane & 15, q4 = lane >> 4;
   const float rem = n >= 8 ? 1.f : 0.f;  // remainder column
   const int g = n & 7;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int split = sv.split, h = blockIdx.y, b = sv.b;
   const int Hq = a.Hkv * a.G;
   const int64_t bh = (int64_t)sv.b_pool * a.Hkv + h;  // (sequence, KV head) in the pools
 
   const WorkList wl = work_list(sv.T, sv.n_fact, a.n_s);
   const int64_t W = (int64_t)sv.n_split * kWaves;
   const int64_t wi = (int64_t)split * kWaves + wave;
-  const bool idle = split >= sv.n_split;  // beyond this cache's splits: an empty state
-  const int64_t e0 = idle ? wl.D + wl.F : unit_bound(wl, a, wi, W);
-  const int64_t e1 = idle ? wl.D + wl.F : unit_bound(wl, a, wi + 1, W);
+  const int64_t e0 = unit_bound(wl, a, wi, W), e1 = unit_bound(wl, a, wi + 1, W);
   // the factor slot of logical page n_s + f is f (pages are factorized in
   // order and never revisited), so unit e >= D lives in slot e - D
   const uint8_t* fac_bh = sv.fac + bh * sv.F_max * a.page_bytes;
@@ -1421,7 +1432,7 @@ __device__ inline float ld_elem(const void* base, int64_t idx) {
 template <typename Elem, bool kRope, class KA>
 __global__ __launch_bounds__(256) void decode_valu_kernel(KA kargs) {
   const DecodeArgs& a = common_args(kargs);
-  const SeqView sv = seq_view(kargs, blockIdx.z);
+  const SeqView sv = seq_view(kargs);
   // pre-RoPE keys: the page's keys, stored or reconstructed, then rotated
   __shared__ float kr[kRope ? kP : 1][kRope ? kD + 1 : 1];
   __shared__ float qs[kMaxG][kD];
@@ -1433,7 +1444,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(KA kargs) {
   __shared__ float sh_l[kMaxG];
 
   const int tid = threadIdx.x;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int split = sv.split, h = blockIdx.y, b = sv.b;
   const int G = a.G;
   const int Hq = a.Hkv * G;
   const int64_t bh = (int64_t)sv.b_pool * a.Hkv + h;  // (sequence, KV head) in the pools
@@ -1452,9 +1463,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(KA kargs) {
   __syncthreads();
 
   const WorkList wl = work_list(sv.T, sv.n_fact, a.n_s);
-  const bool idle = split >= sv.n_split;  // beyond this cache's splits: an empty state
-  const int64_t e0 = idle ? wl.D + wl.F : unit_bound(wl, a, split, sv.n_split);
-  const int64_t e1 = idle ? wl.D + wl.F : unit_bound(wl, a, split + 1, sv.n_split);
+  const int64_t e0 = unit_bound(wl, a, split, sv.n_split), e1 = unit_bound(wl, a, split + 1, sv.n_split);
   for (int64_t e = e0; e < e1; ++e) {
     const int64_t p = unit_page(wl, a, e);
     const int32_t ent = sv.table[p];
@@ -1632,8 +1641,9 @@ struct MergeArgs {
 // The merge of a batch of caches of batch 1 (pkv_decode_step_batch): rows of
 // cache i follow those of cache i - 1; cache i's token goes to app[i].
 struct MergeBatchArgs {
-  MergeArgs m;
+  MergeArgs m;                    // m.n_split: the workspace's row stride
   AppendDst app[kMaxBatchCaches];
+  int ns[kMaxBatchCaches];        // splits holding cache i's states
 };
 
 __device__ inline const MergeArgs& merge_common(const MergeArgs& m) { return m; }
@@ -1647,6 +1657,8 @@ __device__ inline int64_t append_pool_seq(const MergeBatchArgs&, int64_t) { retu
 // per cache: once per launch, or once per cache of a batch)
 __device__ inline bool writes_table(const MergeArgs&, int64_t seq) { return seq == 0; }
 __device__ inline bool writes_table(const MergeBatchArgs&, int64_t) { return true; }
+__device__ inline int split_count(const MergeArgs& m, int64_t) { return m.n_split; }
+__device__ inline int split_count(const MergeBatchArgs& x, int64_t seq) { return x.ns[seq]; }
 
 __device__ inline float load_elem(const void* p, int64_t i, int dtype) {
   if (dtype == PKV_BF16) return __uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
@@ -1673,15 +1685,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MA margs) {
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int grp = tid / (kD / 4), c4 = tid % (kD / 4);
-  const int n_split = m.n_split;
-  const float2* ml = (const float2*)(m.ws_ml + row * n_split * 2);
-  const float4* op = (const float4*)(m.ws_o + row * n_split * kD) + c4;
-
-  // loads
-  float qk = 0.f;
   const int Hq = m.G * m.Hkv;
   const int hq = (int)(row % Hq);
   const int64_t seq = row / Hq;
+  const int n_split = split_count(margs, seq);  // this row's states, m.n_split apart
+  const float2* ml = (const float2*)(m.ws_ml + row * m.n_split * 2);
+  const float4* op = (const float4*)(m.ws_o + row * m.n_split * kD) + c4;
+
+  // loads
+  float qk = 0.f;
   const int64_t bh = seq * m.Hkv + hq / m.G;  // (sequence, KV head) of k_new / v_new
   const AppendDst& ad = append_dst(margs, seq);
   if (m.k_new && tid < kD) {
@@ -1861,6 +1873,40 @@ AppendDst append_dst_of(const CacheGeom& g, const AttnJob& job) {
 
 }  // namespace
 
+bool batched_kernel(const CacheGeom& g) {
+  const int n8k = (g.r_k + 7) / 8, n8v = (g.r_v + 7) / 8;
+  if (n8k != n8v) return false;
+  if (g.dtype == PKV_BF16_INT4) return n8k <= 4;
+  return g.dtype == PKV_BF16 && n8k <= 8 && (!g.rope || n8k <= kRopeMfmaMaxN8);
+}
+
+int decode_batch_splits(const CacheGeom& g, const int64_t* T, int n, int* ns) {
+  // Workgroups that fill the chip in one round (two per CU at two waves per
+  // SIMD), shared in proportion to the caches' pages: each cache's split
+  // gets about q pages, the smallest q (at least 8 pages per wave) whose
+  // splits all fit.  The longest cache then bounds the launch with runs as
+  // short as the others'.
+  const int wps = g.dtype == PKV_BF16 && !g.rope ? mfma_waves_per_simd((g.r_k > g.r_v ? g.r_k + 7 : g.r_v + 7) / 8) : 2;
+  const int64_t budget = (256LL * wps) / g.Hkv;  // splits over all caches
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) total += (T[i] + kP - 1) / kP;
+  int64_t q = budget > 0 ? (total + budget - 1) / budget : total;
+  if (q < 4 * 8) q = 4 * 8;
+  for (;; ++q) {
+    int64_t sum = 0;
+    for (int i = 0; i < n; ++i) sum += std::max<int64_t>(1, ((T[i] + kP - 1) / kP + q - 1) / q);
+    if (sum <= std::max<int64_t>(budget, n)) break;
+  }
+  int grid = 1;
+  for (int i = 0; i < n; ++i) {
+    int64_t s = std::max<int64_t>(1, ((T[i] + kP - 1) / kP + q - 1) / q);
+    if (s > kMaxSplits) s = kMaxSplits;
+    ns[i] = (int)s;
+    grid = std::max(grid, ns[i]);
+  }
+  return grid;
+}
+
 hipError_t launch_merge(const CacheGeom& g, const AttnJob& job, hipStream_t stream) {
   MergeArgs m = merge_args(g, job);
   if (job.k_new) m.app = append_dst_of(g, job);
@@ -1869,13 +1915,15 @@ hipError_t launch_merge(const CacheGeom& g, const AttnJob& job, hipStream_t stre
   return hipGetLastError();
 }
 
-hipError_t launch_merge_batch(const CacheGeom* gs, int n, const AttnJob& job, const AttnJob* apps,
+hipError_t launch_merge_batch(const CacheGeom* gs, int n, const AttnJob& job, const AttnJob* apps, const int* ns,
                               hipStream_t stream) {
   if (n < 1 || n > kMaxBatchCaches) return hipErrorInvalidValue;
   MergeBatchArgs x;
   x.m = merge_args(gs[0], job);
-  for (int i = 0; i < n; ++i)
+  for (int i = 0; i < n; ++i) {
     x.app[i] = job.k_new ? append_dst_of(gs[i], apps[i]) : AppendDst{nullptr, nullptr, 0, nullptr, -1, -1, 0};
+    x.ns[i] = ns[i];
+  }
   hipLaunchKernelGGL(merge_kernel<MergeBatchArgs>, dim3((unsigned)((int64_t)n * gs[0].Hq)),
                      dim3(kMergeThreads), 0, stream, x);
   return hipGetLastError();
@@ -1972,7 +2020,7 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
       default:
         return hipErrorInvalidValue;
     }
-  } else if (kBatch) {
+  } else if constexpr (kBatch) {
     return hipErrorNotSupported;
   } else if (g.dtype == PKV_BF16) {
     if (g.rope)
@@ -2003,13 +2051,17 @@ hipError_t launch_partial_batch(const CacheGeom* gs, const int64_t* T, const int
   if (n < 1 || n > kMaxBatchCaches) return hipErrorInvalidValue;
   DecodeBatchArgs x;
   x.a = make_args(gs[0], job);
+  x.n_seq = n;
+  int cols = 0;
   for (int i = 0; i < n; ++i) {
     const CacheGeom& g = gs[i];
+    if (ns[i] < 1 || ns[i] > job.n_split) return hipErrorInvalidValue;
     x.seq[i] = BatchSeq{g.base + g.lay.factors, g.base + g.lay.sink_k, g.base + g.lay.sink_v,
                         g.base + g.lay.win_k, g.base + g.lay.win_v,
-                        (const int32_t*)(g.base + g.lay.page_table), T[i], n_fact[i], g.F_max, ns[i]};
+                        (const int32_t*)(g.base + g.lay.page_table), T[i], n_fact[i], g.F_max, cols, ns[i]};
+    cols += ns[i];
   }
-  return dispatch_partial(gs[0], x, dim3(job.n_split, gs[0].Hkv, n), stream);
+  return dispatch_partial(gs[0], x, dim3(cols, gs[0].Hkv, 1), stream);
 }
 
 }  // namespace pkv

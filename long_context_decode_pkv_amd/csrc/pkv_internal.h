@@ -345,18 +345,24 @@ struct AttnJob {
 
 hipError_t launch_partial(const CacheGeom& g, const AttnJob& job, hipStream_t stream);
 // One launch over n <= kMaxBatchCaches caches of batch 1 and equal shape
-// (gs[i], lengths T[i], factor counts n_fact[i]); workgroup z takes cache z,
-// whose range is shared by the first ns[i] <= job.n_split splits.
+// (gs[i], lengths T[i], factor counts n_fact[i]); cache i's range is shared
+// by ns[i] <= job.n_split splits, its workspace rows job.n_split apart.
 // hipErrorNotSupported for formats without a batched kernel.
 hipError_t launch_partial_batch(const CacheGeom* gs, const int64_t* T, const int64_t* n_fact, const int* ns,
                                 int n, const AttnJob& job, hipStream_t stream);
 
 hipError_t launch_merge(const CacheGeom& g, const AttnJob& job, hipStream_t stream);
 // The merge of a batch of n caches of batch 1 (rows of cache i after those of
-// cache i - 1); with job.k_new set ([n][H_kv][d]), cache i's token goes to
-// the page, row and entry of apps[i] in cache gs[i].
-hipError_t launch_merge_batch(const CacheGeom* gs, int n, const AttnJob& job, const AttnJob* apps,
+// cache i - 1, each with ns[i] states, job.n_split apart); with job.k_new set
+// ([n][H_kv][d]), cache i's token goes to the page, row and entry of apps[i]
+// in cache gs[i].
+hipError_t launch_merge_batch(const CacheGeom* gs, int n, const AttnJob& job, const AttnJob* apps, const int* ns,
                               hipStream_t stream);
+// Whether a batch of caches of this shape has a batched partial kernel.
+bool batched_kernel(const CacheGeom& g);
+// Splits per cache of a batched launch with caller-chosen count 0 (ns[i]),
+// in proportion to the caches' pages; returns the largest.
+int decode_batch_splits(const CacheGeom& g, const int64_t* T, int n, int* ns);
 int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact);
 
 }  // namespace pkv

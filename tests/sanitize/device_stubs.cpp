@@ -27,8 +27,13 @@ hipError_t launch_partial_batch(const CacheGeom*, const int64_t*, const int64_t*
   return hipErrorNotSupported;
 }
 hipError_t launch_merge(const CacheGeom&, const AttnJob&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_merge_batch(const CacheGeom*, int, const AttnJob&, const AttnJob*, hipStream_t) {
+hipError_t launch_merge_batch(const CacheGeom*, int, const AttnJob&, const AttnJob*, const int*, hipStream_t) {
   return hipErrorNotSupported;
 }
 int decode_default_splits(const CacheGeom&, int64_t, int64_t) { return 1; }
+bool batched_kernel(const CacheGeom&) { return true; }
+int decode_batch_splits(const CacheGeom&, const int64_t*, int n, int* ns) {
+  for (int i = 0; i < n; ++i) ns[i] = 1;
+  return 1;
+}
 }  // namespace pkv
