@@ -27,8 +27,10 @@
  *    the INT4 factors of Sec. 4.3).  K, V, q and the dense pages have the
  *    cache's element type (bf16 for PKV_BF16_INT4); attention output is
  *    float32.
- *  - Fixed in this version: head_dim d = 128 and page length P = 64 (other
- *    values return PKV_ERR_UNSUPPORTED); GQA group size G = H_q / H_kv <= 8.
+ *  - Fixed in this version: head_dim d = 128, page length P = 64 or 32
+ *    (P = 32: PKV_BF16 and PKV_F32 storage, attention on the vector-ALU
+ *    kernel; other values return PKV_ERR_UNSUPPORTED); GQA group size
+ *    G = H_q / H_kv <= 8.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -43,7 +45,7 @@ extern "C" {
 typedef enum pkv_status {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = 1,       /* bad size, null or misaligned pointer, bad combination */
-  PKV_ERR_UNSUPPORTED = 2,       /* valid for the method, not implemented (d != 128, P != 64, G > 8) */
+  PKV_ERR_UNSUPPORTED = 2,       /* valid for the method, not implemented (d != 128, P not 64 or 32, G > 8) */
   PKV_ERR_CAPACITY = 3,          /* more tokens than max_tokens, workspace too small */
   PKV_ERR_NOT_ELIGIBLE = 4,      /* promotion requested with no page waiting */
   PKV_ERR_PROMOTION_PENDING = 5, /* append refused: a completed page must be promoted first */
@@ -82,7 +84,8 @@ typedef struct pkv_shape {
   int32_t n_q_heads;  /* H_q */
   int32_t n_kv_heads; /* H_kv, H_q % H_kv == 0; query head h reads KV head h / G */
   int32_t head_dim;   /* d (must be 128) */
-  int32_t page_len;   /* P (must be 64) */
+  int32_t page_len;   /* P: 64, or 32 (Sec. 4.1 default) for PKV_BF16 / PKV_F32
+                         storage, whose attention runs on vector ALUs */
   int32_t rank_k;     /* r_K, 1 <= r_K <= min(P, d) */
   int32_t rank_v;     /* r_V, 1 <= r_V <= min(P, d) */
   int32_t sink;       /* s: dense sink tokens, a multiple of P (may be 0) */
@@ -100,10 +103,11 @@ typedef struct pkv_shape {
  *   win_v   [B][H_kv][n_w+1][d][P]      ring of value pages, transposed
  *   factors [B][H_kv][F_max][factor_page_bytes]   K part, then V part
  *   page_table [max_pages] int32: (class << 24) | slot
- * The factor parts use a fixed interleaved order matched to the attention
- * kernel's matrix-core register layout; pkv_pack_factors and
- * pkv_unpack_factors convert between it and row-major Lf (P x r), Rf (r x d).
- * Ranks are padded to a multiple of 8 inside a part (padding is zero).
+ * With P = 64 the factor parts use a fixed interleaved order matched to the
+ * attention kernel's matrix-core register layout, ranks padded to a multiple
+ * of 8 (padding is zero); with P = 32 they hold plain row-major blocks at the
+ * exact rank.  pkv_pack_factors and pkv_unpack_factors convert between
+ * either and row-major Lf (P x r), Rf (r x d).
  * PKV_BF16_INT4 parts hold codes and scales in their own interleaved order;
  * pkv_pack_factors_int4 and pkv_unpack_factors_int4 convert it.
  */
@@ -116,8 +120,9 @@ typedef struct pkv_layout {
   int64_t max_pages;         /* ceil(T_max / P) */
   int64_t elem_bytes;        /* bytes of a dense element: 2 (bf16, bf16+int4) or 4 (f32) */
   int64_t dense_page_bytes;  /* P * d * elem_bytes */
-  int64_t factor_k_elems;    /* packed elements (INT4: codes) of a K part: r8_K (P + d) */
-  int64_t factor_v_elems;    /* r8_V (P + d) */
+  int64_t factor_k_elems;    /* packed elements (INT4: codes) of a K part: r8_K (P + d);
+                                P = 32: r_K (P + d) */
+  int64_t factor_v_elems;    /* r8_V (P + d); P = 32: r_V (P + d) */
   int64_t factor_page_bytes; /* factor_k_bytes + factor_v_bytes */
   int64_t factor_k_bytes;    /* bytes of a K part (its offset in the page is 0) */
   int64_t factor_v_bytes;    /* bytes of a V part (offset factor_k_bytes) */
@@ -148,8 +153,10 @@ double pkv_storage_ratio(int32_t P, int32_t r_k, int32_t r_v, int32_t d);
 int32_t pkv_classify(int64_t T, int32_t P, int32_t s, int32_t w, int64_t n_fact, int32_t* cls,
                      int32_t* slot, int64_t n_pages);
 
-/* Packed elements of one factor part for rank r (= r8 (P + d), r8 = r
- * rounded up to a multiple of 8).  Host only. */
+/* Packed elements of one factor part for rank r: r8 (P + d) with r8 = r
+ * rounded up to a multiple of 8 at P = 64, r (P + d) at P = 32.  Errors:
+ * UNSUPPORTED for other P or d != 128; INVALID_ARG unless 1 <= r <= P.
+ * Host only. */
 int32_t pkv_factor_part_elems(int32_t P, int32_t d, int32_t r, int64_t* elems);
 
 /*
@@ -211,8 +218,9 @@ int32_t pkv_cache_state(const pkv_cache* cache, int64_t* T, int64_t* n_fact, int
  * so Lf Rf is the rank-r truncated SVD of X (Sec. 3.2; Eckart-Young-Mirsky).
  * Outputs (device, row-major, `out_dtype`): Lf [n_pages][P][r],
  * Rf [n_pages][r][d]; sigma [n_pages][r] float32 (may be NULL).  Rows with
- * sigma = 0 are zero.  Errors: INVALID_ARG (null/misaligned pointers, bad r),
- * UNSUPPORTED (P != 64 or d != 128), DEVICE (launch failure).
+ * sigma = 0 are zero.  P = 32 pages are decomposed as 64-row pages padded
+ * with zero rows.  Errors: INVALID_ARG (null/misaligned pointers, bad r),
+ * UNSUPPORTED (P not 64 or 32, or d != 128), DEVICE (launch failure).
  */
 int32_t pkv_compress_pages(const void* X, int64_t n_pages, int32_t P, int32_t d, int32_t r,
                            int32_t in_dtype, int32_t out_dtype, void* Lf, void* Rf, float* sigma,

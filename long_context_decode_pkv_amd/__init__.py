@@ -180,24 +180,28 @@ def factor_part_elems(r: int, P: int = PAGE_LEN, d: int = HEAD_DIM) -> int:
     return n.value
 
 
-def pack_factors(kind: int, r: int, dtype: int, Lf, Rf) -> np.ndarray:
+def pack_factors(kind: int, r: int, dtype: int, Lf, Rf, P: int = PAGE_LEN) -> np.ndarray:
     """Row-major float32 Lf (P x r), Rf (r x d) -> one packed factor part
     (uint16 bf16 bits or float32)."""
     Lf = np.ascontiguousarray(Lf, dtype=np.float32)
     Rf = np.ascontiguousarray(Rf, dtype=np.float32)
-    n = factor_part_elems(r)
+    if Lf.shape != (P, r) or Rf.shape != (r, HEAD_DIM):
+        raise ValueError("factor shapes do not match the part")
+    n = factor_part_elems(r, P)
     out = np.zeros(n, dtype=np.uint16 if dtype == BF16 else np.float32)
-    _check(lib().pkv_pack_factors(kind, PAGE_LEN, HEAD_DIM, r, dtype, _np_ptr(Lf), _np_ptr(Rf),
+    _check(lib().pkv_pack_factors(kind, P, HEAD_DIM, r, dtype, _np_ptr(Lf), _np_ptr(Rf),
                                   _np_ptr(out)), "pkv_pack_factors")
     return out
 
 
-def unpack_factors(kind: int, r: int, dtype: int, packed):
+def unpack_factors(kind: int, r: int, dtype: int, packed, P: int = PAGE_LEN):
     """One packed factor part -> float32 Lf (P x r), Rf (r x d)."""
     packed = np.ascontiguousarray(packed, dtype=np.uint16 if dtype == BF16 else np.float32)
-    Lf = np.zeros((PAGE_LEN, r), dtype=np.float32)
+    if packed.size < factor_part_elems(r, P):
+        raise ValueError("packed part too small")
+    Lf = np.zeros((P, r), dtype=np.float32)
     Rf = np.zeros((r, HEAD_DIM), dtype=np.float32)
-    _check(lib().pkv_unpack_factors(kind, PAGE_LEN, HEAD_DIM, r, dtype, _np_ptr(packed),
+    _check(lib().pkv_unpack_factors(kind, P, HEAD_DIM, r, dtype, _np_ptr(packed),
                                     _np_ptr(Lf), _np_ptr(Rf)), "pkv_unpack_factors")
     return Lf, Rf
 
@@ -256,17 +260,19 @@ def cache_layout(shape: Shape) -> dict:
 # ------------------------------------------------------------------ device
 
 def compress_pages(X, r: int, out_dtype=None, with_sigma: bool = True):
-    """Batched page decomposition: X (n, 64, 128) bf16 / f32 device tensor ->
-    Lf (n, 64, r), Rf (n, r, 128) in out_dtype (default X's), sigma (n, r) f32."""
+    """Batched page decomposition: X (n, P, 128) bf16 / f32 device tensor,
+    P = 64 or 32 -> Lf (n, P, r), Rf (n, r, 128) in out_dtype (default X's),
+    sigma (n, r) f32."""
     import torch
-    if X.dim() != 3 or X.shape[1:] != (PAGE_LEN, HEAD_DIM):
-        raise ValueError("X must be (n_pages, 64, 128)")
+    if X.dim() != 3 or X.shape[2] != HEAD_DIM:
+        raise ValueError("X must be (n_pages, P, 128)")
+    P = X.shape[1]
     out_dtype = X.dtype if out_dtype is None else out_dtype
     n = X.shape[0]
-    Lf = torch.empty((n, PAGE_LEN, r), dtype=out_dtype, device=X.device)
+    Lf = torch.empty((n, P, r), dtype=out_dtype, device=X.device)
     Rf = torch.empty((n, r, HEAD_DIM), dtype=out_dtype, device=X.device)
     sg = torch.empty((n, r), dtype=torch.float32, device=X.device) if with_sigma else None
-    _check(lib().pkv_compress_pages(_dev_ptr(X, what="X"), n, PAGE_LEN, HEAD_DIM, r,
+    _check(lib().pkv_compress_pages(_dev_ptr(X, what="X"), n, P, HEAD_DIM, r,
                                     _dtype_code(X.dtype), _dtype_code(out_dtype),
                                     ctypes.c_void_p(Lf.data_ptr()), ctypes.c_void_p(Rf.data_ptr()),
                                     ctypes.c_void_p(sg.data_ptr()) if sg is not None else None,
@@ -278,7 +284,7 @@ class Cache:
     """One layer's hybrid PuzzleKV cache over a torch-owned device buffer."""
 
     def __init__(self, batch, n_q_heads, n_kv_heads, rank_k, rank_v, sink, window, max_tokens,
-                 dtype="bf16", device="cuda:0"):
+                 dtype="bf16", device="cuda:0", page_len=PAGE_LEN):
         import torch
         self.device = torch.device(device)
         if dtype in ("bf16", torch.bfloat16):
@@ -293,7 +299,7 @@ class Cache:
         self.elem_code = F32 if self.dtype_code == F32 else BF16
         self.torch_dtype = torch.float32 if self.dtype_code == F32 else torch.bfloat16
         self.shape = make_shape(batch, n_q_heads, n_kv_heads, rank_k, rank_v, sink, window,
-                                max_tokens, self.dtype_code)
+                                max_tokens, self.dtype_code, page_len=page_len)
         self.layout = cache_layout(self.shape)
         self.buffer = torch.empty(self.layout["total_bytes"], dtype=torch.uint8, device=self.device)
         h = ctypes.c_void_p()

@@ -67,7 +67,8 @@ int32_t check_shape(const pkv_shape* s) {
   if (s->rank_k < 1 || s->rank_v < 1 || s->rank_k > rmax || s->rank_v > rmax)
     return PKV_ERR_INVALID_ARG;
   if (s->max_tokens < 1) return PKV_ERR_INVALID_ARG;
-  if (s->head_dim != kD || s->page_len != kP) return PKV_ERR_UNSUPPORTED;
+  if (s->head_dim != kD || (s->page_len != kP && s->page_len != kMinP)) return PKV_ERR_UNSUPPORTED;
+  if (s->page_len != kP && s->dtype == PKV_BF16_INT4) return PKV_ERR_UNSUPPORTED;
   if (s->n_q_heads / s->n_kv_heads > kMaxG) return PKV_ERR_UNSUPPORTED;
   if (s->dtype == PKV_BF16_INT4 && (s->rank_k > kQ4MaxRank || s->rank_v > kQ4MaxRank))
     return PKV_ERR_UNSUPPORTED;
@@ -85,8 +86,8 @@ void make_layout(const pkv_shape* s, pkv_layout* L) {
   const int64_t fmax = s->max_tokens / P - n_s - n_w;
   L->max_fact_pages = fmax > 0 ? fmax : 0;
   L->dense_page_bytes = P * d * L->elem_bytes;
-  L->factor_k_elems = part_elems(s->rank_k);
-  L->factor_v_elems = part_elems(s->rank_v);
+  L->factor_k_elems = part_elems(s->rank_k, (int)P);
+  L->factor_v_elems = part_elems(s->rank_v, (int)P);
   if (s->dtype == PKV_BF16_INT4) {
     L->factor_k_bytes = q4_dims(s->rank_k).k_bytes;
     L->factor_v_bytes = q4_dims(s->rank_v).v_bytes;
@@ -119,6 +120,7 @@ CacheGeom geom_of(const pkv_cache* c) {
   g.Hkv = c->shape.n_kv_heads;
   g.Hq = c->shape.n_q_heads;
   g.G = g.Hq / g.Hkv;
+  g.P = c->shape.page_len;
   g.n_s = c->shape.sink / c->shape.page_len;
   g.n_w = c->shape.window / c->shape.page_len;
   g.F_max = c->lay.max_fact_pages;
@@ -163,7 +165,7 @@ float bf16_round_host(float x, uint16_t* bits) {
 // factor slots p - n_s.
 CompressSrc ring_src(const pkv_cache* c, int64_t p_lo) {
   const CacheGeom g = geom_of(c);
-  const int64_t ppg = (int64_t)kP * kD;
+  const int64_t ppg = (int64_t)g.P * kD;
   CompressSrc src;
   std::memset(&src, 0, sizeof(src));
   src.base[0] = c->base + c->lay.win_k;
@@ -188,7 +190,7 @@ CompressSrc dense_src(const pkv_cache* c, const void* K, const void* V, int64_t 
   src.base[0] = (const uint8_t*)K + row0 * kD * esz;
   src.base[1] = (const uint8_t*)V + row0 * kD * esz;
   src.bh_stride = T * kD;
-  src.f_stride = (int64_t)kP * kD;
+  src.f_stride = (int64_t)c->shape.page_len * kD;
   src.out_f0 = out_f0;
   return src;
 }
@@ -203,6 +205,7 @@ hipError_t factorize(const pkv_cache* c, const CompressSrc& a, int64_t n0, const
   CompressJob job;
   std::memset(&job, 0, sizeof(job));
   job.n_kind = 2;
+  job.page_rows = g.P;
   job.n_f = n0 + n1;
   job.n_f_src0 = n0;
   job.n_pages = (int64_t)g.B * g.Hkv * job.n_f * 2;
@@ -356,9 +359,9 @@ int32_t pkv_classify(int64_t T, int32_t P, int32_t s, int32_t w, int64_t n_fact,
 
 int32_t pkv_factor_part_elems(int32_t P, int32_t d, int32_t r, int64_t* elems) {
   if (!elems) return PKV_ERR_INVALID_ARG;
-  if (P != kP || d != kD) return PKV_ERR_UNSUPPORTED;
-  if (r < 1 || r > kP) return PKV_ERR_INVALID_ARG;
-  *elems = part_elems(r);
+  if ((P != kP && P != kMinP) || d != kD) return PKV_ERR_UNSUPPORTED;
+  if (r < 1 || r > P) return PKV_ERR_INVALID_ARG;
+  *elems = part_elems(r, P);
   return PKV_OK;
 }
 
@@ -370,8 +373,8 @@ int32_t pkv_pack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t 
   if ((kind != PKV_KEYS && kind != PKV_VALUES && kind != PKV_KEYS_PRE_ROPE) ||
       (dtype != PKV_BF16 && dtype != PKV_F32) || !Lf || !Rf || !packed)
     return PKV_ERR_INVALID_ARG;
-  const PackDims pd = pack_dims(r);
-  const int r8 = 8 * pd.n8;
+  const PackDims pd = pack_dims(r, P);
+  const int r8 = pd.rs;  // stored ranks, the padding ones zero
   auto put = [&](int64_t idx, float v) {
     if (dtype == PKV_BF16) {
       uint16_t b;
@@ -386,7 +389,7 @@ int32_t pkv_pack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t 
       const float v = i < r ? Rf[(int64_t)i * kD + c] : 0.f;
       put(off_rf(kind, pd, i, c), v);
     }
-    for (int j = 0; j < kP; ++j) {
+    for (int j = 0; j < P; ++j) {
       const float v = i < r ? Lf[(int64_t)j * r + i] : 0.f;
       put(off_lf(kind, pd, j, i), v);
     }
@@ -402,7 +405,7 @@ int32_t pkv_unpack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_
   if ((kind != PKV_KEYS && kind != PKV_VALUES && kind != PKV_KEYS_PRE_ROPE) ||
       (dtype != PKV_BF16 && dtype != PKV_F32) || !Lf || !Rf || !packed)
     return PKV_ERR_INVALID_ARG;
-  const PackDims pd = pack_dims(r);
+  const PackDims pd = pack_dims(r, P);
   auto get = [&](int64_t idx) -> float {
     if (dtype == PKV_BF16) {
       uint32_t w = (uint32_t)((const uint16_t*)packed)[idx] << 16;
@@ -415,7 +418,7 @@ int32_t pkv_unpack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_
   for (int i = 0; i < r; ++i) {
     for (int c = 0; c < kD; ++c)
       Rf[(int64_t)i * kD + c] = get(off_rf(kind, pd, i, c));
-    for (int j = 0; j < kP; ++j)
+    for (int j = 0; j < P; ++j)
       Lf[(int64_t)j * r + i] = get(off_lf(kind, pd, j, i));
   }
   return PKV_OK;
@@ -425,14 +428,14 @@ int32_t pkv_factor_part_bytes(int32_t kind, int32_t P, int32_t d, int32_t r, int
                               int64_t* bytes) {
   if (!bytes || (kind != PKV_KEYS && kind != PKV_VALUES && kind != PKV_KEYS_PRE_ROPE))
     return PKV_ERR_INVALID_ARG;
-  if (P != kP || d != kD) return PKV_ERR_UNSUPPORTED;
-  if (r < 1 || r > kP) return PKV_ERR_INVALID_ARG;
+  if ((P != kP && P != kMinP) || d != kD) return PKV_ERR_UNSUPPORTED;
+  if (r < 1 || r > P) return PKV_ERR_INVALID_ARG;
   if (dtype == PKV_BF16 || dtype == PKV_F32) {
-    *bytes = part_elems(r) * (dtype == PKV_BF16 ? 2 : 4);
+    *bytes = part_elems(r, P) * (dtype == PKV_BF16 ? 2 : 4);
     return PKV_OK;
   }
   if (dtype != PKV_BF16_INT4) return PKV_ERR_INVALID_ARG;
-  if (r > kQ4MaxRank || kind == PKV_KEYS_PRE_ROPE) return PKV_ERR_UNSUPPORTED;
+  if (P != kP || r > kQ4MaxRank || kind == PKV_KEYS_PRE_ROPE) return PKV_ERR_UNSUPPORTED;
   const Q4Dims q = q4_dims(r);
   *bytes = kind == PKV_KEYS ? q.k_bytes : q.v_bytes;
   return PKV_OK;
@@ -621,8 +624,8 @@ int32_t pkv_cache_state(const pkv_cache* c, int64_t* T, int64_t* n_fact, int32_t
 int32_t pkv_compress_pages(const void* X, int64_t n_pages, int32_t P, int32_t d, int32_t r,
                            int32_t in_dtype, int32_t out_dtype, void* Lf, void* Rf, float* sigma,
                            void* stream) {
-  if (P != kP || d != kD) return PKV_ERR_UNSUPPORTED;
-  if (n_pages < 0 || r < 1 || r > kP) return PKV_ERR_INVALID_ARG;
+  if ((P != kP && P != kMinP) || d != kD) return PKV_ERR_UNSUPPORTED;
+  if (n_pages < 0 || r < 1 || r > P) return PKV_ERR_INVALID_ARG;
   if ((in_dtype != PKV_BF16 && in_dtype != PKV_F32) || (out_dtype != PKV_BF16 && out_dtype != PKV_F32))
     return PKV_ERR_INVALID_ARG;
   if (n_pages == 0) return PKV_OK;
@@ -633,10 +636,11 @@ int32_t pkv_compress_pages(const void* X, int64_t n_pages, int32_t P, int32_t d,
   std::memset(&job, 0, sizeof(job));
   job.n_pages = n_pages;
   job.n_kind = 1;
+  job.page_rows = P;
   job.n_f = n_pages;
   job.n_f_src0 = n_pages;
   job.src[0].base[0] = job.src[0].base[1] = X;
-  job.src[0].f_stride = (int64_t)kP * kD;
+  job.src[0].f_stride = (int64_t)P * kD;
   job.in_dtype = in_dtype;
   job.rank[0] = job.rank[1] = r;
   job.out_dtype = out_dtype;
@@ -652,14 +656,14 @@ int32_t pkv_prefill(pkv_cache* c, const void* K, const void* V, int64_t T, void*
   if (T > 0 && (!K || !V || !aligned(K, 16) || !aligned(V, 16))) return PKV_ERR_INVALID_ARG;
   if (T > c->shape.max_tokens) return PKV_ERR_CAPACITY;
   const CacheGeom g = geom_of(c);
-  const int64_t n_fact = steady_fact(T, kP, g.n_s, g.n_w);
+  const int64_t n_fact = steady_fact(T, g.P, g.n_s, g.n_w);
   hipStream_t s = (hipStream_t)stream;
   // early factorizations and chunk decompositions still in flight read the
   // ring slots and write the factor slots this prefill overwrites
   if (wait_early(c, s) != hipSuccess || wait_chunk(c, s) != hipSuccess) return PKV_ERR_DEVICE;
   hipError_t e = launch_prefill_dense(g, K, V, T, n_fact, s);
   if (e == hipSuccess) {
-    const CompressSrc src = dense_src(c, K, V, T, (int64_t)g.n_s * kP, 0);
+    const CompressSrc src = dense_src(c, K, V, T, (int64_t)g.n_s * g.P, 0);
     e = factorize(c, src, n_fact, src, 0, s);
   }
   if (e == hipSuccess) e = launch_table_fill(g, T, n_fact, s);
@@ -679,20 +683,20 @@ int32_t pkv_prefill_chunk(pkv_cache* c, const void* K, const void* V, int64_t C,
   const int64_t T0 = c->T, T1 = T0 + C;
   if (T1 > c->shape.max_tokens) return PKV_ERR_CAPACITY;
   const CacheGeom g = geom_of(c);
-  const int64_t nf0 = c->n_fact, nf1 = steady_fact(T1, kP, g.n_s, g.n_w);
+  const int64_t nf0 = c->n_fact, nf1 = steady_fact(T1, g.P, g.n_s, g.n_w);
   if (nf1 > g.F_max) return PKV_ERR_CAPACITY;
   hipStream_t s = (hipStream_t)stream;
   // early factorizations read ring slots that this chunk may overwrite
   hipError_t e = wait_early(c, s);
-  const int64_t p0 = T0 / kP;              // page of token T0
-  const int64_t pc = (T0 + kP - 1) / kP;   // first page that starts inside the chunk
-  const int64_t np1 = (T1 + kP - 1) / kP;  // pages at T1
+  const int64_t p0 = T0 / g.P;               // page of token T0
+  const int64_t pc = (T0 + g.P - 1) / g.P;   // first page that starts inside the chunk
+  const int64_t np1 = (T1 + g.P - 1) / g.P;  // pages at T1
   const int64_t leave_lo = g.n_s + nf0, fact_hi = g.n_s + nf1;  // pages that leave the window
   // ... of them, those in the ring at T0 (none when T0 is inside the sink)
   const int64_t ring_hi = std::max(leave_lo, std::min(fact_hi, pc));
   const int64_t chunk_lo = std::max(leave_lo, pc);               // ... and those never in it
   const int64_t n_chunk = fact_hi > chunk_lo ? fact_hi - chunk_lo : 0;
-  const CompressSrc chunk = dense_src(c, K, V, C, chunk_lo * kP - T0, chunk_lo - g.n_s);
+  const CompressSrc chunk = dense_src(c, K, V, C, chunk_lo * g.P - T0, chunk_lo - g.n_s);
   // ring pages already factorized on the aux stream (their factor slots are
   // written; the wait above ordered this stream after that work)
   auto clamp = [](int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); };
@@ -701,7 +705,7 @@ int32_t pkv_prefill_chunk(pkv_cache* c, const void* K, const void* V, int64_t C,
   const int64_t b_lo = early ? clamp(c->early_hi, leave_lo, ring_hi) : ring_hi;
   // 1. the page filling at T0, when it leaves the window in this chunk: its
   //    rows from the chunk first, in its ring slot
-  if (e == hipSuccess && T0 % kP != 0 && p0 >= g.n_s && p0 < fact_hi)
+  if (e == hipSuccess && T0 % g.P != 0 && p0 >= g.n_s && p0 < fact_hi)
     e = launch_chunk_dense(g, K, V, T0, T1, p0, p0 + 1, s);
   // 2. decomposition of the pages leaving the window, as one launch: ring
   //    pages [leave_lo, a_hi) and [b_lo, ring_hi), and -- without an aux
@@ -723,7 +727,7 @@ int32_t pkv_prefill_chunk(pkv_cache* c, const void* K, const void* V, int64_t C,
   int64_t x_lo = fact_hi, x_hi = fact_hi;
   if (e == hipSuccess && c->aux) {
     x_lo = early && c->early_hi > fact_hi ? c->early_hi : fact_hi;
-    x_hi = T1 / kP < g.n_s + g.F_max ? T1 / kP : g.n_s + g.F_max;
+    x_hi = T1 / g.P < g.n_s + g.F_max ? T1 / g.P : g.n_s + g.F_max;
     if (g.n_w == 0 || x_hi < x_lo) x_hi = x_lo;
     if (x_hi > x_lo || n_chunk > 0) {
       e = hipEventRecord(c->written, s);
@@ -759,7 +763,7 @@ int32_t pkv_append(pkv_cache* c, const void* k_new, const void* v_new, int32_t* 
   if (e != hipSuccess) return PKV_ERR_DEVICE;
   c->T += 1;
   // a completed page enters the window; the oldest window page leaves it
-  const int64_t n_old_ok = steady_fact(c->T, kP, g.n_s, g.n_w);
+  const int64_t n_old_ok = steady_fact(c->T, g.P, g.n_s, g.n_w);
   c->pending = n_old_ok > c->n_fact ? 1 : 0;
   if (promotion_pending) *promotion_pending = c->pending;
   return PKV_OK;
@@ -960,9 +964,9 @@ int32_t pkv_decode_step(pkv_cache* c, const void* k_new, const void* v_new, cons
   if (c->T >= c->shape.max_tokens) return PKV_ERR_CAPACITY;
   const CacheGeom g = geom_of(c);
   const int64_t T0 = c->T, T1 = T0 + 1;
-  const int64_t p = T0 / kP;                // page of the new token
-  const int row = (int)(T0 % kP);
-  const bool promote = steady_fact(T1, kP, g.n_s, g.n_w) > c->n_fact;
+  const int64_t p = T0 / g.P;               // page of the new token
+  const int row = (int)(T0 % g.P);
+  const bool promote = steady_fact(T1, g.P, g.n_s, g.n_w) > c->n_fact;
   const int64_t p_old = g.n_s + c->n_fact;  // page leaving the window when promote
   if (promote && c->n_fact >= g.F_max) return PKV_ERR_CAPACITY;
   hipStream_t s = (hipStream_t)stream;
@@ -998,7 +1002,7 @@ int32_t pkv_decode_step(pkv_cache* c, const void* k_new, const void* v_new, cons
   job.app_page = p;
   job.app_row = row;
   job.app_entry = p < g.n_s ? table_entry(PKV_PAGE_SINK, (int)p)
-                            : table_entry(row == kP - 1 ? PKV_PAGE_WIN : PKV_PAGE_PART,
+                            : table_entry(row == g.P - 1 ? PKV_PAGE_WIN : PKV_PAGE_PART,
                                           (int)((p - g.n_s) % (g.n_w + 1)));
   hipError_t e = hipSuccess;
   if (T0 > 0) e = launch_partial(g, job, s);
@@ -1008,7 +1012,7 @@ int32_t pkv_decode_step(pkv_cache* c, const void* k_new, const void* v_new, cons
   c->T = T1;
   // the token completed window page p: factorize it ahead of the step at
   // which it leaves the window
-  if (c->aux && row == kP - 1 && p >= g.n_s && g.n_w > 0) return factorize_early(c, p, s);
+  if (c->aux && row == g.P - 1 && p >= g.n_s && g.n_w > 0) return factorize_early(c, p, s);
   return PKV_OK;
 }
 
@@ -1030,11 +1034,11 @@ int32_t pkv_decode_step_batch(pkv_cache* const* caches, int32_t n, const void* k
     if (c->pending) return PKV_ERR_PROMOTION_PENDING;
     if (c->T >= c->shape.max_tokens) return PKV_ERR_CAPACITY;
     const CacheGeom g = geom_of(c);
-    const bool promote = steady_fact(c->T + 1, kP, g.n_s, g.n_w) > c->n_fact;
+    const bool promote = steady_fact(c->T + 1, g.P, g.n_s, g.n_w) > c->n_fact;
     if (promote && c->n_fact >= g.F_max) return PKV_ERR_CAPACITY;
     // no window: the page a token completes is factorized at once, after the
     // token is in place (pkv_decode_step's separate launches)
-    if (promote && g.n_s + c->n_fact == c->T / kP) one_by_one = true;
+    if (promote && g.n_s + c->n_fact == c->T / g.P) one_by_one = true;
   }
   hipStream_t s = (hipStream_t)stream;
   const CacheGeom g0 = geom_of(caches[0]);
@@ -1055,7 +1059,7 @@ int32_t pkv_decode_step_batch(pkv_cache* const* caches, int32_t n, const void* k
   for (int i = 0; i < n; ++i) {
     pkv_cache* c = caches[i];
     const CacheGeom g = geom_of(c);
-    if (steady_fact(c->T + 1, kP, g.n_s, g.n_w) > c->n_fact) {
+    if (steady_fact(c->T + 1, g.P, g.n_s, g.n_w) > c->n_fact) {
       st = promote_now(c, stream);
       if (st != PKV_OK) return st;
     }
@@ -1069,12 +1073,12 @@ int32_t pkv_decode_step_batch(pkv_cache* const* caches, int32_t n, const void* k
     gs[i] = geom_of(c);
     T[i] = c->T;
     nf[i] = c->n_fact;
-    const int64_t p = c->T / kP;
-    const int row = (int)(c->T % kP);
+    const int64_t p = c->T / gs[i].P;
+    const int row = (int)(c->T % gs[i].P);
     apps[i].app_page = p;
     apps[i].app_row = row;
     apps[i].app_entry = p < gs[i].n_s ? table_entry(PKV_PAGE_SINK, (int)p)
-                                      : table_entry(row == kP - 1 ? PKV_PAGE_WIN : PKV_PAGE_PART,
+                                      : table_entry(row == gs[i].P - 1 ? PKV_PAGE_WIN : PKV_PAGE_PART,
                                                     (int)((p - gs[i].n_s) % (gs[i].n_w + 1)));
   }
   const uint64_t rows = (uint64_t)n * g0.Hq * ns;
@@ -1106,11 +1110,11 @@ int32_t pkv_decode_step_batch(pkv_cache* const* caches, int32_t n, const void* k
   if (e != hipSuccess) return PKV_ERR_DEVICE;
   for (int i = 0; i < n; ++i) {
     pkv_cache* c = caches[i];
-    const int64_t p = c->T / kP;
-    const int row = (int)(c->T % kP);
+    const int64_t p = c->T / gs[i].P;
+    const int row = (int)(c->T % gs[i].P);
     c->T += 1;
     // a token that completed a window page: factorize it early (aux stream)
-    if (c->aux && row == kP - 1 && p >= gs[i].n_s && gs[i].n_w > 0) {
+    if (c->aux && row == gs[i].P - 1 && p >= gs[i].n_s && gs[i].n_w > 0) {
       st = factorize_early(c, p, s);
       if (st != PKV_OK) return st;
     }

@@ -15,10 +15,10 @@
 namespace pkv {
 namespace {
 
-// Logical page held by a dense slot of a cache of length T with n_fact
-// factorized pages, or -1 when the slot is unused.
-__device__ inline int64_t slot_page(int slot_id, int n_s, int n_w, int64_t T, int64_t n_fact) {
-  const int64_t n_pages = (T + kP - 1) / kP;
+// Logical page held by a dense slot of a cache of length T (pages of P
+// tokens) with n_fact factorized pages, or -1 when the slot is unused.
+__device__ inline int64_t slot_page(int slot_id, int n_s, int n_w, int64_t T, int64_t n_fact, int P) {
+  const int64_t n_pages = (T + P - 1) / P;
   if (slot_id < n_s) return slot_id < n_pages ? slot_id : -1;
   const int k = slot_id - n_s;
   const int64_t first = (int64_t)n_s + n_fact;  // first dense page after the factors
@@ -32,13 +32,14 @@ __device__ inline int64_t slot_page(int slot_id, int n_s, int n_w, int64_t T, in
 template <typename Elem>
 __global__ __launch_bounds__(256) void prefill_dense_kernel(CacheGeom g, const Elem* K, const Elem* V,
                                                             int64_t T, int64_t n_fact) {
-  __shared__ Elem tile[kP][kD + 2];
+  __shared__ Elem tile[kP][kD + 2];  // P <= kP rows
+  const int P = g.P;
   const int slot_id = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * g.Hkv + h;
-  const int64_t p = slot_page(slot_id, g.n_s, g.n_w, T, n_fact);
-  const int64_t nv = p < 0 ? 0 : ((T - p * kP) < kP ? (T - p * kP) : kP);
+  const int64_t p = slot_page(slot_id, g.n_s, g.n_w, T, n_fact, P);
+  const int64_t nv = p < 0 ? 0 : ((T - p * P) < P ? (T - p * P) : P);
   Elem *dk, *dv;
-  const int64_t ppg = (int64_t)kP * kD;
+  const int64_t ppg = (int64_t)P * kD;
   if (slot_id < g.n_s) {
     dk = (Elem*)(g.base + g.lay.sink_k) + (bh * g.n_s + slot_id) * ppg;
     dv = (Elem*)(g.base + g.lay.sink_v) + (bh * g.n_s + slot_id) * ppg;
@@ -47,16 +48,16 @@ __global__ __launch_bounds__(256) void prefill_dense_kernel(CacheGeom g, const E
     dk = (Elem*)(g.base + g.lay.win_k) + (bh * (g.n_w + 1) + k) * ppg;
     dv = (Elem*)(g.base + g.lay.win_v) + (bh * (g.n_w + 1) + k) * ppg;
   }
-  const Elem* sk = K + (bh * T + (p < 0 ? 0 : p * kP)) * kD;
-  const Elem* sv = V + (bh * T + (p < 0 ? 0 : p * kP)) * kD;
-  for (int idx = threadIdx.x; idx < kP * kD; idx += 256) {
+  const Elem* sk = K + (bh * T + (p < 0 ? 0 : p * P)) * kD;
+  const Elem* sv = V + (bh * T + (p < 0 ? 0 : p * P)) * kD;
+  for (int idx = threadIdx.x; idx < P * kD; idx += 256) {
     const int j = idx / kD, c = idx % kD;
     dk[idx] = j < nv ? sk[idx] : Elem(0);
     tile[j][c] = j < nv ? sv[idx] : Elem(0);
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < kP * kD; idx += 256) {
-    const int c = idx / kP, j = idx % kP;
+  for (int idx = threadIdx.x; idx < P * kD; idx += 256) {
+    const int c = idx / P, j = idx % P;
     dv[idx] = tile[j][c];
   }
 }
@@ -69,16 +70,17 @@ __global__ __launch_bounds__(256) void prefill_dense_kernel(CacheGeom g, const E
 template <typename Elem>
 __global__ __launch_bounds__(256) void chunk_dense_kernel(CacheGeom g, const Elem* K, const Elem* V,
                                                           int64_t T0, int64_t T1, int64_t p_lo) {
-  __shared__ Elem tile[kP][kD + 2];
+  __shared__ Elem tile[kP][kD + 2];  // P <= kP rows
+  const int P = g.P;
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t p = p_lo + blockIdx.x;
   const int64_t bh = (int64_t)b * g.Hkv + h;
   const int64_t C = T1 - T0;
-  const int64_t t0 = p * kP > T0 ? p * kP : T0;
-  const int64_t t1 = p * kP + kP < T1 ? p * kP + kP : T1;
+  const int64_t t0 = p * P > T0 ? p * P : T0;
+  const int64_t t1 = p * P + P < T1 ? p * P + P : T1;
   if (t1 <= t0) return;
-  const int r0 = (int)(t0 - p * kP), nr = (int)(t1 - t0);
-  const int64_t ppg = (int64_t)kP * kD;
+  const int r0 = (int)(t0 - p * P), nr = (int)(t1 - t0);
+  const int64_t ppg = (int64_t)P * kD;
   Elem *dk, *dv;
   if (p < g.n_s) {
     dk = (Elem*)(g.base + g.lay.sink_k) + (bh * g.n_s + p) * ppg;
@@ -98,12 +100,12 @@ __global__ __launch_bounds__(256) void chunk_dense_kernel(CacheGeom g, const Ele
   __syncthreads();
   for (int idx = threadIdx.x; idx < nr * kD; idx += 256) {
     const int c = idx / nr, j = idx % nr;
-    dv[c * kP + r0 + j] = tile[j][c];
+    dv[c * P + r0 + j] = tile[j][c];
   }
 }
 
-__device__ inline int32_t classify_entry(int64_t p, int64_t T, int n_s, int n_w, int64_t n_fact) {
-  const int64_t n_full = T / kP, n_pages = (T + kP - 1) / kP;
+__device__ inline int32_t classify_entry(int64_t p, int64_t T, int n_s, int n_w, int64_t n_fact, int P) {
+  const int64_t n_full = T / P, n_pages = (T + P - 1) / P;
   if (p >= n_pages) return table_entry(PKV_PAGE_UNUSED, 0);
   if (p < n_s) return table_entry(PKV_PAGE_SINK, (int)p);
   if (p < n_s + n_fact) return table_entry(PKV_PAGE_FACT, (int)(p - n_s));
@@ -112,9 +114,9 @@ __device__ inline int32_t classify_entry(int64_t p, int64_t T, int n_s, int n_w,
 }
 
 __global__ void table_fill_kernel(int32_t* table, int64_t max_pages, int64_t T, int n_s, int n_w,
-                                  int64_t n_fact) {
+                                  int64_t n_fact, int P) {
   const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (p < max_pages) table[p] = classify_entry(p, T, n_s, n_w, n_fact);
+  if (p < max_pages) table[p] = classify_entry(p, T, n_s, n_w, n_fact, P);
 }
 
 __global__ void table_set_kernel(int32_t* table, int64_t page, int32_t entry) {
@@ -124,11 +126,12 @@ __global__ void table_set_kernel(int32_t* table, int64_t page, int32_t entry) {
 template <typename Elem>
 __global__ __launch_bounds__(128) void append_kernel(CacheGeom g, const Elem* k, const Elem* v,
                                                      int64_t T) {
+  const int P = g.P;
   const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
   const int64_t bh = (int64_t)b * g.Hkv + h;
-  const int64_t p = T / kP;
-  const int row = (int)(T % kP);
-  const int64_t ppg = (int64_t)kP * kD;
+  const int64_t p = T / P;
+  const int row = (int)(T % P);
+  const int64_t ppg = (int64_t)P * kD;
   Elem *dk, *dv;
   if (p < g.n_s) {
     dk = (Elem*)(g.base + g.lay.sink_k) + (bh * g.n_s + p) * ppg;
@@ -139,12 +142,12 @@ __global__ __launch_bounds__(128) void append_kernel(CacheGeom g, const Elem* k,
     dv = (Elem*)(g.base + g.lay.win_v) + (bh * (g.n_w + 1) + slot) * ppg;
   }
   dk[row * kD + c] = k[bh * kD + c];
-  dv[(int64_t)c * kP + row] = v[bh * kD + c];
+  dv[(int64_t)c * P + row] = v[bh * kD + c];
   if (b == 0 && h == 0 && c == 0) {
     int32_t* table = (int32_t*)(g.base + g.lay.page_table);
     int32_t e;
     if (p < g.n_s) e = table_entry(PKV_PAGE_SINK, (int)p);
-    else e = table_entry(row == kP - 1 ? PKV_PAGE_WIN : PKV_PAGE_PART, (int)((p - g.n_s) % (g.n_w + 1)));
+    else e = table_entry(row == P - 1 ? PKV_PAGE_WIN : PKV_PAGE_PART, (int)((p - g.n_s) % (g.n_w + 1)));
     table[p] = e;
   }
 }
@@ -179,7 +182,7 @@ hipError_t launch_chunk_dense(const CacheGeom& g, const void* K, const void* V, 
 hipError_t launch_table_fill(const CacheGeom& g, int64_t T, int64_t n_fact, hipStream_t stream) {
   const unsigned blocks = (unsigned)((g.max_pages + 255) / 256);
   hipLaunchKernelGGL(table_fill_kernel, dim3(blocks), dim3(256), 0, stream,
-                     (int32_t*)(g.base + g.lay.page_table), g.max_pages, T, g.n_s, g.n_w, n_fact);
+                     (int32_t*)(g.base + g.lay.page_table), g.max_pages, T, g.n_s, g.n_w, n_fact, g.P);
   return hipGetLastError();
 }
 

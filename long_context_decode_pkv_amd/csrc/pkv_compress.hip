@@ -46,7 +46,7 @@ __device__ inline void store_gram_tile(float* Gs, int ta, int tb, floatx4 acc, i
 
 // The 10 upper 16x16 tiles of G = X X^T, spread over the page's waves.
 template <typename Elem, int WPP>
-__device__ void gram(const Elem* X, int trans, float* Gs, int lane, int wv) {
+__device__ void gram(const Elem* X, int trans, int P, float* Gs, int lane, int wv) {
   for (int tile = wv; tile < 10; tile += WPP) {
     // tile -> (ta, tb), ta <= tb
     int ta = 0, rem = tile;
@@ -55,7 +55,7 @@ __device__ void gram(const Elem* X, int trans, float* Gs, int lane, int wv) {
       ++ta;
     }
     const int tb = ta + rem;
-    const floatx4 acc = gram_tile(X, trans, ta, tb, lane);
+    const floatx4 acc = gram_tile(X, trans, P, ta, tb, lane);
     store_gram_tile(Gs, ta, tb, acc, lane);
   }
 }
@@ -229,10 +229,10 @@ __device__ void compress_one(const CompressJob& job, int64_t n, CompressShared& 
   const int kind = pr.kind;
   const Elem* X = (const Elem*)pr.X;
   const int trans = pr.trans;
-  const int r = pr.r;
+  const int r = pr.r;  // > 32, so the page has 64 rows (launch_compress)
 
   // 1. Gram matrix, eigenvector accumulator = I
-  gram<Elem, WPP>(X, trans, sh.G, lane, wv);
+  gram<Elem, WPP>(X, trans, kP, sh.G, lane, wv);
   for (int idx = tid; idx < kP * kP; idx += 64 * WPP) {
     const int j = idx / kP, c = idx % kP;
     sh.V[j * kLd + c] = (j == c) ? 1.f : 0.f;
@@ -277,7 +277,7 @@ __device__ void compress_one(const CompressJob& job, int64_t n, CompressShared& 
     const int j = 4 * kc + q;
     float bv[MC];
 #pragma unroll
-    for (int m = 0; m < MC; ++m) bv[m] = page_elem(X, trans, j, 16 * (wv * MC + m) + ci);
+    for (int m = 0; m < MC; ++m) bv[m] = page_elem(X, trans, kP, j, 16 * (wv * MC + m) + ci);
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       if (mi < RT16) {
@@ -380,6 +380,7 @@ hipError_t launch_compress(const CompressJob& job, hipStream_t stream) {
   const KernelEvents ev = take_kernel_events();
   const int r_max = job.n_kind == 2 && job.rank[1] > job.rank[0] ? job.rank[1] : job.rank[0];
   if (r_max <= kTriMaxRank) return launch_compress_tri(job, stream, ev.start, ev.stop);
+  if (job.page_rows != kP) return hipErrorInvalidValue;  // ranks above 32 need 64-row pages
   const int64_t cap = 1 << 30;
   const unsigned grid = (unsigned)(job.n_pages < cap ? job.n_pages : cap);
   const bool few = job.n_pages <= kLatencyModePages;

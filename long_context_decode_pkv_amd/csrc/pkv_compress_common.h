@@ -22,10 +22,15 @@ __device__ inline uint16_t f32_to_bf16_bits(float x) {
   return (uint16_t)(u >> 16);
 }
 
-// Element (j, c) of a page, j < P (token), c < d (channel).
+// Element (j, c) of a page of P rows, j < P (token), c < d (channel).
+// The kernels decompose every page as 64 rows: a page of P = 32 rows is
+// padded with zero rows, which leaves its nonzero singular triplets
+// unchanged.  P is a multiple of 16, so a 16-row tile or a 4-row
+// reduction step lies wholly inside the page or wholly in the padding, and
+// the callers skip the padding as a whole.
 template <typename Elem>
-__device__ inline float page_elem(const Elem* X, int trans, int j, int c) {
-  Elem v = trans ? X[c * kP + j] : X[j * kD + c];
+__device__ inline float page_elem(const Elem* X, int trans, int P, int j, int c) {
+  Elem v = trans ? X[c * P + j] : X[j * kD + c];
   if constexpr (sizeof(Elem) == 2) return bf16_bits_to_f32(v);
   else return v;
 }
@@ -35,34 +40,42 @@ __device__ inline void store_elem(void* base, int64_t idx, int dtype, float v) {
   else ((float*)base)[idx] = v;
 }
 
-// 8 consecutive channels c0.. of page row `row` as a bf16 MFMA operand.
-__device__ inline bf16x8 row8(const uint16_t* X, int trans, int row, int c0) {
+// 8 consecutive channels c0.. of page row `row` < P as a bf16 MFMA operand.
+__device__ inline bf16x8 row8(const uint16_t* X, int trans, int P, int row, int c0) {
   if (!trans) return __builtin_bit_cast(bf16x8, *(const uint4*)(X + row * kD + c0));
+  // the column stride as a constant keeps the 8 loads on one address
   bf16x8 v;
+  if (P == kP) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(__bf16, X[(c0 + e) * kP + row]);
+    for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(__bf16, X[(c0 + e) * kP + row]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(__bf16, X[(c0 + e) * kMinP + row]);
+  }
   return v;
 }
 
 // One 16x16 tile (rows 16 ta.., columns 16 tb..) of G = X X^T on the matrix
 // cores: lane l holds G[16 ta + 4 (l / 16) + v][16 tb + l % 16], v < 4.
+// Tiles in the padding rows of a short page are zero.
 template <typename Elem>
-__device__ inline floatx4 gram_tile(const Elem* X, int trans, int ta, int tb, int lane) {
+__device__ inline floatx4 gram_tile(const Elem* X, int trans, int P, int ta, int tb, int lane) {
   const int i = lane & 15, q = lane >> 4;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (16 * ta >= P || 16 * tb >= P) return acc;  // uniform
   if constexpr (sizeof(Elem) == 2) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 av = row8(X, trans, 16 * ta + i, 32 * ks + 8 * q);
-      const bf16x8 bv = row8(X, trans, 16 * tb + i, 32 * ks + 8 * q);
+      const bf16x8 av = row8(X, trans, P, 16 * ta + i, 32 * ks + 8 * q);
+      const bf16x8 bv = row8(X, trans, P, 16 * tb + i, 32 * ks + 8 * q);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
     }
   } else {
 #pragma unroll 4
     for (int kc = 0; kc < kD / 4; ++kc) {
       if ((kc & 3) == 0) __builtin_amdgcn_sched_barrier(0);
-      const float av = page_elem(X, trans, 16 * ta + i, 4 * kc + q);
-      const float bv = page_elem(X, trans, 16 * tb + i, 4 * kc + q);
+      const float av = page_elem(X, trans, P, 16 * ta + i, 4 * kc + q);
+      const float bv = page_elem(X, trans, P, 16 * tb + i, 4 * kc + q);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
     }
   }
@@ -75,6 +88,7 @@ struct PageRef {
   int64_t bh;
   int64_t slot;  // factor slot (cache jobs)
   int trans, r;
+  int P;         // page rows
   const void* X;
 };
 
@@ -91,6 +105,7 @@ __device__ inline PageRef page_ref(const CompressJob& job, int64_t n, int elem_b
   p.slot = src.out_f0 + f;
   p.trans = src.trans[p.kind];
   p.r = job.rank[p.kind];
+  p.P = job.page_rows;
   p.X = (const uint8_t*)src.base[p.kind] + (p.bh * src.bh_stride + in * src.f_stride) * elem_bytes;
   return p;
 }
@@ -105,14 +120,16 @@ struct FactorDst {
   bool packed;
   PackDims pd;
   int r, r_store, kind;
+  int P;
   int64_t n;
   void* rf;
   void* lf;
   __device__ FactorDst(const CompressJob& job, const PageRef& p, int64_t n_) {
     packed = job.fac != nullptr;
-    pd = pack_dims(p.r);
+    pd = pack_dims(p.r, p.P);
     r = p.r;
-    r_store = packed ? 8 * pd.n8 : p.r;
+    P = p.P;
+    r_store = packed ? pd.rs : p.r;
     kind = p.kind == 0 ? job.key_part_kind : PKV_VALUES;  // part layout
     n = n_;
     if (packed) {
@@ -127,7 +144,7 @@ struct FactorDst {
     return off_rf(kind, pd, i, c);
   }
   __device__ int64_t lf_idx(int j, int i) const {
-    if (!packed) return n * (int64_t)kP * r + (int64_t)j * r + i;
+    if (!packed) return n * (int64_t)P * r + (int64_t)j * r + i;
     return off_lf(kind, pd, j, i);
   }
 };

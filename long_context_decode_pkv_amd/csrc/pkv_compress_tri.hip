@@ -35,6 +35,12 @@
 //      nearest-even to the output dtype.  INT4 caches (Sec. 4.3) instead
 //      store Lt = Q_r diag(sigma^(1/2)) and Rt = diag(sigma^(-1/2)) R as
 //      symmetric 4-bit codes with bf16 group scales (store_q4).
+//
+// A page of N = 32 rows sits in the 64-row frame with zero rows below it: G,
+// the reflectors and Q_H are block-diagonal with an identity / zero block, T
+// splits after row N - 1, and steps 2-5 run on the leading N x N block only
+// (the zero block's eigenvalues are exact zeros that the search must not
+// mistake for the page's smallest ones).
 #include "pkv_compress_common.h"
 
 namespace pkv {
@@ -102,12 +108,12 @@ __device__ __forceinline__ float wave_reduce(float x) {
 
 // 1. G into the row registers: lane i gets G[i][0..63].
 template <typename Elem>
-__device__ __forceinline__ void gram_rows(const Elem* X, int trans, TriShared& sh, float (&g)[kP], int lane) {
+__device__ __forceinline__ void gram_rows(const Elem* X, int trans, int P, TriShared& sh, float (&g)[kP], int lane) {
   const int c = lane & 15, q = lane >> 4;
   for (int ta = 0; ta < 4; ++ta) {
     for (int tb = 0; tb < 4; ++tb) {
       __builtin_amdgcn_sched_barrier(0);
-      const floatx4 acc = gram_tile(X, trans, ta, tb, lane);
+      const floatx4 acc = gram_tile(X, trans, P, ta, tb, lane);
 #pragma unroll
       for (int v = 0; v < 4; ++v) sh.u.band[(4 * q + v) * kLd + 16 * tb + c] = acc[v];
     }
@@ -120,15 +126,16 @@ __device__ __forceinline__ void gram_rows(const Elem* X, int trans, TriShared& s
   }
 }
 
-// 2. Householder tridiagonalization.  On return lane i holds a_i (my_a), b_i
-// (my_b) and row i of Q_H.
+// 2. Householder tridiagonalization of the leading N x N block (the rest of
+// G is zero).  On return lane i holds a_i (my_a), b_i (my_b) and row i of Q_H.
+template <int N>
 __device__ __forceinline__ void tridiagonalize(TriShared& sh, float (&g)[kP], float (&qh)[kP], int lane,
                                       float& my_a, float& my_b) {
 #pragma unroll
   for (int j = 0; j < kP; ++j) qh[j] = (j == lane) ? 1.f : 0.f;
   my_a = 0.f;
   my_b = 0.f;
-  for (int k = 0; k < kP - 1; ++k) {
+  for (int k = 0; k < N - 1; ++k) {
     if (lane == k) {
 #pragma unroll
       for (int jc = 0; jc < kP / 4; ++jc)
@@ -153,7 +160,7 @@ __device__ __forceinline__ void tridiagonalize(TriShared& sh, float (&g)[kP], fl
     // chunks left of k + 1 are skipped (uniform branch)
     float pacc = 0.f, tacc = 0.f;
 #pragma unroll
-    for (int jc = 0; jc < kP / 4; ++jc) {
+    for (int jc = 0; jc < N / 4; ++jc) {
       __builtin_amdgcn_sched_barrier(0);
       if (4 * jc + 3 <= k) continue;
       const float4 vv = *(const float4*)&sh.v[4 * jc];
@@ -174,7 +181,7 @@ __device__ __forceinline__ void tridiagonalize(TriShared& sh, float (&g)[kP], fl
     // G <- G - v w^T - w v^T ; Q_H <- Q_H - tau (Q_H v) v^T
     const float tq = tau * tacc;
 #pragma unroll
-    for (int jc = 0; jc < kP / 4; ++jc) {
+    for (int jc = 0; jc < N / 4; ++jc) {
       __builtin_amdgcn_sched_barrier(0);
       if (4 * jc + 3 <= k) continue;
       const float4 vv = *(const float4*)&sh.v[4 * jc];
@@ -192,7 +199,7 @@ __device__ __forceinline__ void tridiagonalize(TriShared& sh, float (&g)[kP], fl
     __syncthreads();
   }
   // the last diagonal entry is already in place: no reflection touches it
-  if (lane == kP - 1) my_a = g[kP - 1];
+  if (lane == N - 1) my_a = g[N - 1];
 }
 
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
@@ -200,11 +207,12 @@ __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x);
 // Number of eigenvalues of T below x: non-positive pivots of T - x I = L D L^T.
 // The couplings b2s are floored at a tiny positive value (setup), so a zero
 // pivot gives rcp = inf and the next pivot -inf, never 0 * inf.
+template <int N>
 __device__ __forceinline__ int sturm_count(const TriShared& sh, float x) {
   int cnt = 0;
   float d = 1.f;
 #pragma unroll 4
-  for (int ic = 0; ic < kP / 4; ++ic) {
+  for (int ic = 0; ic < N / 4; ++ic) {
     const float4 a4 = *(const float4*)&sh.a[4 * ic];
     const float4 b4 = *(const float4*)&sh.b2s[4 * ic];
     const float av[4] = {a4.x, a4.y, a4.z, a4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
@@ -234,23 +242,24 @@ __device__ __forceinline__ int multisection_rounds(int L) {
 // formed.  The column doubles as the scratch for the pivots, so a lane holds
 // no per-row state in registers.  Lanes sharing a column compute identical
 // values; only `writer` lanes store.
+template <int N>
 __device__ __forceinline__ void twisted_vector(TriShared& sh, float lam, float pivmin, int col,
                                                bool writer) {
   auto guard = [pivmin](float d) { return fabsf(d) < pivmin ? -pivmin : d; };
   float* Zc = sh.u.Z + col;
   // forward pivots d+_i -> Z[i]
   float d = 1.f;
-  for (int i = 0; i < kP; ++i) {
+  for (int i = 0; i < N; ++i) {
     d = guard(fmaf(-sh.b2s[i], rcp(d), sh.a[i] - lam));
     if (writer) Zc[i * kZs] = d;
   }
   __syncthreads();
   // backward pivots d-_i (b2s[i + 1] = b_i^2) and the twist index
   float dm = 1.f, best = __builtin_inff();
-  int kk = kP - 1;
-  for (int i = kP - 1; i >= 0; --i) {
+  int kk = N - 1;
+  for (int i = N - 1; i >= 0; --i) {
     const float ai = sh.a[i] - lam;
-    dm = guard(fmaf(-(i < kP - 1 ? sh.b2s[i + 1] : 0.f), rcp(dm), ai));
+    dm = guard(fmaf(-(i < N - 1 ? sh.b2s[i + 1] : 0.f), rcp(dm), ai));
     const float gam = fabsf(Zc[i * kZs] + dm - ai);
     if (gam < best) {
       best = gam;
@@ -260,13 +269,13 @@ __device__ __forceinline__ void twisted_vector(TriShared& sh, float lam, float p
   // z_kk = 1; above kk: z_i = -b_{i-1} z_{i-1} / d-_i, so the d-_i are formed
   // again top-down and kept where i > kk
   dm = 1.f;
-  for (int i = kP - 1; i > kk; --i) {
-    dm = guard(fmaf(-(i < kP - 1 ? sh.b2s[i + 1] : 0.f), rcp(dm), sh.a[i] - lam));
+  for (int i = N - 1; i > kk; --i) {
+    dm = guard(fmaf(-(i < N - 1 ? sh.b2s[i + 1] : 0.f), rcp(dm), sh.a[i] - lam));
     if (writer) Zc[i * kZs] = dm;
   }
   __syncthreads();
   float ss = 1.f, zz = 1.f;
-  for (int i = kk + 1; i < kP; ++i) {
+  for (int i = kk + 1; i < N; ++i) {
     zz = -sh.b[i - 1] * zz * rcp(Zc[i * kZs]);
     ss = fmaf(zz, zz, ss);
     if (writer) Zc[i * kZs] = zz;
@@ -282,7 +291,7 @@ __device__ __forceinline__ void twisted_vector(TriShared& sh, float lam, float p
   __syncthreads();
   const bool ok = ss > 0.f && ss < __builtin_inff();
   const float inv = ok ? rsqrtf(ss) : 0.f;
-  for (int i = 0; i < kP; ++i) {
+  for (int i = 0; i < N; ++i) {
     const float zi = Zc[i * kZs];
     if (writer) Zc[i * kZs] = ok ? zi * inv : 0.f;
   }
@@ -469,7 +478,7 @@ __device__ __forceinline__ void store_q4(const CompressJob& job, const PageRef& 
   }
 }
 
-template <typename Elem, bool kQ4>
+template <typename Elem, bool kQ4, int N>
 __device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t n, TriShared& sh, int lane) {
   const PageRef pr = page_ref(job, n, (int)sizeof(Elem));
   const Elem* X = (const Elem*)pr.X;
@@ -479,8 +488,8 @@ __device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t
   float my_a, my_b;
   {
     float g[kP];
-    gram_rows<Elem>(X, pr.trans, sh, g, lane);
-    tridiagonalize(sh, g, qh, lane, my_a, my_b);
+    gram_rows<Elem>(X, pr.trans, pr.P, sh, g, lane);
+    tridiagonalize<N>(sh, g, qh, lane, my_a, my_b);
   }
 
   // T to LDS, Gershgorin interval, pivot floor
@@ -504,12 +513,12 @@ __device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t
   const int t = lane & (L - 1);
   const int jl = lane / L;
   const int j = jl < r ? jl : r - 1;  // descending index
-  const int m = kP - 1 - j;           // ascending index
+  const int m = N - 1 - j;            // ascending index (the zero block's N below)
   float lo = glo, hi = ghi;
   {
     const float x0 = fmaf(ghi - glo, (float)(lane + 1) / (float)(kP + 1), glo);
     sh.xrow[lane] = x0;
-    sh.w[lane] = __int_as_float(sturm_count(sh, x0));
+    sh.w[lane] = __int_as_float(sturm_count<N>(sh, x0));
     __syncthreads();
 #pragma unroll 8
     for (int l = 0; l < kP; ++l) {
@@ -523,7 +532,7 @@ __device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t
   const float frac = (float)(t + 1) / (float)(L + 1);
   for (int it = 0; it < rounds; ++it) {
     const float x = fmaf(hi - lo, frac, lo);
-    const int cnt = sturm_count(sh, x);
+    const int cnt = sturm_count<N>(sh, x);
     float nlo = cnt <= m ? x : lo, nhi = cnt <= m ? hi : x;
     for (int o = 1; o < L; o <<= 1) {
       nlo = fmaxf(nlo, __shfl_xor(nlo, o));
@@ -535,7 +544,7 @@ __device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t
   const float lam = 0.5f * (lo + hi);
 
   // 4. eigenvectors of T -> Z[:, j]
-  twisted_vector(sh, lam, pivmin, j, t == 0 && jl < r);
+  twisted_vector<N>(sh, lam, pivmin, j, t == 0 && jl < r);
   __syncthreads();
 
   // 5a. Q_r = Q_H Z: lane i forms row i
@@ -545,7 +554,7 @@ __device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t
     float4 acc = {0.f, 0.f, 0.f, 0.f};
     if (4 * jc < r) {
 #pragma unroll
-      for (int mm = 0; mm < kP; ++mm) {
+      for (int mm = 0; mm < N; ++mm) {  // Z has N rows; Q_H's other columns are e_i
         if ((mm & 3) == 0) __builtin_amdgcn_sched_barrier(0);
         const float4 z4 = *(const float4*)&sh.u.Z[mm * kZs + 4 * jc];
         acc.x = fmaf(qh[mm], z4.x, acc.x);
@@ -578,12 +587,12 @@ __device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t
     for (int mc = 0; mc < 8; ++mc) R[mi][mc] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll 2
-  for (int kc = 0; kc < kP / 4; ++kc) {
+  for (int kc = 0; kc < N / 4; ++kc) {  // page rows
     __builtin_amdgcn_sched_barrier(0);
     const int jr = 4 * kc + q;
     float bv[8];
 #pragma unroll
-    for (int mc = 0; mc < 8; ++mc) bv[mc] = page_elem(X, pr.trans, jr, 16 * mc + ci);
+    for (int mc = 0; mc < 8; ++mc) bv[mc] = page_elem(X, pr.trans, pr.P, jr, 16 * mc + ci);
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
       if (mi < RT16) {
@@ -638,7 +647,7 @@ __device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t
       }
     }
   }
-  for (int i = 0; i < dst.r_store; ++i) {
+  for (int i = 0; i < dst.r_store && lane < N; ++i) {  // page rows
     float val = 0.f;
     if (i < r) {
       const float sg = sh.sig[i];
@@ -652,11 +661,11 @@ __device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t
 
 // One page per workgroup (no page loop: a loop around the page body costs the
 // register allocator ~70 extra VGPRs).  Page n = blockIdx.y * gridDim.x + blockIdx.x.
-template <typename Elem, bool kQ4>
+template <typename Elem, bool kQ4, int N>
 __global__ __launch_bounds__(64, 3) void compress_tri_kernel(CompressJob job) {
   __shared__ TriShared sh;
   const int64_t n = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-  if (n < job.n_pages) compress_tri_one<Elem, kQ4>(job, n, sh, threadIdx.x);
+  if (n < job.n_pages) compress_tri_one<Elem, kQ4, N>(job, n, sh, threadIdx.x);
 }
 
 }  // namespace
@@ -669,13 +678,20 @@ hipError_t launch_compress_tri(const CompressJob& job, hipStream_t stream, hipEv
   if (gy > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)gx, (unsigned)gy);
   const bool q4 = job.out_dtype == PKV_BF16_INT4;
-  if (q4 && (job.fac == nullptr || job.in_dtype != PKV_BF16)) return hipErrorInvalidValue;
+  if (q4 && (job.fac == nullptr || job.in_dtype != PKV_BF16 || job.page_rows != kP)) return hipErrorInvalidValue;
+  if (job.page_rows != kP && job.page_rows != kMinP) return hipErrorInvalidValue;
+  const bool full = job.page_rows == kP;
   if (q4)
-    hipExtLaunchKernelGGL((compress_tri_kernel<uint16_t, true>), grid, dim3(64), 0, stream, start, stop, 0, job);
+    hipExtLaunchKernelGGL((compress_tri_kernel<uint16_t, true, kP>), grid, dim3(64), 0, stream, start, stop, 0, job);
+  else if (job.in_dtype == PKV_BF16 && full)
+    hipExtLaunchKernelGGL((compress_tri_kernel<uint16_t, false, kP>), grid, dim3(64), 0, stream, start, stop, 0, job);
   else if (job.in_dtype == PKV_BF16)
-    hipExtLaunchKernelGGL((compress_tri_kernel<uint16_t, false>), grid, dim3(64), 0, stream, start, stop, 0, job);
+    hipExtLaunchKernelGGL((compress_tri_kernel<uint16_t, false, kMinP>), grid, dim3(64), 0, stream, start, stop, 0,
+                          job);
+  else if (full)
+    hipExtLaunchKernelGGL((compress_tri_kernel<float, false, kP>), grid, dim3(64), 0, stream, start, stop, 0, job);
   else
-    hipExtLaunchKernelGGL((compress_tri_kernel<float, false>), grid, dim3(64), 0, stream, start, stop, 0, job);
+    hipExtLaunchKernelGGL((compress_tri_kernel<float, false, kMinP>), grid, dim3(64), 0, stream, start, stop, 0, job);
   return hipGetLastError();
 }
 

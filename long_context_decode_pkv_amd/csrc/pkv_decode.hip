@@ -49,6 +49,7 @@ struct DecodeArgs {
   float* ws_o;
   float* ws_ml;
   int B, Hkv, G, n_split;
+  int P;                        // page length (the matrix-core kernels: 64)
   int n_s, n_w;
   int r_k, r_v;
   int64_t T, n_fact, F_max;
@@ -66,9 +67,9 @@ struct WorkList {
   int64_t n_sinkp, first_tail, D, F;
 };
 
-__device__ inline WorkList work_list(int64_t T, int64_t n_fact, int n_s) {
+__device__ inline WorkList work_list(int64_t T, int64_t n_fact, int n_s, int P = kP) {
   WorkList w;
-  const int64_t n_pages = (T + kP - 1) / kP;
+  const int64_t n_pages = (T + P - 1) / P;
   w.n_sinkp = n_pages < n_s ? n_pages : n_s;
   w.first_tail = n_s + n_fact;
   const int64_t tail = n_pages - w.first_tail;
@@ -1434,7 +1435,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(KA kargs) {
   const DecodeArgs& a = common_args(kargs);
   const SeqView sv = seq_view(kargs);
   // pre-RoPE keys: the page's keys, stored or reconstructed, then rotated
-  __shared__ float kr[kRope ? kP : 1][kRope ? kD + 1 : 1];
+  __shared__ float kr[kRope ? kP : 1][kRope ? kD + 1 : 1];  // rows < P <= kP
   __shared__ float qs[kMaxG][kD];
   __shared__ float ts[kMaxG][kP];
   __shared__ float ss[kMaxG][kP];
@@ -1448,7 +1449,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(KA kargs) {
   const int G = a.G;
   const int Hq = a.Hkv * G;
   const int64_t bh = (int64_t)sv.b_pool * a.Hkv + h;  // (sequence, KV head) in the pools
-  const PackDims pk = pack_dims(a.r_k), pv = pack_dims(a.r_v);
+  const int P = a.P;  // <= P
+  const PackDims pk = pack_dims(a.r_k, P), pv = pack_dims(a.r_v, P);
   constexpr int kEsz = sizeof(Elem);
 
   for (int idx = tid; idx < G * kD; idx += 256) {
@@ -1462,18 +1464,18 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(KA kargs) {
   float o[4] = {0.f, 0.f, 0.f, 0.f};
   __syncthreads();
 
-  const WorkList wl = work_list(sv.T, sv.n_fact, a.n_s);
+  const WorkList wl = work_list(sv.T, sv.n_fact, a.n_s, P);
   const int64_t e0 = unit_bound(wl, a, split, sv.n_split), e1 = unit_bound(wl, a, split + 1, sv.n_split);
   for (int64_t e = e0; e < e1; ++e) {
     const int64_t p = unit_page(wl, a, e);
     const int32_t ent = sv.table[p];
     const int cls = table_class(ent), slot = table_slot(ent);
     const bool dense = e < wl.D;
-    const int64_t rem = sv.T - p * kP;
-    const int nv = dense ? (int)(rem < kP ? rem : kP) : kP;
+    const int64_t rem = sv.T - p * P;
+    const int nv = dense ? (int)(rem < P ? rem : P) : P;
     const void *Kp = nullptr, *Vt = nullptr, *kpart = nullptr, *vpart = nullptr;
     if (kRope) {
-      const int64_t ppg = (int64_t)kP * kD;
+      const int64_t ppg = (int64_t)P * kD;
       if (!dense) {
         kpart = sv.fac + (bh * sv.F_max + slot) * a.page_bytes;
         vpart = (const uint8_t*)kpart + a.k_part_bytes;
@@ -1484,7 +1486,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(KA kargs) {
         Kp = (const uint8_t*)sv.win_k + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
         Vt = (const uint8_t*)sv.win_v + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
       }
-      for (int idx = tid; idx < kP * kD; idx += 256) {
+      for (int idx = tid; idx < P * kD; idx += 256) {
         const int j = idx / kD, c = idx % kD;
         float x = 0.f;
         if (dense) {
@@ -1496,17 +1498,17 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(KA kargs) {
         kr[j][c] = x;
       }
       __syncthreads();
-      for (int idx = tid; idx < kP * (kD / 2); idx += 256) {
+      for (int idx = tid; idx < P * (kD / 2); idx += 256) {
         const int j = idx / (kD / 2), m = idx % (kD / 2);
         float cs, sn;
-        rope_sincos(p * kP + j, a.rope_freq[m], cs, sn);
+        rope_sincos(p * P + j, a.rope_freq[m], cs, sn);
         const float x = kr[j][m], y = kr[j][m + kD / 2];
         kr[j][m] = x * cs - y * sn;
         kr[j][m + kD / 2] = y * cs + x * sn;
       }
       __syncthreads();
-      for (int idx = tid; idx < G * kP; idx += 256) {
-        const int g = idx / kP, j = idx % kP;
+      for (int idx = tid; idx < G * P; idx += 256) {
+        const int g = idx / P, j = idx % P;
         float acc = -INFINITY;
         if (j < nv) {
           acc = 0.f;
@@ -1515,7 +1517,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(KA kargs) {
         ss[g][j] = acc;
       }
     } else if (dense) {
-      const int64_t ppg = (int64_t)kP * kD;
+      const int64_t ppg = (int64_t)P * kD;
       if (cls == PKV_PAGE_SINK) {
         Kp = (const uint8_t*)sv.sink_k + (bh * a.n_s + slot) * ppg * kEsz;
         Vt = (const uint8_t*)sv.sink_v + (bh * a.n_s + slot) * ppg * kEsz;
@@ -1523,8 +1525,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(KA kargs) {
         Kp = (const uint8_t*)sv.win_k + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
         Vt = (const uint8_t*)sv.win_v + (bh * (a.n_w + 1) + slot) * ppg * kEsz;
       }
-      for (int idx = tid; idx < G * kP; idx += 256) {
-        const int g = idx / kP, j = idx % kP;
+      for (int idx = tid; idx < G * P; idx += 256) {
+        const int g = idx / P, j = idx % P;
         float acc = -INFINITY;
         if (j < nv) {
           acc = 0.f;
@@ -1542,8 +1544,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(KA kargs) {
         ts[g][i] = acc;
       }
       __syncthreads();
-      for (int idx = tid; idx < G * kP; idx += 256) {
-        const int g = idx / kP, j = idx % kP;
+      for (int idx = tid; idx < G * P; idx += 256) {
+        const int g = idx / P, j = idx % P;
         float acc = 0.f;
         for (int i = 0; i < a.r_k; ++i) acc += ld_elem<Elem>(kpart, off_lf_k(pk, j, i)) * ts[g][i];
         ss[g][j] = acc;
@@ -1552,11 +1554,11 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(KA kargs) {
     __syncthreads();
     if (tid < G) {
       float mx = -INFINITY;
-      for (int j = 0; j < kP; ++j) mx = fmaxf(mx, ss[tid][j]);
+      for (int j = 0; j < P; ++j) mx = fmaxf(mx, ss[tid][j]);
       const float m_new = fmaxf(sh_m[tid], mx);
       const float alpha = exp2f(sh_m[tid] - m_new);
       float sum = 0.f;
-      for (int j = 0; j < kP; ++j) {
+      for (int j = 0; j < P; ++j) {
         const float pj = exp2f(ss[tid][j] - m_new);
         ss[tid][j] = pj;
         sum += pj;
@@ -1571,14 +1573,14 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(KA kargs) {
         const int idx = tid + 256 * k, g = idx / kD, c = idx % kD;
         if (g >= G) break;
         float acc = o[k] * sh_alpha[g];
-        for (int j = 0; j < nv; ++j) acc += ss[g][j] * ld_elem<Elem>(Vt, (int64_t)c * kP + j);
+        for (int j = 0; j < nv; ++j) acc += ss[g][j] * ld_elem<Elem>(Vt, (int64_t)c * P + j);
         o[k] = acc;
       }
     } else {
       for (int idx = tid; idx < G * a.r_v; idx += 256) {
         const int g = idx / a.r_v, i = idx % a.r_v;
         float acc = 0.f;
-        for (int j = 0; j < kP; ++j) acc += ld_elem<Elem>(vpart, off_lf_v(pv, j, i)) * ss[g][j];
+        for (int j = 0; j < P; ++j) acc += ld_elem<Elem>(vpart, off_lf_v(pv, j, i)) * ss[g][j];
         us[g][i] = acc;
       }
       __syncthreads();
@@ -1620,6 +1622,7 @@ struct AppendDst {
   int64_t app_page;
   int app_row;
   int32_t app_entry;
+  int P;  // page length of the destination cache
 };
 
 struct MergeArgs {
@@ -1702,7 +1705,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MA margs) {
       const int mm = tid & (kD / 2 - 1);
       const float other = load_elem(m.k_new, bh * kD + (tid ^ (kD / 2)), m.dtype);
       float cs, sn;
-      rope_sincos(ad.app_page * kP + ad.app_row, m.rope_freq[mm], cs, sn);
+      rope_sincos(ad.app_page * ad.P + ad.app_row, m.rope_freq[mm], cs, sn);
       kk = tid < kD / 2 ? __builtin_fmaf(-other, sn, kk * cs) : __builtin_fmaf(other, sn, kk * cs);
     }
     qk = load_elem(m.q, row * kD + tid, m.dtype) * kk;
@@ -1732,7 +1735,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MA margs) {
       const int esz = m.dtype == PKV_BF16 ? 2 : 4;
       const int64_t bhp = append_pool_seq(margs, seq) * m.Hkv + hq / m.G;  // its pages
       uint8_t* kd = ad.k_dst + bhp * ad.dst_bh_stride + ((int64_t)ad.app_row * kD + tid) * esz;
-      uint8_t* vd = ad.v_dst + bhp * ad.dst_bh_stride + ((int64_t)tid * kP + ad.app_row) * esz;
+      uint8_t* vd = ad.v_dst + bhp * ad.dst_bh_stride + ((int64_t)tid * ad.P + ad.app_row) * esz;
       if (esz == 2) {
         *(uint16_t*)kd = ((const uint16_t*)m.k_new)[bh * kD + tid];
         *(uint16_t*)vd = ((const uint16_t*)m.v_new)[bh * kD + tid];
@@ -1809,7 +1812,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MA margs) {
 
 int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact) {
   (void)n_fact;
-  const int64_t pages = (T + kP - 1) / kP;
+  const int64_t pages = (T + g.P - 1) / g.P;
   const int64_t bh = (int64_t)g.B * g.Hkv;
   // Two four-wave workgroups per CU fill the chip at 2 waves per SIMD; halve
   // the split count while a wave would get fewer than min_run pages and a CU
@@ -1845,7 +1848,7 @@ MergeArgs merge_args(const CacheGeom& g, const AttnJob& job) {
   m.qscale = kLog2e / sqrtf((float)kD);
   m.G = g.G;
   m.Hkv = g.Hkv;
-  m.app = AppendDst{nullptr, nullptr, 0, nullptr, -1, -1, 0};
+  m.app = AppendDst{nullptr, nullptr, 0, nullptr, -1, -1, 0, g.P};
   m.rope = g.rope && job.k_new;
   std::memcpy(m.rope_freq, g.rope_freq, sizeof(m.rope_freq));
   return m;
@@ -1855,8 +1858,8 @@ MergeArgs merge_args(const CacheGeom& g, const AttnJob& job) {
 // page or a ring slot).
 AppendDst append_dst_of(const CacheGeom& g, const AttnJob& job) {
   AppendDst d{nullptr, nullptr, 0, (int32_t*)(g.base + g.lay.page_table), job.app_page, job.app_row,
-              job.app_entry};
-  const int64_t ppg_bytes = (int64_t)kP * kD * g.lay.elem_bytes;
+              job.app_entry, g.P};
+  const int64_t ppg_bytes = (int64_t)g.P * kD * g.lay.elem_bytes;
   const int64_t p = job.app_page;
   if (p < g.n_s) {
     d.k_dst = g.base + g.lay.sink_k + p * ppg_bytes;
@@ -1874,6 +1877,7 @@ AppendDst append_dst_of(const CacheGeom& g, const AttnJob& job) {
 }  // namespace
 
 bool batched_kernel(const CacheGeom& g) {
+  if (g.P != kP) return false;
   const int n8k = (g.r_k + 7) / 8, n8v = (g.r_v + 7) / 8;
   if (n8k != n8v) return false;
   if (g.dtype == PKV_BF16_INT4) return n8k <= 4;
@@ -1889,17 +1893,17 @@ int decode_batch_splits(const CacheGeom& g, const int64_t* T, int n, int* ns) {
   const int wps = g.dtype == PKV_BF16 && !g.rope ? mfma_waves_per_simd((g.r_k > g.r_v ? g.r_k + 7 : g.r_v + 7) / 8) : 2;
   const int64_t budget = (256LL * wps) / g.Hkv;  // splits over all caches
   int64_t total = 0;
-  for (int i = 0; i < n; ++i) total += (T[i] + kP - 1) / kP;
+  for (int i = 0; i < n; ++i) total += (T[i] + g.P - 1) / g.P;
   int64_t q = budget > 0 ? (total + budget - 1) / budget : total;
   if (q < 4 * 8) q = 4 * 8;
   for (;; ++q) {
     int64_t sum = 0;
-    for (int i = 0; i < n; ++i) sum += std::max<int64_t>(1, ((T[i] + kP - 1) / kP + q - 1) / q);
+    for (int i = 0; i < n; ++i) sum += std::max<int64_t>(1, ((T[i] + g.P - 1) / g.P + q - 1) / q);
     if (sum <= std::max<int64_t>(budget, n)) break;
   }
   int grid = 1;
   for (int i = 0; i < n; ++i) {
-    int64_t s = std::max<int64_t>(1, ((T[i] + kP - 1) / kP + q - 1) / q);
+    int64_t s = std::max<int64_t>(1, ((T[i] + g.P - 1) / g.P + q - 1) / q);
     if (s > kMaxSplits) s = kMaxSplits;
     ns[i] = (int)s;
     grid = std::max(grid, ns[i]);
@@ -1921,7 +1925,7 @@ hipError_t launch_merge_batch(const CacheGeom* gs, int n, const AttnJob& job, co
   MergeBatchArgs x;
   x.m = merge_args(gs[0], job);
   for (int i = 0; i < n; ++i) {
-    x.app[i] = job.k_new ? append_dst_of(gs[i], apps[i]) : AppendDst{nullptr, nullptr, 0, nullptr, -1, -1, 0};
+    x.app[i] = job.k_new ? append_dst_of(gs[i], apps[i]) : AppendDst{nullptr, nullptr, 0, nullptr, -1, -1, 0, gs[i].P};
     x.ns[i] = ns[i];
   }
   hipLaunchKernelGGL(merge_kernel<MergeBatchArgs>, dim3((unsigned)((int64_t)n * gs[0].Hq)),
@@ -1946,6 +1950,7 @@ DecodeArgs make_args(const CacheGeom& g, const AttnJob& job) {
   a.Hkv = g.Hkv;
   a.G = g.G;
   a.n_split = job.n_split;
+  a.P = g.P;
   a.n_s = g.n_s;
   a.n_w = g.n_w;
   a.r_k = g.r_k;
@@ -1991,7 +1996,7 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
       default:
         return hipErrorInvalidValue;
     }
-  } else if (g.dtype == PKV_BF16 && n8k == n8v && (!g.rope || n8k <= kRopeMfmaMaxN8)) {
+  } else if (g.dtype == PKV_BF16 && g.P == kP && n8k == n8v && (!g.rope || n8k <= kRopeMfmaMaxN8)) {
     switch (n8k * 2 + (g.rope ? 1 : 0)) {
 #define PKV_CASE(N)                                                                                       \
   case 2 * N:                                                                                             \

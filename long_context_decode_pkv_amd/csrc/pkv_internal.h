@@ -10,7 +10,8 @@
 
 namespace pkv {
 
-constexpr int kP = 64;    // page length supported by the kernels
+constexpr int kP = 64;    // page length of the matrix-core layouts and kernels
+constexpr int kMinP = 32;  // shortest page (the plain layout and the VALU kernel)
 constexpr int kD = 128;   // head dim supported by the kernels
 constexpr int kMaxG = 8;  // query heads per KV head handled by one wave
 constexpr int kMaxBatchCaches = 32;    // caches of one batched attention launch
@@ -40,30 +41,44 @@ constexpr int kMaxDecodeSplits = 512;  // workgroups per (sequence, KV head) in 
 // --------------------------------------------------------------------------
 
 struct PackDims {
+  int P;    // page length
   int n8;   // ceil(r / 8)
   int A;    // ranks per lane quad = 2 * n8
   int RT;   // rank tiles = ceil(A / 4)
   int KS2;  // 32-wide reduction steps over the rank = ceil(A / 8)
+  int rs;   // ranks stored per part: r8 = 8 n8 (64-token pages), else r
   int64_t k1, k2, v1, v2;  // element counts of the four operands
 };
 
-__host__ __device__ constexpr PackDims pack_dims(int r) {
+__host__ __device__ constexpr PackDims pack_dims(int r, int P = kP) {
   PackDims p{};
+  p.P = P;
   p.n8 = (r + 7) / 8;
   p.A = 2 * p.n8;
   p.RT = (p.A + 3) / 4;
   p.KS2 = (p.A + 7) / 8;
-  p.k1 = (int64_t)8 * p.n8 * kD;
-  p.k2 = (int64_t)kP * 8 * p.n8;
-  p.v1 = (int64_t)8 * p.n8 * kP;
-  p.v2 = (int64_t)kD * 8 * p.n8;
+  p.rs = P == kP ? 8 * p.n8 : r;
+  p.k1 = (int64_t)p.rs * kD;
+  p.k2 = (int64_t)P * p.rs;
+  p.v1 = (int64_t)p.rs * P;
+  p.v2 = (int64_t)kD * p.rs;
   return p;
 }
 
-__host__ __device__ inline int64_t part_elems(int r) {
-  PackDims p = pack_dims(r);
-  return p.k1 + p.k2;  // == p.v1 + p.v2 == r8 (P + d)
+__host__ __device__ inline int64_t part_elems(int r, int P = kP) {
+  PackDims p = pack_dims(r, P);
+  return p.k1 + p.k2;  // == p.v1 + p.v2 == rs (P + d)
 }
+
+// --------------------------------------------------------------------------
+// Plain layout of pages shorter than 64 tokens (read by the VALU kernel
+// only), at the exact rank r (no padding, so a part holds r (P + d)
+// elements, the count of Sec. 3.3 Eq. 3):
+//   K part:  Rf_K  r x d, row-major; then Lf_K  P x r, row-major
+//   V part:  Lf_V^T r x P;           then Rf_V^T d x r
+//   pre-RoPE K part: Rf_K^T d x r;   then Lf_K  P x r
+// The offsets below pick it whenever P != 64.
+// --------------------------------------------------------------------------
 
 // Rank i -> (tile mt, row-in-tile rho, compact index pieces).
 struct RankSlot {
@@ -84,6 +99,7 @@ __host__ __device__ inline RankSlot rank_slot(const PackDims& p, int i) {
 
 // K1: Rf_K[i][c]
 __host__ __device__ inline int64_t off_rf_k(const PackDims& p, int i, int c) {
+  if (p.P != kP) return (int64_t)i * kD + c;
   RankSlot s = rank_slot(p, i);
   int ks = c / 32, qk = (c % 32) / 8, e = c % 8;
   int64_t base = (int64_t)s.mt * 2048;
@@ -94,6 +110,7 @@ __host__ __device__ inline int64_t off_rf_k(const PackDims& p, int i, int c) {
 
 // K2: Lf_K[j][i]
 __host__ __device__ inline int64_t off_lf_k(const PackDims& p, int j, int i) {
+  if (p.P != kP) return p.k1 + (int64_t)j * p.rs + i;
   int bq = j / 16, mt = (j % 16) / 4, vj = j % 4;
   int rho = 4 * bq + vj;
   int qk = i / p.A, a = i % p.A, ks = a / 8, e = a % 8;
@@ -104,6 +121,7 @@ __host__ __device__ inline int64_t off_lf_k(const PackDims& p, int j, int i) {
 
 // V1: Lf_V[j][i] (stored as Lf_V^T)
 __host__ __device__ inline int64_t off_lf_v(const PackDims& p, int j, int i) {
+  if (p.P != kP) return (int64_t)i * p.P + j;
   RankSlot s = rank_slot(p, i);
   int qk = j / 16, ks = (j % 16) / 8, e = j % 8;
   int64_t base = (int64_t)s.mt * 1024;
@@ -114,6 +132,7 @@ __host__ __device__ inline int64_t off_lf_v(const PackDims& p, int j, int i) {
 
 // V2: Rf_V[i][c] (stored as Rf_V^T)
 __host__ __device__ inline int64_t off_rf_v(const PackDims& p, int i, int c) {
+  if (p.P != kP) return p.v1 + (int64_t)c * p.rs + i;
   int mt = c / 16, rho = c % 16;
   int qk = i / p.A, a = i % p.A, ks = a / 8, e = a % 8;
   int w = (p.A - 8 * ks) < 8 ? (p.A - 8 * ks) : 8;
@@ -270,6 +289,7 @@ struct CompressJob {
   // f < n_f_src0 is page f of src[0], the others page f - n_f_src0 of src[1]
   int64_t n_pages;
   int n_kind;                   // 1 (standalone) or 2 (K and V of a cache)
+  int page_rows;                // P: 64, or 32 (decomposed as 64 rows, the rest zero)
   int64_t n_f;
   int64_t n_f_src0;
   CompressSrc src[2];
@@ -305,6 +325,7 @@ hipError_t launch_compress_tri(const CompressJob& job, hipStream_t stream, hipEv
 
 struct CacheGeom {
   int B, Hkv, Hq, G;
+  int P;                        // page length (64, or 32 on the VALU kernel)
   int n_s, n_w;
   int64_t F_max, max_pages;
   int dtype;

@@ -14,58 +14,9 @@ import pytest
 import oracle
 import synth
 import long_context_decode_pkv_amd as pkv
-from gpu_common import TOL, make_cache, rel_err, require_gpu, to_dev, to_f64
+from gpu_common import TOL, assert_same_cache, make_cache, rel_err, require_gpu, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
-
-
-def _valid_dense_rows(cache, T):
-    """{(b, h, page): (K rows, V columns)} of every dense page's valid rows."""
-    import torch
-    L, sh = cache.layout, cache.shape
-    B, H, P, d = sh.batch, sh.n_kv_heads, 64, 128
-    esz = L["elem_bytes"]
-    n_s, ring = L["n_sink_slots"], L["n_ring_slots"]
-    cls, slot = cache.page_table(-(-T // P))
-    buf = cache.buffer
-    out = {}
-    for p in range(len(cls)):
-        if cls[p] == pkv.FACT:
-            continue
-        nv = min(P, T - p * P)
-        for b in range(B):
-            for h in range(H):
-                if cls[p] == pkv.SINK:
-                    base_k = L["sink_k"] + ((b * H + h) * n_s + slot[p]) * P * d * esz
-                    base_v = L["sink_v"] + ((b * H + h) * n_s + slot[p]) * P * d * esz
-                else:
-                    base_k = L["win_k"] + ((b * H + h) * ring + slot[p]) * P * d * esz
-                    base_v = L["win_v"] + ((b * H + h) * ring + slot[p]) * P * d * esz
-                k = buf[base_k: base_k + P * d * esz].view(P, d * esz)[:nv].clone()
-                v = buf[base_v: base_v + P * d * esz].view(d, P * esz)[:, :nv * esz].clone()
-                out[(b, h, p)] = (k, v)
-    torch.cuda.synchronize()
-    return out
-
-
-def _assert_same_cache(a, b, label):
-    import torch
-    assert a.state() == b.state(), (label, a.state(), b.state())
-    T, nf, _ = a.state()
-    n = -(-T // 64)
-    for x, y in zip(a.page_table(n), b.page_table(n)):
-        np.testing.assert_array_equal(x, y, err_msg=label)
-    L, sh = a.layout, a.shape
-    for bb in range(sh.batch):
-        for h in range(sh.n_kv_heads):
-            for f in range(nf):
-                for kind in (pkv.KEYS, pkv.VALUES):
-                    assert torch.equal(a.factor_part(bb, h, f, kind), b.factor_part(bb, h, f, kind)), \
-                        (label, bb, h, f, kind)
-    da, db = _valid_dense_rows(a, T), _valid_dense_rows(b, T)
-    assert da.keys() == db.keys()
-    for key in da:
-        assert torch.equal(da[key][0], db[key][0]) and torch.equal(da[key][1], db[key][1]), (label, key)
 
 
 def _chunk_vs_tokens(cfg_id, T0, chunks, B=1, kv_heads=2, store=None, aux=False, **kw):
@@ -102,7 +53,7 @@ def _chunk_vs_tokens(cfg_id, T0, chunks, B=1, kv_heads=2, store=None, aux=False,
         ob = b.decode(q)
         torch.cuda.synchronize()
         label = f"cfg{cfg_id} T0={T0} chunk {i} (C={C}, T={T})"
-        _assert_same_cache(a, b, label)
+        assert_same_cache(a, b, label)
         assert torch.equal(oa, ob), label
     return a, d
 

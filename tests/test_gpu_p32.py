@@ -1,0 +1,221 @@
+"""GPU parity of caches with 32-token pages against the oracle at P = 32
+(PuzzleKV Sec. 4.1 "Implementation": pages of 32 tokens, (r_K, r_V) =
+(16, 14), one 32-token sink page, the most recent completed page and the
+page being filled kept dense).
+
+Such caches keep their factor parts in the plain layout at the exact ranks
+and are attended by the vector-ALU kernel; a 32-row page is decomposed as a
+64-row page whose other rows are zero.  Gates as for 64-token pages: bf16
+storage 1e-2, fp32 storage 1e-4, relative to max |o_ref|; stored factors meet
+the reconstruction bound of the standalone decomposition; chunked prefill and
+batched steps agree bit for bit with their token-by-token and per-cache twins.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import long_context_decode_pkv_amd as pkv
+from gpu_common import TOL, make_cache, rel_err, require_gpu, to_dev, to_f64
+from test_gpu_chunk import _chunk_vs_tokens
+
+pytestmark = pytest.mark.gpu
+
+P = 32
+RK, RV = 16, 14  # the pages' operating point
+S, W = 32, 32    # one sink page, one window page
+
+
+def _case(cfg_id, T, B=1, kv_heads=2, rk=RK, rv=RV, s=S, w=W, splits=(0,), rope=None, label=""):
+    import torch
+    require_gpu()
+    d = synth.decode_inputs(cfg_id, T=T, B=B, kv_heads=kv_heads, with_f64=True)
+    dt = d["cfg"]["dtype"]
+    cache = make_cache(d, r_k=rk, r_v=rv, s=s, w=w, P=P)
+    if rope is not None:
+        cache.set_key_rope(rope)
+    cache.prefill(to_dev(d["K"], dt), to_dev(d["V"], dt))
+    ref = oracle.decode(d["q64"], d["K64"], d["V64"], T, P, s, w, rk, rv, dt, key_rope=rope)
+    q = to_dev(d["q"], dt)
+    for ns in splits:
+        o = to_f64(cache.decode(q, n_split=ns))
+        torch.cuda.synchronize()
+        e_s, e_e = rel_err(o, ref["o_stored"]), rel_err(o, ref["o_exact"])
+        print(f"[P=32 {label} cfg{cfg_id} T={T} r=({rk},{rv}) s={s} w={w} split={ns}] "
+              f"err_vs_stored={e_s:.3e} err_vs_exact={e_e:.3e}")
+        assert e_s <= TOL[dt], (label, ns, e_s)
+    return cache, d
+
+
+@pytest.mark.parametrize("cfg_id,T,B,kv,rk,rv,splits", [
+    (2, 32 * 40 + 5, 2, 2, RK, RV, (0, 1, 5)),  # bf16, ragged tail
+    (2, 32 * 64, 1, 2, RK, RV, (0, 7)),         # page-aligned T
+    (2, 32 * 20 + 31, 1, 1, 32, 32, (0,)),     # full rank of a 32-token page
+    (2, 32 * 20 + 1, 1, 2, 1, 3, (0, 2)),      # tiny ranks
+    (1, 32 * 30 + 17, 1, 1, RK, RV, (0, 3)),   # fp32 storage
+    (1, 32 * 12, 1, 1, 32, 32, (0,)),          # fp32, full rank
+])
+def test_p32_decode_against_oracle(cfg_id, T, B, kv, rk, rv, splits):
+    _case(cfg_id, T, B, kv, rk, rv, splits=splits, label="decode")
+
+
+def test_p32_short_and_windowless_caches():
+    _case(2, 20, label="sink only")
+    _case(2, 32 * 2 + 3, label="all dense")
+    _case(2, 32 * 10 + 7, s=0, w=0, splits=(0, 2), label="no sink, no window")
+    _case(2, 32 * 10 + 7, s=64, w=96, splits=(0,), label="s=64 w=96")
+
+
+def test_p32_pre_rope_keys():
+    _case(2, 32 * 30 + 9, rope=synth.rope_inv_freq(5e5), splits=(0, 2), label="pre-RoPE")
+
+
+def test_p32_factors_are_the_pages_own():
+    """The packed parts (plain layout, exact ranks) of a 32-token page hold
+    its rank-r decomposition: unpacked at P = 32 their product meets the bf16
+    reconstruction bound against the oracle's optimal error."""
+    import torch
+    cache, d = _case(2, 32 * 12 + 4, label="factors")
+    T, nf, _ = cache.state()
+    assert nf == 12 - 1 - 1
+    for kind, r, src in ((pkv.KEYS, RK, d["K64"]), (pkv.VALUES, RV, d["V64"])):
+        for h in range(2):
+            X = src[0, h, P:P * (1 + nf)].reshape(nf, P, 128)
+            U, S_, Wt = oracle.svd_batch(X)
+            opt = oracle.optimal_error(S_, r)
+            for f in range(nf):
+                part = cache.factor_part(0, h, f, kind).cpu().numpy()
+                torch.cuda.synchronize()
+                assert part.size == 2 * r * (P + 128)
+                Lf, Rf = pkv.unpack_factors(kind, r, pkv.BF16, part.view(np.uint16), P=P)
+                err = np.linalg.norm(X[f] - Lf.astype(np.float64) @ Rf.astype(np.float64))
+                nrm = np.linalg.norm(X[f])
+                bound = np.hypot(1.001 * opt[f] + 1e-5 * nrm, 2.0 ** -8 * nrm)
+                assert err <= bound, (kind, h, f, err, opt[f], bound)
+
+
+@pytest.mark.parametrize("r,out,pages", [
+    (16, "f32", "kv"), (14, "bf16", "kv"), (8, "f32", "kv"), (1, "f32", "kv"), (32, "f32", "gauss"),
+])
+def test_p32_standalone_decomposition(r, out, pages):
+    """pkv_compress_pages on (n, 32, 128) pages against the oracle's SVD:
+    ||X - Lf Rf|| <= 1.001 opt + 1e-5 ||X|| (bf16 output: plus the 2^-8 ||X||
+    storage floor), sigma within 2e-3 relative where the spectrum is
+    resolved.  Full rank (r = P) on well-conditioned Gaussian pages: the
+    fp32 Gram route's eigenvectors are orthogonal only to eps ||G|| / gap, so
+    r = P reconstructs a page to 1e-5 only where its trailing singular values
+    are separated (the synthetic key / value pages crowd sixteen of them into
+    1-2% of sigma_1)."""
+    import torch
+    require_gpu()
+    if pages == "kv":
+        cfg = synth.CONFIGS[2]
+        k, v = synth.kv_head(cfg, 0, 0, 64 * P)
+        X0 = np.concatenate([k, v]).reshape(-1, P, 128)
+    else:
+        X0 = np.random.default_rng(32).standard_normal((16, P, 128))
+    dt = "bf16" if pages == "kv" else "f32"
+    Xs = synth.to_storage(X0, dt)
+    X = to_dev(Xs, dt)
+    tdt = torch.bfloat16 if out == "bf16" else torch.float32
+    Lf, Rf, sig = pkv.compress_pages(X, r, out_dtype=tdt)
+    torch.cuda.synchronize()
+    assert tuple(Lf.shape) == (Xs.shape[0], P, r)
+    X64 = synth.storage_to_f64(Xs, dt)
+    err = np.sqrt(((X64 - to_f64(Lf) @ to_f64(Rf)) ** 2).sum(axis=(1, 2)))
+    U, S_, Wt = oracle.svd_batch(X64)
+    opt = oracle.optimal_error(S_, r)
+    nrm = np.sqrt((X64 ** 2).sum(axis=(1, 2)))
+    bound = 1.001 * opt + 1e-5 * nrm
+    if out == "bf16":
+        bound = np.sqrt(bound ** 2 + (2.0 ** -8 * nrm) ** 2)
+    print(f"[P=32 compress {pages} r={r} out={out}] worst err/bound = "
+          f"{np.max(err / np.maximum(bound, 1e-300)):.4f}")
+    assert np.all(err <= bound)
+    dev = np.abs(sig.cpu().numpy().astype(np.float64) - S_[:, :r]) - (2e-3 * S_[:, :r] + 1e-5 * S_[:, :1])
+    assert np.all(dev <= 0), float(dev.max())
+
+
+def test_p32_decode_steps_against_oracle():
+    """pkv_decode_step over 100 tokens from a ragged start: a page completes
+    every 32 steps and the page leaving the window is factorized in the same
+    call; every step's output against the oracle's incremental decoder."""
+    import torch
+    require_gpu()
+    cfg_id, T0, steps = 4, 32 * 10 + 3, 100
+    d = synth.decode_inputs(cfg_id, T=T0 + steps, B=2, kv_heads=2, with_f64=True)
+    dt = d["cfg"]["dtype"]
+    cache = make_cache(d, r_k=RK, r_v=RV, s=S, w=W, P=P, max_tokens=T0 + steps)
+    Kd, Vd = to_dev(d["K"], dt), to_dev(d["V"], dt)
+    cache.prefill(Kd[:, :, :T0].contiguous(), Vd[:, :, :T0].contiguous())
+    inc = oracle.IncrementalDecoder(d["K64"], d["V64"], P, S, W, RK, RV, dt)
+    ws = cache.workspace(512)
+    worst = 0.0
+    for t in range(steps):
+        T = T0 + t
+        qs = synth.step_queries(cfg_id, t, d["B"], d["Hq"], 128, dt)
+        o = to_f64(cache.step(Kd[:, :, T].contiguous(), Vd[:, :, T].contiguous(), to_dev(qs, dt),
+                              workspace=ws))
+        torch.cuda.synchronize()
+        ref_s, _ = inc.step(synth.storage_to_f64(qs, dt), T + 1)
+        err = rel_err(o, ref_s)
+        worst = max(worst, err)
+        assert err <= TOL[dt], (t, err)
+    assert cache.state()[1] == (T0 + steps) // P - 2
+    print(f"[P=32 step vs oracle] {steps} steps, worst err {worst:.3e}")
+
+
+def test_p32_chunks_match_token_by_token():
+    _chunk_vs_tokens(2, 32 * 5 + 17, [40, 7, 32, 300, ("step", 45), 1, 513], P=P, r_k=RK, r_v=RV, s=S, w=W)
+
+
+def test_p32_chunks_on_aux_stream():
+    _chunk_vs_tokens(2, 32 * 3 + 5, [40, 600, ("tok", 70), 1, 333], B=2, aux=True, P=P, r_k=RK, r_v=RV,
+                     s=S, w=W)
+
+
+def test_p32_batches_equal_single_caches():
+    """Batched attention and batched steps over 32-token caches of different
+    lengths (one launch per cache inside the batched call) equal the per-cache
+    calls bit for bit."""
+    import torch
+    require_gpu()
+    lengths, steps, ns = [32 * 20 + 5, 7, 32 * 3, 32 * 9 + 31], 40, 3
+    A, Bs, seqs = [], [], []
+    for i, T in enumerate(lengths):
+        d = synth.decode_inputs(2, T=T + steps + 32 * i, B=1, kv_heads=2)
+        Kd = to_dev(np.ascontiguousarray(d["K"][:, :, 32 * i:]), "bf16")
+        Vd = to_dev(np.ascontiguousarray(d["V"][:, :, 32 * i:]), "bf16")
+        for group in (A, Bs):
+            c = make_cache(d, r_k=RK, r_v=RV, s=S, w=W, P=P, max_tokens=T + steps)
+            c.prefill(Kd[:, :, :T].contiguous(), Vd[:, :, :T].contiguous())
+            group.append(c)
+        seqs.append((Kd, Vd, T))
+    Hq = d["Hq"]
+    q0 = to_dev(synth.step_queries(2, 999, len(lengths), Hq, 128, "bf16"), "bf16")
+    out = pkv.decode_batch(A, q0, n_split=ns)
+    for i, c in enumerate(Bs):
+        assert torch.equal(out[i:i + 1], c.decode(q0[i:i + 1].contiguous(), n_split=ns)), i
+    ws = pkv.batch_workspace(A, ns)
+    for t in range(steps):
+        k = torch.stack([Kd[0, :, T + t] for Kd, _, T in seqs]).contiguous()
+        v = torch.stack([Vd[0, :, T + t] for _, Vd, T in seqs]).contiguous()
+        q = to_dev(synth.step_queries(2, t, len(lengths), Hq, 128, "bf16"), "bf16")
+        oa = pkv.step_batch(A, k, v, q, n_split=ns, workspace=ws)
+        for i, c in enumerate(Bs):
+            ob = c.step(k[i:i + 1].contiguous(), v[i:i + 1].contiguous(), q[i:i + 1].contiguous(), n_split=ns)
+            torch.cuda.synchronize()
+            assert torch.equal(oa[i:i + 1], ob), (t, i)
+    for a, b in zip(A, Bs):
+        assert a.state() == b.state()
+
+
+def test_p32_errors():
+    require_gpu()
+    d = synth.decode_inputs(2, T=200, B=1, kv_heads=1)
+    with pytest.raises(pkv.PKVError) as ei:  # INT4 factor pages need 64-token pages
+        make_cache(d, r_k=RK, r_v=RV, s=S, w=W, P=P, store="int4")
+    assert ei.value.status == 2
+    with pytest.raises(pkv.PKVError) as ei:  # rank above the page length
+        make_cache(d, r_k=33, r_v=RV, s=S, w=W, P=P)
+    assert ei.value.status == 1

@@ -135,7 +135,8 @@ def test_layout_sizes():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(head_dim=64), 2), (dict(page_len=32), 2), (dict(n_q_heads=32, n_kv_heads=2), 2),
+    (dict(head_dim=64), 2), (dict(page_len=16), 2), (dict(page_len=32, dtype=pkv.BF16_INT4), 2),
+    (dict(page_len=128, sink=128, window=128), 2), (dict(page_len=32, rank_k=33), 1), (dict(n_q_heads=32, n_kv_heads=2), 2),
     (dict(sink=32), 1), (dict(window=100), 1), (dict(rank_k=0), 1), (dict(rank_v=65), 1),
     (dict(n_q_heads=7), 1), (dict(max_tokens=0), 1), (dict(dtype=5), 1),
 ])
@@ -143,6 +144,49 @@ def test_layout_validation(kw, status):
     with pytest.raises(pkv.PKVError) as ei:
         pkv.cache_layout(_shape(**kw))
     assert ei.value.status == status
+
+
+def test_layout_of_32_token_pages_meets_eq3():
+    """P = 32 (the pages' default page length) at (r_K, r_V) = (16, 14):
+    the factor parts hold the exact ranks, so a factorized page pair takes
+    (r_K + r_V)(P + d) / (2 P d) = 0.586 of its dense bytes (Sec. 3.3 Eq. 3;
+    Sec. 4.2)."""
+    lay = pkv.cache_layout(_shape(page_len=32, rank_k=16, rank_v=14, sink=32, window=32))
+    assert lay["dense_page_bytes"] == 32 * 128 * 2
+    assert lay["factor_k_elems"] == 16 * (32 + 128) and lay["factor_v_elems"] == 14 * (32 + 128)
+    assert lay["max_pages"] == 4096 // 32 and lay["max_fact_pages"] == 4096 // 32 - 2
+    ratio = lay["factor_page_bytes"] / (2 * lay["dense_page_bytes"])
+    assert ratio == pkv.storage_ratio(32, 16, 14, 128)
+    assert abs(ratio - 0.586) < 5e-4
+
+
+@pytest.mark.parametrize("r", [1, 7, 14, 16, 32])
+def test_plain_layout_of_32_token_pages(r):
+    """P = 32 parts: Rf_K r x d then Lf_K P x r (keys), Lf_V^T r x P then
+    Rf_V^T d x r (values), Rf_K^T d x r then Lf_K (pre-RoPE keys), all
+    row-major, every slot used once; pack and unpack are inverse."""
+    P = 32
+    n = pkv.factor_part_elems(r, P)
+    assert n == r * (P + 128)
+    Lf = np.arange(P * r, dtype=np.float32).reshape(P, r) + 1
+    Rf = np.arange(r * 128, dtype=np.float32).reshape(r, 128) + 1 + P * r
+    expect = {
+        pkv.KEYS: np.concatenate([Rf.ravel(), Lf.ravel()]),
+        pkv.VALUES: np.concatenate([Lf.T.ravel(), Rf.T.ravel()]),
+        pkv.KEYS_PRE_ROPE: np.concatenate([Rf.T.ravel(), Lf.ravel()]),
+    }
+    for kind, ref in expect.items():
+        packed = pkv.pack_factors(kind, r, pkv.F32, Lf, Rf, P=P)
+        np.testing.assert_array_equal(packed, ref)
+        Lb, Rb = pkv.unpack_factors(kind, r, pkv.F32, packed, P=P)
+        np.testing.assert_array_equal(Lb, Lf)
+        np.testing.assert_array_equal(Rb, Rf)
+        assert pkv.factor_part_bytes(kind, r, pkv.BF16, P=P) == 2 * n
+    L = pkv.lib()
+    nb = ctypes.c_int64()
+    assert L.pkv_factor_part_bytes(pkv.KEYS, P, 128, r, pkv.BF16_INT4, ctypes.byref(nb)) == 2
+    assert L.pkv_factor_part_elems(P, 128, P + 1, ctypes.byref(nb)) == 1
+    assert L.pkv_factor_part_elems(16, 128, 8, ctypes.byref(nb)) == 2
 
 
 def test_create_validation_without_gpu():
@@ -178,7 +222,8 @@ def test_create_validation_without_gpu():
 def test_compress_validation_without_gpu():
     L = pkv.lib()
     p = ctypes.c_void_p(4096)
-    assert L.pkv_compress_pages(p, 4, 32, 128, 8, 0, 0, p, p, None, None) == 2
+    assert L.pkv_compress_pages(p, 4, 16, 128, 8, 0, 0, p, p, None, None) == 2
+    assert L.pkv_compress_pages(p, 4, 32, 128, 33, 0, 0, p, p, None, None) == 1
     assert L.pkv_compress_pages(p, 4, 64, 128, 0, 0, 0, p, p, None, None) == 1
     assert L.pkv_compress_pages(p, 4, 64, 128, 65, 0, 0, p, p, None, None) == 1
     assert L.pkv_compress_pages(None, 4, 64, 128, 8, 0, 0, p, p, None, None) == 1
