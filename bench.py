@@ -15,7 +15,9 @@ Inputs are seeded synthetic pages with the sigma_i = i^-1.2 spectrum
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 Prints one JSON line.  Other workloads: llama3.1-8b-layer (B = 8, T = 32768,
-r = 16), qwen3-32b-layer-128k-int4 and llama3.1-8b-layer-int4 (the same
+r = 16), llama3.1-8b-layer-p32 (the same tokens in 32-token pages at
+(r_K, r_V) = (16, 14), sink 32, window 32: PuzzleKV Sec. 4.1), the same
+layers with pre-RoPE keys (-prerope), qwen3-32b-layer-128k-int4 and llama3.1-8b-layer-int4 (the same
 layers with INT4 factor pages, PuzzleKV Sec. 4.3), and compress (batched page
 decomposition, 524288 pages, r in {8,16,32}).
 """
@@ -153,15 +155,23 @@ def cpu_baseline_decode(cfg, K, V, q, T, store=None, key_rope=None):
 ROPE_BASE = {2: 5e5, 3: 1e6}  # rotary bases of the Llama 3.1 and Qwen3 checkpoints
 
 
-def bench_decode(args, cfg_id, name, store=None, rope=False):
+# The pages' own operating point (Sec. 4.1): 32-token pages, (r_K, r_V) =
+# (16, 14), one sink page and one window page.
+P32_POINT = dict(P=32, r_k=16, r_v=14, s=32, w=32)
+
+
+def bench_decode(args, cfg_id, name, store=None, rope=False, overrides=None):
     """One decode step of the workload's layer, on NL independent layer caches
     in rotation (a decode step of an NL-layer stack), so that no cache is
-    re-read from the 256 MB Infinity Cache between its uses."""
+    re-read from the 256 MB Infinity Cache between its uses.  `overrides`
+    replaces cache parameters of the workload (page length, ranks, sink,
+    window) over the same input tokens."""
     import torch
     import synth
     import long_context_decode_pkv_amd as pkv
 
     cfg = dict(synth.CONFIGS[cfg_id])
+    cfg.update(overrides or {})
     B, Hq, Hkv, T0 = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"]
     NL = args.layers
     total = T0 + args.warmup + 2 * args.steps  # timed pass, then an instrumented pass
@@ -169,7 +179,8 @@ def bench_decode(args, cfg_id, name, store=None, rope=False):
     dt = cfg["dtype"]
     Kd, Vd = to_dev(inp["K"], dt), to_dev(inp["V"], dt)
     caches = [pkv.Cache(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, rank_k=cfg["r_k"], rank_v=cfg["r_v"],
-                        sink=cfg["s"], window=cfg["w"], max_tokens=total, dtype=store or dt)
+                        sink=cfg["s"], window=cfg["w"], max_tokens=total, dtype=store or dt,
+                        page_len=cfg["P"])
               for _ in range(NL)]
     freqs = synth.rope_inv_freq(ROPE_BASE[cfg_id]) if rope else None
     if rope:  # pre-RoPE keys, rotated at attention (App. D.3)
@@ -309,7 +320,8 @@ def bench_decode(args, cfg_id, name, store=None, rope=False):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None if traffic is None else traffic["fetch"] + traffic["write"],
-                     "kernel": "decode_mfma_kernel (pkv_decode_partial)",
+                     "kernel": ("decode_mfma_kernel (pkv_decode_partial)" if cfg["P"] == 64
+                                else "decode_valu_kernel (pkv_decode_partial)"),
                      "launch_us_mean": durs.mean() * 1e6,
                      "bytes_per_launch": float(nbytes.mean()),
                      "traffic_read_write": None if traffic is None else [traffic["fetch"],
@@ -599,7 +611,8 @@ def main():
     ap.add_argument("--workload", default="qwen3-32b-layer-128k",
                     choices=["qwen3-32b-layer-128k", "llama3.1-8b-layer", "qwen3-32b-layer-128k-int4",
                              "llama3.1-8b-layer-int4", "qwen3-32b-layer-128k-prerope",
-                             "llama3.1-8b-layer-prerope", "llama3.1-8b-ragged-batch", "compress", "copy"])
+                             "llama3.1-8b-layer-prerope", "llama3.1-8b-layer-p32", "llama3.1-8b-ragged-batch",
+                             "compress", "copy"])
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--workers", type=int, default=1)
     ap.add_argument("--layers", type=int, default=4,
@@ -612,7 +625,7 @@ def main():
                     help="decode workloads: skip the batched-compression figure")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the hot path is measured on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     import torch
@@ -632,7 +645,8 @@ def main():
     else:
         cfg_id = 2 if args.workload.startswith("llama3.1-8b-layer") else 3
         res = bench_decode(args, cfg_id, args.workload, "int4" if args.workload.endswith("-int4") else None,
-                           rope=args.workload.endswith("-prerope"))
+                           rope=args.workload.endswith("-prerope"),
+                           overrides=P32_POINT if args.workload.endswith("-p32") else None)
     print(json.dumps(res), flush=True)
 
 

@@ -374,7 +374,7 @@ int32_t pkv_pack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t 
       (dtype != PKV_BF16 && dtype != PKV_F32) || !Lf || !Rf || !packed)
     return PKV_ERR_INVALID_ARG;
   const PackDims pd = pack_dims(r, P);
-  const int r8 = pd.rs;  // stored ranks, the padding ones zero
+  const int r8 = 8 * pd.n8;
   auto put = [&](int64_t idx, float v) {
     if (dtype == PKV_BF16) {
       uint16_t b;

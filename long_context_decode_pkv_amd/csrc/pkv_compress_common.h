@@ -129,7 +129,7 @@ struct FactorDst {
     pd = pack_dims(p.r, p.P);
     r = p.r;
     P = p.P;
-    r_store = packed ? pd.rs : p.r;
+    r_store = packed ? 8 * pd.n8 : p.r;
     kind = p.kind == 0 ? job.key_part_kind : PKV_VALUES;  // part layout
     n = n_;
     if (packed) {

@@ -317,6 +317,75 @@ __device__ inline void load_values(VRegs<N8>& R, const uint16_t* vp, int lane) {
   }
 }
 
+// The same register images from the parts of 32-token pages (K2 and V1
+// without the operand rows of page rows 32..63): lanes whose rows are absent
+// read a valid address and are zeroed.
+template <int W>
+__device__ inline void zero_unless(RawW<W>& r, bool ok) {
+#pragma unroll
+  for (int k = 0; k < W / 2; ++k) r.d[k] = ok ? r.d[k] : 0u;
+}
+
+template <int N8>
+__device__ inline void load_keys_half(KRegs<N8>& R, const uint16_t* kp, int lane) {
+  using Dm = FactDims<N8>;
+  const TileLane tl = tile_lane(lane);
+#pragma unroll
+  for (int mt = 0; mt < Dm::RT; ++mt) {
+    const bool part = Dm::kPartialTile && (mt == Dm::RT - 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (!part) {
+        R.k1[mt][ks] = ld16(kp + mt * 2048 + ks * 512 + lane * 8);
+      } else {
+        const bf16x8 v = ld16(kp + mt * 2048 + ks * 256 + tl.lam * 8);
+        R.k1[mt][ks] = tl.ok ? v : bf16x8{};
+      }
+    }
+  }
+  const int rho = lane & 15;
+  const bool ok = rho < 8;                        // page rows 16 (rho / 4) + ...
+  const int lam = ok ? 8 * (lane >> 4) + rho : 0;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const uint16_t* base = kp + Dm::K1 + mt * 32 * Dm::A;
+    ldraw(R.k2a[mt], base + lam * Dm::W0);
+    zero_unless(R.k2a[mt], ok);
+    if constexpr (Dm::KS2 > 1) {
+      ldraw(R.k2b[mt], base + 256 + lam * Dm::W1);
+      zero_unless(R.k2b[mt], ok);
+    }
+  }
+}
+
+template <int N8>
+__device__ inline void load_values_half(VRegs<N8>& R, const uint16_t* vp, int lane) {
+  using Dm = FactDims<N8>;
+  const TileLane tl = tile_lane(lane);
+  const bool lo = lane < 32;  // page rows 16 (lane / 16) + ...
+  const bool pok = tl.ok && lo;
+#pragma unroll
+  for (int mt = 0; mt < Dm::RT; ++mt) {
+    const bool part = Dm::kPartialTile && (mt == Dm::RT - 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (!part) {
+        const bf16x8 v = ld16(vp + mt * 512 + ks * 256 + (lane & 31) * 8);
+        R.v1[mt][ks] = lo ? v : bf16x8{};
+      } else {
+        const bf16x8 v = ld16(vp + mt * 512 + ks * 128 + (pok ? tl.lam : 0) * 8);
+        R.v1[mt][ks] = pok ? v : bf16x8{};
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const uint16_t* base = vp + Dm::V1 / 2 + mt * 64 * Dm::A;
+    ldraw(R.v2a[mt], base + lane * Dm::W0);
+    if constexpr (Dm::KS2 > 1) ldraw(R.v2b[mt], base + 512 + lane * Dm::W1);
+  }
+}
+
 struct SoftState {
   float m, l;
   floatx4 o[8];
@@ -456,7 +525,7 @@ __device__ inline void rank_operand(const floatx4 (&acc)[FactDims<N8>::RT], floa
 // the probability operand.
 template <int N8>
 __device__ inline void fact_keys(SoftState& st, const KRegs<N8>& R, const bf16x8 (&qb)[4], int q4,
-                                 float rem, bf16x8 (&pb)[2]) {
+                                 float rem, bf16x8 (&pb)[2], int nvalid = kP) {
   using Dm = FactDims<N8>;
   floatx4 at[Dm::RT];
 #pragma unroll
@@ -474,7 +543,7 @@ __device__ inline void fact_keys(SoftState& st, const KRegs<N8>& R, const bf16x8
 #pragma unroll
     for (int ks = 0; ks < Dm::KS2; ++ks) as_[mt] = mfma(R.k2(mt, ks), tb[ks], as_[mt]);
   }
-  softmax_page(st, as_, kP, q4, rem, pb);
+  softmax_page(st, as_, nvalid, q4, rem, pb);
 }
 
 // Eq. 4, value half: u = Lf_V^T p, o += Rf_V^T u.
@@ -498,6 +567,9 @@ __device__ inline void fact_values(SoftState& st, const VRegs<N8>& R, const bf16
   }
 }
 
+// A dense page of kRows <= 64 rows ([kRows][d] keys, [d][kRows] values) in
+// the 64-row frame: the operands of rows from kRows on are zero.
+template <int kRows = kP>
 __device__ inline void dense_page(SoftState& st, const uint16_t* Kp, const uint16_t* Vt, int nvalid,
                                   const bf16x8 (&qb)[4], int lane, float rem) {
   const int n = lane & 15, q4 = lane >> 4;
@@ -506,18 +578,24 @@ __device__ inline void dense_page(SoftState& st, const uint16_t* Kp, const uint1
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int j = 16 * (n >> 2) + 4 * mt + (n & 3);
+    const bool ok = kRows == kP || j < kRows;
     as_[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      as_[mt] = mfma(ld16(Kp + j * kD + 32 * ks + 8 * q4), qb[ks], as_[mt]);
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 k = ok ? ld16(Kp + j * kD + 32 * ks + 8 * q4) : bf16x8{};
+      as_[mt] = mfma(k, qb[ks], as_[mt]);
+    }
   }
   bf16x8 pb[2];
   softmax_page(st, as_, nvalid, q4, rem, pb);
+  const bool vok = kRows == kP || 16 * q4 < kRows;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      st.o[mt] = mfma(ld16(Vt + (16 * mt + n) * kP + 16 * q4 + 8 * ks), pb[ks], st.o[mt]);
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 v = vok ? ld16(Vt + (16 * mt + n) * kRows + 16 * q4 + 8 * ks) : bf16x8{};
+      st.o[mt] = mfma(v, pb[ks], st.o[mt]);
+    }
   }
 }
 
@@ -547,6 +625,7 @@ struct Bf16Factors {
   static constexpr bool kLdsRing = false;
   static constexpr bool kRope = false;
   static constexpr int kLdsBytes = 0;
+  static constexpr int kPageRows = kP;
   using K = KRegs<N8>;
   using V = VRegs<N8>;
   struct Query {
@@ -573,6 +652,28 @@ struct Bf16Factors {
   }
   __device__ static void values(SoftState& st, const V& R, const Probs& pb, int q4, float rem) {
     fact_values<N8>(st, R, pb, rem);
+  }
+};
+
+// bf16 factors of 32-token pages (the page length of Sec. 4.1), rank
+// 8 N8 <= 32: Bf16Factors' contractions in the 64-row frame with page rows
+// 32..63 absent (zero operands, masked scores).
+template <int N8>
+struct Bf16Half : Bf16Factors<N8> {
+  static constexpr int kPageRows = kMinP;
+  using Base = Bf16Factors<N8>;
+  using typename Base::K;
+  using typename Base::V;
+  using typename Base::Query;
+  using typename Base::Probs;
+  __device__ static void load_keys(K& R, const uint8_t* kp, int lane) {
+    pkv::load_keys_half<N8>(R, (const uint16_t*)kp, lane);
+  }
+  __device__ static void load_values(V& R, const uint8_t* vp, int lane) {
+    pkv::load_values_half<N8>(R, (const uint16_t*)vp, lane);
+  }
+  __device__ static void keys(SoftState& st, const K& R, const Query& Q, int q4, float rem, Probs& pb) {
+    fact_keys<N8>(st, R, Q.qb, q4, rem, pb, kMinP);
   }
 };
 
@@ -758,6 +859,7 @@ struct RopeFactors {
   static constexpr bool kKeyDoubleBuffer = false;
   static constexpr bool kLdsRing = false;
   static constexpr bool kRope = true;
+  static constexpr int kPageRows = kP;
   static constexpr int kLdsBytes = 0;
   struct K {
     RawW<Dm::W0> rfa[8];
@@ -983,6 +1085,7 @@ struct Int4Factors {
   static constexpr int kWavesPerSimd = 2;
   static constexpr bool kKeyDoubleBuffer = false;
   static constexpr bool kRope = false;
+  static constexpr int kPageRows = kP;
   // Factor pages stream through a per-wave ring of kRingSlots page slots in
   // LDS, filled by direct global -> LDS loads kRingSlots - 1 pages ahead of
   // the page being computed (registers cannot hold that much prefetch).
@@ -1203,7 +1306,8 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(KA k
   const int Hq = a.Hkv * a.G;
   const int64_t bh = (int64_t)sv.b_pool * a.Hkv + h;  // (sequence, KV head) in the pools
 
-  const WorkList wl = work_list(sv.T, sv.n_fact, a.n_s);
+  constexpr int PR = F::kPageRows;
+  const WorkList wl = work_list(sv.T, sv.n_fact, a.n_s, PR);
   const int64_t W = (int64_t)sv.n_split * kWaves;
   const int64_t wi = (int64_t)split * kWaves + wave;
   const int64_t e0 = unit_bound(wl, a, wi, W), e1 = unit_bound(wl, a, wi + 1, W);
@@ -1357,7 +1461,7 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(KA k
     const int64_t p = unit_page(wl, a, e);
     const int32_t ent = sv.table[p];
     const int cls = table_class(ent), slot = table_slot(ent);
-    const int64_t ppg = (int64_t)kP * kD;
+    const int64_t ppg = (int64_t)PR * kD;
     const uint16_t *Kp, *Vt;
     if (cls == PKV_PAGE_SINK) {
       Kp = (const uint16_t*)sv.sink_k + (bh * a.n_s + slot) * ppg;
@@ -1366,12 +1470,12 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(KA k
       Kp = (const uint16_t*)sv.win_k + (bh * (a.n_w + 1) + slot) * ppg;
       Vt = (const uint16_t*)sv.win_v + (bh * (a.n_w + 1) + slot) * ppg;
     }
-    const int64_t left = sv.T - p * kP;
+    const int64_t left = sv.T - p * PR;
     if constexpr (F::kRope) {
       rope_page_query(fq.qb, rl.q[wave], p * kP, a.rope_freq, fq.qscale, rl.base[wave], lane, rem);
       dense_page_rope(st, Kp, Vt, (int)(left < kP ? left : kP), fq.qb, rl, lane, rem);
     } else {
-      dense_page(st, Kp, Vt, (int)(left < kP ? left : kP), qd, lane, rem);
+      dense_page<PR>(st, Kp, Vt, (int)(left < PR ? left : PR), qd, lane, rem);
     }
   }
 
@@ -1877,9 +1981,9 @@ AppendDst append_dst_of(const CacheGeom& g, const AttnJob& job) {
 }  // namespace
 
 bool batched_kernel(const CacheGeom& g) {
-  if (g.P != kP) return false;
   const int n8k = (g.r_k + 7) / 8, n8v = (g.r_v + 7) / 8;
   if (n8k != n8v) return false;
+  if (g.P != kP) return g.dtype == PKV_BF16 && !g.rope;  // Bf16Half (r <= P = 32)
   if (g.dtype == PKV_BF16_INT4) return n8k <= 4;
   return g.dtype == PKV_BF16 && n8k <= 8 && (!g.rope || n8k <= kRopeMfmaMaxN8);
 }
@@ -2022,6 +2126,21 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
       PKV_ROPE(4)
 #undef PKV_ROPE
 #undef PKV_CASE
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else if (g.dtype == PKV_BF16 && g.P == kMinP && n8k == n8v && !g.rope) {
+    switch (n8k) {
+#define PKV_HALF(N)                                                                                    \
+  case N:                                                                                              \
+    hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Half<N>, KA>), grid, dim3(256), 0, stream, ev.start, \
+                          ev.stop, 0, ka);                                                             \
+    break;
+      PKV_HALF(1)
+      PKV_HALF(2)
+      PKV_HALF(3)
+      PKV_HALF(4)
+#undef PKV_HALF
       default:
         return hipErrorInvalidValue;
     }

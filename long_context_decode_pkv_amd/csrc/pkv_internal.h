@@ -46,7 +46,6 @@ struct PackDims {
   int A;    // ranks per lane quad = 2 * n8
   int RT;   // rank tiles = ceil(A / 4)
   int KS2;  // 32-wide reduction steps over the rank = ceil(A / 8)
-  int rs;   // ranks stored per part: r8 = 8 n8 (64-token pages), else r
   int64_t k1, k2, v1, v2;  // element counts of the four operands
 };
 
@@ -57,27 +56,26 @@ __host__ __device__ constexpr PackDims pack_dims(int r, int P = kP) {
   p.A = 2 * p.n8;
   p.RT = (p.A + 3) / 4;
   p.KS2 = (p.A + 7) / 8;
-  p.rs = P == kP ? 8 * p.n8 : r;
-  p.k1 = (int64_t)p.rs * kD;
-  p.k2 = (int64_t)P * p.rs;
-  p.v1 = (int64_t)p.rs * P;
-  p.v2 = (int64_t)kD * p.rs;
+  p.k1 = (int64_t)8 * p.n8 * kD;
+  p.k2 = (int64_t)P * 8 * p.n8;
+  p.v1 = (int64_t)8 * p.n8 * P;
+  p.v2 = (int64_t)kD * 8 * p.n8;
   return p;
 }
 
 __host__ __device__ inline int64_t part_elems(int r, int P = kP) {
   PackDims p = pack_dims(r, P);
-  return p.k1 + p.k2;  // == p.v1 + p.v2 == rs (P + d)
+  return p.k1 + p.k2;  // == p.v1 + p.v2 == r8 (P + d)
 }
 
 // --------------------------------------------------------------------------
-// Plain layout of pages shorter than 64 tokens (read by the VALU kernel
-// only), at the exact rank r (no padding, so a part holds r (P + d)
-// elements, the count of Sec. 3.3 Eq. 3):
-//   K part:  Rf_K  r x d, row-major; then Lf_K  P x r, row-major
-//   V part:  Lf_V^T r x P;           then Rf_V^T d x r
-//   pre-RoPE K part: Rf_K^T d x r;   then Lf_K  P x r
-// The offsets below pick it whenever P != 64.
+// Pages of P = 32 tokens keep the 64-row layout with page rows 32..63
+// absent: K1 and V2 (rank x channel operands) are unchanged; K2 and V1 drop
+// the lanes whose rows those are and store the rest compacted -- K2 lane
+// lam = 8 qk + rho (rho < 8), 32 A elements per row tile; V1 lanes 0..31,
+// 512 elements per full rank tile (a compacted last tile: lanes
+// lam = 8 qk + 2 b + v with qk < 2, 256).  A part holds r8 (32 + d)
+// elements.
 // --------------------------------------------------------------------------
 
 // Rank i -> (tile mt, row-in-tile rho, compact index pieces).
@@ -99,7 +97,6 @@ __host__ __device__ inline RankSlot rank_slot(const PackDims& p, int i) {
 
 // K1: Rf_K[i][c]
 __host__ __device__ inline int64_t off_rf_k(const PackDims& p, int i, int c) {
-  if (p.P != kP) return (int64_t)i * kD + c;
   RankSlot s = rank_slot(p, i);
   int ks = c / 32, qk = (c % 32) / 8, e = c % 8;
   int64_t base = (int64_t)s.mt * 2048;
@@ -110,29 +107,28 @@ __host__ __device__ inline int64_t off_rf_k(const PackDims& p, int i, int c) {
 
 // K2: Lf_K[j][i]
 __host__ __device__ inline int64_t off_lf_k(const PackDims& p, int j, int i) {
-  if (p.P != kP) return p.k1 + (int64_t)j * p.rs + i;
   int bq = j / 16, mt = (j % 16) / 4, vj = j % 4;
   int rho = 4 * bq + vj;
   int qk = i / p.A, a = i % p.A, ks = a / 8, e = a % 8;
   int w = (p.A - 8 * ks) < 8 ? (p.A - 8 * ks) : 8;
+  if (p.P != kP) return p.k1 + (int64_t)mt * 32 * p.A + 256 * ks + (8 * qk + rho) * w + e;  // rho < 8
   int lane = 16 * qk + rho;
   return p.k1 + (int64_t)mt * 64 * p.A + 512 * ks + lane * w + e;
 }
 
 // V1: Lf_V[j][i] (stored as Lf_V^T)
 __host__ __device__ inline int64_t off_lf_v(const PackDims& p, int j, int i) {
-  if (p.P != kP) return (int64_t)i * p.P + j;
   RankSlot s = rank_slot(p, i);
   int qk = j / 16, ks = (j % 16) / 8, e = j % 8;
-  int64_t base = (int64_t)s.mt * 1024;
-  if (!s.partial) return base + ks * 512 + (16 * qk + s.rho) * 8 + e;
+  const int64_t tile = p.P == kP ? 1024 : 512;  // P = 32: lanes 0..31 (qk < 2)
+  int64_t base = (int64_t)s.mt * tile;
+  if (!s.partial) return base + ks * (tile / 2) + (16 * qk + s.rho) * 8 + e;
   int lam = qk * 8 + s.b * 2 + s.v;
-  return base + ks * 256 + lam * 8 + e;
+  return base + ks * (tile / 4) + lam * 8 + e;
 }
 
 // V2: Rf_V[i][c] (stored as Rf_V^T)
 __host__ __device__ inline int64_t off_rf_v(const PackDims& p, int i, int c) {
-  if (p.P != kP) return p.v1 + (int64_t)c * p.rs + i;
   int mt = c / 16, rho = c % 16;
   int qk = i / p.A, a = i % p.A, ks = a / 8, e = a % 8;
   int w = (p.A - 8 * ks) < 8 ? (p.A - 8 * ks) : 8;

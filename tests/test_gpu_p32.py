@@ -3,9 +3,12 @@
 (16, 14), one 32-token sink page, the most recent completed page and the
 page being filled kept dense).
 
-Such caches keep their factor parts in the plain layout at the exact ranks
-and are attended by the vector-ALU kernel; a 32-row page is decomposed as a
-64-row page whose other rows are zero.  Gates as for 64-token pages: bf16
+Such caches keep their factor parts in the 64-token matrix-core operand
+order with the operand rows of page rows 32..63 left out; bf16 caches with
+equal padded ranks are attended by the matrix-core kernel in its 64-row frame
+(absent rows zero, their scores masked), fp32, unequal padded ranks and
+pre-RoPE keys by the vector-ALU kernel.  A 32-row page is decomposed on the
+leading 32 x 32 block of its zero-padded 64-row Gram matrix.  Gates as for 64-token pages: bf16
 storage 1e-2, fp32 storage 1e-4, relative to max |o_ref|; stored factors meet
 the reconstruction bound of the standalone decomposition; chunked prefill and
 batched steps agree bit for bit with their token-by-token and per-cache twins.
@@ -52,6 +55,8 @@ def _case(cfg_id, T, B=1, kv_heads=2, rk=RK, rv=RV, s=S, w=W, splits=(0,), rope=
     (2, 32 * 64, 1, 2, RK, RV, (0, 7)),         # page-aligned T
     (2, 32 * 20 + 31, 1, 1, 32, 32, (0,)),     # full rank of a 32-token page
     (2, 32 * 20 + 1, 1, 2, 1, 3, (0, 2)),      # tiny ranks
+    (2, 32 * 20 + 9, 1, 2, 8, 24, (0, 2)),     # unequal padded ranks: vector-ALU kernel
+    (2, 32 * 33 + 17, 1, 2, 24, 24, (0, 4)),   # odd n8: compacted last rank tile
     (1, 32 * 30 + 17, 1, 1, RK, RV, (0, 3)),   # fp32 storage
     (1, 32 * 12, 1, 1, 32, 32, (0,)),          # fp32, full rank
 ])
@@ -71,7 +76,7 @@ def test_p32_pre_rope_keys():
 
 
 def test_p32_factors_are_the_pages_own():
-    """The packed parts (plain layout, exact ranks) of a 32-token page hold
+    """The packed parts (compacted matrix-core order) of a 32-token page hold
     its rank-r decomposition: unpacked at P = 32 their product meets the bf16
     reconstruction bound against the oracle's optimal error."""
     import torch
@@ -86,7 +91,7 @@ def test_p32_factors_are_the_pages_own():
             for f in range(nf):
                 part = cache.factor_part(0, h, f, kind).cpu().numpy()
                 torch.cuda.synchronize()
-                assert part.size == 2 * r * (P + 128)
+                assert part.size == 2 * (-(-r // 8) * 8) * (P + 128)
                 Lf, Rf = pkv.unpack_factors(kind, r, pkv.BF16, part.view(np.uint16), P=P)
                 err = np.linalg.norm(X[f] - Lf.astype(np.float64) @ Rf.astype(np.float64))
                 nrm = np.linalg.norm(X[f])

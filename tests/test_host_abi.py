@@ -146,38 +146,35 @@ def test_layout_validation(kw, status):
     assert ei.value.status == status
 
 
-def test_layout_of_32_token_pages_meets_eq3():
-    """P = 32 (the pages' default page length) at (r_K, r_V) = (16, 14):
-    the factor parts hold the exact ranks, so a factorized page pair takes
-    (r_K + r_V)(P + d) / (2 P d) = 0.586 of its dense bytes (Sec. 3.3 Eq. 3;
-    Sec. 4.2)."""
+def test_layout_of_32_token_pages():
+    """P = 32 (the pages' default page length) at (r_K, r_V) = (16, 14): a
+    part holds r8 (P + d) elements, ranks padded to a multiple of 8 as at
+    P = 64, so a factorized page pair takes (r8_K + r8_V)(P + d) / (2 P d) of
+    its dense bytes -- Sec. 3.3 Eq. 3 exactly when the ranks are multiples of
+    8 (0.625 here, against Eq. 3's 0.586 at the unpadded (16, 14))."""
     lay = pkv.cache_layout(_shape(page_len=32, rank_k=16, rank_v=14, sink=32, window=32))
     assert lay["dense_page_bytes"] == 32 * 128 * 2
-    assert lay["factor_k_elems"] == 16 * (32 + 128) and lay["factor_v_elems"] == 14 * (32 + 128)
+    assert lay["factor_k_elems"] == 16 * (32 + 128) and lay["factor_v_elems"] == 16 * (32 + 128)
     assert lay["max_pages"] == 4096 // 32 and lay["max_fact_pages"] == 4096 // 32 - 2
     ratio = lay["factor_page_bytes"] / (2 * lay["dense_page_bytes"])
-    assert ratio == pkv.storage_ratio(32, 16, 14, 128)
-    assert abs(ratio - 0.586) < 5e-4
+    assert ratio == pkv.storage_ratio(32, 16, 16, 128) == 0.625
+    assert abs(pkv.storage_ratio(32, 16, 14, 128) - 0.586) < 5e-4
 
 
-@pytest.mark.parametrize("r", [1, 7, 14, 16, 32])
-def test_plain_layout_of_32_token_pages(r):
-    """P = 32 parts: Rf_K r x d then Lf_K P x r (keys), Lf_V^T r x P then
-    Rf_V^T d x r (values), Rf_K^T d x r then Lf_K (pre-RoPE keys), all
-    row-major, every slot used once; pack and unpack are inverse."""
+@pytest.mark.parametrize("r", [1, 7, 8, 14, 16, 24, 32])
+def test_packed_layout_of_32_token_pages_is_a_bijection(r):
+    """Every (operand, row, col) of a P = 32 part maps to a distinct slot,
+    every slot is used, and pack and unpack are inverse."""
     P = 32
     n = pkv.factor_part_elems(r, P)
-    assert n == r * (P + 128)
-    Lf = np.arange(P * r, dtype=np.float32).reshape(P, r) + 1
-    Rf = np.arange(r * 128, dtype=np.float32).reshape(r, 128) + 1 + P * r
-    expect = {
-        pkv.KEYS: np.concatenate([Rf.ravel(), Lf.ravel()]),
-        pkv.VALUES: np.concatenate([Lf.T.ravel(), Rf.T.ravel()]),
-        pkv.KEYS_PRE_ROPE: np.concatenate([Rf.T.ravel(), Lf.ravel()]),
-    }
-    for kind, ref in expect.items():
+    r8 = -(-r // 8) * 8
+    assert n == r8 * (P + 128)
+    for kind in (pkv.KEYS, pkv.VALUES, pkv.KEYS_PRE_ROPE):
+        Lf = np.arange(P * r8, dtype=np.float32).reshape(P, r8)[:, :r] + 1
+        Rf = np.arange(r8 * 128, dtype=np.float32).reshape(r8, 128)[:r] + 1 + P * r8
         packed = pkv.pack_factors(kind, r, pkv.F32, Lf, Rf, P=P)
-        np.testing.assert_array_equal(packed, ref)
+        vals = packed[packed != 0]
+        assert len(np.unique(vals)) == len(vals) == P * r + r * 128
         Lb, Rb = pkv.unpack_factors(kind, r, pkv.F32, packed, P=P)
         np.testing.assert_array_equal(Lb, Lf)
         np.testing.assert_array_equal(Rb, Rf)
@@ -187,6 +184,37 @@ def test_plain_layout_of_32_token_pages(r):
     assert L.pkv_factor_part_bytes(pkv.KEYS, P, 128, r, pkv.BF16_INT4, ctypes.byref(nb)) == 2
     assert L.pkv_factor_part_elems(P, 128, P + 1, ctypes.byref(nb)) == 1
     assert L.pkv_factor_part_elems(16, 128, 8, ctypes.byref(nb)) == 2
+
+
+def test_operand_order_of_32_token_parts():
+    """Spot-check the compacted operands of a P = 32 part against the P = 64
+    order: K1 and V2 (rank x channel) are the same; K2 keeps lane
+    lam = 8 (l // 16) + l % 16 of the lanes l % 16 < 8, V1 lanes 0..31."""
+    r = 16  # n8 = 2: A = 4 ranks per lane quad, one rank tile
+    g = np.random.default_rng(5)
+    Lf32 = g.standard_normal((32, r)).astype(np.float32)
+    Rf = g.standard_normal((r, 128)).astype(np.float32)
+    Lf64 = np.concatenate([Lf32, np.zeros((32, r), np.float32)])
+    for kind in (pkv.KEYS, pkv.VALUES):
+        p32 = pkv.pack_factors(kind, r, pkv.F32, Lf32, Rf, P=32)
+        p64 = pkv.pack_factors(kind, r, pkv.F32, Lf64, Rf)
+        if kind == pkv.KEYS:
+            k1 = 16 * 128
+            np.testing.assert_array_equal(p32[:k1], p64[:k1])
+            A = 4
+            for mt in range(4):
+                t32 = p32[k1 + mt * 32 * A: k1 + (mt + 1) * 32 * A].reshape(32, A)
+                t64 = p64[k1 + mt * 64 * A: k1 + (mt + 1) * 64 * A].reshape(64, A)
+                keep = [l for l in range(64) if l % 16 < 8]
+                np.testing.assert_array_equal(t32, t64[keep])
+                assert not t64[[l for l in range(64) if l % 16 >= 8]].any()
+        else:
+            v1_32, v1_64 = 16 * 32, 16 * 64
+            t32 = p32[:v1_32].reshape(2, 32, 8)
+            t64 = p64[:v1_64].reshape(2, 64, 8)
+            np.testing.assert_array_equal(t32, t64[:, :32])
+            assert not t64[:, 32:].any()
+            np.testing.assert_array_equal(p32[v1_32:], p64[v1_64:])
 
 
 def test_create_validation_without_gpu():
