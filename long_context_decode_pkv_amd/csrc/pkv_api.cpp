@@ -195,12 +195,9 @@ CompressSrc dense_src(const pkv_cache* c, const void* K, const void* V, int64_t 
   return src;
 }
 
-// Decomposition of n0 pages of `a` then n1 pages of `b` into the factor pool,
-// one launch on `s` (nothing when n0 + n1 == 0).
-hipError_t factorize(const pkv_cache* c, const CompressSrc& a, int64_t n0, const CompressSrc& b,
-                     int64_t n1, hipStream_t s) {
-  if (n0 < 0 || n1 < 0) return hipErrorInvalidValue;
-  if (n0 + n1 == 0) return hipSuccess;
+// The job that decomposes n0 pages of `a` then n1 pages of `b` into the
+// factor pool.
+CompressJob factor_job(const pkv_cache* c, const CompressSrc& a, int64_t n0, const CompressSrc& b, int64_t n1) {
   const CacheGeom g = geom_of(c);
   CompressJob job;
   std::memset(&job, 0, sizeof(job));
@@ -220,7 +217,16 @@ hipError_t factorize(const pkv_cache* c, const CompressSrc& a, int64_t n0, const
   job.fac_bh_pages = g.F_max;
   job.page_bytes = c->lay.factor_page_bytes;
   job.k_part_bytes = c->lay.factor_k_bytes;
-  return launch_compress(job, s);
+  return job;
+}
+
+// Decomposition of n0 pages of `a` then n1 pages of `b` into the factor pool,
+// one launch on `s` (nothing when n0 + n1 == 0).
+hipError_t factorize(const pkv_cache* c, const CompressSrc& a, int64_t n0, const CompressSrc& b,
+                     int64_t n1, hipStream_t s) {
+  if (n0 < 0 || n1 < 0) return hipErrorInvalidValue;
+  if (n0 + n1 == 0) return hipSuccess;
+  return launch_compress(factor_job(c, a, n0, b, n1), s);
 }
 
 // Factorize window pages [p_lo, p_hi) from their ring slots on `s`.
@@ -1055,13 +1061,57 @@ int32_t pkv_decode_step_batch(pkv_cache* const* caches, int32_t n, const void* k
   }
   for (int i = 0; i < n; ++i)
     if (wait_chunk(caches[i], s) != hipSuccess) return PKV_ERR_DEVICE;
-  // promotions of the pages leaving the windows (at most one per cache)
+  // promotions of the pages leaving the windows (at most one per cache):
+  // pages factorized early only wait for their event; the others are
+  // decomposed in one launch that also sets their table entries
+  int due[kMaxBatchCaches];
+  int n_due = 0;
   for (int i = 0; i < n; ++i) {
     pkv_cache* c = caches[i];
     const CacheGeom g = geom_of(c);
-    if (steady_fact(c->T + 1, g.P, g.n_s, g.n_w) > c->n_fact) {
+    if (steady_fact(c->T + 1, g.P, g.n_s, g.n_w) <= c->n_fact) continue;
+    const int64_t p_old = g.n_s + c->n_fact;
+    if (c->early_lo <= p_old && p_old < c->early_hi) {
       st = promote_now(c, stream);
       if (st != PKV_OK) return st;
+    } else {
+      due[n_due++] = i;
+    }
+  }
+  if (n_due == 1) {
+    st = promote_now(caches[due[0]], stream);
+    if (st != PKV_OK) return st;
+  } else if (n_due > 1) {
+    CompressBatch jb;
+    std::memset(&jb, 0, sizeof(jb));
+    const pkv_cache* c0 = caches[due[0]];
+    jb.base = factor_job(c0, ring_src(c0, g0.n_s), 1, ring_src(c0, g0.n_s), 0);
+    jb.n = n_due;
+    for (int k = 0; k < n_due; ++k) {
+      pkv_cache* c = caches[due[k]];
+      const int64_t f = c->n_fact;
+      CompressMember& m = jb.m[k];
+      m.src_k = c->base + c->lay.win_k;
+      m.src_v = c->base + c->lay.win_v;
+      m.fac = c->base + c->lay.factors;
+      m.fac_bh_pages = c->lay.max_fact_pages;
+      m.in_f0 = f;  // window page n_s + f sits in ring slot f mod (n_w + 1)
+      m.out_f0 = f;
+      m.table = (int32_t*)(c->base + c->lay.page_table);
+      m.table_page = g0.n_s + f;
+      m.table_entry = table_entry(PKV_PAGE_FACT, (int)f);
+    }
+    hipError_t e = launch_compress_batch(jb, s);
+    if (e == hipErrorNotSupported) {  // ranks above 32: one launch per cache
+      (void)hipGetLastError();
+      for (int k = 0; k < n_due; ++k) {
+        st = promote_now(caches[due[k]], stream);
+        if (st != PKV_OK) return st;
+      }
+    } else if (e != hipSuccess) {
+      return PKV_ERR_DEVICE;
+    } else {
+      for (int k = 0; k < n_due; ++k) caches[due[k]]->n_fact += 1;
     }
   }
   // attention over each cache's T_i tokens, then the merge with the new tokens

@@ -90,6 +90,7 @@ struct PageRef {
   int trans, r;
   int P;         // page rows
   const void* X;
+  uint8_t* part; // its packed factor part (cache jobs), else nullptr
 };
 
 __device__ inline PageRef page_ref(const CompressJob& job, int64_t n, int elem_bytes) {
@@ -107,13 +108,37 @@ __device__ inline PageRef page_ref(const CompressJob& job, int64_t n, int elem_b
   p.r = job.rank[p.kind];
   p.P = job.page_rows;
   p.X = (const uint8_t*)src.base[p.kind] + (p.bh * src.bh_stride + in * src.f_stride) * elem_bytes;
+  p.part = job.fac ? job.fac + (p.bh * job.fac_bh_pages + p.slot) * job.page_bytes +
+                         (int64_t)p.kind * job.k_part_bytes
+                   : nullptr;
+  return p;
+}
+
+// Page n of a batch of cache jobs: member n / per (per = jb.base.n_pages),
+// page n % per of its job -- jb.base with the member's pools.
+__device__ inline PageRef page_ref(const CompressBatch& jb, int64_t n, int elem_bytes) {
+  const CompressJob& job = jb.base;
+  const int64_t per = job.n_pages;
+  const CompressMember& m = jb.m[n / per];
+  const int64_t local = n % per;
+  PageRef p;
+  p.kind = (int)(local % job.n_kind);
+  const int64_t f = (local / job.n_kind) % job.n_f;
+  p.bh = local / ((int64_t)job.n_kind * job.n_f);
+  const CompressSrc& src = job.src[0];
+  int64_t in = m.in_f0 + f;
+  if (src.f_mod > 0) in %= src.f_mod;
+  p.slot = m.out_f0 + f;
+  p.trans = src.trans[p.kind];
+  p.r = job.rank[p.kind];
+  p.P = job.page_rows;
+  p.X = (const uint8_t*)(p.kind ? m.src_v : m.src_k) + (p.bh * src.bh_stride + in * src.f_stride) * elem_bytes;
+  p.part = m.fac + (p.bh * m.fac_bh_pages + p.slot) * job.page_bytes + (int64_t)p.kind * job.k_part_bytes;
   return p;
 }
 
 // Packed factor part of a cache job's page.
-__device__ inline uint8_t* factor_part(const CompressJob& job, const PageRef& p) {
-  return job.fac + (p.bh * job.fac_bh_pages + p.slot) * job.page_bytes + (int64_t)p.kind * job.k_part_bytes;
-}
+__device__ inline uint8_t* factor_part(const CompressJob&, const PageRef& p) { return p.part; }
 
 // Destination of factor element Rf[i][c] (i < r_store) and Lf[j][i].
 struct FactorDst {
@@ -125,7 +150,7 @@ struct FactorDst {
   void* rf;
   void* lf;
   __device__ FactorDst(const CompressJob& job, const PageRef& p, int64_t n_) {
-    packed = job.fac != nullptr;
+    packed = p.part != nullptr;
     pd = pack_dims(p.r, p.P);
     r = p.r;
     P = p.P;

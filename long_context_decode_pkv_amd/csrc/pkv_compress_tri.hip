@@ -478,9 +478,13 @@ __device__ __forceinline__ void store_q4(const CompressJob& job, const PageRef& 
   }
 }
 
-template <typename Elem, bool kQ4, int N>
-__device__ __forceinline__ void compress_tri_one(const CompressJob& job, int64_t n, TriShared& sh, int lane) {
-  const PageRef pr = page_ref(job, n, (int)sizeof(Elem));
+__device__ inline const CompressJob& base_job(const CompressJob& job) { return job; }
+__device__ inline const CompressJob& base_job(const CompressBatch& jb) { return jb.base; }
+
+template <typename Elem, bool kQ4, int N, class J>
+__device__ __forceinline__ void compress_tri_one(const J& jobs, int64_t n, TriShared& sh, int lane) {
+  const CompressJob& job = base_job(jobs);
+  const PageRef pr = page_ref(jobs, n, (int)sizeof(Elem));
   const Elem* X = (const Elem*)pr.X;
   const int r = pr.r;
 
@@ -668,15 +672,59 @@ __global__ __launch_bounds__(64, 3) void compress_tri_kernel(CompressJob job) {
   if (n < job.n_pages) compress_tri_one<Elem, kQ4, N>(job, n, sh, threadIdx.x);
 }
 
+// The batch of cache jobs; the first page of a member also sets its table
+// entry (read only by later launches on the stream).
+template <typename Elem, bool kQ4, int N>
+__global__ __launch_bounds__(64, 3) void compress_tri_batch_kernel(CompressBatch jb) {
+  __shared__ TriShared sh;
+  const int64_t n = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int64_t per = jb.base.n_pages;
+  if (n >= per * jb.n) return;
+  const CompressMember& m = jb.m[n / per];
+  if (n % per == 0 && threadIdx.x == 0 && m.table) m.table[m.table_page] = m.table_entry;
+  compress_tri_one<Elem, kQ4, N>(jb, n, sh, threadIdx.x);
+}
+
+// Grid of n pages: x up to 65536, y the rest.
+bool page_grid(int64_t n, dim3& grid) {
+  constexpr int64_t kGx = 65536;
+  const int64_t gx = n < kGx ? n : kGx;
+  const int64_t gy = (n + gx - 1) / gx;
+  if (gy > 65535) return false;
+  grid = dim3((unsigned)gx, (unsigned)gy);
+  return true;
+}
+
 }  // namespace
+
+hipError_t launch_compress_batch(const CompressBatch& jb, hipStream_t stream) {
+  const CompressJob& job = jb.base;
+  if (jb.n < 1 || jb.n > kMaxBatchCaches || job.n_pages <= 0) return hipErrorInvalidValue;
+  const int r_max = job.rank[1] > job.rank[0] ? job.rank[1] : job.rank[0];
+  if (r_max > kTriMaxRank || job.n_kind != 2) return hipErrorNotSupported;
+  dim3 grid;
+  if (!page_grid(job.n_pages * jb.n, grid)) return hipErrorInvalidValue;
+  const bool q4 = job.out_dtype == PKV_BF16_INT4;
+  if (q4 && (job.in_dtype != PKV_BF16 || job.page_rows != kP)) return hipErrorInvalidValue;
+  if (job.page_rows != kP && job.page_rows != kMinP) return hipErrorInvalidValue;
+  const bool full = job.page_rows == kP;
+  if (q4)
+    hipLaunchKernelGGL((compress_tri_batch_kernel<uint16_t, true, kP>), grid, dim3(64), 0, stream, jb);
+  else if (job.in_dtype == PKV_BF16 && full)
+    hipLaunchKernelGGL((compress_tri_batch_kernel<uint16_t, false, kP>), grid, dim3(64), 0, stream, jb);
+  else if (job.in_dtype == PKV_BF16)
+    hipLaunchKernelGGL((compress_tri_batch_kernel<uint16_t, false, kMinP>), grid, dim3(64), 0, stream, jb);
+  else if (full)
+    hipLaunchKernelGGL((compress_tri_batch_kernel<float, false, kP>), grid, dim3(64), 0, stream, jb);
+  else
+    hipLaunchKernelGGL((compress_tri_batch_kernel<float, false, kMinP>), grid, dim3(64), 0, stream, jb);
+  return hipGetLastError();
+}
 
 hipError_t launch_compress_tri(const CompressJob& job, hipStream_t stream, hipEvent_t start,
                                hipEvent_t stop) {
-  constexpr int64_t kGx = 65536;
-  const int64_t gx = job.n_pages < kGx ? job.n_pages : kGx;
-  const int64_t gy = (job.n_pages + gx - 1) / gx;
-  if (gy > 65535) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)gx, (unsigned)gy);
+  dim3 grid;
+  if (!page_grid(job.n_pages, grid)) return hipErrorInvalidValue;
   const bool q4 = job.out_dtype == PKV_BF16_INT4;
   if (q4 && (job.fac == nullptr || job.in_dtype != PKV_BF16 || job.page_rows != kP)) return hipErrorInvalidValue;
   if (job.page_rows != kP && job.page_rows != kMinP) return hipErrorInvalidValue;

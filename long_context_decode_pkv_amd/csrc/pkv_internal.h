@@ -304,6 +304,29 @@ struct CompressJob {
   float* sigma;
 };
 
+// Pages of several caches of one shape in one launch (the promotions of a
+// batched decode step).  Page n belongs to member n / base.n_pages and is
+// page n % base.n_pages of `base` (one source, src[0]) with the member's
+// window ring (src_k, src_v), input and factor slots and factor pool (whose
+// per-(sequence, KV head) stride is the member's own F_max); the first page
+// of a member also writes its page-table entry.
+struct CompressMember {
+  const void* src_k;
+  const void* src_v;
+  uint8_t* fac;
+  int64_t fac_bh_pages;  // the member's F_max (its own capacity)
+  int64_t in_f0, out_f0;
+  int32_t* table;
+  int64_t table_page;
+  int32_t table_entry;
+};
+
+struct CompressBatch {
+  CompressJob base;
+  int n;
+  CompressMember m[kMaxBatchCaches];
+};
+
 // Events the caller asked to bracket the next decode-partial or page
 // decomposition kernel with (pkv_time_next_kernel).  Taking them clears the
 // request; both are null when none is pending.
@@ -318,6 +341,9 @@ hipError_t launch_compress(const CompressJob& job, hipStream_t stream);
 constexpr int kTriMaxRank = 32;
 hipError_t launch_compress_tri(const CompressJob& job, hipStream_t stream, hipEvent_t start,
                                hipEvent_t stop);
+// One launch over a batch of cache jobs; ranks up to kTriMaxRank only
+// (hipErrorNotSupported above).
+hipError_t launch_compress_batch(const CompressBatch& jb, hipStream_t stream);
 
 struct CacheGeom {
   int B, Hkv, Hq, G;

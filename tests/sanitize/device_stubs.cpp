@@ -6,6 +6,7 @@
 
 namespace pkv {
 hipError_t launch_compress(const CompressJob&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_compress_batch(const CompressBatch&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_compress_tri(const CompressJob&, hipStream_t, hipEvent_t, hipEvent_t) {
   return hipErrorNotSupported;
 }

@@ -220,6 +220,17 @@ def test_step_batch_equals_per_cache_steps(label, cfg_id, kw):
     _run_step_twins(cfg_id, [0, 5, 64 * 3 + 60, 64 * 10 + 63, 64 * 20 + 1], 70, **kw)
 
 
+@pytest.mark.parametrize("label,cfg_id,kw", [
+    ("bf16", 2, {}),
+    ("int4", 2, dict(store="int4")),
+    ("pre-RoPE", 2, dict(rope=synth.rope_inv_freq(5e5))),
+])
+def test_step_batch_promotes_together(label, cfg_id, kw):
+    # every cache completes a page at the same steps, so the pages leaving the
+    # windows are decomposed by one launch (which also sets their entries)
+    _run_step_twins(cfg_id, [64 * 5 + 40, 64 * 9 + 40, 64 * 3 + 40, 64 * 12 + 40], 90, **kw)
+
+
 def test_step_batch_without_window():
     # w = 0: a completed page is promoted by the step that completes it (the
     # caches step one by one)

@@ -179,13 +179,16 @@ def test_p32_chunks_on_aux_stream():
                      s=S, w=W)
 
 
-def test_p32_batches_equal_single_caches():
+@pytest.mark.parametrize("lengths", [
+    [32 * 20 + 5, 7, 32 * 3, 32 * 9 + 31],   # pages complete at different steps
+    [32 * 20 + 9, 32 * 5 + 9, 32 * 11 + 9],  # ... at the same steps: one promotion launch
+])
+def test_p32_batches_equal_single_caches(lengths):
     """Batched attention and batched steps over 32-token caches of different
-    lengths (one launch per cache inside the batched call) equal the per-cache
-    calls bit for bit."""
+    lengths equal the per-cache calls bit for bit."""
     import torch
     require_gpu()
-    lengths, steps, ns = [32 * 20 + 5, 7, 32 * 3, 32 * 9 + 31], 40, 3
+    steps, ns = 40, 3
     A, Bs, seqs = [], [], []
     for i, T in enumerate(lengths):
         d = synth.decode_inputs(2, T=T + steps + 32 * i, B=1, kv_heads=2)
