@@ -28,8 +28,9 @@ def test_compress_pages_is_deterministic(r, out):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("store,rope", [(None, False), ("int4", False), (None, True)])
-def test_prefill_and_attention_are_deterministic(store, rope):
+@pytest.mark.parametrize("store,rope,P", [(None, False, 64), ("int4", False, 64), (None, True, 64),
+                                          (None, False, 32)])
+def test_prefill_and_attention_are_deterministic(store, rope, P):
     import torch
     require_gpu()
     d = synth.decode_inputs(3, T=64 * 300 + 17, B=1, kv_heads=2)
@@ -37,7 +38,7 @@ def test_prefill_and_attention_are_deterministic(store, rope):
     q = to_dev(d["q"], "bf16")
     outs, parts = [], []
     for _ in range(2):
-        c = make_cache(d, store=store)
+        c = make_cache(d, store=store, P=P)
         c.buffer.zero_()  # bytes no kernel writes compare equal too
         if rope:
             c.set_key_rope(synth.rope_inv_freq(1e6))

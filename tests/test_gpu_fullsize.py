@@ -3,7 +3,8 @@ bench.py times (default split counts, one launch over the whole batch).
 
 Sampling, so that the oracle finishes in seconds:
 - Workloads 2 and 3 (one decode step; workload 3 also with INT4 factor
-  pages) and 4 (512 incremental steps): every
+  pages, workload 2 also in 32-token pages at (16, 14)) and 4 (512
+  incremental steps): every
   (sequence, KV head) holds the recipe's pages of (sequence 0, KV head 0),
   so one oracle reconstruction serves all heads.  The queries are the
   recipe's own, distinct per query head, and every query head's output is
@@ -48,7 +49,7 @@ def recipe_queries(cfg_id):
 def make_full_cache(cfg, max_tokens, store=None):
     return pkv.Cache(batch=cfg["B"], n_q_heads=cfg["Hq"], n_kv_heads=cfg["Hkv"], rank_k=cfg["r_k"],
                      rank_v=cfg["r_v"], sink=cfg["s"], window=cfg["w"], max_tokens=max_tokens,
-                     dtype=store or cfg["dtype"])
+                     dtype=store or cfg["dtype"], page_len=cfg["P"])
 
 
 def oracle_outputs(q64, Khat, Vhat):
@@ -57,10 +58,14 @@ def oracle_outputs(q64, Khat, Vhat):
     return oracle.attention(q64.reshape(B * Hq, d), Khat, Vhat).reshape(B, Hq, d)
 
 
-def decode_full(cfg_id, store=None):
+def decode_full(cfg_id, store=None, overrides=None):
+    """One decode and one decode step of workload cfg_id at full size;
+    `overrides` replaces cache parameters (page length, ranks, sink, window)
+    over the same tokens."""
     import torch
     require_gpu()
-    cfg = synth.CONFIGS[cfg_id]
+    cfg = dict(synth.CONFIGS[cfg_id])
+    cfg.update(overrides or {})
     T, P, dt = cfg["T"], cfg["P"], cfg["dtype"]
     st = store or dt
     K, V, k64, v64 = replicated_kv(cfg_id, T + 1)
@@ -78,7 +83,7 @@ def decode_full(cfg_id, store=None):
         Vs = oracle.reconstruct_cache(v64[:TT], TT, P, cfg["s"], cfg["w"], cfg["r_v"], st, kind="V")[0]
         ref = oracle_outputs(q64, Ks, Vs)
         err = rel_err(o, ref)
-        print(f"[full size workload {cfg_id} {st}] T={TT}: max err / max|o_ref| = {err:.3e} "
+        print(f"[full size workload {cfg_id} {st} P={P}] T={TT}: max err / max|o_ref| = {err:.3e} "
               f"over {o.shape[0] * o.shape[1]} query heads")
         assert err <= TOL[st], (cfg_id, TT, err)
     cls, slot = cache.page_table(-(-(T + 1) // P))
@@ -93,6 +98,12 @@ def test_qwen3_32b_layer_128k_full():
 
 def test_llama31_8b_layer_32k_full():
     decode_full(2)
+
+
+def test_llama31_8b_layer_32k_p32_full():
+    # the bench's llama3.1-8b-layer-p32: 32-token pages at (16, 14), sink 32,
+    # window 32 (Sec. 4.1's operating point) on the matrix-core kernel
+    decode_full(2, overrides=dict(P=32, r_k=16, r_v=14, s=32, w=32))
 
 
 def test_qwen3_32b_layer_128k_int4_full():

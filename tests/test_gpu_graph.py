@@ -12,22 +12,22 @@ from gpu_common import make_cache, require_gpu, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _layers(n_layers, T, store=None):
+def _layers(n_layers, T, store=None, P=64):
     d = synth.decode_inputs(2, T=T, B=2, kv_heads=2)
     Kd, Vd = to_dev(d["K"], "bf16"), to_dev(d["V"], "bf16")
     caches = []
     for _ in range(n_layers):
-        c = make_cache(d, store=store)
+        c = make_cache(d, store=store, P=P)
         c.prefill(Kd, Vd)
         caches.append(c)
     return caches, d
 
 
-@pytest.mark.parametrize("store", [None, "int4"])
-def test_captured_attention_replays_exactly(store):
+@pytest.mark.parametrize("store,P", [(None, 64), ("int4", 64), (None, 32)])
+def test_captured_attention_replays_exactly(store, P):
     import torch
     require_gpu()
-    caches, d = _layers(4, 64 * 30 + 11, store)
+    caches, d = _layers(4, 64 * 30 + 11, store, P)
     q = to_dev(d["q"], "bf16").clone()
     outs = [torch.empty(q.shape, dtype=torch.float32, device="cuda:0") for _ in caches]
     wss = [c.workspace(0) for c in caches]
