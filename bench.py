@@ -613,7 +613,8 @@ def main():
     ap.add_argument("--workload", default="qwen3-32b-layer-128k",
                     choices=["qwen3-32b-layer-128k", "llama3.1-8b-layer", "qwen3-32b-layer-128k-int4",
                              "llama3.1-8b-layer-int4", "qwen3-32b-layer-128k-prerope",
-                             "llama3.1-8b-layer-prerope", "llama3.1-8b-layer-p32", "llama3.1-8b-ragged-batch",
+                             "llama3.1-8b-layer-prerope", "llama3.1-8b-layer-p32", "llama3.1-8b-layer-p32-prerope",
+                             "llama3.1-8b-ragged-batch",
                              "compress", "copy"])
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--workers", type=int, default=1)
@@ -648,7 +649,7 @@ def main():
         cfg_id = 2 if args.workload.startswith("llama3.1-8b-layer") else 3
         res = bench_decode(args, cfg_id, args.workload, "int4" if args.workload.endswith("-int4") else None,
                            rope=args.workload.endswith("-prerope"),
-                           overrides=P32_POINT if args.workload.endswith("-p32") else None)
+                           overrides=P32_POINT if "-p32" in args.workload else None)
     print(json.dumps(res), flush=True)
 
 

@@ -819,6 +819,8 @@ __device__ inline floatx4 rope_scores(const halfx8 (&ka)[4], const halfx8 (&qb)[
 
 // A dense page of pre-RoPE keys: rows loaded in the rotation's channel
 // order, rotated by their offsets; values as in dense_page.
+// (kRows = 32: the operands of rows 32..63 are zero, as in dense_page)
+template <int kRows = kP>
 __device__ inline void dense_page_rope(SoftState& st, const uint16_t* Kp, const uint16_t* Vt, int nvalid,
                                        const halfx8 (&qb)[4], const RopeLds& L, int lane, float rem) {
   const int n = lane & 15, q4 = lane >> 4;
@@ -826,8 +828,10 @@ __device__ inline void dense_page_rope(SoftState& st, const uint16_t* Kp, const 
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int j = 16 * (n >> 2) + 4 * mt + (n & 3);
+    const bool ok = kRows == kP || j < kRows;
     auto ld4 = [&](int ct) {
-      const u32x2 w = __builtin_nontemporal_load((const u32x2*)(Kp + j * kD + 16 * ct + 4 * q4));
+      const u32x2 w = ok ? __builtin_nontemporal_load((const u32x2*)(Kp + j * kD + 16 * ct + 4 * q4))
+                         : u32x2{0u, 0u};
       return floatx4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
                      __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
     };
@@ -838,11 +842,14 @@ __device__ inline void dense_page_rope(SoftState& st, const uint16_t* Kp, const 
   }
   bf16x8 pb[2];
   softmax_page(st, as_, nvalid, q4, rem, pb);
+  const bool vok = kRows == kP || 16 * q4 < kRows;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      st.o[mt] = mfma(ld16(Vt + (16 * mt + n) * kP + 16 * q4 + 8 * ks), pb[ks], st.o[mt]);
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 v = vok ? ld16(Vt + (16 * mt + n) * kRows + 16 * q4 + 8 * ks) : bf16x8{};
+      st.o[mt] = mfma(v, pb[ks], st.o[mt]);
+    }
   }
 }
 
@@ -852,14 +859,14 @@ constexpr int kRopeMfmaMaxN8 = 4;
 
 // bf16 factors of pre-RoPE keys: the key part holds Rf_K channel-major (the
 // V part's Rf layout) and Lf_K as in Bf16Factors; the V part as there.
-template <int N8>
+template <int N8, int PR = kP>  // PR: page rows (32: rows 32..63 absent, as in Bf16Half)
 struct RopeFactors {
   using Dm = FactDims<N8>;
   static constexpr int kWavesPerSimd = mfma_waves_per_simd(N8);
   static constexpr bool kKeyDoubleBuffer = false;
   static constexpr bool kLdsRing = false;
   static constexpr bool kRope = true;
-  static constexpr int kPageRows = kP;
+  static constexpr int kPageRows = PR;
   static constexpr int kLdsBytes = 0;
   struct K {
     RawW<Dm::W0> rfa[8];
@@ -900,15 +907,32 @@ struct RopeFactors {
       ldraw(R.rfa[ct], base + lane * Dm::W0);
       if constexpr (Dm::KS2 > 1) ldraw(R.rfb[ct], base + 512 + lane * Dm::W1);
     }
+    if constexpr (PR == kP) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const uint16_t* base = p + Dm::K1 + mt * 64 * Dm::A;
-      ldraw(R.k2a[mt], base + lane * Dm::W0);
-      if constexpr (Dm::KS2 > 1) ldraw(R.k2b[mt], base + 512 + lane * Dm::W1);
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint16_t* base = p + Dm::K1 + mt * 64 * Dm::A;
+        ldraw(R.k2a[mt], base + lane * Dm::W0);
+        if constexpr (Dm::KS2 > 1) ldraw(R.k2b[mt], base + 512 + lane * Dm::W1);
+      }
+    } else {  // compacted K2: lanes of tokens 32..63 zero
+      const int rho = lane & 15;
+      const bool ok = rho < 8;
+      const int lam = ok ? 8 * (lane >> 4) + rho : 0;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint16_t* base = p + Dm::K1 + mt * 32 * Dm::A;
+        ldraw(R.k2a[mt], base + lam * Dm::W0);
+        zero_unless(R.k2a[mt], ok);
+        if constexpr (Dm::KS2 > 1) {
+          ldraw(R.k2b[mt], base + 256 + lam * Dm::W1);
+          zero_unless(R.k2b[mt], ok);
+        }
+      }
     }
   }
   __device__ static void load_values(V& R, const uint8_t* vp, int lane) {
-    pkv::load_values<N8>(R, (const uint16_t*)vp, lane);
+    if constexpr (PR == kP) pkv::load_values<N8>(R, (const uint16_t*)vp, lane);
+    else pkv::load_values_half<N8>(R, (const uint16_t*)vp, lane);
   }
   // token tile mt: K_p^T columns = its 16 tokens, 8 channel tiles of rows
   __device__ static void keys(SoftState& st, const K& R, const Query& Q, const RopeLds& L, int lane,
@@ -931,7 +955,7 @@ struct RopeFactors {
       }
       as_[mt] = rope_scores(ka, Q.qb);
     }
-    softmax_page(st, as_, kP, q4, rem, pb);
+    softmax_page(st, as_, PR, q4, rem, pb);
   }
   __device__ static void values(SoftState& st, const V& R, const Probs& pb, int, float rem) {
     fact_values<N8>(st, R, pb, rem);
@@ -1438,7 +1462,7 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(KA k
       for (; e < e1; ++e) {
         typename F::Probs pb;
         if constexpr (F::kRope) {
-          rope_page_query(fq.qb, rl.q[wave], unit_page(wl, a, e) * kP, a.rope_freq, fq.qscale, rl.base[wave],
+          rope_page_query(fq.qb, rl.q[wave], unit_page(wl, a, e) * PR, a.rope_freq, fq.qscale, rl.base[wave],
                           lane, rem);
           F::keys(st, kr, fq, rl, lane, rem, pb);
         } else {
@@ -1472,8 +1496,8 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(KA k
     }
     const int64_t left = sv.T - p * PR;
     if constexpr (F::kRope) {
-      rope_page_query(fq.qb, rl.q[wave], p * kP, a.rope_freq, fq.qscale, rl.base[wave], lane, rem);
-      dense_page_rope(st, Kp, Vt, (int)(left < kP ? left : kP), fq.qb, rl, lane, rem);
+      rope_page_query(fq.qb, rl.q[wave], p * PR, a.rope_freq, fq.qscale, rl.base[wave], lane, rem);
+      dense_page_rope<PR>(st, Kp, Vt, (int)(left < PR ? left : PR), fq.qb, rl, lane, rem);
     } else {
       dense_page<PR>(st, Kp, Vt, (int)(left < PR ? left : PR), qd, lane, rem);
     }
@@ -1983,7 +2007,7 @@ AppendDst append_dst_of(const CacheGeom& g, const AttnJob& job) {
 bool batched_kernel(const CacheGeom& g) {
   const int n8k = (g.r_k + 7) / 8, n8v = (g.r_v + 7) / 8;
   if (n8k != n8v) return false;
-  if (g.P != kP) return g.dtype == PKV_BF16 && !g.rope;  // Bf16Half (r <= P = 32)
+  if (g.P != kP) return g.dtype == PKV_BF16;  // Bf16Half, RopeFactors<N8, 32> (r <= P = 32)
   if (g.dtype == PKV_BF16_INT4) return n8k <= 4;
   return g.dtype == PKV_BF16 && n8k <= 8 && (!g.rope || n8k <= kRopeMfmaMaxN8);
 }
@@ -2126,6 +2150,21 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
       PKV_ROPE(4)
 #undef PKV_ROPE
 #undef PKV_CASE
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else if (g.dtype == PKV_BF16 && g.P == kMinP && n8k == n8v && g.rope && n8k <= kRopeMfmaMaxN8) {
+    switch (n8k) {
+#define PKV_HALF_ROPE(N)                                                                                   \
+  case N:                                                                                                  \
+    hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<N, kMinP>, KA>), grid, dim3(256), 0, stream,     \
+                          ev.start, ev.stop, 0, ka);                                                       \
+    break;
+      PKV_HALF_ROPE(1)
+      PKV_HALF_ROPE(2)
+      PKV_HALF_ROPE(3)
+      PKV_HALF_ROPE(4)
+#undef PKV_HALF_ROPE
       default:
         return hipErrorInvalidValue;
     }

@@ -4,14 +4,15 @@
 page being filled kept dense).
 
 Such caches keep their factor parts in the 64-token matrix-core operand
-order with the operand rows of page rows 32..63 left out; bf16 caches with
-equal padded ranks are attended by the matrix-core kernel in its 64-row frame
-(absent rows zero, their scores masked), fp32, unequal padded ranks and
-pre-RoPE keys by the vector-ALU kernel.  A 32-row page is decomposed on the
-leading 32 x 32 block of its zero-padded 64-row Gram matrix.  Gates as for 64-token pages: bf16
-storage 1e-2, fp32 storage 1e-4, relative to max |o_ref|; stored factors meet
-the reconstruction bound of the standalone decomposition; chunked prefill and
-batched steps agree bit for bit with their token-by-token and per-cache twins.
+order with the operand rows of page rows 32..63 left out.  bf16 caches with
+equal padded ranks, pre-RoPE keys included, are attended by the matrix-core
+kernel in its 64-row frame (absent rows zero, their scores masked); fp32
+caches and unequal padded ranks by the vector-ALU kernel.  A 32-row page is
+decomposed on the leading 32 x 32 block of its zero-padded 64-row Gram
+matrix.  Gates as for 64-token pages: bf16 storage 1e-2, fp32 storage 1e-4,
+relative to max |o_ref|; stored factors meet the reconstruction bound of the
+standalone decomposition; chunked prefill and batched steps agree bit for
+bit with their token-by-token and per-cache twins.
 """
 import numpy as np
 import pytest
@@ -72,7 +73,10 @@ def test_p32_short_and_windowless_caches():
 
 
 def test_p32_pre_rope_keys():
+    # matrix-core kernel (equal padded ranks), then the vector-ALU kernel
     _case(2, 32 * 30 + 9, rope=synth.rope_inv_freq(5e5), splits=(0, 2), label="pre-RoPE")
+    _case(3, 32 * 40 + 21, rk=24, rv=24, rope=synth.rope_inv_freq(1e6), splits=(0, 3), label="pre-RoPE r=24")
+    _case(2, 32 * 12 + 7, rk=8, rv=24, rope=synth.rope_inv_freq(5e5), label="pre-RoPE valu")
 
 
 def test_p32_factors_are_the_pages_own():
@@ -141,19 +145,24 @@ def test_p32_standalone_decomposition(r, out, pages):
     assert np.all(dev <= 0), float(dev.max())
 
 
-def test_p32_decode_steps_against_oracle():
+@pytest.mark.parametrize("rope", [False, True])
+def test_p32_decode_steps_against_oracle(rope):
     """pkv_decode_step over 100 tokens from a ragged start: a page completes
     every 32 steps and the page leaving the window is factorized in the same
-    call; every step's output against the oracle's incremental decoder."""
+    call; every step's output against the oracle's incremental decoder (with
+    pre-RoPE keys the new key turns at its position in the merge)."""
     import torch
     require_gpu()
     cfg_id, T0, steps = 4, 32 * 10 + 3, 100
     d = synth.decode_inputs(cfg_id, T=T0 + steps, B=2, kv_heads=2, with_f64=True)
     dt = d["cfg"]["dtype"]
+    f = synth.rope_inv_freq(5e5) if rope else None
     cache = make_cache(d, r_k=RK, r_v=RV, s=S, w=W, P=P, max_tokens=T0 + steps)
+    if rope:
+        cache.set_key_rope(f)
     Kd, Vd = to_dev(d["K"], dt), to_dev(d["V"], dt)
     cache.prefill(Kd[:, :, :T0].contiguous(), Vd[:, :, :T0].contiguous())
-    inc = oracle.IncrementalDecoder(d["K64"], d["V64"], P, S, W, RK, RV, dt)
+    inc = oracle.IncrementalDecoder(d["K64"], d["V64"], P, S, W, RK, RV, dt, key_rope=f)
     ws = cache.workspace(512)
     worst = 0.0
     for t in range(steps):
@@ -179,11 +188,12 @@ def test_p32_chunks_on_aux_stream():
                      s=S, w=W)
 
 
-@pytest.mark.parametrize("lengths", [
-    [32 * 20 + 5, 7, 32 * 3, 32 * 9 + 31],   # pages complete at different steps
-    [32 * 20 + 9, 32 * 5 + 9, 32 * 11 + 9],  # ... at the same steps: one promotion launch
+@pytest.mark.parametrize("lengths,rope", [
+    ([32 * 20 + 5, 7, 32 * 3, 32 * 9 + 31], False),   # pages complete at different steps
+    ([32 * 20 + 9, 32 * 5 + 9, 32 * 11 + 9], False),  # ... at the same steps: one promotion launch
+    ([32 * 20 + 5, 7, 32 * 3, 32 * 9 + 31], True),    # pre-RoPE keys
 ])
-def test_p32_batches_equal_single_caches(lengths):
+def test_p32_batches_equal_single_caches(lengths, rope):
     """Batched attention and batched steps over 32-token caches of different
     lengths equal the per-cache calls bit for bit."""
     import torch
@@ -196,6 +206,8 @@ def test_p32_batches_equal_single_caches(lengths):
         Vd = to_dev(np.ascontiguousarray(d["V"][:, :, 32 * i:]), "bf16")
         for group in (A, Bs):
             c = make_cache(d, r_k=RK, r_v=RV, s=S, w=W, P=P, max_tokens=T + steps)
+            if rope:
+                c.set_key_rope(synth.rope_inv_freq(5e5))
             c.prefill(Kd[:, :, :T].contiguous(), Vd[:, :, :T].contiguous())
             group.append(c)
         seqs.append((Kd, Vd, T))
