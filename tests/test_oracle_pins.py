@@ -169,16 +169,18 @@ def test_eckart_young_bruteforce_3x4():
     assert best - opt < 1e-4 * np.linalg.norm(X)
 
 
-def test_full_rank_reconstructs(oracle):
+@pytest.mark.parametrize("P", [64, 32])
+def test_full_rank_reconstructs(oracle, P):
     g = np.random.default_rng(6)
-    X = g.standard_normal((64, 128))
-    Lf, Rf, _ = oracle.factorize(X, 64)
+    X = g.standard_normal((P, 128))
+    Lf, Rf, _ = oracle.factorize(X, P)  # r = min(P, d)
     assert np.linalg.norm(X - Lf @ Rf) <= 1e-13 * np.linalg.norm(X)
 
 
-def test_exact_rank_k_reconstructs(oracle):
+@pytest.mark.parametrize("P", [64, 32])
+def test_exact_rank_k_reconstructs(oracle, P):
     g = np.random.default_rng(7)
-    X = g.standard_normal((64, 8)) @ g.standard_normal((8, 128))
+    X = g.standard_normal((P, 8)) @ g.standard_normal((8, 128))
     for r in (8, 9, 16):
         Lf, Rf, _ = oracle.factorize(X, r)
         assert np.linalg.norm(X - Lf @ Rf) <= 1e-12 * np.linalg.norm(X)
@@ -273,11 +275,13 @@ def test_pagewise_eq4_eq5_equals_global_softmax(oracle):
     assert (cls == oracle.FACT).sum() == 6
 
 
-def test_full_rank_decode_equals_dense(oracle):
+@pytest.mark.parametrize("P,s,w", [(64, 64, 128), (32, 32, 32)])
+def test_full_rank_decode_equals_dense(oracle, P, s, w):
+    # r = min(P, d): every factorized page is reproduced, so the hybrid cache
+    # is the dense cache (32-token pages: the pages' default dense region)
     d = synth.decode_inputs(1, with_f64=True)
-    cfg = d["cfg"]
-    out = oracle.decode(d["q64"], d["K64"], d["V64"], d["T"], cfg["P"], cfg["s"], cfg["w"], 64, 64,
-                        None)["o_stored"]
+    assert int((oracle.classify(d["T"], P, s, w)[0] == oracle.FACT).sum()) > 0
+    out = oracle.decode(d["q64"], d["K64"], d["V64"], d["T"], P, s, w, P, P, None)["o_stored"]
     dense = oracle.attention(d["q64"][0], d["K64"][0, 0], d["V64"][0, 0])
     np.testing.assert_allclose(out[0], dense, atol=1e-12 * np.abs(dense).max())
 
