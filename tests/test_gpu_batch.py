@@ -169,12 +169,15 @@ def _step_twins(cfg_id, lengths, steps, kv_heads=2, store=None, rope=None, aux=F
             c.prefill(Kd[:, :, :T].contiguous(), Vd[:, :, :T].contiguous())
             group.append(c)
         seqs.append((Kd, Vd, T))
-    if aux:
+    if aux:  # True, or one flag per cache
+        mask = list(aux) if isinstance(aux, (list, tuple)) else [True] * len(lengths)
         st_a, st_b = torch.cuda.Stream(), torch.cuda.Stream()
-        for c in A:
-            c.set_aux_stream(st_a)
-        for c in Bs:
-            c.set_aux_stream(st_b)
+        for c, m in zip(A, mask):
+            if m:
+                c.set_aux_stream(st_a)
+        for c, m in zip(Bs, mask):
+            if m:
+                c.set_aux_stream(st_b)
     return seqs, A, Bs, d
 
 
@@ -224,6 +227,9 @@ def test_step_batch_equals_per_cache_steps(label, cfg_id, kw):
     ("bf16", 2, {}),
     ("int4", 2, dict(store="int4")),
     ("pre-RoPE", 2, dict(rope=synth.rope_inv_freq(5e5))),
+    # caches with an aux stream only wait for their early factorization; the
+    # others share the one decomposition launch
+    ("mixed aux", 2, dict(aux=[True, False, True, False])),
 ])
 def test_step_batch_promotes_together(label, cfg_id, kw):
     # every cache completes a page at the same steps, so the pages leaving the
