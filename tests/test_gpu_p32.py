@@ -239,3 +239,32 @@ def test_p32_errors():
     with pytest.raises(pkv.PKVError) as ei:  # rank above the page length
         make_cache(d, r_k=33, r_v=RV, s=S, w=W, P=P)
     assert ei.value.status == 1
+
+
+def test_p32_random_shapes_against_oracle():
+    """Seeded random 32-token caches: workload recipes with GQA groups 1, 4
+    and 8, ranks 1..32 (K and V drawn apart, so both kernels run), sink and
+    window of 0..3 pages, ragged lengths, batch and KV heads 1..2, default
+    and explicit split counts -- each against the oracle."""
+    import torch
+    require_gpu()
+    g = np.random.default_rng(3232)
+    for case in range(14):
+        cfg_id = int(g.choice([1, 2, 3, 4]))
+        rk = int(g.integers(1, 33))
+        rv = rk if g.random() < 0.5 else int(g.integers(1, 33))
+        s, w = 32 * int(g.integers(0, 4)), 32 * int(g.integers(0, 4))
+        T = int(g.integers(1, 32 * 40))
+        B, kv = int(g.integers(1, 3)), int(g.integers(1, 3))
+        ns = int(g.choice([0, 1, 3, 8]))
+        d = synth.decode_inputs(cfg_id, T=T, B=B, kv_heads=kv, with_f64=True)
+        dt = d["cfg"]["dtype"]
+        cache = make_cache(d, r_k=rk, r_v=rv, s=s, w=w, P=P)
+        cache.prefill(to_dev(d["K"], dt), to_dev(d["V"], dt))
+        o = to_f64(cache.decode(to_dev(d["q"], dt), n_split=ns))
+        torch.cuda.synchronize()
+        ref = oracle.decode(d["q64"], d["K64"], d["V64"], T, P, s, w, rk, rv, dt)
+        err = rel_err(o, ref["o_stored"])
+        print(f"[P=32 random {case}] cfg{cfg_id} T={T} B={B} kv={kv} r=({rk},{rv}) s={s} w={w} "
+              f"split={ns}: err {err:.3e}")
+        assert err <= TOL[dt], (case, cfg_id, T, rk, rv, s, w, ns, err)
