@@ -212,34 +212,34 @@ def factor_part_bytes(kind: int, r: int, dtype: int, P: int = PAGE_LEN, d: int =
     return n.value
 
 
-def pack_factors_int4(kind: int, r: int, Lq, Ls, Rq, Rs) -> np.ndarray:
-    """Host packing of INT4 codes (Lq (64, r), Rq (r, 128), values -7..7) and
-    scales (Ls (r,) for keys / (64,) for values, Rs (128,)) into one part
+def pack_factors_int4(kind: int, r: int, Lq, Ls, Rq, Rs, P: int = PAGE_LEN) -> np.ndarray:
+    """Host packing of INT4 codes (Lq (P, r), Rq (r, 128), values -7..7) and
+    scales (Ls (r,) for keys / (P,) for values, Rs (128,)) into one part
     (uint8)."""
     Lq = np.ascontiguousarray(Lq, dtype=np.int8)
     Rq = np.ascontiguousarray(Rq, dtype=np.int8)
     Ls = np.ascontiguousarray(Ls, dtype=np.float32)
     Rs = np.ascontiguousarray(Rs, dtype=np.float32)
-    if Lq.shape != (PAGE_LEN, r) or Rq.shape != (r, HEAD_DIM) or Rs.shape != (HEAD_DIM,) or \
-            Ls.shape != ((r,) if kind == KEYS else (PAGE_LEN,)):
+    if Lq.shape != (P, r) or Rq.shape != (r, HEAD_DIM) or Rs.shape != (HEAD_DIM,) or \
+            Ls.shape != ((r,) if kind == KEYS else (P,)):
         raise ValueError("code / scale shapes do not match the part")
-    out = np.zeros(factor_part_bytes(kind, r, BF16_INT4), dtype=np.uint8)
-    _check(lib().pkv_pack_factors_int4(kind, PAGE_LEN, HEAD_DIM, r, _np_ptr(Lq), _np_ptr(Ls),
+    out = np.zeros(factor_part_bytes(kind, r, BF16_INT4, P=P), dtype=np.uint8)
+    _check(lib().pkv_pack_factors_int4(kind, P, HEAD_DIM, r, _np_ptr(Lq), _np_ptr(Ls),
                                        _np_ptr(Rq), _np_ptr(Rs), _np_ptr(out)),
            "pkv_pack_factors_int4")
     return out
 
 
-def unpack_factors_int4(kind: int, r: int, packed):
+def unpack_factors_int4(kind: int, r: int, packed, P: int = PAGE_LEN):
     """Inverse of pack_factors_int4: (Lq, Ls, Rq, Rs)."""
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
-    if packed.size < factor_part_bytes(kind, r, BF16_INT4):
+    if packed.size < factor_part_bytes(kind, r, BF16_INT4, P=P):
         raise ValueError("packed part too small")
-    Lq = np.zeros((PAGE_LEN, r), dtype=np.int8)
+    Lq = np.zeros((P, r), dtype=np.int8)
     Rq = np.zeros((r, HEAD_DIM), dtype=np.int8)
-    Ls = np.zeros(r if kind == KEYS else PAGE_LEN, dtype=np.float32)
+    Ls = np.zeros(r if kind == KEYS else P, dtype=np.float32)
     Rs = np.zeros(HEAD_DIM, dtype=np.float32)
-    _check(lib().pkv_unpack_factors_int4(kind, PAGE_LEN, HEAD_DIM, r, _np_ptr(packed), _np_ptr(Lq),
+    _check(lib().pkv_unpack_factors_int4(kind, P, HEAD_DIM, r, _np_ptr(packed), _np_ptr(Lq),
                                          _np_ptr(Ls), _np_ptr(Rq), _np_ptr(Rs)),
            "pkv_unpack_factors_int4")
     return Lq, Ls, Rq, Rs

@@ -68,7 +68,9 @@ int32_t check_shape(const pkv_shape* s) {
     return PKV_ERR_INVALID_ARG;
   if (s->max_tokens < 1) return PKV_ERR_INVALID_ARG;
   if (s->head_dim != kD || (s->page_len != kP && s->page_len != kMinP)) return PKV_ERR_UNSUPPORTED;
-  if (s->page_len != kP && s->dtype == PKV_BF16_INT4) return PKV_ERR_UNSUPPORTED;
+  // INT4 at P = 32: equal padded ranks only (the kernels instantiated)
+  if (s->page_len != kP && s->dtype == PKV_BF16_INT4 && (s->rank_k + 7) / 8 != (s->rank_v + 7) / 8)
+    return PKV_ERR_UNSUPPORTED;
   if (s->n_q_heads / s->n_kv_heads > kMaxG) return PKV_ERR_UNSUPPORTED;
   if (s->dtype == PKV_BF16_INT4 && (s->rank_k > kQ4MaxRank || s->rank_v > kQ4MaxRank))
     return PKV_ERR_UNSUPPORTED;
@@ -89,8 +91,8 @@ void make_layout(const pkv_shape* s, pkv_layout* L) {
   L->factor_k_elems = part_elems(s->rank_k, (int)P);
   L->factor_v_elems = part_elems(s->rank_v, (int)P);
   if (s->dtype == PKV_BF16_INT4) {
-    L->factor_k_bytes = q4_dims(s->rank_k).k_bytes;
-    L->factor_v_bytes = q4_dims(s->rank_v).v_bytes;
+    L->factor_k_bytes = q4_dims(s->rank_k, (int)P).k_bytes;
+    L->factor_v_bytes = q4_dims(s->rank_v, (int)P).v_bytes;
   } else {
     L->factor_k_bytes = L->factor_k_elems * L->elem_bytes;
     L->factor_v_bytes = L->factor_v_elems * L->elem_bytes;
@@ -441,8 +443,8 @@ int32_t pkv_factor_part_bytes(int32_t kind, int32_t P, int32_t d, int32_t r, int
     return PKV_OK;
   }
   if (dtype != PKV_BF16_INT4) return PKV_ERR_INVALID_ARG;
-  if (P != kP || r > kQ4MaxRank || kind == PKV_KEYS_PRE_ROPE) return PKV_ERR_UNSUPPORTED;
-  const Q4Dims q = q4_dims(r);
+  if (r > kQ4MaxRank || kind == PKV_KEYS_PRE_ROPE) return PKV_ERR_UNSUPPORTED;
+  const Q4Dims q = q4_dims(r, P);
   *bytes = kind == PKV_KEYS ? q.k_bytes : q.v_bytes;
   return PKV_OK;
 }
@@ -450,9 +452,9 @@ int32_t pkv_factor_part_bytes(int32_t kind, int32_t P, int32_t d, int32_t r, int
 namespace {
 
 int32_t check_q4_part(int32_t kind, int32_t P, int32_t d, int32_t r) {
-  if (P != kP || d != kD) return PKV_ERR_UNSUPPORTED;
+  if ((P != kP && P != kMinP) || d != kD) return PKV_ERR_UNSUPPORTED;
   if (kind != PKV_KEYS && kind != PKV_VALUES) return PKV_ERR_INVALID_ARG;
-  if (r < 1 || r > kP) return PKV_ERR_INVALID_ARG;
+  if (r < 1 || r > P) return PKV_ERR_INVALID_ARG;
   if (r > kQ4MaxRank) return PKV_ERR_UNSUPPORTED;
   return PKV_OK;
 }
@@ -489,11 +491,11 @@ int32_t pkv_pack_factors_int4(int32_t kind, int32_t P, int32_t d, int32_t r, con
   const int32_t st = check_q4_part(kind, P, d, r);
   if (st != PKV_OK) return st;
   if (!Lq || !Ls || !Rq || !Rs || !packed) return PKV_ERR_INVALID_ARG;
-  for (int64_t n = 0; n < (int64_t)kP * r; ++n)
+  for (int64_t n = 0; n < (int64_t)P * r; ++n)
     if (Lq[n] < -7 || Lq[n] > 7) return PKV_ERR_INVALID_ARG;
   for (int64_t n = 0; n < (int64_t)r * kD; ++n)
     if (Rq[n] < -7 || Rq[n] > 7) return PKV_ERR_INVALID_ARG;
-  const Q4Dims q = q4_dims(r);
+  const Q4Dims q = q4_dims(r, P);
   const bool keys = kind == PKV_KEYS;
   uint8_t* part = (uint8_t*)packed;
   // every nibble starts as code 0 and every byte not holding a code or a
@@ -505,7 +507,7 @@ int32_t pkv_pack_factors_int4(int32_t kind, int32_t P, int32_t d, int32_t r, con
       const int code = i < r ? Rq[(int64_t)i * kD + c] : 0;
       put_nibble(part, keys ? q4_rt_k(q, i, c) : q4_rt_v(q, i, c), code);
     }
-    for (int j = 0; j < kP; ++j) {
+    for (int j = 0; j < P; ++j) {
       const int code = i < r ? Lq[(int64_t)j * r + i] : 0;
       put_nibble(part, keys ? q4_lt_k(q, j, i) : q4_lt_v(q, j, i), code);
     }
@@ -514,7 +516,7 @@ int32_t pkv_pack_factors_int4(int32_t kind, int32_t P, int32_t d, int32_t r, con
   if (keys) {
     for (int i = 0; i < r8; ++i) put_scale(part, q4_sl_k(q, i), i < r ? Ls[i] : 0.f);
   } else {
-    for (int j = 0; j < kP; ++j) put_scale(part, q4_sl_v(q, j), Ls[j]);
+    for (int j = 0; j < P; ++j) put_scale(part, q4_sl_v(q, j), Ls[j]);
   }
   return PKV_OK;
 }
@@ -524,20 +526,20 @@ int32_t pkv_unpack_factors_int4(int32_t kind, int32_t P, int32_t d, int32_t r, c
   const int32_t st = check_q4_part(kind, P, d, r);
   if (st != PKV_OK) return st;
   if (!Lq || !Ls || !Rq || !Rs || !packed) return PKV_ERR_INVALID_ARG;
-  const Q4Dims q = q4_dims(r);
+  const Q4Dims q = q4_dims(r, P);
   const bool keys = kind == PKV_KEYS;
   const uint8_t* part = (const uint8_t*)packed;
   for (int i = 0; i < r; ++i) {
     for (int c = 0; c < kD; ++c)
       Rq[(int64_t)i * kD + c] = (int8_t)get_nibble(part, keys ? q4_rt_k(q, i, c) : q4_rt_v(q, i, c));
-    for (int j = 0; j < kP; ++j)
+    for (int j = 0; j < P; ++j)
       Lq[(int64_t)j * r + i] = (int8_t)get_nibble(part, keys ? q4_lt_k(q, j, i) : q4_lt_v(q, j, i));
   }
   for (int c = 0; c < kD; ++c) Rs[c] = get_scale(part, keys ? q4_sr_k(q, c) : q4_sr_v(q, c));
   if (keys) {
     for (int i = 0; i < r; ++i) Ls[i] = get_scale(part, q4_sl_k(q, i));
   } else {
-    for (int j = 0; j < kP; ++j) Ls[j] = get_scale(part, q4_sl_v(q, j));
+    for (int j = 0; j < P; ++j) Ls[j] = get_scale(part, q4_sl_v(q, j));
   }
   return PKV_OK;
 }

@@ -326,10 +326,12 @@ __device__ __forceinline__ void q4_store_unit(uint8_t* p, uint32_t u, int ub) {
 
 __device__ __forceinline__ void q4_store_scale(uint8_t* p, float s) { *(uint16_t*)p = f32_to_bf16_bits(s); }
 
+// N page rows (32: K2 units and V1 rows of page rows 32..63 are not stored).
+template <int N>
 __device__ __forceinline__ void store_q4(const CompressJob& job, const PageRef& pr, TriShared& sh,
                                          const floatx4 (&R)[2][8], int lane) {
   const int r = pr.r;
-  const Q4Dims qd = q4_dims(r);
+  const Q4Dims qd = q4_dims(r, N);
   const int A = qd.pd.A, r8 = 8 * qd.pd.n8, ub = qd.ub;
   const bool keys = pr.kind == 0;
   uint8_t* part = factor_part(job, pr);
@@ -442,9 +444,11 @@ __device__ __forceinline__ void store_q4(const CompressJob& job, const PageRef& 
       const int i = A * b + 4 * mt + v;
       *(uint32_t*)(part + mt * 1024 + (row * 4 + ks) * 4) = q4_pack(&Rc[i * kD + 32 * ks + 8 * qk], 1, 8, 8);
     }
-    // K2: Lt_K page-row tiles, units of the lane quad's A ranks
-    for (int u = lane; u < 256; u += kP) {
-      const int ln = u / 4, mt = u % 4, qk = ln / 16, rho = ln % 16;
+    // K2: Lt_K page-row tiles, units of the lane quad's A ranks (N = 32:
+    // the lanes with rho < 8, compacted)
+    constexpr int kLanesK2 = N == kP ? 64 : 32;
+    for (int u = lane; u < 4 * kLanesK2; u += kP) {
+      const int ln = u / 4, mt = u % 4, qk = ln / (kLanesK2 / 4), rho = ln % (kLanesK2 / 4);
       const int j = 16 * (rho / 4) + 4 * mt + rho % 4;
       q4_store_unit(part + qd.k2 + (int64_t)u * ub, q4_pack(&Lc[j * kTriMaxRank + A * qk], 1, A, 2 * ub), ub);
     }
@@ -453,19 +457,21 @@ __device__ __forceinline__ void store_q4(const CompressJob& job, const PageRef& 
     // so that a part's bytes depend on the page alone
     for (int64_t b = qd.sl_k + 2 * r8 + lane; b < qd.k_bytes; b += kP) part[b] = 0x88;
   } else {
-    // V1: Lt_V^T rank tiles, dwords of 8 tokens
-    for (int u = lane; u < full * 128 + partial * 64; u += kP) {
+    // V1: Lt_V^T rank tiles, dwords of 8 tokens (N = 32: the rows of lanes
+    // 0..31, a compacted last tile's 16)
+    constexpr int kRows = N == kP ? 64 : 32;  // rows of a full tile
+    for (int u = lane; u < full * 2 * kRows + partial * kRows; u += kP) {
       int mt, row, ks, qk, b, v;
-      if (u < full * 128) {
-        mt = u / 128, row = (u % 128) / 2, ks = u % 2;
+      if (u < full * 2 * kRows) {
+        mt = u / (2 * kRows), row = (u % (2 * kRows)) / 2, ks = u % 2;
         qk = row / 16, b = (row % 16) / 4, v = row % 4;
       } else {
-        const int w = u - full * 128;
+        const int w = u - full * 2 * kRows;
         mt = full, row = w / 2, ks = w % 2;
         qk = row / 8, b = (row % 8) / 2, v = row % 2;
       }
       const int i = A * b + 4 * mt + v;
-      *(uint32_t*)(part + mt * 512 + (row * 2 + ks) * 4) =
+      *(uint32_t*)(part + mt * 8 * kRows + (row * 2 + ks) * 4) =
           q4_pack(&Lc[(16 * qk + 8 * ks) * kTriMaxRank + i], kTriMaxRank, 8, 8);
     }
     // V2: Rt_V^T channel tiles, units of the lane quad's A ranks
@@ -473,7 +479,7 @@ __device__ __forceinline__ void store_q4(const CompressJob& job, const PageRef& 
       const int ln = u / 8, mt = u % 8, qk = ln / 16, c = 16 * mt + ln % 16;
       q4_store_unit(part + qd.v2 + (int64_t)u * ub, q4_pack(&Rc[A * qk * kD + c], kD, A, 2 * ub), ub);
     }
-    q4_store_scale(part + q4_sl_v(qd, lane), lsv);
+    if (lane < N) q4_store_scale(part + q4_sl_v(qd, lane), lsv);
     for (int64_t b = qd.sr_v + 2 * kD + lane; b < qd.v_bytes; b += kP) part[b] = 0x88;
   }
 }
@@ -626,7 +632,7 @@ __device__ __forceinline__ void compress_tri_one(const J& jobs, int64_t n, TriSh
   __syncthreads();
 
   if constexpr (kQ4) {
-    store_q4(job, pr, sh, R, lane);
+    store_q4<N>(job, pr, sh, R, lane);
     __syncthreads();
     return;
   }
@@ -705,11 +711,13 @@ hipError_t launch_compress_batch(const CompressBatch& jb, hipStream_t stream) {
   dim3 grid;
   if (!page_grid(job.n_pages * jb.n, grid)) return hipErrorInvalidValue;
   const bool q4 = job.out_dtype == PKV_BF16_INT4;
-  if (q4 && (job.in_dtype != PKV_BF16 || job.page_rows != kP)) return hipErrorInvalidValue;
+  if (q4 && job.in_dtype != PKV_BF16) return hipErrorInvalidValue;
   if (job.page_rows != kP && job.page_rows != kMinP) return hipErrorInvalidValue;
   const bool full = job.page_rows == kP;
-  if (q4)
+  if (q4 && full)
     hipLaunchKernelGGL((compress_tri_batch_kernel<uint16_t, true, kP>), grid, dim3(64), 0, stream, jb);
+  else if (q4)
+    hipLaunchKernelGGL((compress_tri_batch_kernel<uint16_t, true, kMinP>), grid, dim3(64), 0, stream, jb);
   else if (job.in_dtype == PKV_BF16 && full)
     hipLaunchKernelGGL((compress_tri_batch_kernel<uint16_t, false, kP>), grid, dim3(64), 0, stream, jb);
   else if (job.in_dtype == PKV_BF16)
@@ -726,11 +734,14 @@ hipError_t launch_compress_tri(const CompressJob& job, hipStream_t stream, hipEv
   dim3 grid;
   if (!page_grid(job.n_pages, grid)) return hipErrorInvalidValue;
   const bool q4 = job.out_dtype == PKV_BF16_INT4;
-  if (q4 && (job.fac == nullptr || job.in_dtype != PKV_BF16 || job.page_rows != kP)) return hipErrorInvalidValue;
+  if (q4 && (job.fac == nullptr || job.in_dtype != PKV_BF16)) return hipErrorInvalidValue;
   if (job.page_rows != kP && job.page_rows != kMinP) return hipErrorInvalidValue;
   const bool full = job.page_rows == kP;
-  if (q4)
+  if (q4 && full)
     hipExtLaunchKernelGGL((compress_tri_kernel<uint16_t, true, kP>), grid, dim3(64), 0, stream, start, stop, 0, job);
+  else if (q4)
+    hipExtLaunchKernelGGL((compress_tri_kernel<uint16_t, true, kMinP>), grid, dim3(64), 0, stream, start, stop, 0,
+                          job);
   else if (job.in_dtype == PKV_BF16 && full)
     hipExtLaunchKernelGGL((compress_tri_kernel<uint16_t, false, kP>), grid, dim3(64), 0, stream, start, stop, 0, job);
   else if (job.in_dtype == PKV_BF16)

@@ -471,13 +471,16 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ inline void softmax_probs_lazy(SoftState& st, const floatx4 (&acc)[4], int q4, float (&p)[4][4]) {
+// (nvalid < 64: the scores of page rows from nvalid on are masked)
+__device__ inline void softmax_probs_lazy(SoftState& st, const floatx4 (&acc)[4], int q4, float (&p)[4][4],
+                                          int nvalid = kP) {
   float mx = -INFINITY;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       p[mt][v] = acc[mt][v] + ror8(acc[mt][v]);
+      if (nvalid < kP && 16 * q4 + 4 * mt + v >= nvalid) p[mt][v] = -INFINITY;
       mx = fmaxf(mx, p[mt][v]);
     }
   }
@@ -1095,12 +1098,15 @@ __device__ __forceinline__ void ldw(uint32_t* d, const uint8_t* p) {
 // LDS budget of a four-wave workgroup at two workgroups per CU (160 KB).
 constexpr int kWgLdsBytes = 80 * 1024;
 
-template <int N8K, int N8V>
+// PR page rows (32: K2 and V1 without the lanes of page rows 32..63; those
+// lanes read codes of a valid address, which meet masked scores and zero
+// probabilities)
+template <int N8K, int N8V, int PR = kP>
 struct Int4Factors {
   static constexpr int AK = 2 * N8K, AV = 2 * N8V;  // ranks per lane quad
   static constexpr int RTK = (AK + 3) / 4, RTV = (AV + 3) / 4;
   static constexpr bool kPartK = AK % 4 != 0, kPartV = AV % 4 != 0;
-  static constexpr Q4Dims kQK = q4_dims(8 * N8K), kQV = q4_dims(8 * N8V);
+  static constexpr Q4Dims kQK = q4_dims(8 * N8K, PR), kQV = q4_dims(8 * N8V, PR);
   static constexpr int UK = kQK.ub, UV = kQV.ub;  // K2 / V2 unit bytes
   // byte offsets within the parts
   static constexpr int kK2 = kQK.k2, kSRK = kQK.sr_k, kSLK = kQK.sl_k;
@@ -1109,7 +1115,7 @@ struct Int4Factors {
   static constexpr int kWavesPerSimd = 2;
   static constexpr bool kKeyDoubleBuffer = false;
   static constexpr bool kRope = false;
-  static constexpr int kPageRows = kP;
+  static constexpr int kPageRows = PR;
   // Factor pages stream through a per-wave ring of kRingSlots page slots in
   // LDS, filled by direct global -> LDS loads kRingSlots - 1 pages ahead of
   // the page being computed (registers cannot hold that much prefetch).
@@ -1184,7 +1190,9 @@ struct Int4Factors {
       const bool part = kPartK && mt == RTK - 1;
       ldw<4>(R.k1[mt], kp + mt * 1024 + (part ? tl.lam : lane) * 16);
     }
-    ldw<UK>(R.k2, kp + kK2 + lane * 4 * UK);
+    // (PR = 32: compacted lanes rho < 8; the others read lane 0's units)
+    const int lk = PR == kP ? lane : ((lane & 15) < 8 ? 8 * (lane >> 4) + (lane & 15) : 0);
+    ldw<UK>(R.k2, kp + kK2 + lk * 4 * UK);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) ldw<4>(&R.sr[4 * ks], kp + kSRK + 2 * (32 * ks + 8 * q4));
     ldw<N8K>(R.sl, kp + kSLK + 2 * AK * q4);
@@ -1196,7 +1204,11 @@ struct Int4Factors {
 #pragma unroll
     for (int mt = 0; mt < RTV; ++mt) {
       const bool part = kPartV && mt == RTV - 1;
-      ldw<2>(R.v1[mt], vp + mt * 512 + (part ? tl.lam : lane) * 8);
+      if constexpr (PR == kP) {
+        ldw<2>(R.v1[mt], vp + mt * 512 + (part ? tl.lam : lane) * 8);
+      } else {  // rows of lanes 0..31 (compacted last tile: 16); lanes 32.. read filler
+        ldw<2>(R.v1[mt], vp + mt * 256 + (part ? (lane < 32 ? tl.lam : 0) : (lane & 31)) * 8);
+      }
     }
     if constexpr (UV == 4) {
       ldw<4>(R.v2, vp + kV2 + lane * 32);
@@ -1250,7 +1262,7 @@ struct Int4Factors {
     floatx4 as_[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) as_[mt] = mfma(q4_operand<2 * UK, N8K>(q4_unit<UK>(R.k2, mt)), tb, base2);
-    softmax_probs_lazy(st, as_, q4, p);
+    softmax_probs_lazy(st, as_, q4, p, PR);
   }
 
   // Eq. 4, value half on the codes: u = Lt_V^T p, o += Rt_V^T u.
@@ -2007,7 +2019,7 @@ AppendDst append_dst_of(const CacheGeom& g, const AttnJob& job) {
 bool batched_kernel(const CacheGeom& g) {
   const int n8k = (g.r_k + 7) / 8, n8v = (g.r_v + 7) / 8;
   if (n8k != n8v) return false;
-  if (g.P != kP) return g.dtype == PKV_BF16;  // Bf16Half, RopeFactors<N8, 32> (r <= P = 32)
+  if (g.P != kP) return g.dtype == PKV_BF16 || g.dtype == PKV_BF16_INT4;  // the 32-row formats (r <= 32)
   if (g.dtype == PKV_BF16_INT4) return n8k <= 4;
   return g.dtype == PKV_BF16 && n8k <= 8 && (!g.rope || n8k <= kRopeMfmaMaxN8);
 }
@@ -2105,7 +2117,23 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
   constexpr bool kBatch = std::is_same<KA, DecodeBatchArgs>::value;
   const KernelEvents ev = take_kernel_events();
   const int n8k = (g.r_k + 7) / 8, n8v = (g.r_v + 7) / 8;
-  if (g.dtype == PKV_BF16_INT4) {
+  if (g.dtype == PKV_BF16_INT4 && g.P == kMinP) {  // equal padded ranks only
+    if (n8k != n8v) return hipErrorNotSupported;
+    switch (n8k) {
+#define PKV_Q4H(N)                                                                                      \
+  case N:                                                                                               \
+    hipExtLaunchKernelGGL((decode_mfma_kernel<Int4Factors<N, N, kMinP>, KA>), grid, dim3(256), 0, stream, \
+                          ev.start, ev.stop, 0, ka);                                                    \
+    break;
+      PKV_Q4H(1)
+      PKV_Q4H(2)
+      PKV_Q4H(3)
+      PKV_Q4H(4)
+#undef PKV_Q4H
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else if (g.dtype == PKV_BF16_INT4) {
     if (kBatch && n8k != n8v) return hipErrorNotSupported;
     switch (n8k * 8 + n8v) {
 #define PKV_Q4(NK, NV)                                                                              \

@@ -189,18 +189,23 @@ struct Q4Dims {
   int64_t v2, sl_v, sr_v, v_bytes;
 };
 
-__host__ __device__ constexpr Q4Dims q4_dims(int r) {
+// 32-token pages (P = 32) drop the lanes of page rows 32..63 from K2 and
+// V1 as in the bf16 layout: K2 keeps the units of lanes l % 16 < 8 at
+// lam = 8 (l / 16) + l % 16, V1 the rows of lanes 0..31 (a compacted last
+// tile: rows qk * 8 + 2 b + v with qk < 2); sL_V holds P scales.
+__host__ __device__ constexpr Q4Dims q4_dims(int r, int P = kP) {
   Q4Dims q{};
-  q.pd = pack_dims(r);
+  q.pd = pack_dims(r, P);
   const int A = q.pd.A, full = A / 4, part = (A % 4) ? 1 : 0;
+  const int64_t h = P == kP ? 1 : 2;  // lanes kept of K2 and V1: 1 / h
   q.ub = q4_unit_bytes(A);
   q.k2 = (int64_t)full * 1024 + part * 512;
-  q.sr_k = q.k2 + 256LL * q.ub;
+  q.sr_k = q.k2 + 256LL / h * q.ub;
   q.sl_k = q.sr_k + 2LL * kD;
   q.k_bytes = (q.sl_k + 2LL * 4 * A + 63) / 64 * 64;
-  q.v2 = (int64_t)full * 512 + part * 256;
+  q.v2 = ((int64_t)full * 512 + part * 256) / h;
   q.sl_v = q.v2 + 512LL * q.ub;
-  q.sr_v = q.sl_v + 2LL * kP;
+  q.sr_v = q.sl_v + 2LL * P;
   q.v_bytes = (q.sr_v + 2LL * kD + 63) / 64 * 64;
   return q;
 }
@@ -230,7 +235,8 @@ __host__ __device__ inline Q4Slot q4_rt_k(const Q4Dims& q, int i, int c) {
 
 // K2: Lt_K[j][i]
 __host__ __device__ inline Q4Slot q4_lt_k(const Q4Dims& q, int j, int i) {
-  const int mt = (j % 16) / 4, lane = 16 * (i / q.pd.A) + 4 * (j / 16) + j % 4;
+  const int mt = (j % 16) / 4, rho = 4 * (j / 16) + j % 4;
+  const int lane = q.pd.P == kP ? 16 * (i / q.pd.A) + rho : 8 * (i / q.pd.A) + rho;  // P = 32: rho < 8
   return Q4Slot{q.k2 + ((int64_t)lane * 4 + mt) * q.ub, 2 * q.ub, q4_nibble_bit(2 * q.ub, i % q.pd.A)};
 }
 
@@ -238,7 +244,8 @@ __host__ __device__ inline Q4Slot q4_lt_k(const Q4Dims& q, int j, int i) {
 __host__ __device__ inline Q4Slot q4_lt_v(const Q4Dims& q, int j, int i) {
   const RankSlot s = rank_slot(q.pd, i);
   const int qk = j / 16, ks = (j % 16) / 8, e = j % 8;
-  return Q4Slot{(int64_t)s.mt * 512 + (q4_tile_row(s, qk) * 2 + ks) * 4, 8, q4_nibble_bit(8, e)};
+  const int64_t tile = q.pd.P == kP ? 512 : 256;  // P = 32: rows of lanes 0..31
+  return Q4Slot{(int64_t)s.mt * tile + (q4_tile_row(s, qk) * 2 + ks) * 4, 8, q4_nibble_bit(8, e)};
 }
 
 // V2: Rt_V[i][c] (as Rt_V^T)

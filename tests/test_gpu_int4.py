@@ -34,26 +34,27 @@ pytestmark = pytest.mark.gpu
 KIND = {pkv.KEYS: "K", pkv.VALUES: "V"}
 
 
-def _prefilled(cfg_id, T, B, kv_heads, r_k=None, r_v=None, s=None, w=None, max_tokens=None):
+def _prefilled(cfg_id, T, B, kv_heads, r_k=None, r_v=None, s=None, w=None, max_tokens=None, P=64):
     d = synth.decode_inputs(cfg_id, T=T, B=B, kv_heads=kv_heads, with_f64=True)
-    cache = make_cache(d, r_k=r_k, r_v=r_v, s=s, w=w, max_tokens=max_tokens, store="int4")
+    cache = make_cache(d, r_k=r_k, r_v=r_v, s=s, w=w, max_tokens=max_tokens, store="int4", P=P)
     cache.prefill(to_dev(d["K"], "bf16"), to_dev(d["V"], "bf16"))
     return d, cache
 
 
 def _fact_pages(d, cache, b, h, kind):
-    """float64 pages (n_fact, 64, 128) of the factorized region of (b, h)."""
+    """float64 pages (n_fact, P, 128) of the factorized region of (b, h)."""
     T, nf, _ = cache.state()
-    n_s = cache.shape.sink // 64
+    P = cache.shape.page_len
+    n_s = cache.shape.sink // P
     src = d["K64"] if kind == pkv.KEYS else d["V64"]
-    return src[b, h, 64 * n_s: 64 * (n_s + nf)].reshape(nf, 64, 128)
+    return src[b, h, P * n_s: P * (n_s + nf)].reshape(nf, P, 128)
 
 
 def _gpu_codes(cache, b, h, slot, kind, r):
     import torch
     part = cache.factor_part(b, h, slot, kind).cpu().numpy()
     torch.cuda.synchronize()
-    return pkv.unpack_factors_int4(kind, r, part)
+    return pkv.unpack_factors_int4(kind, r, part, P=cache.shape.page_len)
 
 
 def _compare_codes(gq, gs, oq, os_, x, label):
@@ -67,12 +68,14 @@ def _compare_codes(gq, gs, oq, os_, x, label):
     return int((gq == oq).sum())
 
 
-@pytest.mark.parametrize("cfg_id,r", [(3, 24), (3, 16), (3, 8), (3, 32), (3, 20)])
-def test_int4_decomposition_codes_match_oracle(cfg_id, r):
+@pytest.mark.parametrize("cfg_id,r,P", [(3, 24, 64), (3, 16, 64), (3, 8, 64), (3, 32, 64), (3, 20, 64),
+                                        (3, 16, 32), (3, 24, 32)])
+def test_int4_decomposition_codes_match_oracle(cfg_id, r, P):
     """Prefill factorizes every FACT page straight into INT4 parts (cfg-3
-    key/value recipe: sigma_i = i^-1.2, distinct singular values)."""
+    key/value recipe: sigma_i = i^-1.2, distinct singular values); also for
+    32-token pages."""
     require_gpu()
-    d, cache = _prefilled(cfg_id, 64 * 24, B=1, kv_heads=2, r_k=r, r_v=r)
+    d, cache = _prefilled(cfg_id, 64 * 24, B=1, kv_heads=2, r_k=r, r_v=r, P=P)
     equal = total = 0
     for b in range(d["B"]):
         for h in range(d["Hkv"]):
@@ -92,22 +95,22 @@ def test_int4_decomposition_codes_match_oracle(cfg_id, r):
                     equal += _compare_codes(gl, gls, lq[f], ls[f], Lt[f], lab + " Lt")
                     equal += _compare_codes(gr, grs[None, :], rq[f], rs[f], Rt[f], lab + " Rt")
                     total += gl.size + gr.size
-    print(f"[int4 codes r={r}] {equal}/{total} codes equal to the oracle's, all within the bound")
+    print(f"[int4 codes r={r} P={P}] {equal}/{total} codes equal to the oracle's, all within the bound")
     assert equal >= 0.99 * total
 
 
-@pytest.mark.parametrize("r", [24, 8, 20, 32])
-def test_int4_parts_are_canonical(r):
+@pytest.mark.parametrize("r,P", [(24, 64), (8, 64), (20, 64), (32, 64), (16, 32), (20, 32), (24, 32)])
+def test_int4_parts_are_canonical(r, P):
     """Every byte of a GPU-written part, padding included, is what the host
     packer writes for the part's own codes and scales: pack(unpack(part))
     reproduces it exactly, so a part depends on the page alone."""
     require_gpu()
-    d, cache = _prefilled(3, 64 * 8, B=1, kv_heads=2, r_k=r, r_v=r)
+    d, cache = _prefilled(3, 64 * 8, B=1, kv_heads=2, r_k=r, r_v=r, P=P)
     for h in range(2):
         for f in range(cache.state()[1]):
             for kind in (pkv.KEYS, pkv.VALUES):
                 part = cache.factor_part(0, h, f, kind).cpu().numpy()
-                again = pkv.pack_factors_int4(kind, r, *pkv.unpack_factors_int4(kind, r, part))
+                again = pkv.pack_factors_int4(kind, r, *pkv.unpack_factors_int4(kind, r, part, P=P), P=P)
                 np.testing.assert_array_equal(part, again, err_msg=f"h{h} page {f} kind {kind}")
 
 
@@ -122,52 +125,55 @@ def _oracle_parts(d, cache, r_k, r_v):
                 _, _, lq, ls, rq, rs = oracle.int4_codes(U, S, Wt, r, KIND[kind])
                 for f in range(X.shape[0]):
                     lsf = ls[f, 0] if kind == pkv.KEYS else ls[f, :, 0]
-                    part = pkv.pack_factors_int4(kind, r, lq[f], lsf, rq[f], rs[f, 0])
+                    part = pkv.pack_factors_int4(kind, r, lq[f], lsf, rq[f], rs[f, 0], P=cache.shape.page_len)
                     cache.factor_part(b, h, f, kind).copy_(torch.from_numpy(part))
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("cfg_id,T,B,kv,rk,rv,splits", [
-    (3, 64 * 48 + 5, 1, 2, 24, 24, (0, 3)),
-    (2, 64 * 40 + 37, 2, 2, 16, 16, (0, 1, 64)),
-    (2, 64 * 20 + 1, 1, 2, 16, 14, (0,)),
-    (2, 64 * 20 + 1, 1, 2, 24, 16, (0,)),
-    (2, 64 * 20 + 63, 1, 2, 8, 8, (0,)),
-    (2, 64 * 20, 1, 2, 32, 32, (0,)),
-    (2, 64 * 20 + 9, 1, 2, 20, 12, (0,)),
+@pytest.mark.parametrize("cfg_id,T,B,kv,rk,rv,splits,P", [
+    (3, 64 * 48 + 5, 1, 2, 24, 24, (0, 3), 64),
+    (2, 64 * 40 + 37, 2, 2, 16, 16, (0, 1, 64), 64),
+    (2, 64 * 20 + 1, 1, 2, 16, 14, (0,), 64),
+    (2, 64 * 20 + 1, 1, 2, 24, 16, (0,), 64),
+    (2, 64 * 20 + 63, 1, 2, 8, 8, (0,), 64),
+    (2, 64 * 20, 1, 2, 32, 32, (0,), 64),
+    (2, 64 * 20 + 9, 1, 2, 20, 12, (0,), 64),
+    (3, 32 * 60 + 5, 1, 2, 24, 24, (0, 3), 32),   # 32-token pages
+    (2, 32 * 40 + 9, 2, 2, 16, 14, (0, 2), 32),
 ])
-def test_int4_attention_on_oracle_codes(cfg_id, T, B, kv, rk, rv, splits):
+def test_int4_attention_on_oracle_codes(cfg_id, T, B, kv, rk, rv, splits, P):
     require_gpu()
-    d, cache = _prefilled(cfg_id, T, B, kv, r_k=rk, r_v=rv)
+    d, cache = _prefilled(cfg_id, T, B, kv, r_k=rk, r_v=rv, P=P)
     _oracle_parts(d, cache, rk, rv)
     cfg = d["cfg"]
-    ref = oracle.decode(d["q64"], d["K64"], d["V64"], T, 64, cfg["s"], cfg["w"], rk, rv, "int4")
+    ref = oracle.decode(d["q64"], d["K64"], d["V64"], T, P, cfg["s"], cfg["w"], rk, rv, "int4")
     q = to_dev(d["q"], "bf16")
     for ns in splits:
         o = to_f64(cache.decode(q, n_split=ns))
         err = rel_err(o, ref["o_stored"])
-        print(f"[int4 oracle codes cfg{cfg_id} T={T} r=({rk},{rv}) split={ns}] err={err:.3e} "
+        print(f"[int4 oracle codes cfg{cfg_id} T={T} P={P} r=({rk},{rv}) split={ns}] err={err:.3e} "
               f"(vs unquantized: {rel_err(o, ref['o_exact']):.3e})")
         assert err <= 1e-3, (ns, err)
 
 
-@pytest.mark.parametrize("cfg_id,T,B,kv,rk,rv", [
-    (3, 64 * 48 + 5, 1, 2, 24, 24),
-    (2, 64 * 40 + 37, 2, 2, 16, 16),
-    (2, 64 * 30 + 17, 1, 2, 16, 14),
+@pytest.mark.parametrize("cfg_id,T,B,kv,rk,rv,P", [
+    (3, 64 * 48 + 5, 1, 2, 24, 24, 64),
+    (2, 64 * 40 + 37, 2, 2, 16, 16, 64),
+    (2, 64 * 30 + 17, 1, 2, 16, 14, 64),
+    (2, 32 * 60 + 17, 1, 2, 16, 14, 32),  # the pages' operating point (sink 64, window 128)
 ])
-def test_int4_decode_end_to_end(cfg_id, T, B, kv, rk, rv):
+def test_int4_decode_end_to_end(cfg_id, T, B, kv, rk, rv, P):
     require_gpu()
-    d, cache = _prefilled(cfg_id, T, B, kv, r_k=rk, r_v=rv)
+    d, cache = _prefilled(cfg_id, T, B, kv, r_k=rk, r_v=rv, P=P)
     cfg = d["cfg"]
-    ref = oracle.decode(d["q64"], d["K64"], d["V64"], T, 64, cfg["s"], cfg["w"], rk, rv, "int4")
+    ref = oracle.decode(d["q64"], d["K64"], d["V64"], T, P, cfg["s"], cfg["w"], rk, rv, "int4")
     o = to_f64(cache.decode(to_dev(d["q"], "bf16")))
     err = rel_err(o, ref["o_stored"])
-    print(f"[int4 end to end cfg{cfg_id} T={T} r=({rk},{rv})] err={err:.3e} "
+    print(f"[int4 end to end cfg{cfg_id} T={T} P={P} r=({rk},{rv})] err={err:.3e} "
           f"(vs unquantized: {rel_err(o, ref['o_exact']):.3e})")
     assert err <= TOL["int4"]
-    cls, slot = cache.page_table(-(-T // 64))
-    ocls, oslot = oracle.classify(T, 64, cfg["s"], cfg["w"])
+    cls, slot = cache.page_table(-(-T // P))
+    ocls, oslot = oracle.classify(T, P, cfg["s"], cfg["w"])
     np.testing.assert_array_equal(cls, ocls)
     np.testing.assert_array_equal(slot, oslot)
 
@@ -209,7 +215,8 @@ def test_int4_step_matches_separate_calls():
     assert promos == 2
 
 
-def test_int4_step_against_oracle():
+@pytest.mark.parametrize("P", [64, 32])
+def test_int4_step_against_oracle(P):
     """Incremental decode on INT4 pages against the oracle at every step.
     The cfg-3 recipe (distinct singular values) makes the codes of each
     promoted page unique up to rounding ties; on the cfg-2/4 recipe (rank 8
@@ -221,10 +228,10 @@ def test_int4_step_against_oracle():
     cfg_id, T0, steps = 3, 64 * 10 + 3, 140
     d = synth.decode_inputs(cfg_id, T=T0 + steps, B=1, kv_heads=2, with_f64=True)
     cfg = d["cfg"]
-    cache = make_cache(d, max_tokens=T0 + steps, store="int4")
+    cache = make_cache(d, max_tokens=T0 + steps, store="int4", P=P)
     Kd, Vd = to_dev(d["K"], "bf16"), to_dev(d["V"], "bf16")
     cache.prefill(Kd[:, :, :T0].contiguous(), Vd[:, :, :T0].contiguous())
-    inc = oracle.IncrementalDecoder(d["K64"], d["V64"], 64, cfg["s"], cfg["w"], cfg["r_k"], cfg["r_v"],
+    inc = oracle.IncrementalDecoder(d["K64"], d["V64"], P, cfg["s"], cfg["w"], cfg["r_k"], cfg["r_v"],
                                     "int4")
     worst, promos = 0.0, 0
     for t in range(steps):
@@ -238,8 +245,8 @@ def test_int4_step_against_oracle():
         err = rel_err(o, ref)
         worst = max(worst, err)
         assert err <= TOL["int4"], (t, err)
-    print(f"[int4 step vs oracle] {steps} steps, {promos} promotions, worst err {worst:.3e}")
-    assert promos == 2
+    print(f"[int4 step vs oracle P={P}] {steps} steps, {promos} promotions, worst err {worst:.3e}")
+    assert promos == (T0 + steps) // P - T0 // P
 
 
 def test_int4_decomposition_valid_on_degenerate_spectra():

@@ -183,17 +183,24 @@ def test_p32_chunks_match_token_by_token():
     _chunk_vs_tokens(2, 32 * 5 + 17, [40, 7, 32, 300, ("step", 45), 1, 513], P=P, r_k=RK, r_v=RV, s=S, w=W)
 
 
+def test_p32_chunks_int4_pages():
+    # INT4 factor pages (Sec. 4.3) of 32 tokens at (16, 14)
+    _chunk_vs_tokens(3, 32 * 3 + 9, [100, 33, ("step", 40), 600, ("tok", 33), 5], store="int4", P=P, r_k=RK,
+                     r_v=RV, s=S, w=W)
+
+
 def test_p32_chunks_on_aux_stream():
     _chunk_vs_tokens(2, 32 * 3 + 5, [40, 600, ("tok", 70), 1, 333], B=2, aux=True, P=P, r_k=RK, r_v=RV,
                      s=S, w=W)
 
 
-@pytest.mark.parametrize("lengths,rope", [
-    ([32 * 20 + 5, 7, 32 * 3, 32 * 9 + 31], False),   # pages complete at different steps
-    ([32 * 20 + 9, 32 * 5 + 9, 32 * 11 + 9], False),  # ... at the same steps: one promotion launch
-    ([32 * 20 + 5, 7, 32 * 3, 32 * 9 + 31], True),    # pre-RoPE keys
+@pytest.mark.parametrize("lengths,rope,store", [
+    ([32 * 20 + 5, 7, 32 * 3, 32 * 9 + 31], False, None),    # pages complete at different steps
+    ([32 * 20 + 9, 32 * 5 + 9, 32 * 11 + 9], False, None),   # ... at the same steps: one promotion launch
+    ([32 * 20 + 5, 7, 32 * 3, 32 * 9 + 31], True, None),     # pre-RoPE keys
+    ([32 * 20 + 9, 32 * 5 + 9, 32 * 11 + 9], False, "int4"),  # INT4 factor pages
 ])
-def test_p32_batches_equal_single_caches(lengths, rope):
+def test_p32_batches_equal_single_caches(lengths, rope, store):
     """Batched attention and batched steps over 32-token caches of different
     lengths equal the per-cache calls bit for bit."""
     import torch
@@ -205,7 +212,7 @@ def test_p32_batches_equal_single_caches(lengths, rope):
         Kd = to_dev(np.ascontiguousarray(d["K"][:, :, 32 * i:]), "bf16")
         Vd = to_dev(np.ascontiguousarray(d["V"][:, :, 32 * i:]), "bf16")
         for group in (A, Bs):
-            c = make_cache(d, r_k=RK, r_v=RV, s=S, w=W, P=P, max_tokens=T + steps)
+            c = make_cache(d, r_k=RK, r_v=RV, s=S, w=W, P=P, max_tokens=T + steps, store=store)
             if rope:
                 c.set_key_rope(synth.rope_inv_freq(5e5))
             c.prefill(Kd[:, :, :T].contiguous(), Vd[:, :, :T].contiguous())
@@ -233,8 +240,8 @@ def test_p32_batches_equal_single_caches(lengths, rope):
 def test_p32_errors():
     require_gpu()
     d = synth.decode_inputs(2, T=200, B=1, kv_heads=1)
-    with pytest.raises(pkv.PKVError) as ei:  # INT4 factor pages need 64-token pages
-        make_cache(d, r_k=RK, r_v=RV, s=S, w=W, P=P, store="int4")
+    with pytest.raises(pkv.PKVError) as ei:  # INT4 at 32 tokens: equal padded ranks only
+        make_cache(d, r_k=8, r_v=RV, s=S, w=W, P=P, store="int4")
     assert ei.value.status == 2
     with pytest.raises(pkv.PKVError) as ei:  # rank above the page length
         make_cache(d, r_k=33, r_v=RV, s=S, w=W, P=P)

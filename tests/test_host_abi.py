@@ -135,7 +135,7 @@ def test_layout_sizes():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(head_dim=64), 2), (dict(page_len=16), 2), (dict(page_len=32, dtype=pkv.BF16_INT4), 2),
+    (dict(head_dim=64), 2), (dict(page_len=16), 2), (dict(page_len=32, dtype=pkv.BF16_INT4, rank_v=8), 2),
     (dict(page_len=128, sink=128, window=128), 2), (dict(page_len=32, rank_k=33), 1), (dict(n_q_heads=32, n_kv_heads=2), 2),
     (dict(sink=32), 1), (dict(window=100), 1), (dict(rank_k=0), 1), (dict(rank_v=65), 1),
     (dict(n_q_heads=7), 1), (dict(max_tokens=0), 1), (dict(dtype=5), 1),
@@ -181,7 +181,8 @@ def test_packed_layout_of_32_token_pages_is_a_bijection(r):
         assert pkv.factor_part_bytes(kind, r, pkv.BF16, P=P) == 2 * n
     L = pkv.lib()
     nb = ctypes.c_int64()
-    assert L.pkv_factor_part_bytes(pkv.KEYS, P, 128, r, pkv.BF16_INT4, ctypes.byref(nb)) == 2
+    assert L.pkv_factor_part_bytes(pkv.KEYS, P, 128, r, pkv.BF16_INT4, ctypes.byref(nb)) == 0
+    assert nb.value == pkv.factor_part_bytes(pkv.KEYS, r, pkv.BF16_INT4, P=P)  # INT4 parts at P = 32
     assert L.pkv_factor_part_elems(P, 128, P + 1, ctypes.byref(nb)) == 1
     assert L.pkv_factor_part_elems(16, 128, 8, ctypes.byref(nb)) == 2
 

@@ -29,22 +29,25 @@ def _bf16_values(g, shape):
     return oracle.round_to(np.exp(g.normal(-3.0, 1.0, shape)), "bf16").astype(np.float32)
 
 
-def _random_part(g, kind, r):
-    Lq = g.integers(-7, 8, (64, r)).astype(np.int8)
+def _random_part(g, kind, r, P=64):
+    Lq = g.integers(-7, 8, (P, r)).astype(np.int8)
     Rq = g.integers(-7, 8, (r, 128)).astype(np.int8)
-    Ls = _bf16_values(g, r if kind == pkv.KEYS else 64)
+    Ls = _bf16_values(g, r if kind == pkv.KEYS else P)
     Rs = _bf16_values(g, 128)
     return Lq, Ls, Rq, Rs
 
 
+@pytest.mark.parametrize("P", [64, 32])
 @pytest.mark.parametrize("r", RANKS)
 @pytest.mark.parametrize("kind", [pkv.KEYS, pkv.VALUES])
-def test_int4_pack_unpack_round_trip(kind, r):
-    g = np.random.default_rng(100 * r + kind)
-    Lq, Ls, Rq, Rs = _random_part(g, kind, r)
-    packed = pkv.pack_factors_int4(kind, r, Lq, Ls, Rq, Rs)
-    assert packed.size == pkv.factor_part_bytes(kind, r, pkv.BF16_INT4)
-    L2, Ls2, R2, Rs2 = pkv.unpack_factors_int4(kind, r, packed)
+def test_int4_pack_unpack_round_trip(kind, r, P):
+    g = np.random.default_rng(100 * r + kind + P)
+    Lq, Ls, Rq, Rs = _random_part(g, kind, r, P)
+    packed = pkv.pack_factors_int4(kind, r, Lq, Ls, Rq, Rs, P=P)
+    assert packed.size == pkv.factor_part_bytes(kind, r, pkv.BF16_INT4, P=P)
+    # every code nibble of the part is used once: a part of codes 0 (nibble
+    # 8) and zero scales differs from this one at each code position
+    L2, Ls2, R2, Rs2 = pkv.unpack_factors_int4(kind, r, packed, P=P)
     np.testing.assert_array_equal(L2, Lq)
     np.testing.assert_array_equal(R2, Rq)
     np.testing.assert_array_equal(Ls2, Ls)
@@ -165,6 +168,38 @@ def test_int4_part_sizes_against_the_pages_count():
     assert pkv.factor_part_bytes(pkv.KEYS, 24, pkv.BF16_INT4) + \
         pkv.factor_part_bytes(pkv.VALUES, 24, pkv.BF16_INT4) == 6080
     assert 2 * pkv.factor_part_bytes(pkv.KEYS, 24, pkv.BF16) == 18432
+
+
+def test_int4_part_sizes_of_32_token_pages():
+    """P = 32 parts hold the (32 + d) r / 2 code bytes of the pages' count
+    for r = 16, 32 (no compacted tile) plus the 16-bit scales, rounded up to
+    64 bytes."""
+    for r in (16, 32):
+        codes = (32 + 128) * r // 2
+        k = pkv.factor_part_bytes(pkv.KEYS, r, pkv.BF16_INT4, P=32)
+        v = pkv.factor_part_bytes(pkv.VALUES, r, pkv.BF16_INT4, P=32)
+        assert k == -(-(codes + 2 * (128 + r)) // 64) * 64
+        assert v == -(-(codes + 2 * (32 + 128)) // 64) * 64
+
+
+def test_int4_cache_at_the_pages_operating_point():
+    """P = 32, (r_K, r_V) = (16, 14), one sink page and one window page: the
+    whole cache comes within the part padding (r_V padded to 16, parts to 64
+    bytes) of the pages' INT4 accounting, 0.187 at long contexts (oracle,
+    pinned against the printed figure)."""
+    T, rk, rv = 16384, 16, 14
+    lay = pkv.cache_layout(pkv.make_shape(batch=1, n_q_heads=8, n_kv_heads=1, rank_k=rk, rank_v=rv, sink=32,
+                                          window=32, max_tokens=T, dtype=pkv.BF16_INT4, page_len=32))
+    assert lay["factor_k_bytes"] == pkv.factor_part_bytes(pkv.KEYS, rk, pkv.BF16_INT4, P=32)
+    assert lay["factor_v_bytes"] == pkv.factor_part_bytes(pkv.VALUES, rv, pkv.BF16_INT4, P=32)
+    n_pages = T // 32
+    dense = 2 * 32 * 128 * 2
+    ours = (lay["max_fact_pages"] * lay["factor_page_bytes"] + 2 * dense) / (n_pages * dense)
+    ref = oracle.int4_storage_ratio(T, 32, 128, rk, rv, 2)
+    assert ref <= ours <= ref * 1.12, (ours, ref)
+    with pytest.raises(pkv.PKVError) as ei:  # unequal padded ranks: not at P = 32
+        pkv.cache_layout(pkv.make_shape(1, 8, 1, 8, 16, 32, 32, T, pkv.BF16_INT4, page_len=32))
+    assert ei.value.status == 2
 
 
 def test_int4_cache_layout_and_storage_ratio():
