@@ -39,16 +39,16 @@ CACHE_DIR = os.environ.get("PKV_BENCH_CACHE", "/tmp/pkv_bench_inputs")
 # HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc runs of
 # this script (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled
 # by what the same counter reads for the 1 GiB device copy of `--workload copy`
-# (FETCH_SIZE reads 524301.6 KiB for 2^30 bytes read -> x1.99995; WRITE_SIZE
+# (FETCH_SIZE reads 524301.7 KiB for 2^30 bytes read -> x1.99995; WRITE_SIZE
 # reads 1048576 KiB for 2^30 bytes written -> x1.0).  A figure holds only for
 # the kernel sources whose hash it carries; any change to them makes it null.
 PMC_TRAFFIC = {
-    "qwen3-32b-layer-128k": {"sha256": "ad40a9095c58a2f36d4a5451d751a8530dc589b8d07e5aa33671137d4e19cdef",
-                             "fetch": 303084276, "write": 1114112},
-    "qwen3-32b-layer-128k-int4": {"sha256": "ad40a9095c58a2f36d4a5451d751a8530dc589b8d07e5aa33671137d4e19cdef",
-                                  "fetch": 101415151, "write": 2228244},
-    "llama3.1-8b-layer-p32": {"sha256": "ad40a9095c58a2f36d4a5451d751a8530dc589b8d07e5aa33671137d4e19cdef",
-                              "fetch": 673894889, "write": 1114112},
+    "qwen3-32b-layer-128k": {"sha256": "275f2a12325790955bcd85c67ebbc7b324620345a75a5701445fbf8d040d893f",
+                             "fetch": 303083429, "write": 1114112},
+    "qwen3-32b-layer-128k-int4": {"sha256": "275f2a12325790955bcd85c67ebbc7b324620345a75a5701445fbf8d040d893f",
+                                  "fetch": 101440987, "write": 2228232},
+    "llama3.1-8b-layer-p32": {"sha256": "275f2a12325790955bcd85c67ebbc7b324620345a75a5701445fbf8d040d893f",
+                              "fetch": 673902215, "write": 1114112},
 }
 TRAFFIC_SOURCES = ("long_context_decode_pkv_amd/csrc/pkv_decode.hip",
                    "long_context_decode_pkv_amd/csrc/pkv_internal.h")
@@ -614,6 +614,7 @@ def main():
                     choices=["qwen3-32b-layer-128k", "llama3.1-8b-layer", "qwen3-32b-layer-128k-int4",
                              "llama3.1-8b-layer-int4", "qwen3-32b-layer-128k-prerope",
                              "llama3.1-8b-layer-prerope", "llama3.1-8b-layer-p32", "llama3.1-8b-layer-p32-prerope",
+                             "llama3.1-8b-layer-p32-int4",
                              "llama3.1-8b-ragged-batch",
                              "compress", "copy"])
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
