@@ -28,8 +28,8 @@
  *    cache's element type (bf16 for PKV_BF16_INT4); attention output is
  *    float32.
  *  - Fixed in this version: head_dim d = 128, page length P = 64 or 32
- *    (P = 32: PKV_BF16 and PKV_F32 storage, attention on the vector-ALU
- *    kernel; other values return PKV_ERR_UNSUPPORTED); GQA group size
+ *    (other values return PKV_ERR_UNSUPPORTED; PKV_BF16_INT4 at P = 32
+ *    needs r_K and r_V in the same multiple of 8); GQA group size
  *    G = H_q / H_kv <= 8.
  */
 #ifndef PKV_H
@@ -84,8 +84,7 @@ typedef struct pkv_shape {
   int32_t n_q_heads;  /* H_q */
   int32_t n_kv_heads; /* H_kv, H_q % H_kv == 0; query head h reads KV head h / G */
   int32_t head_dim;   /* d (must be 128) */
-  int32_t page_len;   /* P: 64, or 32 (Sec. 4.1 default) for PKV_BF16 / PKV_F32
-                         storage, whose attention runs on vector ALUs */
+  int32_t page_len;   /* P: 64, or 32 (Sec. 4.1 default) */
   int32_t rank_k;     /* r_K, 1 <= r_K <= min(P, d) */
   int32_t rank_v;     /* r_V, 1 <= r_V <= min(P, d) */
   int32_t sink;       /* s: dense sink tokens, a multiple of P (may be 0) */
@@ -186,7 +185,7 @@ int32_t pkv_factor_part_bytes(int32_t kind, int32_t P, int32_t d, int32_t r, int
  * Scales are float32 here and bfloat16 in the part (packing rounds
  * nearest-even).  Packing sets padding ranks to code 0, scale 0.
  * Errors: INVALID_ARG (null pointer, bad kind, r < 1, r > min(P, d), a code
- * outside -7..7), UNSUPPORTED (P != 64, d != 128, r > 32).  Host only.
+ * outside -7..7), UNSUPPORTED (P not 64 or 32, d != 128, r > 32).  Host only.
  */
 int32_t pkv_pack_factors_int4(int32_t kind, int32_t P, int32_t d, int32_t r, const int8_t* Lq,
                               const float* Ls, const int8_t* Rq, const float* Rs, void* packed);
