@@ -106,6 +106,11 @@ def test_llama31_8b_layer_32k_p32_full():
     decode_full(2, overrides=dict(P=32, r_k=16, r_v=14, s=32, w=32))
 
 
+def test_llama31_8b_layer_32k_p32_int4_full():
+    # the bench's llama3.1-8b-layer-p32-int4: INT4 factor pages of 32 tokens
+    decode_full(2, store="int4", overrides=dict(P=32, r_k=16, r_v=14, s=32, w=32))
+
+
 def test_qwen3_32b_layer_128k_int4_full():
     # INT4 factor pages (Sec. 4.3), the bench's qwen3-32b-layer-128k-int4
     decode_full(3, store="int4")
