@@ -23,11 +23,11 @@ __device__ inline uint16_t f32_to_bf16_bits(float x) {
 }
 
 // Element (j, c) of a page of P rows, j < P (token), c < d (channel).
-// The kernels decompose every page as 64 rows: a page of P = 32 rows is
-// padded with zero rows, which leaves its nonzero singular triplets
-// unchanged.  P is a multiple of 16, so a 16-row tile or a 4-row
-// reduction step lies wholly inside the page or wholly in the padding, and
-// the callers skip the padding as a whole.
+// A page of P = 32 rows sits in the kernels' 64-row frame with zero rows
+// below it (its Gram matrix has a zero block; the eigen-solve then runs on
+// the leading 32 x 32 block).  P is a multiple of 16, so a 16-row tile or a
+// 4-row reduction step lies wholly inside the page or wholly in the zero
+// rows, and the callers skip those as a whole instead of reading them.
 template <typename Elem>
 __device__ inline float page_elem(const Elem* X, int trans, int P, int j, int c) {
   Elem v = trans ? X[c * P + j] : X[j * kD + c];

@@ -49,7 +49,7 @@ struct DecodeArgs {
   float* ws_o;
   float* ws_ml;
   int B, Hkv, G, n_split;
-  int P;                        // page length (the matrix-core kernels: 64)
+  int P;                        // page length (the matrix-core formats fix theirs: kPageRows)
   int n_s, n_w;
   int r_k, r_v;
   int64_t T, n_fact, F_max;

@@ -11,7 +11,7 @@
 namespace pkv {
 
 constexpr int kP = 64;    // page length of the matrix-core layouts and kernels
-constexpr int kMinP = 32;  // shortest page (the plain layout and the VALU kernel)
+constexpr int kMinP = 32;  // the other page length: 32-row pages in the 64-row frame
 constexpr int kD = 128;   // head dim supported by the kernels
 constexpr int kMaxG = 8;  // query heads per KV head handled by one wave
 constexpr int kMaxBatchCaches = 32;    // caches of one batched attention launch
@@ -354,7 +354,7 @@ hipError_t launch_compress_batch(const CompressBatch& jb, hipStream_t stream);
 
 struct CacheGeom {
   int B, Hkv, Hq, G;
-  int P;                        // page length (64, or 32 on the VALU kernel)
+  int P;                        // page length: 64 or 32
   int n_s, n_w;
   int64_t F_max, max_pages;
   int dtype;
