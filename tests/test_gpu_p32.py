@@ -145,8 +145,8 @@ def test_p32_standalone_decomposition(r, out, pages):
     assert np.all(dev <= 0), float(dev.max())
 
 
-@pytest.mark.parametrize("rope", [False, True])
-def test_p32_decode_steps_against_oracle(rope):
+@pytest.mark.parametrize("rope,w", [(False, W), (True, W), (False, 0)])
+def test_p32_decode_steps_against_oracle(rope, w):
     """pkv_decode_step over 100 tokens from a ragged start: a page completes
     every 32 steps and the page leaving the window is factorized in the same
     call; every step's output against the oracle's incremental decoder (with
@@ -157,12 +157,12 @@ def test_p32_decode_steps_against_oracle(rope):
     d = synth.decode_inputs(cfg_id, T=T0 + steps, B=2, kv_heads=2, with_f64=True)
     dt = d["cfg"]["dtype"]
     f = synth.rope_inv_freq(5e5) if rope else None
-    cache = make_cache(d, r_k=RK, r_v=RV, s=S, w=W, P=P, max_tokens=T0 + steps)
+    cache = make_cache(d, r_k=RK, r_v=RV, s=S, w=w, P=P, max_tokens=T0 + steps)
     if rope:
         cache.set_key_rope(f)
     Kd, Vd = to_dev(d["K"], dt), to_dev(d["V"], dt)
     cache.prefill(Kd[:, :, :T0].contiguous(), Vd[:, :, :T0].contiguous())
-    inc = oracle.IncrementalDecoder(d["K64"], d["V64"], P, S, W, RK, RV, dt, key_rope=f)
+    inc = oracle.IncrementalDecoder(d["K64"], d["V64"], P, S, w, RK, RV, dt, key_rope=f)
     ws = cache.workspace(512)
     worst = 0.0
     for t in range(steps):
@@ -175,8 +175,8 @@ def test_p32_decode_steps_against_oracle(rope):
         err = rel_err(o, ref_s)
         worst = max(worst, err)
         assert err <= TOL[dt], (t, err)
-    assert cache.state()[1] == (T0 + steps) // P - 2
-    print(f"[P=32 step vs oracle] {steps} steps, worst err {worst:.3e}")
+    assert cache.state()[1] == (T0 + steps) // P - S // P - w // P
+    print(f"[P=32 step vs oracle w={w}] {steps} steps, worst err {worst:.3e}")
 
 
 def test_p32_chunks_match_token_by_token():
