@@ -43,12 +43,12 @@ CACHE_DIR = os.environ.get("PKV_BENCH_CACHE", "/tmp/pkv_bench_inputs")
 # reads 1048576 KiB for 2^30 bytes written -> x1.0).  A figure holds only for
 # the kernel sources whose hash it carries; any change to them makes it null.
 PMC_TRAFFIC = {
-    "qwen3-32b-layer-128k": {"sha256": "275f2a12325790955bcd85c67ebbc7b324620345a75a5701445fbf8d040d893f",
-                             "fetch": 303083429, "write": 1114112},
-    "qwen3-32b-layer-128k-int4": {"sha256": "275f2a12325790955bcd85c67ebbc7b324620345a75a5701445fbf8d040d893f",
-                                  "fetch": 101440987, "write": 2228232},
-    "llama3.1-8b-layer-p32": {"sha256": "275f2a12325790955bcd85c67ebbc7b324620345a75a5701445fbf8d040d893f",
-                              "fetch": 673902215, "write": 1114112},
+    "qwen3-32b-layer-128k": {"sha256": "1217ba8b2fe906eda42bad0129ad95eaec8fd696ccc98eb0d4059f280d27249c",
+                             "fetch": 303083995, "write": 1114112},
+    "qwen3-32b-layer-128k-int4": {"sha256": "1217ba8b2fe906eda42bad0129ad95eaec8fd696ccc98eb0d4059f280d27249c",
+                                  "fetch": 101441360, "write": 2228259},
+    "llama3.1-8b-layer-p32": {"sha256": "1217ba8b2fe906eda42bad0129ad95eaec8fd696ccc98eb0d4059f280d27249c",
+                              "fetch": 673900837, "write": 1114112},
 }
 TRAFFIC_SOURCES = ("long_context_decode_pkv_amd/csrc/pkv_decode.hip",
                    "long_context_decode_pkv_amd/csrc/pkv_internal.h")
