@@ -16,8 +16,9 @@ Inputs are seeded synthetic pages with the sigma_i = i^-1.2 spectrum
 
 Prints one JSON line.  Other workloads: llama3.1-8b-layer (B = 8, T = 32768,
 r = 16), llama3.1-8b-layer-p32 (the same tokens in 32-token pages at
-(r_K, r_V) = (16, 14), sink 32, window 32: PuzzleKV Sec. 4.1), the same
-layers with pre-RoPE keys (-prerope), qwen3-32b-layer-128k-int4 and llama3.1-8b-layer-int4 (the same
+(r_K, r_V) = (16, 14), sink 32, window 32: PuzzleKV Sec. 4.1; -p32-int4 and
+-p32-prerope with INT4 factors or pre-RoPE keys), the same layers with
+pre-RoPE keys (-prerope), qwen3-32b-layer-128k-int4 and llama3.1-8b-layer-int4 (the same
 layers with INT4 factor pages, PuzzleKV Sec. 4.3), and compress (batched page
 decomposition, 524288 pages, r in {8,16,32}).
 """
