@@ -245,13 +245,27 @@ int32_t promote_now(pkv_cache* c, void* stream) {
   if (f >= g.F_max) return PKV_ERR_CAPACITY;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
+  bool entry_set = false;
   if (c->early_lo <= p_old && p_old < c->early_hi) {
     e = hipStreamWaitEvent(s, c->ready[f % (g.n_w + 1)], 0);
     c->early_lo = p_old + 1;
   } else {
-    e = factorize_ring(c, p_old, p_old + 1, s);
+    // one launch: the decomposition also writes the page's table entry
+    CompressBatch jb;
+    std::memset(&jb, 0, sizeof(jb));
+    jb.base = factor_job(c, ring_src(c, p_old), 1, ring_src(c, p_old), 0);
+    jb.n = 1;
+    jb.m[0] = CompressMember{c->base + c->lay.win_k, c->base + c->lay.win_v, c->base + c->lay.factors, g.F_max, f, f,
+                             (int32_t*)(c->base + c->lay.page_table), p_old, table_entry(PKV_PAGE_FACT, (int)f)};
+    e = launch_compress_batch(jb, s);
+    if (e == hipErrorNotSupported) {  // ranks above 32: the decomposition, then the entry
+      (void)hipGetLastError();
+      e = factorize_ring(c, p_old, p_old + 1, s);
+    } else {
+      entry_set = true;
+    }
   }
-  if (e == hipSuccess) e = launch_table_set(g, p_old, table_entry(PKV_PAGE_FACT, (int)f), s);
+  if (e == hipSuccess && !entry_set) e = launch_table_set(g, p_old, table_entry(PKV_PAGE_FACT, (int)f), s);
   if (e != hipSuccess) return PKV_ERR_DEVICE;
   c->n_fact += 1;
   return PKV_OK;

@@ -708,6 +708,7 @@ hipError_t launch_compress_batch(const CompressBatch& jb, hipStream_t stream) {
   if (jb.n < 1 || jb.n > kMaxBatchCaches || job.n_pages <= 0) return hipErrorInvalidValue;
   const int r_max = job.rank[1] > job.rank[0] ? job.rank[1] : job.rank[0];
   if (r_max > kTriMaxRank || job.n_kind != 2) return hipErrorNotSupported;
+  const KernelEvents ev = take_kernel_events();  // pkv_time_next_kernel brackets this launch
   dim3 grid;
   if (!page_grid(job.n_pages * jb.n, grid)) return hipErrorInvalidValue;
   const bool q4 = job.out_dtype == PKV_BF16_INT4;
@@ -715,17 +716,23 @@ hipError_t launch_compress_batch(const CompressBatch& jb, hipStream_t stream) {
   if (job.page_rows != kP && job.page_rows != kMinP) return hipErrorInvalidValue;
   const bool full = job.page_rows == kP;
   if (q4 && full)
-    hipLaunchKernelGGL((compress_tri_batch_kernel<uint16_t, true, kP>), grid, dim3(64), 0, stream, jb);
+    hipExtLaunchKernelGGL((compress_tri_batch_kernel<uint16_t, true, kP>), grid, dim3(64), 0, stream, ev.start, ev.stop, 0,
+                          jb);
   else if (q4)
-    hipLaunchKernelGGL((compress_tri_batch_kernel<uint16_t, true, kMinP>), grid, dim3(64), 0, stream, jb);
+    hipExtLaunchKernelGGL((compress_tri_batch_kernel<uint16_t, true, kMinP>), grid, dim3(64), 0, stream, ev.start, ev.stop, 0,
+                          jb);
   else if (job.in_dtype == PKV_BF16 && full)
-    hipLaunchKernelGGL((compress_tri_batch_kernel<uint16_t, false, kP>), grid, dim3(64), 0, stream, jb);
+    hipExtLaunchKernelGGL((compress_tri_batch_kernel<uint16_t, false, kP>), grid, dim3(64), 0, stream, ev.start, ev.stop, 0,
+                          jb);
   else if (job.in_dtype == PKV_BF16)
-    hipLaunchKernelGGL((compress_tri_batch_kernel<uint16_t, false, kMinP>), grid, dim3(64), 0, stream, jb);
+    hipExtLaunchKernelGGL((compress_tri_batch_kernel<uint16_t, false, kMinP>), grid, dim3(64), 0, stream, ev.start, ev.stop, 0,
+                          jb);
   else if (full)
-    hipLaunchKernelGGL((compress_tri_batch_kernel<float, false, kP>), grid, dim3(64), 0, stream, jb);
+    hipExtLaunchKernelGGL((compress_tri_batch_kernel<float, false, kP>), grid, dim3(64), 0, stream, ev.start, ev.stop, 0,
+                          jb);
   else
-    hipLaunchKernelGGL((compress_tri_batch_kernel<float, false, kMinP>), grid, dim3(64), 0, stream, jb);
+    hipExtLaunchKernelGGL((compress_tri_batch_kernel<float, false, kMinP>), grid, dim3(64), 0, stream, ev.start, ev.stop, 0,
+                          jb);
   return hipGetLastError();
 }
 
