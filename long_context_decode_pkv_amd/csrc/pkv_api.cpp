@@ -1174,16 +1174,55 @@ int32_t pkv_decode_step_batch(pkv_cache* const* caches, int32_t n, const void* k
   job.v_new = v_new;
   if (e == hipSuccess) e = launch_merge_batch(gs, n, job, apps, ns_seq, s);
   if (e != hipSuccess) return PKV_ERR_DEVICE;
+  // tokens that completed a window page: factorize those pages early on the
+  // caches' aux streams -- one launch when the caches share one aux stream
+  int early[kMaxBatchCaches];
+  int64_t early_page[kMaxBatchCaches];
+  int n_early = 0;
+  bool shared_aux = true;
   for (int i = 0; i < n; ++i) {
     pkv_cache* c = caches[i];
     const int64_t p = c->T / gs[i].P;
     const int row = (int)(c->T % gs[i].P);
     c->T += 1;
-    // a token that completed a window page: factorize it early (aux stream)
-    if (c->aux && row == gs[i].P - 1 && p >= gs[i].n_s && gs[i].n_w > 0) {
-      st = factorize_early(c, p, s);
-      if (st != PKV_OK) return st;
+    if (c->aux && row == gs[i].P - 1 && p >= gs[i].n_s && gs[i].n_w > 0 && p - gs[i].n_s < gs[i].F_max) {
+      shared_aux = shared_aux && (n_early == 0 || c->aux == caches[early[0]]->aux);
+      early_page[n_early] = p;
+      early[n_early++] = i;
     }
+  }
+  if (n_early > 1 && shared_aux) {
+    pkv_cache* c0 = caches[early[0]];
+    hipStream_t aux = c0->aux;
+    CompressBatch jb;
+    std::memset(&jb, 0, sizeof(jb));
+    jb.base = factor_job(c0, ring_src(c0, early_page[0]), 1, ring_src(c0, early_page[0]), 0);
+    jb.n = n_early;
+    for (int k = 0; k < n_early; ++k) {
+      pkv_cache* c = caches[early[k]];
+      const int64_t f = early_page[k] - g0.n_s;  // the page keeps its WIN entry until it leaves
+      jb.m[k] = CompressMember{c->base + c->lay.win_k, c->base + c->lay.win_v, c->base + c->lay.factors,
+                               c->lay.max_fact_pages, f, f, nullptr, 0, 0};
+    }
+    hipError_t e = hipEventRecord(c0->written, s);  // after this step's launches on s
+    if (e == hipSuccess) e = hipStreamWaitEvent(aux, c0->written, 0);
+    if (e == hipSuccess) e = launch_compress_batch(jb, aux);
+    if (e == hipErrorNotSupported) {  // ranks above 32: one launch per cache
+      (void)hipGetLastError();
+    } else {
+      for (int k = 0; k < n_early && e == hipSuccess; ++k) {
+        pkv_cache* c = caches[early[k]];
+        const int64_t p = early_page[k];
+        e = hipEventRecord(c->ready[(p - g0.n_s) % (g0.n_w + 1)], aux);
+        if (c->early_lo == c->early_hi) c->early_lo = p;
+        c->early_hi = p + 1;
+      }
+      return dev_status(e);
+    }
+  }
+  for (int k = 0; k < n_early; ++k) {
+    st = factorize_early(caches[early[k]], early_page[k], s);
+    if (st != PKV_OK) return st;
   }
   return PKV_OK;
 }

@@ -230,6 +230,8 @@ def test_step_batch_equals_per_cache_steps(label, cfg_id, kw):
     # caches with an aux stream only wait for their early factorization; the
     # others share the one decomposition launch
     ("mixed aux", 2, dict(aux=[True, False, True, False])),
+    # every cache on one aux stream: their early factorizations share a launch
+    ("aux together", 2, dict(aux=True)),
 ])
 def test_step_batch_promotes_together(label, cfg_id, kw):
     # every cache completes a page at the same steps, so the pages leaving the
