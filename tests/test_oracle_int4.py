@@ -81,6 +81,46 @@ def test_sqrt_sigma_split_and_group_axes():
         assert np.linalg.norm(Lq @ Rq - Lt @ Rt) <= bound
 
 
+def test_group_orientation_of_int4_codes_by_outcome():
+    """Sec. 4.3 groups Lt_K, Rt_K and Rt_V by column and Lt_V by row.  The
+    page below makes each choice visible in the codes int4_codes returns:
+    U (Hadamard / 8) and W (the first 64 rows of Hadamard / sqrt(128)) have
+    entries of one magnitude, and sigma_1 exceeds the other kept singular
+    values 256-fold, so Lt = U_r Sigma_r^(1/2) has entries +-7 * 2^0 in its
+    first column and +-7 * 2^-4 elsewhere.
+      - per column of Lt (keys): every column sits on its own grid, so the
+        dequantized Lt_K is exact;
+      - per row of Lt (values): each row's scale comes from its first-column
+        entry, so every other column rounds to code 0;
+      - per column of Rt (keys and values): each channel's scale comes from
+        row 0, so rows 1.. round to code 0.
+    A swapped axis in any of the four factors flips one of these."""
+    from scipy.linalg import hadamard
+    P, d, r = 64, 128, 8
+    U = hadamard(P).astype(np.float64) / 8.0
+    Wt = hadamard(d)[:P].astype(np.float64) / np.sqrt(d)
+    # Lt[j, i] = U[j, i] sqrt(S_i) = +-7 * 2^e_i  <=>  S_i = (56 * 2^e_i)^2
+    e = np.array([0.0] + [-4.0] * (P - 1))
+    S = (56.0 * 2.0 ** e) ** 2
+    np.testing.assert_allclose(U.T @ U, np.eye(P), atol=1e-15)
+    np.testing.assert_allclose(Wt @ Wt.T, np.eye(P), atol=1e-15)
+    for kind in ("K", "V"):
+        Lt, Rt, lq, ls, rq, rs = O.int4_codes(U, S, Wt, r, kind)
+        np.testing.assert_allclose(np.abs(Lt[:, 0]), 7.0, rtol=1e-15)
+        np.testing.assert_allclose(np.abs(Lt[:, 1:]), 7.0 / 16, rtol=1e-15)
+        Ld, Rd = O.dequantize_int4(lq, ls), O.dequantize_int4(rq, rs)
+        if kind == "K":
+            np.testing.assert_array_equal(Ld, Lt)  # each column on its own grid
+            assert np.all(np.abs(lq) == 7)
+        else:
+            np.testing.assert_array_equal(Ld[:, 0], Lt[:, 0])
+            assert np.all(lq[:, 1:] == 0)  # coarsened by the row's first entry
+        # Rt, per column for both kinds: row 0 kept to the scale's rounding,
+        # the smaller rows round to zero
+        assert np.all(np.abs(rq[0]) == 7) and np.all(rq[1:] == 0)
+        np.testing.assert_allclose(Rd[0], Rt[0], rtol=2.0 ** -8)
+
+
 def test_int4_storage_ratio_printed_value():
     for e in json.load(open(GOLDEN))["int4_storage_ratio"]:
         v = O.int4_storage_ratio(e["T"], e["P"], e["d"], e["r_k"], e["r_v"], e["dense_pages"])
