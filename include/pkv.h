@@ -437,6 +437,26 @@ int32_t pkv_cache_set_aux_stream(pkv_cache* cache, void* aux_stream);
  */
 int32_t pkv_cache_set_key_rope(pkv_cache* cache, const float* inv_freq, int32_t n_freq);
 
+/*
+ * pkv_decode_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and result as pkv_decode_attn (bit-identical output for the
+ * same n_split), but the split partials go to a workspace the library holds:
+ * one array of PKV_NOALLOC_WORKSPACE_BYTES per device, in the library's
+ * device image, kept until the process ends.  The call allocates and frees
+ * nothing, and the workspace needs no clearing (the partial kernel writes
+ * every state the merge reads).  Every call on one device shares that
+ * device's array, so calls that overlap on one device (two streams, two
+ * host threads) race; calls in stream order do not.  The first call on a
+ * device looks the array's address up once (hipGetSymbolAddress).
+ * Errors: as pkv_decode_attn; CAPACITY when pkv_decode_workspace_bytes for
+ * n_split exceeds PKV_NOALLOC_WORKSPACE_BYTES (checked before any device
+ * call); DEVICE if the lookup fails.
+ */
+#define PKV_NOALLOC_WORKSPACE_BYTES (16ull << 20)
+int32_t pkv_decode_attn_noalloc(const pkv_cache* cache, const void* q, float* out, int32_t n_split,
+                                void* stream);
+
 /* Kernel timing (measurement only; no passage of the method).
  *
  * start_event, stop_event: hipEvent_t handles (as void*) that the caller

@@ -26,6 +26,7 @@ BF16, F32, BF16_INT4 = 0, 1, 2
 KEYS, VALUES, KEYS_PRE_ROPE = 0, 1, 2
 UNUSED, SINK, FACT, WIN, PART = 0, 1, 2, 3, 4
 PAGE_LEN, HEAD_DIM = 64, 128
+NOALLOC_WORKSPACE_BYTES = 16 << 20  # PKV_NOALLOC_WORKSPACE_BYTES of include/pkv.h
 
 
 class PKVError(RuntimeError):
@@ -85,6 +86,7 @@ def lib():
         "pkv_promote_page": ([vp, vp], i32),
         "pkv_decode_workspace_bytes": ([vp, i32, P(u64)], i32),
         "pkv_decode_attn": ([vp, vp, vp, vp, u64, i32, vp], i32),
+        "pkv_decode_attn_noalloc": ([vp, vp, vp, i32, vp], i32),
         "pkv_decode_partial": ([vp, vp, vp, u64, i32, vp], i32),
         "pkv_decode_merge": ([vp, vp, u64, i32, vp, vp], i32),
         "pkv_read_page_table": ([vp, vp, vp, i64, vp], i32),
@@ -377,6 +379,14 @@ class Cache:
         _check(lib().pkv_decode_attn(self._h, _dev_ptr(q, self.elem_code, "q"),
                                      _dev_ptr(out, None, "out"), ctypes.c_void_p(ws.data_ptr()),
                                      ws.numel(), n_split, _stream(self.device)), "pkv_decode_attn")
+        return out
+
+    def decode_noalloc(self, q, out, n_split: int = 0):
+        """pkv_decode_attn_noalloc: decode attention into the caller's `out`
+        with the library-held workspace (no allocation by the call)."""
+        _check(lib().pkv_decode_attn_noalloc(self._h, _dev_ptr(q, self.elem_code, "q"),
+                                             _dev_ptr(out, None, "out"), n_split,
+                                             _stream(self.device)), "pkv_decode_attn_noalloc")
         return out
 
     def decode_partial(self, q, n_split: int = 0, workspace=None):

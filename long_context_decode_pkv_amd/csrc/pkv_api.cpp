@@ -977,6 +977,19 @@ int32_t pkv_decode_attn(const pkv_cache* c, const void* q, float* out, void* wor
   return dev_status(e);
 }
 
+int32_t pkv_decode_attn_noalloc(const pkv_cache* c, const void* q, float* out, int32_t n_split,
+                                void* stream) {
+  if (!c || !q || !out || !aligned(out, 16)) return PKV_ERR_INVALID_ARG;
+  if (n_split < 0 || n_split > kMaxDecodeSplits) return PKV_ERR_INVALID_ARG;
+  uint64_t need = 0;
+  int32_t st = pkv_decode_workspace_bytes(c, n_split, &need);
+  if (st != PKV_OK) return st;
+  if (need > kNoAllocScratchBytes) return PKV_ERR_CAPACITY;  // before any device call
+  void* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return PKV_ERR_DEVICE;
+  return pkv_decode_attn(c, q, out, ws, kNoAllocScratchBytes, n_split, stream);
+}
+
 int32_t pkv_decode_step(pkv_cache* c, const void* k_new, const void* v_new, const void* q,
                         float* out, void* workspace, uint64_t workspace_bytes, int32_t n_split,
                         void* stream) {

@@ -26,6 +26,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "pkv_internal.h"
@@ -2253,6 +2254,39 @@ hipError_t launch_partial_batch(const CacheGeom* gs, const int64_t* T, const int
     cols += ns[i];
   }
   return dispatch_partial(gs[0], x, dim3(cols, gs[0].Hkv, 1), stream);
+}
+
+// Library-held decode workspace for callers that cannot allocate
+// (pkv_decode_attn_noalloc).  In host code `scratch` names a host-side
+// stand-in, not device memory: its address on each device comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is handed to kernels.  Every call on a device shares the
+// device's copy, so calls that overlap on one device race.
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace pkv

@@ -415,4 +415,11 @@ bool batched_kernel(const CacheGeom& g);
 int decode_batch_splits(const CacheGeom& g, const int64_t* T, int n, int* ns);
 int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact);
 
+// Size of the library-held decode workspace of pkv_decode_attn_noalloc
+// (one copy per device, held until the process ends).
+constexpr uint64_t kNoAllocScratchBytes = PKV_NOALLOC_WORKSPACE_BYTES;
+// That workspace's device address on the current device (looked up once per
+// device by hipGetSymbolAddress).
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace pkv
