@@ -94,21 +94,28 @@ typedef struct pkv_shape {
 } pkv_shape;
 
 /*
- * Device-buffer layout of a cache (byte offsets from the caller's buffer,
- * every region 256-byte aligned).  With n_s = s/P, n_w = w/P:
+ * Device-buffer layout of a cache: the preallocated dense sink, the dense
+ * window ring, the factor pool and the page table of Sec. 3.3 (1)-(3) and
+ * (5).  Byte offsets from the caller's buffer, in this order, each region
+ * starting at the previous one's end rounded up to 256 bytes.  With
+ * n_s = s/P, n_w = w/P:
  *   sink_k  [B][H_kv][n_s][P][d]        keys, row-major
  *   sink_v  [B][H_kv][n_s][d][P]        values, transposed per page
  *   win_k   [B][H_kv][n_w+1][P][d]      ring of window/partial key pages
  *   win_v   [B][H_kv][n_w+1][d][P]      ring of value pages, transposed
  *   factors [B][H_kv][F_max][factor_page_bytes]   K part, then V part
  *   page_table [max_pages] int32: (class << 24) | slot
- * With P = 64 the factor parts use a fixed interleaved order matched to the
- * attention kernel's matrix-core register layout, ranks padded to a multiple
- * of 8 (padding is zero); with P = 32 they hold plain row-major blocks at the
- * exact rank.  pkv_pack_factors and pkv_unpack_factors convert between
- * either and row-major Lf (P x r), Rf (r x d).
- * PKV_BF16_INT4 parts hold codes and scales in their own interleaved order;
- * pkv_pack_factors_int4 and pkv_unpack_factors_int4 convert it.
+ * total_bytes is the page table's end rounded up to 256.
+ * Factor parts (PKV_BF16, PKV_F32) use a fixed interleaved order matched to
+ * the attention kernel's matrix-core register layout, with the rank padded
+ * to r8 = 8 ceil(r / 8) (padding ranks hold zeros), so a part holds
+ * r8 (P + d) elements at either page length.  A P = 32 part is the P = 64
+ * order with the operand rows of page rows 32..63 left out.
+ * pkv_pack_factors and pkv_unpack_factors convert between a part and
+ * row-major Lf (P x r), Rf (r x d).
+ * PKV_BF16_INT4 parts hold codes and scales in their own interleaved order
+ * (sizes at pkv_factor_part_bytes); pkv_pack_factors_int4 and
+ * pkv_unpack_factors_int4 convert it.
  */
 typedef struct pkv_layout {
   uint64_t sink_k, sink_v, win_k, win_v, factors, page_table;
@@ -119,11 +126,12 @@ typedef struct pkv_layout {
   int64_t max_pages;         /* ceil(T_max / P) */
   int64_t elem_bytes;        /* bytes of a dense element: 2 (bf16, bf16+int4) or 4 (f32) */
   int64_t dense_page_bytes;  /* P * d * elem_bytes */
-  int64_t factor_k_elems;    /* packed elements (INT4: codes) of a K part: r8_K (P + d);
-                                P = 32: r_K (P + d) */
-  int64_t factor_v_elems;    /* r8_V (P + d); P = 32: r_V (P + d) */
+  int64_t factor_k_elems;    /* packed elements (INT4: codes) of a K part: r8_K (P + d),
+                                r8 = 8 ceil(r / 8), at P = 64 and P = 32 */
+  int64_t factor_v_elems;    /* r8_V (P + d) */
   int64_t factor_page_bytes; /* factor_k_bytes + factor_v_bytes */
-  int64_t factor_k_bytes;    /* bytes of a K part (its offset in the page is 0) */
+  int64_t factor_k_bytes;    /* bytes of a K part (its offset in the page is 0): elems x
+                                elem_bytes, or pkv_factor_part_bytes for INT4 */
   int64_t factor_v_bytes;    /* bytes of a V part (offset factor_k_bytes) */
 } pkv_layout;
 
@@ -153,7 +161,7 @@ int32_t pkv_classify(int64_t T, int32_t P, int32_t s, int32_t w, int64_t n_fact,
                      int32_t* slot, int64_t n_pages);
 
 /* Packed elements of one factor part for rank r: r8 (P + d) with r8 = r
- * rounded up to a multiple of 8 at P = 64, r (P + d) at P = 32.  Errors:
+ * rounded up to a multiple of 8, at P = 64 and at P = 32.  Errors:
  * UNSUPPORTED for other P or d != 128; INVALID_ARG unless 1 <= r <= P.
  * Host only. */
 int32_t pkv_factor_part_elems(int32_t P, int32_t d, int32_t r, int64_t* elems);
@@ -171,8 +179,15 @@ int32_t pkv_unpack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_
                            const void* packed, float* Lf, float* Rf);
 
 /* Bytes of one factor part (kind: any pkv_factor_kind) of rank r in
- * storage format `dtype` (for PKV_BF16_INT4 the INT4 part of Sec. 4.3; its
- * K and V parts differ in size).  Host only. */
+ * storage format `dtype`.  PKV_BF16 / PKV_F32: r8 (P + d) elements of 2 / 4
+ * bytes.  PKV_BF16_INT4 (the INT4 part of Sec. 4.3; K and V parts differ),
+ * with A = r8 / 4 and a unit of ub = 1, 2 or 4 bytes for A <= 2, <= 4,
+ * else, and h = 1 at P = 64, 2 at P = 32:
+ *   K part: roundup64(r8 d / 2 + (256 / h) ub + 2 d + 2 r8)
+ *           (codes of Rt_K, codes of Lt_K in units of A, scales of Rt_K, Lt_K)
+ *   V part: roundup64(r8 P / 2 + 4 d ub + 2 P + 2 d)
+ *           (codes of Lt_V, codes of Rt_V in units of A, scales of Lt_V, Rt_V).
+ * Host only. */
 int32_t pkv_factor_part_bytes(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t dtype,
                               int64_t* bytes);
 
@@ -192,7 +207,10 @@ int32_t pkv_pack_factors_int4(int32_t kind, int32_t P, int32_t d, int32_t r, con
 int32_t pkv_unpack_factors_int4(int32_t kind, int32_t P, int32_t d, int32_t r, const void* packed,
                                 int8_t* Lq, float* Ls, int8_t* Rq, float* Rs);
 
-/* Bytes and layout of the device buffer a cache of this shape needs. */
+/* Bytes and layout of the device buffer a cache of this shape needs: the
+ * preallocated dense and factor storage of Sec. 3.3 (1)-(3) and (5), laid
+ * out as described at pkv_layout.  Errors: as pkv_cache_create's shape
+ * checks.  Host only. */
 int32_t pkv_cache_layout(const pkv_shape* shape, pkv_layout* out);
 
 /* Create a cache over a caller-owned device buffer of at least
@@ -210,16 +228,20 @@ int32_t pkv_cache_state(const pkv_cache* cache, int64_t* T, int64_t* n_fact, int
 /*
  * Batched page decomposition (Sec. 3.3, text after Eq. 3): for each of
  * n_pages pages X (P x d, row-major, contiguous, `in_dtype`) form the Gram
- * matrix G = X X^T in float32, take its top-r eigenvectors Q (float32 Jacobi
- * eigen-solve, one page per wavefront), and write
+ * matrix G = X X^T in float32 on the matrix cores, take its top-r
+ * eigenvectors Q in float32, and write
  *   Lf = Q diag(sigma)  (P x r),   Rf = diag(1/sigma) Q^T X  (r x d),
  *   sigma_i = || (Q^T X)_i ||,
  * so Lf Rf is the rank-r truncated SVD of X (Sec. 3.2; Eckart-Young-Mirsky).
+ * The eigen-solve, one page per wavefront: r <= 32 (every 32-token page):
+ * Householder reduction of G to tridiagonal form, bisection for the r
+ * largest eigenvalues, one eigenvector each from a twisted factorization,
+ * back-transformation; a 32-token page is solved on its own 32 x 32 Gram
+ * matrix.  r > 32: cyclic Jacobi rotations of G.
  * Outputs (device, row-major, `out_dtype`): Lf [n_pages][P][r],
  * Rf [n_pages][r][d]; sigma [n_pages][r] float32 (may be NULL).  Rows with
- * sigma = 0 are zero.  P = 32 pages are decomposed as 64-row pages padded
- * with zero rows.  Errors: INVALID_ARG (null/misaligned pointers, bad r),
- * UNSUPPORTED (P not 64 or 32, or d != 128), DEVICE (launch failure).
+ * sigma = 0 are zero.  Errors: INVALID_ARG (null/misaligned pointers, bad
+ * r), UNSUPPORTED (P not 64 or 32, or d != 128), DEVICE (launch failure).
  */
 int32_t pkv_compress_pages(const void* X, int64_t n_pages, int32_t P, int32_t d, int32_t r,
                            int32_t in_dtype, int32_t out_dtype, void* Lf, void* Rf, float* sigma,
@@ -328,7 +350,11 @@ int32_t pkv_decode_step_batch(pkv_cache* const* caches, int32_t n, const void* k
                               int32_t n_split, void* stream);
 
 /* Workspace bytes pkv_decode_attn needs for n_split splits per (sequence,
- * KV head); n_split = 0 selects the library's choice; at most 512. */
+ * KV head): the split-K partial states that the Eq. 5 merge combines
+ * (Sec. 3.3 (4)), rows = B H_q n_split, laid out as at pkv_decode_partial:
+ * roundup256(rows d 4) + roundup256(rows 2 4).  n_split = 0 selects the
+ * library's choice for the cache's current length; at most 512.  Host
+ * only.  Errors: INVALID_ARG (null pointers, n_split out of range). */
 int32_t pkv_decode_workspace_bytes(const pkv_cache* cache, int32_t n_split, uint64_t* bytes);
 
 /*
@@ -368,8 +394,10 @@ int32_t pkv_decode_partial(const pkv_cache* cache, const void* q, void* workspac
 int32_t pkv_decode_merge(const pkv_cache* cache, const void* workspace, uint64_t workspace_bytes,
                          int32_t n_split, float* out, void* stream);
 
-/* Copy the page table to host: cls[p], slot[p] for p < n (n <= max_pages).
- * Synchronizes `stream`. */
+/* Copy the page table (the page classes and slots of Sec. 3.3 (1)-(3) and
+ * (5), as pkv_classify describes them) to host: cls[p], slot[p] for p < n
+ * (n <= max_pages).  Synchronizes `stream`.  Errors: INVALID_ARG (null
+ * pointers, n < 0 or n > max_pages), DEVICE. */
 int32_t pkv_read_page_table(const pkv_cache* cache, int32_t* cls, int32_t* slot, int64_t n,
                             void* stream);
 
