@@ -219,6 +219,87 @@ def noise_page_ids(seed: int, n_pages: int, frac: float) -> np.ndarray:
     return np.sort(perm[:n_noise])
 
 
+def bf16_bits_torch(x):
+    """float64 torch tensor (any device) -> int16 tensor of bfloat16 bit
+    patterns, nearest-even with exactly one rounding (as to_bf16_bits): the
+    float32 step rounds to odd (exact float32, else its magnitude truncated
+    and the last bit set), which makes the following nearest-even step
+    round as if from the double.  Finite inputs only."""
+    import torch
+
+    x32 = x.to(torch.float32)                     # nearest-even
+    back = x32.to(torch.float64)
+    inexact = back != x
+    u = x32.view(torch.int32)
+    u = torch.where(inexact & (back.abs() > x.abs()), u - 1, u)  # toward zero
+    u = torch.where(inexact, u | 1, u)                            # odd
+    u = u + 0x7FFF + ((u >> 16) & 1)              # float32 -> bf16 nearest-even
+    return (u >> 16).to(torch.int16)
+
+
+def _haar_columns_torch(Z):
+    """Orthonormal columns of Gaussian Z (n, rows, k) float64 on Z's device by
+    classical Gram-Schmidt applied twice per column (batched matrix-vector
+    products only): column j is Z_j minus its projection on columns < j,
+    divided by its norm, so R_jj > 0 -- the Q of the QR with diag(R) > 0,
+    the construction of haar_columns.  The basis is kept in both orders so no
+    product reads a transposed view."""
+    import torch
+
+    n, m, k = Z.shape
+    Q = torch.empty_like(Z)                      # (n, m, k)
+    Qt = torch.empty((n, k, m), dtype=Z.dtype, device=Z.device)
+    for j in range(k):
+        v = Z[:, :, j:j + 1].contiguous()
+        for _ in range(2 if j else 0):
+            c = torch.bmm(Qt[:, :j, :], v)       # (n, j, 1)
+            v = v - torch.bmm(Q[:, :, :j], c)
+        v = v / torch.linalg.vector_norm(v, dim=1, keepdim=True)
+        Q[:, :, j:j + 1] = v
+        Qt[:, j:j + 1, :] = v.transpose(1, 2)
+    return Q
+
+
+def compression_pool_device(n_total: int | None = None, device="cuda:0", cfg_id: int = 5,
+                            chunk: int = 16384):
+    """The batched-compression workload drawn on a torch device: int16
+    tensor (n_total, P, d) of bfloat16 bit patterns (view it as bfloat16).
+
+    Same recipe as compression_pages -- page i is U diag(i^-1.2) W^T with U
+    Haar on O(64) and W 128 x 64 with Haar columns, or N(0,1) noise when i is
+    one of noise_page_ids -- generated in float64 and rounded once, but drawn
+    from torch's device generator: chunk c (pages c*chunk ..) from a
+    generator seeded from (seed, c).  The bytes are fixed by the seed, the
+    chunk size and torch's generator; they differ from compression_pages'
+    per-page streams.  For pools too large to draw on the host in seconds."""
+    import torch
+
+    cfg = CONFIGS[cfg_id]
+    P, d, seed = cfg["P"], cfg["d"], cfg["seed"]
+    if n_total is None:
+        n_total = cfg["layers"] * cfg["Hkv"] * 2 * cfg["pages_per_head"]
+    noise = torch.from_numpy(noise_page_ids(seed, n_total, cfg["noise_frac"]))
+    k = min(P, d)
+    sig = torch.arange(1, k + 1, dtype=torch.float64, device=device) ** -1.2
+    out = torch.empty((n_total, P, d), dtype=torch.int16, device=device)
+    for c0 in range(0, n_total, chunk):
+        n = min(chunk, n_total - c0)
+        ss = np.random.SeedSequence(entropy=seed, spawn_key=(c0 // chunk, KIND_PAGE, 99))
+        g = torch.Generator(device=device)
+        g.manual_seed(int(ss.generate_state(1, np.uint64)[0] >> np.uint64(1)))
+        U = _haar_columns_torch(torch.randn((n, P, P), generator=g, dtype=torch.float64, device=device))
+        W = _haar_columns_torch(torch.randn((n, d, k), generator=g, dtype=torch.float64, device=device))
+        X = torch.bmm((U[:, :, :k] * sig).contiguous(), W.transpose(-1, -2).contiguous())
+        del U, W
+        nz = noise[(noise >= c0) & (noise < c0 + n)] - c0
+        if nz.numel():
+            X[nz.to(device)] = torch.randn((nz.numel(), P, d), generator=g, dtype=torch.float64,
+                                           device=device)
+        out[c0:c0 + n] = bf16_bits_torch(X)
+        del X
+    return out
+
+
 def compression_pages(page_ids, n_total: int | None = None, cfg_id: int = 5) -> np.ndarray:
     """float64 pages (len(page_ids), P, d) of the batched-compression workload.
     Page i is drawn from its own stream; noise pages are N(0,1)."""
