@@ -19,8 +19,10 @@ r = 16), llama3.1-8b-layer-p32 (the same tokens in 32-token pages at
 (r_K, r_V) = (16, 14), sink 32, window 32: PuzzleKV Sec. 4.1; -p32-int4 and
 -p32-prerope with INT4 factors or pre-RoPE keys), the same layers with
 pre-RoPE keys (-prerope), qwen3-32b-layer-128k-int4 and llama3.1-8b-layer-int4 (the same
-layers with INT4 factor pages, PuzzleKV Sec. 4.3), and compress (batched page
-decomposition, 524288 pages, r in {8,16,32}).
+layers with INT4 factor pages, PuzzleKV Sec. 4.3), incremental (workload 4:
+the Llama-shaped layer decoded for 512 steps from T = 8192 with its
+promotions), and compress (batched page decomposition, 524288 distinct pages,
+r in {8,16,32}).
 """
 import argparse
 import json
@@ -113,12 +115,35 @@ def decode_bytes(cfg, B, Hkv, Hq, T, n_fact, store=None):
     return B * Hkv * (fact + dense) + B * Hq * d * esz + B * Hq * d * 4
 
 
+def host_cpu():
+    """The host the oracle runs on: CPU model and the cores this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "nproc": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count()}
+
+
+def one_core(fn):
+    """Run fn with the oracle's OpenMP core and numpy's BLAS on one thread."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        return fn()
+
+
 def cpu_baseline_decode(cfg, K, V, q, T, store=None, key_rope=None):
     """The oracle on a bounded sample: KV head 0 of the same cache.  The
     oracle reconstructs that head (Jacobi SVD of its factorized pages,
     truncation, storage rounding; timed -> pages/s), then its naive float64
     attention for the head's query heads is timed and scaled to the full step
-    (all (sequence, KV head) pairs) -> tokens/s."""
+    (all (sequence, KV head) pairs) -> tokens/s.  Both are timed on all the
+    host's cores and again on one core (the SVD on a 128-page share of the
+    head's pages there)."""
     import oracle
     import synth
     try:
@@ -145,6 +170,20 @@ def cpu_baseline_decode(cfg, K, V, q, T, store=None, key_rope=None):
         oracle.attention(q64, Ka, Vhat)
     t_att = (time.perf_counter() - t) / reps
     step = t_att * n_pairs
+
+    def timed_one_core():
+        t0 = time.perf_counter()
+        Ka = Khat if key_rope is None else oracle.rope_rotate(Khat, np.arange(T), key_rope)
+        oracle.attention(q64, Ka, Vhat)
+        t_att1 = time.perf_counter() - t0
+        n1 = min(128, n_fact)
+        pages = np.stack([k64[p * P:(p + 1) * P] for p in
+                          np.nonzero(oracle.classify(T, P, s, w)[0] == oracle.FACT)[0][:n1]])
+        t0 = time.perf_counter()
+        oracle.svd_batch(pages)
+        return t_att1, n1 / (time.perf_counter() - t0)
+
+    t_att1, svd1 = one_core(timed_one_core)
     return dict(value=K.shape[0] / step, unit="tokens/s", cores=int(max(blas, oracle.num_threads())),
                 kind="oracle",
                 sample=(f"KV head 0 of the same cache: naive float64 attention of its {G} query "
@@ -152,6 +191,11 @@ def cpu_baseline_decode(cfg, K, V, q, T, store=None, key_rope=None):
                         f"by {n_pairs} (sequence, KV head) pairs per step; the oracle's "
                         f"reconstruction of that head ({2 * n_fact} Jacobi SVDs) ran at "
                         f"{2 * n_fact / t_rec:.1f} pages/s"),
+                one_core={"value": K.shape[0] / (t_att1 * n_pairs), "unit": "tokens/s",
+                          "svd_pages_per_s": svd1,
+                          "sample": f"the same attention on one core ({t_att1 * 1e3:.1f} ms), "
+                                    f"the Jacobi SVD of {min(128, n_fact)} of the head's pages"},
+                host=host_cpu(),
                 svd_pages_per_s=2 * n_fact / t_rec)
 
 
@@ -177,7 +221,8 @@ def bench_decode(args, cfg_id, name, store=None, rope=False, overrides=None):
     cfg.update(overrides or {})
     B, Hq, Hkv, T0 = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"]
     NL = args.layers
-    total = T0 + args.warmup + 2 * args.steps  # timed pass, then an instrumented pass
+    # timed pass, an instrumented pass, then up to P steps to a promotion per layer
+    total = T0 + args.warmup + 2 * args.steps + cfg["P"]
     inp = cached_inputs(cfg_id, total, workers=args.workers)
     dt = cfg["dtype"]
     Kd, Vd = to_dev(inp["K"], dt), to_dev(inp["V"], dt)
@@ -244,6 +289,7 @@ def bench_decode(args, cfg_id, name, store=None, rope=False, overrides=None):
     torch.cuda.synchronize()
     # timed pass: exactly `steps` layer steps per layer cache, nothing but the
     # library calls inside the timed region
+    nf_timed0 = sum(c.state()[1] for c in caches)
     torch.cuda.synchronize()
     t = time.perf_counter()
     for j in range(args.steps):
@@ -251,6 +297,7 @@ def bench_decode(args, cfg_id, name, store=None, rope=False, overrides=None):
             layer_step(c, ws, args.warmup + j)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t
+    promos_timed = sum(c.state()[1] for c in caches) - nf_timed0  # promotions inside `value`
 
     # instrumented pass (not part of `value`): the same steps on the next
     # tokens, each attention launch bracketed by its kernel's own events
@@ -266,11 +313,28 @@ def bench_decode(args, cfg_id, name, store=None, rope=False, overrides=None):
             states.append(layer_step(c, ws, args.warmup + args.steps + j, recs[j][li]))
     torch.cuda.synchronize()
     elapsed_instr = time.perf_counter() - t
+    # one promotion per layer cache whatever the step count: step on to the
+    # first step at which a page leaves the window and time its decomposition
+    # (the first kernel of that step)
+    i = args.warmup + 2 * args.steps
+    extra = []
+    while not extra and i < total - T0:
+        T, nf, _ = caches[0].state()  # every cache has the same length
+        due = (T + 1) // P - n_s - n_w > nf
+        for c, ws in zip(caches, wss):
+            if due and aux is None:
+                pair = (ev(), ev())
+                pkv.time_next_kernel(*pair)
+                extra.append(pair)
+            c.step(rows_k[i], rows_v[i], qs[i], out=out, workspace=ws)
+        i += 1
+    torch.cuda.synchronize()
     flat = [r for step in recs for r in step]
     keep = [k for k, r in enumerate(flat) if not r["promoted"]]
     durs = np.array([flat[k]["partial"][0].elapsed_time(flat[k]["partial"][1]) * 1e-3 for k in keep])
     merges = np.array([flat[k]["partial"][1].elapsed_time(flat[k]["merge"][1]) * 1e-3 for k in keep])
     promos = [r["promote"][0].elapsed_time(r["promote"][1]) * 1e-3 for r in flat if r["promoted"]]
+    promos += [a.elapsed_time(b) * 1e-3 for a, b in extra]
     if aux is not None:
         # early factorizations overlap later steps; time the same launch
         # (one page of every (sequence, KV head, K/V)) on its own
@@ -290,12 +354,18 @@ def bench_decode(args, cfg_id, name, store=None, rope=False, overrides=None):
     achieved = nbytes.sum() / durs.sum() / 1e9
     layer_steps = args.steps * NL
     traffic = pmc_traffic(name)
+    # promotions at their rate: one per P steps of a layer; the timed pass
+    # holds promos_timed of them
+    t_promo = float(np.mean(promos)) if promos else 0.0
+    step_amortized = (elapsed - promos_timed * t_promo) / layer_steps + t_promo / P
     log(f"partial kernel: mean {durs.mean() * 1e6:.2f} us (median {np.median(durs) * 1e6:.2f}), "
         f"{nbytes.mean() / 1e6:.1f} MB -> {achieved:.0f} GB/s; partial end to merge end "
         f"{merges.mean() * 1e6:.2f} us; "
         f"{len(promos)} promotions, mean {np.mean(promos) * 1e6 if promos else 0:.1f} us; "
         f"layer step {elapsed / layer_steps * 1e6:.1f} us "
-        f"({elapsed_instr / layer_steps * 1e6:.1f} us with per-launch events)")
+        f"({elapsed_instr / layer_steps * 1e6:.1f} us with per-launch events); "
+        f"{promos_timed} promotions in the timed pass; with one promotion per {P} steps "
+        f"{step_amortized * 1e6:.1f} us per layer step")
 
     res = {
         "metric": "decode-attn tokens/s (one layer: batch tokens per second of a layer decode step)",
@@ -322,6 +392,10 @@ def bench_decode(args, cfg_id, name, store=None, rope=False, overrides=None):
                    "early_factorization": bool(args.aux)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
+                     # the whole layer step (partial, merge and the gaps
+                     # between launches) against the same bytes
+                     "frac_step": nbytes.mean() / (elapsed / layer_steps) / 1e9 / HBM_PEAK_GBS,
+                     "frac_step_promotions_amortized": nbytes.mean() / step_amortized / 1e9 / HBM_PEAK_GBS,
                      "traffic": None if traffic is None else traffic["fetch"] + traffic["write"],
                      "kernel": ("decode_mfma_kernel (pkv_decode_partial)" if cfg["P"] == 64
                                 else "decode_valu_kernel (pkv_decode_partial)"),
@@ -332,8 +406,12 @@ def bench_decode(args, cfg_id, name, store=None, rope=False, overrides=None):
         "breakdown_us": {"decode_partial": durs.mean() * 1e6,
                          "partial_end_to_merge_end": merges.mean() * 1e6,
                          "promote_mean": float(np.mean(promos) * 1e6) if promos else None,
-                         "layer_step_with_events": elapsed_instr / layer_steps * 1e6,
-                         "promotions": len(promos)},
+                         "promotions_timed": len(promos),
+                         "promotions_in_value": promos_timed,
+                         "promote_amortized_per_step": t_promo / P * 1e6,
+                         "layer_step_promotions_amortized": step_amortized * 1e6,
+                         "layer_step_with_events": elapsed_instr / layer_steps * 1e6},
+        "ms_per_step_promotions_amortized": step_amortized * 1e3,
         "decode_effective_GBps": achieved,
         "pages_compressed_per_s": pages0 / t_prefill,
         "prefill_ms": t_prefill * 1e3,
@@ -345,10 +423,7 @@ def bench_decode(args, cfg_id, name, store=None, rope=False, overrides=None):
         # (524288 pages, r = 16), measured after the decode steps
         c5 = synth.CONFIGS[5]
         n_total = c5["layers"] * c5["Hkv"] * 2 * c5["pages_per_head"]
-        pool = compress_pool(args.distinct_pages, n_total)
-        Xp = to_dev(pool, "bf16")
-        X = Xp.repeat((n_total + len(pool) - 1) // len(pool), 1, 1)[:n_total].contiguous()
-        del Xp
+        X = compress_pool(n_total)
         cres = measure_compress(X, n_total, [c5["ranks"][1]], 3, 1)
         del X
         res["compress"] = {"workload": "batched-prefill-compression", "pages": n_total,
@@ -357,7 +432,7 @@ def bench_decode(args, cfg_id, name, store=None, rope=False, overrides=None):
     if args.cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")
         cb = cpu_baseline_decode(cfg, inp["K"], inp["V"], inp["q"], T0, store, freqs)
-        res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample", "one_core", "host")}
         res["cpu_baseline_svd_pages_per_s"] = cb["svd_pages_per_s"]
     return res
 
@@ -377,17 +452,16 @@ def compress_flops(r, P=64, d=128):
                 valu=(8 * P ** 3) // 3 + 2 * P * P * r)
 
 
-def compress_pool(n_distinct, n_total):
+def compress_pool(n_total):
+    """The batched-compression workload's n_total distinct pages, drawn on
+    the device (synth.compression_pool_device), as a bf16 device tensor."""
+    import torch
     import synth
-    path = os.path.join(CACHE_DIR, f"cfg5_pool{n_distinct}.npy")
-    os.makedirs(CACHE_DIR, exist_ok=True)
-    if os.path.exists(path):
-        return np.load(path, allow_pickle=False)
     t = time.time()
-    pool = synth.to_storage(synth.compression_pages(np.arange(n_distinct), n_total), "bf16")
-    np.save(path, pool)
-    log(f"generated {n_distinct} distinct pages in {time.time() - t:.1f}s")
-    return pool
+    X = synth.compression_pool_device(n_total, device="cuda:0").view(torch.bfloat16)
+    torch.cuda.synchronize()
+    log(f"drew {n_total} distinct pages on the device in {time.time() - t:.1f}s")
+    return X
 
 
 def measure_compress(X, n_total, ranks, steps, warmup):
@@ -425,18 +499,29 @@ def measure_compress(X, n_total, ranks, steps, warmup):
     return out
 
 
-def cpu_baseline_compress(pool, n_sample):
+def cpu_baseline_compress(X, n_sample):
     """The oracle's Jacobi SVD (double precision, OpenMP) on a sample of the
-    workload's pages -> pages/s.  The SVD cost does not depend on r."""
+    workload's pages -> pages/s, on all cores and on one core (a 256-page
+    share).  The SVD cost does not depend on r."""
+    import torch
     import oracle
     import synth
-    X64 = synth.storage_to_f64(pool[:n_sample], "bf16")
+    X64 = synth.storage_to_f64(X[:n_sample].view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
     t = time.perf_counter()
     oracle.svd_batch(X64)
     dt = time.perf_counter() - t
+
+    def single():
+        t0 = time.perf_counter()
+        oracle.svd_batch(X64[:256])
+        return 256 / (time.perf_counter() - t0)
+
     return dict(value=n_sample / dt, unit="pages/s", cores=int(oracle.num_threads()), kind="oracle",
                 sample=f"Jacobi SVD of the first {n_sample} pages of the workload's page pool "
-                       f"(same recipe: sigma_i = i^-1.2 spectrum plus 2% noise pages), {dt:.1f} s")
+                       f"(same recipe: sigma_i = i^-1.2 spectrum plus 2% noise pages), {dt:.1f} s",
+                one_core={"value": one_core(single), "unit": "pages/s",
+                          "sample": "Jacobi SVD of the first 256 of those pages on one core"},
+                host=host_cpu())
 
 
 def compress_summary(res, r0):
@@ -454,10 +539,7 @@ def bench_compress(args):
     import synth
     cfg = synth.CONFIGS[5]
     n_total = cfg["layers"] * cfg["Hkv"] * 2 * cfg["pages_per_head"]
-    pool = compress_pool(args.distinct_pages, n_total)
-    Xp = to_dev(pool, "bf16")
-    X = Xp.repeat((n_total + len(pool) - 1) // len(pool), 1, 1)[:n_total].contiguous()
-    del Xp
+    X = compress_pool(n_total)
     steps = max(1, min(args.steps, 8))
     res = measure_compress(X, n_total, cfg["ranks"], steps, max(1, min(args.warmup, 2)))
     r0 = cfg["ranks"][1]
@@ -466,15 +548,123 @@ def bench_compress(args):
         "value": res[r0]["pages_per_s"], "unit": "pages/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": res[r0]["ms"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in/out, f32 eigen-solve",
-        "data": f"synthetic: {len(pool)} distinct seeded pages tiled to {n_total}",
+        "data": f"synthetic: {n_total} distinct seeded pages drawn on the device",
         "config": {"workload": "batched-prefill-compression", "pages": n_total, "rank": r0,
                    "pages_per_s_by_rank": {r: m["pages_per_s"] for r, m in res.items()}},
         "roofline": compress_summary(res, r0),
     }
     if args.cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")
-        out["cpu_baseline"] = cpu_baseline_compress(pool, 4096)
+        out["cpu_baseline"] = cpu_baseline_compress(X, 4096)
     return out
+
+
+def bench_incremental(args):
+    """Workload 4: the Llama-3.1-8B-shaped layer (B = 8, 32 query heads, 8 KV
+    heads, r = 16, sink 64, window 128) from T = 8192, 512 decode steps; each
+    appends one token per (sequence, KV head) and every 64th promotes the page
+    leaving the window (128 page decompositions), then attends.  NL layer
+    caches are stepped in rotation (4 x 105-111 MB, above the 256 MB Infinity
+    Cache).  Timed twice from the same prefilled state: once with nothing but
+    the library calls inside the timed region (`value`), once with an event
+    after every layer step, which splits the steps into promotion and
+    non-promotion steps (the promotion overhead, cf. the pages' +0.18% TPOT,
+    Sec. 4.5 Table 4) and times each promotion's decomposition kernel."""
+    import torch
+    import synth
+    import long_context_decode_pkv_amd as pkv
+
+    cfg = dict(synth.CONFIGS[4])
+    B, Hq, Hkv, T0, n_steps, P = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], cfg["steps"], cfg["P"]
+    dt, NL = cfg["dtype"], args.layers
+    total = T0 + n_steps
+    inp = cached_inputs(4, total, workers=args.workers)
+    Kd, Vd = to_dev(inp["K"], dt), to_dev(inp["V"], dt)
+    K0, V0 = Kd[:, :, :T0].contiguous(), Vd[:, :, :T0].contiguous()
+    rows_k = [Kd[:, :, t].contiguous() for t in range(T0, total)]
+    rows_v = [Vd[:, :, t].contiguous() for t in range(T0, total)]
+    qs = [to_dev(synth.step_queries(4, t, B, Hq, cfg["d"], dt), dt) for t in range(n_steps)]
+    del Kd, Vd
+    caches = [pkv.Cache(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, rank_k=cfg["r_k"], rank_v=cfg["r_v"],
+                        sink=cfg["s"], window=cfg["w"], max_tokens=total, dtype=dt) for _ in range(NL)]
+    wss = [c.workspace(512) for c in caches]
+    out = torch.empty((B, Hq, cfg["d"]), dtype=torch.float32, device="cuda:0")
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def prefill():
+        for c in caches:
+            c.prefill(K0, V0)
+        torch.cuda.synchronize()
+
+    # warm-up (kernels loaded, clocks up), then the timed pass from T0
+    prefill()
+    for t in range(min(args.warmup, n_steps)):
+        for c, ws in zip(caches, wss):
+            c.step(rows_k[t], rows_v[t], qs[t], out=out, workspace=ws)
+    prefill()
+    t0 = time.perf_counter()
+    for t in range(n_steps):
+        for c, ws in zip(caches, wss):
+            c.step(rows_k[t], rows_v[t], qs[t], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # instrumented pass: the same 512 steps again
+    prefill()
+    marks = [ev() for _ in range(n_steps * NL + 1)]
+    promo = []  # (layer step index, decomposition events)
+    for e in marks:
+        e.record()
+    torch.cuda.synchronize()
+    marks[0].record()
+    k = 0
+    for t in range(n_steps):
+        for c, ws in zip(caches, wss):
+            T, nf, _ = c.state()
+            if (T + 1) // P - cfg["s"] // P - cfg["w"] // P > nf:
+                pair = (ev(), ev())
+                pkv.time_next_kernel(*pair)
+                promo.append((k, pair))
+            c.step(rows_k[t], rows_v[t], qs[t], out=out, workspace=ws)
+            k += 1
+            marks[k].record()
+    torch.cuda.synchronize()
+    durs = np.array([marks[i].elapsed_time(marks[i + 1]) * 1e-3 for i in range(n_steps * NL)])
+    is_promo = np.zeros(n_steps * NL, dtype=bool)
+    is_promo[[k for k, _ in promo]] = True
+    dec = np.array([a.elapsed_time(b) * 1e-3 for _, (a, b) in promo])
+    plain, with_p = durs[~is_promo], durs[is_promo]
+    overhead = with_p.mean() - plain.mean()
+    amortized = overhead * is_promo.sum() / durs.size
+    states = [(T0 + t, (T0 + t) // P - cfg["s"] // P - cfg["w"] // P) for t in range(n_steps)]
+    nbytes = float(np.mean([decode_bytes(cfg, B, Hkv, Hq, T, nf) for T, nf in states]))
+    step = elapsed / (n_steps * NL)
+    log(f"incremental: {n_steps} steps x {NL} layers from T={T0}: {step * 1e6:.1f} us per layer step; "
+        f"instrumented: plain steps {plain.mean() * 1e6:.1f} us, promotion steps {with_p.mean() * 1e6:.1f} us "
+        f"({is_promo.sum()} of {durs.size}), decomposition of {2 * B * Hkv} pages {dec.mean() * 1e6:.1f} us; "
+        f"promotion overhead {amortized / plain.mean() * 100:.2f}% per step")
+    return {
+        "metric": "decode-attn tokens/s (one layer: incremental decode steps with promotions)",
+        "value": B * n_steps * NL / elapsed, "unit": "tokens/s", "n_gpus": 1, "steps": n_steps,
+        "warmup": args.warmup, "ms_per_step": step * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 storage, f32 math",
+        "data": "synthetic (seeded generator, workload-4 recipe)",
+        "config": {"workload": "incremental-llama3.1-8b", "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": cfg["d"], "context_tokens": [T0, total], "page_len": P,
+                   "rank_k": cfg["r_k"], "rank_v": cfg["r_v"], "sink": cfg["s"], "window": cfg["w"],
+                   "layer_caches_rotated": NL,
+                   "step": "pkv_decode_step per layer: append, promotion when a page leaves the window, "
+                           "decode partial, merge"},
+        "roofline": {"bound": "hbm", "achieved": nbytes / step / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": nbytes / step / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "whole layer step (algorithmic bytes of its attention / step time)",
+                     "bytes_per_step": nbytes},
+        "breakdown_us": {"plain_step": plain.mean() * 1e6, "promotion_step": with_p.mean() * 1e6,
+                         "promotion_steps": int(is_promo.sum()), "steps": int(durs.size),
+                         "decomposition_kernel": float(dec.mean() * 1e6),
+                         "promotion_overhead_per_step": amortized * 1e6,
+                         "promotion_overhead_frac": amortized / plain.mean(),
+                         "instrumented_step": durs.mean() * 1e6},
+    }
 
 
 RAGGED_LENGTHS = [32768, 28672, 24576, 20480, 16384, 12288, 8192, 4096]
@@ -616,13 +806,12 @@ def main():
                              "llama3.1-8b-layer-int4", "qwen3-32b-layer-128k-prerope",
                              "llama3.1-8b-layer-prerope", "llama3.1-8b-layer-p32", "llama3.1-8b-layer-p32-prerope",
                              "llama3.1-8b-layer-p32-int4",
-                             "llama3.1-8b-ragged-batch",
+                             "llama3.1-8b-ragged-batch", "incremental",
                              "compress", "copy"])
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--workers", type=int, default=1)
     ap.add_argument("--layers", type=int, default=4,
                     help="independent layer caches decoded in rotation (defeats cache reuse)")
-    ap.add_argument("--distinct-pages", type=int, default=8192)
     ap.add_argument("--aux", action="store_true",
                     help="decode workloads: factorize completed window pages early on a second "
                          "stream (pkv_cache_set_aux_stream); measured slower on the 128K layer")
@@ -647,6 +836,8 @@ def main():
         res = bench_copy(args)
     elif args.workload == "llama3.1-8b-ragged-batch":
         res = bench_ragged_batch(args)
+    elif args.workload == "incremental":
+        res = bench_incremental(args)
     else:
         cfg_id = 2 if args.workload.startswith("llama3.1-8b-layer") else 3
         res = bench_decode(args, cfg_id, args.workload, "int4" if args.workload.endswith("-int4") else None,

@@ -1809,56 +1809,61 @@ __device__ inline float load_elem(const void* p, int64_t i, int dtype) {
   return ((const float*)p)[i];
 }
 
-// Eq. 5 across splits: one 256-thread workgroup per (sequence, query head),
-// arranged as 8 groups of 32 lanes; lane c4 of group grp owns channels
-// 4 c4 .. 4 c4 + 3 of the splits grp, grp + 8, ...  Every load of the merge
-// (the split maxima, the group's own split states and partial outputs, q and
-// the new key) is issued up front, so the kernel waits on memory about once:
-// one barrier publishes the global maximum (and the new token's score), each
-// group then weights its own splits, and a second barrier sums the 8 groups.
-constexpr int kMergeThreads = 256;
-constexpr int kMergeGroups = kMergeThreads / (kD / 4);
-constexpr int kMergePrefetch = 8;  // splits per group held in registers (n_split <= 64)
+// Eq. 5 across splits: one wavefront per (sequence, query head, quarter of
+// the channels), four per row, so a launch spreads over 4 B H_q workgroups.
+// Lane l = 8 s + c4 owns channels 32 qt + 4 c4 .. + 3 of the splits s, s + 8,
+// ...  Every load of the merge (the split maxima, the lane's own split states
+// and partial outputs, q and the new key) is issued up front.  The maximum,
+// the new token's score and the sums over splits are lane exchanges; there
+// is no LDS and no barrier.  Each of the row's four wavefronts forms the new
+// token's score from the whole q and k_new (lane l: channels l and l + 64, a
+// rotary pair), and writes its own 32 channels of the token into the page.
+constexpr int kMergeThreads = 64;
+constexpr int kMergeQuarters = 4;                 // wavefronts per row
+constexpr int kMergeCh = kD / kMergeQuarters;      // channels per wavefront
+constexpr int kMergeGroups = kMergeThreads / (kMergeCh / 4);  // split lanes: 8
+constexpr int kMergePrefetch = 8;  // splits per lane held in registers (n_split <= 64)
 
 template <class MA>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MA margs) {
   const MergeArgs& m = merge_common(margs);
-  __shared__ float sh_m[kMergeThreads / 64], sh_dot[kMergeThreads / 64];
-  __shared__ float4 sh_acc[kMergeGroups][kD / 4];
-  __shared__ float sh_l[kMergeGroups];
-  const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int grp = tid / (kD / 4), c4 = tid % (kD / 4);
+  const int64_t row = blockIdx.x / kMergeQuarters;
+  const int qt = blockIdx.x % kMergeQuarters;
+  const int lane = threadIdx.x;
+  const int grp = lane / (kMergeCh / 4), c4 = lane % (kMergeCh / 4);
+  const int ch0 = kMergeCh * qt + 4 * c4;  // this lane's first channel
   const int Hq = m.G * m.Hkv;
   const int hq = (int)(row % Hq);
   const int64_t seq = row / Hq;
   const int n_split = split_count(margs, seq);  // this row's states, m.n_split apart
   const float2* ml = (const float2*)(m.ws_ml + row * m.n_split * 2);
-  const float4* op = (const float4*)(m.ws_o + row * m.n_split * kD) + c4;
+  const float4* op = (const float4*)(m.ws_o + row * m.n_split * kD + ch0);
 
   // loads
   float qk = 0.f;
   const int64_t bh = seq * m.Hkv + hq / m.G;  // (sequence, KV head) of k_new / v_new
   const AppendDst& ad = append_dst(margs, seq);
-  if (m.k_new && tid < kD) {
-    float kk = load_elem(m.k_new, bh * kD + tid, m.dtype);
-    if (m.rope) {  // pair (c, c + d/2) of the new key, rotated at its position
-      const int mm = tid & (kD / 2 - 1);
-      const float other = load_elem(m.k_new, bh * kD + (tid ^ (kD / 2)), m.dtype);
+  if (m.k_new) {
+    const float k0 = load_elem(m.k_new, bh * kD + lane, m.dtype);
+    const float k1 = load_elem(m.k_new, bh * kD + lane + kD / 2, m.dtype);
+    float kr0 = k0, kr1 = k1;
+    if (m.rope) {  // pair (lane, lane + d/2) of the new key, rotated at its position
       float cs, sn;
-      rope_sincos(ad.app_page * ad.P + ad.app_row, m.rope_freq[mm], cs, sn);
-      kk = tid < kD / 2 ? __builtin_fmaf(-other, sn, kk * cs) : __builtin_fmaf(other, sn, kk * cs);
+      rope_sincos(ad.app_page * ad.P + ad.app_row, m.rope_freq[lane], cs, sn);
+      kr0 = __builtin_fmaf(-k1, sn, k0 * cs);
+      kr1 = __builtin_fmaf(k0, sn, k1 * cs);
     }
-    qk = load_elem(m.q, row * kD + tid, m.dtype) * kk;
+    qk = load_elem(m.q, row * kD + lane, m.dtype) * kr0 +
+         load_elem(m.q, row * kD + lane + kD / 2, m.dtype) * kr1;
   }
   float4 vnew = {0.f, 0.f, 0.f, 0.f};
-  if (m.k_new && tid < kD / 4) {
-    const int64_t vb = bh * kD + 4 * tid;
+  if (m.k_new && grp == 0) {
+    const int64_t vb = bh * kD + ch0;
     vnew = float4{load_elem(m.v_new, vb, m.dtype), load_elem(m.v_new, vb + 1, m.dtype),
                   load_elem(m.v_new, vb + 2, m.dtype), load_elem(m.v_new, vb + 3, m.dtype)};
   }
   float mx = -INFINITY;
-  for (int sp = tid; sp < n_split; sp += kMergeThreads) mx = fmaxf(mx, ml[sp].x);
+  for (int sp = lane; sp < n_split; sp += kMergeThreads) mx = fmaxf(mx, ml[sp].x);
   float2 own[kMergePrefetch];
   float4 ov[kMergePrefetch];
 #pragma unroll
@@ -1869,43 +1874,38 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MA margs) {
       ov[i] = op[(int64_t)sp * (kD / 4)];
     }
   }
-  // the new token goes into its dense page (one workgroup per (sequence, KV
-  // head)) and its table entry is set (one workgroup)
+  // the new token goes into its dense page (the wavefronts of one query head
+  // per (sequence, KV head), 32 channels each) and its table entry is set
+  // (one wavefront)
   if (m.k_new) {
-    if (hq % m.G == 0 && tid < kD) {
+    if (hq % m.G == 0 && lane < kMergeCh) {
+      const int c = kMergeCh * qt + lane;
       const int esz = m.dtype == PKV_BF16 ? 2 : 4;
       const int64_t bhp = append_pool_seq(margs, seq) * m.Hkv + hq / m.G;  // its pages
-      uint8_t* kd = ad.k_dst + bhp * ad.dst_bh_stride + ((int64_t)ad.app_row * kD + tid) * esz;
-      uint8_t* vd = ad.v_dst + bhp * ad.dst_bh_stride + ((int64_t)tid * ad.P + ad.app_row) * esz;
+      uint8_t* kd = ad.k_dst + bhp * ad.dst_bh_stride + ((int64_t)ad.app_row * kD + c) * esz;
+      uint8_t* vd = ad.v_dst + bhp * ad.dst_bh_stride + ((int64_t)c * ad.P + ad.app_row) * esz;
       if (esz == 2) {
-        *(uint16_t*)kd = ((const uint16_t*)m.k_new)[bh * kD + tid];
-        *(uint16_t*)vd = ((const uint16_t*)m.v_new)[bh * kD + tid];
+        *(uint16_t*)kd = ((const uint16_t*)m.k_new)[bh * kD + c];
+        *(uint16_t*)vd = ((const uint16_t*)m.v_new)[bh * kD + c];
       } else {
-        *(float*)kd = ((const float*)m.k_new)[bh * kD + tid];
-        *(float*)vd = ((const float*)m.v_new)[bh * kD + tid];
+        *(float*)kd = ((const float*)m.k_new)[bh * kD + c];
+        *(float*)vd = ((const float*)m.v_new)[bh * kD + c];
       }
     }
-    if (hq == 0 && tid == 0 && writes_table(margs, seq)) ad.table_w[ad.app_page] = ad.app_entry;
+    if (hq == 0 && qt == 0 && lane == 0 && writes_table(margs, seq)) ad.table_w[ad.app_page] = ad.app_entry;
   }
 
-  // global maximum and the new token's score (log2 units)
+  // global maximum and the new token's score (log2 units), in every lane
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     mx = fmaxf(mx, __shfl_xor(mx, o));
     qk += __shfl_xor(qk, o);
   }
-  if (lane == 0) {
-    sh_m[wv] = mx;
-    sh_dot[wv] = qk;
-  }
-  __syncthreads();
-  float M = -INFINITY, s_new = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kMergeThreads / 64; ++w) M = fmaxf(M, sh_m[w]);
-  if (m.k_new) s_new = (sh_dot[0] + sh_dot[1]) * m.qscale;
+  float M = mx, s_new = -INFINITY;
+  if (m.k_new) s_new = qk * m.qscale;
   M = fmaxf(M, s_new);
 
-  // this group's splits, weighted e^(m_s - M) (empty split: weight 0)
+  // this lane's splits, weighted e^(m_s - M) (empty split: weight 0)
   float4 acc = {0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
   auto add = [&](float2 st, float4 v) {
@@ -1921,21 +1921,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MA margs) {
     if (grp + kMergeGroups * i < n_split) add(own[i], ov[i]);
   for (int sp = grp + kMergeGroups * kMergePrefetch; sp < n_split; sp += kMergeGroups)
     add(ml[sp], op[(int64_t)sp * (kD / 4)]);
-  sh_acc[grp][c4] = acc;
-  if (c4 == 0) sh_l[grp] = lsum;
-  __syncthreads();
-  if (tid < kD / 4) {
-    float4 t = sh_acc[0][tid];
-    float L = sh_l[0];
+  // sum over the 8 split lanes of each channel group (lanes c4, c4 + 8, ...)
 #pragma unroll
-    for (int gi = 1; gi < kMergeGroups; ++gi) {
-      const float4 u = sh_acc[gi][tid];
-      t.x += u.x;
-      t.y += u.y;
-      t.z += u.z;
-      t.w += u.w;
-      L += sh_l[gi];
-    }
+  for (int o = kMergeCh / 4; o < kMergeThreads; o <<= 1) {
+    acc.x += __shfl_xor(acc.x, o);
+    acc.y += __shfl_xor(acc.y, o);
+    acc.z += __shfl_xor(acc.z, o);
+    acc.w += __shfl_xor(acc.w, o);
+    lsum += __shfl_xor(lsum, o);
+  }
+  if (grp == 0) {
+    float4 t = acc;
+    float L = lsum;
     if (m.k_new) {
       const float w_new = exp2f(s_new - M);
       t.x += w_new * vnew.x;
@@ -1945,7 +1942,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MA margs) {
       L += w_new;
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    ((float4*)(m.out + row * kD))[tid] = float4{t.x * inv, t.y * inv, t.z * inv, t.w * inv};
+    *(float4*)(m.out + row * kD + ch0) = float4{t.x * inv, t.y * inv, t.z * inv, t.w * inv};
   }
 }
 
@@ -2055,8 +2052,8 @@ int decode_batch_splits(const CacheGeom& g, const int64_t* T, int n, int* ns) {
 hipError_t launch_merge(const CacheGeom& g, const AttnJob& job, hipStream_t stream) {
   MergeArgs m = merge_args(g, job);
   if (job.k_new) m.app = append_dst_of(g, job);
-  hipLaunchKernelGGL(merge_kernel<MergeArgs>, dim3((unsigned)((int64_t)g.B * g.Hq)), dim3(kMergeThreads), 0,
-                     stream, m);
+  hipLaunchKernelGGL(merge_kernel<MergeArgs>, dim3((unsigned)((int64_t)g.B * g.Hq * kMergeQuarters)),
+                     dim3(kMergeThreads), 0, stream, m);
   return hipGetLastError();
 }
 
@@ -2069,7 +2066,7 @@ hipError_t launch_merge_batch(const CacheGeom* gs, int n, const AttnJob& job, co
     x.app[i] = job.k_new ? append_dst_of(gs[i], apps[i]) : AppendDst{nullptr, nullptr, 0, nullptr, -1, -1, 0, gs[i].P};
     x.ns[i] = ns[i];
   }
-  hipLaunchKernelGGL(merge_kernel<MergeBatchArgs>, dim3((unsigned)((int64_t)n * gs[0].Hq)),
+  hipLaunchKernelGGL(merge_kernel<MergeBatchArgs>, dim3((unsigned)((int64_t)n * gs[0].Hq * kMergeQuarters)),
                      dim3(kMergeThreads), 0, stream, x);
   return hipGetLastError();
 }
