@@ -236,7 +236,10 @@ int32_t pkv_cache_state(const pkv_cache* cache, int64_t* T, int64_t* n_fact, int
  * The eigen-solve, one page per wavefront: r <= 32 (every 32-token page):
  * Householder reduction of G to tridiagonal form, bisection for the r
  * largest eigenvalues, one eigenvector each from a twisted factorization,
- * back-transformation; a 32-token page is solved on its own 32 x 32 Gram
+ * back-transformation, then one Cholesky QR pass that makes the r columns
+ * orthonormal (and, for eigenvalues the bisection cannot tell apart, such
+ * as an exactly repeated singular value, refilled columns refined by
+ * orthogonal iteration); a 32-token page is solved on its own 32 x 32 Gram
  * matrix.  r > 32: cyclic Jacobi rotations of G.
  * Outputs (device, row-major, `out_dtype`): Lf [n_pages][P][r],
  * Rf [n_pages][r][d]; sigma [n_pages][r] float32 (may be NULL).  Rows with

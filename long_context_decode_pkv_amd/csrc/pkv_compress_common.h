@@ -164,11 +164,11 @@ struct FactorDst {
       lf = job.lf;
     }
   }
-  __device__ int64_t rf_idx(int i, int c) const {
+  __device__ __forceinline__ int64_t rf_idx(int i, int c) const {
     if (!packed) return n * (int64_t)r * kD + (int64_t)i * kD + c;
     return off_rf(kind, pd, i, c);
   }
-  __device__ int64_t lf_idx(int j, int i) const {
+  __device__ __forceinline__ int64_t lf_idx(int j, int i) const {
     if (!packed) return n * (int64_t)P * r + (int64_t)j * r + i;
     return off_lf(kind, pd, j, i);
   }

@@ -30,7 +30,15 @@
 //      factorization of T - lambda I: forward pivots d+_i, backward pivots
 //      d-_i, twist index k = argmin |d+_k + d-_k - (a_k - lambda)|, z_k = 1 and
 //      the two one-sided recurrences outward from k.
-//   5. Q_r = Q_H Z, R = Q_r^T X on the matrix cores in fp32, sigma_i = ||R_i||,
+//   5'. Q_r = Q_H Z is orthonormalized: the twisted vectors of close
+//      eigenvalues are orthogonal only to about eps ||T|| / gap, so one
+//      Cholesky QR pass (W = Q_r^T Q_r on the matrix cores, its Cholesky
+//      factor in LDS, a forward solve per row) restores orthonormality.
+//      Eigenvalues the bisection cannot tell apart (an exactly repeated
+//      singular value, a null space) give one vector several times; then the
+//      dead columns are refilled with fixed pseudo-random vectors and Q_r is
+//      refined by 8 steps of orthogonal iteration Q <- orth(X (X^T Q)).
+//   5. R = Q_r^T X on the matrix cores in fp32, sigma_i = ||R_i||,
 //      Lf = Q_r diag(sigma), Rf = diag(1/sigma) R (zero where sigma = 0), rounded
 //      nearest-even to the output dtype.  INT4 caches (Sec. 4.3) instead
 //      store Lt = Q_r diag(sigma^(1/2)) and Rt = diag(sigma^(-1/2)) R as
@@ -294,6 +302,216 @@ __device__ __forceinline__ void twisted_vector(TriShared& sh, float lam, float p
   for (int i = 0; i < N; ++i) {
     const float zi = Zc[i * kZs];
     if (writer) Zc[i * kZs] = ok ? zi * inv : 0.f;
+  }
+}
+
+// 5a'. One Cholesky QR pass over the columns of Q_r (N x r, lane p holds row
+// p in qr[], LDS sh.u.Z the same rows): W = Q_r^T Q_r on the matrix cores in
+// fp32, W = L L^T in LDS, then each row solves y L^T = q (forward
+// substitution), so the new columns are orthonormal to about eps times the
+// old columns' condition number squared.  A pivot below 2^-20 of W's largest
+// diagonal marks a dependent column, which becomes zero (bit j of `dead`).
+// The result goes back to qr[] and to sh.u.Z.  Returns (wave-uniform)
+// whether some pivot was below 1/4 of W's largest diagonal, i.e. some column
+// was nearly dependent on the ones before it.
+constexpr int kWs = 36;  // LDS row stride of W and L (floats; 16-byte aligned rows)
+
+template <int N>
+__device__ __forceinline__ bool orthonormalize(TriShared& sh, float (&qr)[kTriMaxRank], int r, int lane,
+                                               uint32_t& dead) {
+  const int c = lane & 15, q = lane >> 4;
+  const int RT16 = (r + 15) / 16;
+  // W tiles (ti <= tj) on the matrix cores; lane l holds W[16 ti + 4 q + v][16 tj + c]
+  floatx4 Wt[3];
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const int ti = t == 2 ? 1 : 0, tj = t == 0 ? 0 : 1;
+    Wt[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (tj < RT16) {
+#pragma unroll 4
+      for (int s = 0; s < N / 4; ++s) {
+        const float av = sh.u.Z[(4 * s + q) * kZs + 16 * ti + c];
+        const float bv = sh.u.Z[(4 * s + q) * kZs + 16 * tj + c];
+        Wt[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, Wt[t], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();  // Z is read; W takes its place (qr[] keeps Q_r)
+  float* W = sh.u.Z;
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const int ti = t == 2 ? 1 : 0, tj = t == 0 ? 0 : 1;
+    if (tj < RT16) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = 16 * ti + 4 * q + v, jj = 16 * tj + c;
+        W[i * kWs + jj] = Wt[t][v];
+        W[jj * kWs + i] = Wt[t][v];
+      }
+    }
+  }
+  __syncthreads();
+  // Cholesky, right-looking, in LDS: lane (i, h) = (lane % 32, lane / 32)
+  // updates row i's columns 16 h .. 16 h + 15; column k of L goes through
+  // sh.xrow, and the lane whose chunk holds column k writes it into W
+  const float dmax = wave_reduce<1>(lane < r ? W[lane * kWs + lane] : 0.f);
+  const int i = lane & 31, h = lane >> 5;
+  bool weak = false;
+  dead = 0;
+  for (int k = 0; k < r; ++k) {
+    const float piv = W[k * kWs + k];
+    const bool live = piv > 0x1p-20f * dmax;
+    weak |= piv < 0.25f * dmax;
+    dead |= live ? 0u : 1u << k;
+    const float lkk = live ? __builtin_amdgcn_sqrtf(piv) : 0.f;
+    const float inv = live ? __builtin_amdgcn_rcpf(lkk) : 0.f;
+    if (h == 0) sh.xrow[i] = i < r ? (i == k ? lkk : (i > k ? W[i * kWs + k] * inv : 0.f)) : 0.f;
+    __syncthreads();
+    if (i >= k && i < r) {
+      const float lik = sh.xrow[i];
+#pragma unroll
+      for (int jc = 0; jc < 4; ++jc) {
+        const int j0 = 16 * h + 4 * jc;
+        if (j0 + 3 >= k && j0 <= i) {
+          float4 wv = *(const float4*)&W[i * kWs + j0];
+          const float4 lv = *(const float4*)&sh.xrow[j0];
+          float* wp = &wv.x;
+          const float* lp = &lv.x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = j0 + e;
+            wp[e] = j == k ? lik : (j > k && j <= i ? fmaf(-lik, lp[e], wp[e]) : wp[e]);
+          }
+          *(float4*)&W[i * kWs + j0] = wv;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // y L^T = q: y_j = (q_j - sum_{i<j} L[j][i] y_i) / L[j][j]; dead columns stay zero
+#pragma unroll
+  for (int j = 0; j < kTriMaxRank; ++j) {
+    if (j < r) {
+      float acc = qr[j];
+#pragma unroll
+      for (int ic = 0; ic < kTriMaxRank / 4; ++ic) {
+        if (4 * ic < j) {
+          const float4 l4 = *(const float4*)&W[j * kWs + 4 * ic];
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * ic + e < j) acc = fmaf(-lv[e], qr[4 * ic + e], acc);
+        }
+      }
+      const float ljj = W[j * kWs + j];
+      qr[j] = ljj > 0.f ? acc * __builtin_amdgcn_rcpf(ljj) : 0.f;
+    }
+  }
+  __syncthreads();  // L is read; Q_r goes back to Z
+#pragma unroll
+  for (int jc = 0; jc < kTriMaxRank / 4; ++jc) {
+    if (4 * jc < r)
+      *(float4*)&sh.u.Z[lane * kZs + 4 * jc] = float4{qr[4 * jc], qr[4 * jc + 1], qr[4 * jc + 2], qr[4 * jc + 3]};
+  }
+  __syncthreads();
+  return __ballot(weak) != 0;
+}
+
+// Y = X (X^T Q) = G Q for the columns of Q in sh.u.Z (N rows, r columns), on
+// the matrix cores in fp32 (the bf16 page enters exactly): V = X^T Q is formed
+// 16 channels x 16 columns at a time in LDS (the padding columns 32..35 of
+// sh.u.Z, 256 floats) and folded into Y right away, so G itself is never
+// stored.  Y replaces Q in sh.u.Z and in qr[] (lane p: row p).
+template <typename Elem, int N>
+__device__ __forceinline__ void gram_times(TriShared& sh, const Elem* X, int trans, int P, float (&qr)[kTriMaxRank],
+                                           int r, int lane) {
+  const int c = lane & 15, q = lane >> 4;
+  const int RT16 = (r + 15) / 16;
+  // V chunk [16 channels][16 columns]: element k at Z[k / 4][32 + k % 4]
+  auto buf = [&sh](int k) -> float& { return sh.u.Z[(k >> 2) * kZs + kTriMaxRank + (k & 3)]; };
+  floatx4 Y[4][2];
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti) Y[ti][0] = Y[ti][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int mc = 0; mc < kD / 16; ++mc) {
+#pragma unroll
+    for (int th = 0; th < 2; ++th) {
+      if (th < RT16) {
+        floatx4 V = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int s = 0; s < N / 4; ++s) {  // V[c][j] = sum_p X[p][c] Q[p][j]
+          const float av = page_elem(X, trans, P, 4 * s + q, 16 * mc + c);
+          const float bv = sh.u.Z[(4 * s + q) * kZs + 16 * th + c];
+          V = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, V, 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) buf((4 * q + v) * 16 + c) = V[v];
+        __syncthreads();
+#pragma unroll
+        for (int ti = 0; ti < N / 16; ++ti) {  // Y[p][j] += sum_{c in chunk} X[p][c] V[c][j]
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const float av = page_elem(X, trans, P, 16 * ti + c, 16 * mc + 4 * s + q);
+            const float bv = buf((4 * s + q) * 16 + c);
+            Y[ti][th] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, Y[ti][th], 0, 0, 0);
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+#pragma unroll
+  for (int ti = 0; ti < N / 16; ++ti) {
+#pragma unroll
+    for (int th = 0; th < 2; ++th) {
+      if (th < RT16) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sh.u.Z[(16 * ti + 4 * q + v) * kZs + 16 * th + c] = Y[ti][th][v];
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kTriMaxRank; ++j) qr[j] = j < r && lane < N ? sh.u.Z[lane * kZs + j] : 0.f;
+}
+
+// Kept eigenvalues that the bisection could not tell apart (a cluster within
+// rounding: an exactly repeated singular value, or a null space) give the
+// same twisted vector more than once, and the Cholesky QR pass leaves such
+// columns dead or nearly dependent.  The dead columns are refilled with
+// fixed pseudo-random vectors and Q_r is refined by orthogonal iteration,
+// Q <- orth(G Q): a column that is already an eigenvector stays (up to
+// rounding), and a refilled column converges to the largest eigen-direction
+// not yet held by the columns before it -- the missing copies of the cluster
+// (or, beyond the page's rank, a direction with sigma ~ 0).
+constexpr int kRefineSteps = 8;
+
+__device__ __forceinline__ float refill_value(int row, int col) {
+  uint32_t x = (uint32_t)row * 0x9E3779B1u ^ (uint32_t)(col + 1) * 0x85EBCA77u;
+  x ^= x >> 15;
+  x *= 0x2C1B3C6Du;
+  x ^= x >> 12;
+  return (float)(int)(x & 0xFFFFu) * (1.f / 32768.f) - 1.f;  // in [-1, 1)
+}
+
+template <typename Elem, int N>
+__device__ __forceinline__ void orthonormal_columns(TriShared& sh, const Elem* X, int trans, int P,
+                                                    float (&qr)[kTriMaxRank], int r, int lane) {
+  uint32_t dead = 0;
+  const bool weak = orthonormalize<N>(sh, qr, r, lane, dead);
+  if (!weak && !dead) return;  // wave-uniform
+#pragma unroll
+  for (int j = 0; j < kTriMaxRank; ++j)
+    if (j < r && ((dead >> j) & 1u) && lane < N) qr[j] = refill_value(lane, j);
+#pragma unroll
+  for (int jc = 0; jc < kTriMaxRank / 4; ++jc) {
+    if (4 * jc < r)
+      *(float4*)&sh.u.Z[lane * kZs + 4 * jc] = float4{qr[4 * jc], qr[4 * jc + 1], qr[4 * jc + 2], qr[4 * jc + 3]};
+  }
+  __syncthreads();
+  orthonormalize<N>(sh, qr, r, lane, dead);
+  for (int it = 0; it < kRefineSteps; ++it) {
+    gram_times<Elem, N>(sh, X, trans, P, qr, r, lane);
+    orthonormalize<N>(sh, qr, r, lane, dead);
   }
 }
 
@@ -585,6 +803,10 @@ __device__ __forceinline__ void compress_tri_one(const J& jobs, int64_t n, TriSh
       *(float4*)&sh.u.Z[lane * kZs + 4 * jc] = float4{qr[4 * jc], qr[4 * jc + 1], qr[4 * jc + 2], qr[4 * jc + 3]};
   }
   __syncthreads();
+  // 5a'. Orthonormalize Q_r (the twisted vectors of close eigenvalues are
+  // orthogonal only to about eps ||T|| / gap), and resolve clusters the
+  // bisection could not split
+  orthonormal_columns<Elem, N>(sh, X, pr.trans, pr.P, qr, r, lane);
 
   // 5b. R = Q_r^T X in fp32 on the matrix cores: lane (ci, q) holds
   // R[16 mi + 4 q + v][16 mc + ci]

@@ -18,7 +18,7 @@ from gpu_common import require_gpu, to_dev, to_f64
 pytestmark = pytest.mark.gpu
 
 
-def _check(Xs, dtype, r, out_dtype, label):
+def _check(Xs, dtype, r, out_dtype, label, check_sigma=True):
     """Xs: stored pages (n, 64, 128) numpy; returns worst ratios."""
     import torch
     require_gpu()
@@ -39,6 +39,8 @@ def _check(Xs, dtype, r, out_dtype, label):
     print(f"[compress {label} r={r} out={out_dtype}] worst err/bound = {worst:.4f} "
           f"max (e-opt)/opt = {np.max((err - opt) / np.maximum(opt, 1e-300)):.3e}")
     assert np.all(err <= bound), (label, r, out_dtype, worst)
+    if not check_sigma:
+        return worst
     # singular values agree with the oracle's for well-separated ranks
     sg = sig.cpu().numpy().astype(np.float64)
     dev = np.abs(sg - S[:, :r]) - (2e-3 * S[:, :r] + 1e-5 * S[:, :1])
@@ -114,6 +116,55 @@ def test_compress_full_rank_reconstructs():
     X64 = Xs.astype(np.float64)
     err = np.sqrt(((X64 - to_f64(Lf) @ to_f64(Rf)) ** 2).sum(axis=(1, 2)))
     assert np.all(err <= 1e-5 * np.sqrt((X64 ** 2).sum(axis=(1, 2))))
+
+
+def _tied_pages(n, seed):
+    """Pages with exactly repeated singular values, exact in bf16: X = A diag(s) B
+    with A a row-permuted, sign-flipped 64 x 64 Hadamard matrix, B the first
+    64 rows of a column-signed 128 x 128 Hadamard matrix and s = (4 x 8,
+    2 x 16, 1 x 40).  Entries are integers of magnitude <= 104; the singular
+    values are 8 sqrt(128) s, in three tied groups."""
+    from scipy.linalg import hadamard
+    g = np.random.default_rng(seed)
+    s = np.concatenate([np.full(8, 4.0), np.full(16, 2.0), np.full(40, 1.0)])
+    H64, H128 = hadamard(64).astype(np.float64), hadamard(128).astype(np.float64)
+    out = []
+    for _ in range(n):
+        A = H64[g.permutation(64)] * g.choice([-1.0, 1.0], 64)[:, None]
+        B = H128[g.permutation(128)[:64]] * g.choice([-1.0, 1.0], 128)[None, :]
+        out.append((A * s) @ B)
+    X = np.stack(out)
+    assert np.abs(X).max() <= 104 and np.all(X == np.rint(X))
+    return X
+
+
+@pytest.mark.parametrize("r", [8, 12, 16, 24, 32])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_compress_exactly_tied_singular_values(r, out):
+    """Error-only (the truncation inside a tied group is not unique): the
+    kept columns must stay orthonormal across each group, so a rank-r
+    truncation reaches the optimal error whatever the cut (r = 8 and 24 cut
+    between groups, 12, 16 and 32 inside one)."""
+    X = _tied_pages(12, 7)
+    Xs = synth.to_storage(X, "bf16")
+    assert np.array_equal(synth.storage_to_f64(Xs, "bf16"), X)
+    _check(Xs, "bf16", r, out, "tied sigma", check_sigma=False)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("r", [8, 16, 32])
+def test_compress_crowded_spectrum(dt, r):
+    """Kept singular values 1e-4 apart (relative) on Haar factors: the
+    eigenvectors of such a cluster come out orthogonal only after the kept
+    columns are orthonormalized; the literal bound on float32 output."""
+    g = np.random.default_rng(100 + r)
+    n = 12
+    U = synth.haar_columns(g.standard_normal((n, 64, 64)))
+    W = synth.haar_columns(g.standard_normal((n, 128, 64)))
+    s = 1.0 - 1e-4 * np.arange(64)
+    s[40:] *= 1e-2  # a clear drop after the first 40
+    X = (U * s) @ np.swapaxes(W, -1, -2)
+    _check(synth.to_storage(X, dt), dt, r, "f32", f"crowded {dt}", check_sigma=False)
 
 
 def test_compress_zero_page():
