@@ -151,10 +151,12 @@ def test_batch_errors():
     assert ei.value.status == 3
 
 
-def _step_twins(cfg_id, lengths, steps, kv_heads=2, store=None, rope=None, aux=False, w=None):
+def _step_twins(cfg_id, lengths, steps, kv_heads=2, store=None, rope=None, aux=False, w=None, headroom=0):
     """Two identical sets of caches (one per length) with `steps` further
     tokens per sequence: set a steps through pkv_decode_step_batch, set b
-    through pkv_decode_step per cache."""
+    through pkv_decode_step per cache.  `headroom` tokens of capacity beyond
+    the run let the pages completed during it leave the window (a window
+    page is factorized early only if it can leave within capacity)."""
     import torch
     seqs, A, Bs = [], [], []
     for i, T in enumerate(lengths):
@@ -163,7 +165,7 @@ def _step_twins(cfg_id, lengths, steps, kv_heads=2, store=None, rope=None, aux=F
         Kd = to_dev(np.ascontiguousarray(d["K"][:, :, 64 * i:]), dt)
         Vd = to_dev(np.ascontiguousarray(d["V"][:, :, 64 * i:]), dt)
         for group in (A, Bs):
-            c = make_cache(d, max_tokens=T + steps, store=store, w=w)
+            c = make_cache(d, max_tokens=T + steps + headroom, store=store, w=w)
             if rope is not None:
                 c.set_key_rope(rope)
             c.prefill(Kd[:, :, :T].contiguous(), Vd[:, :, :T].contiguous())
@@ -181,23 +183,60 @@ def _step_twins(cfg_id, lengths, steps, kv_heads=2, store=None, rope=None, aux=F
     return seqs, A, Bs, d
 
 
-def _run_step_twins(cfg_id, lengths, steps, n_split=4, **kw):
+def _run_step_twins(cfg_id, lengths, steps, n_split=4, expect_early=False, **kw):
+    """expect_early: the batched caches with an aux stream must factorize
+    completed window pages early -- a page's factor slot is written by the
+    step that completes the page, before the page leaves the window, and
+    holds after the promotion exactly what it held then -- and at least one
+    such page must leave the window during the run."""
     import torch
     require_gpu()
     seqs, A, Bs, d = _step_twins(cfg_id, lengths, steps, **kw)
     dt = d["cfg"]["dtype"]
     n, Hq = len(lengths), d["Hq"]
     ws = pkv.batch_workspace(A, n_split)
+    aux = kw.get("aux", False)
+    mask = list(aux) if isinstance(aux, (list, tuple)) else [bool(aux)] * n
+    P, n_s, n_w = 64, A[0].layout["n_sink_slots"], A[0].layout["n_ring_slots"] - 1
+    early = {}  # (cache, slot) -> (slot before the completing step, right after it)
+    if expect_early:
+        # factor slots not yet written get a sentinel (the allocator may hand
+        # out a buffer that already holds these very factors)
+        for c in A:
+            L, nf = c.layout, c.state()[1]
+            for h in range(c.shape.n_kv_heads):
+                lo = L["factors"] + (h * L["max_fact_pages"] + nf) * L["factor_page_bytes"]
+                hi = L["factors"] + (h + 1) * L["max_fact_pages"] * L["factor_page_bytes"]
+                c.buffer[lo:hi].fill_(0xFF)
     for t in range(steps):
         k = torch.stack([Kd[0, :, T + t] for Kd, _, T in seqs]).contiguous()
         v = torch.stack([Vd[0, :, T + t] for _, Vd, T in seqs]).contiguous()
         q = to_dev(synth.step_queries(cfg_id, t, n, Hq, 128, dt), dt)
+        watch = []
+        if expect_early:
+            torch.cuda.synchronize()
+            for i, c in enumerate(A):
+                T1 = c.state()[0] + 1
+                p = T1 // P - 1  # the page this step completes
+                if mask[i] and n_w > 0 and T1 % P == 0 and p >= n_s and p - n_s < c.layout["max_fact_pages"]:
+                    watch.append((i, p - n_s, c.factor_part(0, 0, p - n_s, pkv.KEYS).clone()))
         oa = pkv.step_batch(A, k, v, q, n_split=n_split, workspace=ws)
         for i, c in enumerate(Bs):
             ob = c.step(k[i:i + 1].contiguous(), v[i:i + 1].contiguous(), q[i:i + 1].contiguous(), n_split=n_split)
             torch.cuda.synchronize()
             assert torch.equal(oa[i:i + 1], ob), (t, i)
+        for i, f, before in watch:  # the aux stream's work is done (device synchronized)
+            assert A[i].state()[1] <= f, "the completed page must still be in the window"
+            early[(i, f)] = (before, A[i].factor_part(0, 0, f, pkv.KEYS).clone())
     torch.cuda.synchronize()
+    if expect_early:
+        left = [(i, f) for (i, f) in early if A[i].state()[1] > f]
+        assert left, "no early-factorized page left the window during the run"
+        for i, f in left:
+            before, after_step = early[(i, f)]
+            assert not torch.equal(before, after_step), ("slot not written early", i, f)
+            assert torch.equal(after_step, A[i].factor_part(0, 0, f, pkv.KEYS)), ("slot changed at promotion", i, f)
+        print(f"[early factorization] {len(left)} early-factorized pages left the window during the run")
     for a, b in zip(A, Bs):
         assert a.state() == b.state()
         T, nf, _ = a.state()
@@ -210,17 +249,25 @@ def _run_step_twins(cfg_id, lengths, steps, n_split=4, **kw):
     return A
 
 
+# steps and capacity of the aux-stream cases: early-factorized pages (those
+# completed during the run) leave the window inside it, (n_w + 1) P = 192
+# tokens after completing
+EARLY = dict(steps=230, headroom=192, expect_early=True)
+
+
 @pytest.mark.parametrize("label,cfg_id,kw", [
     ("bf16", 2, {}),
     ("int4", 2, dict(store="int4")),
     ("pre-RoPE", 2, dict(rope=synth.rope_inv_freq(5e5))),
-    ("aux stream", 2, dict(aux=True)),
+    ("aux stream", 2, dict(aux=True, **EARLY)),
     ("fp32", 1, dict(kv_heads=1)),
 ])
 def test_step_batch_equals_per_cache_steps(label, cfg_id, kw):
     # an empty cache, one in the sink, and caches whose pages complete and
     # leave the window at different steps
-    _run_step_twins(cfg_id, [0, 5, 64 * 3 + 60, 64 * 10 + 63, 64 * 20 + 1], 70, **kw)
+    kw = dict(kw)
+    steps = kw.pop("steps", 70)
+    _run_step_twins(cfg_id, [0, 5, 64 * 3 + 60, 64 * 10 + 63, 64 * 20 + 1], steps, **kw)
 
 
 @pytest.mark.parametrize("label,cfg_id,kw", [
@@ -229,14 +276,16 @@ def test_step_batch_equals_per_cache_steps(label, cfg_id, kw):
     ("pre-RoPE", 2, dict(rope=synth.rope_inv_freq(5e5))),
     # caches with an aux stream only wait for their early factorization; the
     # others share the one decomposition launch
-    ("mixed aux", 2, dict(aux=[True, False, True, False])),
+    ("mixed aux", 2, dict(aux=[True, False, True, False], **EARLY)),
     # every cache on one aux stream: their early factorizations share a launch
-    ("aux together", 2, dict(aux=True)),
+    ("aux together", 2, dict(aux=True, **EARLY)),
 ])
 def test_step_batch_promotes_together(label, cfg_id, kw):
     # every cache completes a page at the same steps, so the pages leaving the
     # windows are decomposed by one launch (which also sets their entries)
-    _run_step_twins(cfg_id, [64 * 5 + 40, 64 * 9 + 40, 64 * 3 + 40, 64 * 12 + 40], 90, **kw)
+    kw = dict(kw)
+    steps = kw.pop("steps", 90)
+    _run_step_twins(cfg_id, [64 * 5 + 40, 64 * 9 + 40, 64 * 3 + 40, 64 * 12 + 40], steps, **kw)
 
 
 def test_step_batch_without_window():

@@ -323,8 +323,8 @@ def test_classification_workload_counts(oracle):
 
 
 def test_classification_default_dense_region(oracle):
-    """Sec. 4.1 default: one 32-token sink page, the most recently completed
-    page and the current incomplete page stay dense."""
+    """PuzzleKV, Sec. 4.1 (default dense region): a 32-token sink page, the
+    last page to complete and the page being filled are kept uncompressed."""
     gold = json.load(open(GOLDEN))["default_dense_region"]
     P = gold["P"]
     cls, slot = oracle.classify(10 * P + 5, P, gold["sink_tokens"], gold["window_completed_pages"] * P)
