@@ -114,10 +114,43 @@ __device__ __forceinline__ float wave_reduce(float x) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 63));
 }
 
-// 1. G into the row registers: lane i gets G[i][0..63].
+// 1. G into the row registers: lane i gets G[i][0..63].  bf16 pages: a
+// lane's operand chunks (rows 16 t + c, channels 32 ks + 8 q .. + 7) are the
+// same for every tile, as A and as B operand, so the page is loaded once --
+// 16 independent 16-byte loads, one memory latency -- and the 16 tiles run
+// from registers.
 template <typename Elem>
 __device__ __forceinline__ void gram_rows(const Elem* X, int trans, int P, TriShared& sh, float (&g)[kP], int lane) {
   const int c = lane & 15, q = lane >> 4;
+  if constexpr (sizeof(Elem) == 2) {
+    bf16x8 op[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        op[t][ks] = 16 * t < P ? row8((const uint16_t*)X, trans, P, 16 * t + c, 32 * ks + 8 * q) : bf16x8{};
+    }
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta) {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (16 * ta < P && 16 * tb < P) {  // tiles in the padding rows of a short page are zero
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op[ta][ks], op[tb][ks], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sh.u.band[(4 * q + v) * kLd + 16 * tb + c] = acc[v];
+      }
+      __syncthreads();
+      if (q == ta) {
+#pragma unroll
+        for (int j = 0; j < kP; ++j) g[j] = sh.u.band[c * kLd + j];
+      }
+      __syncthreads();
+    }
+    return;
+  }
   for (int ta = 0; ta < 4; ++ta) {
     for (int tb = 0; tb < 4; ++tb) {
       __builtin_amdgcn_sched_barrier(0);
@@ -184,24 +217,23 @@ __device__ __forceinline__ void tridiagonalize(TriShared& sh, float (&g)[kP], fl
     const float pi = lane > k ? tau * pacc : 0.f;
     const float K = 0.5f * tau * wave_reduce<0>(pi * vi);
     const float wi = fmaf(-K, vi, pi);
-    sh.w[lane] = wi;
-    __syncthreads();
-    // G <- G - v w^T - w v^T ; Q_H <- Q_H - tau (Q_H v) v^T
+    // G <- G - v w^T - w v^T ; Q_H <- Q_H - tau (Q_H v) v^T.  v_j and w_j
+    // are wave-uniform: read from their lanes into scalar registers
+    // (v_readlane) rather than broadcast through LDS, whose data return
+    // (1 KB per 16-byte read of a wave) the workgroups of a CU share.
     const float tq = tau * tacc;
 #pragma unroll
     for (int jc = 0; jc < N / 4; ++jc) {
       __builtin_amdgcn_sched_barrier(0);
       if (4 * jc + 3 <= k) continue;
-      const float4 vv = *(const float4*)&sh.v[4 * jc];
-      const float4 ww = *(const float4*)&sh.w[4 * jc];
-      g[4 * jc] = fmaf(-vi, ww.x, fmaf(-wi, vv.x, g[4 * jc]));
-      g[4 * jc + 1] = fmaf(-vi, ww.y, fmaf(-wi, vv.y, g[4 * jc + 1]));
-      g[4 * jc + 2] = fmaf(-vi, ww.z, fmaf(-wi, vv.z, g[4 * jc + 2]));
-      g[4 * jc + 3] = fmaf(-vi, ww.w, fmaf(-wi, vv.w, g[4 * jc + 3]));
-      qh[4 * jc] = fmaf(-tq, vv.x, qh[4 * jc]);
-      qh[4 * jc + 1] = fmaf(-tq, vv.y, qh[4 * jc + 1]);
-      qh[4 * jc + 2] = fmaf(-tq, vv.z, qh[4 * jc + 2]);
-      qh[4 * jc + 3] = fmaf(-tq, vv.w, qh[4 * jc + 3]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * jc + e;
+        const float vj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vi), j));
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), j));
+        g[j] = fmaf(-vi, wj, fmaf(-wi, vj, g[j]));
+        qh[j] = fmaf(-tq, vj, qh[j]);
+      }
     }
     if (lane == k) my_b = beta;
     __syncthreads();
