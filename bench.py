@@ -46,12 +46,12 @@ CACHE_DIR = os.environ.get("PKV_BENCH_CACHE", "/tmp/pkv_bench_inputs")
 # reads 1048576 KiB for 2^30 bytes written -> x1.0).  A figure holds only for
 # the kernel sources whose hash it carries; any change to them makes it null.
 PMC_TRAFFIC = {
-    "qwen3-32b-layer-128k": {"sha256": "1217ba8b2fe906eda42bad0129ad95eaec8fd696ccc98eb0d4059f280d27249c",
-                             "fetch": 303083995, "write": 1114112},
-    "qwen3-32b-layer-128k-int4": {"sha256": "1217ba8b2fe906eda42bad0129ad95eaec8fd696ccc98eb0d4059f280d27249c",
-                                  "fetch": 101441360, "write": 2228259},
-    "llama3.1-8b-layer-p32": {"sha256": "1217ba8b2fe906eda42bad0129ad95eaec8fd696ccc98eb0d4059f280d27249c",
-                              "fetch": 673900837, "write": 1114112},
+    "qwen3-32b-layer-128k": {"sha256": "76708175841f22b9a38d3d8cb79028cdd0aa48960408e385d9e37140d8b05e0e",
+                             "fetch": 303083932, "write": 1114112},
+    "qwen3-32b-layer-128k-int4": {"sha256": "76708175841f22b9a38d3d8cb79028cdd0aa48960408e385d9e37140d8b05e0e",
+                                  "fetch": 101449581, "write": 2228234},
+    "llama3.1-8b-layer-p32": {"sha256": "76708175841f22b9a38d3d8cb79028cdd0aa48960408e385d9e37140d8b05e0e",
+                              "fetch": 673912961, "write": 1114112},
 }
 TRAFFIC_SOURCES = ("long_context_decode_pkv_amd/csrc/pkv_decode.hip",
                    "long_context_decode_pkv_amd/csrc/pkv_internal.h")
