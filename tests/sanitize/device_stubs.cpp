@@ -28,6 +28,10 @@ hipError_t launch_partial_batch(const CacheGeom*, const int64_t*, const int64_t*
   return hipErrorNotSupported;
 }
 hipError_t launch_merge(const CacheGeom&, const AttnJob&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t noalloc_scratch(void** ptr) {
+  *ptr = nullptr;
+  return hipErrorNotSupported;
+}
 hipError_t launch_merge_batch(const CacheGeom*, int, const AttnJob&, const AttnJob*, const int*, hipStream_t) {
   return hipErrorNotSupported;
 }
