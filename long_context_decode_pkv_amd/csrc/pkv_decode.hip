@@ -618,20 +618,22 @@ constexpr int mfma_waves_per_simd(int n8) { return n8 <= 6 ? 2 : 1; }
 // keys() leaves the page's probabilities in Probs, values() accumulates the
 // page's output.
 
-// bf16 factors Lf = U Sigma, Rf = W^T (Sec. 3.3, Eq. 2), rank 8 N8.
-template <int N8>
+// bf16 factors Lf = U Sigma, Rf = W^T (Sec. 3.3, Eq. 2), key rank 8 N8K and
+// value rank 8 N8V (each part in its own rank's operand order).
+template <int N8K, int N8V = N8K>
 struct Bf16Factors {
-  static constexpr int kWavesPerSimd = mfma_waves_per_simd(N8);
+  static constexpr int kN8Max = N8K > N8V ? N8K : N8V;
+  static constexpr int kWavesPerSimd = mfma_waves_per_simd(kN8Max);
   // Key parts double-buffered where the extra page half fits the budget
   // without spilling (all but r/8 = 5, 6).  Qwen3-32B-shaped layer (r = 24):
   // 51.8 -> 50.7 us.
-  static constexpr bool kKeyDoubleBuffer = N8 <= 4 || N8 >= 7;
+  static constexpr bool kKeyDoubleBuffer = kN8Max <= 4 || kN8Max >= 7;
   static constexpr bool kLdsRing = false;
   static constexpr bool kRope = false;
   static constexpr int kLdsBytes = 0;
   static constexpr int kPageRows = kP;
-  using K = KRegs<N8>;
-  using V = VRegs<N8>;
+  using K = KRegs<N8K>;
+  using V = VRegs<N8V>;
   struct Query {
     bf16x8 qb[4];
   };
@@ -646,38 +648,38 @@ struct Bf16Factors {
     for (int ks = 0; ks < 4; ++ks) qd[ks] = Q.qb[ks];
   }
   __device__ static void load_keys(K& R, const uint8_t* kp, int lane) {
-    pkv::load_keys<N8>(R, (const uint16_t*)kp, lane);
+    pkv::load_keys<N8K>(R, (const uint16_t*)kp, lane);
   }
   __device__ static void load_values(V& R, const uint8_t* vp, int lane) {
-    pkv::load_values<N8>(R, (const uint16_t*)vp, lane);
+    pkv::load_values<N8V>(R, (const uint16_t*)vp, lane);
   }
   __device__ static void keys(SoftState& st, const K& R, const Query& Q, int q4, float rem, Probs& pb) {
-    fact_keys<N8>(st, R, Q.qb, q4, rem, pb);
+    fact_keys<N8K>(st, R, Q.qb, q4, rem, pb);
   }
   __device__ static void values(SoftState& st, const V& R, const Probs& pb, int q4, float rem) {
-    fact_values<N8>(st, R, pb, rem);
+    fact_values<N8V>(st, R, pb, rem);
   }
 };
 
-// bf16 factors of 32-token pages (the page length of Sec. 4.1), rank
-// 8 N8 <= 32: Bf16Factors' contractions in the 64-row frame with page rows
-// 32..63 absent (zero operands, masked scores).
-template <int N8>
-struct Bf16Half : Bf16Factors<N8> {
+// bf16 factors of 32-token pages (the page length of Sec. 4.1), ranks
+// 8 N8K, 8 N8V <= 32: Bf16Factors' contractions in the 64-row frame with
+// page rows 32..63 absent (zero operands, masked scores).
+template <int N8K, int N8V = N8K>
+struct Bf16Half : Bf16Factors<N8K, N8V> {
   static constexpr int kPageRows = kMinP;
-  using Base = Bf16Factors<N8>;
+  using Base = Bf16Factors<N8K, N8V>;
   using typename Base::K;
   using typename Base::V;
   using typename Base::Query;
   using typename Base::Probs;
   __device__ static void load_keys(K& R, const uint8_t* kp, int lane) {
-    pkv::load_keys_half<N8>(R, (const uint16_t*)kp, lane);
+    pkv::load_keys_half<N8K>(R, (const uint16_t*)kp, lane);
   }
   __device__ static void load_values(V& R, const uint8_t* vp, int lane) {
-    pkv::load_values_half<N8>(R, (const uint16_t*)vp, lane);
+    pkv::load_values_half<N8V>(R, (const uint16_t*)vp, lane);
   }
   __device__ static void keys(SoftState& st, const K& R, const Query& Q, int q4, float rem, Probs& pb) {
-    fact_keys<N8>(st, R, Q.qb, q4, rem, pb, kMinP);
+    fact_keys<N8K>(st, R, Q.qb, q4, rem, pb, kMinP);
   }
 };
 
@@ -2206,6 +2208,32 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
       PKV_HALF(3)
       PKV_HALF(4)
 #undef PKV_HALF
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else if (g.dtype == PKV_BF16 && !g.rope && n8k != n8v && n8k <= 4 && n8v <= 4) {
+    // unequal padded ranks up to 32 (batches launch once per cache: the
+    // batched kernel's caches share one format)
+    if constexpr (kBatch) return hipErrorNotSupported;
+    switch ((g.P == kMinP ? 64 : 0) + n8k * 8 + n8v) {
+#define PKV_ASYM(NK, NV)                                                                                 \
+  case NK * 8 + NV:                                                                                      \
+    if constexpr (NK != NV)                                                                              \
+      hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Factors<NK, NV>, KA>), grid, dim3(256), 0, stream,   \
+                            ev.start, ev.stop, 0, ka);                                                   \
+    break;                                                                                               \
+  case 64 + NK * 8 + NV:                                                                                 \
+    if constexpr (NK != NV)                                                                              \
+      hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Half<NK, NV>, KA>), grid, dim3(256), 0, stream,      \
+                            ev.start, ev.stop, 0, ka);                                                   \
+    break;
+#define PKV_ASYM_ROW(NK) PKV_ASYM(NK, 1) PKV_ASYM(NK, 2) PKV_ASYM(NK, 3) PKV_ASYM(NK, 4)
+      PKV_ASYM_ROW(1)
+      PKV_ASYM_ROW(2)
+      PKV_ASYM_ROW(3)
+      PKV_ASYM_ROW(4)
+#undef PKV_ASYM_ROW
+#undef PKV_ASYM
       default:
         return hipErrorInvalidValue;
     }

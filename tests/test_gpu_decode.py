@@ -77,7 +77,9 @@ def test_bf16_other_ranks(r):
     run_case(2, 64 * 20 + 1, B=1, kv_heads=2, r_k=r, r_v=r, label=f"rank{r}")
 
 
-@pytest.mark.parametrize("rk,rv", [(16, 14), (24, 16)])
+# (16, 14) pads to one multiple of 8; the others to two (the two-rank
+# matrix-core format), up to r = 32 on either side
+@pytest.mark.parametrize("rk,rv", [(16, 14), (24, 16), (8, 24), (32, 8), (1, 17), (20, 31)])
 def test_bf16_asymmetric_ranks(rk, rv):
     run_case(2, 64 * 16 + 30, B=1, kv_heads=2, r_k=rk, r_v=rv, label="asym")
 
