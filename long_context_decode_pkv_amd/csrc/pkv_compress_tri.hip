@@ -49,6 +49,8 @@
 // splits after row N - 1, and steps 2-5 run on the leading N x N block only
 // (the zero block's eigenvalues are exact zeros that the search must not
 // mistake for the page's smallest ones).
+#include <type_traits>
+
 #include "pkv_compress_common.h"
 
 namespace pkv {
@@ -63,7 +65,7 @@ struct TriShared {
     float band[16 * kLd];  // one 16-row band of G on its way into the row registers
     float Z[kP * kZs];     // eigenvectors of T as columns, then Q_r
   } u;
-  float xrow[kP];  // row k of the current G
+  float xrow[kP];  // scratch row: bisection points, a Cholesky column, INT4 scale factors
   float v[kP];     // Householder vector
   float w[kP];     // rank-2 update vector
   float a[kP];     // diagonal of T
@@ -167,6 +169,45 @@ __device__ __forceinline__ void gram_rows(const Elem* X, int trans, int P, TriSh
   }
 }
 
+// f(integral_constant<int, c>) for c = c0 .. NC - 1 (NC <= 16): a switch
+// whose cases fall through into one unrolled chunk sequence, so register
+// indices stay compile-time constants and a uniform start costs one
+// dispatch, not a test per chunk.
+template <int NC, class F>
+__device__ __forceinline__ void from_chunk(int c0, F&& f) {
+  static_assert(NC <= 16, "at most 16 chunks");
+#define PKV_CHUNK(c)                                                  \
+  case c:                                                             \
+    if constexpr (c < NC) f(std::integral_constant<int, c>{});        \
+    [[fallthrough]];
+  switch (c0) {
+    PKV_CHUNK(0) PKV_CHUNK(1) PKV_CHUNK(2) PKV_CHUNK(3) PKV_CHUNK(4) PKV_CHUNK(5) PKV_CHUNK(6) PKV_CHUNK(7)
+    PKV_CHUNK(8) PKV_CHUNK(9) PKV_CHUNK(10) PKV_CHUNK(11) PKV_CHUNK(12) PKV_CHUNK(13) PKV_CHUNK(14)
+    PKV_CHUNK(15)
+    default:
+      break;
+  }
+#undef PKV_CHUNK
+}
+
+// f(integral_constant<int, c>) for the one chunk c (NC <= 16).
+template <int NC, class F>
+__device__ __forceinline__ void at_chunk(int c, F&& f) {
+  static_assert(NC <= 16, "at most 16 chunks");
+#define PKV_CHUNK(c)                                                  \
+  case c:                                                             \
+    if constexpr (c < NC) f(std::integral_constant<int, c>{});        \
+    break;
+  switch (c) {
+    PKV_CHUNK(0) PKV_CHUNK(1) PKV_CHUNK(2) PKV_CHUNK(3) PKV_CHUNK(4) PKV_CHUNK(5) PKV_CHUNK(6) PKV_CHUNK(7)
+    PKV_CHUNK(8) PKV_CHUNK(9) PKV_CHUNK(10) PKV_CHUNK(11) PKV_CHUNK(12) PKV_CHUNK(13) PKV_CHUNK(14)
+    PKV_CHUNK(15)
+    default:
+      break;
+  }
+#undef PKV_CHUNK
+}
+
 // 2. Householder tridiagonalization of the leading N x N block (the rest of
 // G is zero).  On return lane i holds a_i (my_a), b_i (my_b) and row i of Q_H.
 template <int N>
@@ -177,15 +218,16 @@ __device__ __forceinline__ void tridiagonalize(TriShared& sh, float (&g)[kP], fl
   my_a = 0.f;
   my_b = 0.f;
   for (int k = 0; k < N - 1; ++k) {
-    if (lane == k) {
-#pragma unroll
-      for (int jc = 0; jc < kP / 4; ++jc)
-        *(float4*)&sh.xrow[4 * jc] = float4{g[4 * jc], g[4 * jc + 1], g[4 * jc + 2], g[4 * jc + 3]};
-    }
-    __syncthreads();
-    const float x = sh.xrow[lane];  // G[k][lane] = G[lane][k]
+    // G stays symmetric, so G[k][lane] = G[lane][k] is the lane's own g[k]:
+    // a uniform switch on the chunk of k, then a select within it
+    float x = 0.f;
+    at_chunk<N / 4>(k >> 2, [&](auto J) {
+      constexpr int jc = decltype(J)::value;
+      const int e = k & 3;
+      x = e == 0 ? g[4 * jc] : (e == 1 ? g[4 * jc + 1] : (e == 2 ? g[4 * jc + 2] : g[4 * jc + 3]));
+    });
     if (lane == k) my_a = x;
-    const float alpha = sh.xrow[k + 1];
+    const float alpha = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k + 1));
     const float tail = wave_reduce<0>(lane >= k + 2 ? x * x : 0.f);
     // H_k = I - tau v v^T; tail == 0 means no reflection (tau = 0, v = e_{k+1})
     const bool refl = tail > 0.f;
@@ -197,14 +239,19 @@ __device__ __forceinline__ void tridiagonalize(TriShared& sh, float (&g)[kP], fl
     const float vi = lane == k + 1 ? 1.f : (lane >= k + 2 ? x * scal : 0.f);
     sh.v[lane] = vi;
     __syncthreads();
-    // p = tau G v (rows > k), t = Q_H v; v_j = 0 for j <= k, so 4-column
-    // chunks left of k + 1 are skipped (uniform branch)
+    // p = tau G v (rows > k), t = Q_H v; v_j = 0 for j <= k, so the 4-column
+    // chunks left of k + 1 are skipped: the step enters the unrolled chunk
+    // sequence at its first active chunk (one uniform branch per loop)
+    // (each v chunk is read one chunk ahead of its use: the LDS latency
+    // overlaps the FMAs of the chunk before)
+    const int jc0 = (k + 1) >> 2;
     float pacc = 0.f, tacc = 0.f;
-#pragma unroll
-    for (int jc = 0; jc < N / 4; ++jc) {
+    float4 vq = *(const float4*)&sh.v[4 * jc0];
+    from_chunk<N / 4>(jc0, [&](auto J) {
+      constexpr int jc = decltype(J)::value;
       __builtin_amdgcn_sched_barrier(0);
-      if (4 * jc + 3 <= k) continue;
-      const float4 vv = *(const float4*)&sh.v[4 * jc];
+      const float4 vv = vq;
+      if constexpr (jc + 1 < N / 4) vq = *(const float4*)&sh.v[4 * (jc + 1)];
       pacc = fmaf(g[4 * jc], vv.x, pacc);
       pacc = fmaf(g[4 * jc + 1], vv.y, pacc);
       pacc = fmaf(g[4 * jc + 2], vv.z, pacc);
@@ -213,28 +260,28 @@ __device__ __forceinline__ void tridiagonalize(TriShared& sh, float (&g)[kP], fl
       tacc = fmaf(qh[4 * jc + 1], vv.y, tacc);
       tacc = fmaf(qh[4 * jc + 2], vv.z, tacc);
       tacc = fmaf(qh[4 * jc + 3], vv.w, tacc);
-    }
+    });
     const float pi = lane > k ? tau * pacc : 0.f;
     const float K = 0.5f * tau * wave_reduce<0>(pi * vi);
     const float wi = fmaf(-K, vi, pi);
-    // G <- G - v w^T - w v^T ; Q_H <- Q_H - tau (Q_H v) v^T.  v_j and w_j
-    // are wave-uniform: read from their lanes into scalar registers
-    // (v_readlane) rather than broadcast through LDS, whose data return
-    // (1 KB per 16-byte read of a wave) the workgroups of a CU share.
+    sh.w[lane] = wi;
+    __syncthreads();
+    // G <- G - v w^T - w v^T ; Q_H <- Q_H - tau (Q_H v) v^T
     const float tq = tau * tacc;
-#pragma unroll
-    for (int jc = 0; jc < N / 4; ++jc) {
+    from_chunk<N / 4>(jc0, [&](auto J) {
+      constexpr int jc = decltype(J)::value;
       __builtin_amdgcn_sched_barrier(0);
-      if (4 * jc + 3 <= k) continue;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 4 * jc + e;
-        const float vj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vi), j));
-        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), j));
-        g[j] = fmaf(-vi, wj, fmaf(-wi, vj, g[j]));
-        qh[j] = fmaf(-tq, vj, qh[j]);
-      }
-    }
+      const float4 vv = *(const float4*)&sh.v[4 * jc];
+      const float4 ww = *(const float4*)&sh.w[4 * jc];
+      g[4 * jc] = fmaf(-vi, ww.x, fmaf(-wi, vv.x, g[4 * jc]));
+      g[4 * jc + 1] = fmaf(-vi, ww.y, fmaf(-wi, vv.y, g[4 * jc + 1]));
+      g[4 * jc + 2] = fmaf(-vi, ww.z, fmaf(-wi, vv.z, g[4 * jc + 2]));
+      g[4 * jc + 3] = fmaf(-vi, ww.w, fmaf(-wi, vv.w, g[4 * jc + 3]));
+      qh[4 * jc] = fmaf(-tq, vv.x, qh[4 * jc]);
+      qh[4 * jc + 1] = fmaf(-tq, vv.y, qh[4 * jc + 1]);
+      qh[4 * jc + 2] = fmaf(-tq, vv.z, qh[4 * jc + 2]);
+      qh[4 * jc + 3] = fmaf(-tq, vv.w, qh[4 * jc + 3]);
+    });
     if (lane == k) my_b = beta;
     __syncthreads();
   }
