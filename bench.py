@@ -46,12 +46,12 @@ CACHE_DIR = os.environ.get("PKV_BENCH_CACHE", "/tmp/pkv_bench_inputs")
 # reads 1048576 KiB for 2^30 bytes written -> x1.0).  A figure holds only for
 # the kernel sources whose hash it carries; any change to them makes it null.
 PMC_TRAFFIC = {
-    "qwen3-32b-layer-128k": {"sha256": "76708175841f22b9a38d3d8cb79028cdd0aa48960408e385d9e37140d8b05e0e",
-                             "fetch": 303083932, "write": 1114112},
-    "qwen3-32b-layer-128k-int4": {"sha256": "76708175841f22b9a38d3d8cb79028cdd0aa48960408e385d9e37140d8b05e0e",
-                                  "fetch": 101449581, "write": 2228234},
-    "llama3.1-8b-layer-p32": {"sha256": "76708175841f22b9a38d3d8cb79028cdd0aa48960408e385d9e37140d8b05e0e",
-                              "fetch": 673912961, "write": 1114112},
+    "qwen3-32b-layer-128k": {"sha256": "5936d16d4b5a18d7310ec4b9a15adc3dfab306983a2a05011aba5fef58f0f8b9",
+                             "fetch": 303099215, "write": 1114112},
+    "qwen3-32b-layer-128k-int4": {"sha256": "5936d16d4b5a18d7310ec4b9a15adc3dfab306983a2a05011aba5fef58f0f8b9",
+                                  "fetch": 101412945, "write": 2228233},
+    "llama3.1-8b-layer-p32": {"sha256": "5936d16d4b5a18d7310ec4b9a15adc3dfab306983a2a05011aba5fef58f0f8b9",
+                              "fetch": 673885986, "write": 1114112},
 }
 TRAFFIC_SOURCES = ("long_context_decode_pkv_amd/csrc/pkv_decode.hip",
                    "long_context_decode_pkv_amd/csrc/pkv_internal.h")
