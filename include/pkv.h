@@ -181,8 +181,9 @@ int32_t pkv_unpack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_
 /* Bytes of one factor part (kind: any pkv_factor_kind) of rank r in
  * storage format `dtype`.  PKV_BF16 / PKV_F32: r8 (P + d) elements of 2 / 4
  * bytes.  PKV_BF16_INT4 (the INT4 part of Sec. 4.3; K and V parts differ),
- * with A = r8 / 4 and a unit of ub = 1, 2 or 4 bytes for A <= 2, <= 4,
- * else, and h = 1 at P = 64, 2 at P = 32:
+ * with A = r8 / 4 codes in a rank unit of ub = A / 2 bytes (a nibble per
+ * code: 1, 2, 3 or 4 bytes; 3-byte units start at any byte), and h = 1 at
+ * P = 64, 2 at P = 32:
  *   K part: roundup64(r8 d / 2 + (256 / h) ub + 2 d + 2 r8)
  *           (codes of Rt_K, codes of Lt_K in units of A, scales of Rt_K, Lt_K)
  *   V part: roundup64(r8 P / 2 + 4 d ub + 2 P + 2 d)

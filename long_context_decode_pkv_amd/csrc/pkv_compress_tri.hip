@@ -615,10 +615,19 @@ __device__ __forceinline__ uint32_t q4_pack(const uint8_t* src, int stride, int 
   return u;
 }
 
+// ub = 3 units start at any byte: three byte stores
 __device__ __forceinline__ void q4_store_unit(uint8_t* p, uint32_t u, int ub) {
-  if (ub == 4) *(uint32_t*)p = u;
-  else if (ub == 2) *(uint16_t*)p = (uint16_t)u;
-  else *p = (uint8_t)u;
+  if (ub == 4) {
+    *(uint32_t*)p = u;
+  } else if (ub == 3) {
+    p[0] = (uint8_t)u;
+    p[1] = (uint8_t)(u >> 8);
+    p[2] = (uint8_t)(u >> 16);
+  } else if (ub == 2) {
+    *(uint16_t*)p = (uint16_t)u;
+  } else {
+    *p = (uint8_t)u;
+  }
 }
 
 __device__ __forceinline__ void q4_store_scale(uint8_t* p, float s) { *(uint16_t*)p = f32_to_bf16_bits(s); }

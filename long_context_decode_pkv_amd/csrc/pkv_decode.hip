@@ -1020,11 +1020,12 @@ __device__ __forceinline__ uint32_t split2(float x0, float x1, float rem) {
 }
 
 // unit of W nibbles in the low 4 W bits of x -> operand slots 0 .. 2 NP - 1
-// (slots above are 0)
+// (slots above are 0; a 6-nibble unit's halves are nibbles 0..2 and 3..5)
 template <int W, int NP>
 __device__ __forceinline__ bf16x8 q4_operand(uint32_t x) {
   uint32_t u = x;
-  if constexpr (W == 4) u = x | (x << 8);
+  if constexpr (W == 6) u = __builtin_amdgcn_ubfe(x, 0, 12) | ((x << 4) & vgpr_const<0x0fff0000u>());
+  else if constexpr (W == 4) u = x | (x << 8);
   else if constexpr (W == 2) u = x | (x << 12);
   uint4 w = {q4_pair<0>(u), 0u, 0u, 0u};
   if constexpr (NP > 1) w.y = q4_pair<1>(u);
@@ -1033,12 +1034,22 @@ __device__ __forceinline__ bf16x8 q4_operand(uint32_t x) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// unit m of UB bytes from consecutive dwords
+// unit m of UB bytes from consecutive dwords (UB = 3: the unit's bytes
+// 3 m .. 3 m + 2 in the low 24 bits, the bits above it unspecified)
 template <int UB>
 __device__ __forceinline__ uint32_t q4_unit(const uint32_t* d, int m) {
-  if constexpr (UB == 4) return d[m];
-  else if constexpr (UB == 2) return __builtin_amdgcn_ubfe(d[m / 2], 16 * (m % 2), 16);
-  else return __builtin_amdgcn_ubfe(d[m / 4], 8 * (m % 4), 8);
+  if constexpr (UB == 4) {
+    return d[m];
+  } else if constexpr (UB == 3) {
+    const int i = 3 * m / 4, o = 3 * m % 4;
+    if (o == 0) return d[i];
+    if (o == 1) return d[i] >> 8;
+    return __builtin_amdgcn_alignbyte(d[i + 1], d[i], o);
+  } else if constexpr (UB == 2) {
+    return __builtin_amdgcn_ubfe(d[m / 2], 16 * (m % 2), 16);
+  } else {
+    return __builtin_amdgcn_ubfe(d[m / 4], 8 * (m % 4), 8);
+  }
 }
 
 __device__ __forceinline__ bf16x8 q4_offset_operand() {
@@ -1084,7 +1095,11 @@ __device__ __forceinline__ void vm_wait() {
 // N consecutive dwords, streamed
 template <int N>
 __device__ __forceinline__ void ldw(uint32_t* d, const uint8_t* p) {
-  if constexpr (N == 4) {
+  if constexpr (N == 6) {  // 8-byte aligned
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+    const u32x2 w = __builtin_nontemporal_load((const u32x2*)(p + 16));
+    d[0] = v.x, d[1] = v.y, d[2] = v.z, d[3] = v.w, d[4] = w.x, d[5] = w.y;
+  } else if constexpr (N == 4) {
     const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
     d[0] = v.x, d[1] = v.y, d[2] = v.z, d[3] = v.w;
   } else if constexpr (N == 3) {

@@ -160,11 +160,13 @@ __host__ __device__ inline int64_t off_lf(int kind, const PackDims& p, int j, in
 // A code is stored as the nibble c + 8.  The operands keep the matrix-core
 // roles and lane order of the bf16 layout above; a lane's 8 reduction slots
 // of one MFMA step form one unit.  K1 / V1 units (8 channels / tokens) are
-// dwords; K2 / V2 units hold the lane quad's A ranks in UB bytes
-// (A = 2 -> 1 byte, 4 -> 2, 6 or 8 -> 4; padding nibbles hold 8, i.e. c = 0).
+// dwords; K2 / V2 units hold the lane quad's A ranks in UB = A / 2 bytes
+// (A = 2, 4, 6, 8 -> 1, 2, 3, 4 bytes; a 3-byte unit starts at any byte).
 // Within a unit of W = 2 UB nibbles, element e sits at bit
 // 4 ((e % 2) W / 2 + e / 2): for a dword, ((u >> 4k) & 0x000F000F) are the
-// nibbles of elements 2k and 2k + 1 in the two 16-bit halves.
+// nibbles of elements 2k and 2k + 1 in the two 16-bit halves; a 3-byte unit
+// holds elements 0, 2, 4 in its low 12 bits and 1, 3, 5 in its high 12.
+// Padding ranks (r < 8 ceil(r / 8)) hold the nibble 8, i.e. c = 0.
 //
 // K part (byte offsets):  K1 codes  [tile][lane][ks 0..3] dwords; 1024 per
 //                                   full tile, 512 for a compacted last tile
@@ -180,7 +182,9 @@ __host__ __device__ inline int64_t off_lf(int kind, const PackDims& p, int j, in
 
 constexpr int kQ4MaxRank = 32;
 
-__host__ __device__ constexpr int q4_unit_bytes(int A) { return A <= 2 ? 1 : (A <= 4 ? 2 : 4); }
+// A rank unit holds the A codes of a lane quad (A = 2, 4, 6 or 8: one nibble
+// each) in A / 2 bytes.
+__host__ __device__ constexpr int q4_unit_bytes(int A) { return A / 2; }
 
 struct Q4Dims {
   PackDims pd;

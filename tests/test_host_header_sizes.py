@@ -22,7 +22,7 @@ def r8(r):
 def int4_part_bytes(kind, P, r):
     """The INT4 part sizes as the header gives them at pkv_factor_part_bytes."""
     A = r8(r) // 4
-    ub = 1 if A <= 2 else (2 if A <= 4 else 4)
+    ub = A // 2  # a rank unit: A codes, one nibble each
     h = 1 if P == 64 else 2
     if kind == pkv.VALUES:
         return roundup(r8(r) * P // 2 + 4 * D * ub + 2 * P + 2 * D, 64)

@@ -60,7 +60,7 @@ def _dims(r):
     n8 = -(-r // 8)
     A = 2 * n8
     full, part = A // 4, int(A % 4 != 0)
-    ub = 1 if A <= 2 else (2 if A <= 4 else 4)
+    ub = A // 2  # a rank unit: A codes, one nibble each
     return n8, A, full, part, ub
 
 
@@ -155,18 +155,19 @@ def test_int4_part_follows_documented_layout(kind, r):
 
 
 def test_int4_part_sizes_against_the_pages_count():
-    """For r a multiple of 8 with no compacted tile (r = 16, 32) a part holds
-    exactly the pages' (P + d) r / 2 code bytes plus its 16-bit scales (keys:
-    d + r, values: P + d), rounded up to 64 bytes."""
-    for r in (16, 32):
+    """For r a multiple of 8 (r = 8 .. 32; 24 in 3-byte rank units) a part
+    holds exactly the pages' (P + d) r / 2 code bytes plus its 16-bit scales
+    (keys: d + r, values: P + d), rounded up to 64 bytes."""
+    for r in (8, 16, 24, 32):
         codes = (64 + 128) * r // 2
         k = pkv.factor_part_bytes(pkv.KEYS, r, pkv.BF16_INT4)
         v = pkv.factor_part_bytes(pkv.VALUES, r, pkv.BF16_INT4)
-        assert k == -(-(codes + 2 * (128 + r)) // 64) * 64
-        assert v == -(-(codes + 2 * (64 + 128)) // 64) * 64
-    # the qwen-shaped rank 24: 6080 bytes per page pair against 18432 for bf16
+        assert k == -(-(codes + 2 * (128 + r)) // 64) * 64, r
+        assert v == -(-(codes + 2 * (64 + 128)) // 64) * 64, r
+    # the qwen-shaped rank 24: 5312 bytes per page pair (the pages' count:
+    # 5296, before the 64-byte rounding of the key part) against 18432 for bf16
     assert pkv.factor_part_bytes(pkv.KEYS, 24, pkv.BF16_INT4) + \
-        pkv.factor_part_bytes(pkv.VALUES, 24, pkv.BF16_INT4) == 6080
+        pkv.factor_part_bytes(pkv.VALUES, 24, pkv.BF16_INT4) == 5312
     assert 2 * pkv.factor_part_bytes(pkv.KEYS, 24, pkv.BF16) == 18432
 
 
