@@ -312,6 +312,7 @@ def bench_decode(args, cfg_id, name, store=None, rope=False, overrides=None):
             states.append(layer_step(c, ws, args.warmup + args.steps + j, recs[j][li]))
     torch.cuda.synchronize()
     elapsed_instr = time.perf_counter() - t
+    layer_steps = args.steps * NL
     # one promotion per layer cache whatever the step count: step on to the
     # first step at which a page leaves the window and time its decomposition
     # (the first kernel of that step)
@@ -348,6 +349,20 @@ def bench_decode(args, cfg_id, name, store=None, rope=False, overrides=None):
             torch.cuda.synchronize()
             promos.append(a.elapsed_time(b) * 1e-3)
         promos = promos[1:]
+    # the attention call alone (pkv_decode_attn: the split partials and the
+    # merge, no append or promotion), `steps` calls per layer cache over the
+    # tokens the caches now hold
+    T_call, nf_call, _ = caches[0].state()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for j in range(args.steps):
+        for c, ws in zip(caches, wss):
+            c.decode(qs[j], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t_call = (time.perf_counter() - t) / layer_steps
+    bytes_call = decode_bytes(cfg, B, Hkv, Hq, T_call, nf_call, store)
+    log(f"attention call (pkv_decode_attn) at T={T_call}: {t_call * 1e6:.1f} us per layer, "
+        f"{bytes_call / t_call / 1e9:.0f} GB/s ({bytes_call / t_call / 1e9 / HBM_PEAK_GBS * 100:.1f}% of peak)")
     # early factorization in steady state (without --aux): the caches refilled
     # through pkv_prefill_chunk with a second stream, which factorizes the
     # window's complete pages there, then P steps per layer -- one page
@@ -374,7 +389,6 @@ def bench_decode(args, cfg_id, name, store=None, rope=False, overrides=None):
     states = [states[k] for k in keep]
     nbytes = np.array([decode_bytes(cfg, B, Hkv, Hq, T, nf, store) for T, nf in states], dtype=np.float64)
     achieved = nbytes.sum() / durs.sum() / 1e9
-    layer_steps = args.steps * NL
     traffic = pmc_traffic(name)
     # promotions at their rate: one per P steps of a layer; the timed pass
     # holds promos_timed of them
@@ -418,6 +432,8 @@ def bench_decode(args, cfg_id, name, store=None, rope=False, overrides=None):
                      # between launches) against the same bytes
                      "frac_step": nbytes.mean() / (elapsed / layer_steps) / 1e9 / HBM_PEAK_GBS,
                      "frac_step_promotions_amortized": nbytes.mean() / step_amortized / 1e9 / HBM_PEAK_GBS,
+                     # the attention call (pkv_decode_attn: partial + merge)
+                     "frac_call": bytes_call / t_call / 1e9 / HBM_PEAK_GBS,
                      "traffic": None if traffic is None else traffic["fetch"] + traffic["write"],
                      "kernel": ("decode_mfma_kernel (pkv_decode_partial)" if cfg["P"] == 64
                                 else "decode_valu_kernel (pkv_decode_partial)"),
@@ -433,6 +449,7 @@ def bench_decode(args, cfg_id, name, store=None, rope=False, overrides=None):
                          "promote_amortized_per_step": t_promo / P * 1e6,
                          "layer_step_promotions_amortized": step_amortized * 1e6,
                          "layer_step_early_factorization": None if step_early is None else step_early * 1e6,
+                         "attention_call": t_call * 1e6,
                          "layer_step_with_events": elapsed_instr / layer_steps * 1e6},
         "ms_per_step_promotions_amortized": step_amortized * 1e3,
         "decode_effective_GBps": achieved,
