@@ -65,6 +65,14 @@ def test_p32_decode_against_oracle(cfg_id, T, B, kv, rk, rv, splits):
     _case(cfg_id, T, B, kv, rk, rv, splits=splits, label="decode")
 
 
+@pytest.mark.parametrize("T", [32 * 9 + 3, 32 * 10 + 3, 32 * 41 + 30, 32 * 42 + 30])
+def test_p32_factorized_counts_and_splits_against_oracle(T):
+    """The pages' operating point at odd and even factorized page counts
+    (7, 8, 39, 40) and split counts from one workgroup to more waves than
+    factorized pages, so that waves hold none, one, or runs of them."""
+    _case(2, T, 1, 2, RK, RV, splits=(0, 1, 2, 3, 16, 64), label="counts")
+
+
 def test_p32_short_and_windowless_caches():
     _case(2, 20, label="sink only")
     _case(2, 32 * 2 + 3, label="all dense")
