@@ -392,14 +392,16 @@ struct SoftState {
   floatx4 o[8];
 };
 
-// Fold one page's 64 raw scores (MFMA output, hi/lo column halves not yet
-// summed) into the running state; s receives the page's probabilities
-// e^(score - m) (slot [ks][e] of the value contraction in s[2 ks + e / 4][e % 4]).
-__device__ inline void softmax_probs(SoftState& st, const floatx4 (&acc)[4], int nvalid, int q4,
-                                     float (&s)[4][4]) {
+// Fold one page's 16 NT raw scores per query (NT score tiles of MFMA output,
+// hi/lo column halves not yet summed) into the running state; s receives the
+// page's probabilities e^(score - m) (slot [ks][e] of the value contraction in
+// s[2 ks + e / 4][e % 4]).
+template <int NT = 4>
+__device__ inline void softmax_probs(SoftState& st, const floatx4 (&acc)[NT], int nvalid, int q4,
+                                     float (&s)[NT][4]) {
   float mx = -INFINITY;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < NT; ++mt) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       float x = acc[mt][v] + ror8(acc[mt][v]);
@@ -415,7 +417,7 @@ __device__ inline void softmax_probs(SoftState& st, const floatx4 (&acc)[4], int
   const float alpha = fast_exp2(st.m - m_new);
   float ps = 0.f;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < NT; ++mt) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const float p = fast_exp2(s[mt][v] - m_new);
@@ -431,13 +433,14 @@ __device__ inline void softmax_probs(SoftState& st, const floatx4 (&acc)[4], int
   for (int mt = 0; mt < 8; ++mt) st.o[mt] *= alpha;
 }
 
-// ... and the probability operand pb[2] of the value contraction.
-__device__ inline void softmax_page(SoftState& st, const floatx4 (&acc)[4], int nvalid, int q4,
-                                    float rem, bf16x8 (&pb)[2]) {
-  float s[4][4];
-  softmax_probs(st, acc, nvalid, q4, s);
+// ... and the probability operand pb[NT / 2] of the value contraction.
+template <int NT = 4>
+__device__ inline void softmax_page(SoftState& st, const floatx4 (&acc)[NT], int nvalid, int q4,
+                                    float rem, bf16x8 (&pb)[NT / 2]) {
+  float s[NT][4];
+  softmax_probs<NT>(st, acc, nvalid, q4, s);
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  for (int ks = 0; ks < NT / 2; ++ks) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) pb[ks][e] = split_bf16(s[2 * ks + e / 4][e % 4], rem);
   }
@@ -865,7 +868,14 @@ constexpr int kRopeMfmaMaxN8 = 4;
 
 // bf16 factors of pre-RoPE keys: the key part holds Rf_K channel-major (the
 // V part's Rf layout) and Lf_K as in Bf16Factors; the V part as there.
-template <int N8, int PR = kP>  // PR: page rows (32: rows 32..63 absent, as in Bf16Half)
+// PR: page rows.  A 32-token page is reconstructed, rotated and scored as
+// two 16-token tiles in a compact token order: tile t, column n holds token
+// 8 (n / 4) + 4 t + n % 4, so score row 4 b + v of tile t is token
+// 8 b + 4 t + v, and slot e of lane quad b of the value contraction's single
+// reduction step is token 8 b + e (eight consecutive tokens of the stored
+// Lf_V^T).  Only the loads follow this order; the stored parts are the
+// compacted 64-row layout.
+template <int N8, int PR = kP>
 struct RopeFactors {
   using Dm = FactDims<N8>;
   static constexpr int kWavesPerSimd = mfma_waves_per_simd(N8);
@@ -874,11 +884,12 @@ struct RopeFactors {
   static constexpr bool kRope = true;
   static constexpr int kPageRows = PR;
   static constexpr int kLdsBytes = 0;
+  static constexpr int kTiles = PR / 16;  // token tiles
   struct K {
     RawW<Dm::W0> rfa[8];
     RawW<Dm::W1> rfb[Dm::KS2 > 1 ? 8 : 1];
-    RawW<Dm::W0> k2a[4];
-    RawW<Dm::W1> k2b[Dm::KS2 > 1 ? 4 : 1];
+    RawW<Dm::W0> k2a[kTiles];
+    RawW<Dm::W1> k2b[Dm::KS2 > 1 ? kTiles : 1];
     __device__ bf16x8 rf(int ct, int ks) const { return ks == 0 ? operand(rfa[ct]) : operand(rfb[ct]); }
     __device__ bf16x8 k2(int mt, int ks) const { return ks == 0 ? operand(k2a[mt]) : operand(k2b[mt]); }
   };
@@ -920,34 +931,58 @@ struct RopeFactors {
         ldraw(R.k2a[mt], base + lane * Dm::W0);
         if constexpr (Dm::KS2 > 1) ldraw(R.k2b[mt], base + 512 + lane * Dm::W1);
       }
-    } else {  // compacted K2: lanes of tokens 32..63 zero
-      const int rho = lane & 15;
-      const bool ok = rho < 8;
-      const int lam = ok ? 8 * (lane >> 4) + rho : 0;
+    } else {
+      // column n of tile t: token tau = 8 (n / 4) + 4 t + n % 4, stored as
+      // page row 16 bq + 4 mt + v of the compacted K2 (bq = tau / 16,
+      // mt = tau / 4 % 4, v = tau % 4) at lane 8 qk + 4 bq + v
+      const int n = lane & 15, qk = lane >> 4;
+      const int lam = 8 * qk + 4 * (n >> 3) + (n & 3);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const uint16_t* base = p + Dm::K1 + mt * 32 * Dm::A;
-        ldraw(R.k2a[mt], base + lam * Dm::W0);
-        zero_unless(R.k2a[mt], ok);
-        if constexpr (Dm::KS2 > 1) {
-          ldraw(R.k2b[mt], base + 256 + lam * Dm::W1);
-          zero_unless(R.k2b[mt], ok);
-        }
+      for (int t = 0; t < kTiles; ++t) {
+        const uint16_t* base = p + Dm::K1 + ((2 * (n >> 2) + t) & 3) * 32 * Dm::A;
+        ldraw(R.k2a[t], base + lam * Dm::W0);
+        if constexpr (Dm::KS2 > 1) ldraw(R.k2b[t], base + 256 + lam * Dm::W1);
       }
     }
   }
   __device__ static void load_values(V& R, const uint8_t* vp, int lane) {
-    if constexpr (PR == kP) pkv::load_values<N8>(R, (const uint16_t*)vp, lane);
-    else pkv::load_values_half<N8>(R, (const uint16_t*)vp, lane);
+    if constexpr (PR == kP) {
+      pkv::load_values<N8>(R, (const uint16_t*)vp, lane);
+    } else {
+      // V1 in the single reduction step: lane (rho, b) takes tokens
+      // 8 b .. 8 b + 7, stored at lane 16 (b / 2) + rho, step b % 2 (a
+      // compacted last rank tile: rows v < 2 of each lane quad only)
+      const uint16_t* p = (const uint16_t*)vp;
+      const int rho = lane & 15, b = lane >> 4;
+      const TileLane tl = tile_lane(lane);
+#pragma unroll
+      for (int mt = 0; mt < Dm::RT; ++mt) {
+        const bool part = Dm::kPartialTile && mt == Dm::RT - 1;
+        if (!part) {
+          R.v1[mt][0] = ld16(p + mt * 512 + (b & 1) * 256 + (16 * (b >> 1) + rho) * 8);
+        } else {
+          const int lam = tl.ok ? 8 * (b >> 1) + 2 * (rho >> 2) + (rho & 3) : 0;
+          const bf16x8 v = ld16(p + mt * 512 + (b & 1) * 128 + lam * 8);
+          R.v1[mt][0] = tl.ok ? v : bf16x8{};
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const uint16_t* base = p + Dm::V1 / 2 + mt * 64 * Dm::A;
+        ldraw(R.v2a[mt], base + lane * Dm::W0);
+        if constexpr (Dm::KS2 > 1) ldraw(R.v2b[mt], base + 512 + lane * Dm::W1);
+      }
+    }
   }
   // token tile mt: K_p^T columns = its 16 tokens, 8 channel tiles of rows
   __device__ static void keys(SoftState& st, const K& R, const Query& Q, const RopeLds& L, int lane,
                               float rem, Probs& pb) {
     const int n = lane & 15, q4 = lane >> 4;
-    floatx4 as_[4];
+    floatx4 as_[kTiles];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const float* row = &L.table[16 * (n >> 2) + 4 * mt + (n & 3)][0];
+    for (int mt = 0; mt < kTiles; ++mt) {
+      const int tok = PR == kP ? 16 * (n >> 2) + 4 * mt + (n & 3) : 8 * (n >> 2) + 4 * mt + (n & 3);
+      const float* row = &L.table[tok][0];
       halfx8 ka[4];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
@@ -961,10 +996,29 @@ struct RopeFactors {
       }
       as_[mt] = rope_scores(ka, Q.qb);
     }
-    softmax_page(st, as_, PR, q4, rem, pb);
+    if constexpr (PR == kP) {
+      softmax_page(st, as_, PR, q4, rem, pb);
+    } else {  // every token of a factorized page is valid
+      bf16x8 p1[1];
+      softmax_page<kTiles>(st, as_, kP, q4, rem, p1);
+      pb[0] = p1[0];
+    }
   }
   __device__ static void values(SoftState& st, const V& R, const Probs& pb, int, float rem) {
-    fact_values<N8>(st, R, pb, rem);
+    if constexpr (PR == kP) {
+      fact_values<N8>(st, R, pb, rem);
+    } else {  // Eq. 4's value half over the page's 32 tokens: one reduction step
+      floatx4 au[Dm::RT];
+#pragma unroll
+      for (int mt = 0; mt < Dm::RT; ++mt) au[mt] = mfma(R.v1[mt][0], pb[0], floatx4{0.f, 0.f, 0.f, 0.f});
+      bf16x8 ub[Dm::KS2];
+      rank_operand<N8>(au, rem, ub);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+        for (int ks = 0; ks < Dm::KS2; ++ks) st.o[mt] = mfma(R.v2(mt, ks), ub[ks], st.o[mt]);
+      }
+    }
   }
 };
 

@@ -87,6 +87,19 @@ def test_p32_pre_rope_keys():
     _case(2, 32 * 12 + 7, rk=8, rv=24, rope=synth.rope_inv_freq(5e5), label="pre-RoPE valu")
 
 
+@pytest.mark.parametrize("cfg_id,T,rk,rv,splits", [
+    (2, 32 * 25 + 3, 8, 8, (0, 3)),     # n8 = 1: compacted rank tile
+    (4, 32 * 18 + 30, 5, 7, (0, 1)),    # n8 = 1, unequal ranks
+    (3, 32 * 27 + 16, 20, 24, (0, 5)),  # n8 = 3
+    (2, 32 * 22 + 1, 32, 32, (0, 2)),   # n8 = 4: full rank of a 32-token page
+])
+def test_p32_pre_rope_every_rank_tile_count(cfg_id, T, rk, rv, splits):
+    """Pre-RoPE 32-token pages on the matrix-core kernel at every padded rank
+    it takes (8 to 32), against the oracle."""
+    f = synth.rope_inv_freq(5e5 if cfg_id != 3 else 1e6)
+    _case(cfg_id, T, rk=rk, rv=rv, rope=f, splits=splits, label="pre-RoPE n8")
+
+
 def test_p32_factors_are_the_pages_own():
     """The packed parts (compacted matrix-core order) of a 32-token page hold
     its rank-r decomposition: unpacked at P = 32 their product meets the bf16
