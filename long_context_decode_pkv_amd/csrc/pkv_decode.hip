@@ -475,12 +475,14 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// (nvalid < 64: the scores of page rows from nvalid on are masked)
-__device__ inline void softmax_probs_lazy(SoftState& st, const floatx4 (&acc)[4], int q4, float (&p)[4][4],
+// (nvalid < 64: the scores of page rows from nvalid on are masked; NT score
+// tiles)
+template <int NT = 4>
+__device__ inline void softmax_probs_lazy(SoftState& st, const floatx4 (&acc)[NT], int q4, float (&p)[NT][4],
                                           int nvalid = kP) {
   float mx = -INFINITY;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < NT; ++mt) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       p[mt][v] = acc[mt][v] + ror8(acc[mt][v]);
@@ -500,7 +502,7 @@ __device__ inline void softmax_probs_lazy(SoftState& st, const floatx4 (&acc)[4]
   const float mref = st.m - 8.f;  // 256 e^(s - m) = 2^(s - (m - 8))
   float ps = 0.f;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < NT; ++mt) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       p[mt][v] = fast_exp2(p[mt][v] - mref);
@@ -1170,9 +1172,12 @@ __device__ __forceinline__ void ldw(uint32_t* d, const uint8_t* p) {
 // LDS budget of a four-wave workgroup at two workgroups per CU (160 KB).
 constexpr int kWgLdsBytes = 80 * 1024;
 
-// PR page rows (32: K2 and V1 without the lanes of page rows 32..63; those
-// lanes read codes of a valid address, which meet masked scores and zero
-// probabilities)
+// PR page rows.  A 32-token page is scored in two 16-row tiles in the
+// compact token order of RopeFactors<N8, 32>: row rho of tile t is token
+// 8 (rho / 4) + 4 t + rho % 4, and slot e of lane quad b of the value
+// contraction's single reduction step is token 8 b + e.  Each lane reads the
+// two K2 units of its rows (adjacent in the stored compacted layout) and the
+// V1 dword of its eight tokens; the stored parts are unchanged.
 template <int N8K, int N8V, int PR = kP>
 struct Int4Factors {
   static constexpr int AK = 2 * N8K, AV = 2 * N8V;  // ranks per lane quad
@@ -1188,6 +1193,7 @@ struct Int4Factors {
   static constexpr bool kKeyDoubleBuffer = false;
   static constexpr bool kRope = false;
   static constexpr int kPageRows = PR;
+  static constexpr int kTiles = PR / 16;  // score tiles of a page
   // Factor pages stream through a per-wave ring of kRingSlots page slots in
   // LDS, filled by direct global -> LDS loads kRingSlots - 1 pages ahead of
   // the page being computed (registers cannot hold that much prefetch).
@@ -1199,21 +1205,21 @@ struct Int4Factors {
   static_assert(kRingSlots >= 2, "an INT4 page pair must fit twice per wave");
 
   struct K {
-    uint32_t k1[RTK][4];  // Rq_K rank tiles, one dword per reduction step
-    uint32_t k2[UK];      // Lq_K units of the 4 page-row tiles
-    uint32_t sr[16];      // sR_K of channels 32 ks + 8 q4 + e: [ks][e] as bf16 pairs
-    uint32_t sl[N8K];     // sL_K of the lane quad's ranks
+    uint32_t k1[RTK][4];                          // Rq_K rank tiles, one dword per reduction step
+    uint32_t k2[PR == kP ? UK : (UK + 1) / 2];     // Lq_K units of the page-row tiles
+    uint32_t sr[16];                              // sR_K of channels 32 ks + 8 q4 + e: [ks][e] as bf16 pairs
+    uint32_t sl[N8K];                             // sL_K of the lane quad's ranks
   };
   struct V {
-    uint32_t v1[RTV][2];  // Lq_V^T rank tiles
-    uint32_t v2[2 * UV];  // Rq_V^T units of the 8 channel tiles
-    uint32_t sl[8];       // sL_V of tokens 16 q4 .. 16 q4 + 15
-    uint32_t sr[16];      // sR_V of channels 16 mt + 4 q4 + v: [mt][v]
+    uint32_t v1[RTV][kTiles / 2];  // Lq_V^T rank tiles
+    uint32_t v2[2 * UV];           // Rq_V^T units of the 8 channel tiles
+    uint32_t sl[2 * kTiles];       // sL_V of the lane quad's tokens (16 q4 .. + 15; compact: 8 q4 .. + 7)
+    uint32_t sr[16];               // sR_V of channels 16 mt + 4 q4 + v: [mt][v]
   };
   struct Query {
     float qf[4][8];
   };
-  using Probs = float[4][4];
+  using Probs = float[kTiles][4];
 
   __device__ static void query(Query& Q, const float (&qs)[4][8], const bf16x8 (&)[4]) {
 #pragma unroll
@@ -1262,9 +1268,28 @@ struct Int4Factors {
       const bool part = kPartK && mt == RTK - 1;
       ldw<4>(R.k1[mt], kp + mt * 1024 + (part ? tl.lam : lane) * 16);
     }
-    // (PR = 32: compacted lanes rho < 8; the others read lane 0's units)
-    const int lk = PR == kP ? lane : ((lane & 15) < 8 ? 8 * (lane >> 4) + (lane & 15) : 0);
-    ldw<UK>(R.k2, kp + kK2 + lk * 4 * UK);
+    if constexpr (PR == kP) {
+      ldw<UK>(R.k2, kp + kK2 + lane * 4 * UK);
+    } else {
+      // rows of tiles 0, 1: tokens 8 (rho / 4) + rho % 4 (+ 4), stored as
+      // units m0, m0 + 1 (m0 = 0 or 2) of compacted lane 8 qk + 4 (rho / 8) + rho % 4
+      const int rho = lane & 15;
+      const int m0 = (2 * (rho >> 2)) & 2;
+      const uint8_t* u = kp + kK2 + (8 * q4 + 4 * (rho >> 3) + (rho & 3)) * 4 * UK;
+      if constexpr (UK == 1) {
+        R.k2[0] = *(const uint32_t*)u >> (8 * m0);
+      } else if constexpr (UK == 2) {
+        R.k2[0] = *(const uint32_t*)(u + 2 * m0);
+      } else if constexpr (UK == 3) {  // 6 bytes from byte 3 m0: two dwords from 2 m0, shifted by m0 bytes
+        const uint32_t x0 = *(const uint32_t*)(u + 2 * m0), x1 = *(const uint32_t*)(u + 2 * m0 + 4);
+        R.k2[0] = __builtin_amdgcn_alignbyte(x1, x0, m0);
+        R.k2[1] = x1 >> (8 * m0);
+      } else {
+        const u32x2 x = *(const u32x2*)(u + 4 * m0);
+        R.k2[0] = x.x;
+        R.k2[1] = x.y;
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) ldw<4>(&R.sr[4 * ks], kp + kSRK + 2 * (32 * ks + 8 * q4));
     ldw<N8K>(R.sl, kp + kSLK + 2 * AK * q4);
@@ -1278,8 +1303,10 @@ struct Int4Factors {
       const bool part = kPartV && mt == RTV - 1;
       if constexpr (PR == kP) {
         ldw<2>(R.v1[mt], vp + mt * 512 + (part ? tl.lam : lane) * 8);
-      } else {  // rows of lanes 0..31 (compacted last tile: 16); lanes 32.. read filler
-        ldw<2>(R.v1[mt], vp + mt * 256 + (part ? (lane < 32 ? tl.lam : 0) : (lane & 31)) * 8);
+      } else {  // tokens 8 q4 .. + 7: stored lane 16 (q4 / 2) + rho, step q4 % 2
+        const int rho = lane & 15;
+        const int lam = part ? (tl.ok ? 8 * (q4 >> 1) + 2 * (rho >> 2) + (rho & 3) : 0) : 16 * (q4 >> 1) + rho;
+        R.v1[mt][0] = *(const uint32_t*)(vp + mt * 256 + lam * 8 + (q4 & 1) * 4);
       }
     }
     if constexpr (UV == 4) {
@@ -1288,8 +1315,12 @@ struct Int4Factors {
     } else {
       ldw<2 * UV>(R.v2, vp + kV2 + lane * 8 * UV);
     }
-    ldw<4>(R.sl, vp + kSLV + 32 * q4);
-    ldw<4>(R.sl + 4, vp + kSLV + 32 * q4 + 16);
+    if constexpr (PR == kP) {
+      ldw<4>(R.sl, vp + kSLV + 32 * q4);
+      ldw<4>(R.sl + 4, vp + kSLV + 32 * q4 + 16);
+    } else {
+      ldw<4>(R.sl, vp + kSLV + 16 * q4);
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) ldw<4>(&R.sr[4 * k], vp + kSRV + 64 * q4 + 16 * k);
   }
@@ -1331,21 +1362,23 @@ struct Int4Factors {
     }
     const bf16x8 tb = __builtin_bit_cast(bf16x8, w);
     const floatx4 base2 = mfma(off, tb, floatx4{0.f, 0.f, 0.f, 0.f});
-    floatx4 as_[4];
+    floatx4 as_[kTiles];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) as_[mt] = mfma(q4_operand<2 * UK, N8K>(q4_unit<UK>(R.k2, mt)), tb, base2);
-    softmax_probs_lazy(st, as_, q4, p, PR);
+    for (int mt = 0; mt < kTiles; ++mt)
+      as_[mt] = mfma(q4_operand<2 * UK, N8K>(q4_unit<UK>(R.k2, mt)), tb, base2);
+    softmax_probs_lazy<kTiles>(st, as_, q4, p);  // (every token of a factorized page is valid)
   }
 
   // Eq. 4, value half on the codes: u = Lt_V^T p, o += Rt_V^T u.
   __device__ static void values(SoftState& st, const V& R, const Probs& p, int q4, float rem) {
     const bf16x8 off = q4_offset_operand();
-    bf16x8 pb[2];
+    constexpr int KS = kTiles / 2;  // reduction steps over the page's tokens
+    bf16x8 pb[KS];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       uint4 w;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {  // tokens 16 q4 + 8 ks + 2k, + 1
+      for (int k = 0; k < 4; ++k) {  // tokens 16 q4 + 8 ks + 2k, + 1 (compact: 8 q4 + 2k, + 1)
         const uint32_t d = R.sl[4 * ks + k];
         const int mt = 2 * ks + k / 2, v = 2 * (k % 2);
         (&w.x)[k] = split2(p[mt][v] * bf16_lo(d), p[mt][v + 1] * bf16_hi(d), rem);
@@ -1353,13 +1386,14 @@ struct Int4Factors {
       pb[ks] = __builtin_bit_cast(bf16x8, w);
     }
     floatx4 base = mfma(off, pb[0], floatx4{0.f, 0.f, 0.f, 0.f});
-    base = mfma(off, pb[1], base);
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks) base = mfma(off, pb[ks], base);
     floatx4 au[RTV];
 #pragma unroll
     for (int mt = 0; mt < RTV; ++mt) {
       au[mt] = base;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) au[mt] = mfma(q4_operand<8, 4>(R.v1[mt][ks]), pb[ks], au[mt]);
+      for (int ks = 0; ks < KS; ++ks) au[mt] = mfma(q4_operand<8, 4>(R.v1[mt][ks]), pb[ks], au[mt]);
     }
     uint4 w = {0u, 0u, 0u, 0u};
 #pragma unroll

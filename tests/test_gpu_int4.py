@@ -138,8 +138,10 @@ def _oracle_parts(d, cache, r_k, r_v):
     (2, 64 * 20 + 63, 1, 2, 8, 8, (0,), 64),
     (2, 64 * 20, 1, 2, 32, 32, (0,), 64),
     (2, 64 * 20 + 9, 1, 2, 20, 12, (0,), 64),
-    (3, 32 * 60 + 5, 1, 2, 24, 24, (0, 3), 32),   # 32-token pages
-    (2, 32 * 40 + 9, 2, 2, 16, 14, (0, 2), 32),
+    (3, 32 * 60 + 5, 1, 2, 24, 24, (0, 3), 32),   # 32-token pages: 3-byte rank units
+    (2, 32 * 40 + 9, 2, 2, 16, 14, (0, 2), 32),   # 2-byte units
+    (2, 32 * 30 + 3, 1, 2, 8, 8, (0, 2), 32),     # 1-byte units
+    (2, 32 * 24 + 30, 1, 2, 32, 32, (0, 5), 32),  # 4-byte units (full rank)
 ])
 def test_int4_attention_on_oracle_codes(cfg_id, T, B, kv, rk, rv, splits, P):
     require_gpu()
