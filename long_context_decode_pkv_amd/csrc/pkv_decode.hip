@@ -318,75 +318,6 @@ __device__ inline void load_values(VRegs<N8>& R, const uint16_t* vp, int lane) {
   }
 }
 
-// The same register images from the parts of 32-token pages (K2 and V1
-// without the operand rows of page rows 32..63): lanes whose rows are absent
-// read a valid address and are zeroed.
-template <int W>
-__device__ inline void zero_unless(RawW<W>& r, bool ok) {
-#pragma unroll
-  for (int k = 0; k < W / 2; ++k) r.d[k] = ok ? r.d[k] : 0u;
-}
-
-template <int N8>
-__device__ inline void load_keys_half(KRegs<N8>& R, const uint16_t* kp, int lane) {
-  using Dm = FactDims<N8>;
-  const TileLane tl = tile_lane(lane);
-#pragma unroll
-  for (int mt = 0; mt < Dm::RT; ++mt) {
-    const bool part = Dm::kPartialTile && (mt == Dm::RT - 1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (!part) {
-        R.k1[mt][ks] = ld16(kp + mt * 2048 + ks * 512 + lane * 8);
-      } else {
-        const bf16x8 v = ld16(kp + mt * 2048 + ks * 256 + tl.lam * 8);
-        R.k1[mt][ks] = tl.ok ? v : bf16x8{};
-      }
-    }
-  }
-  const int rho = lane & 15;
-  const bool ok = rho < 8;                        // page rows 16 (rho / 4) + ...
-  const int lam = ok ? 8 * (lane >> 4) + rho : 0;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const uint16_t* base = kp + Dm::K1 + mt * 32 * Dm::A;
-    ldraw(R.k2a[mt], base + lam * Dm::W0);
-    zero_unless(R.k2a[mt], ok);
-    if constexpr (Dm::KS2 > 1) {
-      ldraw(R.k2b[mt], base + 256 + lam * Dm::W1);
-      zero_unless(R.k2b[mt], ok);
-    }
-  }
-}
-
-template <int N8>
-__device__ inline void load_values_half(VRegs<N8>& R, const uint16_t* vp, int lane) {
-  using Dm = FactDims<N8>;
-  const TileLane tl = tile_lane(lane);
-  const bool lo = lane < 32;  // page rows 16 (lane / 16) + ...
-  const bool pok = tl.ok && lo;
-#pragma unroll
-  for (int mt = 0; mt < Dm::RT; ++mt) {
-    const bool part = Dm::kPartialTile && (mt == Dm::RT - 1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (!part) {
-        const bf16x8 v = ld16(vp + mt * 512 + ks * 256 + (lane & 31) * 8);
-        R.v1[mt][ks] = lo ? v : bf16x8{};
-      } else {
-        const bf16x8 v = ld16(vp + mt * 512 + ks * 128 + (pok ? tl.lam : 0) * 8);
-        R.v1[mt][ks] = pok ? v : bf16x8{};
-      }
-    }
-  }
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    const uint16_t* base = vp + Dm::V1 / 2 + mt * 64 * Dm::A;
-    ldraw(R.v2a[mt], base + lane * Dm::W0);
-    if constexpr (Dm::KS2 > 1) ldraw(R.v2b[mt], base + 512 + lane * Dm::W1);
-  }
-}
-
 struct SoftState {
   float m, l;
   floatx4 o[8];
@@ -667,24 +598,98 @@ struct Bf16Factors {
 };
 
 // bf16 factors of 32-token pages (the page length of Sec. 4.1), ranks
-// 8 N8K, 8 N8V <= 32: Bf16Factors' contractions in the 64-row frame with
-// page rows 32..63 absent (zero operands, masked scores).
+// 8 N8K, 8 N8V <= 32, in the two-tile compact token order of
+// RopeFactors<N8, 32>: score row 4 b + v of tile t is token 8 b + 4 t + v,
+// slot e of lane quad b of the value contraction's one reduction step is
+// token 8 b + e.  Each lane loads its tokens' K2 rows and V1 columns from
+// the stored compacted 64-row layout.
 template <int N8K, int N8V = N8K>
 struct Bf16Half : Bf16Factors<N8K, N8V> {
+  static_assert(N8K <= 4 && N8V <= 4, "ranks up to the page length");
   static constexpr int kPageRows = kMinP;
   using Base = Bf16Factors<N8K, N8V>;
-  using typename Base::K;
-  using typename Base::V;
   using typename Base::Query;
   using typename Base::Probs;
+  using DK = FactDims<N8K>;
+  using DV = FactDims<N8V>;
+  struct K {
+    bf16x8 k1[DK::RT][4];
+    RawW<DK::W0> k2a[2];
+  };
+  struct V {
+    bf16x8 v1[DV::RT];
+    RawW<DV::W0> v2a[8];
+  };
   __device__ static void load_keys(K& R, const uint8_t* kp, int lane) {
-    pkv::load_keys_half<N8K>(R, (const uint16_t*)kp, lane);
+    const uint16_t* p = (const uint16_t*)kp;
+    const TileLane tl = tile_lane(lane);
+#pragma unroll
+    for (int mt = 0; mt < DK::RT; ++mt) {
+      const bool part = DK::kPartialTile && mt == DK::RT - 1;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (!part) {
+          R.k1[mt][ks] = ld16(p + mt * 2048 + ks * 512 + lane * 8);
+        } else {
+          const bf16x8 v = ld16(p + mt * 2048 + ks * 256 + tl.lam * 8);
+          R.k1[mt][ks] = tl.ok ? v : bf16x8{};
+        }
+      }
+    }
+    // row rho of tile t: token 8 (rho / 4) + 4 t + rho % 4, stored as page
+    // row 16 bq + 4 mt + v of the compacted K2 at lane 8 qk + 4 bq + v
+    const int rho = lane & 15, qk = lane >> 4;
+    const int lam = 8 * qk + 4 * (rho >> 3) + (rho & 3);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      ldraw(R.k2a[t], p + DK::K1 + ((2 * (rho >> 2) + t) & 3) * 32 * DK::A + lam * DK::W0);
   }
   __device__ static void load_values(V& R, const uint8_t* vp, int lane) {
-    pkv::load_values_half<N8V>(R, (const uint16_t*)vp, lane);
+    // tokens 8 b .. 8 b + 7 of lane quad b: stored lane 16 (b / 2) + rho, step b % 2
+    const uint16_t* p = (const uint16_t*)vp;
+    const int rho = lane & 15, b = lane >> 4;
+    const TileLane tl = tile_lane(lane);
+#pragma unroll
+    for (int mt = 0; mt < DV::RT; ++mt) {
+      const bool part = DV::kPartialTile && mt == DV::RT - 1;
+      if (!part) {
+        R.v1[mt] = ld16(p + mt * 512 + (b & 1) * 256 + (16 * (b >> 1) + rho) * 8);
+      } else {
+        const int lam = tl.ok ? 8 * (b >> 1) + 2 * (rho >> 2) + (rho & 3) : 0;
+        const bf16x8 v = ld16(p + mt * 512 + (b & 1) * 128 + lam * 8);
+        R.v1[mt] = tl.ok ? v : bf16x8{};
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) ldraw(R.v2a[mt], p + DV::V1 / 2 + mt * 64 * DV::A + lane * DV::W0);
   }
+  // Eq. 4, key half: t = Rf_K q, s = Lf_K t over the two tiles, online softmax
   __device__ static void keys(SoftState& st, const K& R, const Query& Q, int q4, float rem, Probs& pb) {
-    fact_keys<N8K>(st, R, Q.qb, q4, rem, pb, kMinP);
+    floatx4 at[DK::RT];
+#pragma unroll
+    for (int mt = 0; mt < DK::RT; ++mt) {
+      at[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) at[mt] = mfma(R.k1[mt][ks], Q.qb[ks], at[mt]);
+    }
+    bf16x8 tb[DK::KS2];
+    rank_operand<N8K>(at, rem, tb);
+    floatx4 as_[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) as_[t] = mfma(operand(R.k2a[t]), tb[0], floatx4{0.f, 0.f, 0.f, 0.f});
+    bf16x8 p1[1];
+    softmax_page<2>(st, as_, kP, q4, rem, p1);  // (every token of a factorized page is valid)
+    pb[0] = p1[0];
+  }
+  // Eq. 4, value half: u = Lf_V^T p in one reduction step, o += Rf_V^T u
+  __device__ static void values(SoftState& st, const V& R, const Probs& pb, int, float rem) {
+    floatx4 au[DV::RT];
+#pragma unroll
+    for (int mt = 0; mt < DV::RT; ++mt) au[mt] = mfma(R.v1[mt], pb[0], floatx4{0.f, 0.f, 0.f, 0.f});
+    bf16x8 ub[DV::KS2];
+    rank_operand<N8V>(au, rem, ub);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) st.o[mt] = mfma(operand(R.v2a[mt]), ub[0], st.o[mt]);
   }
 };
 
