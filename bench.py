@@ -42,16 +42,16 @@ CACHE_DIR = os.environ.get("PKV_BENCH_CACHE", "/tmp/pkv_bench_inputs")
 # HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc runs of
 # this script (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled
 # by what the same counter reads for the 1 GiB device copy of `--workload copy`
-# (FETCH_SIZE reads 524303.7 KiB for 2^30 bytes read -> x1.99994; WRITE_SIZE
+# (FETCH_SIZE reads 524301.6 KiB for 2^30 bytes read -> x1.99995; WRITE_SIZE
 # reads 1048576 KiB for 2^30 bytes written -> x1.0).  A figure holds only for
 # the kernel sources whose hash it carries; any change to them makes it null.
 PMC_TRAFFIC = {
-    "qwen3-32b-layer-128k": {"sha256": "5a65b61696390013c987df3d177b13e8e88c057dbfcbbec93547f4e236d487ed",
-                           "fetch": 303079359, "write": 1114112},
-    "qwen3-32b-layer-128k-int4": {"sha256": "5a65b61696390013c987df3d177b13e8e88c057dbfcbbec93547f4e236d487ed",
-                                "fetch": 88824835, "write": 2228224},
-    "llama3.1-8b-layer-p32": {"sha256": "5a65b61696390013c987df3d177b13e8e88c057dbfcbbec93547f4e236d487ed",
-                            "fetch": 673921733, "write": 1114112},
+    "qwen3-32b-layer-128k": {"sha256": "78ac5de6c1f14392fba7f2da396b51d9282a597e50ffc51869bbf568572e90cf",
+                           "fetch": 303082007, "write": 1114112},
+    "qwen3-32b-layer-128k-int4": {"sha256": "78ac5de6c1f14392fba7f2da396b51d9282a597e50ffc51869bbf568572e90cf",
+                                "fetch": 88817613, "write": 2228224},
+    "llama3.1-8b-layer-p32": {"sha256": "78ac5de6c1f14392fba7f2da396b51d9282a597e50ffc51869bbf568572e90cf",
+                            "fetch": 673830841, "write": 1114112},
 }
 TRAFFIC_SOURCES = ("long_context_decode_pkv_amd/csrc/pkv_decode.hip",
                    "long_context_decode_pkv_amd/csrc/pkv_internal.h")
