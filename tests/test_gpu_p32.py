@@ -4,10 +4,12 @@
 page being filled kept dense).
 
 Such caches keep their factor parts in the 64-token matrix-core operand
-order with the operand rows of page rows 32..63 left out.  bf16 caches with
-equal padded ranks, pre-RoPE keys included, are attended by the matrix-core
-kernel in its 64-row frame (absent rows zero, their scores masked); fp32
-caches and unequal padded ranks by the vector-ALU kernel.  A 32-row page is
+order with the operand rows of page rows 32..63 left out.  bf16 caches
+(any rank pair up to 32; pre-RoPE keys at equal padded ranks) and INT4
+caches are attended by the matrix-core kernel, which reads a factorized page
+in a two-tile compact token order and dense pages in the 64-row frame
+(absent rows zero, their scores masked); fp32 caches and pre-RoPE keys with
+unequal padded ranks by the vector-ALU kernel.  A 32-row page is
 decomposed on the leading 32 x 32 block of its zero-padded 64-row Gram
 matrix.  Gates as for 64-token pages: bf16 storage 1e-2, fp32 storage 1e-4,
 relative to max |o_ref|; stored factors meet the reconstruction bound of the
@@ -56,7 +58,7 @@ def _case(cfg_id, T, B=1, kv_heads=2, rk=RK, rv=RV, s=S, w=W, splits=(0,), rope=
     (2, 32 * 64, 1, 2, RK, RV, (0, 7)),         # page-aligned T
     (2, 32 * 20 + 31, 1, 1, 32, 32, (0,)),     # full rank of a 32-token page
     (2, 32 * 20 + 1, 1, 2, 1, 3, (0, 2)),      # tiny ranks
-    (2, 32 * 20 + 9, 1, 2, 8, 24, (0, 2)),     # unequal padded ranks: vector-ALU kernel
+    (2, 32 * 20 + 9, 1, 2, 8, 24, (0, 2)),     # unequal padded ranks (compacted K1 and V1 tiles)
     (2, 32 * 33 + 17, 1, 2, 24, 24, (0, 4)),   # odd n8: compacted last rank tile
     (1, 32 * 30 + 17, 1, 1, RK, RV, (0, 3)),   # fp32 storage
     (1, 32 * 12, 1, 1, 32, 32, (0,)),          # fp32, full rank
