@@ -107,10 +107,13 @@ typedef struct pkv_shape {
  *   page_table [max_pages] int32: (class << 24) | slot
  * total_bytes is the page table's end rounded up to 256.
  * Factor parts (PKV_BF16, PKV_F32) use a fixed interleaved order matched to
- * the attention kernel's matrix-core register layout, with the rank padded
- * to r8 = 8 ceil(r / 8) (padding ranks hold zeros), so a part holds
- * r8 (P + d) elements at either page length.  A P = 32 part is the P = 64
- * order with the operand rows of page rows 32..63 left out.
+ * the attention kernel's matrix-core register layout.  The Lf operands, and
+ * Rf of key parts, pad the rank to r8 = 8 ceil(r / 8) (padding ranks hold
+ * zeros); Rf of value parts keeps r2 = r rounded up to even when r8 <= 32
+ * (r8 otherwise).  A key part holds r8 (P + d) elements, a value part
+ * r8 P + r2 d, at either page length (the same count when 8 divides r).  A
+ * P = 32 part is the P = 64 order with the operand rows of page rows 32..63
+ * left out.
  * pkv_pack_factors and pkv_unpack_factors convert between a part and
  * row-major Lf (P x r), Rf (r x d).
  * PKV_BF16_INT4 parts hold codes and scales in their own interleaved order
@@ -128,7 +131,7 @@ typedef struct pkv_layout {
   int64_t dense_page_bytes;  /* P * d * elem_bytes */
   int64_t factor_k_elems;    /* packed elements (INT4: codes) of a K part: r8_K (P + d),
                                 r8 = 8 ceil(r / 8), at P = 64 and P = 32 */
-  int64_t factor_v_elems;    /* r8_V (P + d) */
+  int64_t factor_v_elems;    /* of a V part: r8_V P + r2_V d (INT4: codes, r8_V (P + d)) */
   int64_t factor_page_bytes; /* factor_k_bytes + factor_v_bytes */
   int64_t factor_k_bytes;    /* bytes of a K part (its offset in the page is 0): elems x
                                 elem_bytes, or pkv_factor_part_bytes for INT4 */
@@ -160,11 +163,13 @@ double pkv_storage_ratio(int32_t P, int32_t r_k, int32_t r_v, int32_t d);
 int32_t pkv_classify(int64_t T, int32_t P, int32_t s, int32_t w, int64_t n_fact, int32_t* cls,
                      int32_t* slot, int64_t n_pages);
 
-/* Packed elements of one factor part for rank r: r8 (P + d) with r8 = r
- * rounded up to a multiple of 8, at P = 64 and at P = 32.  Errors:
- * UNSUPPORTED for other P or d != 128; INVALID_ARG unless 1 <= r <= P.
- * Host only. */
-int32_t pkv_factor_part_elems(int32_t P, int32_t d, int32_t r, int64_t* elems);
+/* Packed elements of one factor part of `kind` (pkv_factor_kind) for rank r,
+ * at P = 64 and at P = 32: r8 (P + d) for PKV_KEYS and PKV_KEYS_PRE_ROPE,
+ * r8 P + r2 d for PKV_VALUES, with r8 = r rounded up to a multiple of 8 and
+ * r2 = r rounded up to even (r2 = r8 when r8 > 32).  Errors: UNSUPPORTED
+ * for other P or d != 128; INVALID_ARG for another kind or unless
+ * 1 <= r <= P.  Host only. */
+int32_t pkv_factor_part_elems(int32_t kind, int32_t P, int32_t d, int32_t r, int64_t* elems);
 
 /*
  * Host-side conversion between row-major factors (float32 Lf [P][r] with
@@ -179,8 +184,8 @@ int32_t pkv_unpack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_
                            const void* packed, float* Lf, float* Rf);
 
 /* Bytes of one factor part (kind: any pkv_factor_kind) of rank r in
- * storage format `dtype`.  PKV_BF16 / PKV_F32: r8 (P + d) elements of 2 / 4
- * bytes.  PKV_BF16_INT4 (the INT4 part of Sec. 4.3; K and V parts differ),
+ * storage format `dtype`.  PKV_BF16 / PKV_F32: pkv_factor_part_elems
+ * elements of 2 / 4 bytes.  PKV_BF16_INT4 (the INT4 part of Sec. 4.3; K and V parts differ),
  * with A = r8 / 4 codes in a rank unit of ub = A / 2 bytes (a nibble per
  * code: 1, 2, 3 or 4 bytes; 3-byte units start at any byte), and h = 1 at
  * P = 64, 2 at P = 32:

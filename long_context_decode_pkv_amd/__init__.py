@@ -69,7 +69,7 @@ def lib():
         "pkv_version": ([], ctypes.c_char_p),
         "pkv_storage_ratio": ([i32, i32, i32, i32], ctypes.c_double),
         "pkv_classify": ([i64, i32, i32, i32, i64, vp, vp, i64], i32),
-        "pkv_factor_part_elems": ([i32, i32, i32, P(i64)], i32),
+        "pkv_factor_part_elems": ([i32, i32, i32, i32, P(i64)], i32),
         "pkv_pack_factors": ([i32, i32, i32, i32, i32, vp, vp, vp], i32),
         "pkv_unpack_factors": ([i32, i32, i32, i32, i32, vp, vp, vp], i32),
         "pkv_factor_part_bytes": ([i32, i32, i32, i32, i32, P(i64)], i32),
@@ -176,9 +176,10 @@ def classify(T: int, P: int, s: int, w: int, n_fact: int = -1, n_pages: int | No
     return cls, slot
 
 
-def factor_part_elems(r: int, P: int = PAGE_LEN, d: int = HEAD_DIM) -> int:
+def factor_part_elems(kind: int, r: int, P: int = PAGE_LEN, d: int = HEAD_DIM) -> int:
+    """Elements of one packed factor part of `kind` (KEYS, VALUES, KEYS_PRE_ROPE)."""
     n = ctypes.c_int64()
-    _check(lib().pkv_factor_part_elems(P, d, r, ctypes.byref(n)), "pkv_factor_part_elems")
+    _check(lib().pkv_factor_part_elems(kind, P, d, r, ctypes.byref(n)), "pkv_factor_part_elems")
     return n.value
 
 
@@ -189,7 +190,7 @@ def pack_factors(kind: int, r: int, dtype: int, Lf, Rf, P: int = PAGE_LEN) -> np
     Rf = np.ascontiguousarray(Rf, dtype=np.float32)
     if Lf.shape != (P, r) or Rf.shape != (r, HEAD_DIM):
         raise ValueError("factor shapes do not match the part")
-    n = factor_part_elems(r, P)
+    n = factor_part_elems(kind, r, P)
     out = np.zeros(n, dtype=np.uint16 if dtype == BF16 else np.float32)
     _check(lib().pkv_pack_factors(kind, P, HEAD_DIM, r, dtype, _np_ptr(Lf), _np_ptr(Rf),
                                   _np_ptr(out)), "pkv_pack_factors")
@@ -199,7 +200,7 @@ def pack_factors(kind: int, r: int, dtype: int, Lf, Rf, P: int = PAGE_LEN) -> np
 def unpack_factors(kind: int, r: int, dtype: int, packed, P: int = PAGE_LEN):
     """One packed factor part -> float32 Lf (P x r), Rf (r x d)."""
     packed = np.ascontiguousarray(packed, dtype=np.uint16 if dtype == BF16 else np.float32)
-    if packed.size < factor_part_elems(r, P):
+    if packed.size < factor_part_elems(kind, r, P):
         raise ValueError("packed part too small")
     Lf = np.zeros((P, r), dtype=np.float32)
     Rf = np.zeros((r, HEAD_DIM), dtype=np.float32)

@@ -88,8 +88,9 @@ void make_layout(const pkv_shape* s, pkv_layout* L) {
   const int64_t fmax = s->max_tokens / P - n_s - n_w;
   L->max_fact_pages = fmax > 0 ? fmax : 0;
   L->dense_page_bytes = P * d * L->elem_bytes;
-  L->factor_k_elems = part_elems(s->rank_k, (int)P);
-  L->factor_v_elems = part_elems(s->rank_v, (int)P);
+  L->factor_k_elems = part_elems(PKV_KEYS, s->rank_k, (int)P);
+  // (INT4 value parts keep the padded code count of their own layout)
+  L->factor_v_elems = part_elems(s->dtype == PKV_BF16_INT4 ? PKV_KEYS : PKV_VALUES, s->rank_v, (int)P);
   if (s->dtype == PKV_BF16_INT4) {
     L->factor_k_bytes = q4_dims(s->rank_k, (int)P).k_bytes;
     L->factor_v_bytes = q4_dims(s->rank_v, (int)P).v_bytes;
@@ -379,21 +380,21 @@ int32_t pkv_classify(int64_t T, int32_t P, int32_t s, int32_t w, int64_t n_fact,
   return PKV_OK;
 }
 
-int32_t pkv_factor_part_elems(int32_t P, int32_t d, int32_t r, int64_t* elems) {
-  if (!elems) return PKV_ERR_INVALID_ARG;
+int32_t pkv_factor_part_elems(int32_t kind, int32_t P, int32_t d, int32_t r, int64_t* elems) {
+  if (!elems || (kind != PKV_KEYS && kind != PKV_VALUES && kind != PKV_KEYS_PRE_ROPE))
+    return PKV_ERR_INVALID_ARG;
   if ((P != kP && P != kMinP) || d != kD) return PKV_ERR_UNSUPPORTED;
   if (r < 1 || r > P) return PKV_ERR_INVALID_ARG;
-  *elems = part_elems(r, P);
+  *elems = part_elems(kind, r, P);
   return PKV_OK;
 }
 
 int32_t pkv_pack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t dtype,
                          const float* Lf, const float* Rf, void* packed) {
   int64_t n;
-  int32_t st = pkv_factor_part_elems(P, d, r, &n);
+  int32_t st = pkv_factor_part_elems(kind, P, d, r, &n);
   if (st != PKV_OK) return st;
-  if ((kind != PKV_KEYS && kind != PKV_VALUES && kind != PKV_KEYS_PRE_ROPE) ||
-      (dtype != PKV_BF16 && dtype != PKV_F32) || !Lf || !Rf || !packed)
+  if ((dtype != PKV_BF16 && dtype != PKV_F32) || !Lf || !Rf || !packed)
     return PKV_ERR_INVALID_ARG;
   const PackDims pd = pack_dims(r, P);
   const int r8 = 8 * pd.n8;
@@ -406,8 +407,9 @@ int32_t pkv_pack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t 
       ((float*)packed)[idx] = v;
     }
   };
+  const int r_rf = kind == PKV_VALUES ? pd.r2 : r8;  // ranks the Rf operand stores
   for (int i = 0; i < r8; ++i) {
-    for (int c = 0; c < kD; ++c) {
+    for (int c = 0; c < kD && i < r_rf; ++c) {
       const float v = i < r ? Rf[(int64_t)i * kD + c] : 0.f;
       put(off_rf(kind, pd, i, c), v);
     }
@@ -422,10 +424,9 @@ int32_t pkv_pack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t 
 int32_t pkv_unpack_factors(int32_t kind, int32_t P, int32_t d, int32_t r, int32_t dtype,
                            const void* packed, float* Lf, float* Rf) {
   int64_t n;
-  int32_t st = pkv_factor_part_elems(P, d, r, &n);
+  int32_t st = pkv_factor_part_elems(kind, P, d, r, &n);
   if (st != PKV_OK) return st;
-  if ((kind != PKV_KEYS && kind != PKV_VALUES && kind != PKV_KEYS_PRE_ROPE) ||
-      (dtype != PKV_BF16 && dtype != PKV_F32) || !Lf || !Rf || !packed)
+  if ((dtype != PKV_BF16 && dtype != PKV_F32) || !Lf || !Rf || !packed)
     return PKV_ERR_INVALID_ARG;
   const PackDims pd = pack_dims(r, P);
   auto get = [&](int64_t idx) -> float {
@@ -453,7 +454,7 @@ int32_t pkv_factor_part_bytes(int32_t kind, int32_t P, int32_t d, int32_t r, int
   if ((P != kP && P != kMinP) || d != kD) return PKV_ERR_UNSUPPORTED;
   if (r < 1 || r > P) return PKV_ERR_INVALID_ARG;
   if (dtype == PKV_BF16 || dtype == PKV_F32) {
-    *bytes = part_elems(r, P) * (dtype == PKV_BF16 ? 2 : 4);
+    *bytes = part_elems(kind, r, P) * (dtype == PKV_BF16 ? 2 : 4);
     return PKV_OK;
   }
   if (dtype != PKV_BF16_INT4) return PKV_ERR_INVALID_ARG;

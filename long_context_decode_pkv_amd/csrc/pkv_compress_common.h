@@ -140,11 +140,13 @@ __device__ inline PageRef page_ref(const CompressBatch& jb, int64_t n, int elem_
 // Packed factor part of a cache job's page.
 __device__ inline uint8_t* factor_part(const CompressJob&, const PageRef& p) { return p.part; }
 
-// Destination of factor element Rf[i][c] (i < r_store) and Lf[j][i].
+// Destination of factor element Rf[i][c] (i < rf_store) and Lf[j][i]
+// (i < r_store): a packed part stores Lf at r8 ranks, zero-padded, and Rf at
+// r8 (key parts) or at its even-rounded rank r2 (value parts).
 struct FactorDst {
   bool packed;
   PackDims pd;
-  int r, r_store, kind;
+  int r, r_store, rf_store, kind;
   int P;
   int64_t n;
   void* rf;
@@ -156,6 +158,7 @@ struct FactorDst {
     P = p.P;
     r_store = packed ? 8 * pd.n8 : p.r;
     kind = p.kind == 0 ? job.key_part_kind : PKV_VALUES;  // part layout
+    rf_store = packed && kind == PKV_VALUES ? pd.r2 : r_store;
     n = n_;
     if (packed) {
       rf = lf = factor_part(job, p);

@@ -951,11 +951,11 @@ __device__ __forceinline__ void compress_tri_one(const J& jobs, int64_t n, TriSh
   const FactorDst dst(job, pr, n);
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
-    if (16 * mi < dst.r_store) {
+    if (16 * mi < dst.rf_store) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int i = 16 * mi + 4 * q + v;
-        if (i < dst.r_store) {
+        if (i < dst.rf_store) {
           const float sg = i < r ? sh.sig[i] : 0.f;
           const float inv = sg > 0.f ? 1.f / sg : 0.f;
 #pragma unroll

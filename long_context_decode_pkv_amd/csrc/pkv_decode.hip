@@ -293,6 +293,37 @@ __device__ inline void load_keys(KRegs<N8>& R, const uint16_t* kp, int lane) {
   }
 }
 
+// A lane's V2 operand in a value part stored at its exact rank (r8 <= 32):
+// element offset within a channel tile and the tile's elements (16 r2).  A
+// lane loads its quad's A slots from there.  Slots past its own ranks (the
+// partial quad's last A - ap, every slot of a quad beyond it) read other
+// lanes' values of the same tile.  They meet the u entries of ranks >= r2,
+// which are exactly zero: Lf_V^T stores zero rows for ranks >= r.
+struct V2Lane {
+  int off, tile;
+};
+
+__device__ inline V2Lane v2_lane(int r, int A, int lane) {
+  const int r2 = r + (r & 1), nf = r2 / A, ap = r2 % A;
+  const int rho = lane & 15, qk = lane >> 4;
+  V2Lane v;
+  v.tile = 16 * r2;
+  if (qk < nf) v.off = 16 * ap + (16 * qk + rho) * A;
+  else if (qk == nf && ap > 0) v.off = rho * ap;  // the partial quad: ap of its A slots
+  else v.off = 0;                                  // no ranks
+  return v;
+}
+
+// V2 of a value part in the exact-rank order, through the lane's V2Lane (v2
+// points at the operand).
+template <int N8, bool EV>
+__device__ inline void load_v2(VRegs<N8>& R, const uint16_t* v2, int, const V2Lane& vl) {
+  using Dm = FactDims<N8>;
+  static_assert(EV && Dm::KS2 == 1, "exact-rank V2 up to r8 = 32");
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) ldraw(R.v2a[mt], v2 + mt * vl.tile + vl.off);
+}
+
 template <int N8>
 __device__ inline void load_values(VRegs<N8>& R, const uint16_t* vp, int lane) {
   using Dm = FactDims<N8>;
@@ -316,6 +347,27 @@ __device__ inline void load_values(VRegs<N8>& R, const uint16_t* vp, int lane) {
     ldraw(R.v2a[mt], base + lane * Dm::W0);
     if constexpr (Dm::KS2 > 1) ldraw(R.v2b[mt], base + 512 + lane * Dm::W1);
   }
+}
+
+// The same from a value part whose V2 holds the exact rank.
+template <int N8>
+__device__ inline void load_values_ev(VRegs<N8>& R, const uint16_t* vp, int lane, const V2Lane& vl) {
+  using Dm = FactDims<N8>;
+  const TileLane tl = tile_lane(lane);
+#pragma unroll
+  for (int mt = 0; mt < Dm::RT; ++mt) {
+    const bool part = Dm::kPartialTile && (mt == Dm::RT - 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (!part) {
+        R.v1[mt][ks] = ld16(vp + mt * 1024 + ks * 512 + lane * 8);
+      } else {
+        const bf16x8 v = ld16(vp + mt * 1024 + ks * 256 + tl.lam * 8);
+        R.v1[mt][ks] = tl.ok ? v : bf16x8{};
+      }
+    }
+  }
+  load_v2<N8, true>(R, vp + Dm::V1, lane, vl);
 }
 
 struct SoftState {
@@ -556,8 +608,11 @@ constexpr int mfma_waves_per_simd(int n8) { return n8 <= 6 ? 2 : 1; }
 
 // bf16 factors Lf = U Sigma, Rf = W^T (Sec. 3.3, Eq. 2), key rank 8 N8K and
 // value rank 8 N8V (each part in its own rank's operand order).
-template <int N8K, int N8V = N8K>
+// EV: the value part's V2 at its exact rank (r_V not a multiple of 8).
+template <int N8K, int N8V = N8K, bool EV = false>
 struct Bf16Factors {
+  static constexpr bool kExactV = EV;
+  static constexpr int kAV = 2 * N8V;  // value ranks per lane quad
   static constexpr int kN8Max = N8K > N8V ? N8K : N8V;
   static constexpr int kWavesPerSimd = mfma_waves_per_simd(kN8Max);
   // Key parts double-buffered where the extra page half fits the budget
@@ -589,6 +644,9 @@ struct Bf16Factors {
   __device__ static void load_values(V& R, const uint8_t* vp, int lane) {
     pkv::load_values<N8V>(R, (const uint16_t*)vp, lane);
   }
+  __device__ static void load_values(V& R, const uint8_t* vp, int lane, const V2Lane& vl) {
+    pkv::load_values_ev<N8V>(R, (const uint16_t*)vp, lane, vl);
+  }
   __device__ static void keys(SoftState& st, const K& R, const Query& Q, int q4, float rem, Probs& pb) {
     fact_keys<N8K>(st, R, Q.qb, q4, rem, pb);
   }
@@ -603,11 +661,11 @@ struct Bf16Factors {
 // slot e of lane quad b of the value contraction's one reduction step is
 // token 8 b + e.  Each lane loads its tokens' K2 rows and V1 columns from
 // the stored compacted 64-row layout.
-template <int N8K, int N8V = N8K>
-struct Bf16Half : Bf16Factors<N8K, N8V> {
+template <int N8K, int N8V = N8K, bool EV = false>
+struct Bf16Half : Bf16Factors<N8K, N8V, EV> {
   static_assert(N8K <= 4 && N8V <= 4, "ranks up to the page length");
   static constexpr int kPageRows = kMinP;
-  using Base = Bf16Factors<N8K, N8V>;
+  using Base = Bf16Factors<N8K, N8V, EV>;
   using typename Base::Query;
   using typename Base::Probs;
   using DK = FactDims<N8K>;
@@ -644,9 +702,8 @@ struct Bf16Half : Bf16Factors<N8K, N8V> {
     for (int t = 0; t < 2; ++t)
       ldraw(R.k2a[t], p + DK::K1 + ((2 * (rho >> 2) + t) & 3) * 32 * DK::A + lam * DK::W0);
   }
-  __device__ static void load_values(V& R, const uint8_t* vp, int lane) {
-    // tokens 8 b .. 8 b + 7 of lane quad b: stored lane 16 (b / 2) + rho, step b % 2
-    const uint16_t* p = (const uint16_t*)vp;
+  // tokens 8 b .. 8 b + 7 of lane quad b: stored lane 16 (b / 2) + rho, step b % 2
+  __device__ static void load_v1(V& R, const uint16_t* p, int lane) {
     const int rho = lane & 15, b = lane >> 4;
     const TileLane tl = tile_lane(lane);
 #pragma unroll
@@ -660,8 +717,18 @@ struct Bf16Half : Bf16Factors<N8K, N8V> {
         R.v1[mt] = tl.ok ? v : bf16x8{};
       }
     }
+  }
+  __device__ static void load_values(V& R, const uint8_t* vp, int lane) {
+    const uint16_t* p = (const uint16_t*)vp;
+    load_v1(R, p, lane);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) ldraw(R.v2a[mt], p + DV::V1 / 2 + mt * 64 * DV::A + lane * DV::W0);
+  }
+  __device__ static void load_values(V& R, const uint8_t* vp, int lane, const V2Lane& vl) {
+    const uint16_t* p = (const uint16_t*)vp;
+    load_v1(R, p, lane);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) ldraw(R.v2a[mt], p + DV::V1 / 2 + mt * vl.tile + vl.off);
   }
   // Eq. 4, key half: t = Rf_K q, s = Lf_K t over the two tiles, online softmax
   __device__ static void keys(SoftState& st, const K& R, const Query& Q, int q4, float rem, Probs& pb) {
@@ -882,9 +949,11 @@ constexpr int kRopeMfmaMaxN8 = 4;
 // reduction step is token 8 b + e (eight consecutive tokens of the stored
 // Lf_V^T).  Only the loads follow this order; the stored parts are the
 // compacted 64-row layout.
-template <int N8, int PR = kP>
+template <int N8, int PR = kP, bool EV = false>
 struct RopeFactors {
   using Dm = FactDims<N8>;
+  static constexpr bool kExactV = EV;
+  static constexpr int kAV = 2 * N8;
   static constexpr int kWavesPerSimd = mfma_waves_per_simd(N8);
   static constexpr bool kKeyDoubleBuffer = false;
   static constexpr bool kLdsRing = false;
@@ -952,33 +1021,45 @@ struct RopeFactors {
       }
     }
   }
+  // V1 of a 32-token page in the single reduction step: lane (rho, b) takes
+  // tokens 8 b .. 8 b + 7, stored at lane 16 (b / 2) + rho, step b % 2 (a
+  // compacted last rank tile: rows v < 2 of each lane quad only)
+  __device__ static void load_v1_half(V& R, const uint16_t* p, int lane) {
+    const int rho = lane & 15, b = lane >> 4;
+    const TileLane tl = tile_lane(lane);
+#pragma unroll
+    for (int mt = 0; mt < Dm::RT; ++mt) {
+      const bool part = Dm::kPartialTile && mt == Dm::RT - 1;
+      if (!part) {
+        R.v1[mt][0] = ld16(p + mt * 512 + (b & 1) * 256 + (16 * (b >> 1) + rho) * 8);
+      } else {
+        const int lam = tl.ok ? 8 * (b >> 1) + 2 * (rho >> 2) + (rho & 3) : 0;
+        const bf16x8 v = ld16(p + mt * 512 + (b & 1) * 128 + lam * 8);
+        R.v1[mt][0] = tl.ok ? v : bf16x8{};
+      }
+    }
+  }
   __device__ static void load_values(V& R, const uint8_t* vp, int lane) {
     if constexpr (PR == kP) {
       pkv::load_values<N8>(R, (const uint16_t*)vp, lane);
     } else {
-      // V1 in the single reduction step: lane (rho, b) takes tokens
-      // 8 b .. 8 b + 7, stored at lane 16 (b / 2) + rho, step b % 2 (a
-      // compacted last rank tile: rows v < 2 of each lane quad only)
       const uint16_t* p = (const uint16_t*)vp;
-      const int rho = lane & 15, b = lane >> 4;
-      const TileLane tl = tile_lane(lane);
-#pragma unroll
-      for (int mt = 0; mt < Dm::RT; ++mt) {
-        const bool part = Dm::kPartialTile && mt == Dm::RT - 1;
-        if (!part) {
-          R.v1[mt][0] = ld16(p + mt * 512 + (b & 1) * 256 + (16 * (b >> 1) + rho) * 8);
-        } else {
-          const int lam = tl.ok ? 8 * (b >> 1) + 2 * (rho >> 2) + (rho & 3) : 0;
-          const bf16x8 v = ld16(p + mt * 512 + (b & 1) * 128 + lam * 8);
-          R.v1[mt][0] = tl.ok ? v : bf16x8{};
-        }
-      }
+      load_v1_half(R, p, lane);
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         const uint16_t* base = p + Dm::V1 / 2 + mt * 64 * Dm::A;
         ldraw(R.v2a[mt], base + lane * Dm::W0);
         if constexpr (Dm::KS2 > 1) ldraw(R.v2b[mt], base + 512 + lane * Dm::W1);
       }
+    }
+  }
+  __device__ static void load_values(V& R, const uint8_t* vp, int lane, const V2Lane& vl) {
+    if constexpr (PR == kP) {
+      pkv::load_values_ev<N8>(R, (const uint16_t*)vp, lane, vl);
+    } else {
+      const uint16_t* p = (const uint16_t*)vp;
+      load_v1_half(R, p, lane);
+      load_v2<N8, true>(R, p + Dm::V1 / 2, lane, vl);
     }
   }
   // token tile mt: K_p^T columns = its 16 tokens, 8 channel tiles of rows
@@ -1197,6 +1278,8 @@ struct Int4Factors {
   static constexpr int kWavesPerSimd = 2;
   static constexpr bool kKeyDoubleBuffer = false;
   static constexpr bool kRope = false;
+  static constexpr bool kExactV = false;  // (INT4 parts: their own layout)
+  static constexpr int kAV = 2 * N8V;
   static constexpr int kPageRows = PR;
   static constexpr int kTiles = PR / 16;  // score tiles of a page
   // Factor pages stream through a per-wave ring of kRingSlots page slots in
@@ -1431,6 +1514,14 @@ struct WaveMergeLds {
   float l[kWaves][kMaxG];
 };
 
+// A format's value-part loads (formats reading exact-rank value parts take
+// the lane's V2Lane).
+#define PKV_LOAD_V(R, VP)                                                   \
+  do {                                                                      \
+    if constexpr (F::kExactV) F::load_values(R, VP, lane, v2_lane(a.r_v, F::kAV, lane)); \
+    else F::load_values(R, VP, lane);                                       \
+  } while (0)
+
 template <class F, class KA>
 __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(KA kargs) {
   const DecodeArgs& a = common_args(kargs);
@@ -1483,14 +1574,14 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(KA k
     // loads wait for the factorized section, which keeps them spill-free)
     if (f0 < e1) {
       F::load_keys(ka, kptr(f0), lane);
-      F::load_values(vr, vptr(f0), lane);
+      PKV_LOAD_V(vr, vptr(f0));
       if (f0 + 1 < e1) F::load_keys(kb, kptr(f0 + 1), lane);
     }
   } else if constexpr (F::kRope) {
     // the first page's loads overlap the rotation table's construction
     if (f0 < e1) {
       F::load_keys(ka, kptr(f0), lane);
-      F::load_values(vr, vptr(f0), lane);
+      PKV_LOAD_V(vr, vptr(f0));
     }
   }
   if constexpr (F::kRope) {
@@ -1553,7 +1644,7 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(KA k
         }
         const uint8_t* slot = ring + s_cur * F::kPageBytes;
         s_cur = s_cur + 1 == NS ? 0 : s_cur + 1;
-        F::load_values(vr, slot + F::kKBytes, lane);
+        PKV_LOAD_V(vr, slot + F::kKBytes);
         typename F::Probs pb;
         F::keys(st, kr, fq, q4, rem, pb);
         if (e + 1 < e1) {
@@ -1568,7 +1659,7 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(KA k
         F::keys(st, kc, fq, q4, rem, pb);
         if (e + 2 < e1) F::load_keys(kc, kptr(e + 2), lane);
         F::values(st, vr, pb, q4, rem);
-        if (e + 1 < e1) F::load_values(vr, vptr(e + 1), lane);
+        if (e + 1 < e1) PKV_LOAD_V(vr, vptr(e + 1));
       };
       while (true) {
         step(ka);
@@ -1580,7 +1671,7 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(KA k
       typename F::K& kr = ka;
       if constexpr (!F::kRope) {  // (pre-RoPE formats loaded the first page above)
         F::load_keys(kr, kptr(e), lane);
-        F::load_values(vr, vptr(e), lane);
+        PKV_LOAD_V(vr, vptr(e));
       }
       for (; e < e1; ++e) {
         typename F::Probs pb;
@@ -1594,7 +1685,7 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(KA k
         const bool more = e + 1 < e1;
         if (more) F::load_keys(kr, kptr(e + 1), lane);
         F::values(st, vr, pb, q4, rem);
-        if (more) F::load_values(vr, vptr(e + 1), lane);
+        if (more) PKV_LOAD_V(vr, vptr(e + 1));
       }
     }
   }
@@ -1668,6 +1759,8 @@ __global__ __launch_bounds__(256, F::kWavesPerSimd) void decode_mfma_kernel(KA k
     }
   }
 }
+
+#undef PKV_LOAD_V
 
 // ---------------------------------------------------------------------------
 // Generic VALU kernel (fp32 or bf16 storage, any rank <= 64, G <= 8)
@@ -2223,15 +2316,18 @@ DecodeArgs make_args(const CacheGeom& g, const AttnJob& job) {
 template <class KA>
 hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStream_t stream) {
   constexpr bool kBatch = std::is_same<KA, DecodeBatchArgs>::value;
-  const KernelEvents ev = take_kernel_events();
+  const KernelEvents kev = take_kernel_events();
   const int n8k = (g.r_k + 7) / 8, n8v = (g.r_v + 7) / 8;
+  // bf16 value parts below r8 = 32 whose rank 8 does not divide keep V2 at
+  // the exact rank: their formats' EV instantiations
+  const bool ev = g.r_v % 8 != 0 && n8v <= 4;
   if (g.dtype == PKV_BF16_INT4 && g.P == kMinP) {  // equal padded ranks only
     if (n8k != n8v) return hipErrorNotSupported;
     switch (n8k) {
 #define PKV_Q4H(N)                                                                                      \
   case N:                                                                                               \
     hipExtLaunchKernelGGL((decode_mfma_kernel<Int4Factors<N, N, kMinP>, KA>), grid, dim3(256), 0, stream, \
-                          ev.start, ev.stop, 0, ka);                                                    \
+                          kev.start, kev.stop, 0, ka);                                                    \
     break;
       PKV_Q4H(1)
       PKV_Q4H(2)
@@ -2248,7 +2344,7 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
   case NK * 8 + NV:                                                                                 \
     if constexpr (!kBatch || NK == NV)                                                              \
       hipExtLaunchKernelGGL((decode_mfma_kernel<Int4Factors<NK, NV>, KA>), grid, dim3(256), 0, stream, \
-                            ev.start, ev.stop, 0, ka);                                              \
+                            kev.start, kev.stop, 0, ka);                                              \
     break;
 #define PKV_Q4_ROW(NK) PKV_Q4(NK, 1) PKV_Q4(NK, 2) PKV_Q4(NK, 3) PKV_Q4(NK, 4)
       PKV_Q4_ROW(1)
@@ -2262,15 +2358,26 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
     }
   } else if (g.dtype == PKV_BF16 && g.P == kP && n8k == n8v && (!g.rope || n8k <= kRopeMfmaMaxN8)) {
     switch (n8k * 2 + (g.rope ? 1 : 0)) {
-#define PKV_CASE(N)                                                                                       \
-  case 2 * N:                                                                                             \
-    hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Factors<N>, KA>), grid, dim3(256), 0, stream, ev.start, \
-                          ev.stop, 0, ka);                                                                \
+#define PKV_CASE(N)                                                                                        \
+  case 2 * N:                                                                                              \
+    if constexpr (N <= 4) {                                                                                \
+      if (ev) {                                                                                            \
+        hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Factors<N, N, true>, KA>), grid, dim3(256), 0, stream, \
+                              kev.start, kev.stop, 0, ka);                                                 \
+        break;                                                                                             \
+      }                                                                                                    \
+    }                                                                                                      \
+    hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Factors<N>, KA>), grid, dim3(256), 0, stream, kev.start, \
+                          kev.stop, 0, ka);                                                                \
     break;
-#define PKV_ROPE(N)                                                                                       \
-  case 2 * N + 1:                                                                                         \
-    hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<N>, KA>), grid, dim3(256), 0, stream, ev.start, \
-                          ev.stop, 0, ka);                                                                \
+#define PKV_ROPE(N)                                                                                        \
+  case 2 * N + 1:                                                                                          \
+    if (ev)                                                                                                \
+      hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<N, kP, true>, KA>), grid, dim3(256), 0, stream, \
+                            kev.start, kev.stop, 0, ka);                                                   \
+    else                                                                                                   \
+      hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<N>, KA>), grid, dim3(256), 0, stream, kev.start, \
+                            kev.stop, 0, ka);                                                              \
     break;
       PKV_CASE(1)
       PKV_CASE(2)
@@ -2293,8 +2400,12 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
     switch (n8k) {
 #define PKV_HALF_ROPE(N)                                                                                   \
   case N:                                                                                                  \
-    hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<N, kMinP>, KA>), grid, dim3(256), 0, stream,     \
-                          ev.start, ev.stop, 0, ka);                                                       \
+    if (ev)                                                                                                \
+      hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<N, kMinP, true>, KA>), grid, dim3(256), 0,     \
+                            stream, kev.start, kev.stop, 0, ka);                                           \
+    else                                                                                                   \
+      hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<N, kMinP>, KA>), grid, dim3(256), 0, stream,   \
+                            kev.start, kev.stop, 0, ka);                                                   \
     break;
       PKV_HALF_ROPE(1)
       PKV_HALF_ROPE(2)
@@ -2308,8 +2419,12 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
     switch (n8k) {
 #define PKV_HALF(N)                                                                                    \
   case N:                                                                                              \
-    hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Half<N>, KA>), grid, dim3(256), 0, stream, ev.start, \
-                          ev.stop, 0, ka);                                                             \
+    if (ev)                                                                                            \
+      hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Half<N, N, true>, KA>), grid, dim3(256), 0, stream, \
+                            kev.start, kev.stop, 0, ka);                                               \
+    else                                                                                               \
+      hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Half<N>, KA>), grid, dim3(256), 0, stream, kev.start, \
+                            kev.stop, 0, ka);                                                          \
     break;
       PKV_HALF(1)
       PKV_HALF(2)
@@ -2326,14 +2441,24 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
     switch ((g.P == kMinP ? 64 : 0) + n8k * 8 + n8v) {
 #define PKV_ASYM(NK, NV)                                                                                 \
   case NK * 8 + NV:                                                                                      \
-    if constexpr (NK != NV)                                                                              \
-      hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Factors<NK, NV>, KA>), grid, dim3(256), 0, stream,   \
-                            ev.start, ev.stop, 0, ka);                                                   \
+    if constexpr (NK != NV) {                                                                            \
+      if (ev)                                                                                            \
+        hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Factors<NK, NV, true>, KA>), grid, dim3(256), 0,   \
+                              stream, kev.start, kev.stop, 0, ka);                                       \
+      else                                                                                               \
+        hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Factors<NK, NV>, KA>), grid, dim3(256), 0, stream, \
+                              kev.start, kev.stop, 0, ka);                                               \
+    }                                                                                                    \
     break;                                                                                               \
   case 64 + NK * 8 + NV:                                                                                 \
-    if constexpr (NK != NV)                                                                              \
-      hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Half<NK, NV>, KA>), grid, dim3(256), 0, stream,      \
-                            ev.start, ev.stop, 0, ka);                                                   \
+    if constexpr (NK != NV) {                                                                            \
+      if (ev)                                                                                            \
+        hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Half<NK, NV, true>, KA>), grid, dim3(256), 0,      \
+                              stream, kev.start, kev.stop, 0, ka);                                       \
+      else                                                                                               \
+        hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Half<NK, NV>, KA>), grid, dim3(256), 0, stream,    \
+                              kev.start, kev.stop, 0, ka);                                               \
+    }                                                                                                    \
     break;
 #define PKV_ASYM_ROW(NK) PKV_ASYM(NK, 1) PKV_ASYM(NK, 2) PKV_ASYM(NK, 3) PKV_ASYM(NK, 4)
       PKV_ASYM_ROW(1)
@@ -2349,18 +2474,18 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
     return hipErrorNotSupported;
   } else if (g.dtype == PKV_BF16) {
     if (g.rope)
-      hipExtLaunchKernelGGL((decode_valu_kernel<uint16_t, true, KA>), grid, dim3(256), 0, stream, ev.start,
-                            ev.stop, 0, ka);
+      hipExtLaunchKernelGGL((decode_valu_kernel<uint16_t, true, KA>), grid, dim3(256), 0, stream, kev.start,
+                            kev.stop, 0, ka);
     else
-      hipExtLaunchKernelGGL((decode_valu_kernel<uint16_t, false, KA>), grid, dim3(256), 0, stream, ev.start,
-                            ev.stop, 0, ka);
+      hipExtLaunchKernelGGL((decode_valu_kernel<uint16_t, false, KA>), grid, dim3(256), 0, stream, kev.start,
+                            kev.stop, 0, ka);
   } else {
     if (g.rope)
-      hipExtLaunchKernelGGL((decode_valu_kernel<float, true, KA>), grid, dim3(256), 0, stream, ev.start,
-                            ev.stop, 0, ka);
+      hipExtLaunchKernelGGL((decode_valu_kernel<float, true, KA>), grid, dim3(256), 0, stream, kev.start,
+                            kev.stop, 0, ka);
     else
-      hipExtLaunchKernelGGL((decode_valu_kernel<float, false, KA>), grid, dim3(256), 0, stream, ev.start,
-                            ev.stop, 0, ka);
+      hipExtLaunchKernelGGL((decode_valu_kernel<float, false, KA>), grid, dim3(256), 0, stream, kev.start,
+                            kev.stop, 0, ka);
   }
   return hipGetLastError();
 }

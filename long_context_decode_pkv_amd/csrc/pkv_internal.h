@@ -46,6 +46,9 @@ struct PackDims {
   int A;    // ranks per lane quad = 2 * n8
   int RT;   // rank tiles = ceil(A / 4)
   int KS2;  // 32-wide reduction steps over the rank = ceil(A / 8)
+  int r2;   // ranks V2 stores: r rounded up to even (KS2 = 1), else r8
+  int nf;   // V2 (KS2 = 1): lane quads holding A ranks ...
+  int ap;   // ... and the ranks of the partial quad after them (0 or even)
   int64_t k1, k2, v1, v2;  // element counts of the four operands
 };
 
@@ -56,16 +59,22 @@ __host__ __device__ constexpr PackDims pack_dims(int r, int P = kP) {
   p.A = 2 * p.n8;
   p.RT = (p.A + 3) / 4;
   p.KS2 = (p.A + 7) / 8;
+  p.r2 = p.KS2 == 1 ? r + (r & 1) : 8 * p.n8;
+  p.nf = p.r2 / p.A;
+  p.ap = p.r2 % p.A;
   p.k1 = (int64_t)8 * p.n8 * kD;
   p.k2 = (int64_t)P * 8 * p.n8;
   p.v1 = (int64_t)8 * p.n8 * P;
-  p.v2 = (int64_t)kD * 8 * p.n8;
+  p.v2 = (int64_t)kD * p.r2;
   return p;
 }
 
-__host__ __device__ inline int64_t part_elems(int r, int P = kP) {
+// Elements of a factor part: r8 (P + d) for key parts, r8 P + r2 d for
+// value parts (V2 at the exact, even-rounded rank; the same as keys when 8
+// divides r).
+__host__ __device__ inline int64_t part_elems(int kind, int r, int P = kP) {
   PackDims p = pack_dims(r, P);
-  return p.k1 + p.k2;  // == p.v1 + p.v2 == r8 (P + d)
+  return kind == PKV_VALUES ? p.v1 + p.v2 : p.k1 + p.k2;
 }
 
 // --------------------------------------------------------------------------
@@ -127,19 +136,36 @@ __host__ __device__ inline int64_t off_lf_v(const PackDims& p, int j, int i) {
   return base + ks * (tile / 4) + lam * 8 + e;
 }
 
-// V2: Rf_V[i][c] (stored as Rf_V^T)
-__host__ __device__ inline int64_t off_rf_v(const PackDims& p, int i, int c) {
+// Channel-major Rf (d x r8) in the A-operand order of o += Rf^T u: channel
+// tile mt, lane 16 qk + rho holds ranks A qk .. A qk + A - 1 of channel
+// 16 mt + rho (offset within the operand).
+__host__ __device__ inline int64_t off_rf_cm_padded(const PackDims& p, int i, int c) {
   int mt = c / 16, rho = c % 16;
   int qk = i / p.A, a = i % p.A, ks = a / 8, e = a % 8;
   int w = (p.A - 8 * ks) < 8 ? (p.A - 8 * ks) : 8;
   int lane = 16 * qk + rho;
-  return p.v1 + (int64_t)mt * 64 * p.A + 512 * ks + lane * w + e;
+  return (int64_t)mt * 64 * p.A + 512 * ks + lane * w + e;
 }
 
-// Rf_K of a pre-RoPE cache's key part (PKV_KEYS_PRE_ROPE): channel-major,
-// in V2's order, at the start of the part (Lf_K follows at K2's offset).
+// V2: Rf_V[i][c] (stored as Rf_V^T, i < r2).  For r8 <= 32 (KS2 = 1) the
+// ranks are kept exactly, rounded up to even: channel tile mt holds 16 r2
+// elements, first the partial lane quad nf (16 lanes x ap ranks), then the
+// full quads 0 .. nf - 1 (16 lanes x A ranks each, lane 16 qk + rho).  When
+// 8 divides r (nf = 4, ap = 0) that is the padded order.
+__host__ __device__ inline int64_t off_rf_v(const PackDims& p, int i, int c) {
+  if (p.KS2 > 1) return p.v1 + off_rf_cm_padded(p, i, c);
+  int mt = c / 16, rho = c % 16;
+  int qk = i / p.A, a = i % p.A;
+  int64_t tile = p.v1 + (int64_t)mt * 16 * p.r2;
+  if (qk < p.nf) return tile + 16 * p.ap + (16 * qk + rho) * p.A + a;
+  return tile + rho * p.ap + a;  // the partial quad (a < ap)
+}
+
+// Rf_K of a pre-RoPE cache's key part (PKV_KEYS_PRE_ROPE): channel-major in
+// the padded order (r8 ranks), at the start of the part (Lf_K follows at
+// K2's offset).
 __host__ __device__ inline int64_t off_rf_k_cm(const PackDims& p, int i, int c) {
-  return off_rf_v(p, i, c) - p.v1;
+  return off_rf_cm_padded(p, i, c);
 }
 
 // The offsets of a part of kind PKV_KEYS / PKV_VALUES / PKV_KEYS_PRE_ROPE.

@@ -45,10 +45,10 @@ int main() {
     std::vector<float> Lf(P * r), Rf(r * d), L2(P * r), R2(r * d);
     for (auto& x : Lf) x = frand();
     for (auto& x : Rf) x = frand();
-    int64_t elems = 0;
-    CHECK(pkv_factor_part_elems(P, d, r, &elems) == 0);
-    std::vector<float> packed(elems);
     for (int kind = 0; kind <= 2; ++kind) {
+      int64_t elems = 0;  // (value parts: Rf at the even-rounded rank)
+      CHECK(pkv_factor_part_elems(kind, P, d, r, &elems) == 0);
+      std::vector<float> packed(elems);
       CHECK(pkv_pack_factors(kind, P, d, r, PKV_F32, Lf.data(), Rf.data(), packed.data()) == 0);
       CHECK(pkv_unpack_factors(kind, P, d, r, PKV_F32, packed.data(), L2.data(), R2.data()) == 0);
       CHECK(std::memcmp(Lf.data(), L2.data(), Lf.size() * 4) == 0);

@@ -118,7 +118,7 @@ def test_p32_factors_are_the_pages_own():
             for f in range(nf):
                 part = cache.factor_part(0, h, f, kind).cpu().numpy()
                 torch.cuda.synchronize()
-                assert part.size == 2 * (-(-r // 8) * 8) * (P + 128)
+                assert part.size == pkv.factor_part_bytes(kind, r, pkv.BF16, P=P)
                 Lf, Rf = pkv.unpack_factors(kind, r, pkv.BF16, part.view(np.uint16), P=P)
                 err = np.linalg.norm(X[f] - Lf.astype(np.float64) @ Rf.astype(np.float64))
                 nrm = np.linalg.norm(X[f])

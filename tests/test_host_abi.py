@@ -71,18 +71,28 @@ def test_storage_ratio_is_eq3_and_agrees_with_oracle():
         assert abs(pkv.storage_ratio(P, rk, rv, d) - oracle.storage_ratio(P, rk, rv, d)) < 1e-15
 
 
-@pytest.mark.parametrize("r", [1, 7, 8, 14, 16, 24, 32, 40, 48, 56, 64])
+def _part_elems(kind, r, P):
+    """Key parts r8 (P + d); value parts r8 P + r2 d, their Rf at r rounded
+    up to even (r8 above 32)."""
+    r8 = -(-r // 8) * 8
+    r2 = r + r % 2 if r8 <= 32 else r8
+    return r8 * P + r2 * 128 if kind == pkv.VALUES else r8 * (P + 128)
+
+
+@pytest.mark.parametrize("r", [1, 7, 8, 10, 13, 14, 16, 20, 24, 25, 30, 32, 40, 48, 56, 64])
 def test_packed_layout_is_a_bijection(r):
     """Every (operand, row, col) of the two factor parts maps to a distinct
-    slot and every slot of the part is used."""
-    n = pkv.factor_part_elems(r)
+    slot inside the part (value parts at their exact, even-rounded rank),
+    and pack and unpack are inverse."""
     r8 = -(-r // 8) * 8
-    assert n == r8 * (64 + 128)
     for kind in (pkv.KEYS, pkv.VALUES, pkv.KEYS_PRE_ROPE):
+        n = pkv.factor_part_elems(kind, r)
+        assert n == _part_elems(kind, r, 64)
         # encode each entry's identity in its value, pack, and check coverage
         Lf = np.arange(64 * r8, dtype=np.float32).reshape(64, r8)[:, :r] + 1
         Rf = np.arange(r8 * 128, dtype=np.float32).reshape(r8, 128)[:r] + 1 + 64 * r8
         packed = pkv.pack_factors(kind, r, pkv.F32, Lf, Rf)
+        assert packed.size == n
         vals = packed[packed != 0]
         assert len(np.unique(vals)) == len(vals) == 64 * r + r * 128
         Lb, Rb = pkv.unpack_factors(kind, r, pkv.F32, packed)
@@ -147,32 +157,34 @@ def test_layout_validation(kw, status):
 
 
 def test_layout_of_32_token_pages():
-    """P = 32 (the pages' default page length) at (r_K, r_V) = (16, 14): a
-    part holds r8 (P + d) elements, ranks padded to a multiple of 8 as at
-    P = 64, so a factorized page pair takes (r8_K + r8_V)(P + d) / (2 P d) of
-    its dense bytes -- Sec. 3.3 Eq. 3 exactly when the ranks are multiples of
-    8 (0.625 here, against Eq. 3's 0.586 at the unpadded (16, 14))."""
+    """P = 32 (the pages' default page length) at (r_K, r_V) = (16, 14): the
+    key part holds r8 (P + d) elements, the value part r8 P + r2 d with its
+    Rf_V at the exact rank 14 (only Lf_V^T keeps two zero rank rows).  A
+    factorized page pair then takes 0.594 of its dense bytes, against Sec. 3.3
+    Eq. 3's 0.586 at (16, 14) and 0.625 with both ranks padded to 16."""
     lay = pkv.cache_layout(_shape(page_len=32, rank_k=16, rank_v=14, sink=32, window=32))
     assert lay["dense_page_bytes"] == 32 * 128 * 2
-    assert lay["factor_k_elems"] == 16 * (32 + 128) and lay["factor_v_elems"] == 16 * (32 + 128)
+    assert lay["factor_k_elems"] == 16 * (32 + 128) and lay["factor_v_elems"] == 16 * 32 + 14 * 128
     assert lay["max_pages"] == 4096 // 32 and lay["max_fact_pages"] == 4096 // 32 - 2
     ratio = lay["factor_page_bytes"] / (2 * lay["dense_page_bytes"])
-    assert ratio == pkv.storage_ratio(32, 16, 16, 128) == 0.625
+    assert ratio == (16 * 160 + 16 * 32 + 14 * 128) / (2 * 32 * 128) == 0.59375
+    assert pkv.storage_ratio(32, 16, 16, 128) == 0.625
     assert abs(pkv.storage_ratio(32, 16, 14, 128) - 0.586) < 5e-4
 
 
-@pytest.mark.parametrize("r", [1, 7, 8, 14, 16, 24, 32])
+@pytest.mark.parametrize("r", [1, 7, 8, 10, 13, 14, 16, 20, 24, 25, 30, 32])
 def test_packed_layout_of_32_token_pages_is_a_bijection(r):
     """Every (operand, row, col) of a P = 32 part maps to a distinct slot,
-    every slot is used, and pack and unpack are inverse."""
+    and pack and unpack are inverse."""
     P = 32
-    n = pkv.factor_part_elems(r, P)
     r8 = -(-r // 8) * 8
-    assert n == r8 * (P + 128)
     for kind in (pkv.KEYS, pkv.VALUES, pkv.KEYS_PRE_ROPE):
+        n = pkv.factor_part_elems(kind, r, P)
+        assert n == _part_elems(kind, r, P)
         Lf = np.arange(P * r8, dtype=np.float32).reshape(P, r8)[:, :r] + 1
         Rf = np.arange(r8 * 128, dtype=np.float32).reshape(r8, 128)[:r] + 1 + P * r8
         packed = pkv.pack_factors(kind, r, pkv.F32, Lf, Rf, P=P)
+        assert packed.size == n
         vals = packed[packed != 0]
         assert len(np.unique(vals)) == len(vals) == P * r + r * 128
         Lb, Rb = pkv.unpack_factors(kind, r, pkv.F32, packed, P=P)
@@ -183,8 +195,9 @@ def test_packed_layout_of_32_token_pages_is_a_bijection(r):
     nb = ctypes.c_int64()
     assert L.pkv_factor_part_bytes(pkv.KEYS, P, 128, r, pkv.BF16_INT4, ctypes.byref(nb)) == 0
     assert nb.value == pkv.factor_part_bytes(pkv.KEYS, r, pkv.BF16_INT4, P=P)  # INT4 parts at P = 32
-    assert L.pkv_factor_part_elems(P, 128, P + 1, ctypes.byref(nb)) == 1
-    assert L.pkv_factor_part_elems(16, 128, 8, ctypes.byref(nb)) == 2
+    assert L.pkv_factor_part_elems(pkv.VALUES, P, 128, P + 1, ctypes.byref(nb)) == 1
+    assert L.pkv_factor_part_elems(pkv.KEYS, 16, 128, 8, ctypes.byref(nb)) == 2
+    assert L.pkv_factor_part_elems(7, P, 128, 8, ctypes.byref(nb)) == 1  # no such kind
 
 
 def test_operand_order_of_32_token_parts():

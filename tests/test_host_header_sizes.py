@@ -19,6 +19,16 @@ def r8(r):
     return 8 * (-(-r // 8))
 
 
+def r2(r):
+    """Ranks a value part's Rf operand stores: r rounded up to even up to
+    r8 = 32, r8 above."""
+    return r + r % 2 if r8(r) <= 32 else r8(r)
+
+
+def part_elems(kind, P, r):
+    return r8(r) * P + r2(r) * D if kind == pkv.VALUES else r8(r) * (P + D)
+
+
 def int4_part_bytes(kind, P, r):
     """The INT4 part sizes as the header gives them at pkv_factor_part_bytes."""
     A = r8(r) // 4
@@ -32,10 +42,11 @@ def int4_part_bytes(kind, P, r):
 @pytest.mark.parametrize("P", [32, 64])
 def test_factor_part_sizes_follow_the_header(P):
     for r in range(1, P + 1):
-        assert pkv.factor_part_elems(r, P) == r8(r) * (P + D), (P, r)
         for kind in (pkv.KEYS, pkv.VALUES, pkv.KEYS_PRE_ROPE):
-            assert pkv.factor_part_bytes(kind, r, pkv.BF16, P=P) == 2 * r8(r) * (P + D)
-            assert pkv.factor_part_bytes(kind, r, pkv.F32, P=P) == 4 * r8(r) * (P + D)
+            n = part_elems(kind, P, r)
+            assert pkv.factor_part_elems(kind, r, P) == n, (P, r, kind)
+            assert pkv.factor_part_bytes(kind, r, pkv.BF16, P=P) == 2 * n
+            assert pkv.factor_part_bytes(kind, r, pkv.F32, P=P) == 4 * n
         if r <= 32:
             for kind in (pkv.KEYS, pkv.VALUES):
                 assert pkv.factor_part_bytes(kind, r, pkv.BF16_INT4, P=P) == int4_part_bytes(kind, P, r), \
@@ -57,11 +68,13 @@ def test_cache_layout_follows_the_header(P, dtype):
             assert L["max_pages"] == -(-Tmax // P)
             assert L["max_fact_pages"] == max(0, Tmax // P - n_s - n_w)
             assert L["dense_page_bytes"] == P * D * esz
-            assert L["factor_k_elems"] == r8(r) * (P + D) and L["factor_v_elems"] == r8(r_v) * (P + D)
-            if dtype == pkv.BF16_INT4:
+            if dtype == pkv.BF16_INT4:  # (codes: the padded count)
+                assert L["factor_k_elems"] == r8(r) * (P + D) and L["factor_v_elems"] == r8(r_v) * (P + D)
                 kb, vb = int4_part_bytes(pkv.KEYS, P, r), int4_part_bytes(pkv.VALUES, P, r_v)
             else:
-                kb, vb = r8(r) * (P + D) * esz, r8(r_v) * (P + D) * esz
+                assert L["factor_k_elems"] == part_elems(pkv.KEYS, P, r)
+                assert L["factor_v_elems"] == part_elems(pkv.VALUES, P, r_v)
+                kb, vb = part_elems(pkv.KEYS, P, r) * esz, part_elems(pkv.VALUES, P, r_v) * esz
             assert (L["factor_k_bytes"], L["factor_v_bytes"]) == (kb, vb)
             assert L["factor_page_bytes"] == kb + vb
             # regions in order, each starting at the previous end rounded up to 256
