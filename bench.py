@@ -46,12 +46,12 @@ CACHE_DIR = os.environ.get("PKV_BENCH_CACHE", "/tmp/pkv_bench_inputs")
 # reads 1048576 KiB for 2^30 bytes written -> x1.0).  A figure holds only for
 # the kernel sources whose hash it carries; any change to them makes it null.
 PMC_TRAFFIC = {
-    "qwen3-32b-layer-128k": {"sha256": "78ac5de6c1f14392fba7f2da396b51d9282a597e50ffc51869bbf568572e90cf",
-                           "fetch": 303082007, "write": 1114112},
-    "qwen3-32b-layer-128k-int4": {"sha256": "78ac5de6c1f14392fba7f2da396b51d9282a597e50ffc51869bbf568572e90cf",
-                                "fetch": 88817613, "write": 2228224},
-    "llama3.1-8b-layer-p32": {"sha256": "78ac5de6c1f14392fba7f2da396b51d9282a597e50ffc51869bbf568572e90cf",
-                            "fetch": 673830841, "write": 1114112},
+    "qwen3-32b-layer-128k": {"sha256": "b393b0aad525032a542ab1c6ce65c2ccc31739f483553fd82b922def1b7b9386",
+                           "fetch": 303090813, "write": 1114112},
+    "qwen3-32b-layer-128k-int4": {"sha256": "b393b0aad525032a542ab1c6ce65c2ccc31739f483553fd82b922def1b7b9386",
+                                "fetch": 88819661, "write": 2228224},
+    "llama3.1-8b-layer-p32": {"sha256": "b393b0aad525032a542ab1c6ce65c2ccc31739f483553fd82b922def1b7b9386",
+                            "fetch": 640471834, "write": 1114112},
 }
 TRAFFIC_SOURCES = ("long_context_decode_pkv_amd/csrc/pkv_decode.hip",
                    "long_context_decode_pkv_amd/csrc/pkv_internal.h")
