@@ -58,10 +58,13 @@ def _check_equal_to_single(caches, q, n_split):
     return out
 
 
-@pytest.mark.parametrize("store,r", [(None, 16), ("int4", 16), (None, 24)])
-def test_batch_equals_single_caches(store, r):
+@pytest.mark.parametrize("store,rk,rv", [
+    (None, 16, 16), ("int4", 16, 16), (None, 24, 24),
+    (None, 16, 13), (None, 24, 22), (None, 32, 30),  # value parts at the exact rank
+])
+def test_batch_equals_single_caches(store, rk, rv):
     require_gpu()
-    caches, data = _batch(2, LENGTHS, store=store, r_k=r, r_v=r)
+    caches, data = _batch(2, LENGTHS, store=store, r_k=rk, r_v=rv)
     dt = "bf16"
     q = to_dev(_queries(2, len(caches), data[0]["Hq"], dt), dt)
     for ns in (1, 4, 16):
