@@ -948,13 +948,15 @@ constexpr int kRopeMfmaMaxN8 = 4;
 // 8 b + 4 t + v, and slot e of lane quad b of the value contraction's single
 // reduction step is token 8 b + e (eight consecutive tokens of the stored
 // Lf_V^T).  Only the loads follow this order; the stored parts are the
-// compacted 64-row layout.
-template <int N8, int PR = kP, bool EV = false>
+// compacted 64-row layout.  N8 and N8V: the key and value parts' padded
+// ranks over 8 (they may differ: r_K and r_V are separate budgets).
+template <int N8, int PR = kP, bool EV = false, int N8V = N8>
 struct RopeFactors {
-  using Dm = FactDims<N8>;
+  using Dm = FactDims<N8>;    // key parts
+  using DmV = FactDims<N8V>;  // value parts
   static constexpr bool kExactV = EV;
-  static constexpr int kAV = 2 * N8;
-  static constexpr int kWavesPerSimd = mfma_waves_per_simd(N8);
+  static constexpr int kAV = 2 * N8V;
+  static constexpr int kWavesPerSimd = mfma_waves_per_simd(N8 > N8V ? N8 : N8V);
   static constexpr bool kKeyDoubleBuffer = false;
   static constexpr bool kLdsRing = false;
   static constexpr bool kRope = true;
@@ -969,7 +971,7 @@ struct RopeFactors {
     __device__ bf16x8 rf(int ct, int ks) const { return ks == 0 ? operand(rfa[ct]) : operand(rfb[ct]); }
     __device__ bf16x8 k2(int mt, int ks) const { return ks == 0 ? operand(k2a[mt]) : operand(k2b[mt]); }
   };
-  using V = VRegs<N8>;
+  using V = VRegs<N8V>;
   struct Query {
     float qscale;  // 2^8 log2(e)/sqrt(d), applied with the page's rotation
     halfx8 qb[4];  // R(p0)^T q of the current page, scaled, fp16 hi/lo columns
@@ -1028,8 +1030,8 @@ struct RopeFactors {
     const int rho = lane & 15, b = lane >> 4;
     const TileLane tl = tile_lane(lane);
 #pragma unroll
-    for (int mt = 0; mt < Dm::RT; ++mt) {
-      const bool part = Dm::kPartialTile && mt == Dm::RT - 1;
+    for (int mt = 0; mt < DmV::RT; ++mt) {
+      const bool part = DmV::kPartialTile && mt == DmV::RT - 1;
       if (!part) {
         R.v1[mt][0] = ld16(p + mt * 512 + (b & 1) * 256 + (16 * (b >> 1) + rho) * 8);
       } else {
@@ -1041,25 +1043,25 @@ struct RopeFactors {
   }
   __device__ static void load_values(V& R, const uint8_t* vp, int lane) {
     if constexpr (PR == kP) {
-      pkv::load_values<N8>(R, (const uint16_t*)vp, lane);
+      pkv::load_values<N8V>(R, (const uint16_t*)vp, lane);
     } else {
       const uint16_t* p = (const uint16_t*)vp;
       load_v1_half(R, p, lane);
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        const uint16_t* base = p + Dm::V1 / 2 + mt * 64 * Dm::A;
-        ldraw(R.v2a[mt], base + lane * Dm::W0);
-        if constexpr (Dm::KS2 > 1) ldraw(R.v2b[mt], base + 512 + lane * Dm::W1);
+        const uint16_t* base = p + DmV::V1 / 2 + mt * 64 * DmV::A;
+        ldraw(R.v2a[mt], base + lane * DmV::W0);
+        if constexpr (DmV::KS2 > 1) ldraw(R.v2b[mt], base + 512 + lane * DmV::W1);
       }
     }
   }
   __device__ static void load_values(V& R, const uint8_t* vp, int lane, const V2Lane& vl) {
     if constexpr (PR == kP) {
-      pkv::load_values_ev<N8>(R, (const uint16_t*)vp, lane, vl);
+      pkv::load_values_ev<N8V>(R, (const uint16_t*)vp, lane, vl);
     } else {
       const uint16_t* p = (const uint16_t*)vp;
       load_v1_half(R, p, lane);
-      load_v2<N8, true>(R, p + Dm::V1 / 2, lane, vl);
+      load_v2<N8V, true>(R, p + DmV::V1 / 2, lane, vl);
     }
   }
   // token tile mt: K_p^T columns = its 16 tokens, 8 channel tiles of rows
@@ -1094,17 +1096,17 @@ struct RopeFactors {
   }
   __device__ static void values(SoftState& st, const V& R, const Probs& pb, int, float rem) {
     if constexpr (PR == kP) {
-      fact_values<N8>(st, R, pb, rem);
+      fact_values<N8V>(st, R, pb, rem);
     } else {  // Eq. 4's value half over the page's 32 tokens: one reduction step
-      floatx4 au[Dm::RT];
+      floatx4 au[DmV::RT];
 #pragma unroll
-      for (int mt = 0; mt < Dm::RT; ++mt) au[mt] = mfma(R.v1[mt][0], pb[0], floatx4{0.f, 0.f, 0.f, 0.f});
-      bf16x8 ub[Dm::KS2];
-      rank_operand<N8>(au, rem, ub);
+      for (int mt = 0; mt < DmV::RT; ++mt) au[mt] = mfma(R.v1[mt][0], pb[0], floatx4{0.f, 0.f, 0.f, 0.f});
+      bf16x8 ub[DmV::KS2];
+      rank_operand<N8V>(au, rem, ub);
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-        for (int ks = 0; ks < Dm::KS2; ++ks) st.o[mt] = mfma(R.v2(mt, ks), ub[ks], st.o[mt]);
+        for (int ks = 0; ks < DmV::KS2; ++ks) st.o[mt] = mfma(R.v2(mt, ks), ub[ks], st.o[mt]);
       }
     }
   }
@@ -2437,8 +2439,10 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
   } else if (g.dtype == PKV_BF16 && !g.rope && n8k != n8v && n8k <= 4 && n8v <= 4) {
     // unequal padded ranks up to 32 (batches launch once per cache: the
     // batched kernel's caches share one format)
-    if constexpr (kBatch) return hipErrorNotSupported;
-    switch ((g.P == kMinP ? 64 : 0) + n8k * 8 + n8v) {
+    if constexpr (kBatch) {
+      return hipErrorNotSupported;
+    } else {
+      switch ((g.P == kMinP ? 64 : 0) + n8k * 8 + n8v) {
 #define PKV_ASYM(NK, NV)                                                                                 \
   case NK * 8 + NV:                                                                                      \
     if constexpr (NK != NV) {                                                                            \
@@ -2461,14 +2465,54 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
     }                                                                                                    \
     break;
 #define PKV_ASYM_ROW(NK) PKV_ASYM(NK, 1) PKV_ASYM(NK, 2) PKV_ASYM(NK, 3) PKV_ASYM(NK, 4)
-      PKV_ASYM_ROW(1)
-      PKV_ASYM_ROW(2)
-      PKV_ASYM_ROW(3)
-      PKV_ASYM_ROW(4)
+        PKV_ASYM_ROW(1)
+        PKV_ASYM_ROW(2)
+        PKV_ASYM_ROW(3)
+        PKV_ASYM_ROW(4)
 #undef PKV_ASYM_ROW
 #undef PKV_ASYM
-      default:
-        return hipErrorInvalidValue;
+        default:
+          return hipErrorInvalidValue;
+      }
+    }
+  } else if (g.dtype == PKV_BF16 && g.rope && n8k != n8v && n8k <= kRopeMfmaMaxN8 && n8v <= kRopeMfmaMaxN8) {
+    // pre-RoPE keys at unequal padded ranks up to 32 (one launch per cache
+    // in a batch, as above)
+    if constexpr (kBatch) {
+      return hipErrorNotSupported;
+    } else {
+      switch ((g.P == kMinP ? 64 : 0) + n8k * 8 + n8v) {
+#define PKV_ROPE_ASYM(NK, NV)                                                                              \
+  case NK * 8 + NV:                                                                                        \
+    if constexpr (NK != NV) {                                                                              \
+      if (ev)                                                                                              \
+        hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<NK, kP, true, NV>, KA>), grid, dim3(256), 0, \
+                              stream, kev.start, kev.stop, 0, ka);                                         \
+      else                                                                                                 \
+        hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<NK, kP, false, NV>, KA>), grid, dim3(256), 0, \
+                              stream, kev.start, kev.stop, 0, ka);                                         \
+    }                                                                                                      \
+    break;                                                                                                 \
+  case 64 + NK * 8 + NV:                                                                                   \
+    if constexpr (NK != NV) {                                                                              \
+      if (ev)                                                                                              \
+        hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<NK, kMinP, true, NV>, KA>), grid, dim3(256), \
+                              0, stream, kev.start, kev.stop, 0, ka);                                      \
+      else                                                                                                 \
+        hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<NK, kMinP, false, NV>, KA>), grid, dim3(256), \
+                              0, stream, kev.start, kev.stop, 0, ka);                                      \
+    }                                                                                                      \
+    break;
+#define PKV_ROPE_ASYM_ROW(NK) PKV_ROPE_ASYM(NK, 1) PKV_ROPE_ASYM(NK, 2) PKV_ROPE_ASYM(NK, 3) PKV_ROPE_ASYM(NK, 4)
+        PKV_ROPE_ASYM_ROW(1)
+        PKV_ROPE_ASYM_ROW(2)
+        PKV_ROPE_ASYM_ROW(3)
+        PKV_ROPE_ASYM_ROW(4)
+#undef PKV_ROPE_ASYM_ROW
+#undef PKV_ROPE_ASYM
+        default:
+          return hipErrorInvalidValue;
+      }
     }
   } else if constexpr (kBatch) {
     return hipErrorNotSupported;

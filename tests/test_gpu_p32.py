@@ -83,10 +83,12 @@ def test_p32_short_and_windowless_caches():
 
 
 def test_p32_pre_rope_keys():
-    # matrix-core kernel (equal padded ranks), then the vector-ALU kernel
+    # matrix-core kernel (equal, then unequal padded ranks), then the
+    # vector-ALU kernel (fp32 storage)
     _case(2, 32 * 30 + 9, rope=synth.rope_inv_freq(5e5), splits=(0, 2), label="pre-RoPE")
     _case(3, 32 * 40 + 21, rk=24, rv=24, rope=synth.rope_inv_freq(1e6), splits=(0, 3), label="pre-RoPE r=24")
-    _case(2, 32 * 12 + 7, rk=8, rv=24, rope=synth.rope_inv_freq(5e5), label="pre-RoPE valu")
+    _case(2, 32 * 12 + 7, rk=8, rv=24, rope=synth.rope_inv_freq(5e5), label="pre-RoPE r=(8,24)")
+    _case(1, 32 * 12 + 7, rk=8, rv=24, rope=synth.rope_inv_freq(1e4), splits=(0, 2), label="pre-RoPE fp32 valu")
 
 
 @pytest.mark.parametrize("cfg_id,T,rk,rv,splits", [
@@ -94,10 +96,15 @@ def test_p32_pre_rope_keys():
     (4, 32 * 18 + 30, 5, 7, (0, 1)),    # n8 = 1, unequal ranks
     (3, 32 * 27 + 16, 20, 24, (0, 5)),  # n8 = 3
     (2, 32 * 22 + 1, 32, 32, (0, 2)),   # n8 = 4: full rank of a 32-token page
+    (2, 32 * 20 + 9, 8, 24, (0, 2)),    # unequal padded ranks: key n8 = 1, value n8 = 3
+    (3, 32 * 23 + 5, 32, 13, (0, 3)),   # key n8 = 4, value n8 = 2 (exact-rank part, r2 = 14)
+    (4, 32 * 19 + 17, 24, 30, (0,)),    # key n8 = 3, value n8 = 4
+    (2, 32 * 21 + 2, 16, 1, (0,)),      # value rank 1
 ])
 def test_p32_pre_rope_every_rank_tile_count(cfg_id, T, rk, rv, splits):
     """Pre-RoPE 32-token pages on the matrix-core kernel at every padded rank
-    it takes (8 to 32), against the oracle."""
+    it takes (8 to 32, key and value ranks equal or not), against the
+    oracle."""
     f = synth.rope_inv_freq(5e5 if cfg_id != 3 else 1e6)
     _case(cfg_id, T, rk=rk, rv=rv, rope=f, splits=splits, label="pre-RoPE n8")
 
