@@ -28,8 +28,7 @@
  *    cache's element type (bf16 for PKV_BF16_INT4); attention output is
  *    float32.
  *  - Fixed in this version: head_dim d = 128, page length P = 64 or 32
- *    (other values return PKV_ERR_UNSUPPORTED; PKV_BF16_INT4 at P = 32
- *    needs r_K and r_V in the same multiple of 8); GQA group size
+ *    (other values return PKV_ERR_UNSUPPORTED); GQA group size
  *    G = H_q / H_kv <= 8.
  */
 #ifndef PKV_H

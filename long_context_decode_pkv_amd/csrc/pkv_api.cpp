@@ -68,9 +68,6 @@ int32_t check_shape(const pkv_shape* s) {
     return PKV_ERR_INVALID_ARG;
   if (s->max_tokens < 1) return PKV_ERR_INVALID_ARG;
   if (s->head_dim != kD || (s->page_len != kP && s->page_len != kMinP)) return PKV_ERR_UNSUPPORTED;
-  // INT4 at P = 32: equal padded ranks only (the kernels instantiated)
-  if (s->page_len != kP && s->dtype == PKV_BF16_INT4 && (s->rank_k + 7) / 8 != (s->rank_v + 7) / 8)
-    return PKV_ERR_UNSUPPORTED;
   if (s->n_q_heads / s->n_kv_heads > kMaxG) return PKV_ERR_UNSUPPORTED;
   if (s->dtype == PKV_BF16_INT4 && (s->rank_k > kQ4MaxRank || s->rank_v > kQ4MaxRank))
     return PKV_ERR_UNSUPPORTED;

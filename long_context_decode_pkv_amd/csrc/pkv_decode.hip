@@ -2323,18 +2323,21 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
   // bf16 value parts below r8 = 32 whose rank 8 does not divide keep V2 at
   // the exact rank: their formats' EV instantiations
   const bool ev = g.r_v % 8 != 0 && n8v <= 4;
-  if (g.dtype == PKV_BF16_INT4 && g.P == kMinP) {  // equal padded ranks only
-    if (n8k != n8v) return hipErrorNotSupported;
-    switch (n8k) {
-#define PKV_Q4H(N)                                                                                      \
-  case N:                                                                                               \
-    hipExtLaunchKernelGGL((decode_mfma_kernel<Int4Factors<N, N, kMinP>, KA>), grid, dim3(256), 0, stream, \
-                          kev.start, kev.stop, 0, ka);                                                    \
+  if (g.dtype == PKV_BF16_INT4 && g.P == kMinP) {
+    if (kBatch && n8k != n8v) return hipErrorNotSupported;
+    switch (n8k * 8 + n8v) {
+#define PKV_Q4H(NK, NV)                                                                                    \
+  case NK * 8 + NV:                                                                                        \
+    if constexpr (!kBatch || NK == NV)                                                                     \
+      hipExtLaunchKernelGGL((decode_mfma_kernel<Int4Factors<NK, NV, kMinP>, KA>), grid, dim3(256), 0, stream, \
+                            kev.start, kev.stop, 0, ka);                                                     \
     break;
-      PKV_Q4H(1)
-      PKV_Q4H(2)
-      PKV_Q4H(3)
-      PKV_Q4H(4)
+#define PKV_Q4H_ROW(NK) PKV_Q4H(NK, 1) PKV_Q4H(NK, 2) PKV_Q4H(NK, 3) PKV_Q4H(NK, 4)
+      PKV_Q4H_ROW(1)
+      PKV_Q4H_ROW(2)
+      PKV_Q4H_ROW(3)
+      PKV_Q4H_ROW(4)
+#undef PKV_Q4H_ROW
 #undef PKV_Q4H
       default:
         return hipErrorInvalidValue;

@@ -142,6 +142,9 @@ def _oracle_parts(d, cache, r_k, r_v):
     (2, 32 * 40 + 9, 2, 2, 16, 14, (0, 2), 32),   # 2-byte units
     (2, 32 * 30 + 3, 1, 2, 8, 8, (0, 2), 32),     # 1-byte units
     (2, 32 * 24 + 30, 1, 2, 32, 32, (0, 5), 32),  # 4-byte units (full rank)
+    (2, 32 * 30 + 7, 1, 2, 8, 24, (0, 2), 32),    # unequal padded ranks: 1- and 3-byte units
+    (3, 32 * 28 + 19, 1, 2, 32, 13, (0, 3), 32),  # 4- and 2-byte units
+    (2, 32 * 26 + 5, 2, 2, 24, 8, (0,), 32),
 ])
 def test_int4_attention_on_oracle_codes(cfg_id, T, B, kv, rk, rv, splits, P):
     require_gpu()
@@ -163,6 +166,7 @@ def test_int4_attention_on_oracle_codes(cfg_id, T, B, kv, rk, rv, splits, P):
     (2, 64 * 40 + 37, 2, 2, 16, 16, 64),
     (2, 64 * 30 + 17, 1, 2, 16, 14, 64),
     (2, 32 * 60 + 17, 1, 2, 16, 14, 32),  # the pages' operating point (sink 64, window 128)
+    (3, 32 * 44 + 11, 1, 2, 8, 24, 32),   # 32-token pages, unequal padded ranks
 ])
 def test_int4_decode_end_to_end(cfg_id, T, B, kv, rk, rv, P):
     require_gpu()

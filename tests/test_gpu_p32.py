@@ -5,11 +5,11 @@ page being filled kept dense).
 
 Such caches keep their factor parts in the 64-token matrix-core operand
 order with the operand rows of page rows 32..63 left out.  bf16 caches
-(any rank pair up to 32; pre-RoPE keys at equal padded ranks) and INT4
-caches are attended by the matrix-core kernel, which reads a factorized page
-in a two-tile compact token order and dense pages in the 64-row frame
-(absent rows zero, their scores masked); fp32 caches and pre-RoPE keys with
-unequal padded ranks by the vector-ALU kernel.  A 32-row page is
+(any rank pair up to 32, keys post- or pre-RoPE) and INT4 caches (any rank
+pair up to 32) are attended by the matrix-core kernel, which reads a
+factorized page in a two-tile compact token order and dense pages in the
+64-row frame (absent rows zero, their scores masked); fp32 caches by the
+vector-ALU kernel.  A 32-row page is
 decomposed on the leading 32 x 32 block of its zero-padded 64-row Gram
 matrix.  Gates as for 64-token pages: bf16 storage 1e-2, fp32 storage 1e-4,
 relative to max |o_ref|; stored factors meet the reconstruction bound of the
@@ -224,13 +224,15 @@ def test_p32_chunks_on_aux_stream():
                      s=S, w=W)
 
 
-@pytest.mark.parametrize("lengths,rope,store", [
-    ([32 * 20 + 5, 7, 32 * 3, 32 * 9 + 31], False, None),    # pages complete at different steps
-    ([32 * 20 + 9, 32 * 5 + 9, 32 * 11 + 9], False, None),   # ... at the same steps: one promotion launch
-    ([32 * 20 + 5, 7, 32 * 3, 32 * 9 + 31], True, None),     # pre-RoPE keys
-    ([32 * 20 + 9, 32 * 5 + 9, 32 * 11 + 9], False, "int4"),  # INT4 factor pages
+@pytest.mark.parametrize("lengths,rope,store,rk,rv", [
+    ([32 * 20 + 5, 7, 32 * 3, 32 * 9 + 31], False, None, RK, RV),    # pages complete at different steps
+    ([32 * 20 + 9, 32 * 5 + 9, 32 * 11 + 9], False, None, RK, RV),   # ... at the same steps: one promotion launch
+    ([32 * 20 + 5, 7, 32 * 3, 32 * 9 + 31], True, None, RK, RV),     # pre-RoPE keys
+    ([32 * 20 + 9, 32 * 5 + 9, 32 * 11 + 9], False, "int4", RK, RV),  # INT4 factor pages
+    ([32 * 20 + 5, 32 * 3, 32 * 9 + 31], True, None, 8, 24),         # unequal padded ranks: one launch per cache
+    ([32 * 20 + 9, 32 * 5 + 9, 32 * 11 + 9], False, "int4", 24, 8),
 ])
-def test_p32_batches_equal_single_caches(lengths, rope, store):
+def test_p32_batches_equal_single_caches(lengths, rope, store, rk, rv):
     """Batched attention and batched steps over 32-token caches of different
     lengths equal the per-cache calls bit for bit."""
     import torch
@@ -242,7 +244,7 @@ def test_p32_batches_equal_single_caches(lengths, rope, store):
         Kd = to_dev(np.ascontiguousarray(d["K"][:, :, 32 * i:]), "bf16")
         Vd = to_dev(np.ascontiguousarray(d["V"][:, :, 32 * i:]), "bf16")
         for group in (A, Bs):
-            c = make_cache(d, r_k=RK, r_v=RV, s=S, w=W, P=P, max_tokens=T + steps, store=store)
+            c = make_cache(d, r_k=rk, r_v=rv, s=S, w=W, P=P, max_tokens=T + steps, store=store)
             if rope:
                 c.set_key_rope(synth.rope_inv_freq(5e5))
             c.prefill(Kd[:, :, :T].contiguous(), Vd[:, :, :T].contiguous())
@@ -270,9 +272,6 @@ def test_p32_batches_equal_single_caches(lengths, rope, store):
 def test_p32_errors():
     require_gpu()
     d = synth.decode_inputs(2, T=200, B=1, kv_heads=1)
-    with pytest.raises(pkv.PKVError) as ei:  # INT4 at 32 tokens: equal padded ranks only
-        make_cache(d, r_k=8, r_v=RV, s=S, w=W, P=P, store="int4")
-    assert ei.value.status == 2
     with pytest.raises(pkv.PKVError) as ei:  # rank above the page length
         make_cache(d, r_k=33, r_v=RV, s=S, w=W, P=P)
     assert ei.value.status == 1

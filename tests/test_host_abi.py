@@ -145,7 +145,7 @@ def test_layout_sizes():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(head_dim=64), 2), (dict(page_len=16), 2), (dict(page_len=32, dtype=pkv.BF16_INT4, rank_v=8), 2),
+    (dict(head_dim=64), 2), (dict(page_len=16), 2),
     (dict(page_len=128, sink=128, window=128), 2), (dict(page_len=32, rank_k=33), 1), (dict(n_q_heads=32, n_kv_heads=2), 2),
     (dict(sink=32), 1), (dict(window=100), 1), (dict(rank_k=0), 1), (dict(rank_v=65), 1),
     (dict(n_q_heads=7), 1), (dict(max_tokens=0), 1), (dict(dtype=5), 1),

@@ -198,9 +198,11 @@ def test_int4_cache_at_the_pages_operating_point():
     ours = (lay["max_fact_pages"] * lay["factor_page_bytes"] + 2 * dense) / (n_pages * dense)
     ref = oracle.int4_storage_ratio(T, 32, 128, rk, rv, 2)
     assert ref <= ours <= ref * 1.12, (ours, ref)
-    with pytest.raises(pkv.PKVError) as ei:  # unequal padded ranks: not at P = 32
-        pkv.cache_layout(pkv.make_shape(1, 8, 1, 8, 16, 32, 32, T, pkv.BF16_INT4, page_len=32))
-    assert ei.value.status == 2
+    # unequal padded ranks: each part in its own rank's layout
+    lay = pkv.cache_layout(pkv.make_shape(1, 8, 1, 8, 24, 32, 32, T, pkv.BF16_INT4, page_len=32))
+    assert lay["factor_k_bytes"] == pkv.factor_part_bytes(pkv.KEYS, 8, pkv.BF16_INT4, P=32)
+    assert lay["factor_v_bytes"] == pkv.factor_part_bytes(pkv.VALUES, 24, pkv.BF16_INT4, P=32)
+    assert lay["factor_page_bytes"] == lay["factor_k_bytes"] + lay["factor_v_bytes"]
 
 
 def test_int4_cache_layout_and_storage_ratio():
