@@ -936,9 +936,12 @@ __device__ inline void dense_page_rope(SoftState& st, const uint16_t* Kp, const 
   }
 }
 
-// Ranks of the matrix-core pre-RoPE path (r <= 32); larger ranks of
-// pre-RoPE caches take the VALU kernel.
-constexpr int kRopeMfmaMaxN8 = 4;
+// Ranks of the matrix-core pre-RoPE path: equal padded ranks up to 64
+// (64-token pages), unequal ones up to 32; other pre-RoPE caches take the
+// VALU kernel.  Above r = 32 the format runs one wave per SIMD.
+constexpr int kRopeMfmaMaxN8 = 8;
+constexpr int kRopeAsymMaxN8 = 4;
+constexpr int rope_waves_per_simd(int n8) { return n8 <= 4 ? mfma_waves_per_simd(n8) : 1; }
 
 // bf16 factors of pre-RoPE keys: the key part holds Rf_K channel-major (the
 // V part's Rf layout) and Lf_K as in Bf16Factors; the V part as there.
@@ -956,7 +959,7 @@ struct RopeFactors {
   using DmV = FactDims<N8V>;  // value parts
   static constexpr bool kExactV = EV;
   static constexpr int kAV = 2 * N8V;
-  static constexpr int kWavesPerSimd = mfma_waves_per_simd(N8 > N8V ? N8 : N8V);
+  static constexpr int kWavesPerSimd = rope_waves_per_simd(N8 > N8V ? N8 : N8V);
   static constexpr bool kKeyDoubleBuffer = false;
   static constexpr bool kLdsRing = false;
   static constexpr bool kRope = true;
@@ -2165,7 +2168,8 @@ int decode_default_splits(const CacheGeom& g, int64_t T, int64_t n_fact) {
   // per wave, so both workgroups per CU pay off (same layer: 32 splits
   // 37.1 us, 64 splits 35.0 us), and so do pre-RoPE keys, whose rotation is
   // vector-ALU work (same layer: 32 splits 72.6 us, 64 splits 64.4 us).
-  const int wps = g.dtype == PKV_BF16 ? mfma_waves_per_simd((g.r_k > g.r_v ? g.r_k + 7 : g.r_v + 7) / 8) : 2;  // INT4 and fp32: 2
+  const int n8 = (g.r_k > g.r_v ? g.r_k + 7 : g.r_v + 7) / 8;
+  const int wps = g.dtype != PKV_BF16 ? 2 : g.rope ? rope_waves_per_simd(n8) : mfma_waves_per_simd(n8);  // INT4, fp32: 2
   const int64_t min_run = (g.dtype == PKV_BF16_INT4 || g.rope) ? 8 : 16;
   int64_t s = (256LL * wps + bh - 1) / bh;
   while (s > 1 && pages < min_run * 4 * s && (s / 2) * bh >= 256) s /= 2;
@@ -2233,7 +2237,8 @@ int decode_batch_splits(const CacheGeom& g, const int64_t* T, int n, int* ns) {
   // gets about q pages, the smallest q (at least 8 pages per wave) whose
   // splits all fit.  The longest cache then bounds the launch with runs as
   // short as the others'.
-  const int wps = g.dtype == PKV_BF16 && !g.rope ? mfma_waves_per_simd((g.r_k > g.r_v ? g.r_k + 7 : g.r_v + 7) / 8) : 2;
+  const int n8 = (g.r_k > g.r_v ? g.r_k + 7 : g.r_v + 7) / 8;
+  const int wps = g.dtype != PKV_BF16 ? 2 : g.rope ? rope_waves_per_simd(n8) : mfma_waves_per_simd(n8);
   const int64_t budget = (256LL * wps) / g.Hkv;  // splits over all caches
   int64_t total = 0;
   for (int i = 0; i < n; ++i) total += (T[i] + g.P - 1) / g.P;
@@ -2377,12 +2382,15 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
     break;
 #define PKV_ROPE(N)                                                                                        \
   case 2 * N + 1:                                                                                          \
-    if (ev)                                                                                                \
-      hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<N, kP, true>, KA>), grid, dim3(256), 0, stream, \
-                            kev.start, kev.stop, 0, ka);                                                   \
-    else                                                                                                   \
-      hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<N>, KA>), grid, dim3(256), 0, stream, kev.start, \
-                            kev.stop, 0, ka);                                                              \
+    if constexpr (N <= 4) {                                                                                \
+      if (ev) {                                                                                            \
+        hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<N, kP, true>, KA>), grid, dim3(256), 0,      \
+                              stream, kev.start, kev.stop, 0, ka);                                         \
+        break;                                                                                             \
+      }                                                                                                    \
+    }                                                                                                      \
+    hipExtLaunchKernelGGL((decode_mfma_kernel<RopeFactors<N>, KA>), grid, dim3(256), 0, stream, kev.start,   \
+                          kev.stop, 0, ka);                                                                \
     break;
       PKV_CASE(1)
       PKV_CASE(2)
@@ -2396,12 +2404,16 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
       PKV_ROPE(2)
       PKV_ROPE(3)
       PKV_ROPE(4)
+      PKV_ROPE(5)
+      PKV_ROPE(6)
+      PKV_ROPE(7)
+      PKV_ROPE(8)
 #undef PKV_ROPE
 #undef PKV_CASE
       default:
         return hipErrorInvalidValue;
     }
-  } else if (g.dtype == PKV_BF16 && g.P == kMinP && n8k == n8v && g.rope && n8k <= kRopeMfmaMaxN8) {
+  } else if (g.dtype == PKV_BF16 && g.P == kMinP && n8k == n8v && g.rope && n8k <= kRopeAsymMaxN8) {
     switch (n8k) {
 #define PKV_HALF_ROPE(N)                                                                                   \
   case N:                                                                                                  \
@@ -2478,7 +2490,7 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
           return hipErrorInvalidValue;
       }
     }
-  } else if (g.dtype == PKV_BF16 && g.rope && n8k != n8v && n8k <= kRopeMfmaMaxN8 && n8v <= kRopeMfmaMaxN8) {
+  } else if (g.dtype == PKV_BF16 && g.rope && n8k != n8v && n8k <= kRopeAsymMaxN8 && n8v <= kRopeAsymMaxN8) {
     // pre-RoPE keys at unequal padded ranks up to 32 (one launch per cache
     // in a batch, as above)
     if constexpr (kBatch) {

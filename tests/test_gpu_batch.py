@@ -79,10 +79,13 @@ def test_batch_equals_single_caches(store, rk, rv):
         assert rel_err(out[i:i + 1], o) <= 1e-5, i
 
 
-def test_batch_pre_rope_keys():
+@pytest.mark.parametrize("rk,rv", [(None, None), (48, 48), (24, 8)])
+def test_batch_pre_rope_keys(rk, rv):
+    """Pre-RoPE caches in one batched launch (r = 16; r = 48: the one-wave
+    format above r = 32) or one launch per cache (unequal padded ranks)."""
     require_gpu()
     f = synth.rope_inv_freq(5e5)
-    caches, data = _batch(2, LENGTHS, rope=f)
+    caches, data = _batch(2, LENGTHS, rope=f, r_k=rk, r_v=rv)
     q = to_dev(_queries(2, len(caches), data[0]["Hq"], "bf16"), "bf16")
     _check_equal_to_single(caches, q, 4)
 

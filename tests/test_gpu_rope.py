@@ -5,8 +5,9 @@ The oracle stores and factorizes the keys as given and rotates every key,
 dense or reconstructed, at its token index before the scores; the GPU must
 match it to the same gates as the post-RoPE caches (bf16 storage 1e-2,
 fp32 storage 1e-4, relative to max |o_ref|).  Covered: the matrix-core
-kernel (bf16, r_K and r_V <= 32, equal or unequal padded ranks), the VALU
-kernel (fp32, or a rank above 32), positions up to 131071, decode steps (the new key turns
+kernel (bf16: r_K and r_V <= 32, equal or unequal padded ranks; equal
+padded ranks up to 64), the VALU kernel (fp32, or unequal padded ranks with
+one above 32), positions up to 131071, decode steps (the new key turns
 in the merge), promotions and chunked prefill (the channel-major key part),
 and the stored factors themselves.
 """
@@ -61,6 +62,9 @@ def _rope_case(cfg_id, T, B=1, kv_heads=2, r_k=None, r_v=None, n_splits=(0,), la
     (3, 64 * 16 + 33, 1, 2, 8, 24, (0,)),      # key rank below the value rank
     (2, 64 * 14 + 5, 2, 2, 32, 13, (0, 3)),    # unequal, odd value rank (exact-rank part)
     (4, 64 * 11 + 40, 1, 2, 16, 30, (0,)),     # unequal, value rank 30
+    (2, 64 * 10 + 50, 1, 2, 40, 40, (0, 2)),   # r > 32: one wave per SIMD, two reduction steps
+    (3, 64 * 12 + 3, 1, 2, 64, 64, (0,)),      # full rank of a 64-token page
+    (2, 64 * 9 + 17, 2, 1, 56, 52, (0, 3)),    # (56, 52): same padded rank
 ])
 def test_pre_rope_matrix_core_path(cfg_id, T, B, kv, rk, rv, splits):
     _rope_case(cfg_id, T, B, kv, rk, rv, splits, label="mfma")
@@ -68,7 +72,7 @@ def test_pre_rope_matrix_core_path(cfg_id, T, B, kv, rk, rv, splits):
 
 @pytest.mark.parametrize("cfg_id,T,rk,rv", [
     (2, 64 * 12 + 7, 40, 24),   # unequal, key rank > 32
-    (2, 64 * 10 + 50, 40, 40),  # r > 32
+    (2, 64 * 10 + 50, 24, 48),  # unequal, value rank > 32
     (1, 64 * 16, 16, 16),       # fp32 storage
     (1, 64 * 9 + 3, 64, 64),    # fp32, full rank
 ])
