@@ -229,7 +229,7 @@ __device__ void compress_one(const CompressJob& job, int64_t n, CompressShared& 
   const int kind = pr.kind;
   const Elem* X = (const Elem*)pr.X;
   const int trans = pr.trans;
-  const int r = pr.r;  // > 32, so the page has 64 rows (launch_compress)
+  const int r = pr.r;  // the job's largest rank is > 32, so the page has 64 rows (launch_compress)
 
   // 1. Gram matrix, eigenvector accumulator = I
   gram<Elem, WPP>(X, trans, kP, sh.G, lane, wv);
@@ -317,15 +317,19 @@ __device__ void compress_one(const CompressJob& job, int64_t n, CompressShared& 
   const bool packed = job.fac != nullptr;
   const PackDims pd = pack_dims(r);
   const int r_store = packed ? 8 * pd.n8 : r;
+  // a packed value part holds Rf_V at r2 ranks (the exact rank, rounded up
+  // to even, when r8 <= 32: a job's value rank may be that small while its
+  // key rank takes this route)
+  const int rf_store = packed && kind != 0 ? pd.r2 : r_store;
   uint8_t* part = nullptr;
   if (packed) part = factor_part(job, pr);
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
-    if (16 * mi < r_store) {
+    if (16 * mi < rf_store) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int i = 16 * mi + 4 * q + v;
-        if (i < r_store) {
+        if (i < rf_store) {
           const float sg = i < r ? sh.sig[i] : 0.f;
           const float inv = sg > 0.f ? 1.f / sg : 0.f;
 #pragma unroll

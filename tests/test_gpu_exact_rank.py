@@ -4,8 +4,9 @@ A bf16 / fp32 value part keeps Rf_V (the V2 operand) at r rounded up to
 even, not at r8 = 8 ceil(r / 8), for r8 <= 32: each 16-channel tile holds the
 partial lane quad's ranks first, then the full quads (include/pkv.h, the
 layout note).  Key parts are unchanged.  The attention kernels read such a
-part through each lane's own offset and zero the slots of ranks it does not
-hold.
+part through each lane's own offset; a slot of a rank the part does not
+hold reads a neighbouring entry and meets a zero rank weight (the padded
+rank rows of Lf_V^T are zero).
 
 - The decomposition writes that layout: every element of a GPU-written key
   and value part is what the host packer writes for the part's own factors
@@ -15,7 +16,9 @@ hold.
   (the cfg-3 recipe, sigma_i = i^-1.2: every kept rank shows in the output).
 - End to end at the gates of the cache dtype, at P = 64 and 32, on the
   matrix-core kernels (equal and unequal padded ranks, pre-RoPE keys) and
-  the fp32 (vector-ALU) path.
+  the vector-ALU path (fp32 storage; pre-RoPE keys at unequal ranks above
+  32), including value parts written by the Jacobi route of a cache whose
+  key rank is above 32.
 """
 import numpy as np
 import pytest
@@ -77,6 +80,7 @@ def test_gpu_parts_are_the_host_layout(P, rk, rv):
     (64, 8, 5, (0, 2)),     # A = 2: r2 = 6, the fourth quad empty
     (64, 8, 14, (0,)),      # unequal padded ranks
     (64, 32, 22, (0,)),     # unequal padded ranks (r8 32 / 24)
+    (64, 48, 22, (0, 2)),   # key rank above 32: two reduction steps
     (32, 16, 14, (0, 3)),   # the pages' operating point
     (32, 24, 20, (0,)),
     (32, 32, 26, (0, 2)),
@@ -114,6 +118,8 @@ def test_attention_on_oracle_factors(P, rk, rv, splits):
     (3, 64, 24, 23, None),
     (2, 64, 16, 14, 5e5),    # pre-RoPE keys, matrix-core kernel
     (3, 32, 24, 22, 1e6),    # pre-RoPE keys at 32-token pages
+    (2, 64, 48, 13, None),   # key rank above 32: the job's Jacobi route writes the exact-rank value part
+    (2, 64, 40, 13, 5e5),    # ... read by the vector-ALU kernel (pre-RoPE, unequal ranks above 32)
     (1, 64, 16, 13, None),   # fp32 storage: vector-ALU kernel
     (1, 32, 16, 13, None),
 ])
