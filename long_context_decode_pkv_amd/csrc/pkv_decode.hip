@@ -2490,6 +2490,44 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
           return hipErrorInvalidValue;
       }
     }
+  } else if (g.dtype == PKV_BF16 && !g.rope && g.P == kP && n8k != n8v && n8k <= 8 && n8v <= 8) {
+    // unequal padded ranks with one above 32 (64-token pages; one launch per
+    // cache in a batch, as above)
+    if constexpr (kBatch) {
+      return hipErrorNotSupported;
+    } else {
+      switch (n8k * 8 + n8v) {
+#define PKV_ASYM_WIDE(NK, NV)                                                                             \
+  case NK * 8 + NV:                                                                                       \
+    if constexpr (NK != NV && (NK > 4 || NV > 4)) {                                                       \
+      if constexpr (NV <= 4) {                                                                            \
+        if (ev) {                                                                                         \
+          hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Factors<NK, NV, true>, KA>), grid, dim3(256), 0,  \
+                                stream, kev.start, kev.stop, 0, ka);                                      \
+          break;                                                                                          \
+        }                                                                                                 \
+      }                                                                                                   \
+      hipExtLaunchKernelGGL((decode_mfma_kernel<Bf16Factors<NK, NV>, KA>), grid, dim3(256), 0, stream,    \
+                            kev.start, kev.stop, 0, ka);                                                  \
+    }                                                                                                     \
+    break;
+#define PKV_ASYM_WIDE_ROW(NK)                                                                            \
+  PKV_ASYM_WIDE(NK, 1) PKV_ASYM_WIDE(NK, 2) PKV_ASYM_WIDE(NK, 3) PKV_ASYM_WIDE(NK, 4) PKV_ASYM_WIDE(NK, 5) \
+  PKV_ASYM_WIDE(NK, 6) PKV_ASYM_WIDE(NK, 7) PKV_ASYM_WIDE(NK, 8)
+        PKV_ASYM_WIDE_ROW(1)
+        PKV_ASYM_WIDE_ROW(2)
+        PKV_ASYM_WIDE_ROW(3)
+        PKV_ASYM_WIDE_ROW(4)
+        PKV_ASYM_WIDE_ROW(5)
+        PKV_ASYM_WIDE_ROW(6)
+        PKV_ASYM_WIDE_ROW(7)
+        PKV_ASYM_WIDE_ROW(8)
+#undef PKV_ASYM_WIDE_ROW
+#undef PKV_ASYM_WIDE
+        default:
+          return hipErrorInvalidValue;
+      }
+    }
   } else if (g.dtype == PKV_BF16 && g.rope && n8k != n8v && n8k <= kRopeAsymMaxN8 && n8v <= kRopeAsymMaxN8) {
     // pre-RoPE keys at unequal padded ranks up to 32 (one launch per cache
     // in a batch, as above)

@@ -93,6 +93,7 @@ def test_batch_pre_rope_keys(rk, rv):
 @pytest.mark.parametrize("cfg_id,store,rk,rv", [
     (1, None, 16, 16),     # fp32: VALU kernel, one launch per cache
     (2, None, 24, 16),     # unequal padded ranks
+    (2, None, 48, 22),     # unequal, one rank above 32
     (2, "int4", 24, 16),   # INT4 with unequal padded ranks
 ])
 def test_batch_per_cache_fallback(cfg_id, store, rk, rv):

@@ -78,8 +78,10 @@ def test_bf16_other_ranks(r):
 
 
 # (16, 14) pads to one multiple of 8; the others to two (the two-rank
-# matrix-core format), up to r = 32 on either side
-@pytest.mark.parametrize("rk,rv", [(16, 14), (24, 16), (8, 24), (32, 8), (1, 17), (20, 31)])
+# matrix-core format), up to r = 64 on either side: above 32 one side takes
+# two reduction steps, the value side an exact-rank part when r_V <= 32
+@pytest.mark.parametrize("rk,rv", [(16, 14), (24, 16), (8, 24), (32, 8), (1, 17), (20, 31),
+                                   (48, 24), (64, 13), (8, 64), (40, 56), (60, 36), (33, 5)])
 def test_bf16_asymmetric_ranks(rk, rv):
     run_case(2, 64 * 16 + 30, B=1, kv_heads=2, r_k=rk, r_v=rv, label="asym")
 
