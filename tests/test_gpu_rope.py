@@ -113,10 +113,14 @@ def test_pre_rope_factors_are_the_pages_own():
         assert err <= bound, (f, err, opt[f], bound)
 
 
-def test_pre_rope_decode_steps_against_oracle():
+@pytest.mark.parametrize("rk,rv", [(None, None), (48, 48), (40, 13)])
+def test_pre_rope_decode_steps_against_oracle(rk, rv):
     """pkv_decode_step on a pre-RoPE cache: the new key is rotated at its
     position in the merge, promotions store channel-major key parts; checked
-    against the oracle at every step."""
+    against the oracle at every step.  Ranks: the workload's r = 16; r = 48
+    (the one-wave matrix-core format, promotions on the Jacobi route);
+    (40, 13) (vector-ALU kernel, an exact-rank value part written by the
+    Jacobi route)."""
     import torch
     require_gpu()
     cfg_id, T0, steps = 4, 64 * 10 + 3, 140
@@ -124,12 +128,13 @@ def test_pre_rope_decode_steps_against_oracle():
     cfg = d["cfg"]
     dt = cfg["dtype"]
     f = _freqs(cfg_id)
-    cache = make_cache(d, max_tokens=T0 + steps)
+    rk = cfg["r_k"] if rk is None else rk
+    rv = cfg["r_v"] if rv is None else rv
+    cache = make_cache(d, r_k=rk, r_v=rv, max_tokens=T0 + steps)
     cache.set_key_rope(f)
     Kd, Vd = to_dev(d["K"], dt), to_dev(d["V"], dt)
     cache.prefill(Kd[:, :, :T0].contiguous(), Vd[:, :, :T0].contiguous())
-    inc = oracle.IncrementalDecoder(d["K64"], d["V64"], 64, cfg["s"], cfg["w"], cfg["r_k"], cfg["r_v"], dt,
-                                    key_rope=f)
+    inc = oracle.IncrementalDecoder(d["K64"], d["V64"], 64, cfg["s"], cfg["w"], rk, rv, dt, key_rope=f)
     ws = cache.workspace(512)
     worst = 0.0
     for t in range(steps):
@@ -142,7 +147,7 @@ def test_pre_rope_decode_steps_against_oracle():
         err = rel_err(o, ref_s)
         worst = max(worst, err)
         assert err <= TOL[dt], (t, err)
-    print(f"[pre-RoPE step vs oracle] {steps} steps, worst err {worst:.3e}")
+    print(f"[pre-RoPE step vs oracle r=({rk},{rv})] {steps} steps, worst err {worst:.3e}")
 
 
 def test_pre_rope_chunked_prefill_matches_one_shot():

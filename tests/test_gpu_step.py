@@ -93,19 +93,24 @@ def test_step_fp32_cache():
     _step_vs_separate(1, 64 * 6 + 10, 60, B=1, kv_heads=1, label="fp32")
 
 
-def test_step_against_oracle():
+@pytest.mark.parametrize("rk,rv", [(None, None), (48, 13), (8, 40)])
+def test_step_against_oracle(rk, rv):
     """Incremental decode driven by pkv_decode_step, checked against the
-    oracle at every step (workload-4 recipe, reduced batch and heads)."""
+    oracle at every step (workload-4 recipe, reduced batch and heads), at
+    the workload's ranks and at unequal ranks with one above 32 (promotions
+    on the Jacobi route, exact-rank value part at (48, 13))."""
     import torch
     require_gpu()
     cfg_id, T0, steps = 4, 64 * 10 + 3, 140
     d = synth.decode_inputs(cfg_id, T=T0 + steps, B=2, kv_heads=2, with_f64=True)
     cfg = d["cfg"]
     dt = cfg["dtype"]
-    cache = make_cache(d, max_tokens=T0 + steps)
+    rk = cfg["r_k"] if rk is None else rk
+    rv = cfg["r_v"] if rv is None else rv
+    cache = make_cache(d, r_k=rk, r_v=rv, max_tokens=T0 + steps)
     Kd, Vd = to_dev(d["K"], dt), to_dev(d["V"], dt)
     cache.prefill(Kd[:, :, :T0].contiguous(), Vd[:, :, :T0].contiguous())
-    inc = oracle.IncrementalDecoder(d["K64"], d["V64"], 64, cfg["s"], cfg["w"], cfg["r_k"], cfg["r_v"], dt)
+    inc = oracle.IncrementalDecoder(d["K64"], d["V64"], 64, cfg["s"], cfg["w"], rk, rv, dt)
     ws = cache.workspace(512)
     worst = 0.0
     for t in range(steps):
@@ -122,7 +127,7 @@ def test_step_against_oracle():
         ocls, oslot = oracle.classify(T + 1, 64, cfg["s"], cfg["w"])
         np.testing.assert_array_equal(cls, ocls, err_msg=f"step {t}")
         np.testing.assert_array_equal(slot, oslot, err_msg=f"step {t}")
-    print(f"[step vs oracle] {steps} steps, worst err {worst:.3e}")
+    print(f"[step vs oracle r=({rk},{rv})] {steps} steps, worst err {worst:.3e}")
 
 
 def test_step_errors():
