@@ -42,16 +42,16 @@ CACHE_DIR = os.environ.get("PKV_BENCH_CACHE", "/tmp/pkv_bench_inputs")
 # HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc runs of
 # this script (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled
 # by what the same counter reads for the 1 GiB device copy of `--workload copy`
-# (FETCH_SIZE reads 524301.75 KiB for 2^30 bytes read -> x1.99995; WRITE_SIZE
+# (FETCH_SIZE reads 524301.6 KiB for 2^30 bytes read -> x1.99995; WRITE_SIZE
 # reads 1048576 KiB for 2^30 bytes written -> x1.0).  A figure holds only for
 # the kernel sources whose hash it carries; any change to them makes it null.
 PMC_TRAFFIC = {
-    "qwen3-32b-layer-128k": {"sha256": "0be4a76b28194dec7c243af9ca75f955ec22cd5627c6b059deccfa3953c705ab",
-                           "fetch": 303085536, "write": 1114112},
-    "qwen3-32b-layer-128k-int4": {"sha256": "0be4a76b28194dec7c243af9ca75f955ec22cd5627c6b059deccfa3953c705ab",
-                                "fetch": 88843768, "write": 2228224},
-    "llama3.1-8b-layer-p32": {"sha256": "0be4a76b28194dec7c243af9ca75f955ec22cd5627c6b059deccfa3953c705ab",
-                            "fetch": 640462048, "write": 1114112},
+    "qwen3-32b-layer-128k": {"sha256": "3024b2ca48695e27f815c8ea88ab3a2437e597fb35b9ba98f715ee15fac9ab7c",
+                           "fetch": 303085466, "write": 1114112},
+    "qwen3-32b-layer-128k-int4": {"sha256": "3024b2ca48695e27f815c8ea88ab3a2437e597fb35b9ba98f715ee15fac9ab7c",
+                                "fetch": 88847381, "write": 2228224},
+    "llama3.1-8b-layer-p32": {"sha256": "3024b2ca48695e27f815c8ea88ab3a2437e597fb35b9ba98f715ee15fac9ab7c",
+                            "fetch": 640461063, "write": 1114112},
 }
 TRAFFIC_SOURCES = ("long_context_decode_pkv_amd/csrc/pkv_decode.hip",
                    "long_context_decode_pkv_amd/csrc/pkv_internal.h")

@@ -936,11 +936,11 @@ __device__ inline void dense_page_rope(SoftState& st, const uint16_t* Kp, const 
   }
 }
 
-// Ranks of the matrix-core pre-RoPE path: equal padded ranks up to 64
-// (64-token pages), unequal ones up to 32; other pre-RoPE caches take the
-// VALU kernel.  Above r = 32 the format runs one wave per SIMD.
-constexpr int kRopeMfmaMaxN8 = 8;
-constexpr int kRopeAsymMaxN8 = 4;
+// The matrix-core pre-RoPE path takes equal padded ranks up to 64 at
+// 64-token pages (one wave per SIMD above r = 32) and, at one reduction step
+// per channel tile (r <= 32), every rank pair at either page length; other
+// pre-RoPE caches take the VALU kernel.
+constexpr int kRopeOneStepMaxN8 = 4;
 constexpr int rope_waves_per_simd(int n8) { return n8 <= 4 ? mfma_waves_per_simd(n8) : 1; }
 
 // bf16 factors of pre-RoPE keys: the key part holds Rf_K channel-major (the
@@ -2228,7 +2228,7 @@ bool batched_kernel(const CacheGeom& g) {
   if (n8k != n8v) return false;
   if (g.P != kP) return g.dtype == PKV_BF16 || g.dtype == PKV_BF16_INT4;  // the 32-row formats (r <= 32)
   if (g.dtype == PKV_BF16_INT4) return n8k <= 4;
-  return g.dtype == PKV_BF16 && n8k <= 8 && (!g.rope || n8k <= kRopeMfmaMaxN8);
+  return g.dtype == PKV_BF16 && n8k <= 8;
 }
 
 int decode_batch_splits(const CacheGeom& g, const int64_t* T, int n, int* ns) {
@@ -2366,7 +2366,7 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
       default:
         return hipErrorInvalidValue;
     }
-  } else if (g.dtype == PKV_BF16 && g.P == kP && n8k == n8v && (!g.rope || n8k <= kRopeMfmaMaxN8)) {
+  } else if (g.dtype == PKV_BF16 && g.P == kP && n8k == n8v) {
     switch (n8k * 2 + (g.rope ? 1 : 0)) {
 #define PKV_CASE(N)                                                                                        \
   case 2 * N:                                                                                              \
@@ -2413,7 +2413,7 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
       default:
         return hipErrorInvalidValue;
     }
-  } else if (g.dtype == PKV_BF16 && g.P == kMinP && n8k == n8v && g.rope && n8k <= kRopeAsymMaxN8) {
+  } else if (g.dtype == PKV_BF16 && g.P == kMinP && n8k == n8v && g.rope && n8k <= kRopeOneStepMaxN8) {
     switch (n8k) {
 #define PKV_HALF_ROPE(N)                                                                                   \
   case N:                                                                                                  \
@@ -2528,7 +2528,7 @@ hipError_t dispatch_partial(const CacheGeom& g, const KA& ka, dim3 grid, hipStre
           return hipErrorInvalidValue;
       }
     }
-  } else if (g.dtype == PKV_BF16 && g.rope && n8k != n8v && n8k <= kRopeAsymMaxN8 && n8v <= kRopeAsymMaxN8) {
+  } else if (g.dtype == PKV_BF16 && g.rope && n8k != n8v && n8k <= kRopeOneStepMaxN8 && n8v <= kRopeOneStepMaxN8) {
     // pre-RoPE keys at unequal padded ranks up to 32 (one launch per cache
     // in a batch, as above)
     if constexpr (kBatch) {
